@@ -1,0 +1,137 @@
+"""Seeded synthetic workloads for the gated delta rule forward pass.
+
+This module draws inputs only; it holds none of the method's arithmetic, and
+both the HIP path's tests/bench and the oracle-based checks take their inputs
+from it.  The recipe (one numpy PCG64 stream per workload, fixed draw order):
+
+  1. q ~ N(0,1), then L2-normalised per (batch, token, head) along features
+     in fp64 (the per-head L2 norm of q and k in the DeltaNet block);
+  2. k ~ N(0,1), normalised the same way;
+  3. v ~ N(0,1);
+  4. alpha = sigmoid(N(mu_a, 0.5)) — one value per token-head (scalar gate)
+     or one per key channel (channel gate); mu_a = 2 for every listed workload;
+  5. beta = sigmoid(N(0,1)) per token-head;
+  6. state0 ~ N(0, std^2) per head when std > 0, else no start state.
+
+Values are drawn in fp64, rounded to fp32, and q/k/v are then rounded to
+bf16 (round-to-nearest-even) for bf16 workloads.  The arrays returned hold
+exactly the values that are uploaded, so any checker reads the same numbers.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    chunk: int
+    dtype: str = "bf16"          # dtype of q, k, v: "bf16" or "f32"
+    gate: str = "scalar"         # "scalar" or "channel"
+    state0_std: float = 0.0      # 0 -> zero start state
+    n_segments: int = 1          # >1: sequence-parallel split
+    alpha_mean: float = 2.0      # mean of the gate logits
+    seed: int = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    @property
+    def head_tokens(self) -> int:
+        return self.B * self.T * self.H
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads of this path, index 0..4.
+WORKLOADS = [
+    Workload("tiny-f32", B=1, H=1, T=256, dk=16, dv=16, chunk=16, dtype="f32",
+             seed=1234),
+    Workload("small-bf16", B=4, H=8, T=2048, dk=64, dv=64, chunk=64, seed=1235),
+    Workload("main-bf16", B=2, H=16, T=8192, dk=128, dv=128, chunk=64,
+             state0_std=0.02, seed=1236),
+    Workload("long-seqpar-bf16", B=1, H=4, T=65536, dk=128, dv=128, chunk=64,
+             n_segments=8, seed=1237),
+    Workload("channel-gate-bf16", B=8, H=16, T=4096, dk=128, dv=128, chunk=64,
+             gate="channel", seed=1238),
+]
+
+
+def workload(key) -> Workload:
+    if isinstance(key, Workload):
+        return key
+    if isinstance(key, int):
+        return WORKLOADS[key]
+    for w in WORKLOADS:
+        if w.name == key:
+            return w
+    raise KeyError(key)
+
+
+def _l2_normalise(x):
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    n[n == 0.0] = 1.0
+    return x / n
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _round_bf16(x32):
+    """fp32 numpy -> bf16 values (RNE), returned as fp32 numpy."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32)).to(torch.bfloat16)
+    return t.to(torch.float32).numpy()
+
+
+def make_inputs(w: Workload, seed: int | None = None) -> dict:
+    """Draw one workload.  Returns fp32 numpy arrays: q, k [B,T,H,dk],
+    v [B,T,H,dv], alpha [B,T,H] or [B,T,H,dk], beta [B,T,H], and state0
+    [B,H,dv,dk] or None."""
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    out = {}
+    for name, d in (("q", dk), ("k", dk)):
+        x = _l2_normalise(rng.standard_normal((B, T, H, d)))
+        out[name] = x.astype(np.float32)
+        del x
+    out["v"] = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    ashape = (B, T, H) if w.gate == "scalar" else (B, T, H, dk)
+    out["alpha"] = _sigmoid(rng.normal(w.alpha_mean, 0.5, ashape)).astype(np.float32)
+    out["beta"] = _sigmoid(rng.standard_normal((B, T, H))).astype(np.float32)
+    if w.state0_std > 0:
+        out["state0"] = (w.state0_std * rng.standard_normal((B, H, dv, dk))).astype(np.float32)
+    else:
+        out["state0"] = None
+    if w.dtype == "bf16":
+        for name in ("q", "k", "v"):
+            out[name] = _round_bf16(out[name])
+    elif w.dtype != "f32":
+        raise ValueError(w.dtype)
+    return out
+
+
+def to_device(inputs: dict, w: Workload, device="cuda"):
+    """Upload to torch tensors: q/k/v in the workload dtype, the rest fp32."""
+    import torch
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    res = {}
+    for name, arr in inputs.items():
+        if arr is None:
+            res[name] = None
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+        if name in ("q", "k", "v"):
+            t = t.to(dt)
+        res[name] = t.to(device)
+    return res
