@@ -1,0 +1,202 @@
+"""Benchmark of the chunkwise gated delta rule forward on one MI355X.
+
+One step = one full forward (every kernel of the path) over one batch of the
+workload, inputs already resident in HBM.  Prints ONE JSON line on stdout;
+diagnostics go to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main-bf16]
+
+Default workload: main-bf16 (B=2, H=16, T=8192, dk=dv=128, chunk 64, scalar
+gate, start state N(0, 0.02^2)).  The long workload runs the sequence-parallel
+entry point (8 segments) and also reports the single-stream time beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec + % MFMA/HBM roofline, gated-delta chunk fwd H=16 d=128 T=8K"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> float:
+    """HBM bytes the method must move: read q, k, v (input dtype), alpha,
+    beta (fp32; alpha is dk wide for the channel gate), write O (fp32);
+    per head read the start state (if any) and write the final state."""
+    s_in = 2 if w.dtype == "bf16" else 4
+    per_ht = (2 * w.dk + w.dv) * s_in + 4 + (4 * w.dk if w.gate == "channel" else 4) + 4 * w.dv
+    per_head = 4 * w.dv * w.dk * (2 if w.state0_std > 0 else 1)
+    return float(per_ht * w.head_tokens + per_head * w.B * w.H)
+
+
+def algorithmic_flops(w) -> float:
+    """5 C^2 d + 6 C d^2 + C^3 / 3 per chunk-head (d = dk = dv)."""
+    C, d = w.chunk, w.dk
+    nch = w.B * w.H * ((w.T + C - 1) // C)
+    return float(nch * (5 * C * C * d + 6 * C * d * d + C ** 3 / 3))
+
+
+def cpu_baseline(w, inp, max_threads=16, target_s=10.0):
+    """Time the oracle on a bounded sample of (batch, head) slices."""
+    import numpy as np
+
+    import oracle
+    cores = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    g = oracle.GATE_SCALAR if w.gate == "scalar" else oracle.GATE_CHANNEL
+
+    def run(n_pairs, n_tok):
+        sel = pairs[:n_pairs]
+        q = np.stack([inp["q"][b, :n_tok, h] for b, h in sel])[:, :, None]
+        k = np.stack([inp["k"][b, :n_tok, h] for b, h in sel])[:, :, None]
+        v = np.stack([inp["v"][b, :n_tok, h] for b, h in sel])[:, :, None]
+        a = np.stack([inp["alpha"][b, :n_tok, h] for b, h in sel])[:, :, None]
+        be = np.stack([inp["beta"][b, :n_tok, h] for b, h in sel])[:, :, None]
+        s0 = None
+        if inp["state0"] is not None:
+            s0 = np.stack([inp["state0"][b, h] for b, h in sel])[:, None]
+        t = time.perf_counter()
+        oracle.forward(q, k, v, a, be, s0, gate=g, threads=min(cores, n_pairs))
+        return time.perf_counter() - t
+
+    # probe with one slice of 1024 tokens, then size the sample
+    n_tok = min(w.T, 1024)
+    t1 = run(1, n_tok)
+    n_pairs = min(len(pairs), cores)
+    per_pair_full = t1 * w.T / n_tok
+    n_tok = w.T if per_pair_full <= target_s else max(256, int(w.T * target_s / per_pair_full))
+    dt = run(n_pairs, n_tok)
+    head_tokens = n_pairs * n_tok
+    tok_per_s = head_tokens / dt / w.H   # tokens of the workload (all H heads) per second
+    return {"value": tok_per_s, "unit": "tokens/sec", "cores": min(cores, n_pairs),
+            "kind": "oracle",
+            "sample": f"{n_pairs} (batch,head) slices x {n_tok} tokens of {w.name}, "
+                      f"fp64 token loop, {dt:.2f} s; tokens/s = head-tokens/s / H"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="main-bf16")
+    ap.add_argument("--segments", type=int, default=None,
+                    help="sequence-parallel segments (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU: no sharding or collectives are built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_12_amd import gdn
+    from gated_delta_rule_12_amd.workloads import make_inputs, to_device, workload
+
+    w = workload(int(args.workload) if args.workload.isdigit() else args.workload)
+    G = args.segments if args.segments is not None else w.n_segments
+    log(f"workload {w}, segments {G}")
+    t = time.time()
+    inp = make_inputs(w)
+    d = to_device(inp, w, "cuda")
+    log(f"inputs ready in {time.time() - t:.1f} s")
+    dt_code = gdn.GDN_BF16 if w.dtype == "bf16" else gdn.GDN_F32
+    gate_code = gdn.GDN_GATE_SCALAR if w.gate == "scalar" else gdn.GDN_GATE_CHANNEL
+    path = gdn.gdn_chunk_path(w.dk, w.dv, w.chunk, dt_code, gate_code)
+    out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    st = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+    ws = gdn.workspace_for(d["q"], d["v"], d["alpha"], w.chunk, G)
+
+    def step(nseg=G):
+        gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
+                      chunk=w.chunk, n_segments=nseg, out=out, state_out=st,
+                      workspace=ws if nseg == G else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # timed region: events on the stream the kernels are launched on
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gdn.gdn_profile_enable(True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kern = gdn.gdn_profile_read()
+    gdn.gdn_profile_enable(False)
+    per_kernel_us = {k: 1e3 * v[0] / max(1, v[1]) for k, v in kern.items()}
+    step_kernel_us = sum(per_kernel_us.values())
+    dominant = max(per_kernel_us, key=per_kernel_us.get) if per_kernel_us else None
+    log(f"step {ms * 1e3:.1f} us; kernels (avg us): "
+        + ", ".join(f"{k} {v:.1f}" for k, v in per_kernel_us.items()))
+
+    tokens = w.B * w.T
+    value = tokens / (ms * 1e-3)
+    abytes = algorithmic_bytes(w)
+    aflops = algorithmic_flops(w)
+    achieved = abytes / (step_kernel_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "+".join(per_kernel_us.keys()),
+            "kernel_avg_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
+            "dominant": dominant,
+            "algorithmic_bytes": abytes,
+            "mfma_frac": round(aflops / (step_kernel_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    extra = {}
+    if G > 1:
+        for _ in range(2):
+            step(1)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        n1 = max(1, args.steps // 5)
+        for _ in range(n1):
+            step(1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extra["single_stream_ms"] = round(e0.elapsed_time(e1) / n1, 4)
+        extra["seqpar_ms"] = round(ms, 4)
+        log(f"single-stream {extra['single_stream_ms']} ms vs seq-par {ms:.4f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
+        cpu = cpu_baseline(w, inp)
+        log(f"cpu baseline: {cpu}")
+
+    res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/sec", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if path == gdn.GDN_PATH_MFMA else "f32",
+           "data": "synthetic",
+           "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                      "chunk": w.chunk, "gate": w.gate, "input_dtype": w.dtype,
+                      "entry": "gdn_seqpar_fwd" if G > 1 else "gdn_chunk_fwd",
+                      "segments": G, "global_batch": w.B, "seq_len": w.T,
+                      "parallelism": "single-gpu",
+                      "kernel_path": "mfma" if path == gdn.GDN_PATH_MFMA else "valu"},
+           "roofline": roof, "cpu_baseline": cpu}
+    res.update(extra)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

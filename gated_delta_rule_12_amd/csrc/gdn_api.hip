@@ -1,0 +1,231 @@
+// C ABI of libgdn: argument validation, workspace sizing, dispatch between
+// the MFMA and vector-ALU kernel families, and optional per-kernel timing.
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "gdn_internal.h"
+#include "../../include/gdn.h"
+
+namespace gdn {
+namespace {
+
+bool dim_ok(int64_t d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+bool chunk_ok(int32_t c) { return c == 16 || c == 32 || c == 64; }
+
+int validate(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+             int32_t dtype, int32_t gate, int32_t order, int32_t n_segments) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_E_ARG;
+    if (gate != GDN_GATE_SCALAR && gate != GDN_GATE_CHANNEL) return GDN_E_ARG;
+    if (order != GDN_PREDICT_THEN_DECAY && order != GDN_DECAY_THEN_PREDICT) return GDN_E_ARG;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || chunk <= 0 || n_segments <= 0)
+        return GDN_E_SHAPE;
+    // grid limits: chunks and heads map onto grid dimensions
+    if (H > 65535 || B > 65535 || T / chunk > (int64_t)1 << 30) return GDN_E_SHAPE;
+    if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return GDN_E_UNSUPPORTED;
+    if (H * (int64_t)n_segments > 65535) return GDN_E_UNSUPPORTED;
+    return GDN_OK;
+}
+
+Problem make_problem(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                     int32_t dtype, int32_t gate, int32_t order, float scale) {
+    Problem p{};
+    p.B = B; p.T = T; p.H = H; p.dk = dk; p.dv = dv;
+    p.C = chunk;
+    p.NC = (int)((T + chunk - 1) / chunk);
+    p.dtype = dtype; p.gate = gate; p.order = order; p.scale = scale;
+    return p;
+}
+
+WsLayout layout_for(const Problem& p, const Split& sp) {
+    return mfma_supported(p.dk, p.dv, p.C, p.dtype, p.gate) ? mfma_layout(p, sp)
+                                                             : valu_layout(p, sp);
+}
+
+// ---- profiling record ------------------------------------------------------
+struct ProfEvent { int kernel; hipEvent_t a, b; };
+bool g_prof_on = false;
+std::vector<std::string> g_prof_names;
+std::vector<ProfEvent> g_prof_events;
+std::vector<hipEvent_t> g_prof_pool;
+std::vector<double> g_prof_ms;
+std::vector<int64_t> g_prof_cnt;
+int g_prof_open = -1;
+hipEvent_t g_prof_open_a = nullptr;
+
+hipEvent_t pool_get() {
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+void prof_drain() {
+    for (auto& ev : g_prof_events) {
+        float ms = 0.f;
+        if (hipEventSynchronize(ev.b) == hipSuccess && hipEventElapsedTime(&ms, ev.a, ev.b) == hipSuccess) {
+            g_prof_ms[ev.kernel] += ms;
+            g_prof_cnt[ev.kernel] += 1;
+        }
+        g_prof_pool.push_back(ev.a);
+        g_prof_pool.push_back(ev.b);
+    }
+    g_prof_events.clear();
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
+
+int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                int32_t dtype, int32_t gate, int32_t order, float scale, int32_t n_segments,
+                const void* q, const void* k, const void* v, const float* alpha,
+                const float* beta, const float* state0, float* out, float* state_out,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    int s = validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments);
+    if (s != GDN_OK) return s;
+    Problem p = make_problem(B, T, H, dk, dv, chunk, dtype, gate, order, scale);
+    if (B * H == 0) return GDN_OK;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_E_ARG;
+    p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+    p.s0 = state0; p.out = out; p.s_out = state_out;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.NC == 0) return finish(copy_state(p, st));
+    const Split sp = make_split(p.NC, n_segments);
+    const WsLayout L = layout_for(p, sp);
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return GDN_E_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    if (mfma_supported(dk, dv, chunk, dtype, gate)) return finish(mfma_forward(p, sp, ws, st));
+    return finish(valu_forward(p, sp, ws, st));
+}
+
+}  // namespace
+
+void prof_begin(const char* name, hipStream_t st) {
+    if (!g_prof_on) return;
+    int idx = -1;
+    for (size_t i = 0; i < g_prof_names.size(); ++i)
+        if (g_prof_names[i] == name) idx = (int)i;
+    if (idx < 0) {
+        g_prof_names.emplace_back(name);
+        g_prof_ms.push_back(0.0);
+        g_prof_cnt.push_back(0);
+        idx = (int)g_prof_names.size() - 1;
+    }
+    g_prof_open = idx;
+    g_prof_open_a = pool_get();
+    if (g_prof_open_a) hipEventRecord(g_prof_open_a, st);
+}
+
+void prof_end(hipStream_t st) {
+    if (!g_prof_on || g_prof_open < 0 || !g_prof_open_a) return;
+    hipEvent_t b = pool_get();
+    if (b) {
+        hipEventRecord(b, st);
+        g_prof_events.push_back({g_prof_open, g_prof_open_a, b});
+    }
+    g_prof_open = -1;
+    g_prof_open_a = nullptr;
+    if (g_prof_events.size() > 4096) prof_drain();
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_str(int status) {
+    switch (status) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_E_ARG: return "GDN_E_ARG: null pointer or invalid enum";
+        case GDN_E_SHAPE: return "GDN_E_SHAPE: negative or inconsistent size";
+        case GDN_E_UNSUPPORTED: return "GDN_E_UNSUPPORTED: dk/dv must be multiples of 16 up to 128, chunk 16, 32 or 64";
+        case GDN_E_WORKSPACE: return "GDN_E_WORKSPACE: workspace missing or smaller than gdn_workspace_bytes()";
+        case GDN_E_HIP: return "GDN_E_HIP: a HIP runtime call or kernel launch failed";
+        default: return "unknown gdn status";
+    }
+}
+
+int gdn_validate(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                 int32_t dtype, int32_t gate, int32_t order, int32_t n_segments) {
+    return validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments);
+}
+
+int gdn_chunk_path(int64_t dk, int64_t dv, int32_t chunk, int32_t dtype, int32_t gate) {
+    int s = validate(1, 0, 1, dk, dv, chunk, dtype, gate, 0, 1);
+    if (s != GDN_OK) return s;
+    return mfma_supported(dk, dv, chunk, dtype, gate) ? GDN_PATH_MFMA : GDN_PATH_VALU;
+}
+
+size_t gdn_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           int32_t chunk, int32_t dtype, int32_t gate, int32_t n_segments) {
+    if (validate(B, T, H, dk, dv, chunk, dtype, gate, 0, n_segments) != GDN_OK) return 0;
+    Problem p = make_problem(B, T, H, dk, dv, chunk, dtype, gate, 0, 1.f);
+    if (p.NC == 0 || B * H == 0) return 0;
+    return layout_for(p, make_split(p.NC, n_segments)).total;
+}
+
+int gdn_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                  int32_t dtype, int32_t gate, int32_t order, float scale,
+                  const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta, const float* state0, float* out, float* state_out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, 1, q, k, v, alpha,
+                       beta, state0, out, state_out, workspace, workspace_bytes, stream);
+}
+
+int gdn_seqpar_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                   int32_t dtype, int32_t gate, int32_t order, float scale, int32_t n_segments,
+                   const void* q, const void* k, const void* v, const float* alpha,
+                   const float* beta, const float* state0, float* out, float* state_out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, n_segments, q, k, v,
+                       alpha, beta, state0, out, state_out, workspace, workspace_bytes, stream);
+}
+
+int gdn_recurrent_ref(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t dtype,
+                      int32_t gate, int32_t order, float scale, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta,
+                      const float* state0, float* out, float* state_out, void* stream) {
+    int s = validate(B, T, H, dk, dv, 16, dtype, gate, order, 1);
+    if (s != GDN_OK) return s;
+    if (B * H == 0) return GDN_OK;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_E_ARG;
+    Problem p = make_problem(B, T, H, dk, dv, 16, dtype, gate, order, scale);
+    p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+    p.s0 = state0; p.out = out; p.s_out = state_out;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T == 0) return finish(copy_state(p, st));
+    return finish(recurrent_forward(p, st));
+}
+
+int gdn_profile_enable(int on) {
+    if (!on) {
+        prof_drain();
+        g_prof_names.clear();
+        g_prof_ms.clear();
+        g_prof_cnt.clear();
+    }
+    g_prof_on = on != 0;
+    return GDN_OK;
+}
+
+int gdn_profile_read(int index, char* name, size_t name_len, double* total_ms, int64_t* count) {
+    prof_drain();
+    if (index < 0 || index >= (int)g_prof_names.size()) return GDN_E_ARG;
+    if (name && name_len > 0) {
+        strncpy(name, g_prof_names[index].c_str(), name_len - 1);
+        name[name_len - 1] = '\0';
+    }
+    if (total_ms) *total_ms = g_prof_ms[index];
+    if (count) *count = g_prof_cnt[index];
+    return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Internal declarations shared by the HIP translation units of libgdn.
+// Nothing here is part of the C ABI (include/gdn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace gdn {
+
+// One forward problem, as the entry points received it (already validated).
+struct Problem {
+    int64_t B, T, H, dk, dv;
+    int C;        // chunk length
+    int NC;       // chunks per sequence = ceil(T / C)
+    int dtype;    // GDN_F32 / GDN_BF16
+    int gate;     // GDN_GATE_SCALAR / GDN_GATE_CHANNEL
+    int order;    // GDN_PREDICT_THEN_DECAY / GDN_DECAY_THEN_PREDICT
+    float scale;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* s0;
+    float* out;
+    float* s_out;
+};
+
+// Sequence-parallel split of the NC chunks of every sequence.
+struct Split {
+    int G;     // segments actually used (non-empty)
+    int per;   // chunks per segment (the last may hold fewer)
+};
+
+inline Split make_split(int NC, int n_segments) {
+    Split s;
+    if (NC <= 0 || n_segments <= 1) { s.G = 1; s.per = NC > 0 ? NC : 1; return s; }
+    s.per = (NC + n_segments - 1) / n_segments;
+    s.G = (NC + s.per - 1) / s.per;
+    return s;
+}
+
+// Byte offsets of the pieces of a workspace (all 256-byte aligned).
+struct WsLayout {
+    size_t prep = 0, prep_bytes = 0;     // per-chunk stage-1 results
+    size_t corr = 0, corr_bytes = 0;     // seq-par: per-chunk output corrections R
+    size_t sdend = 0, sdend_bytes = 0;   // seq-par: per-segment end states (S^D)
+    size_t mend = 0, mend_bytes = 0;     // seq-par: per-segment end scaling matrices
+    size_t sstart = 0, sstart_bytes = 0; // seq-par: per-segment true start states
+    size_t total = 0;
+};
+
+// Kernel-family workspace layouts and launchers (each returns a hipError_t).
+WsLayout valu_layout(const Problem& p, const Split& sp);
+hipError_t valu_forward(const Problem& p, const Split& sp, char* ws, hipStream_t st);
+
+WsLayout mfma_layout(const Problem& p, const Split& sp);
+bool mfma_supported(int64_t dk, int64_t dv, int C, int dtype, int gate);
+hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t st);
+
+hipError_t recurrent_forward(const Problem& p, hipStream_t st);
+
+// Sequence-parallel tail shared by both families: chain of start states and
+// output correction (R_i S_start^T), then the final state.
+hipError_t seqpar_finish(const Problem& p, const Split& sp, char* ws,
+                         const WsLayout& L, hipStream_t st);
+
+// Start state copy/zero for empty sequences (T == 0).
+hipError_t copy_state(const Problem& p, hipStream_t st);
+
+// Profiling hooks (gdn_profile_enable): bracket a launch with events.
+void prof_begin(const char* name, hipStream_t st);
+void prof_end(hipStream_t st);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace gdn
+
+// Device helpers -----------------------------------------------------------
+
+__device__ __forceinline__ float gdn_bf16_to_f32(uint16_t x) {
+    return __uint_as_float(uint32_t(x) << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float gdn_ld(const void* p, int64_t i);
+
+template <>
+__device__ __forceinline__ float gdn_ld<0>(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+}
+template <>
+__device__ __forceinline__ float gdn_ld<1>(const void* p, int64_t i) {
+    return gdn_bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}

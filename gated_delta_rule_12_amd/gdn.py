@@ -1,0 +1,235 @@
+"""Thin Python binding of libgdn.so (include/gdn.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of libgdn.so.  PyTorch supplies device memory and the stream.  There
+is no fallback: if the library is missing or no GPU is present, calls raise.
+
+Low-level names mirror the C ABI (gdn_chunk_fwd, gdn_recurrent_ref,
+gdn_seqpar_fwd, ...); chunk_fwd / seqpar_fwd / recurrent_ref are the same
+calls taking torch tensors and allocating the outputs and the workspace.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_GATE_SCALAR, GDN_GATE_CHANNEL = 0, 1
+GDN_PREDICT_THEN_DECAY, GDN_DECAY_THEN_PREDICT = 0, 1
+GDN_OK, GDN_E_ARG, GDN_E_SHAPE, GDN_E_UNSUPPORTED, GDN_E_WORKSPACE, GDN_E_HIP = 0, -1, -2, -3, -4, -5
+GDN_PATH_VALU, GDN_PATH_MFMA = 0, 1
+
+# every symbol include/gdn.h declares
+EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_workspace_bytes",
+           "gdn_validate", "gdn_chunk_path", "gdn_status_str", "gdn_abi_version",
+           "gdn_profile_enable", "gdn_profile_read")
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, f32, vp, sz = (ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                             ctypes.c_void_p, ctypes.c_size_t)
+    shape = [i64, i64, i64, i64, i64]
+    tens = [vp] * 8
+    L.gdn_chunk_fwd.argtypes = shape + [i32, i32, i32, i32, f32] + tens + [vp, sz, vp]
+    L.gdn_chunk_fwd.restype = ctypes.c_int
+    L.gdn_seqpar_fwd.argtypes = shape + [i32, i32, i32, i32, f32, i32] + tens + [vp, sz, vp]
+    L.gdn_seqpar_fwd.restype = ctypes.c_int
+    L.gdn_recurrent_ref.argtypes = shape + [i32, i32, i32, f32] + tens + [vp]
+    L.gdn_recurrent_ref.restype = ctypes.c_int
+    L.gdn_workspace_bytes.argtypes = shape + [i32, i32, i32, i32]
+    L.gdn_workspace_bytes.restype = sz
+    L.gdn_validate.argtypes = shape + [i32, i32, i32, i32, i32]
+    L.gdn_validate.restype = ctypes.c_int
+    L.gdn_chunk_path.argtypes = [i64, i64, i32, i32, i32]
+    L.gdn_chunk_path.restype = ctypes.c_int
+    L.gdn_status_str.argtypes = [ctypes.c_int]
+    L.gdn_status_str.restype = ctypes.c_char_p
+    L.gdn_abi_version.argtypes = []
+    L.gdn_abi_version.restype = ctypes.c_int
+    L.gdn_profile_enable.argtypes = [ctypes.c_int]
+    L.gdn_profile_enable.restype = ctypes.c_int
+    L.gdn_profile_read.argtypes = [ctypes.c_int, ctypes.c_char_p, sz,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    L.gdn_profile_read.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+# ---- raw C ABI ---------------------------------------------------------------
+
+def gdn_chunk_fwd(*args):
+    return lib().gdn_chunk_fwd(*args)
+
+
+def gdn_seqpar_fwd(*args):
+    return lib().gdn_seqpar_fwd(*args)
+
+
+def gdn_recurrent_ref(*args):
+    return lib().gdn_recurrent_ref(*args)
+
+
+def gdn_workspace_bytes(B, T, H, dk, dv, chunk, dtype, gate, n_segments=1) -> int:
+    return int(lib().gdn_workspace_bytes(B, T, H, dk, dv, chunk, dtype, gate, n_segments))
+
+
+def gdn_validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments=1) -> int:
+    return int(lib().gdn_validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments))
+
+
+def gdn_chunk_path(dk, dv, chunk, dtype, gate) -> int:
+    return int(lib().gdn_chunk_path(dk, dv, chunk, dtype, gate))
+
+
+def gdn_status_str(status: int) -> str:
+    return lib().gdn_status_str(int(status)).decode()
+
+
+status_str = gdn_status_str
+
+
+def gdn_abi_version() -> int:
+    return int(lib().gdn_abi_version())
+
+
+def gdn_profile_enable(on: bool) -> int:
+    return int(lib().gdn_profile_enable(1 if on else 0))
+
+
+def gdn_profile_read():
+    """All kernels recorded since profiling was enabled: {name: (ms, count)}."""
+    res = {}
+    i = 0
+    buf = ctypes.create_string_buffer(128)
+    while True:
+        ms, cnt = ctypes.c_double(), ctypes.c_int64()
+        if lib().gdn_profile_read(i, buf, 128, ctypes.byref(ms), ctypes.byref(cnt)) != GDN_OK:
+            break
+        res[buf.value.decode()] = (ms.value, cnt.value)
+        i += 1
+    return res
+
+
+# ---- torch-level helpers -------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(q, k, v, alpha, beta, state0):
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    tensors = [q, k, v, alpha, beta] + ([state0] if state0 is not None else [])
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    for t in tensors[3:]:
+        if t.dtype != torch.float32:
+            raise TypeError("alpha, beta, state0 must be float32")
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if alpha.shape == (B, T, H):
+        gate = GDN_GATE_SCALAR
+    elif alpha.shape == (B, T, H, dk):
+        gate = GDN_GATE_CHANNEL
+    else:
+        raise ValueError("alpha must be [B,T,H] or [B,T,H,dk]")
+    if beta.shape != (B, T, H):
+        raise ValueError("beta must be [B,T,H]")
+    if state0 is not None and state0.shape != (B, H, dv, dk):
+        raise ValueError("state0 must be [B,H,dv,dk]")
+    return B, T, H, dk, dv, gate
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_for(q, v, alpha, chunk=64, n_segments=1):
+    import torch
+    B, T, H, dk = q.shape
+    gate = GDN_GATE_SCALAR if alpha.dim() == 3 else GDN_GATE_CHANNEL
+    n = gdn_workspace_bytes(B, T, H, dk, v.shape[3], chunk, _dtype_code(q), gate, n_segments)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def chunk_fwd(q, k, v, alpha, beta, state0=None, *, chunk=64,
+              order=GDN_PREDICT_THEN_DECAY, scale=1.0, n_segments=1,
+              out=None, state_out=None, workspace=None):
+    """Chunkwise forward (n_segments > 1: the sequence-parallel entry point).
+    Returns (out [B,T,H,dv] fp32, final state [B,H,dv,dk] fp32)."""
+    import torch
+    B, T, H, dk, dv, gate = _check(q, k, v, alpha, beta, state0)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    if state_out is None:
+        state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(q, v, alpha, chunk, n_segments)
+    args = [B, T, H, dk, dv, chunk, _dtype_code(q), gate, order, scale]
+    tens = [_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state0),
+            _ptr(out), _ptr(state_out)]
+    tail = [_ptr(workspace), workspace.numel(), _stream()]
+    if n_segments == 1:
+        rc = gdn_chunk_fwd(*args, *tens, *tail)
+        where = "gdn_chunk_fwd"
+    else:
+        rc = gdn_seqpar_fwd(*args, n_segments, *tens, *tail)
+        where = "gdn_seqpar_fwd"
+    if rc != GDN_OK:
+        raise GdnError(rc, where)
+    return out, state_out
+
+
+def seqpar_fwd(q, k, v, alpha, beta, state0=None, *, n_segments=8, **kw):
+    return chunk_fwd(q, k, v, alpha, beta, state0, n_segments=n_segments, **kw)
+
+
+def recurrent_ref(q, k, v, alpha, beta, state0=None, *, order=GDN_PREDICT_THEN_DECAY,
+                  scale=1.0, out=None, state_out=None):
+    import torch
+    B, T, H, dk, dv, gate = _check(q, k, v, alpha, beta, state0)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    if state_out is None:
+        state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    rc = gdn_recurrent_ref(B, T, H, dk, dv, _dtype_code(q), gate, order, scale,
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state0),
+                           _ptr(out), _ptr(state_out), _stream())
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_recurrent_ref")
+    return out, state_out

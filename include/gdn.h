@@ -1,0 +1,168 @@
+/*
+ * gdn.h — C ABI of the MI355X (gfx950) chunkwise gated delta rule forward.
+ *
+ * The method (state S is dv x dk, a read is o = S q):
+ *
+ *   predict-then-decay (GDN_PREDICT_THEN_DECAY, the default)
+ *       S_t = S_{t-1} D_t + beta_t (v_t - S_{t-1} k_t) k_t^T,   o_t = scale * S_t q_t
+ *     — the recurrence of the Gated DeltaNet GPU-parallelisation blog
+ *       (m.lqnn.cn), section 1.2, here in the dv x dk orientation of the
+ *       DeltaNet illustrated notes (stay-hungry-time.github.io/deltanet);
+ *   decay-then-predict (GDN_DECAY_THEN_PREDICT)
+ *       Sbar = S_{t-1} D_t,  S_t = Sbar + beta_t (v_t - Sbar k_t) k_t^T
+ *     — the GDN / KDA worked examples of the illustrated notes'
+ *       architectures section;
+ *   D_t = alpha_t I for a scalar gate (GDN_GATE_SCALAR) or Diag(alpha_t),
+ *   scaling the key-channel columns of S, for a vector gate
+ *   (GDN_GATE_CHANNEL; GLA gating section and KDA paragraph of the notes).
+ *
+ * Layouts (row-major, contiguous, all device memory owned by the caller):
+ *   q, k       [B, T, H, dk]   bf16 or fp32 (dtype)
+ *   v          [B, T, H, dv]   same dtype as q, k
+ *   alpha      [B, T, H] fp32 (scalar gate) or [B, T, H, dk] fp32 (channel)
+ *   beta       [B, T, H] fp32
+ *   state0     [B, H, dv, dk] fp32, or NULL for a zero start state
+ *   out        [B, T, H, dv] fp32
+ *   state_out  [B, H, dv, dk] fp32, or NULL if not wanted
+ *   workspace  device scratch of at least gdn_workspace_bytes(...) bytes
+ *
+ * Ownership and lifetime: the library allocates no memory and keeps no state
+ * between calls (except the optional profiling record below).  Buffers are
+ * borrowed only for the work the call enqueues on `stream` (a hipStream_t;
+ * NULL is the null stream).  Calls return after enqueueing; the caller
+ * synchronises.  state_out may equal state0 (in-place continuation); out and
+ * the workspace must not alias any input.  Two calls that share a workspace
+ * must be ordered on one stream.
+ *
+ * Errors: every argument check runs on the host before anything is enqueued;
+ * a failing check returns a negative status and enqueues nothing.  A HIP
+ * launch error returns GDN_E_HIP.  NaN/Inf inputs are not checked; they
+ * propagate.  gdn_status_str() names each status.
+ *
+ * Supported shapes: any B, H, T >= 0 (the last chunk may be short; the
+ * kernels pad it with tokens that neither decay nor write, which is exact);
+ * dk, dv in {16, 32, 48, ..., 128} (multiples of 16 up to 128); chunk in
+ * {16, 32, 64}.  bf16 inputs with dk = dv in {64, 128}, chunk 64 run the MFMA
+ * kernels; every other supported case runs the fp32 vector-ALU kernels.
+ * Anything else returns GDN_E_UNSUPPORTED.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
+enum gdn_gate { GDN_GATE_SCALAR = 0, GDN_GATE_CHANNEL = 1 };
+enum gdn_order { GDN_PREDICT_THEN_DECAY = 0, GDN_DECAY_THEN_PREDICT = 1 };
+enum gdn_status {
+    GDN_OK = 0,
+    GDN_E_ARG = -1,          /* NULL pointer where one is required, bad enum */
+    GDN_E_SHAPE = -2,        /* negative or inconsistent size */
+    GDN_E_UNSUPPORTED = -3,  /* valid but not built (dk, dv, chunk) */
+    GDN_E_WORKSPACE = -4,    /* workspace NULL or smaller than required */
+    GDN_E_HIP = -5           /* a HIP call failed */
+};
+enum gdn_path { GDN_PATH_VALU = 0, GDN_PATH_MFMA = 1 };
+
+/*
+ * gdn_chunk_fwd — chunkwise-parallel forward.
+ *
+ * Three chunk stages (DeltaNet illustrated notes, WY/UT section; gates as in
+ * the GLA gating section): per chunk the UT transform of the lower-triangular
+ * system built from beta and the gated K K^T (T' = (I + diag(beta) L)^{-1}
+ * diag(beta)); the inter-chunk state recurrence
+ * S_[i+1] = S_[i] Diag(b_C) + Delta^T Kbar with Delta = T'(V - (K (.) B') S_[i]^T)
+ * (which is S_[i](I - W^T K) + U^T K when every gate is 1); and the fused
+ * output O = (Q (.) B) S_[i]^T + P Delta.  Returns out and state_out.
+ * The workspace holds per-chunk T' and gate prefixes.
+ */
+int gdn_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                  int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
+                  float scale,
+                  const void* q, const void* k, const void* v,
+                  const float* alpha, const float* beta, const float* state0,
+                  float* out, float* state_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_recurrent_ref — the token-by-token recurrence on the GPU (fp32 state
+ * held in registers, one lane per state row), the "fused recurrent" form the
+ * illustrated notes compare the chunkwise algorithm against.  Same tensors
+ * and layouts as gdn_chunk_fwd; needs no workspace.
+ */
+int gdn_recurrent_ref(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                      int32_t dtype, int32_t gate, int32_t order, float scale,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const float* state0,
+                      float* out, float* state_out, void* stream);
+
+/*
+ * gdn_seqpar_fwd — increment-and-correct sequence parallelism (How to
+ * Implement Sequence Parallelism in DeltaNet, papercache notes, sections
+ * "parallel algorithm derivation" and "CP=4").  The chunks of every sequence
+ * are split into n_segments contiguous runs computed concurrently: run 0 from
+ * the true start state; every later run g the increment state S^D from zero
+ * and the scaling matrix M from I (M_[i+1] = M_[i] (Diag(b_C) - W^T Kbar),
+ * which is M_[i](I - W^T K) with unit gates).  Start states are chained
+ * S_start(g+1) = S^D_end(g) + S_start(g) M_end(g), and the correction
+ * S_[i] = S^D_[i] + S_start M_[i] is applied to the outputs, which are
+ * linear in the entry state.  n_segments = 1 is gdn_chunk_fwd.  Segments
+ * hold ceil(NC / n_segments) chunks (NC = ceil(T / chunk)); the last may be
+ * shorter.  Same tensors as gdn_chunk_fwd; a larger workspace.
+ */
+int gdn_seqpar_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                   int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
+                   float scale, int32_t n_segments,
+                   const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* state0,
+                   float* out, float* state_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by gdn_chunk_fwd (n_segments = 1) or
+ * gdn_seqpar_fwd; 0 when the arguments do not validate.  Host only. */
+size_t gdn_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk,
+                           int64_t dv, int32_t chunk, int32_t dtype,
+                           int32_t gate, int32_t n_segments);
+
+/* Host-only argument check; GDN_OK or the status the entry points would
+ * return before enqueueing anything. */
+int gdn_validate(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                 int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
+                 int32_t n_segments);
+
+/* Which kernel family the chunked entry points run for these arguments
+ * (GDN_PATH_VALU or GDN_PATH_MFMA), or a negative status.  Host only. */
+int gdn_chunk_path(int64_t dk, int64_t dv, int32_t chunk, int32_t dtype,
+                   int32_t gate);
+
+/* Static string naming a status code. */
+const char* gdn_status_str(int status);
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+/*
+ * Optional per-kernel timing.  gdn_profile_enable(1) makes the entry points
+ * bracket every kernel they launch with HIP events recorded on the call's
+ * stream (no work is skipped or reordered); gdn_profile_enable(0) stops and
+ * discards the record.  gdn_profile_read(i, name, name_len, &ms, &count)
+ * synchronises the recorded events and returns, for the i-th distinct kernel
+ * seen (0-based), its name, total milliseconds and launch count; it returns
+ * GDN_E_ARG past the last kernel.  Process-global; not thread-safe.
+ */
+int gdn_profile_enable(int on);
+int gdn_profile_read(int index, char* name, size_t name_len, double* total_ms,
+                     int64_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls).
+
+The library loads without a GPU; validation, workspace sizing, path
+selection and status strings are host-only, and argument errors return
+before any HIP call is made.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_delta_rule_12_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = header_functions()
+    assert len(declared) >= 10
+    assert set(declared) == set(gdn.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", out))
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    L = gdn.lib()
+    for f in declared:
+        assert hasattr(L, f)
+
+
+def test_abi_version_and_status_strings():
+    assert gdn.gdn_abi_version() == 1
+    for s in (gdn.GDN_OK, gdn.GDN_E_ARG, gdn.GDN_E_SHAPE, gdn.GDN_E_UNSUPPORTED,
+              gdn.GDN_E_WORKSPACE, gdn.GDN_E_HIP):
+        assert gdn.gdn_status_str(s).startswith("GDN_")
+    assert "unknown" in gdn.gdn_status_str(42)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((1, 256, 1, 16, 16, 16, 0, 0, 0, 1), gdn.GDN_OK),
+    ((2, 8192, 16, 128, 128, 64, 1, 0, 0, 1), gdn.GDN_OK),
+    ((1, 65536, 4, 128, 128, 64, 1, 0, 1, 8), gdn.GDN_OK),
+    ((8, 4096, 16, 128, 128, 64, 1, 1, 0, 1), gdn.GDN_OK),
+    ((1, 0, 1, 64, 64, 64, 1, 0, 0, 1), gdn.GDN_OK),          # empty sequence
+    ((0, 100, 3, 64, 64, 64, 1, 0, 0, 1), gdn.GDN_OK),        # empty batch
+    ((1, 100, 1, 64, 64, 64, 2, 0, 0, 1), gdn.GDN_E_ARG),     # dtype
+    ((1, 100, 1, 64, 64, 64, 1, 2, 0, 1), gdn.GDN_E_ARG),     # gate
+    ((1, 100, 1, 64, 64, 64, 1, 0, 5, 1), gdn.GDN_E_ARG),     # order
+    ((-1, 100, 1, 64, 64, 64, 1, 0, 0, 1), gdn.GDN_E_SHAPE),
+    ((1, -5, 1, 64, 64, 64, 1, 0, 0, 1), gdn.GDN_E_SHAPE),
+    ((1, 100, 1, 64, 64, 64, 1, 0, 0, 0), gdn.GDN_E_SHAPE),   # n_segments
+    ((1, 100, 1, 60, 64, 64, 1, 0, 0, 1), gdn.GDN_E_UNSUPPORTED),
+    ((1, 100, 1, 64, 256, 64, 1, 0, 0, 1), gdn.GDN_E_UNSUPPORTED),
+    ((1, 100, 1, 64, 64, 128, 1, 0, 0, 1), gdn.GDN_E_UNSUPPORTED),
+])
+def test_validate(args, want):
+    assert gdn.gdn_validate(*args) == want
+
+
+def test_workspace_sizes():
+    # zero for empty work or bad arguments
+    assert gdn.gdn_workspace_bytes(1, 0, 1, 64, 64, 64, 1, 0, 1) == 0
+    assert gdn.gdn_workspace_bytes(1, 100, 1, 60, 64, 64, 1, 0, 1) == 0
+    a = gdn.gdn_workspace_bytes(2, 8192, 16, 128, 128, 64, 1, 0, 1)
+    b = gdn.gdn_workspace_bytes(2, 8192, 16, 128, 128, 64, 1, 0, 8)
+    assert a > 0 and b > a and a % 256 == 0 and b % 256 == 0
+    # grows with the number of chunks; a ragged tail rounds up to a chunk
+    assert gdn.gdn_workspace_bytes(1, 129, 1, 64, 64, 64, 1, 0, 1) == \
+        gdn.gdn_workspace_bytes(1, 192, 1, 64, 64, 64, 1, 0, 1)
+    assert gdn.gdn_workspace_bytes(1, 1024, 1, 64, 64, 64, 1, 0, 1) > \
+        gdn.gdn_workspace_bytes(1, 512, 1, 64, 64, 64, 1, 0, 1)
+
+
+def test_chunk_path_selection():
+    for d in (16, 32, 64, 128):
+        assert gdn.gdn_chunk_path(d, d, 16, gdn.GDN_F32, 0) == gdn.GDN_PATH_VALU
+    assert gdn.gdn_chunk_path(60, 64, 64, gdn.GDN_BF16, 0) == gdn.GDN_E_UNSUPPORTED
+    assert gdn.gdn_chunk_path(128, 128, 64, gdn.GDN_BF16, 0) in (gdn.GDN_PATH_VALU,
+                                                                 gdn.GDN_PATH_MFMA)
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch():
+    """Argument checks return a status and touch no device; here they run on
+    a host with no GPU."""
+    import ctypes
+    nul = ctypes.c_void_p(0)
+    ten = [nul] * 8
+    # bad dtype
+    rc = gdn.gdn_chunk_fwd(1, 64, 1, 64, 64, 64, 7, 0, 0, 1.0, *ten, nul, 0, nul)
+    assert rc == gdn.GDN_E_ARG
+    # unsupported shape
+    rc = gdn.gdn_seqpar_fwd(1, 64, 1, 60, 64, 64, 1, 0, 0, 1.0, 2, *ten, nul, 0, nul)
+    assert rc == gdn.GDN_E_UNSUPPORTED
+    # missing input pointers
+    rc = gdn.gdn_chunk_fwd(1, 64, 1, 64, 64, 64, 1, 0, 0, 1.0, *ten, nul, 0, nul)
+    assert rc == gdn.GDN_E_ARG
+    rc = gdn.gdn_recurrent_ref(1, 64, 1, 64, 64, 1, 0, 0, 1.0, *ten, nul)
+    assert rc == gdn.GDN_E_ARG
+    # workspace too small (non-null fake pointers never dereferenced on this path)
+    fake = ctypes.c_void_p(0x1000)
+    rc = gdn.gdn_chunk_fwd(1, 64, 1, 64, 64, 64, 1, 0, 0, 1.0, *([fake] * 8), fake, 16, nul)
+    assert rc == gdn.GDN_E_WORKSPACE
+    # empty batch: nothing to do
+    rc = gdn.gdn_chunk_fwd(0, 64, 1, 64, 64, 64, 1, 0, 0, 1.0, *ten, nul, 0, nul)
+    assert rc == gdn.GDN_OK
+
+
+def test_binding_has_no_fallback(tmp_path, monkeypatch):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        gdn.lib()

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Small cases are compared element by element over every (batch, head) slice;
+they span several chunks and a ragged tail.  Full-size workloads run in the
+launch configuration bench.py times and are compared on sampled (batch,
+head) slices that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+from gated_delta_rule_12_amd import gdn
+from gated_delta_rule_12_amd.workloads import WORKLOADS, Workload, make_inputs, to_device
+from parity import TOL, oracle_on, out_err, state_err
+
+pytestmark = pytest.mark.gpu
+
+PTD, DTP = gdn.GDN_PREDICT_THEN_DECAY, gdn.GDN_DECAY_THEN_PREDICT
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.lib()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def run(w, inp, entry="chunk", order=PTD, n_segments=None):
+    d = to_device(inp, w)
+    if entry == "recurrent":
+        o, s = gdn.recurrent_ref(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
+                                 order=order)
+    else:
+        G = w.n_segments if n_segments is None else n_segments
+        o, s = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
+                             chunk=w.chunk, order=order, n_segments=G)
+    import torch
+    torch.cuda.synchronize()
+    return _np(o), _np(s)
+
+
+def check(w, inp, o, s, order=PTD, bh=None, tol=None):
+    o_ref, s_ref = oracle_on(inp, w.gate, order, bh)
+    if bh is not None:
+        o = np.stack([o[b, :, h:h + 1] for b, h in bh])
+        s = np.stack([s[b, h] for b, h in bh])[:, None]
+    to, ts = tol or TOL[w.dtype]
+    eo, es = out_err(o, o_ref), state_err(s, s_ref)
+    print(f"  {w.name}: out err {eo:.3e} (tol {to}), state err {es:.3e} (tol {ts})", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert eo <= to, eo
+    assert es <= ts, es
+    return eo, es
+
+
+# --------------------------------------------------------------------------
+# the tiny fp32 workload, all entry points
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("entry", ["chunk", "recurrent", "seqpar"])
+@pytest.mark.parametrize("order", [PTD, DTP])
+def test_tiny_f32_workload(entry, order):
+    w = WORKLOADS[0]
+    inp = make_inputs(w)
+    o, s = run(w, inp, entry if entry != "seqpar" else "chunk", order,
+               n_segments=4 if entry == "seqpar" else None)
+    check(w, inp, o, s, order)
+
+
+# --------------------------------------------------------------------------
+# random shapes: several chunks, ragged tail, nonzero start state
+# --------------------------------------------------------------------------
+
+CASES = [
+    # dtype, dk, dv, chunk, T, gate, order
+    ("f32", 16, 16, 16, 200, "scalar", PTD),
+    ("f32", 32, 48, 32, 133, "channel", DTP),
+    ("f32", 64, 64, 64, 300, "scalar", DTP),
+    ("f32", 128, 128, 64, 190, "channel", PTD),
+    ("bf16", 16, 32, 16, 77, "channel", PTD),
+    ("bf16", 64, 64, 64, 257, "scalar", PTD),
+    ("bf16", 64, 64, 64, 320, "channel", DTP),
+    ("bf16", 128, 128, 64, 449, "scalar", DTP),
+    ("bf16", 128, 128, 64, 384, "scalar", PTD),
+    ("bf16", 128, 128, 64, 129, "channel", PTD),
+    ("bf16", 96, 112, 32, 100, "scalar", PTD),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("entry", ["chunk", "recurrent"])
+def test_random_shapes(case, entry):
+    dtype, dk, dv, C, T, gate, order = case
+    w = Workload("rand", B=2, H=3, T=T, dk=dk, dv=dv, chunk=C, dtype=dtype, gate=gate,
+                 state0_std=0.5, seed=100 + dk + T)
+    inp = make_inputs(w)
+    o, s = run(w, inp, entry, order)
+    check(w, inp, o, s, order)
+
+
+@pytest.mark.parametrize("alpha_mean", [6.0, -1.0])
+def test_gate_extremes(alpha_mean):
+    """Long memory (alpha ~ 0.998) and fast forgetting (alpha ~ 0.27)."""
+    w = Workload("gates", B=1, H=2, T=512, dk=128, dv=128, chunk=64, state0_std=0.5,
+                 alpha_mean=alpha_mean, seed=7)
+    inp = make_inputs(w)
+    o, s = run(w, inp)
+    check(w, inp, o, s)
+
+
+# --------------------------------------------------------------------------
+# sequence parallel split
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 40])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_seqpar_segments(G, gate):
+    w = Workload("seqpar", B=1, H=2, T=1000, dk=64, dv=64, chunk=64, gate=gate,
+                 state0_std=0.5, seed=11 + G)
+    inp = make_inputs(w)
+    o, s = run(w, inp, n_segments=G)
+    check(w, inp, o, s)
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [0, 1, 5, 63, 64, 65])
+@pytest.mark.parametrize("entry", ["chunk", "recurrent", "seqpar"])
+def test_short_sequences(T, entry):
+    w = Workload("short", B=2, H=2, T=T, dk=128, dv=128, chunk=64, state0_std=0.5, seed=3)
+    inp = make_inputs(w)
+    o, s = run(w, inp, "recurrent" if entry == "recurrent" else "chunk",
+               n_segments=3 if entry == "seqpar" else 1)
+    if T == 0:
+        np.testing.assert_array_equal(s, inp["state0"])
+        assert o.shape == (2, 0, 2, 128)
+    else:
+        check(w, inp, o, s)
+
+
+def test_empty_batch():
+    import torch
+    z = torch.zeros((0, 16, 2, 64), dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros((0, 16, 2), dtype=torch.float32, device="cuda")
+    o, s = gdn.chunk_fwd(z, z, z, a, a)
+    assert o.shape == (0, 16, 2, 64) and s.shape == (0, 2, 64, 64)
+
+
+def test_zero_start_state_equals_null():
+    import torch
+    w = Workload("z", B=1, H=2, T=256, dk=128, dv=128, chunk=64, seed=5)
+    d = to_device(make_inputs(w), w)
+    o1, s1 = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], None)
+    zero = torch.zeros((1, 2, 128, 128), dtype=torch.float32, device="cuda")
+    o2, s2 = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], zero)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_streaming_equals_one_call():
+    """Two calls with the state threaded through equal one call (resume)."""
+    import torch
+    w = Workload("stream", B=2, H=2, T=512, dk=128, dv=128, chunk=64, state0_std=0.3, seed=9)
+    inp = make_inputs(w)
+    d = to_device(inp, w)
+    o, s = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    cut = 192
+    part = lambda x, a, b: x[:, a:b].contiguous()
+    o1, s1 = gdn.chunk_fwd(*(part(d[n], 0, cut) for n in ("q", "k", "v", "alpha", "beta")),
+                           d["state0"])
+    o2, s2 = gdn.chunk_fwd(*(part(d[n], cut, 512) for n in ("q", "k", "v", "alpha", "beta")),
+                           s1)
+    torch.cuda.synchronize()
+    oo = torch.cat([o1, o2], dim=1)
+    assert (oo - o).abs().max().item() <= 1e-5 * o.abs().max().item()
+    assert (s2 - s).abs().max().item() <= 1e-5 * s.abs().max().item()
+
+
+def test_in_place_state():
+    import torch
+    w = Workload("inplace", B=1, H=2, T=300, dk=64, dv=64, chunk=64, state0_std=0.3, seed=13)
+    inp = make_inputs(w)
+    d = to_device(inp, w)
+    st = d["state0"].clone()
+    o, s = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], st, state_out=st)
+    torch.cuda.synchronize()
+    check(w, inp, _np(o), _np(st))
+
+
+def test_deterministic():
+    import torch
+    w = Workload("det", B=2, H=4, T=1024, dk=128, dv=128, chunk=64, state0_std=0.3, seed=17)
+    d = to_device(make_inputs(w), w)
+    r1 = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    r2 = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    r3 = gdn.seqpar_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], n_segments=4)
+    r4 = gdn.seqpar_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], n_segments=4)
+    torch.cuda.synchronize()
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+    assert torch.equal(r3[0], r4[0]) and torch.equal(r3[1], r4[1])
+
+
+def test_workspace_too_small_is_an_error():
+    import torch
+    w = Workload("ws", B=1, H=1, T=128, dk=64, dv=64, chunk=64, seed=1)
+    d = to_device(make_inputs(w), w)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], workspace=ws)
+    assert ei.value.status == gdn.GDN_E_WORKSPACE
+
+
+# --------------------------------------------------------------------------
+# full-size workloads (bench launch configuration), sampled slices
+# --------------------------------------------------------------------------
+
+SAMPLES = {1: [(0, 0), (3, 7)], 2: [(0, 0), (1, 15), (0, 9)], 3: [(0, 0), (0, 3)],
+           4: [(0, 0), (7, 15)]}
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_full_workload_sampled(idx):
+    w = WORKLOADS[idx]
+    inp = make_inputs(w)
+    o, s = run(w, inp)
+    check(w, inp, o, s, bh=SAMPLES[idx])
+
+
+def test_long_workload_single_stream_sampled():
+    """The long workload through the single-stream entry point as well."""
+    w = WORKLOADS[3]
+    inp = make_inputs(w)
+    o, s = run(w, inp, n_segments=1)
+    check(w, inp, o, s, bh=[(0, 1)])
