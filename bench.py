@@ -70,12 +70,14 @@ def cpu_baseline(w, inp, max_threads=16, target_s=10.0):
         oracle.forward(q, k, v, a, be, s0, gate=g, threads=min(cores, n_pairs))
         return time.perf_counter() - t
 
-    # probe with one slice of 1024 tokens, then size the sample
+    # probe with one slice of up to 1024 tokens, then size the sample: every
+    # (batch, head) slice in full if that fits the time target, else a prefix
     n_tok = min(w.T, 1024)
     t1 = run(1, n_tok)
-    n_pairs = min(len(pairs), cores)
-    per_pair_full = t1 * w.T / n_tok
-    n_tok = w.T if per_pair_full <= target_s else max(256, int(w.T * target_s / per_pair_full))
+    n_pairs = len(pairs)
+    waves = -(-n_pairs // cores)
+    est = t1 * (w.T / n_tok) * waves
+    n_tok = w.T if est <= target_s else max(256, int(w.T * target_s / est))
     dt = run(n_pairs, n_tok)
     head_tokens = n_pairs * n_tok
     tok_per_s = head_tokens / dt / w.H   # tokens of the workload (all H heads) per second
