@@ -1,13 +1,591 @@
-// MFMA kernels (bf16, gfx950) — not built yet: every case runs the VALU family.
+// MFMA kernels of the chunkwise gated delta rule (gfx950, bf16 inputs,
+// dk = dv = D in {64, 128}, chunk C = 64, scalar gate).
+//
+// Chunk algebra as in the vector-ALU family (gdn_valu.hip): per chunk with
+// chunk-local log-gate prefix g_t (gamma_t = exp g_t), prediction prefix g'_t
+// (g_{t-1} predict-then-decay, g_t decay-then-predict), entry state S (dv x dk):
+//   T'    = (I + diag(beta) L)^{-1} diag(beta),  L_tj = exp(g'_t - g_j) k_t.k_j (j < t)
+//   Delta = T' (V - diag(gamma') K S^T)
+//   O     = scale (diag(gamma) Q S^T + P Delta),  P_tj = exp(g_t - g_j) q_t.k_j (j <= t)
+//   S'    = gamma_C S + (diag(gamma_C / gamma) Delta)^T K
+// (DeltaNet illustrated notes, WY/UT section: UT transform, chunk state
+// passing, output; GLA gating section: gate prefixes; the scalar gate of the
+// Gated DeltaNet paragraph of the architectures section).
+//
+// Precision: q, k, v are exact bf16 MFMA operands.  Every operand derived in
+// fp32 (S, T', X, Delta, P) is split into bf16 hi + lo and multiplied as
+// hi*raw + lo*raw (one raw operand) or hi*hi + hi*lo + lo*hi (two derived
+// operands); accumulation is fp32.  Gate factors are applied on the fp32
+// side, as ratios exp(g_t - g_j) <= 1.
+//
+// k_prep_mfma: one workgroup (4 waves) per (batch, head, chunk): gate prefix,
+//   Gram K K^T on MFMA, the gated UT system, its inverse by blocked forward
+//   substitution in fp32 (16 x 16 diagonal blocks, then off-diagonal blocks
+//   by block distance), T' written as bf16 hi/lo MFMA A-operand fragments.
+// k_rec_mfma: one workgroup per (batch, head, segment, 16-row slice of the
+//   state); the slice of S^T lives in registers (fp32) across the chunk loop.
+//   Wave w owns token rows 16w..16w+15 of every chunk product and key rows
+//   (D/4 of them) of the state.  Results in MFMA accumulator layout are fed
+//   to the next product without transposition: a k-step of 32 pairs two
+//   16-row accumulator tiles, k-slot 8g+e <-> index 4g+e (e < 4) of the first
+//   tile and 4g+e-4 of the second, and the other operand is read in the same
+//   slot order.  Three barriers per chunk.
 #include "gdn_internal.h"
 #include "../../include/gdn.h"
 
 namespace gdn {
+namespace {
 
-bool mfma_supported(int64_t, int64_t, int, int, int) { return false; }
-WsLayout mfma_layout(const Problem&, const Split&) { return WsLayout{}; }
-hipError_t mfma_forward(const Problem&, const Split&, char*, hipStream_t) {
-    return hipErrorInvalidValue;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int C = 64;
+constexpr int kThreads = 256;
+constexpr int kTfragPerChunk = 4 * 2 * 2 * 64;  // [m][s][hi/lo][lane] of u16x8
+
+__device__ __forceinline__ f32x4 mfma(const u16x8& a, const u16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned short bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (unsigned short)(u >> 16);
+}
+
+__device__ __forceinline__ void split1(float x, unsigned short& hi, unsigned short& lo) {
+    hi = bf16_rne(x);
+    lo = bf16_rne(x - __uint_as_float((uint32_t)hi << 16));
+}
+
+__device__ __forceinline__ void split4(const f32x4& x, u16x4& hi, u16x4& lo) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        unsigned short a, b;
+        split1(x[r], a, b);
+        hi[r] = a;
+        lo[r] = b;
+    }
+}
+
+__device__ __forceinline__ u16x8 cat(const u16x4& a, const u16x4& b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// stage 1: T' per chunk-head
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag) {
+    constexpr int LDK = D + 8;
+    constexpr int PPR = D / 8;
+    __shared__ __attribute__((aligned(16))) unsigned short Ks[C * LDK];
+    __shared__ float Ms[C][C + 1];
+    __shared__ float Ts[C][C + 1];
+    __shared__ float Xs[3][16][17];
+    __shared__ float gsh[C], gpsh[C], bsh[C];
+
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int64_t H = p.H, T = p.T;
+    const int64_t t0 = (int64_t)i * C;
+    const int nt = (int)((T - t0) < C ? (T - t0) : C);
+    const int64_t ch = ((int64_t)b * H + h) * p.NC + i;
+    const unsigned short* kin = static_cast<const unsigned short*>(p.k);
+
+    for (int e = tid; e < C * PPR; e += kThreads) {
+        const int t = e / PPR, c8 = e - (e / PPR) * PPR;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (t < nt) val = *reinterpret_cast<const uint4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
+        *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = val;
+    }
+    if (w == 0) {
+        float la = 0.f, bt = 0.f;
+        if (l < nt) {
+            const int64_t row = ((int64_t)b * T + t0 + l) * H + h;
+            la = logf(p.alpha[row]);
+            bt = p.beta[row];
+        }
+        const float gv = wave_incl_scan(la, l);
+        float gprev = __shfl_up(gv, 1, 64);
+        if (l == 0) gprev = 0.f;
+        gsh[l] = gv;
+        gpsh[l] = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
+        bsh[l] = bt;
+    }
+    for (int e = tid; e < C * C; e += kThreads) {
+        const int t = e >> 6, j = e & 63;
+        if ((j >> 4) > (t >> 4)) Ts[t][j] = 0.f;
+    }
+    __syncthreads();
+
+    // A_tj = beta_t exp(g'_t - g_j) k_t.k_j for j < t: row block w, column blocks <= w
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        if (nb > w) continue;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            const u16x8 a = *reinterpret_cast<const u16x8*>(&Ks[(16 * w + c16) * LDK + 32 * s + 8 * g4]);
+            const u16x8 bb = *reinterpret_cast<const u16x8*>(&Ks[(16 * nb + c16) * LDK + 32 * s + 8 * g4]);
+            acc = mfma(a, bb, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * g4 + r, j = 16 * nb + c16;
+            Ms[t][j] = j < t ? bsh[t] * expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // diagonal 16 x 16 blocks: forward substitution, one column per lane
+    if (l < 16) {
+        const int j = c16;
+        float col[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float x = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < t; ++mm) x -= Ms[16 * w + t][16 * w + mm] * col[mm];
+            col[t] = t < j ? 0.f : (t == j ? 1.f : x);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Ts[16 * w + t][16 * w + j] = col[t];
+    }
+    __syncthreads();
+
+    // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+    for (int d = 1; d < 4; ++d) {
+        const int nblk = 4 - d;
+        for (int e = tid; e < nblk * 256; e += kThreads) {
+            const int q = e >> 8, r = (e >> 4) & 15, c = e & 15;
+            const int jb = q, ib = q + d;
+            float x = 0.f;
+            for (int kk = 16 * jb; kk < 16 * ib; ++kk) x += Ms[16 * ib + r][kk] * Ts[kk][16 * jb + c];
+            Xs[q][r][c] = x;
+        }
+        __syncthreads();
+        for (int e = tid; e < nblk * 256; e += kThreads) {
+            const int q = e >> 8, r = (e >> 4) & 15, c = e & 15;
+            const int jb = q, ib = q + d;
+            float x = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < 16; ++mm) x -= Ts[16 * ib + r][16 * ib + mm] * Xs[q][mm][c];
+            Ts[16 * ib + r][16 * jb + c] = x;
+        }
+        __syncthreads();
+    }
+
+    // T' = T diag(beta) as A-operand fragments: [m][s][hi/lo][lane] of 8 bf16;
+    // lane (row 16m + lane%16, group g), slot e -> column 32s + 4g + e (e < 4)
+    // or 32s + 16 + 4g + e - 4
+    u16x8* dst = tfrag + ch * kTfragPerChunk;
+    for (int f = tid; f < 4 * 2 * 64; f += kThreads) {
+        const int m = f >> 7, s = (f >> 6) & 1, lane = f & 63;
+        const int t = 16 * m + (lane & 15), gg = lane >> 4;
+        u16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
+            unsigned short a, bb;
+            split1(Ts[t][j] * bsh[j], a, bb);
+            hi[e] = a;
+            lo[e] = bb;
+        }
+        dst[((m * 2 + s) * 2 + 0) * 64 + lane] = hi;
+        dst[((m * 2 + s) * 2 + 1) * 64 + lane] = lo;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// stage 2: the chunk loop
+// ---------------------------------------------------------------------------
+template <int D>
+struct RecShared {
+    static constexpr int LDK = D + 8;
+    static constexpr int KS = D / 32;
+    unsigned short K[2][C * LDK];
+    unsigned short Q[2][C * LDK];
+    unsigned short V[2][C * 16];
+    u16x4 Sf[KS][2][2][64];  // S^T fragments: [k-step][tile half][hi/lo][lane]
+    u16x4 Xf[2][2][2][64];
+    u16x4 Df[2][2][2][64];
+    u16x4 DBf[2][2][2][64];
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLayout L,
+                                                       char* wsb, const u16x8* tfrag,
+                                                       int ntiles, int xcd_remap) {
+    constexpr int LDK = D + 8;
+    constexpr int KS = D / 32;   // k-steps over the key dimension
+    constexpr int TPW = D / 64;  // 16-row key tiles of S^T owned per wave
+    constexpr int PPR = D / 8;   // 16-byte pieces per K/Q row
+    constexpr int KQP = C * PPR / kThreads;
+    __shared__ __attribute__((aligned(16))) RecShared<D> sh;
+
+    // work decode; with xcd_remap the ntiles slices of one (head, segment)
+    // land on one XCD (workgroups are dealt to the 8 XCDs round-robin)
+    const int nwork = gridDim.x;
+    int id = blockIdx.x;
+    if (xcd_remap) {
+        const int xcd = id & 7, slot = id >> 3;
+        id = ((slot / ntiles) * 8 + xcd) * ntiles + slot % ntiles;
+    }
+    (void)nwork;
+    const int x = id % ntiles;
+    const int hg = id / ntiles;  // (b * H + h) * G + seg
+    const int gseg = hg % sp.G;
+    const int64_t bh = hg / sp.G;
+    const int64_t H = p.H, T = p.T;
+    const int b = (int)(bh / H), h = (int)(bh - (bh / H) * H);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int nvt = D / 16;
+    const bool scaling = x >= nvt;
+    if (scaling && gseg == 0) return;
+    const int r0 = (scaling ? x - nvt : x) * 16;
+    const int i_begin = gseg * sp.per;
+    const int i_end = min(p.NC, (gseg + 1) * sp.per);
+    float* corr = reinterpret_cast<float*>(wsb + L.corr);
+    const unsigned short* kin = static_cast<const unsigned short*>(p.k);
+    const unsigned short* qin = static_cast<const unsigned short*>(p.q);
+    const unsigned short* vin = static_cast<const unsigned short*>(p.v);
+
+    // state slice S^T[a][v], a-tile tau = w*TPW + u: lane (v = c16, a = 16 tau + 4 g4 + r)
+    f32x4 Sacc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int a = 16 * (w * TPW + u) + 4 * g4 + r, v = r0 + c16;
+            float s;
+            if (scaling) s = v == a ? 1.f : 0.f;
+            else if (gseg == 0 && p.s0) s = p.s0[(bh * D + v) * D + a];
+            else s = 0.f;
+            Sacc[u][r] = s;
+        }
+    }
+
+    uint4 kreg[KQP], qreg[KQP], vreg;
+    u16x8 tf_n[2][2], tf_c[2][2];
+    float al_n = 1.f, al_c = 1.f;
+
+    auto issue_loads = [&](int i) {
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+#pragma unroll
+        for (int k = 0; k < KQP; ++k) {
+            const int e = tid + kThreads * k;
+            const int t = e / PPR, c8 = e - (e / PPR) * PPR;
+            const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
+            kreg[k] = t < nt ? *reinterpret_cast<const uint4*>(kin + off) : make_uint4(0, 0, 0, 0);
+            qreg[k] = t < nt ? *reinterpret_cast<const uint4*>(qin + off) : make_uint4(0, 0, 0, 0);
+        }
+        vreg = make_uint4(0, 0, 0, 0);
+        if (!scaling && tid < 128) {
+            const int t = tid >> 1, hf = tid & 1;
+            if (t < nt) vreg = *reinterpret_cast<const uint4*>(vin + (((int64_t)b * T + t0 + t) * H + h) * D + r0 + 8 * hf);
+        }
+        al_n = l < nt ? p.alpha[((int64_t)b * T + t0 + l) * H + h] : 1.f;
+        const u16x8* tp = tfrag + (bh * p.NC + i) * kTfragPerChunk;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                if (s <= (w >> 1)) tf_n[s][hl] = tp[((w * 2 + s) * 2 + hl) * 64 + l];
+                else tf_n[s][hl] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_loads = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < KQP; ++k) {
+            const int e = tid + kThreads * k;
+            const int t = e / PPR, c8 = e - (e / PPR) * PPR;
+            *reinterpret_cast<uint4*>(&sh.K[buf][t * LDK + c8 * 8]) = kreg[k];
+            *reinterpret_cast<uint4*>(&sh.Q[buf][t * LDK + c8 * 8]) = qreg[k];
+        }
+        if (tid < 128) {
+            const int t = tid >> 1, hf = tid & 1;
+            *reinterpret_cast<uint4*>(&sh.V[buf][t * 16 + 8 * hf]) = vreg;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) tf_c[s][hl] = tf_n[s][hl];
+        al_c = al_n;
+    };
+
+    if (i_begin < i_end) {
+        issue_loads(i_begin);
+        store_loads(0);
+        if (i_begin + 1 < i_end) issue_loads(i_begin + 1);
+    }
+
+    for (int i = i_begin; i < i_end; ++i) {
+        const int cur = (i - i_begin) & 1;
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+
+        // chunk-local gate prefix; lane = token
+        const float gv = wave_incl_scan(logf(al_c), l);
+        const float gC = __shfl(gv, 63, 64);
+        float gprev = __shfl_up(gv, 1, 64);
+        if (l == 0) gprev = 0.f;
+        const float gpv = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
+        float gam[4], gamp[4], rat[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * g4 + r;
+            const float gt = __shfl(gv, t, 64);
+            gam[r] = expf(gt);
+            gamp[r] = expf(__shfl(gpv, t, 64));
+            rat[r] = expf(gC - gt);
+        }
+        const float gamC = expf(gC);
+        const float gcol = __shfl(gv, 16 * w + c16, 64);
+        float gj[4][4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gj[c][r] = __shfl(gv, 16 * c + 4 * g4 + r, 64);
+
+        // publish the state slice as B-operand fragments
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tau = w * TPW + u;
+            u16x4 hi, lo;
+            split4(Sacc[u], hi, lo);
+            sh.Sf[tau >> 1][tau & 1][0][l] = hi;
+            sh.Sf[tau >> 1][tau & 1][1][l] = lo;
+        }
+        __syncthreads();  // B1: state fragments and this chunk's K/Q/V visible
+
+        // Y = K S^T and Z = Q S^T for token rows 16w..16w+15
+        f32x4 Y = zero4(), Y2 = zero4(), Z = zero4(), Z2 = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const u16x8 shi = cat(sh.Sf[s][0][0][l], sh.Sf[s][1][0][l]);
+            const u16x8 slo = cat(sh.Sf[s][0][1][l], sh.Sf[s][1][1][l]);
+            const unsigned short* kr = &sh.K[cur][(16 * w + c16) * LDK + 32 * s + 4 * g4];
+            const unsigned short* qr = &sh.Q[cur][(16 * w + c16) * LDK + 32 * s + 4 * g4];
+            const u16x8 ka = cat(*reinterpret_cast<const u16x4*>(kr), *reinterpret_cast<const u16x4*>(kr + 16));
+            const u16x8 qa = cat(*reinterpret_cast<const u16x4*>(qr), *reinterpret_cast<const u16x4*>(qr + 16));
+            Y = mfma(ka, shi, Y);
+            Y2 = mfma(ka, slo, Y2);
+            Z = mfma(qa, shi, Z);
+            Z2 = mfma(qa, slo, Z2);
+        }
+        Y += Y2;
+        Z += Z2;
+
+        // X = V - diag(gamma') Y
+        f32x4 X;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * g4 + r;
+            const float vv = scaling ? 0.f : gdn_bf16_to_f32(sh.V[cur][t * 16 + c16]);
+            X[r] = vv - gamp[r] * Y[r];
+        }
+        {
+            u16x4 hi, lo;
+            split4(X, hi, lo);
+            sh.Xf[w >> 1][w & 1][0][l] = hi;
+            sh.Xf[w >> 1][w & 1][1][l] = lo;
+        }
+        __syncthreads();  // B2
+
+        // Delta = T' X for token rows 16w..16w+15 (T' lower triangular)
+        f32x4 Dl = zero4(), Dl2 = zero4(), Dl3 = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (s > (w >> 1)) continue;
+            const u16x8 xh = cat(sh.Xf[s][0][0][l], sh.Xf[s][1][0][l]);
+            const u16x8 xl = cat(sh.Xf[s][0][1][l], sh.Xf[s][1][1][l]);
+            Dl = mfma(tf_c[s][0], xh, Dl);
+            Dl2 = mfma(tf_c[s][0], xl, Dl2);
+            Dl3 = mfma(tf_c[s][1], xh, Dl3);
+        }
+        Dl += Dl2 + Dl3;
+        {
+            f32x4 DB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) DB[r] = rat[r] * Dl[r];
+            u16x4 hi, lo;
+            split4(Dl, hi, lo);
+            sh.Df[w >> 1][w & 1][0][l] = hi;
+            sh.Df[w >> 1][w & 1][1][l] = lo;
+            split4(DB, hi, lo);
+            sh.DBf[w >> 1][w & 1][0][l] = hi;
+            sh.DBf[w >> 1][w & 1][1][l] = lo;
+        }
+        __syncthreads();  // B3
+
+        // gated causal scores, transposed blocks: rows j (block c), cols t (block w)
+        f32x4 PT[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            PT[c] = zero4();
+            if (c > w) continue;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.K[cur][(16 * c + c16) * LDK + 32 * s + 8 * g4]);
+                const u16x8 qb = *reinterpret_cast<const u16x8*>(&sh.Q[cur][(16 * w + c16) * LDK + 32 * s + 8 * g4]);
+                acc = mfma(ka, qb, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * c + 4 * g4 + r, t = 16 * w + c16;
+                PT[c][r] = j <= t ? acc[r] * expf(gcol - gj[c][r]) : 0.f;
+            }
+        }
+        // O = scale (diag(gamma) Z + P Delta)
+        f32x4 O1 = zero4(), O2 = zero4(), O3 = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (s > (w >> 1)) continue;
+            u16x4 ph0, pl0, ph1, pl1;
+            split4(PT[2 * s], ph0, pl0);
+            split4(PT[2 * s + 1], ph1, pl1);
+            const u16x8 pah = cat(ph0, ph1), pal = cat(pl0, pl1);
+            const u16x8 dh = cat(sh.Df[s][0][0][l], sh.Df[s][1][0][l]);
+            const u16x8 dlo = cat(sh.Df[s][0][1][l], sh.Df[s][1][1][l]);
+            O1 = mfma(pah, dh, O1);
+            O2 = mfma(pah, dlo, O2);
+            O3 = mfma(pal, dh, O3);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * g4 + r;
+            const float o = p.scale * (gam[r] * Z[r] + O1[r] + O2[r] + O3[r]);
+            if (scaling)
+                corr[(bh * p.NC + i) * C * D + (int64_t)t * D + r0 + c16] = o;
+            else if (t < nt)
+                p.out[(((int64_t)b * T + t0 + t) * H + h) * D + r0 + c16] = o;
+        }
+
+        // S^T <- gamma_C S^T + K^T (diag(gamma_C / gamma) Delta), key rows of this wave
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tau = w * TPW + u;
+            f32x4 acc = gamC * Sacc[u], acc2 = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u16x8 ka;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
+                    ka[e] = sh.K[cur][j * LDK + 16 * tau + c16];
+                }
+                const u16x8 dbh = cat(sh.DBf[s][0][0][l], sh.DBf[s][1][0][l]);
+                const u16x8 dbl = cat(sh.DBf[s][0][1][l], sh.DBf[s][1][1][l]);
+                acc = mfma(ka, dbh, acc);
+                acc2 = mfma(ka, dbl, acc2);
+            }
+            Sacc[u] = acc + acc2;
+        }
+
+        // next chunk's inputs: prefetched registers -> the other LDS buffer
+        if (i + 1 < i_end) {
+            store_loads(cur ^ 1);
+            if (i + 2 < i_end) issue_loads(i + 2);
+        }
+    }
+
+    float* dst;
+    if (scaling)
+        dst = reinterpret_cast<float*>(wsb + L.mend) + (bh * sp.G + gseg) * D * D;
+    else if (sp.G == 1)
+        dst = p.s_out ? p.s_out + bh * D * D : nullptr;
+    else
+        dst = reinterpret_cast<float*>(wsb + L.sdend) + (bh * sp.G + gseg) * D * D;
+    if (dst) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int a0 = 16 * (w * TPW + u) + 4 * g4;
+            *reinterpret_cast<f32x4*>(&dst[(int64_t)(r0 + c16) * D + a0]) = Sacc[u];
+        }
+    }
+}
+
+template <int D>
+hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L, hipStream_t st) {
+    u16x8* tfrag = reinterpret_cast<u16x8*>(ws + L.prep);
+    {
+        dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
+        prof_begin("k_prep_mfma", st);
+        hipLaunchKernelGGL(k_prep_mfma<D>, grid, dim3(kThreads), 0, st, p, tfrag);
+        prof_end(st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        const int ntiles = D / 16 + (sp.G > 1 ? D / 16 : 0);
+        const int64_t heads = p.B * p.H * sp.G;
+        const int64_t nwork = heads * ntiles;
+        const int remap = (heads % 8 == 0) ? 1 : 0;
+        prof_begin("k_rec_mfma", st);
+        hipLaunchKernelGGL(k_rec_mfma<D>, dim3((unsigned)nwork), dim3(kThreads), 0, st, p, sp, L,
+                           ws, tfrag, ntiles, remap);
+        prof_end(st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (sp.G > 1) return seqpar_finish(p, sp, ws, L, st);
+    return hipSuccess;
+}
+
+}  // namespace
+
+bool mfma_supported(int64_t dk, int64_t dv, int C_, int dtype, int gate) {
+    return dtype == GDN_BF16 && gate == GDN_GATE_SCALAR && C_ == C && dk == dv &&
+           (dk == 64 || dk == 128);
+}
+
+WsLayout mfma_layout(const Problem& p, const Split& sp) {
+    WsLayout L;
+    const int64_t nch = p.B * p.H * (int64_t)p.NC;
+    L.prep = 0;
+    L.prep_bytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8));
+    size_t off = L.prep_bytes;
+    if (sp.G > 1) {
+        L.corr = off;
+        L.corr_bytes = align256(sizeof(float) * nch * p.C * p.dk);
+        off += L.corr_bytes;
+        L.sdend = off;
+        L.sdend_bytes = align256(sizeof(float) * p.B * p.H * sp.G * p.dv * p.dk);
+        off += L.sdend_bytes;
+        L.mend = off;
+        L.mend_bytes = align256(sizeof(float) * p.B * p.H * sp.G * p.dk * p.dk);
+        off += L.mend_bytes;
+        L.sstart = off;
+        L.sstart_bytes = align256(sizeof(float) * p.B * p.H * sp.G * p.dv * p.dk);
+        off += L.sstart_bytes;
+    }
+    L.total = off;
+    return L;
+}
+
+hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t st) {
+    const WsLayout L = mfma_layout(p, sp);
+    if (p.dk == 128) return launch<128>(p, sp, ws, L, st);
+    return launch<64>(p, sp, ws, L, st);
 }
 
 }  // namespace gdn
