@@ -43,32 +43,32 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int C = 64;
 constexpr int kThreads = 256;
-constexpr int kTfragPerChunk = 4 * 2 * 2 * 64;  // [m][s][hi/lo][lane] of u16x8
 
 __device__ __forceinline__ f32x4 mfma(const u16x8& a, const u16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ unsigned short bf16_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (unsigned short)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
 }
 
-__device__ __forceinline__ void split1(float x, unsigned short& hi, unsigned short& lo) {
-    hi = bf16_rne(x);
-    lo = bf16_rne(x - __uint_as_float((uint32_t)hi << 16));
+// x = hi + lo + O(2^-18 |x|): hi = bf16(x), lo = bf16(x - hi), both RNE.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf16(a, b);
+    lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 __device__ __forceinline__ void split4(const f32x4& x, u16x4& hi, u16x4& lo) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        unsigned short a, b;
-        split1(x[r], a, b);
-        hi[r] = a;
-        lo[r] = b;
-    }
+    uint32_t h0, l0, h1, l1;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    hi = __builtin_bit_cast(u16x4, uint2{h0, h1});
+    lo = __builtin_bit_cast(u16x4, uint2{l0, l1});
 }
 
 __device__ __forceinline__ u16x8 cat(const u16x4& a, const u16x4& b) {
@@ -87,17 +87,31 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// stage 1: T' per chunk-head
+// stage 1: T' and the gate block per chunk-head
 // ---------------------------------------------------------------------------
+// Gate block (floats): [0,64) gamma_t, [64,128) gamma'_t, [128,192)
+// gamma_C / gamma_t, [192,256) g_t, [256] gamma_C.
+constexpr int kGateFloats = 272;
+// T' fragments kept per chunk: (m, s) with s <= m / 2 (T' is lower triangular)
+constexpr int kTslots = 6;
+constexpr int kTfragPerChunk = kTslots * 2 * 64;  // [slot][hi/lo][lane] of u16x8
+__host__ __device__ constexpr int tslot(int m, int s) { return m < 2 ? m : 2 + 2 * (m - 2) + s; }
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag) {
+__global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag, float* gates) {
     constexpr int LDK = D + 8;
     constexpr int PPR = D / 8;
-    __shared__ __attribute__((aligned(16))) unsigned short Ks[C * LDK];
+    constexpr int kBufBytes = (C * LDK * 2 > C * (C + 1) * 4) ? C * LDK * 2 : C * (C + 1) * 4;
+    // K (bf16, row stride LDK) during the Gram product, then T (fp32 [C][C+1])
+    __shared__ __attribute__((aligned(16))) unsigned char kt_buf[kBufBytes];
     __shared__ float Ms[C][C + 1];
-    __shared__ float Ts[C][C + 1];
-    __shared__ float Xs[3][16][17];
     __shared__ float gsh[C], gpsh[C], bsh[C];
+    unsigned short* Ks = reinterpret_cast<unsigned short*>(kt_buf);
+    float (*Ts)[C + 1] = reinterpret_cast<float (*)[C + 1]>(kt_buf);
 
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
@@ -123,13 +137,17 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag)
         const float gv = wave_incl_scan(la, l);
         float gprev = __shfl_up(gv, 1, 64);
         if (l == 0) gprev = 0.f;
+        const float gpv = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
+        const float gC = __shfl(gv, 63, 64);
         gsh[l] = gv;
-        gpsh[l] = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
+        gpsh[l] = gpv;
         bsh[l] = bt;
-    }
-    for (int e = tid; e < C * C; e += kThreads) {
-        const int t = e >> 6, j = e & 63;
-        if ((j >> 4) > (t >> 4)) Ts[t][j] = 0.f;
+        float* gb = gates + ch * kGateFloats;
+        gb[l] = expf(gv);
+        gb[64 + l] = expf(gpv);
+        gb[128 + l] = expf(gC - gv);
+        gb[192 + l] = gv;
+        if (l == 0) gb[256] = expf(gC);
     }
     __syncthreads();
 
@@ -150,9 +168,10 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag)
             Ms[t][j] = j < t ? bsh[t] * expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
         }
     }
-    __syncthreads();
+    __syncthreads();  // K is dead from here on; its LDS holds T
 
-    // diagonal 16 x 16 blocks: forward substitution, one column per lane
+    // diagonal 16 x 16 blocks of T = (I + A)^{-1}: forward substitution, one
+    // column per lane; the other lanes clear the blocks above the diagonal
     if (l < 16) {
         const int j = c16;
         float col[16];
@@ -166,54 +185,65 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag)
 #pragma unroll
         for (int t = 0; t < 16; ++t) Ts[16 * w + t][16 * w + j] = col[t];
     }
+    for (int e = tid; e < C * C; e += kThreads) {
+        const int t = e >> 6, j = e & 63;
+        if ((j >> 4) > (t >> 4)) Ts[t][j] = 0.f;
+    }
     __syncthreads();
 
-    // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+    // off-diagonal blocks by distance d, one block per wave, fp32 MFMA:
+    // T_ij = -T_ii X, X = sum_{k=j}^{i-1} A_ik T_kj.  Instruction s contracts the
+    // indices 4G + s (G = lane / 16), so X's accumulator value s of each lane
+    // is the second product's B operand as it stands.
     for (int d = 1; d < 4; ++d) {
-        const int nblk = 4 - d;
-        for (int e = tid; e < nblk * 256; e += kThreads) {
-            const int q = e >> 8, r = (e >> 4) & 15, c = e & 15;
-            const int jb = q, ib = q + d;
-            float x = 0.f;
-            for (int kk = 16 * jb; kk < 16 * ib; ++kk) x += Ms[16 * ib + r][kk] * Ts[kk][16 * jb + c];
-            Xs[q][r][c] = x;
-        }
-        __syncthreads();
-        for (int e = tid; e < nblk * 256; e += kThreads) {
-            const int q = e >> 8, r = (e >> 4) & 15, c = e & 15;
-            const int jb = q, ib = q + d;
-            float x = 0.f;
+        if (w < 4 - d) {
+            const int jb = w, ib = w + d;
+            f32x4 X = zero4();
+            for (int kb = jb; kb < ib; ++kb) {
 #pragma unroll
-            for (int mm = 0; mm < 16; ++mm) x -= Ts[16 * ib + r][16 * ib + mm] * Xs[q][mm][c];
-            Ts[16 * ib + r][16 * jb + c] = x;
+                for (int s = 0; s < 4; ++s)
+                    X = mfma_f32(Ms[16 * ib + c16][16 * kb + 4 * g4 + s],
+                                 Ts[16 * kb + 4 * g4 + s][16 * jb + c16], X);
+            }
+            f32x4 Tij = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Tij = mfma_f32(Ts[16 * ib + c16][16 * ib + 4 * g4 + s], X[s], Tij);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ts[16 * ib + 4 * g4 + r][16 * jb + c16] = -Tij[r];
         }
         __syncthreads();
     }
 
-    // T' = T diag(beta) as A-operand fragments: [m][s][hi/lo][lane] of 8 bf16;
-    // lane (row 16m + lane%16, group g), slot e -> column 32s + 4g + e (e < 4)
-    // or 32s + 16 + 4g + e - 4
+    // T' = T diag(beta) as A-operand fragments: [slot(m, s)][hi/lo][lane] of 8
+    // bf16; lane (row 16m + lane%16, group g), slot e -> column 32s + 4g + e
+    // (e < 4) or 32s + 16 + 4g + e - 4
     u16x8* dst = tfrag + ch * kTfragPerChunk;
-    for (int f = tid; f < 4 * 2 * 64; f += kThreads) {
-        const int m = f >> 7, s = (f >> 6) & 1, lane = f & 63;
+    for (int f = tid; f < kTslots * 64; f += kThreads) {
+        const int slot = f >> 6, lane = f & 63;
+        const int m = slot < 2 ? slot : 2 + ((slot - 2) >> 1);
+        const int s = slot < 2 ? 0 : ((slot - 2) & 1);
         const int t = 16 * m + (lane & 15), gg = lane >> 4;
-        u16x8 hi, lo;
+        uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
-            unsigned short a, bb;
-            split1(Ts[t][j] * bsh[j], a, bb);
-            hi[e] = a;
-            lo[e] = bb;
+        for (int e = 0; e < 8; e += 2) {
+            const int j0 = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
+            split2(Ts[t][j0] * bsh[j0], Ts[t][j0 + 1] * bsh[j0 + 1], hi[e >> 1], lo[e >> 1]);
         }
-        dst[((m * 2 + s) * 2 + 0) * 64 + lane] = hi;
-        dst[((m * 2 + s) * 2 + 1) * 64 + lane] = lo;
+        dst[(slot * 2 + 0) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
+        dst[(slot * 2 + 1) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
     }
 }
 
 // ---------------------------------------------------------------------------
 // stage 2: the chunk loop
 // ---------------------------------------------------------------------------
+// Per chunk i, three phases separated by barriers; only Y -> X -> Delta ->
+// S is on the sequential path, the output of chunk i is finished in phase A
+// of chunk i + 1:
+//   A: Y = K S^T, Z = Q S^T; X = V - diag(gamma') Y -> LDS;  output of i-1
+//   B: Delta = T' X -> LDS (with Delta scaled to the chunk end);  P of chunk i;
+//      gather K^T operands
+//   C: S^T <- gamma_C S^T + K^T Delta-bar; publish S^T; stage chunk i+1 inputs
 template <int D>
 struct RecShared {
     static constexpr int LDK = D + 8;
@@ -221,6 +251,7 @@ struct RecShared {
     unsigned short K[2][C * LDK];
     unsigned short Q[2][C * LDK];
     unsigned short V[2][C * 16];
+    float G[2][kGateFloats];
     u16x4 Sf[KS][2][2][64];  // S^T fragments: [k-step][tile half][hi/lo][lane]
     u16x4 Xf[2][2][2][64];
     u16x4 Df[2][2][2][64];
@@ -230,23 +261,23 @@ struct RecShared {
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLayout L,
                                                        char* wsb, const u16x8* tfrag,
-                                                       int ntiles, int xcd_remap) {
+                                                       const float* gates, int ntiles,
+                                                       int xcd_remap) {
     constexpr int LDK = D + 8;
     constexpr int KS = D / 32;   // k-steps over the key dimension
     constexpr int TPW = D / 64;  // 16-row key tiles of S^T owned per wave
     constexpr int PPR = D / 8;   // 16-byte pieces per K/Q row
     constexpr int KQP = C * PPR / kThreads;
+    constexpr int GP = kGateFloats / 4;  // 16-byte pieces of a gate block
     __shared__ __attribute__((aligned(16))) RecShared<D> sh;
 
     // work decode; with xcd_remap the ntiles slices of one (head, segment)
     // land on one XCD (workgroups are dealt to the 8 XCDs round-robin)
-    const int nwork = gridDim.x;
     int id = blockIdx.x;
     if (xcd_remap) {
         const int xcd = id & 7, slot = id >> 3;
         id = ((slot / ntiles) * 8 + xcd) * ntiles + slot % ntiles;
     }
-    (void)nwork;
     const int x = id % ntiles;
     const int hg = id / ntiles;  // (b * H + h) * G + seg
     const int gseg = hg % sp.G;
@@ -265,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
     const unsigned short* kin = static_cast<const unsigned short*>(p.k);
     const unsigned short* qin = static_cast<const unsigned short*>(p.q);
     const unsigned short* vin = static_cast<const unsigned short*>(p.v);
+    const int nks = (w >> 1) + 1;  // k-steps over tokens for rows of tile w
 
     // state slice S^T[a][v], a-tile tau = w*TPW + u: lane (v = c16, a = 16 tau + 4 g4 + r)
     f32x4 Sacc[TPW];
@@ -281,33 +313,40 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
         }
     }
 
-    uint4 kreg[KQP], qreg[KQP], vreg;
+    uint4 kreg[KQP], qreg[KQP], vreg, greg;
     u16x8 tf_n[2][2], tf_c[2][2];
-    float al_n = 1.f, al_c = 1.f;
 
+    // loop-invariant bases; a chunk advances every token pointer by C*H*D
+    constexpr int RPP = kThreads / PPR;  // token rows per load pass
+    const int trow = tid / PPR, c8 = tid % PPR;
+    const int64_t row_stride = H * D;
+    const int64_t chunk_stride = (int64_t)C * row_stride;
+    const int64_t kq_base = (((int64_t)b * T + trow) * H + h) * D + c8 * 8;
+    const int vrow = tid >> 1, vhf = tid & 1;
+    const int64_t v_base = (((int64_t)b * T + vrow) * H + h) * D + r0 + 8 * vhf;
+    const u16x8* tf_base = tfrag + bh * p.NC * kTfragPerChunk + l;
+    const float* g_base = gates + bh * p.NC * kGateFloats;
     auto issue_loads = [&](int i) {
         const int64_t t0 = (int64_t)i * C;
         const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        const int64_t cofs = (int64_t)i * chunk_stride;
 #pragma unroll
         for (int k = 0; k < KQP; ++k) {
-            const int e = tid + kThreads * k;
-            const int t = e / PPR, c8 = e - (e / PPR) * PPR;
-            const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
-            kreg[k] = t < nt ? *reinterpret_cast<const uint4*>(kin + off) : make_uint4(0, 0, 0, 0);
-            qreg[k] = t < nt ? *reinterpret_cast<const uint4*>(qin + off) : make_uint4(0, 0, 0, 0);
+            const bool ok = trow + RPP * k < nt;
+            const int64_t off = kq_base + cofs + (int64_t)(RPP * k) * row_stride;
+            kreg[k] = ok ? *reinterpret_cast<const uint4*>(kin + off) : make_uint4(0, 0, 0, 0);
+            qreg[k] = ok ? *reinterpret_cast<const uint4*>(qin + off) : make_uint4(0, 0, 0, 0);
         }
         vreg = make_uint4(0, 0, 0, 0);
-        if (!scaling && tid < 128) {
-            const int t = tid >> 1, hf = tid & 1;
-            if (t < nt) vreg = *reinterpret_cast<const uint4*>(vin + (((int64_t)b * T + t0 + t) * H + h) * D + r0 + 8 * hf);
-        }
-        al_n = l < nt ? p.alpha[((int64_t)b * T + t0 + l) * H + h] : 1.f;
-        const u16x8* tp = tfrag + (bh * p.NC + i) * kTfragPerChunk;
+        if (!scaling && tid < 128 && vrow < nt)
+            vreg = *reinterpret_cast<const uint4*>(vin + v_base + cofs);
+        if (tid < GP) greg = reinterpret_cast<const uint4*>(g_base + (int64_t)i * kGateFloats)[tid];
+        const u16x8* tp = tf_base + (int64_t)i * kTfragPerChunk;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl) {
-                if (s <= (w >> 1)) tf_n[s][hl] = tp[((w * 2 + s) * 2 + hl) * 64 + l];
+                if (s < nks) tf_n[s][hl] = tp[(tslot(w, s) * 2 + hl) * 64];
                 else tf_n[s][hl] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
             }
         }
@@ -315,57 +354,17 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
     auto store_loads = [&](int buf) {
 #pragma unroll
         for (int k = 0; k < KQP; ++k) {
-            const int e = tid + kThreads * k;
-            const int t = e / PPR, c8 = e - (e / PPR) * PPR;
-            *reinterpret_cast<uint4*>(&sh.K[buf][t * LDK + c8 * 8]) = kreg[k];
-            *reinterpret_cast<uint4*>(&sh.Q[buf][t * LDK + c8 * 8]) = qreg[k];
+            *reinterpret_cast<uint4*>(&sh.K[buf][(trow + RPP * k) * LDK + c8 * 8]) = kreg[k];
+            *reinterpret_cast<uint4*>(&sh.Q[buf][(trow + RPP * k) * LDK + c8 * 8]) = qreg[k];
         }
-        if (tid < 128) {
-            const int t = tid >> 1, hf = tid & 1;
-            *reinterpret_cast<uint4*>(&sh.V[buf][t * 16 + 8 * hf]) = vreg;
-        }
+        if (tid < 128) *reinterpret_cast<uint4*>(&sh.V[buf][vrow * 16 + 8 * vhf]) = vreg;
+        if (tid < GP) reinterpret_cast<uint4*>(sh.G[buf])[tid] = greg;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl) tf_c[s][hl] = tf_n[s][hl];
-        al_c = al_n;
     };
-
-    if (i_begin < i_end) {
-        issue_loads(i_begin);
-        store_loads(0);
-        if (i_begin + 1 < i_end) issue_loads(i_begin + 1);
-    }
-
-    for (int i = i_begin; i < i_end; ++i) {
-        const int cur = (i - i_begin) & 1;
-        const int64_t t0 = (int64_t)i * C;
-        const int nt = (int)((T - t0) < C ? (T - t0) : C);
-
-        // chunk-local gate prefix; lane = token
-        const float gv = wave_incl_scan(logf(al_c), l);
-        const float gC = __shfl(gv, 63, 64);
-        float gprev = __shfl_up(gv, 1, 64);
-        if (l == 0) gprev = 0.f;
-        const float gpv = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
-        float gam[4], gamp[4], rat[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * w + 4 * g4 + r;
-            const float gt = __shfl(gv, t, 64);
-            gam[r] = expf(gt);
-            gamp[r] = expf(__shfl(gpv, t, 64));
-            rat[r] = expf(gC - gt);
-        }
-        const float gamC = expf(gC);
-        const float gcol = __shfl(gv, 16 * w + c16, 64);
-        float gj[4][4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gj[c][r] = __shfl(gv, 16 * c + 4 * g4 + r, 64);
-
-        // publish the state slice as B-operand fragments
+    auto publish_state = [&]() {
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int tau = w * TPW + u;
@@ -374,9 +373,57 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
             sh.Sf[tau >> 1][tau & 1][0][l] = hi;
             sh.Sf[tau >> 1][tau & 1][1][l] = lo;
         }
-        __syncthreads();  // B1: state fragments and this chunk's K/Q/V visible
+    };
 
-        // Y = K S^T and Z = Q S^T for token rows 16w..16w+15
+    // output of the previous chunk: O = scale (diag(gamma) Z + P Delta)
+    const int64_t out_base = (((int64_t)b * T + 16 * w + 4 * g4) * H + h) * D + r0 + c16;
+    float* corr_base = corr + bh * p.NC * C * D + (int64_t)(16 * w + 4 * g4) * D + r0 + c16;
+    f32x4 Zp = zero4(), gamP = zero4();
+    u16x8 pah[2], pal[2];
+    int64_t tp0 = 0;
+    int ntp = 0, ip = 0;
+    auto emit_output = [&]() {
+        f32x4 O1 = zero4(), O2 = zero4(), O3 = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (s >= nks) continue;
+            const u16x8 dh = cat(sh.Df[s][0][0][l], sh.Df[s][1][0][l]);
+            const u16x8 dlo = cat(sh.Df[s][0][1][l], sh.Df[s][1][1][l]);
+            O1 = mfma(pah[s], dh, O1);
+            O2 = mfma(pah[s], dlo, O2);
+            O3 = mfma(pal[s], dh, O3);
+        }
+        if (scaling) {
+            float* dst = corr_base + (int64_t)ip * C * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[r * D] = p.scale * (gamP[r] * Zp[r] + O1[r] + O2[r] + O3[r]);
+        } else {
+            float* dst = p.out + out_base + tp0 * row_stride;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * w + 4 * g4 + r < ntp)
+                    dst[r * row_stride] = p.scale * (gamP[r] * Zp[r] + O1[r] + O2[r] + O3[r]);
+        }
+    };
+
+    if (i_begin < i_end) {
+        issue_loads(i_begin);
+        store_loads(0);
+        if (i_begin + 1 < i_end) issue_loads(i_begin + 1);
+    }
+    publish_state();
+
+    for (int i = i_begin; i < i_end; ++i) {
+        const int cur = (i - i_begin) & 1;
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        __syncthreads();  // B1: state fragments and chunk i inputs visible
+
+        // ---- phase A
+        const float* G = sh.G[cur];
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(&G[16 * w + 4 * g4]);
+        const f32x4 gamp = *reinterpret_cast<const f32x4*>(&G[64 + 16 * w + 4 * g4]);
         f32x4 Y = zero4(), Y2 = zero4(), Z = zero4(), Z2 = zero4();
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -392,9 +439,6 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
             Z2 = mfma(qa, slo, Z2);
         }
         Y += Y2;
-        Z += Z2;
-
-        // X = V - diag(gamma') Y
         f32x4 X;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -408,13 +452,14 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
             sh.Xf[w >> 1][w & 1][0][l] = hi;
             sh.Xf[w >> 1][w & 1][1][l] = lo;
         }
+        if (i > i_begin) emit_output();
         __syncthreads();  // B2
 
-        // Delta = T' X for token rows 16w..16w+15 (T' lower triangular)
+        // ---- phase B
         f32x4 Dl = zero4(), Dl2 = zero4(), Dl3 = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            if (s > (w >> 1)) continue;
+            if (s >= nks) continue;
             const u16x8 xh = cat(sh.Xf[s][0][0][l], sh.Xf[s][1][0][l]);
             const u16x8 xl = cat(sh.Xf[s][0][1][l], sh.Xf[s][1][1][l]);
             Dl = mfma(tf_c[s][0], xh, Dl);
@@ -423,90 +468,89 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
         }
         Dl += Dl2 + Dl3;
         {
-            f32x4 DB;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) DB[r] = rat[r] * Dl[r];
+            const f32x4 rat = *reinterpret_cast<const f32x4*>(&G[128 + 16 * w + 4 * g4]);
             u16x4 hi, lo;
             split4(Dl, hi, lo);
             sh.Df[w >> 1][w & 1][0][l] = hi;
             sh.Df[w >> 1][w & 1][1][l] = lo;
-            split4(DB, hi, lo);
+            split4(rat * Dl, hi, lo);
             sh.DBf[w >> 1][w & 1][0][l] = hi;
             sh.DBf[w >> 1][w & 1][1][l] = lo;
         }
-        __syncthreads();  // B3
-
-        // gated causal scores, transposed blocks: rows j (block c), cols t (block w)
-        f32x4 PT[4];
+        // gated causal scores of chunk i, transposed blocks: rows j (block c),
+        // columns t (block w); factor exp(g_t - g_j) for j <= t
+        {
+            const float gcol = G[192 + 16 * w + c16];
+            f32x4 PT[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            PT[c] = zero4();
-            if (c > w) continue;
-            f32x4 acc = zero4();
+            for (int c = 0; c < 4; ++c) {
+                PT[c] = zero4();
+                if (c > w) continue;
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.K[cur][(16 * c + c16) * LDK + 32 * s + 8 * g4]);
-                const u16x8 qb = *reinterpret_cast<const u16x8*>(&sh.Q[cur][(16 * w + c16) * LDK + 32 * s + 8 * g4]);
-                acc = mfma(ka, qb, acc);
+                for (int s = 0; s < KS; ++s) {
+                    const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.K[cur][(16 * c + c16) * LDK + 32 * s + 8 * g4]);
+                    const u16x8 qb = *reinterpret_cast<const u16x8*>(&sh.Q[cur][(16 * w + c16) * LDK + 32 * s + 8 * g4]);
+                    acc = mfma(ka, qb, acc);
+                }
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[192 + 16 * c + 4 * g4]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * c + 4 * g4 + r, t = 16 * w + c16;
+                    PT[c][r] = j <= t ? acc[r] * __expf(gcol - gj[r]) : 0.f;
+                }
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * c + 4 * g4 + r, t = 16 * w + c16;
-                PT[c][r] = j <= t ? acc[r] * expf(gcol - gj[c][r]) : 0.f;
-            }
-        }
-        // O = scale (diag(gamma) Z + P Delta)
-        f32x4 O1 = zero4(), O2 = zero4(), O3 = zero4();
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (s > (w >> 1)) continue;
-            u16x4 ph0, pl0, ph1, pl1;
-            split4(PT[2 * s], ph0, pl0);
-            split4(PT[2 * s + 1], ph1, pl1);
-            const u16x8 pah = cat(ph0, ph1), pal = cat(pl0, pl1);
-            const u16x8 dh = cat(sh.Df[s][0][0][l], sh.Df[s][1][0][l]);
-            const u16x8 dlo = cat(sh.Df[s][0][1][l], sh.Df[s][1][1][l]);
-            O1 = mfma(pah, dh, O1);
-            O2 = mfma(pah, dlo, O2);
-            O3 = mfma(pal, dh, O3);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * w + 4 * g4 + r;
-            const float o = p.scale * (gam[r] * Z[r] + O1[r] + O2[r] + O3[r]);
-            if (scaling)
-                corr[(bh * p.NC + i) * C * D + (int64_t)t * D + r0 + c16] = o;
-            else if (t < nt)
-                p.out[(((int64_t)b * T + t0 + t) * H + h) * D + r0 + c16] = o;
-        }
-
-        // S^T <- gamma_C S^T + K^T (diag(gamma_C / gamma) Delta), key rows of this wave
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int tau = w * TPW + u;
-            f32x4 acc = gamC * Sacc[u], acc2 = zero4();
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                u16x8 ka;
+                u16x4 h0, l0, h1, l1;
+                split4(PT[2 * s], h0, l0);
+                split4(PT[2 * s + 1], h1, l1);
+                pah[s] = cat(h0, h1);
+                pal[s] = cat(l0, l1);
+            }
+        }
+        // K^T operands for the state update: rows a = 16 tau + c16, k-slots j
+        u16x8 kt[TPW][2];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int j = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-                    ka[e] = sh.K[cur][j * LDK + 16 * tau + c16];
+                    kt[u][s][e] = sh.K[cur][j * LDK + 16 * (w * TPW + u) + c16];
                 }
+            }
+        }
+        __syncthreads();  // B3
+
+        // ---- phase C
+        const float gamC = G[256];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            f32x4 acc = gamC * Sacc[u], acc2 = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
                 const u16x8 dbh = cat(sh.DBf[s][0][0][l], sh.DBf[s][1][0][l]);
                 const u16x8 dbl = cat(sh.DBf[s][0][1][l], sh.DBf[s][1][1][l]);
-                acc = mfma(ka, dbh, acc);
-                acc2 = mfma(ka, dbl, acc2);
+                acc = mfma(kt[u][s], dbh, acc);
+                acc2 = mfma(kt[u][s], dbl, acc2);
             }
             Sacc[u] = acc + acc2;
         }
-
+        publish_state();
+        Zp = Z + Z2;
+        gamP = gam;
+        tp0 = t0;
+        ntp = nt;
+        ip = i;
         // next chunk's inputs: prefetched registers -> the other LDS buffer
         if (i + 1 < i_end) {
             store_loads(cur ^ 1);
             if (i + 2 < i_end) issue_loads(i + 2);
         }
     }
+    if (i_begin < i_end) emit_output();
 
     float* dst;
     if (scaling)
@@ -527,10 +571,12 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
 template <int D>
 hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L, hipStream_t st) {
     u16x8* tfrag = reinterpret_cast<u16x8*>(ws + L.prep);
+    const int64_t nch = p.B * p.H * (int64_t)p.NC;
+    float* gates = reinterpret_cast<float*>(ws + L.prep + align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)));
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
         prof_begin("k_prep_mfma", st);
-        hipLaunchKernelGGL(k_prep_mfma<D>, grid, dim3(kThreads), 0, st, p, tfrag);
+        hipLaunchKernelGGL(k_prep_mfma<D>, grid, dim3(kThreads), 0, st, p, tfrag, gates);
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -542,7 +588,7 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
         const int remap = (heads % 8 == 0) ? 1 : 0;
         prof_begin("k_rec_mfma", st);
         hipLaunchKernelGGL(k_rec_mfma<D>, dim3((unsigned)nwork), dim3(kThreads), 0, st, p, sp, L,
-                           ws, tfrag, ntiles, remap);
+                           ws, tfrag, gates, ntiles, remap);
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -562,7 +608,8 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
     WsLayout L;
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
     L.prep = 0;
-    L.prep_bytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8));
+    L.prep_bytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
+                   align256((size_t)nch * kGateFloats * sizeof(float));
     size_t off = L.prep_bytes;
     if (sp.G > 1) {
         L.corr = off;
