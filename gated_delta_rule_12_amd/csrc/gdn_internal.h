@@ -48,6 +48,7 @@ struct WsLayout {
     size_t sdend = 0, sdend_bytes = 0;   // seq-par: per-segment end states (S^D)
     size_t mend = 0, mend_bytes = 0;     // seq-par: per-segment end scaling matrices
     size_t sstart = 0, sstart_bytes = 0; // seq-par: per-segment true start states
+    size_t sfrag = 0, sfrag_bytes = 0;   // seq-par, MFMA family: start states as bf16 hi/lo fragments
     size_t total = 0;
 };
 
@@ -64,7 +65,10 @@ hipError_t recurrent_forward(const Problem& p, hipStream_t st);
 // Sequence-parallel tail shared by both families: chain of start states and
 // output correction (R_i S_start^T), then the final state.
 hipError_t seqpar_finish(const Problem& p, const Split& sp, char* ws,
-                         const WsLayout& L, hipStream_t st);
+                         const WsLayout& L, bool mfma, hipStream_t st);
+// MFMA output correction O_i += R_i S_start^T (gdn_mfma.hip).
+hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
+                        hipStream_t st);
 
 // Start state copy/zero for empty sequences (T == 0).
 hipError_t copy_state(const Problem& p, hipStream_t st);

@@ -568,6 +568,75 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
     }
 }
 
+// ---------------------------------------------------------------------------
+// sequence parallel: output correction O_i += R_i S_start(g)^T
+// ---------------------------------------------------------------------------
+// Computed transposed, O^T[v][t] += sum_a S_start[v][a] R[t][a]: the start
+// state is the A operand (pre-split fragments written by the chain kernel),
+// R the B operand (rows of R are contiguous in a); wave w covers value rows
+// 16w' for w' = w, w + 4 (D = 128) and all 64 tokens.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_correct_mfma(Problem p, Split sp, WsLayout L,
+                                                           char* wsb) {
+    constexpr int KS = D / 32;
+    constexpr int NVT = D / 16;
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int g = i / sp.per;
+    if (g == 0) return;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int64_t H = p.H, T = p.T, bh = (int64_t)b * H + h;
+    const int64_t t0 = (int64_t)i * C;
+    const int nt = (int)((T - t0) < C ? (T - t0) : C);
+    const float* R = reinterpret_cast<const float*>(wsb + L.corr) + (bh * p.NC + i) * C * D;
+    const u16x8* fr = reinterpret_cast<const u16x8*>(wsb + L.sfrag) +
+                      (bh * sp.G + g) * (int64_t)NVT * KS * 2 * 64 + l;
+
+    // B operands: R rows t = 16 tn + c16, columns 32s + 8 g4 .. +7, all 4 token tiles
+    u16x8 rh[4][KS], rl[4][KS];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const float* src = R + (int64_t)(16 * tn + c16) * D + 32 * s + 8 * g4;
+            const float4 a = *reinterpret_cast<const float4*>(src);
+            const float4 c = *reinterpret_cast<const float4*>(src + 4);
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            split2(a.x, a.y, h0, l0);
+            split2(a.z, a.w, h1, l1);
+            split2(c.x, c.y, h2, l2);
+            split2(c.z, c.w, h3, l3);
+            rh[tn][s] = __builtin_bit_cast(u16x8, uint4{h0, h1, h2, h3});
+            rl[tn][s] = __builtin_bit_cast(u16x8, uint4{l0, l1, l2, l3});
+        }
+    }
+    for (int vn = w; vn < NVT; vn += 4) {
+        u16x8 sh_[KS], sl_[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sh_[s] = fr[((vn * KS + s) * 2 + 0) * 64];
+            sl_[s] = fr[((vn * KS + s) * 2 + 1) * 64];
+        }
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+            f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                a1 = mfma(sh_[s], rh[tn][s], a1);
+                a2 = mfma(sh_[s], rl[tn][s], a2);
+                a3 = mfma(sl_[s], rh[tn][s], a3);
+            }
+            // accumulator: column t = 16 tn + c16, rows v = 16 vn + 4 g4 + r
+            const int t = 16 * tn + c16;
+            if (t < nt) {
+                float* o = p.out + (((int64_t)b * T + t0 + t) * H + h) * D + 16 * vn + 4 * g4;
+                f32x4 cur = *reinterpret_cast<f32x4*>(o);
+                cur += a1 + a2 + a3;
+                *reinterpret_cast<f32x4*>(o) = cur;
+            }
+        }
+    }
+}
+
 template <int D>
 hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L, hipStream_t st) {
     u16x8* tfrag = reinterpret_cast<u16x8*>(ws + L.prep);
@@ -593,7 +662,7 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (sp.G > 1) return seqpar_finish(p, sp, ws, L, st);
+    if (sp.G > 1) return seqpar_finish(p, sp, ws, L, true, st);
     return hipSuccess;
 }
 
@@ -624,9 +693,24 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
         L.sstart = off;
         L.sstart_bytes = align256(sizeof(float) * p.B * p.H * sp.G * p.dv * p.dk);
         off += L.sstart_bytes;
+        L.sfrag = off;
+        L.sfrag_bytes = align256(2 * sizeof(uint16_t) * p.B * p.H * sp.G * p.dv * p.dk);
+        off += L.sfrag_bytes;
     }
     L.total = off;
     return L;
+}
+
+hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
+                        hipStream_t st) {
+    dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
+    prof_begin("k_correct_mfma", st);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(k_correct_mfma<128>, grid, dim3(kThreads), 0, st, p, sp, L, ws);
+    else
+        hipLaunchKernelGGL(k_correct_mfma<64>, grid, dim3(kThreads), 0, st, p, sp, L, ws);
+    prof_end(st);
+    return hipGetLastError();
 }
 
 hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t st) {

@@ -338,7 +338,7 @@ hipError_t valu_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (sp.G > 1) return seqpar_finish(p, sp, ws, L, st);
+    if (sp.G > 1) return seqpar_finish(p, sp, ws, L, false, st);
     return hipSuccess;
 }
 
@@ -348,8 +348,12 @@ hipError_t valu_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
 namespace {
 
 // S_start(g+1) = S^D_end(g) + S_start(g) M_end(g), 16 state rows per block;
-// rows of the start state evolve independently.
-__global__ __launch_bounds__(kThreads) void k_chain(Problem p, Split sp, WsLayout L, char* wsb) {
+// rows of the start state evolve independently.  M_end(g) is staged in LDS.
+// With frag != nullptr the start states are also written as bf16 hi/lo
+// B-operand fragments for the MFMA correction: [n][s][hi/lo][lane] of 8
+// bf16, lane (row v = 16n + lane%16, columns 32s + 8(lane/16) .. +7).
+__global__ __launch_bounds__(kThreads) void k_chain(Problem p, Split sp, WsLayout L, char* wsb,
+                                                    int write_frag) {
     const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int dk = (int)p.dk, dv = (int)p.dv, tid = threadIdx.x;
     const int r0 = x * kRows;
@@ -361,21 +365,58 @@ __global__ __launch_bounds__(kThreads) void k_chain(Problem p, Split sp, WsLayou
     extern __shared__ float smem[];
     float* Cur = smem;                    // [16][dk+1]
     float* Nxt = Cur + kRows * (dk + 1);  // [16][dk+1]
+    float* Ms = Nxt + kRows * (dk + 1);   // [dk][dk]
     for (int e = tid; e < kRows * dk; e += kThreads) {
         const int r = e / dk, a = e - (e / dk) * dk;
         Cur[r * (dk + 1) + a] = sdend[(bh * sp.G + 0) * dv * dk + (int64_t)(r0 + r) * dk + a];
     }
-    __syncthreads();
     for (int g = 1; g < sp.G; ++g) {
         const float* M = mend + (bh * sp.G + g) * dk * dk;
         const float* SD = sdend + (bh * sp.G + g) * dv * dk;
         float* SS = sstart + (bh * sp.G + g) * dv * dk;
+        for (int e = tid; e < dk * dk / 4; e += kThreads)
+            reinterpret_cast<float4*>(Ms)[e] = reinterpret_cast<const float4*>(M)[e];
+        __syncthreads();
+        if (write_frag) {
+            // fragments of rows r0..r0+15 (one 16-row tile n = x), every k-step
+            const int ks = dk / 32;
+            uint16_t* fr = reinterpret_cast<uint16_t*>(wsb + L.sfrag) +
+                           ((bh * sp.G + g) * (dv / 16) + x) * (int64_t)ks * 2 * 64 * 8;
+            for (int f = tid; f < ks * 64; f += kThreads) {
+                const int s = f >> 6, lane = f & 63;
+                const int r = lane & 15, a0 = 32 * s + 8 * (lane >> 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = Cur[r * (dk + 1) + a0 + e];
+                    const uint32_t ub = __float_as_uint(v);
+                    const uint32_t hi = (ub + 0x7FFFu + ((ub >> 16) & 1u)) >> 16;
+                    const float rem = v - __uint_as_float(hi << 16);
+                    const uint32_t ur = __float_as_uint(rem);
+                    const uint32_t lo = (ur + 0x7FFFu + ((ur >> 16) & 1u)) >> 16;
+                    fr[((s * 2 + 0) * 64 + lane) * 8 + e] = (uint16_t)hi;
+                    fr[((s * 2 + 1) * 64 + lane) * 8 + e] = (uint16_t)lo;
+                }
+            }
+        }
         for (int e = tid; e < kRows * dk; e += kThreads) {
             const int r = e / dk, c = e - (e / dk) * dk;
             SS[(int64_t)(r0 + r) * dk + c] = Cur[r * (dk + 1) + c];
-            float s = SD[(int64_t)(r0 + r) * dk + c];
-            for (int a = 0; a < dk; ++a) s += Cur[r * (dk + 1) + a] * M[(int64_t)a * dk + c];
-            Nxt[r * (dk + 1) + c] = s;
+        }
+        // each thread: one row r, eight consecutive columns c0..c0+7
+        for (int e = tid; e < kRows * (dk / 8); e += kThreads) {
+            const int r = e / (dk / 8), c0 = 8 * (e - r * (dk / 8));
+            float acc[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = SD[(int64_t)(r0 + r) * dk + c0 + q];
+            for (int a = 0; a < dk; ++a) {
+                const float cv = Cur[r * (dk + 1) + a];
+                const float4 m0 = *reinterpret_cast<const float4*>(&Ms[a * dk + c0]);
+                const float4 m1 = *reinterpret_cast<const float4*>(&Ms[a * dk + c0 + 4]);
+                acc[0] += cv * m0.x; acc[1] += cv * m0.y; acc[2] += cv * m0.z; acc[3] += cv * m0.w;
+                acc[4] += cv * m1.x; acc[5] += cv * m1.y; acc[6] += cv * m1.z; acc[7] += cv * m1.w;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) Nxt[r * (dk + 1) + c0 + q] = acc[q];
         }
         __syncthreads();
         for (int e = tid; e < kRows * dk; e += kThreads) {
@@ -421,17 +462,23 @@ __global__ void k_copy_state(Problem p) {
 }  // namespace
 
 hipError_t seqpar_finish(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
-                         hipStream_t st) {
+                         bool mfma, hipStream_t st) {
     const int dk = (int)p.dk, dv = (int)p.dv;
     {
         dim3 grid(dv / kRows, (unsigned)p.H, (unsigned)p.B);
-        const size_t lds = sizeof(float) * 2 * kRows * (dk + 1);
+        const size_t lds = sizeof(float) * (2 * kRows * (dk + 1) + (size_t)dk * dk);
+        if (lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chain),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
         prof_begin("k_chain", st);
-        hipLaunchKernelGGL(k_chain, grid, dim3(kThreads), lds, st, p, sp, L, ws);
+        hipLaunchKernelGGL(k_chain, grid, dim3(kThreads), lds, st, p, sp, L, ws, mfma ? 1 : 0);
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (mfma) return mfma_correct(p, sp, ws, L, st);
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
         prof_begin("k_correct", st);
