@@ -102,13 +102,15 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag, float* gates) {
+__global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag, u16x8* pfrag,
+                                                        float* gates) {
     constexpr int LDK = D + 8;
     constexpr int PPR = D / 8;
     constexpr int kBufBytes = (C * LDK * 2 > C * (C + 1) * 4) ? C * LDK * 2 : C * (C + 1) * 4;
     // K (bf16, row stride LDK) during the Gram product, then T (fp32 [C][C+1])
     __shared__ __attribute__((aligned(16))) unsigned char kt_buf[kBufBytes];
     __shared__ float Ms[C][C + 1];
+    __shared__ __attribute__((aligned(16))) unsigned short Qs[C * LDK];
     __shared__ float gsh[C], gpsh[C], bsh[C];
     unsigned short* Ks = reinterpret_cast<unsigned short*>(kt_buf);
     float (*Ts)[C + 1] = reinterpret_cast<float (*)[C + 1]>(kt_buf);
@@ -120,12 +122,18 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     const int nt = (int)((T - t0) < C ? (T - t0) : C);
     const int64_t ch = ((int64_t)b * H + h) * p.NC + i;
     const unsigned short* kin = static_cast<const unsigned short*>(p.k);
+    const unsigned short* qin = static_cast<const unsigned short*>(p.q);
 
     for (int e = tid; e < C * PPR; e += kThreads) {
         const int t = e / PPR, c8 = e - (e / PPR) * PPR;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (t < nt) val = *reinterpret_cast<const uint4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
-        *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = val;
+        uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
+        if (t < nt) {
+            const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
+            kv = *reinterpret_cast<const uint4*>(kin + off);
+            qv = *reinterpret_cast<const uint4*>(qin + off);
+        }
+        *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = kv;
+        *reinterpret_cast<uint4*>(&Qs[t * LDK + c8 * 8]) = qv;
     }
     if (w == 0) {
         float la = 0.f, bt = 0.f;
@@ -166,6 +174,39 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * w + 4 * g4 + r, j = 16 * nb + c16;
             Ms[t][j] = j < t ? bsh[t] * expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
+        }
+    }
+    // gated causal scores P_tj = exp(g_t - g_j) q_t.k_j (j <= t), row block m = w,
+    // as the A-operand fragments of P Delta: blocks (m, c) computed transposed
+    // (rows j, columns t); fragment (m, s) = blocks 2s and 2s + 1, hi and lo
+    {
+        f32x4 PT[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            PT[c] = zero4();
+            if (c > w) continue;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                const u16x8 ka = *reinterpret_cast<const u16x8*>(&Ks[(16 * c + c16) * LDK + 32 * s + 8 * g4]);
+                const u16x8 qb = *reinterpret_cast<const u16x8*>(&Qs[(16 * w + c16) * LDK + 32 * s + 8 * g4]);
+                acc = mfma(ka, qb, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * c + 4 * g4 + r, t = 16 * w + c16;
+                PT[c][r] = j <= t ? acc[r] * expf(gsh[t] - gsh[j]) : 0.f;
+            }
+        }
+        u16x8* pdst = pfrag + ch * kTfragPerChunk;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (s > (w >> 1)) continue;
+            u16x4 h0, l0, h1, l1;
+            split4(PT[2 * s], h0, l0);
+            split4(PT[2 * s + 1], h1, l1);
+            pdst[(tslot(w, s) * 2 + 0) * 64 + l] = cat(h0, h1);
+            pdst[(tslot(w, s) * 2 + 1) * 64 + l] = cat(l0, l1);
         }
     }
     __syncthreads();  // K is dead from here on; its LDS holds T
@@ -237,13 +278,20 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
 // ---------------------------------------------------------------------------
 // stage 2: the chunk loop
 // ---------------------------------------------------------------------------
-// Per chunk i, three phases separated by barriers; only Y -> X -> Delta ->
-// S is on the sequential path, the output of chunk i is finished in phase A
-// of chunk i + 1:
-//   A: Y = K S^T, Z = Q S^T; X = V - diag(gamma') Y -> LDS;  output of i-1
-//   B: Delta = T' X -> LDS (with Delta scaled to the chunk end);  P of chunk i;
-//      gather K^T operands
-//   C: S^T <- gamma_C S^T + K^T Delta-bar; publish S^T; stage chunk i+1 inputs
+// Eight waves, two per SIMD, in two roles on the same token tile m = w % 4:
+//   chain waves (0-3) carry the sequential path Y -> X -> Delta -> S and own
+//     key rows of the state slice S^T (fp32 registers);
+//   output waves (4-7) compute Z = Q S^T, the gated scores P, P Delta, write
+//     the outputs, and stage the next chunks' inputs from HBM into LDS.
+// Per chunk i, three barriers:
+//   A: chain: Y = K S^T, X = V - diag(gamma') Y -> LDS;  output: Z = Q S^T
+//   B: chain: Delta = T' X -> LDS (also Delta scaled to the chunk end);
+//      gathers K^T operands.  output: store chunk i+1 inputs to the other
+//      LDS buffer, start loading chunk i+2
+//   C: chain: S^T <- gamma_C S^T + K^T Delta-bar, publish S^T
+//      output: O = scale (diag(gamma) Z + P Delta) -> HBM
+// The gated scores P of a chunk do not depend on the state; they arrive as
+// A-operand fragments from the preparation kernel, like T'.
 template <int D>
 struct RecShared {
     static constexpr int LDK = D + 8;
@@ -258,14 +306,16 @@ struct RecShared {
     u16x4 DBf[2][2][2][64];
 };
 
+constexpr int kRecThreads = 512;
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLayout L,
-                                                       char* wsb, const u16x8* tfrag,
-                                                       const float* gates, int ntiles,
-                                                       int xcd_remap) {
+__global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, WsLayout L,
+                                                          char* wsb, const u16x8* tfrag,
+                                                          const u16x8* pfrag,
+                                                          const float* gates, int ntiles,
+                                                          int xcd_remap) {
     constexpr int LDK = D + 8;
     constexpr int KS = D / 32;   // k-steps over the key dimension
-    constexpr int TPW = D / 64;  // 16-row key tiles of S^T owned per wave
+    constexpr int TPW = D / 64;  // 16-row key tiles of S^T owned per chain wave
     constexpr int PPR = D / 8;   // 16-byte pieces per K/Q row
     constexpr int KQP = C * PPR / kThreads;
     constexpr int GP = kGateFloats / 4;  // 16-byte pieces of a gate block
@@ -285,84 +335,35 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
     const int64_t H = p.H, T = p.T;
     const int b = (int)(bh / H), h = (int)(bh - (bh / H) * H);
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int w8 = threadIdx.x >> 6;
+    const bool chain = w8 < 4;
+    const int w = w8 & 3;  // token tile
+    const int l = threadIdx.x & 63, g4 = l >> 4, c16 = l & 15;
+    const int otid = threadIdx.x - 256;  // thread index within the output group
     const int nvt = D / 16;
     const bool scaling = x >= nvt;
     if (scaling && gseg == 0) return;
     const int r0 = (scaling ? x - nvt : x) * 16;
     const int i_begin = gseg * sp.per;
     const int i_end = min(p.NC, (gseg + 1) * sp.per);
-    float* corr = reinterpret_cast<float*>(wsb + L.corr);
     const unsigned short* kin = static_cast<const unsigned short*>(p.k);
     const unsigned short* qin = static_cast<const unsigned short*>(p.q);
     const unsigned short* vin = static_cast<const unsigned short*>(p.v);
     const int nks = (w >> 1) + 1;  // k-steps over tokens for rows of tile w
-
-    // state slice S^T[a][v], a-tile tau = w*TPW + u: lane (v = c16, a = 16 tau + 4 g4 + r)
-    f32x4 Sacc[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int a = 16 * (w * TPW + u) + 4 * g4 + r, v = r0 + c16;
-            float s;
-            if (scaling) s = v == a ? 1.f : 0.f;
-            else if (gseg == 0 && p.s0) s = p.s0[(bh * D + v) * D + a];
-            else s = 0.f;
-            Sacc[u][r] = s;
-        }
-    }
-
-    uint4 kreg[KQP], qreg[KQP], vreg, greg;
-    u16x8 tf_n[2][2], tf_c[2][2];
-
-    // loop-invariant bases; a chunk advances every token pointer by C*H*D
-    constexpr int RPP = kThreads / PPR;  // token rows per load pass
-    const int trow = tid / PPR, c8 = tid % PPR;
     const int64_t row_stride = H * D;
     const int64_t chunk_stride = (int64_t)C * row_stride;
-    const int64_t kq_base = (((int64_t)b * T + trow) * H + h) * D + c8 * 8;
-    const int vrow = tid >> 1, vhf = tid & 1;
-    const int64_t v_base = (((int64_t)b * T + vrow) * H + h) * D + r0 + 8 * vhf;
+
+    // ---- chain-wave state: S^T slice, a-tile tau = w*TPW + u, lane (v = c16, a = 16 tau + 4 g4 + r)
+    f32x4 Sacc[TPW];
+    u16x8 tf_n[2][2], tf_c[2][2];
     const u16x8* tf_base = tfrag + bh * p.NC * kTfragPerChunk + l;
-    const float* g_base = gates + bh * p.NC * kGateFloats;
-    auto issue_loads = [&](int i) {
-        const int64_t t0 = (int64_t)i * C;
-        const int nt = (int)((T - t0) < C ? (T - t0) : C);
-        const int64_t cofs = (int64_t)i * chunk_stride;
-#pragma unroll
-        for (int k = 0; k < KQP; ++k) {
-            const bool ok = trow + RPP * k < nt;
-            const int64_t off = kq_base + cofs + (int64_t)(RPP * k) * row_stride;
-            kreg[k] = ok ? *reinterpret_cast<const uint4*>(kin + off) : make_uint4(0, 0, 0, 0);
-            qreg[k] = ok ? *reinterpret_cast<const uint4*>(qin + off) : make_uint4(0, 0, 0, 0);
-        }
-        vreg = make_uint4(0, 0, 0, 0);
-        if (!scaling && tid < 128 && vrow < nt)
-            vreg = *reinterpret_cast<const uint4*>(vin + v_base + cofs);
-        if (tid < GP) greg = reinterpret_cast<const uint4*>(g_base + (int64_t)i * kGateFloats)[tid];
+    auto load_tfrag = [&](int i) {
         const u16x8* tp = tf_base + (int64_t)i * kTfragPerChunk;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl) {
-                if (s < nks) tf_n[s][hl] = tp[(tslot(w, s) * 2 + hl) * 64];
-                else tf_n[s][hl] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_loads = [&](int buf) {
-#pragma unroll
-        for (int k = 0; k < KQP; ++k) {
-            *reinterpret_cast<uint4*>(&sh.K[buf][(trow + RPP * k) * LDK + c8 * 8]) = kreg[k];
-            *reinterpret_cast<uint4*>(&sh.Q[buf][(trow + RPP * k) * LDK + c8 * 8]) = qreg[k];
-        }
-        if (tid < 128) *reinterpret_cast<uint4*>(&sh.V[buf][vrow * 16 + 8 * vhf]) = vreg;
-        if (tid < GP) reinterpret_cast<uint4*>(sh.G[buf])[tid] = greg;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int hl = 0; hl < 2; ++hl) tf_c[s][hl] = tf_n[s][hl];
+            for (int hl = 0; hl < 2; ++hl)
+                tf_n[s][hl] = s < nks ? tp[(tslot(w, s) * 2 + hl) * 64] : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
     };
     auto publish_state = [&]() {
 #pragma unroll
@@ -375,195 +376,230 @@ __global__ __launch_bounds__(kThreads) void k_rec_mfma(Problem p, Split sp, WsLa
         }
     };
 
-    // output of the previous chunk: O = scale (diag(gamma) Z + P Delta)
+    // ---- output-wave state
+    constexpr int RPP = 256 / PPR;  // token rows per load pass of the output group
+    const int trow = otid / PPR, c8 = otid % PPR;
+    const int64_t kq_base = (((int64_t)b * T + trow) * H + h) * D + c8 * 8;
+    const int vrow = otid >> 1, vhf = otid & 1;
+    const int64_t v_base = (((int64_t)b * T + vrow) * H + h) * D + r0 + 8 * vhf;
+    const float* g_base = gates + bh * p.NC * kGateFloats;
+    uint4 kreg[KQP], qreg[KQP], vreg, greg;
+    auto issue_loads = [&](int i) {
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        const int64_t cofs = (int64_t)i * chunk_stride;
+#pragma unroll
+        for (int k = 0; k < KQP; ++k) {
+            const bool ok = trow + RPP * k < nt;
+            const int64_t off = kq_base + cofs + (int64_t)(RPP * k) * row_stride;
+            kreg[k] = ok ? *reinterpret_cast<const uint4*>(kin + off) : make_uint4(0, 0, 0, 0);
+            qreg[k] = ok ? *reinterpret_cast<const uint4*>(qin + off) : make_uint4(0, 0, 0, 0);
+        }
+        vreg = make_uint4(0, 0, 0, 0);
+        if (!scaling && otid < 128 && vrow < nt)
+            vreg = *reinterpret_cast<const uint4*>(vin + v_base + cofs);
+        if (otid < GP) greg = reinterpret_cast<const uint4*>(g_base + (int64_t)i * kGateFloats)[otid];
+    };
+    auto store_loads = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < KQP; ++k) {
+            *reinterpret_cast<uint4*>(&sh.K[buf][(trow + RPP * k) * LDK + c8 * 8]) = kreg[k];
+            *reinterpret_cast<uint4*>(&sh.Q[buf][(trow + RPP * k) * LDK + c8 * 8]) = qreg[k];
+        }
+        if (otid < 128) *reinterpret_cast<uint4*>(&sh.V[buf][vrow * 16 + 8 * vhf]) = vreg;
+        if (otid < GP) reinterpret_cast<uint4*>(sh.G[buf])[otid] = greg;
+    };
+    float* corr = reinterpret_cast<float*>(wsb + L.corr);
     const int64_t out_base = (((int64_t)b * T + 16 * w + 4 * g4) * H + h) * D + r0 + c16;
     float* corr_base = corr + bh * p.NC * C * D + (int64_t)(16 * w + 4 * g4) * D + r0 + c16;
-    f32x4 Zp = zero4(), gamP = zero4();
-    u16x8 pah[2], pal[2];
-    int64_t tp0 = 0;
-    int ntp = 0, ip = 0;
-    auto emit_output = [&]() {
+    const u16x8* pf_base = pfrag + bh * p.NC * kTfragPerChunk + l;
+    u16x8 pf[2][2];
+    auto load_pfrag = [&](int i) {
+        const u16x8* pp = pf_base + (int64_t)i * kTfragPerChunk;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+                pf[s][hl] = s < nks ? pp[(tslot(w, s) * 2 + hl) * 64] : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    };
+    auto emit_output = [&](int i, const f32x4& Zc, const f32x4& gam) {
         f32x4 O1 = zero4(), O2 = zero4(), O3 = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             if (s >= nks) continue;
+            const u16x8 pah = pf[s][0];
+            const u16x8 pal = pf[s][1];
             const u16x8 dh = cat(sh.Df[s][0][0][l], sh.Df[s][1][0][l]);
             const u16x8 dlo = cat(sh.Df[s][0][1][l], sh.Df[s][1][1][l]);
-            O1 = mfma(pah[s], dh, O1);
-            O2 = mfma(pah[s], dlo, O2);
-            O3 = mfma(pal[s], dh, O3);
+            O1 = mfma(pah, dh, O1);
+            O2 = mfma(pah, dlo, O2);
+            O3 = mfma(pal, dh, O3);
         }
         if (scaling) {
-            float* dst = corr_base + (int64_t)ip * C * D;
+            float* dst = corr_base + (int64_t)i * C * D;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                dst[r * D] = p.scale * (gamP[r] * Zp[r] + O1[r] + O2[r] + O3[r]);
+                dst[r * D] = p.scale * (gam[r] * Zc[r] + O1[r] + O2[r] + O3[r]);
         } else {
-            float* dst = p.out + out_base + tp0 * row_stride;
+            const int64_t t0 = (int64_t)i * C;
+            const int nt = (int)((T - t0) < C ? (T - t0) : C);
+            float* dst = p.out + out_base + t0 * row_stride;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (16 * w + 4 * g4 + r < ntp)
-                    dst[r * row_stride] = p.scale * (gamP[r] * Zp[r] + O1[r] + O2[r] + O3[r]);
+                if (16 * w + 4 * g4 + r < nt)
+                    dst[r * row_stride] = p.scale * (gam[r] * Zc[r] + O1[r] + O2[r] + O3[r]);
         }
     };
 
-    if (i_begin < i_end) {
+    // ---- prologue
+    if (chain) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int a = 16 * (w * TPW + u) + 4 * g4 + r, v = r0 + c16;
+                float sv;
+                if (scaling) sv = v == a ? 1.f : 0.f;
+                else if (gseg == 0 && p.s0) sv = p.s0[(bh * D + v) * D + a];
+                else sv = 0.f;
+                Sacc[u][r] = sv;
+            }
+        }
+        publish_state();
+        if (i_begin < i_end) {
+            load_tfrag(i_begin);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl) tf_c[s][hl] = tf_n[s][hl];
+            if (i_begin + 1 < i_end) load_tfrag(i_begin + 1);
+        }
+    } else if (i_begin < i_end) {
         issue_loads(i_begin);
         store_loads(0);
         if (i_begin + 1 < i_end) issue_loads(i_begin + 1);
     }
-    publish_state();
 
     for (int i = i_begin; i < i_end; ++i) {
         const int cur = (i - i_begin) & 1;
-        const int64_t t0 = (int64_t)i * C;
-        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        const float* G = sh.G[cur];
         __syncthreads();  // B1: state fragments and chunk i inputs visible
 
-        // ---- phase A
-        const float* G = sh.G[cur];
-        const f32x4 gam = *reinterpret_cast<const f32x4*>(&G[16 * w + 4 * g4]);
-        const f32x4 gamp = *reinterpret_cast<const f32x4*>(&G[64 + 16 * w + 4 * g4]);
-        f32x4 Y = zero4(), Y2 = zero4(), Z = zero4(), Z2 = zero4();
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const u16x8 shi = cat(sh.Sf[s][0][0][l], sh.Sf[s][1][0][l]);
-            const u16x8 slo = cat(sh.Sf[s][0][1][l], sh.Sf[s][1][1][l]);
-            const unsigned short* kr = &sh.K[cur][(16 * w + c16) * LDK + 32 * s + 4 * g4];
-            const unsigned short* qr = &sh.Q[cur][(16 * w + c16) * LDK + 32 * s + 4 * g4];
-            const u16x8 ka = cat(*reinterpret_cast<const u16x4*>(kr), *reinterpret_cast<const u16x4*>(kr + 16));
-            const u16x8 qa = cat(*reinterpret_cast<const u16x4*>(qr), *reinterpret_cast<const u16x4*>(qr + 16));
-            Y = mfma(ka, shi, Y);
-            Y2 = mfma(ka, slo, Y2);
-            Z = mfma(qa, shi, Z);
-            Z2 = mfma(qa, slo, Z2);
-        }
-        Y += Y2;
-        f32x4 X;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * w + 4 * g4 + r;
-            const float vv = scaling ? 0.f : gdn_bf16_to_f32(sh.V[cur][t * 16 + c16]);
-            X[r] = vv - gamp[r] * Y[r];
-        }
+        // ---------------- phase A
+        f32x4 Zc = zero4(), Xc = zero4();
         {
+            const unsigned short* src = chain ? sh.K[cur] : sh.Q[cur];
+            f32x4 A1 = zero4(), A2 = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u16x8 shi = cat(sh.Sf[s][0][0][l], sh.Sf[s][1][0][l]);
+                const u16x8 slo = cat(sh.Sf[s][0][1][l], sh.Sf[s][1][1][l]);
+                const unsigned short* rr = &src[(16 * w + c16) * LDK + 32 * s + 4 * g4];
+                const u16x8 ra = cat(*reinterpret_cast<const u16x4*>(rr), *reinterpret_cast<const u16x4*>(rr + 16));
+                A1 = mfma(ra, shi, A1);
+                A2 = mfma(ra, slo, A2);
+            }
+            if (chain) Xc = A1 + A2;
+            else Zc = A1 + A2;
+        }
+        if (!chain) load_pfrag(i);
+        if (chain) {
+            // X = V - diag(gamma') Y
+            const f32x4 gamp = *reinterpret_cast<const f32x4*>(&G[64 + 16 * w + 4 * g4]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float vv = scaling ? 0.f : gdn_bf16_to_f32(sh.V[cur][(16 * w + 4 * g4 + r) * 16 + c16]);
+                Xc[r] = vv - gamp[r] * Xc[r];
+            }
             u16x4 hi, lo;
-            split4(X, hi, lo);
+            split4(Xc, hi, lo);
             sh.Xf[w >> 1][w & 1][0][l] = hi;
             sh.Xf[w >> 1][w & 1][1][l] = lo;
         }
-        if (i > i_begin) emit_output();
         __syncthreads();  // B2
 
-        // ---- phase B
-        f32x4 Dl = zero4(), Dl2 = zero4(), Dl3 = zero4();
+        // ---------------- phase B
+        u16x8 kt[TPW][2];
+        if (chain) {
+            f32x4 D1 = zero4(), D2 = zero4(), D3 = zero4();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (s >= nks) continue;
-            const u16x8 xh = cat(sh.Xf[s][0][0][l], sh.Xf[s][1][0][l]);
-            const u16x8 xl = cat(sh.Xf[s][0][1][l], sh.Xf[s][1][1][l]);
-            Dl = mfma(tf_c[s][0], xh, Dl);
-            Dl2 = mfma(tf_c[s][0], xl, Dl2);
-            Dl3 = mfma(tf_c[s][1], xh, Dl3);
-        }
-        Dl += Dl2 + Dl3;
-        {
+            for (int s = 0; s < 2; ++s) {
+                if (s >= nks) continue;
+                const u16x8 xh = cat(sh.Xf[s][0][0][l], sh.Xf[s][1][0][l]);
+                const u16x8 xl = cat(sh.Xf[s][0][1][l], sh.Xf[s][1][1][l]);
+                D1 = mfma(tf_c[s][0], xh, D1);
+                D2 = mfma(tf_c[s][0], xl, D2);
+                D3 = mfma(tf_c[s][1], xh, D3);
+            }
+            D1 += D2 + D3;
             const f32x4 rat = *reinterpret_cast<const f32x4*>(&G[128 + 16 * w + 4 * g4]);
             u16x4 hi, lo;
-            split4(Dl, hi, lo);
+            split4(D1, hi, lo);
             sh.Df[w >> 1][w & 1][0][l] = hi;
             sh.Df[w >> 1][w & 1][1][l] = lo;
-            split4(rat * Dl, hi, lo);
+            split4(rat * D1, hi, lo);
             sh.DBf[w >> 1][w & 1][0][l] = hi;
             sh.DBf[w >> 1][w & 1][1][l] = lo;
-        }
-        // gated causal scores of chunk i, transposed blocks: rows j (block c),
-        // columns t (block w); factor exp(g_t - g_j) for j <= t
-        {
-            const float gcol = G[192 + 16 * w + c16];
-            f32x4 PT[4];
+            // K^T operands for the state update: rows a = 16 tau + c16, k-slots j
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                PT[c] = zero4();
-                if (c > w) continue;
-                f32x4 acc = zero4();
+            for (int u = 0; u < TPW; ++u)
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.K[cur][(16 * c + c16) * LDK + 32 * s + 8 * g4]);
-                    const u16x8 qb = *reinterpret_cast<const u16x8*>(&sh.Q[cur][(16 * w + c16) * LDK + 32 * s + 8 * g4]);
-                    acc = mfma(ka, qb, acc);
-                }
-                const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[192 + 16 * c + 4 * g4]);
+                for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * c + 4 * g4 + r, t = 16 * w + c16;
-                    PT[c][r] = j <= t ? acc[r] * __expf(gcol - gj[r]) : 0.f;
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u16x4 h0, l0, h1, l1;
-                split4(PT[2 * s], h0, l0);
-                split4(PT[2 * s + 1], h1, l1);
-                pah[s] = cat(h0, h1);
-                pal[s] = cat(l0, l1);
-            }
-        }
-        // K^T operands for the state update: rows a = 16 tau + c16, k-slots j
-        u16x8 kt[TPW][2];
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-                    kt[u][s][e] = sh.K[cur][j * LDK + 16 * (w * TPW + u) + c16];
-                }
-            }
-        }
-        __syncthreads();  // B3
-
-        // ---- phase C
-        const float gamC = G[256];
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            f32x4 acc = gamC * Sacc[u], acc2 = zero4();
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const u16x8 dbh = cat(sh.DBf[s][0][0][l], sh.DBf[s][1][0][l]);
-                const u16x8 dbl = cat(sh.DBf[s][0][1][l], sh.DBf[s][1][1][l]);
-                acc = mfma(kt[u][s], dbh, acc);
-                acc2 = mfma(kt[u][s], dbl, acc2);
-            }
-            Sacc[u] = acc + acc2;
-        }
-        publish_state();
-        Zp = Z + Z2;
-        gamP = gam;
-        tp0 = t0;
-        ntp = nt;
-        ip = i;
-        // next chunk's inputs: prefetched registers -> the other LDS buffer
-        if (i + 1 < i_end) {
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
+                        kt[u][s][e] = sh.K[cur][j * LDK + 16 * (w * TPW + u) + c16];
+                    }
+        } else if (i + 1 < i_end) {
+            // the other LDS buffer held chunk i-1, finished before B1: stage
+            // chunk i+1 there, then start loading chunk i+2
             store_loads(cur ^ 1);
             if (i + 2 < i_end) issue_loads(i + 2);
         }
-    }
-    if (i_begin < i_end) emit_output();
+        __syncthreads();  // B3
 
-    float* dst;
-    if (scaling)
-        dst = reinterpret_cast<float*>(wsb + L.mend) + (bh * sp.G + gseg) * D * D;
-    else if (sp.G == 1)
-        dst = p.s_out ? p.s_out + bh * D * D : nullptr;
-    else
-        dst = reinterpret_cast<float*>(wsb + L.sdend) + (bh * sp.G + gseg) * D * D;
-    if (dst) {
+        // ---------------- phase C
+        if (chain) {
+            const float gamC = G[256];
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int a0 = 16 * (w * TPW + u) + 4 * g4;
-            *reinterpret_cast<f32x4*>(&dst[(int64_t)(r0 + c16) * D + a0]) = Sacc[u];
+            for (int u = 0; u < TPW; ++u) {
+                f32x4 acc = gamC * Sacc[u], acc2 = zero4();
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const u16x8 dbh = cat(sh.DBf[s][0][0][l], sh.DBf[s][1][0][l]);
+                    const u16x8 dbl = cat(sh.DBf[s][0][1][l], sh.DBf[s][1][1][l]);
+                    acc = mfma(kt[u][s], dbh, acc);
+                    acc2 = mfma(kt[u][s], dbl, acc2);
+                }
+                Sacc[u] = acc + acc2;
+            }
+            publish_state();
+            if (i + 1 < i_end) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl) tf_c[s][hl] = tf_n[s][hl];
+                if (i + 2 < i_end) load_tfrag(i + 2);
+            }
+        } else {
+            emit_output(i, Zc, *reinterpret_cast<const f32x4*>(&G[16 * w + 4 * g4]));
+        }
+    }
+
+    if (chain) {
+        float* dst;
+        if (scaling)
+            dst = reinterpret_cast<float*>(wsb + L.mend) + (bh * sp.G + gseg) * D * D;
+        else if (sp.G == 1)
+            dst = p.s_out ? p.s_out + bh * D * D : nullptr;
+        else
+            dst = reinterpret_cast<float*>(wsb + L.sdend) + (bh * sp.G + gseg) * D * D;
+        if (dst) {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int a0 = 16 * (w * TPW + u) + 4 * g4;
+                *reinterpret_cast<f32x4*>(&dst[(int64_t)(r0 + c16) * D + a0]) = Sacc[u];
+            }
         }
     }
 }
@@ -641,11 +677,13 @@ template <int D>
 hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L, hipStream_t st) {
     u16x8* tfrag = reinterpret_cast<u16x8*>(ws + L.prep);
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
-    float* gates = reinterpret_cast<float*>(ws + L.prep + align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)));
+    const size_t fbytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8));
+    u16x8* pfrag = reinterpret_cast<u16x8*>(ws + L.prep + fbytes);
+    float* gates = reinterpret_cast<float*>(ws + L.prep + 2 * fbytes);
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
         prof_begin("k_prep_mfma", st);
-        hipLaunchKernelGGL(k_prep_mfma<D>, grid, dim3(kThreads), 0, st, p, tfrag, gates);
+        hipLaunchKernelGGL(k_prep_mfma<D>, grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -656,8 +694,8 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
         const int64_t nwork = heads * ntiles;
         const int remap = (heads % 8 == 0) ? 1 : 0;
         prof_begin("k_rec_mfma", st);
-        hipLaunchKernelGGL(k_rec_mfma<D>, dim3((unsigned)nwork), dim3(kThreads), 0, st, p, sp, L,
-                           ws, tfrag, gates, ntiles, remap);
+        hipLaunchKernelGGL(k_rec_mfma<D>, dim3((unsigned)nwork), dim3(kRecThreads), 0, st, p, sp, L,
+                           ws, tfrag, pfrag, gates, ntiles, remap);
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -677,7 +715,7 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
     WsLayout L;
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
     L.prep = 0;
-    L.prep_bytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
+    L.prep_bytes = 2 * align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
                    align256((size_t)nch * kGateFloats * sizeof(float));
     size_t off = L.prep_bytes;
     if (sp.G > 1) {
