@@ -1,5 +1,5 @@
 // MFMA kernels of the chunkwise gated delta rule (gfx950, bf16 inputs,
-// dk = dv = D in {64, 128}, chunk C = 64, scalar gate).
+// dk = dv = D in {64, 128}, chunk C = 64, scalar or per-key-channel gate).
 //
 // Chunk algebra as in the vector-ALU family (gdn_valu.hip): per chunk with
 // chunk-local log-gate prefix g_t (gamma_t = exp g_t), prediction prefix g'_t
@@ -40,6 +40,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;
 constexpr int kThreads = 256;
@@ -101,7 +102,14 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+// Per-key-channel gates (CH = 1): the gate is a vector per token and the
+// chunk-local log prefix g[t][a] is a C x D table (stored for the chunk loop).
+// Intra-chunk ratios exp(g_t - g_j) then differ per channel and enter the MFMA
+// operands, anchored at 16-token block boundaries (the secondary chunking of
+// the GLA gating section): for key block c below row block m the anchor is the
+// last token p of block c, so q_t e^{g_t - g_p} and k_j e^{g_p - g_j} are both
+// at most one; on diagonal blocks p is the token before the block.
+template <int D, int CH>
 __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag, u16x8* pfrag,
                                                         float* gates) {
     constexpr int LDK = D + 8;
@@ -112,6 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     __shared__ float Ms[C][C + 1];
     __shared__ __attribute__((aligned(16))) unsigned short Qs[C * LDK];
     __shared__ float gsh[C], gpsh[C], bsh[C];
+    __shared__ __attribute__((aligned(16))) float gt[CH ? C : 1][CH ? D : 1];  // channel log prefix
     unsigned short* Ks = reinterpret_cast<unsigned short*>(kt_buf);
     float (*Ts)[C + 1] = reinterpret_cast<float (*)[C + 1]>(kt_buf);
 
@@ -135,67 +144,195 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
         *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = kv;
         *reinterpret_cast<uint4*>(&Qs[t * LDK + c8 * 8]) = qv;
     }
-    if (w == 0) {
-        float la = 0.f, bt = 0.f;
-        if (l < nt) {
-            const int64_t row = ((int64_t)b * T + t0 + l) * H + h;
-            la = logf(p.alpha[row]);
-            bt = p.beta[row];
+    if constexpr (!CH) {
+        if (w == 0) {
+            float la = 0.f, bt = 0.f;
+            if (l < nt) {
+                const int64_t row = ((int64_t)b * T + t0 + l) * H + h;
+                la = logf(p.alpha[row]);
+                bt = p.beta[row];
+            }
+            const float gv = wave_incl_scan(la, l);
+            float gprev = __shfl_up(gv, 1, 64);
+            if (l == 0) gprev = 0.f;
+            const float gpv = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
+            const float gC = __shfl(gv, 63, 64);
+            gsh[l] = gv;
+            gpsh[l] = gpv;
+            bsh[l] = bt;
+            float* gb = gates + ch * kGateFloats;
+            gb[l] = expf(gv);
+            gb[64 + l] = expf(gpv);
+            gb[128 + l] = expf(gC - gv);
+            gb[192 + l] = gv;
+            if (l == 0) gb[256] = expf(gC);
         }
-        const float gv = wave_incl_scan(la, l);
-        float gprev = __shfl_up(gv, 1, 64);
-        if (l == 0) gprev = 0.f;
-        const float gpv = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
-        const float gC = __shfl(gv, 63, 64);
-        gsh[l] = gv;
-        gpsh[l] = gpv;
-        bsh[l] = bt;
-        float* gb = gates + ch * kGateFloats;
-        gb[l] = expf(gv);
-        gb[64 + l] = expf(gpv);
-        gb[128 + l] = expf(gC - gv);
-        gb[192 + l] = gv;
-        if (l == 0) gb[256] = expf(gC);
+        __syncthreads();
+    } else {
+        if (w == 0) bsh[l] = l < nt ? p.beta[((int64_t)b * T + t0 + l) * H + h] : 0.f;
+        // log gates (zero on padding tokens), then the prefix down each channel
+        for (int e = tid; e < C * PPR * 2; e += kThreads) {
+            const int t = e / (PPR * 2), a4 = e - t * (PPR * 2);
+            float4 la = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < nt) {
+                const float4 av = *reinterpret_cast<const float4*>(
+                    p.alpha + (((int64_t)b * T + t0 + t) * H + h) * D + 4 * a4);
+                la = make_float4(logf(av.x), logf(av.y), logf(av.z), logf(av.w));
+            }
+            *reinterpret_cast<float4*>(&gt[t][4 * a4]) = la;
+        }
+        __syncthreads();
+        float* gdst = gates + ch * (int64_t)C * D;
+        for (int a = tid; a < D; a += kThreads) {
+            float g = 0.f;
+            for (int t = 0; t < C; ++t) {
+                g += gt[t][a];
+                gt[t][a] = g;
+                gdst[t * D + a] = g;
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // A_tj = beta_t exp(g'_t - g_j) k_t.k_j for j < t: row block w, column blocks <= w
+    if constexpr (!CH) {
+        // A_tj = beta_t exp(g'_t - g_j) k_t.k_j for j < t: row block w, column blocks <= w
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        if (nb > w) continue;
-        f32x4 acc = zero4();
+        for (int nb = 0; nb < 4; ++nb) {
+            if (nb > w) continue;
+            f32x4 acc = zero4();
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            const u16x8 a = *reinterpret_cast<const u16x8*>(&Ks[(16 * w + c16) * LDK + 32 * s + 8 * g4]);
-            const u16x8 bb = *reinterpret_cast<const u16x8*>(&Ks[(16 * nb + c16) * LDK + 32 * s + 8 * g4]);
-            acc = mfma(a, bb, acc);
+            for (int s = 0; s < D / 32; ++s) {
+                const u16x8 a = *reinterpret_cast<const u16x8*>(&Ks[(16 * w + c16) * LDK + 32 * s + 8 * g4]);
+                const u16x8 bb = *reinterpret_cast<const u16x8*>(&Ks[(16 * nb + c16) * LDK + 32 * s + 8 * g4]);
+                acc = mfma(a, bb, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * w + 4 * g4 + r, j = 16 * nb + c16;
+                Ms[t][j] = j < t ? bsh[t] * expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
+            }
         }
+        // gated causal scores P_tj = exp(g_t - g_j) q_t.k_j (j <= t), row block m = w,
+        // as the A-operand fragments of P Delta: blocks (m, c) computed transposed
+        // (rows j, columns t); fragment (m, s) = blocks 2s and 2s + 1, hi and lo
+        {
+            f32x4 PT[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * w + 4 * g4 + r, j = 16 * nb + c16;
-            Ms[t][j] = j < t ? bsh[t] * expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
+            for (int c = 0; c < 4; ++c) {
+                PT[c] = zero4();
+                if (c > w) continue;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s < D / 32; ++s) {
+                    const u16x8 ka = *reinterpret_cast<const u16x8*>(&Ks[(16 * c + c16) * LDK + 32 * s + 8 * g4]);
+                    const u16x8 qb = *reinterpret_cast<const u16x8*>(&Qs[(16 * w + c16) * LDK + 32 * s + 8 * g4]);
+                    acc = mfma(ka, qb, acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * c + 4 * g4 + r, t = 16 * w + c16;
+                    PT[c][r] = j <= t ? acc[r] * expf(gsh[t] - gsh[j]) : 0.f;
+                }
+            }
+            u16x8* pdst = pfrag + ch * kTfragPerChunk;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (s > (w >> 1)) continue;
+                u16x4 h0, l0, h1, l1;
+                split4(PT[2 * s], h0, l0);
+                split4(PT[2 * s + 1], h1, l1);
+                pdst[(tslot(w, s) * 2 + 0) * 64 + l] = cat(h0, h1);
+                pdst[(tslot(w, s) * 2 + 1) * 64 + l] = cat(l0, l1);
+            }
         }
-    }
-    // gated causal scores P_tj = exp(g_t - g_j) q_t.k_j (j <= t), row block m = w,
-    // as the A-operand fragments of P Delta: blocks (m, c) computed transposed
-    // (rows j, columns t); fragment (m, s) = blocks 2s and 2s + 1, hi and lo
-    {
+
+    } else {
+        // L_tj = sum_a k_ta k_ja e^{g'_ta - g_ja} (j < t) and P_tj = sum_a q_ta k_ja
+        // e^{g_ta - g_ja} (j <= t) for row block m = w, key blocks c <= w, with
+        // gated operands split hi/lo; accumulators are transposed (rows j, cols t)
+        const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
+        const int t = 16 * w + c16;
         f32x4 PT[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             PT[c] = zero4();
             if (c > w) continue;
-            f32x4 acc = zero4();
+            const int pa = c < w ? 16 * c + 15 : 16 * c - 1;  // anchor token
+            const int j = 16 * c + c16;
+            f32x4 aL = zero4(), aP = zero4();
+            // On a diagonal block the key factor e^{g_p - g_j} grows with the
+            // decay across the block; past e^{64} on some channel (gates far
+            // below any trained range) the block is summed directly instead.
+            bool direct = false;
+            if (c == w) {
+                float span = 0.f;
+                for (int a = l; a < D; a += 64)
+                    span = fmaxf(span, (pa >= 0 ? gt[pa][a] : 0.f) - gt[16 * c + 15][a]);
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+                direct = span > 64.f;
+            }
+            if (direct) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int jj = 16 * c + 4 * g4 + r;
+                    float sp = 0.f, sl = 0.f;
+                    if (jj <= t) {
+                        for (int a = 0; a < D; ++a) {
+                            const float kj = gdn_bf16_to_f32(Ks[jj * LDK + a]);
+                            const float gpr = ptd ? (t > 0 ? gt[t - 1][a] : 0.f) : gt[t][a];
+                            sp += gdn_bf16_to_f32(Qs[t * LDK + a]) * kj * expf(gt[t][a] - gt[jj][a]);
+                            sl += gdn_bf16_to_f32(Ks[t * LDK + a]) * kj * expf(gpr - gt[jj][a]);
+                        }
+                    }
+                    aP[r] = sp;
+                    aL[r] = sl;
+                }
+            }
+            if (!direct) {
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
-                const u16x8 ka = *reinterpret_cast<const u16x8*>(&Ks[(16 * c + c16) * LDK + 32 * s + 8 * g4]);
-                const u16x8 qb = *reinterpret_cast<const u16x8*>(&Qs[(16 * w + c16) * LDK + 32 * s + 8 * g4]);
-                acc = mfma(ka, qb, acc);
+                const int a0 = 32 * s + 8 * g4;
+                const u16x8 kj = *reinterpret_cast<const u16x8*>(&Ks[j * LDK + a0]);
+                const u16x8 kt_ = *reinterpret_cast<const u16x8*>(&Ks[t * LDK + a0]);
+                const u16x8 qt = *reinterpret_cast<const u16x8*>(&Qs[t * LDK + a0]);
+                uint32_t ah[4], al[4], ph[4], pl[4], lh[4], ll[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float fa[2], fp[2], fl[2];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int a = a0 + e + q;
+                        const float gp = pa >= 0 ? gt[pa][a] : 0.f;
+                        const float gpr = ptd ? (t > 0 ? gt[t - 1][a] : 0.f) : gt[t][a];
+                        fa[q] = gdn_bf16_to_f32(kj[e + q]) * expf(gp - gt[j][a]);
+                        fp[q] = gdn_bf16_to_f32(qt[e + q]) * expf(gt[t][a] - gp);
+                        fl[q] = gdn_bf16_to_f32(kt_[e + q]) * expf(gpr - gp);
+                    }
+                    split2(fa[0], fa[1], ah[e >> 1], al[e >> 1]);
+                    split2(fp[0], fp[1], ph[e >> 1], pl[e >> 1]);
+                    split2(fl[0], fl[1], lh[e >> 1], ll[e >> 1]);
+                }
+                const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
+                const u16x8 Al = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
+                const u16x8 Ph = __builtin_bit_cast(u16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
+                const u16x8 Pl = __builtin_bit_cast(u16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
+                const u16x8 Lh = __builtin_bit_cast(u16x8, uint4{lh[0], lh[1], lh[2], lh[3]});
+                const u16x8 Ll = __builtin_bit_cast(u16x8, uint4{ll[0], ll[1], ll[2], ll[3]});
+                aP = mfma(Ah, Ph, aP);
+                aP = mfma(Ah, Pl, aP);
+                aP = mfma(Al, Ph, aP);
+                aL = mfma(Ah, Lh, aL);
+                aL = mfma(Ah, Ll, aL);
+                aL = mfma(Al, Lh, aL);
             }
+            }
+            // accumulator lane: column t = 16w + c16, rows j = 16c + 4g4 + r
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int j = 16 * c + 4 * g4 + r, t = 16 * w + c16;
-                PT[c][r] = j <= t ? acc[r] * expf(gsh[t] - gsh[j]) : 0.f;
+                const int jj = 16 * c + 4 * g4 + r;
+                Ms[t][jj] = jj < t ? bsh[t] * aL[r] : 0.f;
+                PT[c][r] = jj <= t ? aP[r] : 0.f;
             }
         }
         u16x8* pdst = pfrag + ch * kTfragPerChunk;
@@ -292,14 +429,14 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
 //      output: O = scale (diag(gamma) Z + P Delta) -> HBM
 // The gated scores P of a chunk do not depend on the state; they arrive as
 // A-operand fragments from the preparation kernel, like T'.
-template <int D>
+template <int D, int CH>
 struct RecShared {
     static constexpr int LDK = D + 8;
     static constexpr int KS = D / 32;
     unsigned short K[2][C * LDK];
     unsigned short Q[2][C * LDK];
     unsigned short V[2][C * 16];
-    float G[2][kGateFloats];
+    float G[2][CH ? C * D : kGateFloats];  // gate block, or the C x D log-prefix table
     u16x4 Sf[KS][2][2][64];  // S^T fragments: [k-step][tile half][hi/lo][lane]
     u16x4 Xf[2][2][2][64];
     u16x4 Df[2][2][2][64];
@@ -307,7 +444,11 @@ struct RecShared {
 };
 
 constexpr int kRecThreads = 512;
-template <int D>
+// CH = 1 (per-key-channel gates): Y and Z take the gated operands
+// K (.) e^{g'} and Q (.) e^{g}, the state update takes K (.) e^{g_C - g} (all
+// split hi/lo, three MFMAs per product) and the state decays column-wise by
+// e^{g_C}; no row factors remain.
+template <int D, int CH>
 __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, WsLayout L,
                                                           char* wsb, const u16x8* tfrag,
                                                           const u16x8* pfrag,
@@ -318,8 +459,10 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
     constexpr int TPW = D / 64;  // 16-row key tiles of S^T owned per chain wave
     constexpr int PPR = D / 8;   // 16-byte pieces per K/Q row
     constexpr int KQP = C * PPR / kThreads;
-    constexpr int GP = kGateFloats / 4;  // 16-byte pieces of a gate block
-    __shared__ __attribute__((aligned(16))) RecShared<D> sh;
+    constexpr int GP = CH ? C * D / 4 : kGateFloats / 4;  // 16-byte pieces of gate data
+    constexpr int GPT = (GP + 255) / 256;                  // pieces per output thread
+    __shared__ __attribute__((aligned(16))) RecShared<D, CH> sh;
+    const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
 
     // work decode; with xcd_remap the ntiles slices of one (head, segment)
     // land on one XCD (workgroups are dealt to the 8 XCDs round-robin)
@@ -382,8 +525,10 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
     const int64_t kq_base = (((int64_t)b * T + trow) * H + h) * D + c8 * 8;
     const int vrow = otid >> 1, vhf = otid & 1;
     const int64_t v_base = (((int64_t)b * T + vrow) * H + h) * D + r0 + 8 * vhf;
-    const float* g_base = gates + bh * p.NC * kGateFloats;
-    uint4 kreg[KQP], qreg[KQP], vreg, greg;
+    constexpr int GSTRIDE = CH ? C * D : kGateFloats;  // gate floats per chunk-head
+    const float* g_base = gates + bh * p.NC * GSTRIDE;
+    uint4 kreg[KQP], qreg[KQP], vreg;
+    u32x4 greg[GPT];
     auto issue_loads = [&](int i) {
         const int64_t t0 = (int64_t)i * C;
         const int nt = (int)((T - t0) < C ? (T - t0) : C);
@@ -398,7 +543,10 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
         vreg = make_uint4(0, 0, 0, 0);
         if (!scaling && otid < 128 && vrow < nt)
             vreg = *reinterpret_cast<const uint4*>(vin + v_base + cofs);
-        if (otid < GP) greg = reinterpret_cast<const uint4*>(g_base + (int64_t)i * kGateFloats)[otid];
+        const u32x4* gsrc = reinterpret_cast<const u32x4*>(g_base + (int64_t)i * GSTRIDE) + otid;
+#pragma unroll
+        for (int k = 0; k < GPT; ++k)
+            if (GP % 256 == 0 || otid + 256 * k < GP) greg[k] = gsrc[256 * k];
     };
     auto store_loads = [&](int buf) {
 #pragma unroll
@@ -407,7 +555,10 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
             *reinterpret_cast<uint4*>(&sh.Q[buf][(trow + RPP * k) * LDK + c8 * 8]) = qreg[k];
         }
         if (otid < 128) *reinterpret_cast<uint4*>(&sh.V[buf][vrow * 16 + 8 * vhf]) = vreg;
-        if (otid < GP) reinterpret_cast<uint4*>(sh.G[buf])[otid] = greg;
+        u32x4* gdst = reinterpret_cast<u32x4*>(sh.G[buf]) + otid;
+#pragma unroll
+        for (int k = 0; k < GPT; ++k)
+            if (GP % 256 == 0 || otid + 256 * k < GP) gdst[256 * k] = greg[k];
     };
     float* corr = reinterpret_cast<float*>(wsb + L.corr);
     const int64_t out_base = (((int64_t)b * T + 16 * w + 4 * g4) * H + h) * D + r0 + c16;
@@ -451,8 +602,43 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
         }
     };
 
-    // ---- prologue
+    // channel gate: rows of src scaled by e^{g[grow]} (grow = -1: by one),
+    // split hi/lo, times S^T (hi/lo): 16 x 16 tile of rows 16w.. of the chunk
+    auto gated_rows = [&](const unsigned short* src, const float* G, int grow) {
+        f32x4 A1 = zero4(), A2 = zero4(), A3 = zero4();
+        const int t = 16 * w + c16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const u16x8 shi = cat(sh.Sf[s][0][0][l], sh.Sf[s][1][0][l]);
+            const u16x8 slo = cat(sh.Sf[s][0][1][l], sh.Sf[s][1][1][l]);
+            const unsigned short* rr = &src[t * LDK + 32 * s + 4 * g4];
+            const u16x8 raw = cat(*reinterpret_cast<const u16x4*>(rr), *reinterpret_cast<const u16x4*>(rr + 16));
+            f32x4 g0 = zero4(), g1 = zero4();
+            if (grow >= 0) {
+                g0 = *reinterpret_cast<const f32x4*>(&G[grow * D + 32 * s + 4 * g4]);
+                g1 = *reinterpret_cast<const f32x4*>(&G[grow * D + 32 * s + 16 + 4 * g4]);
+            }
+            uint32_t ah[4], al[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float x0 = gdn_bf16_to_f32(raw[e]) * __expf(e < 4 ? g0[e] : g1[e - 4]);
+                const float x1 = gdn_bf16_to_f32(raw[e + 1]) * __expf(e < 4 ? g0[e + 1] : g1[e - 3]);
+                split2(x0, x1, ah[e >> 1], al[e >> 1]);
+            }
+            const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
+            const u16x8 Al = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
+            A1 = mfma(Ah, shi, A1);
+            A2 = mfma(Ah, slo, A2);
+            A3 = mfma(Al, shi, A3);
+        }
+        return A1 + A2 + A3;
+    };
+
+    // The two roles run separate loops with the same barrier sequence (three
+    // per chunk), so neither role's loop-carried registers stay live in the
+    // other's code.
     if (chain) {
+        // ---- chain prologue
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
 #pragma unroll
@@ -474,104 +660,122 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                 for (int hl = 0; hl < 2; ++hl) tf_c[s][hl] = tf_n[s][hl];
             if (i_begin + 1 < i_end) load_tfrag(i_begin + 1);
         }
-    } else if (i_begin < i_end) {
-        issue_loads(i_begin);
-        store_loads(0);
-        if (i_begin + 1 < i_end) issue_loads(i_begin + 1);
-    }
 
-    for (int i = i_begin; i < i_end; ++i) {
-        const int cur = (i - i_begin) & 1;
-        const float* G = sh.G[cur];
-        __syncthreads();  // B1: state fragments and chunk i inputs visible
+        for (int i = i_begin; i < i_end; ++i) {
+            const int cur = (i - i_begin) & 1;
+            const float* G = sh.G[cur];
+            __syncthreads();  // B1: state fragments and chunk i inputs visible
 
-        // ---------------- phase A
-        f32x4 Zc = zero4(), Xc = zero4();
-        {
-            const unsigned short* src = chain ? sh.K[cur] : sh.Q[cur];
-            f32x4 A1 = zero4(), A2 = zero4();
+            // ---- phase A: Y = K S^T (channel gate: gated rows), X = V - gamma' Y
+            f32x4 Xc;
+            if constexpr (!CH) {
+                f32x4 A1 = zero4(), A2 = zero4();
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const u16x8 shi = cat(sh.Sf[s][0][0][l], sh.Sf[s][1][0][l]);
-                const u16x8 slo = cat(sh.Sf[s][0][1][l], sh.Sf[s][1][1][l]);
-                const unsigned short* rr = &src[(16 * w + c16) * LDK + 32 * s + 4 * g4];
-                const u16x8 ra = cat(*reinterpret_cast<const u16x4*>(rr), *reinterpret_cast<const u16x4*>(rr + 16));
-                A1 = mfma(ra, shi, A1);
-                A2 = mfma(ra, slo, A2);
+                for (int s = 0; s < KS; ++s) {
+                    const u16x8 shi = cat(sh.Sf[s][0][0][l], sh.Sf[s][1][0][l]);
+                    const u16x8 slo = cat(sh.Sf[s][0][1][l], sh.Sf[s][1][1][l]);
+                    const unsigned short* rr = &sh.K[cur][(16 * w + c16) * LDK + 32 * s + 4 * g4];
+                    const u16x8 ra = cat(*reinterpret_cast<const u16x4*>(rr), *reinterpret_cast<const u16x4*>(rr + 16));
+                    A1 = mfma(ra, shi, A1);
+                    A2 = mfma(ra, slo, A2);
+                }
+                Xc = A1 + A2;
+            } else {
+                Xc = gated_rows(sh.K[cur], G, ptd ? 16 * w + c16 - 1 : 16 * w + c16);
             }
-            if (chain) Xc = A1 + A2;
-            else Zc = A1 + A2;
-        }
-        if (!chain) load_pfrag(i);
-        if (chain) {
-            // X = V - diag(gamma') Y
-            const f32x4 gamp = *reinterpret_cast<const f32x4*>(&G[64 + 16 * w + 4 * g4]);
+            {
+                f32x4 gamp = f32x4{1.f, 1.f, 1.f, 1.f};
+                if constexpr (!CH) gamp = *reinterpret_cast<const f32x4*>(&G[64 + 16 * w + 4 * g4]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float vv = scaling ? 0.f : gdn_bf16_to_f32(sh.V[cur][(16 * w + 4 * g4 + r) * 16 + c16]);
-                Xc[r] = vv - gamp[r] * Xc[r];
+                for (int r = 0; r < 4; ++r) {
+                    const float vv = scaling ? 0.f : gdn_bf16_to_f32(sh.V[cur][(16 * w + 4 * g4 + r) * 16 + c16]);
+                    Xc[r] = vv - gamp[r] * Xc[r];
+                }
+                u16x4 hi, lo;
+                split4(Xc, hi, lo);
+                sh.Xf[w >> 1][w & 1][0][l] = hi;
+                sh.Xf[w >> 1][w & 1][1][l] = lo;
             }
-            u16x4 hi, lo;
-            split4(Xc, hi, lo);
-            sh.Xf[w >> 1][w & 1][0][l] = hi;
-            sh.Xf[w >> 1][w & 1][1][l] = lo;
-        }
-        __syncthreads();  // B2
+            __syncthreads();  // B2
 
-        // ---------------- phase B
-        u16x8 kt[TPW][2];
-        if (chain) {
-            f32x4 D1 = zero4(), D2 = zero4(), D3 = zero4();
+            // ---- phase B: Delta = T' X; K^T operands of the state update
+            u16x8 kt[TPW][2], ktl[CH ? TPW : 1][2];
+            {
+                f32x4 D1 = zero4(), D2 = zero4(), D3 = zero4();
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s >= nks) continue;
-                const u16x8 xh = cat(sh.Xf[s][0][0][l], sh.Xf[s][1][0][l]);
-                const u16x8 xl = cat(sh.Xf[s][0][1][l], sh.Xf[s][1][1][l]);
-                D1 = mfma(tf_c[s][0], xh, D1);
-                D2 = mfma(tf_c[s][0], xl, D2);
-                D3 = mfma(tf_c[s][1], xh, D3);
+                for (int s = 0; s < 2; ++s) {
+                    if (s >= nks) continue;
+                    const u16x8 xh = cat(sh.Xf[s][0][0][l], sh.Xf[s][1][0][l]);
+                    const u16x8 xl = cat(sh.Xf[s][0][1][l], sh.Xf[s][1][1][l]);
+                    D1 = mfma(tf_c[s][0], xh, D1);
+                    D2 = mfma(tf_c[s][0], xl, D2);
+                    D3 = mfma(tf_c[s][1], xh, D3);
+                }
+                D1 += D2 + D3;
+                u16x4 hi, lo;
+                split4(D1, hi, lo);
+                sh.Df[w >> 1][w & 1][0][l] = hi;
+                sh.Df[w >> 1][w & 1][1][l] = lo;
+                if constexpr (!CH) {
+                    // Delta scaled to the chunk end (gamma_C / gamma_t per row)
+                    const f32x4 rat = *reinterpret_cast<const f32x4*>(&G[128 + 16 * w + 4 * g4]);
+                    split4(rat * D1, hi, lo);
+                }
+                sh.DBf[w >> 1][w & 1][0][l] = hi;
+                sh.DBf[w >> 1][w & 1][1][l] = lo;
             }
-            D1 += D2 + D3;
-            const f32x4 rat = *reinterpret_cast<const f32x4*>(&G[128 + 16 * w + 4 * g4]);
-            u16x4 hi, lo;
-            split4(D1, hi, lo);
-            sh.Df[w >> 1][w & 1][0][l] = hi;
-            sh.Df[w >> 1][w & 1][1][l] = lo;
-            split4(rat * D1, hi, lo);
-            sh.DBf[w >> 1][w & 1][0][l] = hi;
-            sh.DBf[w >> 1][w & 1][1][l] = lo;
-            // K^T operands for the state update: rows a = 16 tau + c16, k-slots j
-#pragma unroll
-            for (int u = 0; u < TPW; ++u)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-                        kt[u][s][e] = sh.K[cur][j * LDK + 16 * (w * TPW + u) + c16];
-                    }
-        } else if (i + 1 < i_end) {
-            // the other LDS buffer held chunk i-1, finished before B1: stage
-            // chunk i+1 there, then start loading chunk i+2
-            store_loads(cur ^ 1);
-            if (i + 2 < i_end) issue_loads(i + 2);
-        }
-        __syncthreads();  // B3
-
-        // ---------------- phase C
-        if (chain) {
-            const float gamC = G[256];
+            // K^T: rows a = 16 tau + c16, k-slots j (channel gate: K (.) e^{g_C - g},
+            // split hi/lo)
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
-                f32x4 acc = gamC * Sacc[u], acc2 = zero4();
+                const int a = 16 * (w * TPW + u) + c16;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if constexpr (!CH) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int j = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
+                            kt[u][s][e] = sh.K[cur][j * LDK + a];
+                        }
+                    } else {
+                        const float gC = G[(C - 1) * D + a];
+                        uint32_t kh[4], kl[4];
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2) {
+                            const int j0 = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
+                            const float x0 = gdn_bf16_to_f32(sh.K[cur][j0 * LDK + a]) * __expf(gC - G[j0 * D + a]);
+                            const float x1 = gdn_bf16_to_f32(sh.K[cur][(j0 + 1) * LDK + a]) *
+                                             __expf(gC - G[(j0 + 1) * D + a]);
+                            split2(x0, x1, kh[e >> 1], kl[e >> 1]);
+                        }
+                        kt[u][s] = __builtin_bit_cast(u16x8, uint4{kh[0], kh[1], kh[2], kh[3]});
+                        ktl[u][s] = __builtin_bit_cast(u16x8, uint4{kl[0], kl[1], kl[2], kl[3]});
+                    }
+                }
+            }
+            __syncthreads();  // B3
+
+            // ---- phase C: S^T <- decay (.) S^T + K^T Delta-bar, publish
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                f32x4 acc, acc2 = zero4(), acc3 = zero4();
+                if constexpr (!CH) {
+                    acc = G[256] * Sacc[u];
+                } else {
+                    // column decay e^{g_C[a]} for key rows a = 16 tau + 4 g4 + r
+                    const f32x4 gC = *reinterpret_cast<const f32x4*>(&G[(C - 1) * D + 16 * (w * TPW + u) + 4 * g4]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] = __expf(gC[r]) * Sacc[u][r];
+                }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const u16x8 dbh = cat(sh.DBf[s][0][0][l], sh.DBf[s][1][0][l]);
                     const u16x8 dbl = cat(sh.DBf[s][0][1][l], sh.DBf[s][1][1][l]);
                     acc = mfma(kt[u][s], dbh, acc);
                     acc2 = mfma(kt[u][s], dbl, acc2);
+                    if constexpr (CH) acc3 = mfma(ktl[u][s], dbh, acc3);
                 }
-                Sacc[u] = acc + acc2;
+                Sacc[u] = acc + acc2 + acc3;
             }
             publish_state();
             if (i + 1 < i_end) {
@@ -581,12 +785,9 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                     for (int hl = 0; hl < 2; ++hl) tf_c[s][hl] = tf_n[s][hl];
                 if (i + 2 < i_end) load_tfrag(i + 2);
             }
-        } else {
-            emit_output(i, Zc, *reinterpret_cast<const f32x4*>(&G[16 * w + 4 * g4]));
         }
-    }
 
-    if (chain) {
+        // ---- chain epilogue: the slice of the end state (or of M, or S^Delta)
         float* dst;
         if (scaling)
             dst = reinterpret_cast<float*>(wsb + L.mend) + (bh * sp.G + gseg) * D * D;
@@ -600,6 +801,51 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                 const int a0 = 16 * (w * TPW + u) + 4 * g4;
                 *reinterpret_cast<f32x4*>(&dst[(int64_t)(r0 + c16) * D + a0]) = Sacc[u];
             }
+        }
+    } else {
+        // ---- output prologue
+        if (i_begin < i_end) {
+            issue_loads(i_begin);
+            store_loads(0);
+            if (i_begin + 1 < i_end) issue_loads(i_begin + 1);
+        }
+        for (int i = i_begin; i < i_end; ++i) {
+            const int cur = (i - i_begin) & 1;
+            const float* G = sh.G[cur];
+            __syncthreads();  // B1
+
+            // ---- phase A: Z = Q S^T (channel gate: rows Q (.) e^{g})
+            f32x4 Zc;
+            if constexpr (!CH) {
+                f32x4 A1 = zero4(), A2 = zero4();
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const u16x8 shi = cat(sh.Sf[s][0][0][l], sh.Sf[s][1][0][l]);
+                    const u16x8 slo = cat(sh.Sf[s][0][1][l], sh.Sf[s][1][1][l]);
+                    const unsigned short* rr = &sh.Q[cur][(16 * w + c16) * LDK + 32 * s + 4 * g4];
+                    const u16x8 ra = cat(*reinterpret_cast<const u16x4*>(rr), *reinterpret_cast<const u16x4*>(rr + 16));
+                    A1 = mfma(ra, shi, A1);
+                    A2 = mfma(ra, slo, A2);
+                }
+                Zc = A1 + A2;
+            } else {
+                Zc = gated_rows(sh.Q[cur], G, 16 * w + c16);
+            }
+            load_pfrag(i);
+            __syncthreads();  // B2
+
+            // ---- phase B: the other LDS buffer held chunk i-1, finished before
+            // B1: stage chunk i+1 there, then start loading chunk i+2
+            if (i + 1 < i_end) {
+                store_loads(cur ^ 1);
+                if (i + 2 < i_end) issue_loads(i + 2);
+            }
+            __syncthreads();  // B3
+
+            // ---- phase C: O = scale (gamma Z + P Delta)
+            f32x4 gam = f32x4{1.f, 1.f, 1.f, 1.f};
+            if constexpr (!CH) gam = *reinterpret_cast<const f32x4*>(&G[16 * w + 4 * g4]);
+            emit_output(i, Zc, gam);
         }
     }
 }
@@ -673,7 +919,7 @@ __global__ __launch_bounds__(kThreads) void k_correct_mfma(Problem p, Split sp, 
     }
 }
 
-template <int D>
+template <int D, int CH>
 hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L, hipStream_t st) {
     u16x8* tfrag = reinterpret_cast<u16x8*>(ws + L.prep);
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
@@ -683,7 +929,7 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
         prof_begin("k_prep_mfma", st);
-        hipLaunchKernelGGL(k_prep_mfma<D>, grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
+        hipLaunchKernelGGL((k_prep_mfma<D, CH>), grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -694,7 +940,7 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
         const int64_t nwork = heads * ntiles;
         const int remap = (heads % 8 == 0) ? 1 : 0;
         prof_begin("k_rec_mfma", st);
-        hipLaunchKernelGGL(k_rec_mfma<D>, dim3((unsigned)nwork), dim3(kRecThreads), 0, st, p, sp, L,
+        hipLaunchKernelGGL((k_rec_mfma<D, CH>), dim3((unsigned)nwork), dim3(kRecThreads), 0, st, p, sp, L,
                            ws, tfrag, pfrag, gates, ntiles, remap);
         prof_end(st);
         hipError_t e = hipGetLastError();
@@ -707,16 +953,17 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
 }  // namespace
 
 bool mfma_supported(int64_t dk, int64_t dv, int C_, int dtype, int gate) {
-    return dtype == GDN_BF16 && gate == GDN_GATE_SCALAR && C_ == C && dk == dv &&
-           (dk == 64 || dk == 128);
+    return dtype == GDN_BF16 && (gate == GDN_GATE_SCALAR || gate == GDN_GATE_CHANNEL) &&
+           C_ == C && dk == dv && (dk == 64 || dk == 128);
 }
 
 WsLayout mfma_layout(const Problem& p, const Split& sp) {
     WsLayout L;
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
     L.prep = 0;
+    const size_t gate_floats = p.gate == GDN_GATE_CHANNEL ? (size_t)C * p.dk : kGateFloats;
     L.prep_bytes = 2 * align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
-                   align256((size_t)nch * kGateFloats * sizeof(float));
+                   align256((size_t)nch * gate_floats * sizeof(float));
     size_t off = L.prep_bytes;
     if (sp.G > 1) {
         L.corr = off;
@@ -753,8 +1000,9 @@ hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLay
 
 hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t st) {
     const WsLayout L = mfma_layout(p, sp);
-    if (p.dk == 128) return launch<128>(p, sp, ws, L, st);
-    return launch<64>(p, sp, ws, L, st);
+    const bool ch = p.gate == GDN_GATE_CHANNEL;
+    if (p.dk == 128) return ch ? launch<128, 1>(p, sp, ws, L, st) : launch<128, 0>(p, sp, ws, L, st);
+    return ch ? launch<64, 1>(p, sp, ws, L, st) : launch<64, 0>(p, sp, ws, L, st);
 }
 
 }  // namespace gdn

@@ -83,9 +83,10 @@ def test_chunk_path_selection():
     for d in (16, 32, 64, 128):
         assert gdn.gdn_chunk_path(d, d, 16, gdn.GDN_F32, 0) == gdn.GDN_PATH_VALU
     assert gdn.gdn_chunk_path(60, 64, 64, gdn.GDN_BF16, 0) == gdn.GDN_E_UNSUPPORTED
-    # bf16, dk = dv in {64, 128}, chunk 64, scalar gate: the MFMA kernels
+    # bf16, dk = dv in {64, 128}, chunk 64, either gate: the MFMA kernels
     for d in (64, 128):
-        assert gdn.gdn_chunk_path(d, d, 64, gdn.GDN_BF16, 0) == gdn.GDN_PATH_MFMA
+        for gate in (0, 1):
+            assert gdn.gdn_chunk_path(d, d, 64, gdn.GDN_BF16, gate) == gdn.GDN_PATH_MFMA
     assert gdn.gdn_chunk_path(128, 128, 64, gdn.GDN_F32, 0) == gdn.GDN_PATH_VALU
     assert gdn.gdn_chunk_path(128, 128, 32, gdn.GDN_BF16, 0) == gdn.GDN_PATH_VALU
     assert gdn.gdn_chunk_path(128, 64, 64, gdn.GDN_BF16, 0) == gdn.GDN_PATH_VALU

@@ -102,14 +102,20 @@ def test_random_shapes(case, entry):
     check(w, inp, o, s, order)
 
 
-@pytest.mark.parametrize("alpha_mean", [6.0, -1.0])
-def test_gate_extremes(alpha_mean):
-    """Long memory (alpha ~ 0.998) and fast forgetting (alpha ~ 0.27)."""
+@pytest.mark.parametrize("gate,alpha_mean", [
+    ("scalar", 6.0), ("scalar", -1.0), ("scalar", -6.0),
+    ("channel", 6.0), ("channel", -1.0), ("channel", -3.0), ("channel", -6.0)])
+def test_gate_extremes(gate, alpha_mean):
+    """Long memory (alpha ~ 0.998) to fast forgetting (alpha ~ 0.0025).  With
+    per-channel gates at -3 a 16-token block decays by ~e^-48 per channel;
+    at -6 by ~e^-96, past the range where the block is factored."""
     w = Workload("gates", B=1, H=2, T=512, dk=128, dv=128, chunk=64, state0_std=0.5,
-                 alpha_mean=alpha_mean, seed=7)
+                 gate=gate, alpha_mean=alpha_mean, seed=7)
     inp = make_inputs(w)
     o, s = run(w, inp)
     check(w, inp, o, s)
+    o, s = run(w, inp, order=DTP)
+    check(w, inp, o, s, DTP)
 
 
 # --------------------------------------------------------------------------
