@@ -103,12 +103,12 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 }
 
 // Per-key-channel gates (CH = 1): the gate is a vector per token and the
-// chunk-local log prefix g[t][a] is a C x D table (stored for the chunk loop).
-// Intra-chunk ratios exp(g_t - g_j) then differ per channel and enter the MFMA
-// operands, anchored at 16-token block boundaries (the secondary chunking of
-// the GLA gating section): for key block c below row block m the anchor is the
-// last token p of block c, so q_t e^{g_t - g_p} and k_j e^{g_p - g_j} are both
-// at most one; on diagonal blocks p is the token before the block.
+// chunk-local prefix becomes a C x D table, kept in log2 units
+// (lam[t][a] = sum_{s <= t} log2 alpha_sa, so every ratio is one exp2) and
+// stored for the chunk loop.  Intra-chunk ratios 2^{lam_t - lam_j} differ per
+// channel, so they enter the MFMA operands as row and key factors about an
+// anchor token, per 16-token row block (the secondary chunking of the GLA
+// gating section).
 template <int D, int CH>
 __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag, u16x8* pfrag,
                                                         float* gates) {
@@ -117,10 +117,12 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     constexpr int kBufBytes = (C * LDK * 2 > C * (C + 1) * 4) ? C * LDK * 2 : C * (C + 1) * 4;
     // K (bf16, row stride LDK) during the Gram product, then T (fp32 [C][C+1])
     __shared__ __attribute__((aligned(16))) unsigned char kt_buf[kBufBytes];
-    __shared__ float Ms[C][C + 1];
-    __shared__ __attribute__((aligned(16))) unsigned short Qs[C * LDK];
-    __shared__ float gsh[C], gpsh[C], bsh[C];
-    __shared__ __attribute__((aligned(16))) float gt[CH ? C : 1][CH ? D : 1];  // channel log prefix
+    __shared__ __attribute__((aligned(16))) float Ms[C][C + 1];
+    // Q rows (scalar gate only: the channel gate reads Q fragments from HBM)
+    __shared__ __attribute__((aligned(16))) unsigned short Qs[CH ? 8 : C * LDK];
+    __shared__ float gsh[CH ? 1 : C], gpsh[CH ? 1 : C], bsh[C];
+    // channel log2 prefix; rows padded by 16 bytes against bank conflicts
+    __shared__ __attribute__((aligned(16))) float gt[CH ? C : 1][CH ? D + 4 : 1];
     unsigned short* Ks = reinterpret_cast<unsigned short*>(kt_buf);
     float (*Ts)[C + 1] = reinterpret_cast<float (*)[C + 1]>(kt_buf);
 
@@ -139,10 +141,10 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
         if (t < nt) {
             const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
             kv = *reinterpret_cast<const uint4*>(kin + off);
-            qv = *reinterpret_cast<const uint4*>(qin + off);
+            if constexpr (!CH) qv = *reinterpret_cast<const uint4*>(qin + off);
         }
         *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = kv;
-        *reinterpret_cast<uint4*>(&Qs[t * LDK + c8 * 8]) = qv;
+        if constexpr (!CH) *reinterpret_cast<uint4*>(&Qs[t * LDK + c8 * 8]) = qv;
     }
     if constexpr (!CH) {
         if (w == 0) {
@@ -170,26 +172,34 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
         __syncthreads();
     } else {
         if (w == 0) bsh[l] = l < nt ? p.beta[((int64_t)b * T + t0 + l) * H + h] : 0.f;
-        // log gates (zero on padding tokens), then the prefix down each channel
-        for (int e = tid; e < C * PPR * 2; e += kThreads) {
-            const int t = e / (PPR * 2), a4 = e - t * (PPR * 2);
-            float4 la = make_float4(0.f, 0.f, 0.f, 0.f);
+        // log2 prefix lam[t][a] = sum_{s <= t} log2 alpha_sa (padding tokens add
+        // zero): thread (group, a4) scans TPG tokens of four channels in
+        // registers, then adds the totals of the earlier groups
+        constexpr int A4 = D / 4, NG = kThreads / A4, TPG = C / NG;
+        f32x4(*part)[A4] = reinterpret_cast<f32x4(*)[A4]>(&Ms[0][0]);  // Ms is free until L
+        const int a4 = tid % A4, grp = tid / A4;
+        f32x4 run = zero4(), vals[TPG];
+#pragma unroll
+        for (int u = 0; u < TPG; ++u) {
+            const int t = grp * TPG + u;
             if (t < nt) {
-                const float4 av = *reinterpret_cast<const float4*>(
+                const f32x4 av = *reinterpret_cast<const f32x4*>(
                     p.alpha + (((int64_t)b * T + t0 + t) * H + h) * D + 4 * a4);
-                la = make_float4(logf(av.x), logf(av.y), logf(av.z), logf(av.w));
+                run += f32x4{log2f(av[0]), log2f(av[1]), log2f(av[2]), log2f(av[3])};
             }
-            *reinterpret_cast<float4*>(&gt[t][4 * a4]) = la;
+            vals[u] = run;
         }
+        part[grp][a4] = run;
         __syncthreads();
+        f32x4 off = zero4();
+        for (int gg = 0; gg < grp; ++gg) off += part[gg][a4];
         float* gdst = gates + ch * (int64_t)C * D;
-        for (int a = tid; a < D; a += kThreads) {
-            float g = 0.f;
-            for (int t = 0; t < C; ++t) {
-                g += gt[t][a];
-                gt[t][a] = g;
-                gdst[t * D + a] = g;
-            }
+#pragma unroll
+        for (int u = 0; u < TPG; ++u) {
+            const int t = grp * TPG + u;
+            const f32x4 v = vals[u] + off;
+            *reinterpret_cast<f32x4*>(&gt[t][4 * a4]) = v;
+            *reinterpret_cast<f32x4*>(&gdst[t * D + 4 * a4]) = v;
         }
         __syncthreads();
     }
@@ -247,85 +257,116 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
         }
 
     } else {
-        // L_tj = sum_a k_ta k_ja e^{g'_ta - g_ja} (j < t) and P_tj = sum_a q_ta k_ja
-        // e^{g_ta - g_ja} (j <= t) for row block m = w, key blocks c <= w, with
-        // gated operands split hi/lo; accumulators are transposed (rows j, cols t)
+        // Scores with per-channel ratios 2^{lam_t - lam_j}, row block m = w,
+        // every key block c <= w anchored at p = 16w - 1 (lam_{-1} = 0):
+        //   P_tj = sum_a [q_ta 2^{lam_ta - lam_pa}] [k_ja 2^{lam_pa - lam_ja}]   (j <= t)
+        //   L_tj = sum_a [k_ta 2^{lam'_ta - lam_pa}] [k_ja 2^{lam_pa - lam_ja}]  (j < t)
+        // Row factors are at most one, key factors too off the diagonal block;
+        // on it they grow with the decay across the block.  All gated operands
+        // are split hi/lo; accumulators are transposed (rows j, columns t).
         const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
-        const int t = 16 * w + c16;
+        const int pa = 16 * w - 1, t = 16 * w + c16;
+        const int tp = ptd ? t - 1 : t;  // row of lam' (-1: zero)
+        const f32x4 z4 = zero4();
+        u16x8 qh[D / 32], ql[D / 32], lh[D / 32], ll[D / 32];
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            const int a0 = 32 * s + 8 * g4;
+            u16x8 qt = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (t < nt)
+                qt = *reinterpret_cast<const u16x8*>(qin + (((int64_t)b * T + t0 + t) * H + h) * D + a0);
+            const u16x8 kt_ = *reinterpret_cast<const u16x8*>(&Ks[t * LDK + a0]);
+            const f32x4 gp0 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0]) : z4;
+            const f32x4 gp1 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0 + 4]) : z4;
+            const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&gt[t][a0]);
+            const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&gt[t][a0 + 4]);
+            const f32x4 gq0 = tp >= 0 ? *reinterpret_cast<const f32x4*>(&gt[tp][a0]) : z4;
+            const f32x4 gq1 = tp >= 0 ? *reinterpret_cast<const f32x4*>(&gt[tp][a0 + 4]) : z4;
+            uint32_t h1[4], l1[4], h2[4], l2[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                float xq[2], xl[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int ee = e + u;
+                    const float g_p = ee < 4 ? gp0[ee] : gp1[ee - 4];
+                    xq[u] = gdn_bf16_to_f32(qt[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gt0[ee] : gt1[ee - 4]) - g_p);
+                    xl[u] = gdn_bf16_to_f32(kt_[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gq0[ee] : gq1[ee - 4]) - g_p);
+                }
+                split2(xq[0], xq[1], h1[e >> 1], l1[e >> 1]);
+                split2(xl[0], xl[1], h2[e >> 1], l2[e >> 1]);
+            }
+            qh[s] = __builtin_bit_cast(u16x8, uint4{h1[0], h1[1], h1[2], h1[3]});
+            ql[s] = __builtin_bit_cast(u16x8, uint4{l1[0], l1[1], l1[2], l1[3]});
+            lh[s] = __builtin_bit_cast(u16x8, uint4{h2[0], h2[1], h2[2], h2[3]});
+            ll[s] = __builtin_bit_cast(u16x8, uint4{l2[0], l2[1], l2[2], l2[3]});
+        }
+        // Past 2^92 (about e^64) of decay across the diagonal block on some
+        // channel (gates far below any trained range) that block is summed
+        // directly instead.
+        float span = 0.f;
+        for (int a = l; a < D; a += 64) span = fmaxf(span, (pa >= 0 ? gt[pa][a] : 0.f) - gt[16 * w + 15][a]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+        const bool direct = span > 92.f;
+
         f32x4 PT[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             PT[c] = zero4();
             if (c > w) continue;
-            const int pa = c < w ? 16 * c + 15 : 16 * c - 1;  // anchor token
             const int j = 16 * c + c16;
             f32x4 aL = zero4(), aP = zero4();
-            // On a diagonal block the key factor e^{g_p - g_j} grows with the
-            // decay across the block; past e^{64} on some channel (gates far
-            // below any trained range) the block is summed directly instead.
-            bool direct = false;
-            if (c == w) {
-                float span = 0.f;
-                for (int a = l; a < D; a += 64)
-                    span = fmaxf(span, (pa >= 0 ? gt[pa][a] : 0.f) - gt[16 * c + 15][a]);
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
-                direct = span > 64.f;
-            }
-            if (direct) {
+            if (c == w && direct) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int jj = 16 * c + 4 * g4 + r;
                     float sp = 0.f, sl = 0.f;
-                    if (jj <= t) {
+                    if (jj <= t && t < nt) {
+                        const unsigned short* qrow = qin + (((int64_t)b * T + t0 + t) * H + h) * D;
                         for (int a = 0; a < D; ++a) {
                             const float kj = gdn_bf16_to_f32(Ks[jj * LDK + a]);
-                            const float gpr = ptd ? (t > 0 ? gt[t - 1][a] : 0.f) : gt[t][a];
-                            sp += gdn_bf16_to_f32(Qs[t * LDK + a]) * kj * expf(gt[t][a] - gt[jj][a]);
-                            sl += gdn_bf16_to_f32(Ks[t * LDK + a]) * kj * expf(gpr - gt[jj][a]);
+                            const float lq = tp >= 0 ? gt[tp][a] : 0.f;
+                            sp += gdn_bf16_to_f32(qrow[a]) * kj * __builtin_amdgcn_exp2f(gt[t][a] - gt[jj][a]);
+                            sl += gdn_bf16_to_f32(Ks[t * LDK + a]) * kj * __builtin_amdgcn_exp2f(lq - gt[jj][a]);
                         }
                     }
                     aP[r] = sp;
                     aL[r] = sl;
                 }
-            }
-            if (!direct) {
+            } else {
+                f32x4 aP2 = zero4(), aL2 = zero4();
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
-                const int a0 = 32 * s + 8 * g4;
-                const u16x8 kj = *reinterpret_cast<const u16x8*>(&Ks[j * LDK + a0]);
-                const u16x8 kt_ = *reinterpret_cast<const u16x8*>(&Ks[t * LDK + a0]);
-                const u16x8 qt = *reinterpret_cast<const u16x8*>(&Qs[t * LDK + a0]);
-                uint32_t ah[4], al[4], ph[4], pl[4], lh[4], ll[4];
+                for (int s = 0; s < D / 32; ++s) {
+                    const int a0 = 32 * s + 8 * g4;
+                    const u16x8 kj = *reinterpret_cast<const u16x8*>(&Ks[j * LDK + a0]);
+                    const f32x4 gp0 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0]) : z4;
+                    const f32x4 gp1 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0 + 4]) : z4;
+                    const f32x4 gj0 = *reinterpret_cast<const f32x4*>(&gt[j][a0]);
+                    const f32x4 gj1 = *reinterpret_cast<const f32x4*>(&gt[j][a0 + 4]);
+                    uint32_t ah[4], al[4];
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    float fa[2], fp[2], fl[2];
+                    for (int e = 0; e < 8; e += 2) {
+                        float xa[2];
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int a = a0 + e + q;
-                        const float gp = pa >= 0 ? gt[pa][a] : 0.f;
-                        const float gpr = ptd ? (t > 0 ? gt[t - 1][a] : 0.f) : gt[t][a];
-                        fa[q] = gdn_bf16_to_f32(kj[e + q]) * expf(gp - gt[j][a]);
-                        fp[q] = gdn_bf16_to_f32(qt[e + q]) * expf(gt[t][a] - gp);
-                        fl[q] = gdn_bf16_to_f32(kt_[e + q]) * expf(gpr - gp);
+                        for (int u = 0; u < 2; ++u) {
+                            const int ee = e + u;
+                            xa[u] = gdn_bf16_to_f32(kj[ee]) *
+                                    __builtin_amdgcn_exp2f((ee < 4 ? gp0[ee] : gp1[ee - 4]) - (ee < 4 ? gj0[ee] : gj1[ee - 4]));
+                        }
+                        split2(xa[0], xa[1], ah[e >> 1], al[e >> 1]);
                     }
-                    split2(fa[0], fa[1], ah[e >> 1], al[e >> 1]);
-                    split2(fp[0], fp[1], ph[e >> 1], pl[e >> 1]);
-                    split2(fl[0], fl[1], lh[e >> 1], ll[e >> 1]);
+                    const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
+                    const u16x8 Al = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
+                    aP = mfma(Ah, qh[s], aP);
+                    aP2 = mfma(Ah, ql[s], aP2);
+                    aP = mfma(Al, qh[s], aP);
+                    aL = mfma(Ah, lh[s], aL);
+                    aL2 = mfma(Ah, ll[s], aL2);
+                    aL = mfma(Al, lh[s], aL);
                 }
-                const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
-                const u16x8 Al = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
-                const u16x8 Ph = __builtin_bit_cast(u16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
-                const u16x8 Pl = __builtin_bit_cast(u16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
-                const u16x8 Lh = __builtin_bit_cast(u16x8, uint4{lh[0], lh[1], lh[2], lh[3]});
-                const u16x8 Ll = __builtin_bit_cast(u16x8, uint4{ll[0], ll[1], ll[2], ll[3]});
-                aP = mfma(Ah, Ph, aP);
-                aP = mfma(Ah, Pl, aP);
-                aP = mfma(Al, Ph, aP);
-                aL = mfma(Ah, Lh, aL);
-                aL = mfma(Ah, Ll, aL);
-                aL = mfma(Al, Lh, aL);
-            }
+                aP += aP2;
+                aL += aL2;
             }
             // accumulator lane: column t = 16w + c16, rows j = 16c + 4g4 + r
 #pragma unroll
@@ -436,7 +477,8 @@ struct RecShared {
     unsigned short K[2][C * LDK];
     unsigned short Q[2][C * LDK];
     unsigned short V[2][C * 16];
-    float G[2][CH ? C * D : kGateFloats];  // gate block, or the C x D log-prefix table
+    // gate block, or the C x D log2-prefix table (rows padded to D + 4 floats)
+    float G[2][CH ? C * (D + 4) : kGateFloats];
     u16x4 Sf[KS][2][2][64];  // S^T fragments: [k-step][tile half][hi/lo][lane]
     u16x4 Xf[2][2][2][64];
     u16x4 Df[2][2][2][64];
@@ -444,10 +486,10 @@ struct RecShared {
 };
 
 constexpr int kRecThreads = 512;
-// CH = 1 (per-key-channel gates): Y and Z take the gated operands
-// K (.) e^{g'} and Q (.) e^{g}, the state update takes K (.) e^{g_C - g} (all
-// split hi/lo, three MFMAs per product) and the state decays column-wise by
-// e^{g_C}; no row factors remain.
+// CH = 1 (per-key-channel gates, log2 prefix lam): Y and Z take the gated
+// operands K (.) 2^{lam'} and Q (.) 2^{lam}, the state update takes
+// K (.) 2^{lam_C - lam} (all split hi/lo, three MFMAs per product) and the
+// state decays column-wise by 2^{lam_C}; no row factors remain.
 template <int D, int CH>
 __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, WsLayout L,
                                                           char* wsb, const u16x8* tfrag,
@@ -526,6 +568,8 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
     const int vrow = otid >> 1, vhf = otid & 1;
     const int64_t v_base = (((int64_t)b * T + vrow) * H + h) * D + r0 + 8 * vhf;
     constexpr int GSTRIDE = CH ? C * D : kGateFloats;  // gate floats per chunk-head
+    constexpr int LDG = D + 4;                           // LDS row stride of the channel table
+    static_assert(!CH || (GP % 256 == 0 && 256 % (D / 4) == 0), "channel table staging");
     const float* g_base = gates + bh * p.NC * GSTRIDE;
     uint4 kreg[KQP], qreg[KQP], vreg;
     u32x4 greg[GPT];
@@ -555,10 +599,18 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
             *reinterpret_cast<uint4*>(&sh.Q[buf][(trow + RPP * k) * LDK + c8 * 8]) = qreg[k];
         }
         if (otid < 128) *reinterpret_cast<uint4*>(&sh.V[buf][vrow * 16 + 8 * vhf]) = vreg;
-        u32x4* gdst = reinterpret_cast<u32x4*>(sh.G[buf]) + otid;
+        if constexpr (CH) {
+            // piece q = otid + 256k holds row q / (D/4), columns 4 (q % (D/4)) ..
+            float* gdst = sh.G[buf] + (otid / (D / 4)) * LDG + 4 * (otid % (D / 4));
 #pragma unroll
-        for (int k = 0; k < GPT; ++k)
-            if (GP % 256 == 0 || otid + 256 * k < GP) gdst[256 * k] = greg[k];
+            for (int k = 0; k < GPT; ++k)
+                *reinterpret_cast<u32x4*>(gdst + k * (256 / (D / 4)) * LDG) = greg[k];
+        } else {
+            u32x4* gdst = reinterpret_cast<u32x4*>(sh.G[buf]) + otid;
+#pragma unroll
+            for (int k = 0; k < GPT; ++k)
+                if (GP % 256 == 0 || otid + 256 * k < GP) gdst[256 * k] = greg[k];
+        }
     };
     float* corr = reinterpret_cast<float*>(wsb + L.corr);
     const int64_t out_base = (((int64_t)b * T + 16 * w + 4 * g4) * H + h) * D + r0 + c16;
@@ -602,7 +654,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
         }
     };
 
-    // channel gate: rows of src scaled by e^{g[grow]} (grow = -1: by one),
+    // channel gate: rows of src scaled by 2^{lam[grow]} (grow = -1: by one),
     // split hi/lo, times S^T (hi/lo): 16 x 16 tile of rows 16w.. of the chunk
     auto gated_rows = [&](const unsigned short* src, const float* G, int grow) {
         f32x4 A1 = zero4(), A2 = zero4(), A3 = zero4();
@@ -615,14 +667,14 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
             const u16x8 raw = cat(*reinterpret_cast<const u16x4*>(rr), *reinterpret_cast<const u16x4*>(rr + 16));
             f32x4 g0 = zero4(), g1 = zero4();
             if (grow >= 0) {
-                g0 = *reinterpret_cast<const f32x4*>(&G[grow * D + 32 * s + 4 * g4]);
-                g1 = *reinterpret_cast<const f32x4*>(&G[grow * D + 32 * s + 16 + 4 * g4]);
+                g0 = *reinterpret_cast<const f32x4*>(&G[grow * LDG + 32 * s + 4 * g4]);
+                g1 = *reinterpret_cast<const f32x4*>(&G[grow * LDG + 32 * s + 16 + 4 * g4]);
             }
             uint32_t ah[4], al[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float x0 = gdn_bf16_to_f32(raw[e]) * __expf(e < 4 ? g0[e] : g1[e - 4]);
-                const float x1 = gdn_bf16_to_f32(raw[e + 1]) * __expf(e < 4 ? g0[e + 1] : g1[e - 3]);
+                const float x0 = gdn_bf16_to_f32(raw[e]) * __builtin_amdgcn_exp2f(e < 4 ? g0[e] : g1[e - 4]);
+                const float x1 = gdn_bf16_to_f32(raw[e + 1]) * __builtin_amdgcn_exp2f(e < 4 ? g0[e + 1] : g1[e - 3]);
                 split2(x0, x1, ah[e >> 1], al[e >> 1]);
             }
             const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
@@ -724,7 +776,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                 sh.DBf[w >> 1][w & 1][0][l] = hi;
                 sh.DBf[w >> 1][w & 1][1][l] = lo;
             }
-            // K^T: rows a = 16 tau + c16, k-slots j (channel gate: K (.) e^{g_C - g},
+            // K^T: rows a = 16 tau + c16, k-slots j (channel gate: K (.) 2^{lam_C - lam},
             // split hi/lo)
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
@@ -738,14 +790,14 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                             kt[u][s][e] = sh.K[cur][j * LDK + a];
                         }
                     } else {
-                        const float gC = G[(C - 1) * D + a];
+                        const float gC = G[(C - 1) * LDG + a];
                         uint32_t kh[4], kl[4];
 #pragma unroll
                         for (int e = 0; e < 8; e += 2) {
                             const int j0 = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-                            const float x0 = gdn_bf16_to_f32(sh.K[cur][j0 * LDK + a]) * __expf(gC - G[j0 * D + a]);
+                            const float x0 = gdn_bf16_to_f32(sh.K[cur][j0 * LDK + a]) * __builtin_amdgcn_exp2f(gC - G[j0 * LDG + a]);
                             const float x1 = gdn_bf16_to_f32(sh.K[cur][(j0 + 1) * LDK + a]) *
-                                             __expf(gC - G[(j0 + 1) * D + a]);
+                                             __builtin_amdgcn_exp2f(gC - G[(j0 + 1) * LDG + a]);
                             split2(x0, x1, kh[e >> 1], kl[e >> 1]);
                         }
                         kt[u][s] = __builtin_bit_cast(u16x8, uint4{kh[0], kh[1], kh[2], kh[3]});
@@ -762,10 +814,10 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                 if constexpr (!CH) {
                     acc = G[256] * Sacc[u];
                 } else {
-                    // column decay e^{g_C[a]} for key rows a = 16 tau + 4 g4 + r
-                    const f32x4 gC = *reinterpret_cast<const f32x4*>(&G[(C - 1) * D + 16 * (w * TPW + u) + 4 * g4]);
+                    // column decay 2^{lam_C[a]} for key rows a = 16 tau + 4 g4 + r
+                    const f32x4 gC = *reinterpret_cast<const f32x4*>(&G[(C - 1) * LDG + 16 * (w * TPW + u) + 4 * g4]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] = __expf(gC[r]) * Sacc[u][r];
+                    for (int r = 0; r < 4; ++r) acc[r] = __builtin_amdgcn_exp2f(gC[r]) * Sacc[u][r];
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
@@ -814,7 +866,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
             const float* G = sh.G[cur];
             __syncthreads();  // B1
 
-            // ---- phase A: Z = Q S^T (channel gate: rows Q (.) e^{g})
+            // ---- phase A: Z = Q S^T (channel gate: rows Q (.) 2^{lam})
             f32x4 Zc;
             if constexpr (!CH) {
                 f32x4 A1 = zero4(), A2 = zero4();
