@@ -191,25 +191,35 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     kern = gdn.gdn_profile_read()
     gdn.gdn_profile_enable(False)
-    per_kernel_us = {k: 1e3 * v[0] / max(1, v[1]) for k, v in kern.items()}
-    step_kernel_us = sum(per_kernel_us.values())
+    # per step: total time of each kernel (several launches per step when the
+    # path is pipelined over chunk slabs) and its launches
+    per_kernel_us = {k: 1e3 * v[0] / args.steps for k, v in kern.items()}
+    launches = {k: v[1] / args.steps for k, v in kern.items()}
     dominant = max(per_kernel_us, key=per_kernel_us.get) if per_kernel_us else None
-    log(f"step {ms * 1e3:.1f} us; kernels (avg us): "
-        + ", ".join(f"{k} {v:.1f}" for k, v in per_kernel_us.items()))
+    log(f"step {ms * 1e3:.1f} us; kernel time per step (us): "
+        + ", ".join(f"{k} {v:.1f} ({launches[k]:g} launches)" for k, v in per_kernel_us.items()))
 
     tokens = w.B * w.T
     value = tokens / (ms * 1e-3)
     abytes = algorithmic_bytes(w)
     aflops = algorithmic_flops(w)
-    achieved = abytes / (step_kernel_us * 1e-6) / 1e9
+    # dominant kernel: each launch covers an equal share of the head-tokens and
+    # their algorithmic bytes, so bytes per launch / average launch time equals
+    # bytes per step / that kernel's time per step
+    dom_us = per_kernel_us[dominant]
+    achieved = abytes / (dom_us * 1e-6) / 1e9
+    step_achieved = abytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": stored_traffic(w.name) if G == w.n_segments else None,
-            "kernel": "+".join(per_kernel_us.keys()),
-            "kernel_avg_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
-            "dominant": dominant,
+            "kernel": dominant,
+            "kernel_launches_per_step": launches[dominant],
+            "kernel_avg_launch_us": round(dom_us / launches[dominant], 2),
+            "kernel_us_per_step": {k: round(v, 2) for k, v in per_kernel_us.items()},
             "algorithmic_bytes": abytes,
-            "mfma_frac": round(aflops / (step_kernel_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+            "step_achieved": round(step_achieved, 1),
+            "step_frac": round(step_achieved / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     extra = {}
     if G > 1:
