@@ -30,6 +30,8 @@
 //   16-row accumulator tiles, k-slot 8g+e <-> index 4g+e (e < 4) of the first
 //   tile and 4g+e-4 of the second, and the other operand is read in the same
 //   slot order.  Three barriers per chunk.
+#include <type_traits>
+
 #include "gdn_internal.h"
 #include "../../include/gdn.h"
 
@@ -118,8 +120,6 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     // K (bf16, row stride LDK) during the Gram product, then T (fp32 [C][C+1])
     __shared__ __attribute__((aligned(16))) unsigned char kt_buf[kBufBytes];
     __shared__ __attribute__((aligned(16))) float Ms[C][C + 1];
-    // Q rows (scalar gate only: the channel gate reads Q fragments from HBM)
-    __shared__ __attribute__((aligned(16))) unsigned short Qs[CH ? 8 : C * LDK];
     __shared__ float gsh[CH ? 1 : C], gpsh[CH ? 1 : C], bsh[C];
     // channel log2 prefix; rows padded by 16 bytes against bank conflicts
     __shared__ __attribute__((aligned(16))) float gt[CH ? C : 1][CH ? D + 4 : 1];
@@ -137,14 +137,9 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
 
     for (int e = tid; e < C * PPR; e += kThreads) {
         const int t = e / PPR, c8 = e - (e / PPR) * PPR;
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-        if (t < nt) {
-            const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
-            kv = *reinterpret_cast<const uint4*>(kin + off);
-            if constexpr (!CH) qv = *reinterpret_cast<const uint4*>(qin + off);
-        }
+        uint4 kv = make_uint4(0, 0, 0, 0);
+        if (t < nt) kv = *reinterpret_cast<const uint4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
         *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = kv;
-        if constexpr (!CH) *reinterpret_cast<uint4*>(&Qs[t * LDK + c8 * 8]) = qv;
     }
     if constexpr (!CH) {
         if (w == 0) {
@@ -222,39 +217,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
                 Ms[t][j] = j < t ? bsh[t] * expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
             }
         }
-        // gated causal scores P_tj = exp(g_t - g_j) q_t.k_j (j <= t), row block m = w,
-        // as the A-operand fragments of P Delta: blocks (m, c) computed transposed
-        // (rows j, columns t); fragment (m, s) = blocks 2s and 2s + 1, hi and lo
-        {
-            f32x4 PT[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                PT[c] = zero4();
-                if (c > w) continue;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int s = 0; s < D / 32; ++s) {
-                    const u16x8 ka = *reinterpret_cast<const u16x8*>(&Ks[(16 * c + c16) * LDK + 32 * s + 8 * g4]);
-                    const u16x8 qb = *reinterpret_cast<const u16x8*>(&Qs[(16 * w + c16) * LDK + 32 * s + 8 * g4]);
-                    acc = mfma(ka, qb, acc);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * c + 4 * g4 + r, t = 16 * w + c16;
-                    PT[c][r] = j <= t ? acc[r] * expf(gsh[t] - gsh[j]) : 0.f;
-                }
-            }
-            u16x8* pdst = pfrag + ch * kTfragPerChunk;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s > (w >> 1)) continue;
-                u16x4 h0, l0, h1, l1;
-                split4(PT[2 * s], h0, l0);
-                split4(PT[2 * s + 1], h1, l1);
-                pdst[(tslot(w, s) * 2 + 0) * 64 + l] = cat(h0, h1);
-                pdst[(tslot(w, s) * 2 + 1) * 64 + l] = cat(l0, l1);
-            }
-        }
+        // (the gated causal scores P are formed in the chunk loop for this gate)
 
     } else {
         // Scores with per-channel ratios 2^{lam_t - lam_j}, row block m = w,
@@ -484,6 +447,10 @@ struct RecShared {
     u16x4 Df[2][2][2][64];
     u16x4 DBf[2][2][2][64];
 };
+template <int D>
+struct RecSharedP : RecShared<D, 0> {
+    u16x8 Pf[4][2][2][64];  // P fragments of the chunk, per token tile
+};
 
 constexpr int kRecThreads = 512;
 // CH = 1 (per-key-channel gates, log2 prefix lam): Y and Z take the gated
@@ -503,7 +470,8 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
     constexpr int KQP = C * PPR / kThreads;
     constexpr int GP = CH ? C * D / 4 : kGateFloats / 4;  // 16-byte pieces of gate data
     constexpr int GPT = (GP + 255) / 256;                  // pieces per output thread
-    __shared__ __attribute__((aligned(16))) RecShared<D, CH> sh;
+    // (the scalar gate also hands P fragments over through LDS)
+    __shared__ __attribute__((aligned(16))) std::conditional_t<CH, RecShared<D, CH>, RecSharedP<D>> sh;
     const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
 
     // work decode; with xcd_remap the ntiles slices of one (head, segment)
@@ -615,7 +583,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
     float* corr = reinterpret_cast<float*>(wsb + L.corr);
     const int64_t out_base = (((int64_t)b * T + 16 * w + 4 * g4) * H + h) * D + r0 + c16;
     float* corr_base = corr + bh * p.NC * C * D + (int64_t)(16 * w + 4 * g4) * D + r0 + c16;
-    const u16x8* pf_base = pfrag + bh * p.NC * kTfragPerChunk + l;
+    const u16x8* pf_base = CH ? pfrag + bh * p.NC * kTfragPerChunk + l : nullptr;
     u16x8 pf[2][2];
     auto load_pfrag = [&](int i) {
         const u16x8* pp = pf_base + (int64_t)i * kTfragPerChunk;
@@ -625,13 +593,58 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
             for (int hl = 0; hl < 2; ++hl)
                 pf[s][hl] = s < nks ? pp[(tslot(w, s) * 2 + hl) * 64] : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
     };
+    // scalar gate: the gated causal scores P_tj = exp(g_t - g_j) q_t.k_j (j <= t)
+    // of token tile w from the staged K and Q rows, computed transposed (rows
+    // j, columns t) so that blocks 2s and 2s + 1 form the A fragment of
+    // k-step s as they stand (hi/lo split); formed by the chain wave of the
+    // tile while the output waves stage inputs, handed over through LDS
+    auto scores = [&](int buf) {
+        const float* G = sh.G[buf];
+        const int t = 16 * w + c16;
+        const float gt = G[192 + t];
+        f32x4 PT[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            PT[c] = zero4();
+            if (c > w) continue;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.K[buf][(16 * c + c16) * LDK + 32 * s + 8 * g4]);
+                const u16x8 qb = *reinterpret_cast<const u16x8*>(&sh.Q[buf][t * LDK + 32 * s + 8 * g4]);
+                acc = mfma(ka, qb, acc);
+            }
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[192 + 16 * c + 4 * g4]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * c + 4 * g4 + r;
+                PT[c][r] = j <= t ? acc[r] * __expf(gt - gj[r]) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            u16x4 h0, l0, h1, l1;
+            split4(PT[2 * s], h0, l0);
+            split4(PT[2 * s + 1], h1, l1);
+            if constexpr (!CH) {
+                sh.Pf[w][s][0][l] = cat(h0, h1);
+                sh.Pf[w][s][1][l] = cat(l0, l1);
+            }
+        }
+    };
     auto emit_output = [&](int i, const f32x4& Zc, const f32x4& gam) {
         f32x4 O1 = zero4(), O2 = zero4(), O3 = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             if (s >= nks) continue;
-            const u16x8 pah = pf[s][0];
-            const u16x8 pal = pf[s][1];
+            u16x8 pah, pal;
+            if constexpr (CH) {
+                pah = pf[s][0];
+                pal = pf[s][1];
+            } else {
+                pah = sh.Pf[w][s][0][l];
+                pal = sh.Pf[w][s][1][l];
+            }
             const u16x8 dh = cat(sh.Df[s][0][0][l], sh.Df[s][1][0][l]);
             const u16x8 dlo = cat(sh.Df[s][0][1][l], sh.Df[s][1][1][l]);
             O1 = mfma(pah, dh, O1);
@@ -805,6 +818,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                     }
                 }
             }
+            if constexpr (!CH) scores(cur);
             __syncthreads();  // B3
 
             // ---- phase C: S^T <- decay (.) S^T + K^T Delta-bar, publish
@@ -883,7 +897,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
             } else {
                 Zc = gated_rows(sh.Q[cur], G, 16 * w + c16);
             }
-            load_pfrag(i);
+            if constexpr (CH) load_pfrag(i);
             __syncthreads();  // B2
 
             // ---- phase B: the other LDS buffer held chunk i-1, finished before
@@ -976,8 +990,9 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
     u16x8* tfrag = reinterpret_cast<u16x8*>(ws + L.prep);
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
     const size_t fbytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8));
-    u16x8* pfrag = reinterpret_cast<u16x8*>(ws + L.prep + fbytes);
-    float* gates = reinterpret_cast<float*>(ws + L.prep + 2 * fbytes);
+    // P fragments: channel gates only (the scalar-gate loop forms P itself)
+    u16x8* pfrag = CH ? reinterpret_cast<u16x8*>(ws + L.prep + fbytes) : nullptr;
+    float* gates = reinterpret_cast<float*>(ws + L.prep + (CH ? 2 : 1) * fbytes);
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
         prof_begin("k_prep_mfma", st);
@@ -1014,7 +1029,7 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
     L.prep = 0;
     const size_t gate_floats = p.gate == GDN_GATE_CHANNEL ? (size_t)C * p.dk : kGateFloats;
-    L.prep_bytes = 2 * align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
+    L.prep_bytes = (p.gate == GDN_GATE_CHANNEL ? 2 : 1) * align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
                    align256((size_t)nch * gate_floats * sizeof(float));
     size_t off = L.prep_bytes;
     if (sp.G > 1) {
