@@ -599,14 +599,11 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
     // k-step s as they stand (hi/lo split); formed by the chain wave of the
     // tile while the output waves stage inputs, handed over through LDS
     auto scores = [&](int buf) {
-        const float* G = sh.G[buf];
-        const int t = 16 * w + c16;
-        const float gt = G[192 + t];
-        f32x4 PT[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            PT[c] = zero4();
-            if (c > w) continue;
+        // block (m, c), c <= m: rows j of tile c, columns t of tile m; the ten
+        // blocks are dealt 3, 3, 2, 2 over the four chain waves
+        auto pblock = [&](int m, int c) {
+            const float* G = sh.G[buf];
+            const int t = 16 * m + c16;
             f32x4 acc = zero4();
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
@@ -614,23 +611,25 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                 const u16x8 qb = *reinterpret_cast<const u16x8*>(&sh.Q[buf][t * LDK + 32 * s + 8 * g4]);
                 acc = mfma(ka, qb, acc);
             }
+            const float gt = G[192 + t];
             const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[192 + 16 * c + 4 * g4]);
+            f32x4 pt;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int j = 16 * c + 4 * g4 + r;
-                PT[c][r] = j <= t ? acc[r] * __expf(gt - gj[r]) : 0.f;
+                pt[r] = j <= t ? acc[r] * __expf(gt - gj[r]) : 0.f;
             }
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            u16x4 h0, l0, h1, l1;
-            split4(PT[2 * s], h0, l0);
-            split4(PT[2 * s + 1], h1, l1);
+            u16x4 hi, lo;
+            split4(pt, hi, lo);
             if constexpr (!CH) {
-                sh.Pf[w][s][0][l] = cat(h0, h1);
-                sh.Pf[w][s][1][l] = cat(l0, l1);
+                reinterpret_cast<u16x4*>(&sh.Pf[m][c >> 1][0][l])[c & 1] = hi;
+                reinterpret_cast<u16x4*>(&sh.Pf[m][c >> 1][1][l])[c & 1] = lo;
             }
-        }
+        };
+        if (w == 0) { pblock(0, 0); pblock(3, 0); pblock(3, 1); }
+        else if (w == 1) { pblock(1, 0); pblock(1, 1); pblock(3, 2); }
+        else if (w == 2) { pblock(2, 0); pblock(2, 1); }
+        else { pblock(2, 2); pblock(3, 3); }
     };
     auto emit_output = [&](int i, const f32x4& Zc, const f32x4& gam) {
         f32x4 O1 = zero4(), O2 = zero4(), O3 = zero4();
@@ -714,6 +713,17 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                 else if (gseg == 0 && p.s0) sv = p.s0[(bh * D + v) * D + a];
                 else sv = 0.f;
                 Sacc[u][r] = sv;
+            }
+        }
+        if constexpr (!CH) {
+            // the never-written halves of the P fragments: blocks (0, 1), (2, 3)
+            if (w == 0) {
+                const u16x4 z = u16x4{0, 0, 0, 0};
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl) {
+                    reinterpret_cast<u16x4*>(&sh.Pf[0][0][hl][l])[1] = z;
+                    reinterpret_cast<u16x4*>(&sh.Pf[2][1][hl][l])[1] = z;
+                }
             }
         }
         publish_state();
