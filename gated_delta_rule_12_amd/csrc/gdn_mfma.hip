@@ -931,65 +931,96 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 // ---------------------------------------------------------------------------
 // Computed transposed, O^T[v][t] += sum_a S_start[v][a] R[t][a]: the start
 // state is the A operand (pre-split fragments written by the chain kernel),
-// R the B operand (rows of R are contiguous in a); wave w covers value rows
-// 16w' for w' = w, w + 4 (D = 128) and all 64 tokens.
+// R the B operand (rows of R are contiguous in a).  One workgroup takes a run
+// of kCorrChunks chunks of one segment; wave (tn, half) covers token tile tn
+// and half of the value tiles, whose start-state fragments it keeps in
+// registers for the whole run.
+constexpr int kCorrChunks = 8;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_correct_mfma(Problem p, Split sp, WsLayout L,
-                                                           char* wsb) {
+__global__ __launch_bounds__(512) void k_correct_mfma(Problem p, Split sp, WsLayout L, char* wsb,
+                                                      int runs) {
     constexpr int KS = D / 32;
     constexpr int NVT = D / 16;
-    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int g = i / sp.per;
-    if (g == 0) return;
+    constexpr int VPW = NVT / 2;  // value tiles per wave
+    const int seg = 1 + blockIdx.x / runs, run = blockIdx.x % runs;
+    const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int tn = w & 3, vh = w >> 2;
     const int64_t H = p.H, T = p.T, bh = (int64_t)b * H + h;
-    const int64_t t0 = (int64_t)i * C;
-    const int nt = (int)((T - t0) < C ? (T - t0) : C);
-    const float* R = reinterpret_cast<const float*>(wsb + L.corr) + (bh * p.NC + i) * C * D;
-    const u16x8* fr = reinterpret_cast<const u16x8*>(wsb + L.sfrag) +
-                      (bh * sp.G + g) * (int64_t)NVT * KS * 2 * 64 + l;
-
-    // B operands: R rows t = 16 tn + c16, columns 32s + 8 g4 .. +7, all 4 token tiles
-    u16x8 rh[4][KS], rl[4][KS];
+    const int i0 = seg * sp.per + run * kCorrChunks;
+    const int i1 = min(min(p.NC, (seg + 1) * sp.per), i0 + kCorrChunks);
+    if (i0 >= i1) return;
+    const u16x8* fr = reinterpret_cast<const u16x8*>(wsb + L.sfrag) + (bh * sp.G + seg) * (int64_t)NVT * KS * 2 * 64 + l;
+    u16x8 ah[VPW][KS], al[VPW][KS];
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
+    for (int q = 0; q < VPW; ++q)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int vn = vh * VPW + q;
+            ah[q][s] = fr[((vn * KS + s) * 2 + 0) * 64];
+            al[q][s] = fr[((vn * KS + s) * 2 + 1) * 64];
+        }
+    // R rows t = 16 tn + c16, columns 32s + 8 g4 .. +7, one chunk ahead
+    f32x4 rx[KS], ry[KS];
+    auto load_r = [&](int i) {
+        i = min(i, i1 - 1);
+        const float* R = reinterpret_cast<const float*>(wsb + L.corr) + (bh * p.NC + i) * C * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const float* src = R + (int64_t)(16 * tn + c16) * D + 32 * s + 8 * g4;
-            const float4 a = *reinterpret_cast<const float4*>(src);
-            const float4 c = *reinterpret_cast<const float4*>(src + 4);
-            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-            split2(a.x, a.y, h0, l0);
-            split2(a.z, a.w, h1, l1);
-            split2(c.x, c.y, h2, l2);
-            split2(c.z, c.w, h3, l3);
-            rh[tn][s] = __builtin_bit_cast(u16x8, uint4{h0, h1, h2, h3});
-            rl[tn][s] = __builtin_bit_cast(u16x8, uint4{l0, l1, l2, l3});
+            rx[s] = *reinterpret_cast<const f32x4*>(src);
+            ry[s] = *reinterpret_cast<const f32x4*>(src + 4);
         }
-    }
-    for (int vn = w; vn < NVT; vn += 4) {
-        u16x8 sh_[KS], sl_[KS];
+    };
+    // O values of the wave's tiles (column t, rows 16 vn + 4 g4 ..), one chunk
+    // ahead too; rows past the sequence end read its last row and are not stored
+    const int t = 16 * tn + c16;
+    f32x4 ov[VPW];
+    auto load_o = [&](int i) {
+        i = min(i, i1 - 1);
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        const float* o = p.out + ((b * T + t0 + min(t, nt - 1)) * H + h) * D + 4 * g4;
+#pragma unroll
+        for (int q = 0; q < VPW; ++q) ov[q] = *reinterpret_cast<const f32x4*>(o + 16 * (vh * VPW + q));
+    };
+    load_r(i0);
+    load_o(i0);
+    for (int i = i0; i < i1; ++i) {
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        f32x4 oc[VPW];
+#pragma unroll
+        for (int q = 0; q < VPW; ++q) oc[q] = ov[q];
+        // B operands from R, split hi/lo
+        u16x8 rh[KS], rl[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            sh_[s] = fr[((vn * KS + s) * 2 + 0) * 64];
-            sl_[s] = fr[((vn * KS + s) * 2 + 1) * 64];
+            const f32x4 x = rx[s], y = ry[s];
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            split2(x[0], x[1], h0, l0);
+            split2(x[2], x[3], h1, l1);
+            split2(y[0], y[1], h2, l2);
+            split2(y[2], y[3], h3, l3);
+            rh[s] = __builtin_bit_cast(u16x8, uint4{h0, h1, h2, h3});
+            rl[s] = __builtin_bit_cast(u16x8, uint4{l0, l1, l2, l3});
         }
+        load_r(i + 1);
+        load_o(i + 1);
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
+        for (int q = 0; q < VPW; ++q) {
             f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                a1 = mfma(sh_[s], rh[tn][s], a1);
-                a2 = mfma(sh_[s], rl[tn][s], a2);
-                a3 = mfma(sl_[s], rh[tn][s], a3);
+                a1 = mfma(ah[q][s], rh[s], a1);
+                a2 = mfma(ah[q][s], rl[s], a2);
+                a3 = mfma(al[q][s], rh[s], a3);
             }
-            // accumulator: column t = 16 tn + c16, rows v = 16 vn + 4 g4 + r
-            const int t = 16 * tn + c16;
+            // accumulator: column t, rows v = 16 vn + 4 g4 + r
             if (t < nt) {
-                float* o = p.out + (((int64_t)b * T + t0 + t) * H + h) * D + 16 * vn + 4 * g4;
-                f32x4 cur = *reinterpret_cast<f32x4*>(o);
-                cur += a1 + a2 + a3;
-                *reinterpret_cast<f32x4*>(o) = cur;
+                float* o = p.out + ((b * T + t0 + t) * H + h) * D + 16 * (vh * VPW + q) + 4 * g4;
+                *reinterpret_cast<f32x4*>(o) = oc[q] + a1 + a2 + a3;
             }
         }
     }
@@ -1065,12 +1096,13 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
 
 hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
                         hipStream_t st) {
-    dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
+    const int runs = (sp.per + kCorrChunks - 1) / kCorrChunks;  // runs of chunks per segment
+    dim3 grid((unsigned)((sp.G - 1) * runs), (unsigned)p.H, (unsigned)p.B);
     prof_begin("k_correct_mfma", st);
     if (p.dk == 128)
-        hipLaunchKernelGGL(k_correct_mfma<128>, grid, dim3(kThreads), 0, st, p, sp, L, ws);
+        hipLaunchKernelGGL(k_correct_mfma<128>, grid, dim3(512), 0, st, p, sp, L, ws, runs);
     else
-        hipLaunchKernelGGL(k_correct_mfma<64>, grid, dim3(kThreads), 0, st, p, sp, L, ws);
+        hipLaunchKernelGGL(k_correct_mfma<64>, grid, dim3(512), 0, st, p, sp, L, ws, runs);
     prof_end(st);
     return hipGetLastError();
 }

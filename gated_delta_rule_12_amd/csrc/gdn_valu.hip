@@ -352,83 +352,121 @@ namespace {
 // With frag != nullptr the start states are also written as bf16 hi/lo
 // B-operand fragments for the MFMA correction: [n][s][hi/lo][lane] of 8
 // bf16, lane (row v = 16n + lane%16, columns 32s + 8(lane/16) .. +7).
+// Chain of segment start states, S_start(g + 1) = S^D_end(g) + S_start(g) M_end(g)
+// (sequence-parallel notes: the true state is the increment plus the start
+// state through the scaling matrix).  Rows of S chain independently, so one
+// workgroup takes 16 rows of one head; each step is a 16 x dk x dk product in
+// fp32 on the matrix cores (16x16x4 fp32 MFMA: instruction s contracts the
+// indices 4G + s, G = lane / 16), with M_end(g + 1) fetched into registers
+// while step g computes.  With write_frag the start states are also stored
+// as bf16 hi/lo A-fragments for the MFMA output correction.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
+    const uint32_t ub = __float_as_uint(v);
+    return (uint16_t)((ub + 0x7FFFu + ((ub >> 16) & 1u)) >> 16);
+}
+
+constexpr int kChainMaxD = 128;
+constexpr int kChainMPieces = kChainMaxD * kChainMaxD / 4 / kThreads;  // float4 of M per thread
+
 __global__ __launch_bounds__(kThreads) void k_chain(Problem p, Split sp, WsLayout L, char* wsb,
                                                     int write_frag) {
     const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int dk = (int)p.dk, dv = (int)p.dv, tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int r0 = x * kRows;
     const int64_t bh = (int64_t)b * p.H + h;
     const float* sdend = reinterpret_cast<const float*>(wsb + L.sdend);
     const float* mend = reinterpret_cast<const float*>(wsb + L.mend);
     float* sstart = reinterpret_cast<float*>(wsb + L.sstart);
+    const int ldc = dk + 1, ldm = dk + 4;
 
     extern __shared__ float smem[];
-    float* Cur = smem;                    // [16][dk+1]
-    float* Nxt = Cur + kRows * (dk + 1);  // [16][dk+1]
-    float* Ms = Nxt + kRows * (dk + 1);   // [dk][dk]
+    float* bufA = smem;                   // [16][dk + 1]
+    float* bufB = bufA + kRows * ldc;     // [16][dk + 1]
+    float* Ms = bufB + kRows * ldc;       // [dk][dk + 4]
+    float* Cur = bufA;
+    float* Nxt = bufB;
     for (int e = tid; e < kRows * dk; e += kThreads) {
         const int r = e / dk, a = e - (e / dk) * dk;
-        Cur[r * (dk + 1) + a] = sdend[(bh * sp.G + 0) * dv * dk + (int64_t)(r0 + r) * dk + a];
+        Cur[r * ldc + a] = sdend[(bh * sp.G + 0) * dv * dk + (int64_t)(r0 + r) * dk + a];
     }
+    const int mp = dk * dk / 4;  // float4 pieces of M
+    f32x4v mreg[kChainMPieces];
+    auto load_m = [&](int g) {
+        const f32x4v* M = reinterpret_cast<const f32x4v*>(mend + (bh * sp.G + min(g, sp.G - 1)) * dk * dk);
+#pragma unroll
+        for (int k = 0; k < kChainMPieces; ++k) mreg[k] = M[min(tid + kThreads * k, mp - 1)];
+    };
+    load_m(1);
     for (int g = 1; g < sp.G; ++g) {
-        const float* M = mend + (bh * sp.G + g) * dk * dk;
         const float* SD = sdend + (bh * sp.G + g) * dv * dk;
         float* SS = sstart + (bh * sp.G + g) * dv * dk;
-        for (int e = tid; e < dk * dk / 4; e += kThreads)
-            reinterpret_cast<float4*>(Ms)[e] = reinterpret_cast<const float4*>(M)[e];
-        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kChainMPieces; ++k) {
+            const int e = tid + kThreads * k;
+            if (e < mp) {
+                const int a = (4 * e) / dk, c = (4 * e) % dk;
+                *reinterpret_cast<f32x4v*>(&Ms[a * ldm + c]) = mreg[k];
+            }
+        }
+        load_m(g + 1);
+        __syncthreads();  // M(g) staged, Cur = S_start(g) complete
         if (write_frag) {
-            // fragments of rows r0..r0+15 (one 16-row tile n = x), every k-step
+            // rows r0..r0+15 as A fragments of every k-step: lane (row lane % 16,
+            // keys 32s + 8 (lane / 16) ..), hi and lo halves, 16-byte stores
             const int ks = dk / 32;
-            uint16_t* fr = reinterpret_cast<uint16_t*>(wsb + L.sfrag) +
-                           ((bh * sp.G + g) * (dv / 16) + x) * (int64_t)ks * 2 * 64 * 8;
+            u16x8v* fr = reinterpret_cast<u16x8v*>(wsb + L.sfrag) + ((bh * sp.G + g) * (dv / 16) + x) * (int64_t)ks * 2 * 64;
             for (int f = tid; f < ks * 64; f += kThreads) {
                 const int s = f >> 6, lane = f & 63;
                 const int r = lane & 15, a0 = 32 * s + 8 * (lane >> 4);
+                u16x8v hi, lo;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float v = Cur[r * (dk + 1) + a0 + e];
-                    const uint32_t ub = __float_as_uint(v);
-                    const uint32_t hi = (ub + 0x7FFFu + ((ub >> 16) & 1u)) >> 16;
-                    const float rem = v - __uint_as_float(hi << 16);
-                    const uint32_t ur = __float_as_uint(rem);
-                    const uint32_t lo = (ur + 0x7FFFu + ((ur >> 16) & 1u)) >> 16;
-                    fr[((s * 2 + 0) * 64 + lane) * 8 + e] = (uint16_t)hi;
-                    fr[((s * 2 + 1) * 64 + lane) * 8 + e] = (uint16_t)lo;
+                    const float v = Cur[r * ldc + a0 + e];
+                    const uint16_t hb = bf16_rne(v);
+                    hi[e] = hb;
+                    lo[e] = bf16_rne(v - __uint_as_float((uint32_t)hb << 16));
                 }
+                fr[(s * 2 + 0) * 64 + lane] = hi;
+                fr[(s * 2 + 1) * 64 + lane] = lo;
             }
         }
         for (int e = tid; e < kRows * dk; e += kThreads) {
             const int r = e / dk, c = e - (e / dk) * dk;
-            SS[(int64_t)(r0 + r) * dk + c] = Cur[r * (dk + 1) + c];
+            SS[(int64_t)(r0 + r) * dk + c] = Cur[r * ldc + c];
         }
-        // each thread: one row r, eight consecutive columns c0..c0+7
-        for (int e = tid; e < kRows * (dk / 8); e += kThreads) {
-            const int r = e / (dk / 8), c0 = 8 * (e - r * (dk / 8));
-            float acc[8];
+        // Nxt = SD + Cur M: wave w takes column tiles w, w + 4, ...
+        // (four independent accumulator chains, one per instruction s)
+        for (int nt = w; nt < dk / 16; nt += 4) {
+            f32x4v acc[4];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] = SD[(int64_t)(r0 + r) * dk + c0 + q];
-            for (int a = 0; a < dk; ++a) {
-                const float cv = Cur[r * (dk + 1) + a];
-                const float4 m0 = *reinterpret_cast<const float4*>(&Ms[a * dk + c0]);
-                const float4 m1 = *reinterpret_cast<const float4*>(&Ms[a * dk + c0 + 4]);
-                acc[0] += cv * m0.x; acc[1] += cv * m0.y; acc[2] += cv * m0.z; acc[3] += cv * m0.w;
-                acc[4] += cv * m1.x; acc[5] += cv * m1.y; acc[6] += cv * m1.z; acc[7] += cv * m1.w;
+            for (int i = 0; i < 4; ++i) {
+                acc[0][i] = SD[(int64_t)(r0 + 4 * g4 + i) * dk + 16 * nt + c16];
+                acc[1][i] = acc[2][i] = acc[3][i] = 0.f;
             }
+            for (int kb = 0; kb < dk / 16; ++kb) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) Nxt[r * (dk + 1) + c0 + q] = acc[q];
+                for (int s = 0; s < 4; ++s)
+                    acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(Cur[c16 * ldc + 16 * kb + 4 * g4 + s],
+                                                                  Ms[(16 * kb + 4 * g4 + s) * ldm + 16 * nt + c16],
+                                                                  acc[s], 0, 0, 0);
+            }
+            const f32x4v sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Nxt[(4 * g4 + i) * ldc + 16 * nt + c16] = sum[i];
         }
-        __syncthreads();
-        for (int e = tid; e < kRows * dk; e += kThreads) {
-            const int r = e / dk, a = e - (e / dk) * dk;
-            Cur[r * (dk + 1) + a] = Nxt[r * (dk + 1) + a];
-        }
-        __syncthreads();
+        __syncthreads();  // Nxt complete; Cur and Ms free
+        float* t = Cur;
+        Cur = Nxt;
+        Nxt = t;
     }
     if (p.s_out) {
         for (int e = tid; e < kRows * dk; e += kThreads) {
             const int r = e / dk, a = e - (e / dk) * dk;
-            p.s_out[(bh * dv + r0 + r) * dk + a] = Cur[r * (dk + 1) + a];
+            p.s_out[(bh * dv + r0 + r) * dk + a] = Cur[r * ldc + a];
         }
     }
 }
@@ -466,7 +504,7 @@ hipError_t seqpar_finish(const Problem& p, const Split& sp, char* ws, const WsLa
     const int dk = (int)p.dk, dv = (int)p.dv;
     {
         dim3 grid(dv / kRows, (unsigned)p.H, (unsigned)p.B);
-        const size_t lds = sizeof(float) * (2 * kRows * (dk + 1) + (size_t)dk * dk);
+        const size_t lds = sizeof(float) * (2 * kRows * (dk + 1) + (size_t)dk * (dk + 4));
         if (lds > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chain),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
