@@ -60,10 +60,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload_name):
-    """HBM bytes per step from profiles/traffic_<workload>.json (FETCH_SIZE and
-    WRITE_SIZE per dispatch, scaled by the plain-copy calibration), or None
-    when absent or taken on other kernel sources."""
+def stored_traffic(workload_name, kernel):
+    """HBM bytes (read + write) of one launch of `kernel` from
+    profiles/traffic_<workload>.json (FETCH_SIZE and WRITE_SIZE per dispatch,
+    scaled by the plain-copy calibration), or None when absent, taken on
+    other kernel sources, or not recorded for that kernel."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
     if not os.path.exists(path):
         return None
@@ -71,7 +72,8 @@ def stored_traffic(workload_name):
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_step")
+    k = rec.get("per_kernel", {}).get(kernel)
+    return None if k is None else round(k["read_bytes"] + k["write_bytes"])
 
 
 def copy_calibration(mbytes: int, reps: int = 5):
@@ -137,6 +139,8 @@ def main():
     ap.add_argument("--segments", type=int, default=None,
                     help="sequence-parallel segments (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-stream", action="store_true",
+                    help="sequence parallel: skip the single-stream comparison (for kernel traces)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -211,7 +215,7 @@ def main():
     step_achieved = abytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(w.name) if G == w.n_segments else None,
+            "traffic": stored_traffic(w.name, dominant) if G == w.n_segments else None,
             "kernel": dominant,
             "kernel_launches_per_step": launches[dominant],
             "kernel_avg_launch_us": round(dom_us / launches[dominant], 2),
@@ -222,7 +226,7 @@ def main():
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     extra = {}
-    if G > 1:
+    if G > 1 and not args.no_single_stream:
         for _ in range(2):
             step(1)
         torch.cuda.synchronize()
