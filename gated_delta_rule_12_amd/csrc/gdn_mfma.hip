@@ -135,6 +135,16 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     const unsigned short* kin = static_cast<const unsigned short*>(p.k);
     const unsigned short* qin = static_cast<const unsigned short*>(p.q);
 
+    // (scalar gate: wave 0's alpha and beta loads are issued first, so that
+    // their latency overlaps the K rows')
+    float araw = 1.f, braw = 0.f;
+    if constexpr (!CH) {
+        if (w == 0 && l < nt) {
+            const int64_t row = ((int64_t)b * T + t0 + l) * H + h;
+            araw = p.alpha[row];
+            braw = p.beta[row];
+        }
+    }
     for (int e = tid; e < C * PPR; e += kThreads) {
         const int t = e / PPR, c8 = e - (e / PPR) * PPR;
         uint4 kv = make_uint4(0, 0, 0, 0);
@@ -143,12 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     }
     if constexpr (!CH) {
         if (w == 0) {
-            float la = 0.f, bt = 0.f;
-            if (l < nt) {
-                const int64_t row = ((int64_t)b * T + t0 + l) * H + h;
-                la = logf(p.alpha[row]);
-                bt = p.beta[row];
-            }
+            const float la = __logf(araw), bt = braw;
             const float gv = wave_incl_scan(la, l);
             float gprev = __shfl_up(gv, 1, 64);
             if (l == 0) gprev = 0.f;
@@ -158,11 +163,11 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
             gpsh[l] = gpv;
             bsh[l] = bt;
             float* gb = gates + ch * kGateFloats;
-            gb[l] = expf(gv);
-            gb[64 + l] = expf(gpv);
-            gb[128 + l] = expf(gC - gv);
+            gb[l] = __expf(gv);
+            gb[64 + l] = __expf(gpv);
+            gb[128 + l] = __expf(gC - gv);
             gb[192 + l] = gv;
-            if (l == 0) gb[256] = expf(gC);
+            if (l == 0) gb[256] = __expf(gC);
         }
         __syncthreads();
     } else {
@@ -200,23 +205,26 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     }
 
     if constexpr (!CH) {
-        // A_tj = beta_t exp(g'_t - g_j) k_t.k_j for j < t: row block w, column blocks <= w
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            if (nb > w) continue;
+        // A_tj = beta_t exp(g'_t - g_j) k_t.k_j for j < t, blocks (m, nb) with
+        // nb <= m, the ten blocks dealt 3, 3, 2, 2 over the waves
+        auto ablock = [&](int m, int nb) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
-                const u16x8 a = *reinterpret_cast<const u16x8*>(&Ks[(16 * w + c16) * LDK + 32 * s + 8 * g4]);
+                const u16x8 a = *reinterpret_cast<const u16x8*>(&Ks[(16 * m + c16) * LDK + 32 * s + 8 * g4]);
                 const u16x8 bb = *reinterpret_cast<const u16x8*>(&Ks[(16 * nb + c16) * LDK + 32 * s + 8 * g4]);
                 acc = mfma(a, bb, acc);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * g4 + r, j = 16 * nb + c16;
-                Ms[t][j] = j < t ? bsh[t] * expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
+                const int t = 16 * m + 4 * g4 + r, j = 16 * nb + c16;
+                Ms[t][j] = j < t ? bsh[t] * __expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
             }
-        }
+        };
+        if (w == 0) { ablock(0, 0); ablock(3, 0); ablock(3, 1); }
+        else if (w == 1) { ablock(1, 0); ablock(1, 1); ablock(3, 2); }
+        else if (w == 2) { ablock(2, 0); ablock(2, 1); }
+        else { ablock(2, 2); ablock(3, 3); }
         // (the gated causal scores P are formed in the chunk loop for this gate)
 
     } else {
@@ -352,21 +360,43 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     }
     __syncthreads();  // K is dead from here on; its LDS holds T
 
-    // diagonal 16 x 16 blocks of T = (I + A)^{-1}: forward substitution, one
-    // column per lane; the other lanes clear the blocks above the diagonal
-    if (l < 16) {
-        const int j = c16;
-        float col[16];
+    // diagonal 16 x 16 blocks of T = (I + A)^{-1}, block w per wave: with N
+    // the strictly lower block (N^16 = 0), (I + N)^{-1} = (I - N)(I + N^2)
+    // (I + N^4)(I + N^8), three rounds of P <- P P, X <- X + X P on fp32 MFMA.
+    // Accumulators (lane: column c16, rows 4 g4 + i) serve as B operands as
+    // they stand; A operands pass through the block's own LDS tiles (Ms's
+    // diagonal block, dead after this, and Ts's).
+    {
+        float* Pb = &Ms[16 * w][16 * w];
+        float* Xb = &Ts[16 * w][16 * w];
+        constexpr int LD = C + 1;
+        f32x4 pm, xm;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float x = 0.f;
-#pragma unroll
-            for (int mm = 0; mm < t; ++mm) x -= Ms[16 * w + t][16 * w + mm] * col[mm];
-            col[t] = t < j ? 0.f : (t == j ? 1.f : x);
+        for (int i = 0; i < 4; ++i) {
+            pm[i] = -Pb[(4 * g4 + i) * LD + c16];
+            xm[i] = (4 * g4 + i == c16 ? 1.f : 0.f) + pm[i];
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) Ts[16 * w + t][16 * w + j] = col[t];
+        for (int round = 0; round < 3; ++round) {
+            // P <- P P
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Pb[(4 * g4 + i) * LD + c16] = pm[i];
+            f32x4 np = zero4();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) np = mfma_f32(Pb[c16 * LD + 4 * g4 + q], pm[q], np);
+            pm = np;
+            // X <- X + X P
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Xb[(4 * g4 + i) * LD + c16] = xm[i];
+            f32x4 nx = xm;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) nx = mfma_f32(Xb[c16 * LD + 4 * g4 + q], pm[q], nx);
+            xm = nx;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Xb[(4 * g4 + i) * LD + c16] = xm[i];
     }
+    // clear the blocks above the diagonal
     for (int e = tid; e < C * C; e += kThreads) {
         const int t = e >> 6, j = e & 63;
         if ((j >> 4) > (t >> 4)) Ts[t][j] = 0.f;
@@ -410,6 +440,173 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
         for (int e = 0; e < 8; e += 2) {
             const int j0 = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
             split2(Ts[t][j0] * bsh[j0], Ts[t][j0 + 1] * bsh[j0 + 1], hi[e >> 1], lo[e >> 1]);
+        }
+        dst[(slot * 2 + 0) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
+        dst[(slot * 2 + 1) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
+    }
+}
+
+// Scalar gate, stage 1 with a small LDS footprint (≈22 KiB, so about seven
+// workgroups share a CU): the Gram operands come straight from HBM (16-byte
+// fragment loads), and one 64 x 68 fp32 tile holds both the UT system A
+// (strictly lower blocks stored transposed in the upper triangle, diagonal
+// blocks in place until their inverse replaces them) and T = (I + A)^{-1}
+// (lower triangle).  Same algebra and outputs as k_prep_mfma<D, 0>.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfrag, float* gates) {
+    constexpr int LDA = C + 4;
+    __shared__ __attribute__((aligned(16))) float AT[C * LDA];
+    __shared__ float Pscr[4][16 * 17];  // per-wave scratch of the diagonal inverse
+    __shared__ float gsh[C], gpsh[C], bsh[C];
+
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int64_t H = p.H, T = p.T;
+    const int64_t t0 = (int64_t)i * C;
+    const int nt = (int)((T - t0) < C ? (T - t0) : C);
+    const int64_t ch = ((int64_t)b * H + h) * p.NC + i;
+    const unsigned short* kin = static_cast<const unsigned short*>(p.k);
+
+    // gate prefix (wave 0)
+    if (w == 0) {
+        float la = 0.f, bt = 0.f;
+        if (l < nt) {
+            const int64_t row = ((int64_t)b * T + t0 + l) * H + h;
+            la = __logf(p.alpha[row]);
+            bt = p.beta[row];
+        }
+        const float gv = wave_incl_scan(la, l);
+        float gprev = __shfl_up(gv, 1, 64);
+        if (l == 0) gprev = 0.f;
+        const float gpv = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
+        const float gC = __shfl(gv, 63, 64);
+        gsh[l] = gv;
+        gpsh[l] = gpv;
+        bsh[l] = bt;
+        float* gb = gates + ch * kGateFloats;
+        gb[l] = __expf(gv);
+        gb[64 + l] = __expf(gpv);
+        gb[128 + l] = __expf(gC - gv);
+        gb[192 + l] = gv;
+        if (l == 0) gb[256] = __expf(gC);
+    }
+    // K rows staged (coalesced) in the tile's own LDS, bf16 at row stride D + 8
+    // (17408 bytes, the size of the fp32 tile for D = 128); rows past the
+    // sequence end are zero
+    constexpr int LDK = D + 8, PPR = D / 8;
+    static_assert(C * LDK * 2 <= C * LDA * 4, "K staging fits the tile");
+    unsigned short* Ks = reinterpret_cast<unsigned short*>(AT);
+    for (int e = tid; e < C * PPR; e += kThreads) {
+        const int t = e / PPR, c8 = e - (e / PPR) * PPR;
+        uint4 kv = make_uint4(0, 0, 0, 0);
+        if (t < nt) kv = *reinterpret_cast<const uint4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
+        *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = kv;
+    }
+    __syncthreads();  // K rows and the gate prefix visible
+    auto krow = [&](int m, int s) { return *reinterpret_cast<const u16x8*>(&Ks[(16 * m + c16) * LDK + 32 * s + 8 * g4]); };
+    // Gram blocks (m, nb), nb <= m, dealt 3, 3, 2, 2 over the waves
+    f32x4 acc[3];
+    int bm[3], bn[3], nbk;
+    if (w == 0) { bm[0] = 0; bn[0] = 0; bm[1] = 3; bn[1] = 0; bm[2] = 3; bn[2] = 1; nbk = 3; }
+    else if (w == 1) { bm[0] = 1; bn[0] = 0; bm[1] = 1; bn[1] = 1; bm[2] = 3; bn[2] = 2; nbk = 3; }
+    else if (w == 2) { bm[0] = 2; bn[0] = 0; bm[1] = 2; bn[1] = 1; bm[2] = 0; bn[2] = 0; nbk = 2; }
+    else { bm[0] = 2; bn[0] = 2; bm[1] = 3; bn[1] = 3; bm[2] = 0; bn[2] = 0; nbk = 2; }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        acc[q] = zero4();
+        if (q >= nbk) continue;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) acc[q] = mfma(krow(bm[q], s), krow(bn[q], s), acc[q]);
+    }
+    __syncthreads();  // K is dead: the tile now takes A
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        if (q >= nbk) continue;
+        const int m = bm[q], nb = bn[q];
+        const int j = 16 * nb + c16;
+        f32x4 a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * m + 4 * g4 + r;
+            a[r] = j < t ? bsh[t] * __expf(gpsh[t] - gsh[j]) * acc[q][r] : 0.f;
+        }
+        if (nb < m) {
+            // A_tj stored at (j, t): upper triangle
+            *reinterpret_cast<f32x4*>(&AT[j * LDA + 16 * m + 4 * g4]) = a;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) AT[(16 * m + 4 * g4 + r) * LDA + j] = a[r];
+        }
+    }
+    __syncthreads();
+
+    // diagonal block w: (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8),
+    // three rounds of P <- P P, X <- X + X P on fp32 MFMA (N^16 = 0)
+    {
+        float* Pb = Pscr[w];
+        float* Xb = &AT[(16 * w) * LDA + 16 * w];
+        f32x4 pm, xm;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pm[r] = -Xb[(4 * g4 + r) * LDA + c16];
+            xm[r] = (4 * g4 + r == c16 ? 1.f : 0.f) + pm[r];
+        }
+#pragma unroll
+        for (int round = 0; round < 3; ++round) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Pb[(4 * g4 + r) * 17 + c16] = pm[r];
+            f32x4 np = zero4();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) np = mfma_f32(Pb[c16 * 17 + 4 * g4 + q], pm[q], np);
+            pm = np;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
+            f32x4 nx = xm;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) nx = mfma_f32(Xb[c16 * LDA + 4 * g4 + q], pm[q], nx);
+            xm = nx;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
+    }
+    __syncthreads();
+
+    // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+    for (int d = 1; d < 4; ++d) {
+        if (w < 4 - d) {
+            const int jb = w, ib = w + d;
+            f32x4 X = zero4();
+            for (int kb = jb; kb < ib; ++kb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    X = mfma_f32(AT[(16 * kb + 4 * g4 + q) * LDA + 16 * ib + c16],   // A_ib,kb (transposed)
+                                 AT[(16 * kb + 4 * g4 + q) * LDA + 16 * jb + c16], X);  // T_kb,jb
+            }
+            f32x4 Tij = zero4();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Tij = mfma_f32(AT[(16 * ib + c16) * LDA + 16 * ib + 4 * g4 + q], X[q], Tij);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) AT[(16 * ib + 4 * g4 + r) * LDA + 16 * jb + c16] = -Tij[r];
+        }
+        __syncthreads();
+    }
+
+    // T' = T diag(beta) as A-operand fragments (entries above the block
+    // diagonal are zero; the tile holds A there)
+    u16x8* dst = tfrag + ch * kTfragPerChunk;
+    for (int f = tid; f < kTslots * 64; f += kThreads) {
+        const int slot = f >> 6, lane = f & 63;
+        const int m = slot < 2 ? slot : 2 + ((slot - 2) >> 1);
+        const int s = slot < 2 ? 0 : ((slot - 2) & 1);
+        const int t = 16 * m + (lane & 15), gg = lane >> 4;
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int j0 = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
+            const bool up = (j0 >> 4) > m;
+            const float v0 = up ? 0.f : AT[t * LDA + j0] * bsh[j0];
+            const float v1 = up ? 0.f : AT[t * LDA + j0 + 1] * bsh[j0 + 1];
+            split2(v0, v1, hi[e >> 1], lo[e >> 1]);
         }
         dst[(slot * 2 + 0) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
         dst[(slot * 2 + 1) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
@@ -1037,7 +1234,10 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
         prof_begin("k_prep_mfma", st);
-        hipLaunchKernelGGL((k_prep_mfma<D, CH>), grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
+        if constexpr (CH)
+            hipLaunchKernelGGL((k_prep_mfma<D, CH>), grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
+        else
+            hipLaunchKernelGGL((k_prep_scalar<D>), grid, dim3(kThreads), 0, st, p, tfrag, gates);
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
