@@ -18,10 +18,12 @@
 // operands); accumulation is fp32.  Gate factors are applied on the fp32
 // side, as ratios exp(g_t - g_j) <= 1.
 //
-// k_prep_mfma: one workgroup (4 waves) per (batch, head, chunk): gate prefix,
-//   Gram K K^T on MFMA, the gated UT system, its inverse by blocked forward
-//   substitution in fp32 (16 x 16 diagonal blocks, then off-diagonal blocks
-//   by block distance), T' written as bf16 hi/lo MFMA A-operand fragments.
+// Stage 1, one workgroup (4 waves) per (batch, head, chunk): gate prefix,
+//   Gram K K^T on MFMA, the gated UT system and its inverse in fp32 (16 x 16
+//   diagonal blocks, then off-diagonal blocks by block distance), T' written
+//   as bf16 hi/lo MFMA A-operand fragments.  k_prep_scalar (scalar gate;
+//   the gated scores P are formed in the chunk loop) and k_prep_channel
+//   (per-key-channel gate; also the log2-prefix table and P).
 // k_rec_mfma: one workgroup per (batch, head, segment, 16-row slice of the
 //   state); the slice of S^T lives in registers (fp32) across the chunk loop.
 //   Wave w owns token rows 16w..16w+15 of every chunk product and key rows
@@ -104,25 +106,25 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Per-key-channel gates (CH = 1): the gate is a vector per token and the
+// Stage 1 for per-key-channel gates: the gate is a vector per token and the
 // chunk-local prefix becomes a C x D table, kept in log2 units
 // (lam[t][a] = sum_{s <= t} log2 alpha_sa, so every ratio is one exp2) and
 // stored for the chunk loop.  Intra-chunk ratios 2^{lam_t - lam_j} differ per
 // channel, so they enter the MFMA operands as row and key factors about an
 // anchor token, per 16-token row block (the secondary chunking of the GLA
 // gating section).
-template <int D, int CH>
-__global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag, u16x8* pfrag,
-                                                        float* gates) {
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfrag, u16x8* pfrag,
+                                                           float* gates) {
     constexpr int LDK = D + 8;
     constexpr int PPR = D / 8;
     constexpr int kBufBytes = (C * LDK * 2 > C * (C + 1) * 4) ? C * LDK * 2 : C * (C + 1) * 4;
     // K (bf16, row stride LDK) during the Gram product, then T (fp32 [C][C+1])
     __shared__ __attribute__((aligned(16))) unsigned char kt_buf[kBufBytes];
     __shared__ __attribute__((aligned(16))) float Ms[C][C + 1];
-    __shared__ float gsh[CH ? 1 : C], gpsh[CH ? 1 : C], bsh[C];
+    __shared__ float bsh[C];
     // channel log2 prefix; rows padded by 16 bytes against bank conflicts
-    __shared__ __attribute__((aligned(16))) float gt[CH ? C : 1][CH ? D + 4 : 1];
+    __shared__ __attribute__((aligned(16))) float gt[C][D + 4];
     unsigned short* Ks = reinterpret_cast<unsigned short*>(kt_buf);
     float (*Ts)[C + 1] = reinterpret_cast<float (*)[C + 1]>(kt_buf);
 
@@ -135,228 +137,172 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     const unsigned short* kin = static_cast<const unsigned short*>(p.k);
     const unsigned short* qin = static_cast<const unsigned short*>(p.q);
 
-    // (scalar gate: wave 0's alpha and beta loads are issued first, so that
-    // their latency overlaps the K rows')
-    float araw = 1.f, braw = 0.f;
-    if constexpr (!CH) {
-        if (w == 0 && l < nt) {
-            const int64_t row = ((int64_t)b * T + t0 + l) * H + h;
-            araw = p.alpha[row];
-            braw = p.beta[row];
-        }
-    }
     for (int e = tid; e < C * PPR; e += kThreads) {
         const int t = e / PPR, c8 = e - (e / PPR) * PPR;
         uint4 kv = make_uint4(0, 0, 0, 0);
         if (t < nt) kv = *reinterpret_cast<const uint4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
         *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = kv;
     }
-    if constexpr (!CH) {
-        if (w == 0) {
-            const float la = __logf(araw), bt = braw;
-            const float gv = wave_incl_scan(la, l);
-            float gprev = __shfl_up(gv, 1, 64);
-            if (l == 0) gprev = 0.f;
-            const float gpv = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
-            const float gC = __shfl(gv, 63, 64);
-            gsh[l] = gv;
-            gpsh[l] = gpv;
-            bsh[l] = bt;
-            float* gb = gates + ch * kGateFloats;
-            gb[l] = __expf(gv);
-            gb[64 + l] = __expf(gpv);
-            gb[128 + l] = __expf(gC - gv);
-            gb[192 + l] = gv;
-            if (l == 0) gb[256] = __expf(gC);
-        }
-        __syncthreads();
-    } else {
-        if (w == 0) bsh[l] = l < nt ? p.beta[((int64_t)b * T + t0 + l) * H + h] : 0.f;
-        // log2 prefix lam[t][a] = sum_{s <= t} log2 alpha_sa (padding tokens add
-        // zero): thread (group, a4) scans TPG tokens of four channels in
-        // registers, then adds the totals of the earlier groups
-        constexpr int A4 = D / 4, NG = kThreads / A4, TPG = C / NG;
-        f32x4(*part)[A4] = reinterpret_cast<f32x4(*)[A4]>(&Ms[0][0]);  // Ms is free until L
-        const int a4 = tid % A4, grp = tid / A4;
-        f32x4 run = zero4(), vals[TPG];
+    if (w == 0) bsh[l] = l < nt ? p.beta[((int64_t)b * T + t0 + l) * H + h] : 0.f;
+    // log2 prefix lam[t][a] = sum_{s <= t} log2 alpha_sa (padding tokens add
+    // zero): thread (group, a4) scans TPG tokens of four channels in
+    // registers, then adds the totals of the earlier groups
+    constexpr int A4 = D / 4, NG = kThreads / A4, TPG = C / NG;
+    f32x4(*part)[A4] = reinterpret_cast<f32x4(*)[A4]>(&Ms[0][0]);  // Ms is free until L
+    const int a4 = tid % A4, grp = tid / A4;
+    f32x4 run = zero4(), vals[TPG];
 #pragma unroll
-        for (int u = 0; u < TPG; ++u) {
-            const int t = grp * TPG + u;
-            if (t < nt) {
-                const f32x4 av = *reinterpret_cast<const f32x4*>(
-                    p.alpha + (((int64_t)b * T + t0 + t) * H + h) * D + 4 * a4);
-                run += f32x4{log2f(av[0]), log2f(av[1]), log2f(av[2]), log2f(av[3])};
-            }
-            vals[u] = run;
+    for (int u = 0; u < TPG; ++u) {
+        const int t = grp * TPG + u;
+        if (t < nt) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(
+                p.alpha + (((int64_t)b * T + t0 + t) * H + h) * D + 4 * a4);
+            run += f32x4{log2f(av[0]), log2f(av[1]), log2f(av[2]), log2f(av[3])};
         }
-        part[grp][a4] = run;
-        __syncthreads();
-        f32x4 off = zero4();
-        for (int gg = 0; gg < grp; ++gg) off += part[gg][a4];
-        float* gdst = gates + ch * (int64_t)C * D;
-#pragma unroll
-        for (int u = 0; u < TPG; ++u) {
-            const int t = grp * TPG + u;
-            const f32x4 v = vals[u] + off;
-            *reinterpret_cast<f32x4*>(&gt[t][4 * a4]) = v;
-            *reinterpret_cast<f32x4*>(&gdst[t * D + 4 * a4]) = v;
-        }
-        __syncthreads();
+        vals[u] = run;
     }
+    part[grp][a4] = run;
+    __syncthreads();
+    f32x4 off = zero4();
+    for (int gg = 0; gg < grp; ++gg) off += part[gg][a4];
+    float* gdst = gates + ch * (int64_t)C * D;
+#pragma unroll
+    for (int u = 0; u < TPG; ++u) {
+        const int t = grp * TPG + u;
+        const f32x4 v = vals[u] + off;
+        *reinterpret_cast<f32x4*>(&gt[t][4 * a4]) = v;
+        *reinterpret_cast<f32x4*>(&gdst[t * D + 4 * a4]) = v;
+    }
+    __syncthreads();
 
-    if constexpr (!CH) {
-        // A_tj = beta_t exp(g'_t - g_j) k_t.k_j for j < t, blocks (m, nb) with
-        // nb <= m, the ten blocks dealt 3, 3, 2, 2 over the waves
-        auto ablock = [&](int m, int nb) {
-            f32x4 acc = zero4();
+    // Scores with per-channel ratios 2^{lam_t - lam_j}, row block m = w,
+    // every key block c <= w anchored at p = 16w - 1 (lam_{-1} = 0):
+    //   P_tj = sum_a [q_ta 2^{lam_ta - lam_pa}] [k_ja 2^{lam_pa - lam_ja}]   (j <= t)
+    //   L_tj = sum_a [k_ta 2^{lam'_ta - lam_pa}] [k_ja 2^{lam_pa - lam_ja}]  (j < t)
+    // Row factors are at most one, key factors too off the diagonal block;
+    // on it they grow with the decay across the block.  All gated operands
+    // are split hi/lo; accumulators are transposed (rows j, columns t).
+    const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
+    const int pa = 16 * w - 1, t = 16 * w + c16;
+    const int tp = ptd ? t - 1 : t;  // row of lam' (-1: zero)
+    const f32x4 z4 = zero4();
+    u16x8 qh[D / 32], ql[D / 32], lh[D / 32], ll[D / 32];
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
-                const u16x8 a = *reinterpret_cast<const u16x8*>(&Ks[(16 * m + c16) * LDK + 32 * s + 8 * g4]);
-                const u16x8 bb = *reinterpret_cast<const u16x8*>(&Ks[(16 * nb + c16) * LDK + 32 * s + 8 * g4]);
-                acc = mfma(a, bb, acc);
+    for (int s = 0; s < D / 32; ++s) {
+        const int a0 = 32 * s + 8 * g4;
+        u16x8 qt = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < nt)
+            qt = *reinterpret_cast<const u16x8*>(qin + (((int64_t)b * T + t0 + t) * H + h) * D + a0);
+        const u16x8 kt_ = *reinterpret_cast<const u16x8*>(&Ks[t * LDK + a0]);
+        const f32x4 gp0 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0]) : z4;
+        const f32x4 gp1 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0 + 4]) : z4;
+        const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&gt[t][a0]);
+        const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&gt[t][a0 + 4]);
+        const f32x4 gq0 = tp >= 0 ? *reinterpret_cast<const f32x4*>(&gt[tp][a0]) : z4;
+        const f32x4 gq1 = tp >= 0 ? *reinterpret_cast<const f32x4*>(&gt[tp][a0 + 4]) : z4;
+        uint32_t h1[4], l1[4], h2[4], l2[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            float xq[2], xl[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int ee = e + u;
+                const float g_p = ee < 4 ? gp0[ee] : gp1[ee - 4];
+                xq[u] = gdn_bf16_to_f32(qt[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gt0[ee] : gt1[ee - 4]) - g_p);
+                xl[u] = gdn_bf16_to_f32(kt_[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gq0[ee] : gq1[ee - 4]) - g_p);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * m + 4 * g4 + r, j = 16 * nb + c16;
-                Ms[t][j] = j < t ? bsh[t] * __expf(gpsh[t] - gsh[j]) * acc[r] : 0.f;
-            }
-        };
-        if (w == 0) { ablock(0, 0); ablock(3, 0); ablock(3, 1); }
-        else if (w == 1) { ablock(1, 0); ablock(1, 1); ablock(3, 2); }
-        else if (w == 2) { ablock(2, 0); ablock(2, 1); }
-        else { ablock(2, 2); ablock(3, 3); }
-        // (the gated causal scores P are formed in the chunk loop for this gate)
-
-    } else {
-        // Scores with per-channel ratios 2^{lam_t - lam_j}, row block m = w,
-        // every key block c <= w anchored at p = 16w - 1 (lam_{-1} = 0):
-        //   P_tj = sum_a [q_ta 2^{lam_ta - lam_pa}] [k_ja 2^{lam_pa - lam_ja}]   (j <= t)
-        //   L_tj = sum_a [k_ta 2^{lam'_ta - lam_pa}] [k_ja 2^{lam_pa - lam_ja}]  (j < t)
-        // Row factors are at most one, key factors too off the diagonal block;
-        // on it they grow with the decay across the block.  All gated operands
-        // are split hi/lo; accumulators are transposed (rows j, columns t).
-        const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
-        const int pa = 16 * w - 1, t = 16 * w + c16;
-        const int tp = ptd ? t - 1 : t;  // row of lam' (-1: zero)
-        const f32x4 z4 = zero4();
-        u16x8 qh[D / 32], ql[D / 32], lh[D / 32], ll[D / 32];
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            const int a0 = 32 * s + 8 * g4;
-            u16x8 qt = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (t < nt)
-                qt = *reinterpret_cast<const u16x8*>(qin + (((int64_t)b * T + t0 + t) * H + h) * D + a0);
-            const u16x8 kt_ = *reinterpret_cast<const u16x8*>(&Ks[t * LDK + a0]);
-            const f32x4 gp0 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0]) : z4;
-            const f32x4 gp1 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0 + 4]) : z4;
-            const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&gt[t][a0]);
-            const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&gt[t][a0 + 4]);
-            const f32x4 gq0 = tp >= 0 ? *reinterpret_cast<const f32x4*>(&gt[tp][a0]) : z4;
-            const f32x4 gq1 = tp >= 0 ? *reinterpret_cast<const f32x4*>(&gt[tp][a0 + 4]) : z4;
-            uint32_t h1[4], l1[4], h2[4], l2[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float xq[2], xl[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int ee = e + u;
-                    const float g_p = ee < 4 ? gp0[ee] : gp1[ee - 4];
-                    xq[u] = gdn_bf16_to_f32(qt[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gt0[ee] : gt1[ee - 4]) - g_p);
-                    xl[u] = gdn_bf16_to_f32(kt_[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gq0[ee] : gq1[ee - 4]) - g_p);
-                }
-                split2(xq[0], xq[1], h1[e >> 1], l1[e >> 1]);
-                split2(xl[0], xl[1], h2[e >> 1], l2[e >> 1]);
-            }
-            qh[s] = __builtin_bit_cast(u16x8, uint4{h1[0], h1[1], h1[2], h1[3]});
-            ql[s] = __builtin_bit_cast(u16x8, uint4{l1[0], l1[1], l1[2], l1[3]});
-            lh[s] = __builtin_bit_cast(u16x8, uint4{h2[0], h2[1], h2[2], h2[3]});
-            ll[s] = __builtin_bit_cast(u16x8, uint4{l2[0], l2[1], l2[2], l2[3]});
+            split2(xq[0], xq[1], h1[e >> 1], l1[e >> 1]);
+            split2(xl[0], xl[1], h2[e >> 1], l2[e >> 1]);
         }
-        // Past 2^92 (about e^64) of decay across the diagonal block on some
-        // channel (gates far below any trained range) that block is summed
-        // directly instead.
-        float span = 0.f;
-        for (int a = l; a < D; a += 64) span = fmaxf(span, (pa >= 0 ? gt[pa][a] : 0.f) - gt[16 * w + 15][a]);
+        qh[s] = __builtin_bit_cast(u16x8, uint4{h1[0], h1[1], h1[2], h1[3]});
+        ql[s] = __builtin_bit_cast(u16x8, uint4{l1[0], l1[1], l1[2], l1[3]});
+        lh[s] = __builtin_bit_cast(u16x8, uint4{h2[0], h2[1], h2[2], h2[3]});
+        ll[s] = __builtin_bit_cast(u16x8, uint4{l2[0], l2[1], l2[2], l2[3]});
+    }
+    // Past 2^92 (about e^64) of decay across the diagonal block on some
+    // channel (gates far below any trained range) that block is summed
+    // directly instead.
+    float span = 0.f;
+    for (int a = l; a < D; a += 64) span = fmaxf(span, (pa >= 0 ? gt[pa][a] : 0.f) - gt[16 * w + 15][a]);
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
-        const bool direct = span > 92.f;
+    for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+    const bool direct = span > 92.f;
 
-        f32x4 PT[4];
+    f32x4 PT[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            PT[c] = zero4();
-            if (c > w) continue;
-            const int j = 16 * c + c16;
-            f32x4 aL = zero4(), aP = zero4();
-            if (c == w && direct) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int jj = 16 * c + 4 * g4 + r;
-                    float sp = 0.f, sl = 0.f;
-                    if (jj <= t && t < nt) {
-                        const unsigned short* qrow = qin + (((int64_t)b * T + t0 + t) * H + h) * D;
-                        for (int a = 0; a < D; ++a) {
-                            const float kj = gdn_bf16_to_f32(Ks[jj * LDK + a]);
-                            const float lq = tp >= 0 ? gt[tp][a] : 0.f;
-                            sp += gdn_bf16_to_f32(qrow[a]) * kj * __builtin_amdgcn_exp2f(gt[t][a] - gt[jj][a]);
-                            sl += gdn_bf16_to_f32(Ks[t * LDK + a]) * kj * __builtin_amdgcn_exp2f(lq - gt[jj][a]);
-                        }
-                    }
-                    aP[r] = sp;
-                    aL[r] = sl;
-                }
-            } else {
-                f32x4 aP2 = zero4(), aL2 = zero4();
-#pragma unroll
-                for (int s = 0; s < D / 32; ++s) {
-                    const int a0 = 32 * s + 8 * g4;
-                    const u16x8 kj = *reinterpret_cast<const u16x8*>(&Ks[j * LDK + a0]);
-                    const f32x4 gp0 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0]) : z4;
-                    const f32x4 gp1 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0 + 4]) : z4;
-                    const f32x4 gj0 = *reinterpret_cast<const f32x4*>(&gt[j][a0]);
-                    const f32x4 gj1 = *reinterpret_cast<const f32x4*>(&gt[j][a0 + 4]);
-                    uint32_t ah[4], al[4];
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        float xa[2];
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const int ee = e + u;
-                            xa[u] = gdn_bf16_to_f32(kj[ee]) *
-                                    __builtin_amdgcn_exp2f((ee < 4 ? gp0[ee] : gp1[ee - 4]) - (ee < 4 ? gj0[ee] : gj1[ee - 4]));
-                        }
-                        split2(xa[0], xa[1], ah[e >> 1], al[e >> 1]);
-                    }
-                    const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
-                    const u16x8 Al = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
-                    aP = mfma(Ah, qh[s], aP);
-                    aP2 = mfma(Ah, ql[s], aP2);
-                    aP = mfma(Al, qh[s], aP);
-                    aL = mfma(Ah, lh[s], aL);
-                    aL2 = mfma(Ah, ll[s], aL2);
-                    aL = mfma(Al, lh[s], aL);
-                }
-                aP += aP2;
-                aL += aL2;
-            }
-            // accumulator lane: column t = 16w + c16, rows j = 16c + 4g4 + r
+    for (int c = 0; c < 4; ++c) {
+        PT[c] = zero4();
+        if (c > w) continue;
+        const int j = 16 * c + c16;
+        f32x4 aL = zero4(), aP = zero4();
+        if (c == w && direct) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int jj = 16 * c + 4 * g4 + r;
-                Ms[t][jj] = jj < t ? bsh[t] * aL[r] : 0.f;
-                PT[c][r] = jj <= t ? aP[r] : 0.f;
+                float sp = 0.f, sl = 0.f;
+                if (jj <= t && t < nt) {
+                    const unsigned short* qrow = qin + (((int64_t)b * T + t0 + t) * H + h) * D;
+                    for (int a = 0; a < D; ++a) {
+                        const float kj = gdn_bf16_to_f32(Ks[jj * LDK + a]);
+                        const float lq = tp >= 0 ? gt[tp][a] : 0.f;
+                        sp += gdn_bf16_to_f32(qrow[a]) * kj * __builtin_amdgcn_exp2f(gt[t][a] - gt[jj][a]);
+                        sl += gdn_bf16_to_f32(Ks[t * LDK + a]) * kj * __builtin_amdgcn_exp2f(lq - gt[jj][a]);
+                    }
+                }
+                aP[r] = sp;
+                aL[r] = sl;
             }
-        }
-        u16x8* pdst = pfrag + ch * kTfragPerChunk;
+        } else {
+            f32x4 aP2 = zero4(), aL2 = zero4();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (s > (w >> 1)) continue;
-            u16x4 h0, l0, h1, l1;
-            split4(PT[2 * s], h0, l0);
-            split4(PT[2 * s + 1], h1, l1);
-            pdst[(tslot(w, s) * 2 + 0) * 64 + l] = cat(h0, h1);
-            pdst[(tslot(w, s) * 2 + 1) * 64 + l] = cat(l0, l1);
+            for (int s = 0; s < D / 32; ++s) {
+                const int a0 = 32 * s + 8 * g4;
+                const u16x8 kj = *reinterpret_cast<const u16x8*>(&Ks[j * LDK + a0]);
+                const f32x4 gp0 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0]) : z4;
+                const f32x4 gp1 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0 + 4]) : z4;
+                const f32x4 gj0 = *reinterpret_cast<const f32x4*>(&gt[j][a0]);
+                const f32x4 gj1 = *reinterpret_cast<const f32x4*>(&gt[j][a0 + 4]);
+                uint32_t ah[4], al[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float xa[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int ee = e + u;
+                        xa[u] = gdn_bf16_to_f32(kj[ee]) *
+                                __builtin_amdgcn_exp2f((ee < 4 ? gp0[ee] : gp1[ee - 4]) - (ee < 4 ? gj0[ee] : gj1[ee - 4]));
+                    }
+                    split2(xa[0], xa[1], ah[e >> 1], al[e >> 1]);
+                }
+                const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
+                const u16x8 Al = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
+                aP = mfma(Ah, qh[s], aP);
+                aP2 = mfma(Ah, ql[s], aP2);
+                aP = mfma(Al, qh[s], aP);
+                aL = mfma(Ah, lh[s], aL);
+                aL2 = mfma(Ah, ll[s], aL2);
+                aL = mfma(Al, lh[s], aL);
+            }
+            aP += aP2;
+            aL += aL2;
         }
+        // accumulator lane: column t = 16w + c16, rows j = 16c + 4g4 + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jj = 16 * c + 4 * g4 + r;
+            Ms[t][jj] = jj < t ? bsh[t] * aL[r] : 0.f;
+            PT[c][r] = jj <= t ? aP[r] : 0.f;
+        }
+    }
+    u16x8* pdst = pfrag + ch * kTfragPerChunk;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        if (s > (w >> 1)) continue;
+        u16x4 h0, l0, h1, l1;
+        split4(PT[2 * s], h0, l0);
+        split4(PT[2 * s + 1], h1, l1);
+        pdst[(tslot(w, s) * 2 + 0) * 64 + l] = cat(h0, h1);
+        pdst[(tslot(w, s) * 2 + 1) * 64 + l] = cat(l0, l1);
     }
     __syncthreads();  // K is dead from here on; its LDS holds T
 
@@ -446,12 +392,11 @@ __global__ __launch_bounds__(kThreads) void k_prep_mfma(Problem p, u16x8* tfrag,
     }
 }
 
-// Scalar gate, stage 1 with a small LDS footprint (≈22 KiB, so about seven
-// workgroups share a CU): the Gram operands come straight from HBM (16-byte
-// fragment loads), and one 64 x 68 fp32 tile holds both the UT system A
-// (strictly lower blocks stored transposed in the upper triangle, diagonal
-// blocks in place until their inverse replaces them) and T = (I + A)^{-1}
-// (lower triangle).  Same algebra and outputs as k_prep_mfma<D, 0>.
+// Scalar gate, stage 1 with a small LDS footprint (about 22 KiB, so about
+// seven workgroups share a CU): one 64 x 68 fp32 tile first holds the K rows
+// (bf16) for the Gram product, then both the UT system A (strictly lower
+// blocks stored transposed in the upper triangle, diagonal blocks in place
+// until their inverse replaces them) and T = (I + A)^{-1} (lower triangle).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfrag, float* gates) {
     constexpr int LDA = C + 4;
@@ -1235,7 +1180,7 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
         prof_begin("k_prep_mfma", st);
         if constexpr (CH)
-            hipLaunchKernelGGL((k_prep_mfma<D, CH>), grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
+            hipLaunchKernelGGL((k_prep_channel<D>), grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
         else
             hipLaunchKernelGGL((k_prep_scalar<D>), grid, dim3(kThreads), 0, st, p, tfrag, gates);
         prof_end(st);
