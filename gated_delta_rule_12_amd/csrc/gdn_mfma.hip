@@ -137,11 +137,21 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
     const unsigned short* kin = static_cast<const unsigned short*>(p.k);
     const unsigned short* qin = static_cast<const unsigned short*>(p.q);
 
-    for (int e = tid; e < C * PPR; e += kThreads) {
-        const int t = e / PPR, c8 = e - (e / PPR) * PPR;
-        uint4 kv = make_uint4(0, 0, 0, 0);
-        if (t < nt) kv = *reinterpret_cast<const uint4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
-        *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = kv;
+    // K rows: all loads issued before any is stored (rows past the end: zero)
+    {
+        constexpr int KP = C * PPR / kThreads;
+        u32x4 kv[KP];
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
+            kv[k] = u32x4{0, 0, 0, 0};
+            if (t < nt) kv[k] = *reinterpret_cast<const u32x4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
+            *reinterpret_cast<u32x4*>(&Ks[t * LDK + c8 * 8]) = kv[k];
+        }
     }
     if (w == 0) bsh[l] = l < nt ? p.beta[((int64_t)b * T + t0 + l) * H + h] : 0.f;
     // log2 prefix lam[t][a] = sum_{s <= t} log2 alpha_sa (padding tokens add
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
         if (t < nt) {
             const f32x4 av = *reinterpret_cast<const f32x4*>(
                 p.alpha + (((int64_t)b * T + t0 + t) * H + h) * D + 4 * a4);
-            run += f32x4{log2f(av[0]), log2f(av[1]), log2f(av[2]), log2f(av[3])};
+            run += f32x4{__log2f(av[0]), __log2f(av[1]), __log2f(av[2]), __log2f(av[3])};
         }
         vals[u] = run;
     }
@@ -441,11 +451,20 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
     constexpr int LDK = D + 8, PPR = D / 8;
     static_assert(C * LDK * 2 <= C * LDA * 4, "K staging fits the tile");
     unsigned short* Ks = reinterpret_cast<unsigned short*>(AT);
-    for (int e = tid; e < C * PPR; e += kThreads) {
-        const int t = e / PPR, c8 = e - (e / PPR) * PPR;
-        uint4 kv = make_uint4(0, 0, 0, 0);
-        if (t < nt) kv = *reinterpret_cast<const uint4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
-        *reinterpret_cast<uint4*>(&Ks[t * LDK + c8 * 8]) = kv;
+    {
+        constexpr int KP = C * PPR / kThreads;  // all loads issued before any is stored
+        u32x4 kv[KP];
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
+            kv[k] = u32x4{0, 0, 0, 0};
+            if (t < nt) kv[k] = *reinterpret_cast<const u32x4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
+            *reinterpret_cast<u32x4*>(&Ks[t * LDK + c8 * 8]) = kv[k];
+        }
     }
     __syncthreads();  // K rows and the gate prefix visible
     auto krow = [&](int m, int s) { return *reinterpret_cast<const u16x8*>(&Ks[(16 * m + c16) * LDK + 32 * s + 8 * g4]); };
