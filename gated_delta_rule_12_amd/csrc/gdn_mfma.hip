@@ -1096,7 +1096,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 // of kCorrChunks chunks of one segment; wave (tn, half) covers token tile tn
 // and half of the value tiles, whose start-state fragments it keeps in
 // registers for the whole run.
-constexpr int kCorrChunks = 8;
+constexpr int kCorrChunks = 16;
 
 template <int D>
 __global__ __launch_bounds__(512) void k_correct_mfma(Problem p, Split sp, WsLayout L, char* wsb,

@@ -132,6 +132,17 @@ def test_seqpar_segments(G, gate):
     check(w, inp, o, s)
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_seqpar_segments_span_several_correction_runs(gate):
+    """Segments of 24 chunks (the correction takes runs of chunks of one
+    segment) with a ragged last chunk."""
+    w = Workload("seqpar-runs", B=1, H=2, T=4500, dk=64, dv=64, chunk=64, gate=gate,
+                 state0_std=0.5, seed=77)
+    inp = make_inputs(w)
+    o, s = run(w, inp, n_segments=3)
+    check(w, inp, o, s)
+
+
 # --------------------------------------------------------------------------
 # edge cases
 # --------------------------------------------------------------------------
