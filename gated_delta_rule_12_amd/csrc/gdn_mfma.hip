@@ -106,6 +106,89 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// The UT inverse T = (I + A)^{-1} (fp32) and T' = T diag(beta) written as
+// A-operand fragments, for both stage-1 kernels.  AT (row stride C + 4)
+// holds A's strictly lower off-diagonal blocks transposed (block (i, k) at
+// rows of block k, columns of block i) and A's diagonal blocks in place; T
+// replaces the diagonal blocks and fills the lower triangle.  Called by all
+// threads of the workgroup (it contains barriers); Pw is 16 x 17 floats of
+// scratch for the calling wave.
+//   diagonal block w: (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
+//     (N^16 = 0), three rounds of P <- P P, X <- X + X P on fp32 MFMA;
+//     accumulators (lane: column c16, rows 4 g4 + i) serve as B operands as
+//     they stand (instruction s contracts the indices 4G + s, G = lane / 16);
+//   off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
+__device__ __forceinline__ void ut_inverse_store(float* AT, float* Pw, const float* bsh, u16x8* dst) {
+    constexpr int LDA = C + 4;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    {
+        float* Xb = &AT[(16 * w) * LDA + 16 * w];
+        f32x4 pm, xm;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pm[r] = -Xb[(4 * g4 + r) * LDA + c16];
+            xm[r] = (4 * g4 + r == c16 ? 1.f : 0.f) + pm[r];
+        }
+#pragma unroll
+        for (int round = 0; round < 3; ++round) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Pw[(4 * g4 + r) * 17 + c16] = pm[r];
+            f32x4 np = zero4();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) np = mfma_f32(Pw[c16 * 17 + 4 * g4 + q], pm[q], np);
+            pm = np;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
+            f32x4 nx = xm;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) nx = mfma_f32(Xb[c16 * LDA + 4 * g4 + q], pm[q], nx);
+            xm = nx;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        if (w < 4 - d) {
+            const int jb = w, ib = w + d;
+            f32x4 X = zero4();
+            for (int kb = jb; kb < ib; ++kb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    X = mfma_f32(AT[(16 * kb + 4 * g4 + q) * LDA + 16 * ib + c16],   // A_ib,kb (transposed)
+                                 AT[(16 * kb + 4 * g4 + q) * LDA + 16 * jb + c16], X);  // T_kb,jb
+            }
+            f32x4 Tij = zero4();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Tij = mfma_f32(AT[(16 * ib + c16) * LDA + 16 * ib + 4 * g4 + q], X[q], Tij);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) AT[(16 * ib + 4 * g4 + r) * LDA + 16 * jb + c16] = -Tij[r];
+        }
+        __syncthreads();
+    }
+    // T' = T diag(beta): [slot(m, s)][hi/lo][lane] of 8 bf16; lane (row
+    // 16m + lane % 16, group g), slot e -> column 32s + 4g + e (e < 4) or
+    // 32s + 16 + 4g + e - 4; entries above the block diagonal are zero (the
+    // tile holds A there)
+    for (int f = tid; f < kTslots * 64; f += kThreads) {
+        const int slot = f >> 6, lane = f & 63;
+        const int m = slot < 2 ? slot : 2 + ((slot - 2) >> 1);
+        const int s = slot < 2 ? 0 : ((slot - 2) & 1);
+        const int t = 16 * m + (lane & 15), gg = lane >> 4;
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int j0 = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
+            const bool up = (j0 >> 4) > m;
+            const float v0 = up ? 0.f : AT[t * LDA + j0] * bsh[j0];
+            const float v1 = up ? 0.f : AT[t * LDA + j0 + 1] * bsh[j0 + 1];
+            split2(v0, v1, hi[e >> 1], lo[e >> 1]);
+        }
+        dst[(slot * 2 + 0) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
+        dst[(slot * 2 + 1) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
+    }
+}
+
 // Stage 1 for per-key-channel gates: the gate is a vector per token and the
 // chunk-local prefix becomes a C x D table, kept in log2 units
 // (lam[t][a] = sum_{s <= t} log2 alpha_sa, so every ratio is one exp2) and
@@ -116,17 +199,19 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfrag, u16x8* pfrag,
                                                            float* gates) {
+    constexpr int LDA = C + 4;
     constexpr int LDK = D + 8;
     constexpr int PPR = D / 8;
-    constexpr int kBufBytes = (C * LDK * 2 > C * (C + 1) * 4) ? C * LDK * 2 : C * (C + 1) * 4;
-    // K (bf16, row stride LDK) during the Gram product, then T (fp32 [C][C+1])
-    __shared__ __attribute__((aligned(16))) unsigned char kt_buf[kBufBytes];
-    __shared__ __attribute__((aligned(16))) float Ms[C][C + 1];
+    static_assert(C * LDK * 2 <= C * LDA * 4, "K staging fits the tile");
+    // one 64 x 68 fp32 tile holds in turn the prefix scan's partials, the K
+    // rows (bf16, row stride LDK) and then A and T as in the scalar kernel
+    __shared__ __attribute__((aligned(16))) float AT[C * LDA];
     __shared__ float bsh[C];
-    // channel log2 prefix; rows padded by 16 bytes against bank conflicts
+    // channel log2 prefix, rows padded by 16 bytes against bank conflicts;
+    // once the scores are formed it is the inverse's per-wave scratch
     __shared__ __attribute__((aligned(16))) float gt[C][D + 4];
-    unsigned short* Ks = reinterpret_cast<unsigned short*>(kt_buf);
-    float (*Ts)[C + 1] = reinterpret_cast<float (*)[C + 1]>(kt_buf);
+    static_assert(C * (D + 4) >= 4 * 16 * 17, "inverse scratch fits the prefix table");
+    unsigned short* Ks = reinterpret_cast<unsigned short*>(AT);
 
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
@@ -137,28 +222,23 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
     const unsigned short* kin = static_cast<const unsigned short*>(p.k);
     const unsigned short* qin = static_cast<const unsigned short*>(p.q);
 
-    // K rows: all loads issued before any is stored (rows past the end: zero)
-    {
-        constexpr int KP = C * PPR / kThreads;
-        u32x4 kv[KP];
+    // K rows loaded first (rows past the end: zero) and stored once the
+    // scan partials in the tile are consumed
+    constexpr int KP = C * PPR / kThreads;
+    u32x4 kv[KP];
 #pragma unroll
-        for (int k = 0; k < KP; ++k) {
-            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
-            kv[k] = u32x4{0, 0, 0, 0};
-            if (t < nt) kv[k] = *reinterpret_cast<const u32x4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
-        }
-#pragma unroll
-        for (int k = 0; k < KP; ++k) {
-            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
-            *reinterpret_cast<u32x4*>(&Ks[t * LDK + c8 * 8]) = kv[k];
-        }
+    for (int k = 0; k < KP; ++k) {
+        const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
+        kv[k] = u32x4{0, 0, 0, 0};
+        if (t < nt) kv[k] = *reinterpret_cast<const u32x4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
     }
     if (w == 0) bsh[l] = l < nt ? p.beta[((int64_t)b * T + t0 + l) * H + h] : 0.f;
     // log2 prefix lam[t][a] = sum_{s <= t} log2 alpha_sa (padding tokens add
     // zero): thread (group, a4) scans TPG tokens of four channels in
     // registers, then adds the totals of the earlier groups
     constexpr int A4 = D / 4, NG = kThreads / A4, TPG = C / NG;
-    f32x4(*part)[A4] = reinterpret_cast<f32x4(*)[A4]>(&Ms[0][0]);  // Ms is free until L
+    static_assert(NG * A4 * 4 <= C * LDA, "scan partials fit the tile");
+    f32x4(*part)[A4] = reinterpret_cast<f32x4(*)[A4]>(AT);
     const int a4 = tid % A4, grp = tid / A4;
     f32x4 run = zero4(), vals[TPG];
 #pragma unroll
@@ -182,6 +262,12 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
         const f32x4 v = vals[u] + off;
         *reinterpret_cast<f32x4*>(&gt[t][4 * a4]) = v;
         *reinterpret_cast<f32x4*>(&gdst[t * D + 4 * a4]) = v;
+    }
+    __syncthreads();  // partials consumed: the tile takes K
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
+        *reinterpret_cast<u32x4*>(&Ks[t * LDK + c8 * 8]) = kv[k];
     }
     __syncthreads();
 
@@ -238,10 +324,14 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
     for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
     const bool direct = span > 92.f;
 
-    f32x4 PT[4];
+    // P blocks go out as fragment pairs as soon as a pair is complete; the A
+    // blocks (rows j, column t) stay in registers until K is dead
+    u16x8* pdst = pfrag + ch * kTfragPerChunk;
+    f32x4 PT[4], AL[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) PT[c] = AL[c] = zero4();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        PT[c] = zero4();
         if (c > w) continue;
         const int j = 16 * c + c16;
         f32x4 aL = zero4(), aP = zero4();
@@ -300,106 +390,34 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jj = 16 * c + 4 * g4 + r;
-            Ms[t][jj] = jj < t ? bsh[t] * aL[r] : 0.f;
+            AL[c][r] = jj < t ? bsh[t] * aL[r] : 0.f;
             PT[c][r] = jj <= t ? aP[r] : 0.f;
         }
-    }
-    u16x8* pdst = pfrag + ch * kTfragPerChunk;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        if (s > (w >> 1)) continue;
-        u16x4 h0, l0, h1, l1;
-        split4(PT[2 * s], h0, l0);
-        split4(PT[2 * s + 1], h1, l1);
-        pdst[(tslot(w, s) * 2 + 0) * 64 + l] = cat(h0, h1);
-        pdst[(tslot(w, s) * 2 + 1) * 64 + l] = cat(l0, l1);
-    }
-    __syncthreads();  // K is dead from here on; its LDS holds T
-
-    // diagonal 16 x 16 blocks of T = (I + A)^{-1}, block w per wave: with N
-    // the strictly lower block (N^16 = 0), (I + N)^{-1} = (I - N)(I + N^2)
-    // (I + N^4)(I + N^8), three rounds of P <- P P, X <- X + X P on fp32 MFMA.
-    // Accumulators (lane: column c16, rows 4 g4 + i) serve as B operands as
-    // they stand; A operands pass through the block's own LDS tiles (Ms's
-    // diagonal block, dead after this, and Ts's).
-    {
-        float* Pb = &Ms[16 * w][16 * w];
-        float* Xb = &Ts[16 * w][16 * w];
-        constexpr int LD = C + 1;
-        f32x4 pm, xm;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pm[i] = -Pb[(4 * g4 + i) * LD + c16];
-            xm[i] = (4 * g4 + i == c16 ? 1.f : 0.f) + pm[i];
+        if ((c & 1) || c == w) {
+            const int s = c >> 1;
+            u16x4 h0, l0, h1, l1;
+            split4(PT[2 * s], h0, l0);
+            split4(PT[2 * s + 1], h1, l1);
+            pdst[(tslot(w, s) * 2 + 0) * 64 + l] = cat(h0, h1);
+            pdst[(tslot(w, s) * 2 + 1) * 64 + l] = cat(l0, l1);
         }
-#pragma unroll
-        for (int round = 0; round < 3; ++round) {
-            // P <- P P
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Pb[(4 * g4 + i) * LD + c16] = pm[i];
-            f32x4 np = zero4();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) np = mfma_f32(Pb[c16 * LD + 4 * g4 + q], pm[q], np);
-            pm = np;
-            // X <- X + X P
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Xb[(4 * g4 + i) * LD + c16] = xm[i];
-            f32x4 nx = xm;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) nx = mfma_f32(Xb[c16 * LD + 4 * g4 + q], pm[q], nx);
-            xm = nx;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Xb[(4 * g4 + i) * LD + c16] = xm[i];
     }
-    // clear the blocks above the diagonal
-    for (int e = tid; e < C * C; e += kThreads) {
-        const int t = e >> 6, j = e & 63;
-        if ((j >> 4) > (t >> 4)) Ts[t][j] = 0.f;
+    __syncthreads();  // K and the prefix table are dead
+    // A into the tile: blocks left of the diagonal transposed into the upper
+    // triangle (A_tj at (j, t)), the diagonal block in place
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (c > w) continue;
+        if (c < w) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) AT[(16 * c + 4 * g4 + r) * LDA + t] = AL[c][r];
+        } else {
+            *reinterpret_cast<f32x4*>(&AT[t * LDA + 16 * c + 4 * g4]) = AL[c];
+        }
     }
     __syncthreads();
 
-    // off-diagonal blocks by distance d, one block per wave, fp32 MFMA:
-    // T_ij = -T_ii X, X = sum_{k=j}^{i-1} A_ik T_kj.  Instruction s contracts the
-    // indices 4G + s (G = lane / 16), so X's accumulator value s of each lane
-    // is the second product's B operand as it stands.
-    for (int d = 1; d < 4; ++d) {
-        if (w < 4 - d) {
-            const int jb = w, ib = w + d;
-            f32x4 X = zero4();
-            for (int kb = jb; kb < ib; ++kb) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    X = mfma_f32(Ms[16 * ib + c16][16 * kb + 4 * g4 + s],
-                                 Ts[16 * kb + 4 * g4 + s][16 * jb + c16], X);
-            }
-            f32x4 Tij = zero4();
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Tij = mfma_f32(Ts[16 * ib + c16][16 * ib + 4 * g4 + s], X[s], Tij);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ts[16 * ib + 4 * g4 + r][16 * jb + c16] = -Tij[r];
-        }
-        __syncthreads();
-    }
-
-    // T' = T diag(beta) as A-operand fragments: [slot(m, s)][hi/lo][lane] of 8
-    // bf16; lane (row 16m + lane%16, group g), slot e -> column 32s + 4g + e
-    // (e < 4) or 32s + 16 + 4g + e - 4
-    u16x8* dst = tfrag + ch * kTfragPerChunk;
-    for (int f = tid; f < kTslots * 64; f += kThreads) {
-        const int slot = f >> 6, lane = f & 63;
-        const int m = slot < 2 ? slot : 2 + ((slot - 2) >> 1);
-        const int s = slot < 2 ? 0 : ((slot - 2) & 1);
-        const int t = 16 * m + (lane & 15), gg = lane >> 4;
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const int j0 = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
-            split2(Ts[t][j0] * bsh[j0], Ts[t][j0 + 1] * bsh[j0 + 1], hi[e >> 1], lo[e >> 1]);
-        }
-        dst[(slot * 2 + 0) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
-        dst[(slot * 2 + 1) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
-    }
+    ut_inverse_store(AT, &gt[0][0] + w * 16 * 17, bsh, tfrag + ch * kTfragPerChunk);
 }
 
 // Scalar gate, stage 1 with a small LDS footprint (about 22 KiB, so about
@@ -504,77 +522,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
     }
     __syncthreads();
 
-    // diagonal block w: (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8),
-    // three rounds of P <- P P, X <- X + X P on fp32 MFMA (N^16 = 0)
-    {
-        float* Pb = Pscr[w];
-        float* Xb = &AT[(16 * w) * LDA + 16 * w];
-        f32x4 pm, xm;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pm[r] = -Xb[(4 * g4 + r) * LDA + c16];
-            xm[r] = (4 * g4 + r == c16 ? 1.f : 0.f) + pm[r];
-        }
-#pragma unroll
-        for (int round = 0; round < 3; ++round) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Pb[(4 * g4 + r) * 17 + c16] = pm[r];
-            f32x4 np = zero4();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) np = mfma_f32(Pb[c16 * 17 + 4 * g4 + q], pm[q], np);
-            pm = np;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
-            f32x4 nx = xm;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) nx = mfma_f32(Xb[c16 * LDA + 4 * g4 + q], pm[q], nx);
-            xm = nx;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
-    }
-    __syncthreads();
-
-    // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-    for (int d = 1; d < 4; ++d) {
-        if (w < 4 - d) {
-            const int jb = w, ib = w + d;
-            f32x4 X = zero4();
-            for (int kb = jb; kb < ib; ++kb) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    X = mfma_f32(AT[(16 * kb + 4 * g4 + q) * LDA + 16 * ib + c16],   // A_ib,kb (transposed)
-                                 AT[(16 * kb + 4 * g4 + q) * LDA + 16 * jb + c16], X);  // T_kb,jb
-            }
-            f32x4 Tij = zero4();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) Tij = mfma_f32(AT[(16 * ib + c16) * LDA + 16 * ib + 4 * g4 + q], X[q], Tij);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) AT[(16 * ib + 4 * g4 + r) * LDA + 16 * jb + c16] = -Tij[r];
-        }
-        __syncthreads();
-    }
-
-    // T' = T diag(beta) as A-operand fragments (entries above the block
-    // diagonal are zero; the tile holds A there)
-    u16x8* dst = tfrag + ch * kTfragPerChunk;
-    for (int f = tid; f < kTslots * 64; f += kThreads) {
-        const int slot = f >> 6, lane = f & 63;
-        const int m = slot < 2 ? slot : 2 + ((slot - 2) >> 1);
-        const int s = slot < 2 ? 0 : ((slot - 2) & 1);
-        const int t = 16 * m + (lane & 15), gg = lane >> 4;
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const int j0 = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
-            const bool up = (j0 >> 4) > m;
-            const float v0 = up ? 0.f : AT[t * LDA + j0] * bsh[j0];
-            const float v1 = up ? 0.f : AT[t * LDA + j0 + 1] * bsh[j0 + 1];
-            split2(v0, v1, hi[e >> 1], lo[e >> 1]);
-        }
-        dst[(slot * 2 + 0) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
-        dst[(slot * 2 + 1) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
-    }
+    ut_inverse_store(AT, Pscr[w], bsh, tfrag + ch * kTfragPerChunk);
 }
 
 // ---------------------------------------------------------------------------
