@@ -159,8 +159,9 @@ def main():
     from gated_delta_rule_12_amd.workloads import make_inputs, to_device, workload
 
     w = workload(int(args.workload) if args.workload.isdigit() else args.workload)
-    G = args.segments if args.segments is not None else w.n_segments
-    log(f"workload {w}, segments {G}")
+    # None: gdn_chunk_fwd with the library's schedule; a count: gdn_seqpar_fwd
+    G = args.segments if args.segments is not None else (w.n_segments if w.n_segments > 1 else None)
+    log(f"workload {w}, segments {G if G is not None else 'library schedule'}")
     t = time.time()
     inp = make_inputs(w)
     d = to_device(inp, w, "cuda")
@@ -215,7 +216,7 @@ def main():
     step_achieved = abytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(w.name, dominant) if G == w.n_segments else None,
+            "traffic": stored_traffic(w.name, dominant) if args.segments is None else None,
             "kernel": dominant,
             "kernel_launches_per_step": launches[dominant],
             "kernel_avg_launch_us": round(dom_us / launches[dominant], 2),
@@ -226,7 +227,7 @@ def main():
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     extra = {}
-    if G > 1 and not args.no_single_stream:
+    if G is not None and G > 1 and not args.no_single_stream:
         for _ in range(2):
             step(1)
         torch.cuda.synchronize()
@@ -252,8 +253,10 @@ def main():
            "data": "synthetic",
            "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                       "chunk": w.chunk, "gate": w.gate, "input_dtype": w.dtype,
-                      "entry": "gdn_seqpar_fwd" if G > 1 else "gdn_chunk_fwd",
-                      "segments": G, "global_batch": w.B, "seq_len": w.T,
+                      "entry": "gdn_seqpar_fwd" if G is not None else "gdn_chunk_fwd",
+                      "segments": G if G is not None else gdn.gdn_chunk_segments(
+                          w.B, w.T, w.H, w.dk, w.dv, w.chunk, dt_code, gate_code),
+                      "global_batch": w.B, "seq_len": w.T,
                       "parallelism": "single-gpu",
                       "kernel_path": "mfma" if path == gdn.GDN_PATH_MFMA else "valu"},
            "roofline": roof, "cpu_baseline": cpu}

@@ -43,6 +43,10 @@ WsLayout layout_for(const Problem& p, const Split& sp) {
                                                              : valu_layout(p, sp);
 }
 
+int auto_segments(const Problem& p) {
+    return mfma_supported(p.dk, p.dv, p.C, p.dtype, p.gate) ? mfma_auto_segments(p) : 1;
+}
+
 // ---- profiling record ------------------------------------------------------
 struct ProfEvent { int kernel; hipEvent_t a, b; };
 bool g_prof_on = false;
@@ -85,10 +89,12 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
                 const void* q, const void* k, const void* v, const float* alpha,
                 const float* beta, const float* state0, float* out, float* state_out,
                 void* workspace, size_t workspace_bytes, void* stream) {
-    int s = validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments);
+    // n_segments == 0: the library picks the schedule (gdn_chunk_fwd)
+    int s = validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments > 0 ? n_segments : 1);
     if (s != GDN_OK) return s;
     Problem p = make_problem(B, T, H, dk, dv, chunk, dtype, gate, order, scale);
     if (B * H == 0) return GDN_OK;
+    if (n_segments == 0) n_segments = auto_segments(p);
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_E_ARG;
     p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
     p.s0 = state0; p.out = out; p.s_out = state_out;
@@ -163,12 +169,27 @@ int gdn_chunk_path(int64_t dk, int64_t dv, int32_t chunk, int32_t dtype, int32_t
     return mfma_supported(dk, dv, chunk, dtype, gate) ? GDN_PATH_MFMA : GDN_PATH_VALU;
 }
 
+int gdn_chunk_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                       int32_t dtype, int32_t gate) {
+    int s = validate(B, T, H, dk, dv, chunk, dtype, gate, 0, 1);
+    if (s != GDN_OK) return s;
+    Problem p = make_problem(B, T, H, dk, dv, chunk, dtype, gate, 0, 1.f);
+    if (p.NC == 0 || B * H == 0) return 1;
+    return make_split(p.NC, auto_segments(p)).G;
+}
+
 size_t gdn_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                            int32_t chunk, int32_t dtype, int32_t gate, int32_t n_segments) {
     if (validate(B, T, H, dk, dv, chunk, dtype, gate, 0, n_segments) != GDN_OK) return 0;
     Problem p = make_problem(B, T, H, dk, dv, chunk, dtype, gate, 0, 1.f);
     if (p.NC == 0 || B * H == 0) return 0;
-    return layout_for(p, make_split(p.NC, n_segments)).total;
+    size_t bytes = layout_for(p, make_split(p.NC, n_segments)).total;
+    if (n_segments == 1) {
+        // also covers gdn_chunk_fwd, whose schedule may cut sequences into segments
+        const size_t a = layout_for(p, make_split(p.NC, auto_segments(p))).total;
+        if (a > bytes) bytes = a;
+    }
+    return bytes;
 }
 
 int gdn_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
@@ -176,7 +197,7 @@ int gdn_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32
                   const void* q, const void* k, const void* v, const float* alpha,
                   const float* beta, const float* state0, float* out, float* state_out,
                   void* workspace, size_t workspace_bytes, void* stream) {
-    return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, 1, q, k, v, alpha,
+    return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, 0, q, k, v, alpha,
                        beta, state0, out, state_out, workspace, workspace_bytes, stream);
 }
 

@@ -59,6 +59,11 @@ hipError_t valu_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
 WsLayout mfma_layout(const Problem& p, const Split& sp);
 bool mfma_supported(int64_t dk, int64_t dv, int C, int dtype, int gate);
 hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t st);
+// Segments the MFMA family runs a forward pass in when the caller leaves the
+// schedule to the library (gdn_chunk_fwd): enough (batch, head, segment)
+// workgroups to occupy the device, at least kMinSegChunks chunks each; 1 for
+// paths without the whole-head chunk loop.
+int mfma_auto_segments(const Problem& p);
 
 hipError_t recurrent_forward(const Problem& p, hipStream_t st);
 
@@ -66,6 +71,9 @@ hipError_t recurrent_forward(const Problem& p, hipStream_t st);
 // output correction (R_i S_start^T), then the final state.
 hipError_t seqpar_finish(const Problem& p, const Split& sp, char* ws,
                          const WsLayout& L, bool mfma, hipStream_t st);
+// Start-state chain alone (final_step: also the state after the last segment).
+hipError_t seqpar_chain(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
+                        bool write_frag, bool final_step, hipStream_t st);
 // MFMA output correction O_i += R_i S_start^T (gdn_mfma.hip).
 hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
                         hipStream_t st);

@@ -45,6 +45,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = 64;
 constexpr int kThreads = 256;
@@ -1036,6 +1037,490 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 }
 
 // ---------------------------------------------------------------------------
+// Whole-head chunk loop (scalar gate)
+// ---------------------------------------------------------------------------
+// One workgroup per (batch, head, segment) keeps the whole state S^T (D x D,
+// fp32) in registers: wave w holds value columns 16w..16w+15 for every key
+// row, so each chunk's K, Q, V and T' are fetched from L2 once per head and
+// shared by the D/16 waves through LDS, and no intermediate crosses waves
+// (each wave's X, Delta and output columns depend only on its own slice).
+// Long sequences are cut into segments run side by side in two passes, after
+// the sequence-parallel notes (the state at a segment end is the increment
+// from a zero start plus the entry state through the scaling matrix):
+//   pass 1 (kSegState): per segment g < G-1 the increment S^D from zero
+//     (segment 0: from the true start state) and the scaling matrix M from I
+//     (the same recurrence with V = 0), end values only;
+//   the start-state chain S_start(g+1) = S^D_end(g) + S_start(g) M_end(g);
+//   pass 2 (kSegOut): every segment from its true entry state, with outputs.
+// Per chunk: X = K S^T and Z = Q S^T (S^T split hi/lo), U = V - diag(gamma') X,
+// Delta = T' U, S^T <- gamma_C S^T + K^T diag(gamma_C / gamma) Delta and
+// O = scale (diag(gamma) Z + P Delta); P (gated causal scores) is formed per
+// chunk by the waves together and handed over through LDS.
+constexpr int kSegOut = 0, kSegState = 1;
+
+// K and Q rows are kept with the columns of every 32-column block permuted,
+// 16h + 4g + r -> 8g + 4h + r, so that the 8 key slots of lane group g of a
+// k-step in the paired-tile order (4g + r of one 16-column half, then of the
+// other) are 16 contiguous bytes.
+template <int D, int MODE>
+struct SegShared {
+    static constexpr bool OUT = MODE == kSegOut;
+    static constexpr int LDK = D + 8;  // row stride (bf16) of K, Q, V
+    unsigned short K[C * LDK];
+    unsigned short V[C * LDK];
+    u16x8 KtF[D / 16][2][64];  // K^T A-fragments: [key tile][token k-step][lane]
+    u16x8 Tf[kTfragPerChunk];
+    float G[kGateFloats];
+    unsigned short Q[OUT ? C * LDK : 8];
+    u16x8 Pf[OUT ? 4 : 1][2][2][64];  // P fragments per token tile
+    static constexpr int LDO = D + 4;  // row stride (fp32) of the output tile
+    float O[OUT ? C * LDO : 4];
+};
+
+// KIND 0: the state S (values from V); KIND 1: the scaling matrix M (V = 0,
+// identity start).
+template <int D, int MODE, int KIND>
+__device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, const WsLayout& L, char* wsb,
+                                         const u16x8* tfrag, const float* gates, int64_t bh, int gseg,
+                                         SegShared<D, MODE>& sh) {
+    constexpr bool OUT = MODE == kSegOut;
+    constexpr int NW = D / 16;       // waves; wave w owns value columns 16w..
+    constexpr int NT = 64 * NW;
+    constexpr int LDK = SegShared<D, MODE>::LDK;
+    constexpr int LDO = SegShared<D, MODE>::LDO;
+    constexpr int KS = D / 32;       // k-steps over the key dimension
+    constexpr int TPW = D / 16;      // 16-row key tiles of S^T per wave
+    constexpr int PPR = D / 8;       // 16-byte pieces per K/Q/V row
+    constexpr int KP = C * PPR / NT; // pieces per thread and matrix
+    constexpr int TFP = (kTfragPerChunk + NT - 1) / NT;
+    constexpr int GP = kGateFloats / 4;
+    static_assert(C * PPR % NT == 0 && GP <= NT, "staging split");
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int64_t H = p.H, T = p.T;
+    const int b = (int)(bh / H), h = (int)(bh - (bh / H) * H);
+    const int i_begin = gseg * sp.per;
+    const int i_end = min(p.NC, (gseg + 1) * sp.per);
+    const unsigned short* kin = static_cast<const unsigned short*>(p.k);
+    const unsigned short* qin = static_cast<const unsigned short*>(p.q);
+    const unsigned short* vin = static_cast<const unsigned short*>(p.v);
+    const int64_t row_stride = H * D;
+
+    // ---- state: S^T tile tau, lane (v = 16w + c16, a = 16 tau + 4 g4 + r)
+    const int v = 16 * w + c16;
+    f32x4 Sacc[TPW];
+    {
+        const float* src = nullptr;
+        if (KIND == 0) {
+            if (gseg == 0) src = p.s0 ? p.s0 + bh * D * D : nullptr;
+            else if (OUT) src = reinterpret_cast<const float*>(wsb + L.sstart) + (bh * sp.G + gseg) * D * D;
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int a0 = 16 * u + 4 * g4;
+            if (KIND == 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[u][r] = v == a0 + r ? 1.f : 0.f;
+            } else if (src) {
+                Sacc[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)v * D + a0);
+            } else {
+                Sacc[u] = zero4();
+            }
+        }
+    }
+
+    // ---- staging: chunk i+1 in registers while chunk i computes
+    u32x4 kr[KP], vr[KP], qr[OUT ? KP : 1], tr[TFP], gr;
+    auto issue = [&](int i) {
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int e = tid + NT * k, t = min(e / PPR, nt - 1), c8 = e % PPR;
+            const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
+            kr[k] = *reinterpret_cast<const u32x4*>(kin + off);
+            if (KIND == 0) vr[k] = *reinterpret_cast<const u32x4*>(vin + off);
+            if (OUT) qr[k] = *reinterpret_cast<const u32x4*>(qin + off);
+        }
+        const u32x4* tp = reinterpret_cast<const u32x4*>(tfrag + (bh * p.NC + i) * kTfragPerChunk);
+#pragma unroll
+        for (int k = 0; k < TFP; ++k) tr[k] = tp[min(tid + NT * k, kTfragPerChunk - 1)];
+        gr = reinterpret_cast<const u32x4*>(gates + (bh * p.NC + i) * kGateFloats)[min(tid, GP - 1)];
+    };
+    auto store = [&](int i) {
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        const u32x4 z = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int e = tid + NT * k, t = e / PPR, c8 = e % PPR;
+            const bool ok = t < nt;
+            *reinterpret_cast<u32x4*>(&sh.V[t * LDK + c8 * 8]) = (KIND == 0 && ok) ? vr[k] : z;
+            // columns 8 c8 .. +3 and +4 .. +7 of block c8 / 4 go to the
+            // permuted positions 16 (c8 % 2) + 4 h and that + 8, h = (c8 % 4) / 2
+            const int p0 = t * LDK + 32 * (c8 >> 2) + 16 * (c8 & 1) + 4 * ((c8 >> 1) & 1);
+            const u32x4 kk = ok ? kr[k] : z;
+            *reinterpret_cast<u32x2*>(&sh.K[p0]) = u32x2{kk[0], kk[1]};
+            *reinterpret_cast<u32x2*>(&sh.K[p0 + 8]) = u32x2{kk[2], kk[3]};
+            if (OUT) {
+                const u32x4 qq = ok ? qr[k] : z;
+                *reinterpret_cast<u32x2*>(&sh.Q[p0]) = u32x2{qq[0], qq[1]};
+                *reinterpret_cast<u32x2*>(&sh.Q[p0 + 8]) = u32x2{qq[2], qq[3]};
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < TFP; ++k)
+            if (kTfragPerChunk % NT == 0 || tid + NT * k < kTfragPerChunk)
+                reinterpret_cast<u32x4*>(sh.Tf)[tid + NT * k] = tr[k];
+        if (tid < GP) reinterpret_cast<u32x4*>(sh.G)[tid] = gr;
+    };
+
+    // ---- P blocks (m, c), c <= m, dealt over the waves: rows j of tile c,
+    // columns t of tile m, so that blocks 2s, 2s + 1 form the A fragment of
+    // k-step s as they stand; P_tj = exp(g_t - g_j) q_t.k_j (j <= t)
+    auto scores = [&]() {
+        for (int bi = w; bi < 10; bi += NW) {
+            const int m = bi >= 6 ? 3 : bi >= 3 ? 2 : bi >= 1 ? 1 : 0;
+            const int c = bi - m * (m + 1) / 2;
+            const int t = 16 * m + c16;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.K[(16 * c + c16) * LDK + 32 * s + 8 * g4]);
+                const u16x8 qb = *reinterpret_cast<const u16x8*>(&sh.Q[t * LDK + 32 * s + 8 * g4]);
+                acc = mfma(ka, qb, acc);
+            }
+            const float gt = sh.G[192 + t];
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&sh.G[192 + 16 * c + 4 * g4]);
+            f32x4 pt;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * c + 4 * g4 + r;
+                pt[r] = j <= t ? acc[r] * __expf(gt - gj[r]) : 0.f;
+            }
+            u16x4 hi, lo;
+            split4(pt, hi, lo);
+            reinterpret_cast<u16x4*>(&sh.Pf[m][c >> 1][0][l])[c & 1] = hi;
+            reinterpret_cast<u16x4*>(&sh.Pf[m][c >> 1][1][l])[c & 1] = lo;
+        }
+    };
+
+    if constexpr (OUT) {
+        // the never-written halves of the P fragments: blocks (0, 1), (2, 3)
+        if (w == 0) {
+            const u16x4 z = u16x4{0, 0, 0, 0};
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                reinterpret_cast<u16x4*>(&sh.Pf[0][0][hl][l])[1] = z;
+                reinterpret_cast<u16x4*>(&sh.Pf[2][1][hl][l])[1] = z;
+            }
+        }
+    }
+    if (i_begin < i_end) {
+        issue(i_begin);
+        store(i_begin);
+        if (i_begin + 1 < i_end) issue(i_begin + 1);
+    }
+
+    // identity B fragments selecting the key half h of a k-step: lane (column
+    // c16, slots e) is one where the slot holds key 16h + c16 of the block
+    u16x8 idf[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            idf[hh][e] = ((e >> 2) == hh && 4 * g4 + (e & 3) == c16) ? (unsigned short)0x3F80 : (unsigned short)0;
+
+    for (int i = i_begin; i < i_end; ++i) {
+        __syncthreads();  // chunk i staged
+        if constexpr (OUT) scores();
+        // K^T fragments by exact MFMA products with the identity: job (s', u)
+        // turns token tiles 2s', 2s' + 1 of key tile u into the A fragment of
+        // rows a = 16u + c16, k-step s' over tokens
+        for (int job = w; job < 2 * TPW; job += NW) {
+            const int sp_ = job & 1, u = job >> 1;
+            u16x4 half[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int m = 2 * sp_ + q;
+                const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.K[(16 * m + c16) * LDK + 32 * (u >> 1) + 8 * g4]);
+                const f32x4 d = mfma(ka, idf[u & 1], zero4());
+#pragma unroll
+                for (int r = 0; r < 4; ++r) half[q][r] = (unsigned short)(__float_as_uint(d[r]) >> 16);
+            }
+            sh.KtF[u][sp_][l] = cat(half[0], half[1]);
+        }
+
+        // S^T as B operands of every k-step (tiles 2s, 2s + 1), split hi/lo
+        u16x8 sbh[KS], sbl[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u16x4 h0, l0, h1, l1;
+            split4(Sacc[2 * s], h0, l0);
+            split4(Sacc[2 * s + 1], h1, l1);
+            sbh[s] = cat(h0, h1);
+            sbl[s] = cat(l0, l1);
+        }
+        // rows 16m.. of src times S^T: lane (column v, rows t = 16m + 4 g4 + r)
+        auto times_state = [&](const unsigned short* src, int m) {
+            f32x4 x1 = zero4(), x2 = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u16x8 ra = *reinterpret_cast<const u16x8*>(&src[(16 * m + c16) * LDK + 32 * s + 8 * g4]);
+                x1 = mfma(ra, sbh[s], x1);
+                x2 = mfma(ra, sbl[s], x2);
+            }
+            return x1 + x2;
+        };
+        // X = K S^T
+        f32x4 X[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) X[m] = times_state(sh.K, m);
+        // U = V - diag(gamma') X, split hi/lo; Z = Q S^T (entry state of the
+        // chunk) in the same loop so that its products overlap the U arithmetic
+        u16x4 uh[4], ul[4];
+        f32x4 Z[OUT ? 4 : 1];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            if constexpr (OUT) Z[m] = times_state(sh.Q, m);
+            const f32x4 gp = *reinterpret_cast<const f32x4*>(&sh.G[64 + 16 * m + 4 * g4]);
+            f32x4 u;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float vv = KIND == 0 ? gdn_bf16_to_f32(sh.V[(16 * m + 4 * g4 + r) * LDK + v]) : 0.f;
+                u[r] = vv - gp[r] * X[m][r];
+            }
+            split4(u, uh[m], ul[m]);
+        }
+        // Delta = T' U (tile m takes k-steps s <= m / 2); Delta hi/lo for the
+        // output and Delta-bar = diag(gamma_C / gamma) Delta hi/lo for the state
+        u16x4 dh[4], dl[4], dbh[4], dbl[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 d1 = zero4(), d2 = zero4(), d3 = zero4();
+#pragma unroll
+            for (int s = 0; s <= (m >> 1); ++s) {
+                const u16x8 th = sh.Tf[(tslot(m, s) * 2 + 0) * 64 + l];
+                const u16x8 tl = sh.Tf[(tslot(m, s) * 2 + 1) * 64 + l];
+                const u16x8 xh = cat(uh[2 * s], uh[2 * s + 1]);
+                const u16x8 xl = cat(ul[2 * s], ul[2 * s + 1]);
+                d1 = mfma(th, xh, d1);
+                d2 = mfma(th, xl, d2);
+                d3 = mfma(tl, xh, d3);
+            }
+            const f32x4 dd = d1 + d2 + d3;
+            if constexpr (OUT) split4(dd, dh[m], dl[m]);
+            const f32x4 rat = *reinterpret_cast<const f32x4*>(&sh.G[128 + 16 * m + 4 * g4]);
+            split4(rat * dd, dbh[m], dbl[m]);
+        }
+        __syncthreads();  // K^T (and P) fragments of chunk i complete
+
+        // S^T <- gamma_C S^T + K^T Delta-bar (A operand rows a = 16 tau + c16,
+        // k-slots t in the paired-tile order)
+        const float gC = sh.G[256];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            f32x4 acc = gC * Sacc[u], acc2 = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const u16x8 ka = sh.KtF[u][s][l];
+                acc = mfma(ka, cat(dbh[2 * s], dbh[2 * s + 1]), acc);
+                acc2 = mfma(ka, cat(dbl[2 * s], dbl[2 * s + 1]), acc2);
+            }
+            Sacc[u] = acc + acc2;
+        }
+
+        // O = scale (diag(gamma) Z + P Delta) into the LDS output tile; it goes
+        // to HBM once chunk i + 1 is staged (the staging waits on the
+        // vector-memory counter, which also counts stores)
+        if constexpr (OUT) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 o1 = zero4(), o2 = zero4(), o3 = zero4();
+#pragma unroll
+                for (int s = 0; s <= (m >> 1); ++s) {
+                    const u16x8 ph = sh.Pf[m][s][0][l];
+                    const u16x8 pl = sh.Pf[m][s][1][l];
+                    const u16x8 xh = cat(dh[2 * s], dh[2 * s + 1]);
+                    const u16x8 xl = cat(dl[2 * s], dl[2 * s + 1]);
+                    o1 = mfma(ph, xh, o1);
+                    o2 = mfma(ph, xl, o2);
+                    o3 = mfma(pl, xh, o3);
+                }
+                const f32x4 gam = *reinterpret_cast<const f32x4*>(&sh.G[16 * m + 4 * g4]);
+                const f32x4 o = p.scale * (gam * Z[m] + o1 + o2 + o3);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sh.O[(16 * m + 4 * g4 + r) * LDO + v] = o[r];
+            }
+        }
+        __syncthreads();  // every read of chunk i's inputs done, output tile complete
+        if (i + 1 < i_end) store(i + 1);
+        if constexpr (OUT) {
+            // 16-byte pieces of whole rows; rows past the sequence end dropped
+            constexpr int OPR = D / 4, OP = C * OPR / NT;
+            const int64_t t0 = (int64_t)i * C;
+            const int nt = (int)((T - t0) < C ? (T - t0) : C);
+            float* obase = p.out + (((int64_t)b * T + t0) * H + h) * D;
+#pragma unroll
+            for (int k = 0; k < OP; ++k) {
+                const int e = tid + NT * k, t = e / OPR, c4 = e % OPR;
+                if (t < nt)
+                    *reinterpret_cast<f32x4*>(obase + (int64_t)t * row_stride + 4 * c4) =
+                        *reinterpret_cast<const f32x4*>(&sh.O[t * LDO + 4 * c4]);
+            }
+        }
+        if (i + 2 < i_end) issue(i + 2);
+    }
+
+    // ---- end value: final state (last segment of pass 2), S^D or M (pass 1)
+    float* dst = nullptr;
+    if (OUT) {
+        if (gseg == sp.G - 1 && p.s_out) dst = p.s_out + bh * D * D;
+    } else {
+        dst = reinterpret_cast<float*>(wsb + (KIND ? L.mend : L.sdend)) + (bh * sp.G + gseg) * D * D;
+    }
+    if (dst) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+            *reinterpret_cast<f32x4*>(&dst[(int64_t)v * D + 16 * u + 4 * g4]) = Sacc[u];
+    }
+}
+
+// Start-state chain of the whole-head path, S_start(g + 1) = S^D_end(g) +
+// S_start(g) M_end(g), g = 1 .. G - 2, stopping at the last segment's start
+// state (sequence-parallel notes: the state at a segment end is the
+// increment plus the entry state through the scaling matrix).  One
+// workgroup per 16 rows of one head; each step is a 16 x D x D product on
+// bf16 MFMA with both factors split hi/lo (three products, fp32 accumulate).
+// M_end(g + 1) and the rows of S^D_end(g + 1) are fetched while step g
+// computes; the start states go to HBM after the fetch is issued.
+template <int D>
+__global__ __launch_bounds__(256) void k_chain_split(Problem p, Split sp, WsLayout L, char* wsb) {
+    constexpr int LD = D + 4;
+    constexpr int MP = D * D / 4 / 256;  // float4 pieces of M per thread
+    constexpr int SP = 16 * D / 4;       // float4 pieces of 16 rows
+    constexpr int NTW = D / 64;          // column tiles per wave
+    __shared__ __attribute__((aligned(16))) float Ms[D * LD];
+    __shared__ __attribute__((aligned(16))) float Cb[2][16 * LD];
+    __shared__ __attribute__((aligned(16))) float SDs[16 * LD];
+    const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int r0 = 16 * x;
+    const int64_t bh = (int64_t)b * p.H + h;
+    const float* sdend = reinterpret_cast<const float*>(wsb + L.sdend);
+    const float* mend = reinterpret_cast<const float*>(wsb + L.mend);
+    float* sstart = reinterpret_cast<float*>(wsb + L.sstart);
+    const int last = sp.G - 1;  // steps g = 1 .. last - 1 (none when G == 2)
+
+    f32x4 mreg[MP], sreg[(SP + 255) / 256];
+    auto fetch = [&](int g) {
+        g = min(g, last - 1);
+        const f32x4* M = reinterpret_cast<const f32x4*>(mend + (bh * sp.G + g) * D * D);
+#pragma unroll
+        for (int k = 0; k < MP; ++k) mreg[k] = M[tid + 256 * k];
+        const f32x4* S = reinterpret_cast<const f32x4*>(sdend + (bh * sp.G + g) * D * D + (int64_t)r0 * D);
+#pragma unroll
+        for (int k = 0; k < (SP + 255) / 256; ++k) sreg[k] = S[min(tid + 256 * k, SP - 1)];
+    };
+    // S_start(1) = S^D_end(0), the true end state of segment 0
+    {
+        const f32x4* S = reinterpret_cast<const f32x4*>(sdend + (bh * sp.G + 0) * D * D + (int64_t)r0 * D);
+        for (int e = tid; e < SP; e += 256) {
+            const int r = e / (D / 4), c4 = e % (D / 4);
+            *reinterpret_cast<f32x4*>(&Cb[0][r * LD + 4 * c4]) = S[e];
+        }
+    }
+    if (last > 1) fetch(1);
+    int cur = 0;
+    for (int g = 1;; ++g) {
+        if (g < last) {
+#pragma unroll
+            for (int k = 0; k < MP; ++k) {
+                const int e = tid + 256 * k, c = e / (D / 4), a4 = e % (D / 4);
+                *reinterpret_cast<f32x4*>(&Ms[c * LD + 4 * a4]) = mreg[k];
+            }
+#pragma unroll
+            for (int k = 0; k < (SP + 255) / 256; ++k) {
+                const int e = tid + 256 * k;
+                if (SP % 256 == 0 || e < SP)
+                    *reinterpret_cast<f32x4*>(&SDs[(e / (D / 4)) * LD + 4 * (e % (D / 4))]) = sreg[k];
+            }
+        }
+        __syncthreads();  // S_start(g) complete in Cb[cur]; M(g), S^D(g) staged
+        if (g + 1 < last) fetch(g + 1);
+        {
+            float* SS = sstart + (bh * sp.G + g) * D * D + (int64_t)r0 * D;
+            for (int e = tid; e < SP; e += 256) {
+                const int r = e / (D / 4), c4 = e % (D / 4);
+                *reinterpret_cast<f32x4*>(&SS[r * D + 4 * c4]) = *reinterpret_cast<const f32x4*>(&Cb[cur][r * LD + 4 * c4]);
+            }
+        }
+        if (g == last) break;
+        // Cb[cur ^ 1] = S^D(g) + Cb[cur] M(g): wave w takes column tiles w, w + 4
+        const float* A = Cb[cur];
+        u16x8 ah[D / 32], al[D / 32];
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * s + 8 * g4]);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * s + 8 * g4 + 4]);
+            u16x4 h0, l0, h1, l1;
+            split4(x0, h0, l0);
+            split4(x1, h1, l1);
+            ah[s] = cat(h0, h1);
+            al[s] = cat(l0, l1);
+        }
+#pragma unroll
+        for (int q = 0; q < NTW; ++q) {
+            const int nt = w + 4 * q;
+            f32x4 a1, a2 = zero4(), a3 = zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a1[i] = SDs[(4 * g4 + i) * LD + 16 * nt + c16];
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                f32x4 y0, y1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y0[e] = Ms[(32 * s + 8 * g4 + e) * LD + 16 * nt + c16];
+                    y1[e] = Ms[(32 * s + 8 * g4 + 4 + e) * LD + 16 * nt + c16];
+                }
+                u16x4 h0, l0, h1, l1;
+                split4(y0, h0, l0);
+                split4(y1, h1, l1);
+                const u16x8 bh_ = cat(h0, h1), bl_ = cat(l0, l1);
+                a1 = mfma(ah[s], bh_, a1);
+                a2 = mfma(ah[s], bl_, a2);
+                a3 = mfma(al[s], bh_, a3);
+            }
+            const f32x4 sum = a1 + a2 + a3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Cb[cur ^ 1][(4 * g4 + i) * LD + 16 * nt + c16] = sum[i];
+        }
+        __syncthreads();  // M(g), S^D(g) and S_start(g) consumed
+        cur ^= 1;
+    }
+}
+
+// pass 1: workgroup (head, segment g < G - 1, kind); pass 2: (head, segment)
+template <int D, int MODE>
+__global__ __launch_bounds__(4 * D) void k_seg(Problem p, Split sp, WsLayout L, char* wsb,
+                                               const u16x8* tfrag, const float* gates) {
+    __shared__ __attribute__((aligned(16))) SegShared<D, MODE> sh;
+    if constexpr (MODE == kSegOut) {
+        const int id = blockIdx.x;
+        seg_body<D, MODE, 0>(p, sp, L, wsb, tfrag, gates, id / sp.G, id % sp.G, sh);
+    } else {
+        const int kind = blockIdx.x & 1, id = blockIdx.x >> 1;
+        const int nseg = sp.G - 1;
+        const int gseg = id % nseg;
+        const int64_t bh = id / nseg;
+        if (kind == 0) seg_body<D, MODE, 0>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
+        else if (gseg > 0) seg_body<D, MODE, 1>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // sequence parallel: output correction O_i += R_i S_start(g)^T
 // ---------------------------------------------------------------------------
 // Computed transposed, O^T[v][t] += sum_a S_start[v][a] R[t][a]: the start
@@ -1170,6 +1655,44 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
     return hipSuccess;
 }
 
+// Scalar gate: stage 1, then the whole-head chunk loop (two passes and the
+// start-state chain when the sequence is cut into segments).
+template <int D>
+hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayout& L, hipStream_t st) {
+    u16x8* tfrag = reinterpret_cast<u16x8*>(ws + L.prep);
+    const int64_t nch = p.B * p.H * (int64_t)p.NC;
+    const size_t fbytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8));
+    float* gates = reinterpret_cast<float*>(ws + L.prep + fbytes);
+    {
+        dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
+        prof_begin("k_prep_mfma", st);
+        hipLaunchKernelGGL((k_prep_scalar<D>), grid, dim3(kThreads), 0, st, p, tfrag, gates);
+        prof_end(st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t heads = p.B * p.H;
+    if (sp.G > 1) {
+        prof_begin("k_seg_state", st);
+        hipLaunchKernelGGL((k_seg<D, kSegState>), dim3((unsigned)(heads * (sp.G - 1) * 2)), dim3(4 * D), 0, st,
+                           p, sp, L, ws, tfrag, gates);
+        prof_end(st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dim3 grid(D / 16, (unsigned)p.H, (unsigned)p.B);
+        prof_begin("k_chain", st);
+        hipLaunchKernelGGL((k_chain_split<D>), grid, dim3(256), 0, st, p, sp, L, ws);
+        prof_end(st);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    prof_begin("k_seg_out", st);
+    hipLaunchKernelGGL((k_seg<D, kSegOut>), dim3((unsigned)(heads * sp.G)), dim3(4 * D), 0, st, p, sp, L, ws,
+                       tfrag, gates);
+    prof_end(st);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool mfma_supported(int64_t dk, int64_t dv, int C_, int dtype, int gate) {
@@ -1185,9 +1708,12 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
     L.prep_bytes = (p.gate == GDN_GATE_CHANNEL ? 2 : 1) * align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
                    align256((size_t)nch * gate_floats * sizeof(float));
     size_t off = L.prep_bytes;
+    // the whole-head path (scalar gate) keeps no per-chunk corrections and no
+    // start-state fragments
+    const bool whole = p.gate == GDN_GATE_SCALAR;
     if (sp.G > 1) {
         L.corr = off;
-        L.corr_bytes = align256(sizeof(float) * nch * p.C * p.dk);
+        L.corr_bytes = whole ? 0 : align256(sizeof(float) * nch * p.C * p.dk);
         off += L.corr_bytes;
         L.sdend = off;
         L.sdend_bytes = align256(sizeof(float) * p.B * p.H * sp.G * p.dv * p.dk);
@@ -1199,7 +1725,7 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
         L.sstart_bytes = align256(sizeof(float) * p.B * p.H * sp.G * p.dv * p.dk);
         off += L.sstart_bytes;
         L.sfrag = off;
-        L.sfrag_bytes = align256(2 * sizeof(uint16_t) * p.B * p.H * sp.G * p.dv * p.dk);
+        L.sfrag_bytes = whole ? 0 : align256(2 * sizeof(uint16_t) * p.B * p.H * sp.G * p.dv * p.dk);
         off += L.sfrag_bytes;
     }
     L.total = off;
@@ -1222,8 +1748,20 @@ hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLay
 hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t st) {
     const WsLayout L = mfma_layout(p, sp);
     const bool ch = p.gate == GDN_GATE_CHANNEL;
-    if (p.dk == 128) return ch ? launch<128, 1>(p, sp, ws, L, st) : launch<128, 0>(p, sp, ws, L, st);
-    return ch ? launch<64, 1>(p, sp, ws, L, st) : launch<64, 0>(p, sp, ws, L, st);
+    if (p.dk == 128) return ch ? launch<128, 1>(p, sp, ws, L, st) : launch_seg<128>(p, sp, ws, L, st);
+    return ch ? launch<64, 1>(p, sp, ws, L, st) : launch_seg<64>(p, sp, ws, L, st);
+}
+
+int mfma_auto_segments(const Problem& p) {
+    constexpr int kTargetGroups = 256;  // compute units of a gfx950 device
+    constexpr int kMinSegChunks = 4;
+    if (!mfma_supported(p.dk, p.dv, p.C, p.dtype, p.gate) || p.gate != GDN_GATE_SCALAR) return 1;
+    const int64_t heads = p.B * p.H;
+    if (heads <= 0 || p.NC <= 0) return 1;
+    int64_t g = (kTargetGroups + heads - 1) / heads;
+    const int64_t cap = p.NC / kMinSegChunks;
+    if (g > cap) g = cap;
+    return g < 1 ? 1 : (int)g;
 }
 
 }  // namespace gdn

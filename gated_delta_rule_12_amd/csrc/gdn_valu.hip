@@ -359,7 +359,9 @@ namespace {
 // fp32 on the matrix cores (16x16x4 fp32 MFMA: instruction s contracts the
 // indices 4G + s, G = lane / 16), with M_end(g + 1) fetched into registers
 // while step g computes.  With write_frag the start states are also stored
-// as bf16 hi/lo A-fragments for the MFMA output correction.
+// as bf16 hi/lo A-fragments for the MFMA output correction.  Without
+// final_step the chain stops at the last segment's start state (the
+// whole-head path runs that segment from it and ends the state itself).
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8v __attribute__((ext_vector_type(8)));
 
@@ -372,7 +374,7 @@ constexpr int kChainMaxD = 128;
 constexpr int kChainMPieces = kChainMaxD * kChainMaxD / 4 / kThreads;  // float4 of M per thread
 
 __global__ __launch_bounds__(kThreads) void k_chain(Problem p, Split sp, WsLayout L, char* wsb,
-                                                    int write_frag) {
+                                                    int write_frag, int final_step) {
     const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int dk = (int)p.dk, dv = (int)p.dv, tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
@@ -438,6 +440,7 @@ __global__ __launch_bounds__(kThreads) void k_chain(Problem p, Split sp, WsLayou
             const int r = e / dk, c = e - (e / dk) * dk;
             SS[(int64_t)(r0 + r) * dk + c] = Cur[r * ldc + c];
         }
+        if (g == sp.G - 1 && !final_step) return;  // the last segment ends the state itself
         // Nxt = SD + Cur M: wave w takes column tiles w, w + 4, ...
         // (four independent accumulator chains, one per instruction s)
         for (int nt = w; nt < dk / 16; nt += 4) {
@@ -499,21 +502,27 @@ __global__ void k_copy_state(Problem p) {
 
 }  // namespace
 
+hipError_t seqpar_chain(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
+                        bool write_frag, bool final_step, hipStream_t st) {
+    const int dk = (int)p.dk, dv = (int)p.dv;
+    dim3 grid(dv / kRows, (unsigned)p.H, (unsigned)p.B);
+    const size_t lds = sizeof(float) * (2 * kRows * (dk + 1) + (size_t)dk * (dk + 4));
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chain),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    prof_begin("k_chain", st);
+    hipLaunchKernelGGL(k_chain, grid, dim3(kThreads), lds, st, p, sp, L, ws, write_frag ? 1 : 0,
+                       final_step ? 1 : 0);
+    prof_end(st);
+    return hipGetLastError();
+}
+
 hipError_t seqpar_finish(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
                          bool mfma, hipStream_t st) {
-    const int dk = (int)p.dk, dv = (int)p.dv;
     {
-        dim3 grid(dv / kRows, (unsigned)p.H, (unsigned)p.B);
-        const size_t lds = sizeof(float) * (2 * kRows * (dk + 1) + (size_t)dk * (dk + 4));
-        if (lds > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chain),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-        }
-        prof_begin("k_chain", st);
-        hipLaunchKernelGGL(k_chain, grid, dim3(kThreads), lds, st, p, sp, L, ws, mfma ? 1 : 0);
-        prof_end(st);
-        hipError_t e = hipGetLastError();
+        hipError_t e = seqpar_chain(p, sp, ws, L, mfma, true, st);
         if (e != hipSuccess) return e;
     }
     if (mfma) return mfma_correct(p, sp, ws, L, st);

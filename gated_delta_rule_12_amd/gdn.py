@@ -24,7 +24,7 @@ GDN_PATH_VALU, GDN_PATH_MFMA = 0, 1
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_workspace_bytes",
-           "gdn_validate", "gdn_chunk_path", "gdn_status_str", "gdn_abi_version",
+           "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_status_str", "gdn_abi_version",
            "gdn_profile_enable", "gdn_profile_read")
 
 _lib = None
@@ -61,6 +61,8 @@ def lib():
     L.gdn_validate.restype = ctypes.c_int
     L.gdn_chunk_path.argtypes = [i64, i64, i32, i32, i32]
     L.gdn_chunk_path.restype = ctypes.c_int
+    L.gdn_chunk_segments.argtypes = shape + [i32, i32, i32]
+    L.gdn_chunk_segments.restype = ctypes.c_int
     L.gdn_status_str.argtypes = [ctypes.c_int]
     L.gdn_status_str.restype = ctypes.c_char_p
     L.gdn_abi_version.argtypes = []
@@ -98,6 +100,10 @@ def gdn_validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments=1) -> in
 
 def gdn_chunk_path(dk, dv, chunk, dtype, gate) -> int:
     return int(lib().gdn_chunk_path(dk, dv, chunk, dtype, gate))
+
+
+def gdn_chunk_segments(B, T, H, dk, dv, chunk, dtype, gate) -> int:
+    return int(lib().gdn_chunk_segments(B, T, H, dk, dv, chunk, dtype, gate))
 
 
 def gdn_status_str(status: int) -> str:
@@ -179,18 +185,21 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def workspace_for(q, v, alpha, chunk=64, n_segments=1):
+def workspace_for(q, v, alpha, chunk=64, n_segments=None):
     import torch
     B, T, H, dk = q.shape
     gate = GDN_GATE_SCALAR if alpha.dim() == 3 else GDN_GATE_CHANNEL
-    n = gdn_workspace_bytes(B, T, H, dk, v.shape[3], chunk, _dtype_code(q), gate, n_segments)
+    n = gdn_workspace_bytes(B, T, H, dk, v.shape[3], chunk, _dtype_code(q), gate,
+                            1 if n_segments is None else n_segments)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
 
 
 def chunk_fwd(q, k, v, alpha, beta, state0=None, *, chunk=64,
-              order=GDN_PREDICT_THEN_DECAY, scale=1.0, n_segments=1,
+              order=GDN_PREDICT_THEN_DECAY, scale=1.0, n_segments=None,
               out=None, state_out=None, workspace=None):
-    """Chunkwise forward (n_segments > 1: the sequence-parallel entry point).
+    """Chunkwise forward: gdn_chunk_fwd (the library's schedule) when
+    n_segments is None, else gdn_seqpar_fwd with that many segments (1: a
+    single stream).
     Returns (out [B,T,H,dv] fp32, final state [B,H,dv,dk] fp32)."""
     import torch
     B, T, H, dk, dv, gate = _check(q, k, v, alpha, beta, state0)
@@ -204,7 +213,7 @@ def chunk_fwd(q, k, v, alpha, beta, state0=None, *, chunk=64,
     tens = [_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state0),
             _ptr(out), _ptr(state_out)]
     tail = [_ptr(workspace), workspace.numel(), _stream()]
-    if n_segments == 1:
+    if n_segments is None:
         rc = gdn_chunk_fwd(*args, *tens, *tail)
         where = "gdn_chunk_fwd"
     else:

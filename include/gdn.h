@@ -81,7 +81,11 @@ enum gdn_path { GDN_PATH_VALU = 0, GDN_PATH_MFMA = 1 };
  * S_[i+1] = S_[i] Diag(b_C) + Delta^T Kbar with Delta = T'(V - (K (.) B') S_[i]^T)
  * (which is S_[i](I - W^T K) + U^T K when every gate is 1); and the fused
  * output O = (Q (.) B) S_[i]^T + P Delta.  Returns out and state_out.
- * The workspace holds per-chunk T' and gate prefixes.
+ * The workspace holds per-chunk T' and gate prefixes.  The library picks the
+ * schedule: when B * H heads are too few to occupy the device it may cut
+ * every sequence into segments and run them side by side (the scheme of
+ * gdn_seqpar_fwd; gdn_chunk_segments reports how many), which gives the same
+ * results up to floating-point rounding.
  */
 int gdn_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                   int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
@@ -113,7 +117,7 @@ int gdn_recurrent_ref(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
  * which is M_[i](I - W^T K) with unit gates).  Start states are chained
  * S_start(g+1) = S^D_end(g) + S_start(g) M_end(g), and the correction
  * S_[i] = S^D_[i] + S_start M_[i] is applied to the outputs, which are
- * linear in the entry state.  n_segments = 1 is gdn_chunk_fwd.  Segments
+ * linear in the entry state.  n_segments = 1 is a single stream.  Segments
  * hold ceil(NC / n_segments) chunks (NC = ceil(T / chunk)); the last may be
  * shorter.  Same tensors as gdn_chunk_fwd; a larger workspace.
  */
@@ -125,8 +129,9 @@ int gdn_seqpar_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                    float* out, float* state_out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes needed by gdn_chunk_fwd (n_segments = 1) or
- * gdn_seqpar_fwd; 0 when the arguments do not validate.  Host only. */
+/* Workspace bytes needed by gdn_seqpar_fwd with n_segments, or, for
+ * n_segments = 1, by either gdn_seqpar_fwd or gdn_chunk_fwd; 0 when the
+ * arguments do not validate.  Host only. */
 size_t gdn_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk,
                            int64_t dv, int32_t chunk, int32_t dtype,
                            int32_t gate, int32_t n_segments);
@@ -141,6 +146,11 @@ int gdn_validate(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
  * (GDN_PATH_VALU or GDN_PATH_MFMA), or a negative status.  Host only. */
 int gdn_chunk_path(int64_t dk, int64_t dv, int32_t chunk, int32_t dtype,
                    int32_t gate);
+
+/* Number of segments gdn_chunk_fwd cuts each sequence into for these
+ * arguments (1: a single stream), or a negative status.  Host only. */
+int gdn_chunk_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                       int32_t chunk, int32_t dtype, int32_t gate);
 
 /* Static string naming a status code. */
 const char* gdn_status_str(int status);

@@ -71,7 +71,11 @@ def test_workspace_sizes():
     assert gdn.gdn_workspace_bytes(1, 100, 1, 60, 64, 64, 1, 0, 1) == 0
     a = gdn.gdn_workspace_bytes(2, 8192, 16, 128, 128, 64, 1, 0, 1)
     b = gdn.gdn_workspace_bytes(2, 8192, 16, 128, 128, 64, 1, 0, 8)
-    assert a > 0 and b > a and a % 256 == 0 and b % 256 == 0
+    c = gdn.gdn_workspace_bytes(2, 8192, 16, 128, 128, 64, 1, 0, 16)
+    assert a > 0 and b >= a and c > b and a % 256 == 0 and b % 256 == 0
+    # n_segments = 1 also covers gdn_chunk_fwd's own schedule
+    g = gdn.gdn_chunk_segments(2, 8192, 16, 128, 128, 64, 1, 0)
+    assert a >= gdn.gdn_workspace_bytes(2, 8192, 16, 128, 128, 64, 1, 0, g)
     # grows with the number of chunks; a ragged tail rounds up to a chunk
     assert gdn.gdn_workspace_bytes(1, 129, 1, 64, 64, 64, 1, 0, 1) == \
         gdn.gdn_workspace_bytes(1, 192, 1, 64, 64, 64, 1, 0, 1)
@@ -123,3 +127,17 @@ def test_binding_has_no_fallback(tmp_path, monkeypatch):
     monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         gdn.lib()
+
+
+def test_chunk_schedule():
+    # gdn_chunk_fwd cuts sequences into segments only on the whole-head MFMA
+    # path (bf16, scalar gate) and only when B * H heads leave the device idle
+    seg = gdn.gdn_chunk_segments
+    assert seg(2, 8192, 16, 128, 128, 64, 1, 0) == 8       # 32 heads x 8 segments
+    assert seg(1, 65536, 4, 128, 128, 64, 1, 0) == 64      # 4 heads, 1024 chunks
+    assert seg(64, 8192, 16, 128, 128, 64, 1, 0) == 1      # heads fill the device
+    assert seg(1, 256, 1, 64, 64, 64, 1, 0) == 1           # 4 chunks: one segment
+    assert seg(1, 1024, 1, 64, 64, 64, 1, 0) == 4          # at least 4 chunks each
+    assert seg(8, 4096, 16, 128, 128, 64, 1, 1) == 1       # channel gate
+    assert seg(1, 256, 1, 16, 16, 16, 0, 0) == 1           # fp32 vector-ALU path
+    assert seg(1, 100, 1, 60, 64, 64, 1, 0) < 0            # bad shape

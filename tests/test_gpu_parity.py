@@ -35,7 +35,8 @@ def run(w, inp, entry="chunk", order=PTD, n_segments=None):
         o, s = gdn.recurrent_ref(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
                                  order=order)
     else:
-        G = w.n_segments if n_segments is None else n_segments
+        # None: gdn_chunk_fwd (the library's schedule)
+        G = (w.n_segments if w.n_segments > 1 else None) if n_segments is None else n_segments
         o, s = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
                              chunk=w.chunk, order=order, n_segments=G)
     import torch
