@@ -1218,23 +1218,44 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             }
         }
     }
+    // the output tile of chunk i (LDS) to HBM: 16-byte pieces of whole rows,
+    // rows past the sequence end dropped
+    auto flush = [&](int i) {
+        constexpr int OPR = D / 4, OP = C * OPR / NT;
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        float* obase = p.out + (((int64_t)b * T + t0) * H + h) * D;
+#pragma unroll
+        for (int k = 0; k < OP; ++k) {
+            const int e = tid + NT * k, t = e / OPR, c4 = e % OPR;
+            if (t < nt)
+                *reinterpret_cast<f32x4*>(obase + (int64_t)t * row_stride + 4 * c4) =
+                    *reinterpret_cast<const f32x4*>(&sh.O[t * LDO + 4 * c4]);
+        }
+    };
     if (i_begin < i_end) {
         issue(i_begin);
         store(i_begin);
-        if (i_begin + 1 < i_end) issue(i_begin + 1);
     }
 
-    // identity B fragments selecting the key half h of a k-step: lane (column
-    // c16, slots e) is one where the slot holds key 16h + c16 of the block
-    u16x8 idf[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    // identity B fragment selecting the key half hh of a k-step: lane (column
+    // c16, slots e) is one where the slot holds key 16 hh + c16 of the block
+    auto idfrag = [&](int hh) {
+        u16x8 f;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            idf[hh][e] = ((e >> 2) == hh && 4 * g4 + (e & 3) == c16) ? (unsigned short)0x3F80 : (unsigned short)0;
+            f[e] = ((e >> 2) == hh && 4 * g4 + (e & 3) == c16) ? (unsigned short)0x3F80 : (unsigned short)0;
+        return f;
+    };
 
     for (int i = i_begin; i < i_end; ++i) {
         __syncthreads();  // chunk i staged
+        // the previous chunk's output and the next chunk's loads go out here,
+        // overlapping this chunk's products
+        if constexpr (OUT)
+            if (i > i_begin) flush(i - 1);
+        if constexpr (OUT)
+            if (i + 1 < i_end) issue(i + 1);
         if constexpr (OUT) scores();
         // K^T fragments by exact MFMA products with the identity: job (s', u)
         // turns token tiles 2s', 2s' + 1 of key tile u into the A fragment of
@@ -1246,7 +1267,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             for (int q = 0; q < 2; ++q) {
                 const int m = 2 * sp_ + q;
                 const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.K[(16 * m + c16) * LDK + 32 * (u >> 1) + 8 * g4]);
-                const f32x4 d = mfma(ka, idf[u & 1], zero4());
+                const f32x4 d = mfma(ka, idfrag(u & 1), zero4());
 #pragma unroll
                 for (int r = 0; r < 4; ++r) half[q][r] = (unsigned short)(__float_as_uint(d[r]) >> 16);
             }
@@ -1254,14 +1275,18 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         }
 
         // S^T as B operands of every k-step (tiles 2s, 2s + 1), split hi/lo
-        u16x8 sbh[KS], sbl[KS];
+        // (the output pass keeps them for Z; the state pass forms them per
+        // k-step inside the X product)
+        u16x8 sbh[OUT ? KS : 1], sbl[OUT ? KS : 1];
+        if constexpr (OUT) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            u16x4 h0, l0, h1, l1;
-            split4(Sacc[2 * s], h0, l0);
-            split4(Sacc[2 * s + 1], h1, l1);
-            sbh[s] = cat(h0, h1);
-            sbl[s] = cat(l0, l1);
+            for (int s = 0; s < KS; ++s) {
+                u16x4 h0, l0, h1, l1;
+                split4(Sacc[2 * s], h0, l0);
+                split4(Sacc[2 * s + 1], h1, l1);
+                sbh[s] = cat(h0, h1);
+                sbl[s] = cat(l0, l1);
+            }
         }
         // rows 16m.. of src times S^T: lane (column v, rows t = 16m + 4 g4 + r)
         auto times_state = [&](const unsigned short* src, int m) {
@@ -1276,8 +1301,32 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         };
         // X = K S^T
         f32x4 X[4];
+        if constexpr (OUT) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) X[m] = times_state(sh.K, m);
+            for (int m = 0; m < 4; ++m) X[m] = times_state(sh.K, m);
+        } else {
+            // k-step outer, one accumulator per tile (four waves per SIMD hide
+            // the dependent products)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) X[m] = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                u16x4 h0, l0, h1, l1;
+                split4(Sacc[2 * s], h0, l0);
+                split4(Sacc[2 * s + 1], h1, l1);
+                const u16x8 bh_ = cat(h0, h1), bl_ = cat(l0, l1);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const u16x8 ra = *reinterpret_cast<const u16x8*>(&sh.K[(16 * m + c16) * LDK + 32 * s + 8 * g4]);
+                    X[m] = mfma(ra, bh_, X[m]);
+                    X[m] = mfma(ra, bl_, X[m]);
+                }
+            }
+        }
+        // (the state pass fetches the next chunk only now, so that the staging
+        // registers are not live across these products)
+        if constexpr (!OUT)
+            if (i + 1 < i_end) issue(i + 1);
         // U = V - diag(gamma') X, split hi/lo; Z = Q S^T (entry state of the
         // chunk) in the same loop so that its products overlap the U arithmetic
         u16x4 uh[4], ul[4];
@@ -1306,11 +1355,17 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
                 const u16x8 tl = sh.Tf[(tslot(m, s) * 2 + 1) * 64 + l];
                 const u16x8 xh = cat(uh[2 * s], uh[2 * s + 1]);
                 const u16x8 xl = cat(ul[2 * s], ul[2 * s + 1]);
-                d1 = mfma(th, xh, d1);
-                d2 = mfma(th, xl, d2);
-                d3 = mfma(tl, xh, d3);
+                if constexpr (OUT) {
+                    d1 = mfma(th, xh, d1);
+                    d2 = mfma(th, xl, d2);
+                    d3 = mfma(tl, xh, d3);
+                } else {
+                    d1 = mfma(th, xh, d1);
+                    d1 = mfma(th, xl, d1);
+                    d1 = mfma(tl, xh, d1);
+                }
             }
-            const f32x4 dd = d1 + d2 + d3;
+            const f32x4 dd = OUT ? d1 + d2 + d3 : d1;
             if constexpr (OUT) split4(dd, dh[m], dl[m]);
             const f32x4 rat = *reinterpret_cast<const f32x4*>(&sh.G[128 + 16 * m + 4 * g4]);
             split4(rat * dd, dbh[m], dbl[m]);
@@ -1327,14 +1382,15 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             for (int s = 0; s < 2; ++s) {
                 const u16x8 ka = sh.KtF[u][s][l];
                 acc = mfma(ka, cat(dbh[2 * s], dbh[2 * s + 1]), acc);
-                acc2 = mfma(ka, cat(dbl[2 * s], dbl[2 * s + 1]), acc2);
+                if constexpr (OUT) acc2 = mfma(ka, cat(dbl[2 * s], dbl[2 * s + 1]), acc2);
+                else acc = mfma(ka, cat(dbl[2 * s], dbl[2 * s + 1]), acc);
             }
-            Sacc[u] = acc + acc2;
+            Sacc[u] = OUT ? acc + acc2 : acc;
         }
 
         // O = scale (diag(gamma) Z + P Delta) into the LDS output tile; it goes
-        // to HBM once chunk i + 1 is staged (the staging waits on the
-        // vector-memory counter, which also counts stores)
+        // to HBM early in the next chunk (staging waits on the vector-memory
+        // counter, which also counts stores)
         if constexpr (OUT) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -1357,22 +1413,9 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         }
         __syncthreads();  // every read of chunk i's inputs done, output tile complete
         if (i + 1 < i_end) store(i + 1);
-        if constexpr (OUT) {
-            // 16-byte pieces of whole rows; rows past the sequence end dropped
-            constexpr int OPR = D / 4, OP = C * OPR / NT;
-            const int64_t t0 = (int64_t)i * C;
-            const int nt = (int)((T - t0) < C ? (T - t0) : C);
-            float* obase = p.out + (((int64_t)b * T + t0) * H + h) * D;
-#pragma unroll
-            for (int k = 0; k < OP; ++k) {
-                const int e = tid + NT * k, t = e / OPR, c4 = e % OPR;
-                if (t < nt)
-                    *reinterpret_cast<f32x4*>(obase + (int64_t)t * row_stride + 4 * c4) =
-                        *reinterpret_cast<const f32x4*>(&sh.O[t * LDO + 4 * c4]);
-            }
-        }
-        if (i + 2 < i_end) issue(i + 2);
     }
+    if constexpr (OUT)
+        if (i_begin < i_end) flush(i_end - 1);
 
     // ---- end value: final state (last segment of pass 2), S^D or M (pass 1)
     float* dst = nullptr;
@@ -1503,8 +1546,9 @@ __global__ __launch_bounds__(256) void k_chain_split(Problem p, Split sp, WsLayo
 }
 
 // pass 1: workgroup (head, segment g < G - 1, kind); pass 2: (head, segment)
+// The state pass fits four waves per SIMD (two workgroups per CU).
 template <int D, int MODE>
-__global__ __launch_bounds__(4 * D) void k_seg(Problem p, Split sp, WsLayout L, char* wsb,
+__global__ __launch_bounds__(4 * D, MODE == kSegState ? 4 : 2) void k_seg(Problem p, Split sp, WsLayout L, char* wsb,
                                                const u16x8* tfrag, const float* gates) {
     __shared__ __attribute__((aligned(16))) SegShared<D, MODE> sh;
     if constexpr (MODE == kSegOut) {
@@ -1695,6 +1739,14 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
 
 }  // namespace
 
+// The whole-head chunk loop (scalar gate) needs enough (head, segment)
+// workgroups to occupy the device; below that the state is sliced over
+// 16-column workgroups (k_rec_mfma), eight per head.
+constexpr int64_t kWholeHeadMinGroups = 128;
+static bool whole_head(const Problem& p, const Split& sp) {
+    return p.gate == GDN_GATE_SCALAR && p.B * p.H * (int64_t)sp.G >= kWholeHeadMinGroups;
+}
+
 bool mfma_supported(int64_t dk, int64_t dv, int C_, int dtype, int gate) {
     return dtype == GDN_BF16 && (gate == GDN_GATE_SCALAR || gate == GDN_GATE_CHANNEL) &&
            C_ == C && dk == dv && (dk == 64 || dk == 128);
@@ -1708,9 +1760,9 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
     L.prep_bytes = (p.gate == GDN_GATE_CHANNEL ? 2 : 1) * align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
                    align256((size_t)nch * gate_floats * sizeof(float));
     size_t off = L.prep_bytes;
-    // the whole-head path (scalar gate) keeps no per-chunk corrections and no
-    // start-state fragments
-    const bool whole = p.gate == GDN_GATE_SCALAR;
+    // the whole-head path keeps no per-chunk corrections and no start-state
+    // fragments
+    const bool whole = whole_head(p, sp);
     if (sp.G > 1) {
         L.corr = off;
         L.corr_bytes = whole ? 0 : align256(sizeof(float) * nch * p.C * p.dk);
@@ -1748,8 +1800,9 @@ hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLay
 hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t st) {
     const WsLayout L = mfma_layout(p, sp);
     const bool ch = p.gate == GDN_GATE_CHANNEL;
-    if (p.dk == 128) return ch ? launch<128, 1>(p, sp, ws, L, st) : launch_seg<128>(p, sp, ws, L, st);
-    return ch ? launch<64, 1>(p, sp, ws, L, st) : launch_seg<64>(p, sp, ws, L, st);
+    if (whole_head(p, sp)) return p.dk == 128 ? launch_seg<128>(p, sp, ws, L, st) : launch_seg<64>(p, sp, ws, L, st);
+    if (p.dk == 128) return ch ? launch<128, 1>(p, sp, ws, L, st) : launch<128, 0>(p, sp, ws, L, st);
+    return ch ? launch<64, 1>(p, sp, ws, L, st) : launch<64, 0>(p, sp, ws, L, st);
 }
 
 int mfma_auto_segments(const Problem& p) {
@@ -1761,7 +1814,9 @@ int mfma_auto_segments(const Problem& p) {
     int64_t g = (kTargetGroups + heads - 1) / heads;
     const int64_t cap = p.NC / kMinSegChunks;
     if (g > cap) g = cap;
-    return g < 1 ? 1 : (int)g;
+    if (g < 1) g = 1;
+    // too few workgroups for the whole-head loop: one stream on the sliced loop
+    return whole_head(p, make_split(p.NC, (int)g)) ? (int)g : 1;
 }
 
 }  // namespace gdn

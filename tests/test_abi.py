@@ -131,13 +131,15 @@ def test_binding_has_no_fallback(tmp_path, monkeypatch):
 
 def test_chunk_schedule():
     # gdn_chunk_fwd cuts sequences into segments only on the whole-head MFMA
-    # path (bf16, scalar gate) and only when B * H heads leave the device idle
+    # path (bf16, scalar gate), when B * H heads leave the device idle and the
+    # segments give at least 128 (head, segment) workgroups
     seg = gdn.gdn_chunk_segments
     assert seg(2, 8192, 16, 128, 128, 64, 1, 0) == 8       # 32 heads x 8 segments
     assert seg(1, 65536, 4, 128, 128, 64, 1, 0) == 64      # 4 heads, 1024 chunks
     assert seg(64, 8192, 16, 128, 128, 64, 1, 0) == 1      # heads fill the device
     assert seg(1, 256, 1, 64, 64, 64, 1, 0) == 1           # 4 chunks: one segment
-    assert seg(1, 1024, 1, 64, 64, 64, 1, 0) == 4          # at least 4 chunks each
+    assert seg(4, 1024, 8, 64, 64, 64, 1, 0) == 4          # at least 4 chunks each
+    assert seg(1, 1024, 1, 64, 64, 64, 1, 0) == 1          # too few groups: one stream
     assert seg(8, 4096, 16, 128, 128, 64, 1, 1) == 1       # channel gate
     assert seg(1, 256, 1, 16, 16, 16, 0, 0) == 1           # fp32 vector-ALU path
     assert seg(1, 100, 1, 60, 64, 64, 1, 0) < 0            # bad shape

@@ -238,6 +238,35 @@ def test_workspace_too_small_is_an_error():
 # full-size workloads (bench launch configuration), sampled slices
 # --------------------------------------------------------------------------
 
+# --------------------------------------------------------------------------
+# whole-head chunk loop (scalar gate, at least 128 (head, segment) groups):
+# two passes and the start-state chain, sampled heads against the oracle
+# --------------------------------------------------------------------------
+
+WHOLE = [
+    # B, H, T, d, G (None: gdn_chunk_fwd's schedule), order, state0_std, alpha_mean
+    (1, 32, 1000, 128, 4, PTD, 0.5, 2.0),    # ragged tail, 4 chunks per segment
+    (1, 32, 1050, 128, 5, DTP, 0.5, 2.0),    # last segment a single ragged chunk
+    (1, 32, 700, 64, 4, DTP, 0.3, 2.0),
+    (1, 64, 640, 128, 2, PTD, 0.5, 2.0),     # two segments: no chain step
+    (2, 16, 2000, 128, None, PTD, 0.5, 2.0),  # library schedule (7 segments)
+    (1, 32, 512, 128, 4, PTD, 0.0, 6.0),     # long memory, zero start state
+    (1, 32, 512, 128, 4, DTP, 0.5, -6.0),    # fast forgetting
+]
+
+
+@pytest.mark.parametrize("case", WHOLE, ids=lambda c: "-".join(map(str, c)))
+def test_whole_head_path(case):
+    B, H, T, d, G, order, std, am = case
+    w = Workload("whole", B=B, H=H, T=T, dk=d, dv=d, chunk=64, state0_std=std,
+                 alpha_mean=am, seed=T + H + d)
+    if G is None:
+        assert gdn.gdn_chunk_segments(B, T, H, d, d, 64, gdn.GDN_BF16, gdn.GDN_GATE_SCALAR) * B * H >= 128
+    inp = make_inputs(w)
+    o, s = run(w, inp, order=order, n_segments=G)
+    check(w, inp, o, s, order, bh=[(0, 0), (B - 1, H // 2 + 1), (B - 1, H - 1)])
+
+
 SAMPLES = {1: [(0, 0), (3, 7)], 2: [(0, 0), (1, 15), (0, 9)], 3: [(0, 0), (0, 3)],
            4: [(0, 0), (7, 15)]}
 
