@@ -256,19 +256,26 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
     __syncthreads();
     f32x4 off = zero4();
     for (int gg = 0; gg < grp; ++gg) off += part[gg][a4];
-    float* gdst = gates + ch * (int64_t)C * D;
 #pragma unroll
     for (int u = 0; u < TPG; ++u) {
         const int t = grp * TPG + u;
-        const f32x4 v = vals[u] + off;
-        *reinterpret_cast<f32x4*>(&gt[t][4 * a4]) = v;
-        *reinterpret_cast<f32x4*>(&gdst[t * D + 4 * a4]) = v;
+        *reinterpret_cast<f32x4*>(&gt[t][4 * a4]) = vals[u] + off;
     }
     __syncthreads();  // partials consumed: the tile takes K
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
         const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
         *reinterpret_cast<u32x4*>(&Ks[t * LDK + c8 * 8]) = kv[k];
+    }
+    // the prefix table for the chunk loop (after the K rows, whose wait on
+    // the vector-memory counter would otherwise include these stores)
+    {
+        float* gdst = gates + ch * (int64_t)C * D;
+#pragma unroll
+        for (int u = 0; u < TPG; ++u) {
+            const int t = grp * TPG + u;
+            *reinterpret_cast<f32x4*>(&gdst[t * D + 4 * a4]) = *reinterpret_cast<const f32x4*>(&gt[t][4 * a4]);
+        }
     }
     __syncthreads();
 
@@ -441,6 +448,21 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
     const int64_t ch = ((int64_t)b * H + h) * p.NC + i;
     const unsigned short* kin = static_cast<const unsigned short*>(p.k);
 
+    // K rows staged (coalesced) in the tile's own LDS, bf16 at row stride D + 8
+    // (17408 bytes, the size of the fp32 tile for D = 128); rows past the
+    // sequence end are zero
+    constexpr int LDK = D + 8, PPR = D / 8;
+    static_assert(C * LDK * 2 <= C * LDA * 4, "K staging fits the tile");
+    unsigned short* Ks = reinterpret_cast<unsigned short*>(AT);
+    // K rows first (every wave), then the gate prefix on wave 0, then the rows
+    // go to LDS: the two global fetches overlap
+    constexpr int KP = C * PPR / kThreads;
+    u32x4 kv[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int e = tid + kThreads * k, t = min(e / PPR, nt - 1), c8 = e % PPR;
+        kv[k] = *reinterpret_cast<const u32x4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
+    }
     // gate prefix (wave 0)
     if (w == 0) {
         float la = 0.f, bt = 0.f;
@@ -453,10 +475,20 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
         float gprev = __shfl_up(gv, 1, 64);
         if (l == 0) gprev = 0.f;
         const float gpv = p.order == GDN_PREDICT_THEN_DECAY ? gprev : gv;
-        const float gC = __shfl(gv, 63, 64);
         gsh[l] = gv;
         gpsh[l] = gpv;
         bsh[l] = bt;
+    }
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
+        *reinterpret_cast<u32x4*>(&Ks[t * LDK + c8 * 8]) = t < nt ? kv[k] : u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();  // K rows and the gate prefix visible
+    // the gate block for the chunk loop (after the K rows, whose wait on the
+    // vector-memory counter would otherwise include these stores)
+    if (w == 0) {
+        const float gv = gsh[l], gpv = gpsh[l], gC = gsh[C - 1];
         float* gb = gates + ch * kGateFloats;
         gb[l] = __expf(gv);
         gb[64 + l] = __expf(gpv);
@@ -464,28 +496,6 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
         gb[192 + l] = gv;
         if (l == 0) gb[256] = __expf(gC);
     }
-    // K rows staged (coalesced) in the tile's own LDS, bf16 at row stride D + 8
-    // (17408 bytes, the size of the fp32 tile for D = 128); rows past the
-    // sequence end are zero
-    constexpr int LDK = D + 8, PPR = D / 8;
-    static_assert(C * LDK * 2 <= C * LDA * 4, "K staging fits the tile");
-    unsigned short* Ks = reinterpret_cast<unsigned short*>(AT);
-    {
-        constexpr int KP = C * PPR / kThreads;  // all loads issued before any is stored
-        u32x4 kv[KP];
-#pragma unroll
-        for (int k = 0; k < KP; ++k) {
-            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
-            kv[k] = u32x4{0, 0, 0, 0};
-            if (t < nt) kv[k] = *reinterpret_cast<const u32x4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
-        }
-#pragma unroll
-        for (int k = 0; k < KP; ++k) {
-            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
-            *reinterpret_cast<u32x4*>(&Ks[t * LDK + c8 * 8]) = kv[k];
-        }
-    }
-    __syncthreads();  // K rows and the gate prefix visible
     auto krow = [&](int m, int s) { return *reinterpret_cast<const u16x8*>(&Ks[(16 * m + c16) * LDK + 32 * s + 8 * g4]); };
     // Gram blocks (m, nb), nb <= m, dealt 3, 3, 2, 2 over the waves
     f32x4 acc[3];
