@@ -24,14 +24,22 @@
 //   as bf16 hi/lo MFMA A-operand fragments.  k_prep_scalar (scalar gate;
 //   the gated scores P are formed in the chunk loop) and k_prep_channel
 //   (per-key-channel gate; also the log2-prefix table and P).
-// k_rec_mfma: one workgroup per (batch, head, segment, 16-row slice of the
-//   state); the slice of S^T lives in registers (fp32) across the chunk loop.
-//   Wave w owns token rows 16w..16w+15 of every chunk product and key rows
-//   (D/4 of them) of the state.  Results in MFMA accumulator layout are fed
-//   to the next product without transposition: a k-step of 32 pairs two
-//   16-row accumulator tiles, k-slot 8g+e <-> index 4g+e (e < 4) of the first
-//   tile and 4g+e-4 of the second, and the other operand is read in the same
-//   slot order.  Three barriers per chunk.
+// Stage 2, two chunk loops.  Results in MFMA accumulator layout are fed to
+//   the next product without transposition: a k-step of 32 pairs two 16-row
+//   accumulator tiles, k-slot 8g+e <-> index 4g+e (e < 4) of the first tile
+//   and 4g+e-4 of the second, and the other operand is read in the same slot
+//   order.
+// k_seg (scalar gate, enough (head, segment) workgroups to fill the device):
+//   one workgroup per (batch, head, segment) holds the whole state S^T in
+//   registers, wave w the value columns 16w..16w+15; sequences cut into
+//   segments run as a state pass (increment S^D and scaling matrix M per
+//   segment), the start-state chain (k_chain_split) and an output pass from
+//   the true entry states.
+// k_rec_mfma (channel gate, or too few groups): one workgroup per (batch,
+//   head, segment, 16-row slice of the state); wave w owns token rows
+//   16w..16w+15 of every chunk product and key rows (D/4 of them) of the
+//   state.  Three barriers per chunk.  Segments use increment-and-correct
+//   (scaling tiles, k_chain, k_correct_mfma).
 #include <type_traits>
 
 #include "gdn_internal.h"
