@@ -72,9 +72,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // x = hi + lo + O(2^-18 |x|): hi = bf16(x), lo = bf16(x - hi), both RNE.
+// x - hi is exact in fp32 and is formed by one bf16 dot product per element,
+// x + (-1) hi + (-0) hi' (v_dot2c_f32_bf16), instead of a shift and a
+// subtraction.  The zero factors are -0: the pair (-1, +0) would be emitted as
+// the inline constant -1.0, which the instruction reads as (+0, -1) (checked
+// lane by lane on gfx950); (-1, -0) and (-0, -1) are encoded as literals.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
     hi = pack_bf16(a, b);
-    lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+    const bf16x2_t h = __builtin_bit_cast(bf16x2_t, hi);
+    const bf16x2_t m0 = {(__bf16)-1.f, (__bf16)-0.f}, m1 = {(__bf16)-0.f, (__bf16)-1.f};
+    lo = pack_bf16(__builtin_amdgcn_fdot2_f32_bf16(h, m0, a, false), __builtin_amdgcn_fdot2_f32_bf16(h, m1, b, false));
 }
 
 __device__ __forceinline__ void split4(const f32x4& x, u16x4& hi, u16x4& lo) {
@@ -1097,19 +1104,19 @@ struct SegShared {
 
 // KIND 0: the state S (values from V); KIND 1: the scaling matrix M (V = 0,
 // identity start).
-template <int D, int MODE, int KIND>
+template <int D, int MODE, int KIND, int NV>
 __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, const WsLayout& L, char* wsb,
                                          const u16x8* tfrag, const float* gates, int64_t bh, int gseg,
                                          SegShared<D, MODE>& sh) {
     constexpr bool OUT = MODE == kSegOut;
-    constexpr int NW = D / 16;       // waves; wave w owns value columns 16w..
+    constexpr int NW = D / (16 * NV);  // waves; wave w owns value columns 16 NV w ..
     constexpr int NT = 64 * NW;
     constexpr int LDK = SegShared<D, MODE>::LDK;
     constexpr int LDO = SegShared<D, MODE>::LDO;
-    constexpr int KS = D / 32;       // k-steps over the key dimension
-    constexpr int TPW = D / 16;      // 16-row key tiles of S^T per wave
-    constexpr int PPR = D / 8;       // 16-byte pieces per K/Q/V row
-    constexpr int KP = C * PPR / NT; // pieces per thread and matrix
+    constexpr int KS = D / 32;         // k-steps over the key dimension
+    constexpr int TPW = D / 16;        // 16-row key tiles of S^T per value block
+    constexpr int PPR = D / 8;         // 16-byte pieces per K/Q/V row
+    constexpr int KP = C * PPR / NT;   // pieces per thread and matrix
     constexpr int TFP = (kTfragPerChunk + NT - 1) / NT;
     constexpr int GP = kGateFloats / 4;
     static_assert(C * PPR % NT == 0 && GP <= NT, "staging split");
@@ -1126,9 +1133,12 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     const unsigned short* vin = static_cast<const unsigned short*>(p.v);
     const int64_t row_stride = H * D;
 
-    // ---- state: S^T tile tau, lane (v = 16w + c16, a = 16 tau + 4 g4 + r)
-    const int v = 16 * w + c16;
-    f32x4 Sacc[TPW];
+    // ---- state: value block n of the wave, S^T tile tau, lane
+    // (v = 16 (NV w + n) + c16, a = 16 tau + 4 g4 + r)
+    int v[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) v[n] = 16 * (NV * w + n) + c16;
+    f32x4 Sacc[NV][TPW];
     {
         const float* src = nullptr;
         if (KIND == 0) {
@@ -1136,17 +1146,19 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             else if (OUT) src = reinterpret_cast<const float*>(wsb + L.sstart) + (bh * sp.G + gseg) * D * D;
         }
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int a0 = 16 * u + 4 * g4;
-            if (KIND == 1) {
+        for (int n = 0; n < NV; ++n)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sacc[u][r] = v == a0 + r ? 1.f : 0.f;
-            } else if (src) {
-                Sacc[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)v * D + a0);
-            } else {
-                Sacc[u] = zero4();
+            for (int u = 0; u < TPW; ++u) {
+                const int a0 = 16 * u + 4 * g4;
+                if (KIND == 1) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Sacc[n][u][r] = v[n] == a0 + r ? 1.f : 0.f;
+                } else if (src) {
+                    Sacc[n][u] = *reinterpret_cast<const f32x4*>(src + (int64_t)v[n] * D + a0);
+                } else {
+                    Sacc[n][u] = zero4();
+                }
             }
-        }
     }
 
     // ---- staging: chunk i+1 in registers while chunk i computes
@@ -1295,49 +1307,68 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         // S^T as B operands of every k-step (tiles 2s, 2s + 1), split hi/lo
         // (the output pass keeps them for Z; the state pass forms them per
         // k-step inside the X product)
-        u16x8 sbh[OUT ? KS : 1], sbl[OUT ? KS : 1];
+        u16x8 sbh[NV][OUT ? KS : 1], sbl[NV][OUT ? KS : 1];
         if constexpr (OUT) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                u16x4 h0, l0, h1, l1;
-                split4(Sacc[2 * s], h0, l0);
-                split4(Sacc[2 * s + 1], h1, l1);
-                sbh[s] = cat(h0, h1);
-                sbl[s] = cat(l0, l1);
-            }
+            for (int n = 0; n < NV; ++n)
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    u16x4 h0, l0, h1, l1;
+                    split4(Sacc[n][2 * s], h0, l0);
+                    split4(Sacc[n][2 * s + 1], h1, l1);
+                    sbh[n][s] = cat(h0, h1);
+                    sbl[n][s] = cat(l0, l1);
+                }
         }
-        // rows 16m.. of src times S^T: lane (column v, rows t = 16m + 4 g4 + r)
-        auto times_state = [&](const unsigned short* src, int m) {
-            f32x4 x1 = zero4(), x2 = zero4();
+        // rows 16m.. of src times S^T for every value block of the wave: lane
+        // (column v, rows t = 16m + 4 g4 + r); each A fragment read once
+        auto times_state = [&](const unsigned short* src, int m, f32x4 (&res)[NV]) {
+            f32x4 x1[NV], x2[NV];
+#pragma unroll
+            for (int n = 0; n < NV; ++n) x1[n] = x2[n] = zero4();
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const u16x8 ra = *reinterpret_cast<const u16x8*>(&src[(16 * m + c16) * LDK + 32 * s + 8 * g4]);
-                x1 = mfma(ra, sbh[s], x1);
-                x2 = mfma(ra, sbl[s], x2);
+#pragma unroll
+                for (int n = 0; n < NV; ++n) {
+                    x1[n] = mfma(ra, sbh[n][s], x1[n]);
+                    x2[n] = mfma(ra, sbl[n][s], x2[n]);
+                }
             }
-            return x1 + x2;
+#pragma unroll
+            for (int n = 0; n < NV; ++n) res[n] = x1[n] + x2[n];
         };
         // X = K S^T
-        f32x4 X[4];
+        f32x4 X[4][NV];
         if constexpr (OUT) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) X[m] = times_state(sh.K, m);
+            for (int m = 0; m < 4; ++m) times_state(sh.K, m, X[m]);
         } else {
-            // k-step outer, one accumulator per tile (four waves per SIMD hide
-            // the dependent products)
+            // k-step outer, one accumulator per tile (the state pass runs two
+            // workgroups per CU, whose waves hide the dependent products)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) X[m] = zero4();
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < NV; ++n) X[m][n] = zero4();
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                u16x4 h0, l0, h1, l1;
-                split4(Sacc[2 * s], h0, l0);
-                split4(Sacc[2 * s + 1], h1, l1);
-                const u16x8 bh_ = cat(h0, h1), bl_ = cat(l0, l1);
+                u16x8 bh_[NV], bl_[NV];
+#pragma unroll
+                for (int n = 0; n < NV; ++n) {
+                    u16x4 h0, l0, h1, l1;
+                    split4(Sacc[n][2 * s], h0, l0);
+                    split4(Sacc[n][2 * s + 1], h1, l1);
+                    bh_[n] = cat(h0, h1);
+                    bl_[n] = cat(l0, l1);
+                }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const u16x8 ra = *reinterpret_cast<const u16x8*>(&sh.K[(16 * m + c16) * LDK + 32 * s + 8 * g4]);
-                    X[m] = mfma(ra, bh_, X[m]);
-                    X[m] = mfma(ra, bl_, X[m]);
+#pragma unroll
+                    for (int n = 0; n < NV; ++n) {
+                        X[m][n] = mfma(ra, bh_[n], X[m][n]);
+                        X[m][n] = mfma(ra, bl_[n], X[m][n]);
+                    }
                 }
             }
         }
@@ -1347,46 +1378,57 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             if (i + 1 < i_end) issue(i + 1);
         // U = V - diag(gamma') X, split hi/lo; Z = Q S^T (entry state of the
         // chunk) in the same loop so that its products overlap the U arithmetic
-        u16x4 uh[4], ul[4];
-        f32x4 Z[OUT ? 4 : 1];
+        u16x4 uh[NV][4], ul[NV][4];
+        f32x4 Z[OUT ? 4 : 1][NV];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            if constexpr (OUT) Z[m] = times_state(sh.Q, m);
+            if constexpr (OUT) times_state(sh.Q, m, Z[m]);
             const f32x4 gp = *reinterpret_cast<const f32x4*>(&sh.G[64 + 16 * m + 4 * g4]);
-            f32x4 u;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float vv = KIND == 0 ? gdn_bf16_to_f32(sh.V[(16 * m + 4 * g4 + r) * LDK + v]) : 0.f;
-                u[r] = vv - gp[r] * X[m][r];
+            for (int n = 0; n < NV; ++n) {
+                f32x4 u;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float vv = KIND == 0 ? gdn_bf16_to_f32(sh.V[(16 * m + 4 * g4 + r) * LDK + v[n]]) : 0.f;
+                    u[r] = vv - gp[r] * X[m][n][r];
+                }
+                split4(u, uh[n][m], ul[n][m]);
             }
-            split4(u, uh[m], ul[m]);
         }
         // Delta = T' U (tile m takes k-steps s <= m / 2); Delta hi/lo for the
         // output and Delta-bar = diag(gamma_C / gamma) Delta hi/lo for the state
-        u16x4 dh[4], dl[4], dbh[4], dbl[4];
+        u16x4 dh[NV][4], dl[NV][4], dbh[NV][4], dbl[NV][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            f32x4 d1 = zero4(), d2 = zero4(), d3 = zero4();
+            f32x4 d1[NV], d2[NV], d3[NV];
+#pragma unroll
+            for (int n = 0; n < NV; ++n) d1[n] = d2[n] = d3[n] = zero4();
 #pragma unroll
             for (int s = 0; s <= (m >> 1); ++s) {
                 const u16x8 th = sh.Tf[(tslot(m, s) * 2 + 0) * 64 + l];
                 const u16x8 tl = sh.Tf[(tslot(m, s) * 2 + 1) * 64 + l];
-                const u16x8 xh = cat(uh[2 * s], uh[2 * s + 1]);
-                const u16x8 xl = cat(ul[2 * s], ul[2 * s + 1]);
-                if constexpr (OUT) {
-                    d1 = mfma(th, xh, d1);
-                    d2 = mfma(th, xl, d2);
-                    d3 = mfma(tl, xh, d3);
-                } else {
-                    d1 = mfma(th, xh, d1);
-                    d1 = mfma(th, xl, d1);
-                    d1 = mfma(tl, xh, d1);
+#pragma unroll
+                for (int n = 0; n < NV; ++n) {
+                    const u16x8 xh = cat(uh[n][2 * s], uh[n][2 * s + 1]);
+                    const u16x8 xl = cat(ul[n][2 * s], ul[n][2 * s + 1]);
+                    if constexpr (OUT) {
+                        d1[n] = mfma(th, xh, d1[n]);
+                        d2[n] = mfma(th, xl, d2[n]);
+                        d3[n] = mfma(tl, xh, d3[n]);
+                    } else {
+                        d1[n] = mfma(th, xh, d1[n]);
+                        d1[n] = mfma(th, xl, d1[n]);
+                        d1[n] = mfma(tl, xh, d1[n]);
+                    }
                 }
             }
-            const f32x4 dd = OUT ? d1 + d2 + d3 : d1;
-            if constexpr (OUT) split4(dd, dh[m], dl[m]);
             const f32x4 rat = *reinterpret_cast<const f32x4*>(&sh.G[128 + 16 * m + 4 * g4]);
-            split4(rat * dd, dbh[m], dbl[m]);
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                const f32x4 dd = OUT ? d1[n] + d2[n] + d3[n] : d1[n];
+                if constexpr (OUT) split4(dd, dh[n][m], dl[n][m]);
+                split4(rat * dd, dbh[n][m], dbl[n][m]);
+            }
         }
         __syncthreads();  // K^T (and P) fragments of chunk i complete
 
@@ -1395,15 +1437,24 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         const float gC = sh.G[256];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
-            f32x4 acc = gC * Sacc[u], acc2 = zero4();
+            f32x4 acc[NV], acc2[NV];
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                acc[n] = gC * Sacc[n][u];
+                acc2[n] = zero4();
+            }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const u16x8 ka = sh.KtF[u][s][l];
-                acc = mfma(ka, cat(dbh[2 * s], dbh[2 * s + 1]), acc);
-                if constexpr (OUT) acc2 = mfma(ka, cat(dbl[2 * s], dbl[2 * s + 1]), acc2);
-                else acc = mfma(ka, cat(dbl[2 * s], dbl[2 * s + 1]), acc);
+#pragma unroll
+                for (int n = 0; n < NV; ++n) {
+                    acc[n] = mfma(ka, cat(dbh[n][2 * s], dbh[n][2 * s + 1]), acc[n]);
+                    if constexpr (OUT) acc2[n] = mfma(ka, cat(dbl[n][2 * s], dbl[n][2 * s + 1]), acc2[n]);
+                    else acc[n] = mfma(ka, cat(dbl[n][2 * s], dbl[n][2 * s + 1]), acc[n]);
+                }
             }
-            Sacc[u] = OUT ? acc + acc2 : acc;
+#pragma unroll
+            for (int n = 0; n < NV; ++n) Sacc[n][u] = OUT ? acc[n] + acc2[n] : acc[n];
         }
 
         // O = scale (diag(gamma) Z + P Delta) into the LDS output tile; it goes
@@ -1412,21 +1463,29 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         if constexpr (OUT) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                f32x4 o1 = zero4(), o2 = zero4(), o3 = zero4();
+                f32x4 o1[NV], o2[NV], o3[NV];
+#pragma unroll
+                for (int n = 0; n < NV; ++n) o1[n] = o2[n] = o3[n] = zero4();
 #pragma unroll
                 for (int s = 0; s <= (m >> 1); ++s) {
                     const u16x8 ph = sh.Pf[m][s][0][l];
                     const u16x8 pl = sh.Pf[m][s][1][l];
-                    const u16x8 xh = cat(dh[2 * s], dh[2 * s + 1]);
-                    const u16x8 xl = cat(dl[2 * s], dl[2 * s + 1]);
-                    o1 = mfma(ph, xh, o1);
-                    o2 = mfma(ph, xl, o2);
-                    o3 = mfma(pl, xh, o3);
+#pragma unroll
+                    for (int n = 0; n < NV; ++n) {
+                        const u16x8 xh = cat(dh[n][2 * s], dh[n][2 * s + 1]);
+                        const u16x8 xl = cat(dl[n][2 * s], dl[n][2 * s + 1]);
+                        o1[n] = mfma(ph, xh, o1[n]);
+                        o2[n] = mfma(ph, xl, o2[n]);
+                        o3[n] = mfma(pl, xh, o3[n]);
+                    }
                 }
                 const f32x4 gam = *reinterpret_cast<const f32x4*>(&sh.G[16 * m + 4 * g4]);
-                const f32x4 o = p.scale * (gam * Z[m] + o1 + o2 + o3);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sh.O[(16 * m + 4 * g4 + r) * LDO + v] = o[r];
+                for (int n = 0; n < NV; ++n) {
+                    const f32x4 o = p.scale * (gam * Z[m][n] + o1[n] + o2[n] + o3[n]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sh.O[(16 * m + 4 * g4 + r) * LDO + v[n]] = o[r];
+                }
             }
         }
         __syncthreads();  // every read of chunk i's inputs done, output tile complete
@@ -1444,8 +1503,10 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     }
     if (dst) {
 #pragma unroll
-        for (int u = 0; u < TPW; ++u)
-            *reinterpret_cast<f32x4*>(&dst[(int64_t)v * D + 16 * u + 4 * g4]) = Sacc[u];
+        for (int n = 0; n < NV; ++n)
+#pragma unroll
+            for (int u = 0; u < TPW; ++u)
+                *reinterpret_cast<f32x4*>(&dst[(int64_t)v[n] * D + 16 * u + 4 * g4]) = Sacc[n][u];
     }
 }
 
@@ -1564,21 +1625,34 @@ __global__ __launch_bounds__(256) void k_chain_split(Problem p, Split sp, WsLayo
 }
 
 // pass 1: workgroup (head, segment g < G - 1, kind); pass 2: (head, segment)
-// The state pass fits four waves per SIMD (two workgroups per CU).
+// Value blocks (16 columns) per wave.  One: eight waves at D = 128, two per
+// SIMD.  (Two blocks per wave read every shared A fragment once for twice the
+// products, but leave one wave per SIMD and measured slower.)
+template <int D>
+constexpr int kSegNV = 1;
+template <int D>
+constexpr int seg_threads() { return 64 * D / (16 * kSegNV<D>); }
+// The output pass runs one workgroup per CU, the state pass two.
 template <int D, int MODE>
-__global__ __launch_bounds__(4 * D, MODE == kSegState ? 4 : 2) void k_seg(Problem p, Split sp, WsLayout L, char* wsb,
-                                               const u16x8* tfrag, const float* gates) {
+constexpr int seg_waves_per_eu() {
+    constexpr int w = D / (64 * kSegNV<D>);
+    return (w < 1 ? 1 : w) * (MODE == kSegState ? 2 : 1);
+}
+template <int D, int MODE>
+__global__ __launch_bounds__(seg_threads<D>(), (seg_waves_per_eu<D, MODE>())) void k_seg(
+    Problem p, Split sp, WsLayout L, char* wsb, const u16x8* tfrag, const float* gates) {
+    constexpr int NV = kSegNV<D>;
     __shared__ __attribute__((aligned(16))) SegShared<D, MODE> sh;
     if constexpr (MODE == kSegOut) {
         const int id = blockIdx.x;
-        seg_body<D, MODE, 0>(p, sp, L, wsb, tfrag, gates, id / sp.G, id % sp.G, sh);
+        seg_body<D, MODE, 0, NV>(p, sp, L, wsb, tfrag, gates, id / sp.G, id % sp.G, sh);
     } else {
         const int kind = blockIdx.x & 1, id = blockIdx.x >> 1;
         const int nseg = sp.G - 1;
         const int gseg = id % nseg;
         const int64_t bh = id / nseg;
-        if (kind == 0) seg_body<D, MODE, 0>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
-        else if (gseg > 0) seg_body<D, MODE, 1>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
+        if (kind == 0) seg_body<D, MODE, 0, NV>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
+        else if (gseg > 0) seg_body<D, MODE, 1, NV>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
     }
 }
 
@@ -1736,7 +1810,7 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
     const int64_t heads = p.B * p.H;
     if (sp.G > 1) {
         prof_begin("k_seg_state", st);
-        hipLaunchKernelGGL((k_seg<D, kSegState>), dim3((unsigned)(heads * (sp.G - 1) * 2)), dim3(4 * D), 0, st,
+        hipLaunchKernelGGL((k_seg<D, kSegState>), dim3((unsigned)(heads * (sp.G - 1) * 2)), dim3(seg_threads<D>()), 0, st,
                            p, sp, L, ws, tfrag, gates);
         prof_end(st);
         hipError_t e = hipGetLastError();
@@ -1749,7 +1823,7 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
         if (e != hipSuccess) return e;
     }
     prof_begin("k_seg_out", st);
-    hipLaunchKernelGGL((k_seg<D, kSegOut>), dim3((unsigned)(heads * sp.G)), dim3(4 * D), 0, st, p, sp, L, ws,
+    hipLaunchKernelGGL((k_seg<D, kSegOut>), dim3((unsigned)(heads * sp.G)), dim3(seg_threads<D>()), 0, st, p, sp, L, ws,
                        tfrag, gates);
     prof_end(st);
     return hipGetLastError();
