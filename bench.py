@@ -133,8 +133,10 @@ def cpu_baseline(w, inp, max_threads=16, target_s=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # the GPU clock takes tens of milliseconds of load to settle: 200 untimed
+    # steps (about 0.1 s on the main workload) before the timed region
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="main-bf16")
     ap.add_argument("--segments", type=int, default=None,
                     help="sequence-parallel segments (default: the workload's)")
