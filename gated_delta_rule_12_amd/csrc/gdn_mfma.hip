@@ -1518,19 +1518,32 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 // bf16 MFMA with both factors split hi/lo (three products, fp32 accumulate).
 // M_end(g + 1) and the rows of S^D_end(g + 1) are fetched while step g
 // computes; the start states go to HBM after the fetch is issued.
+// Workgroups are dealt to the eight XCDs round-robin; when the head count is
+// a multiple of eight, the D/16 row blocks of one head are placed on one XCD
+// so that they share its L2 copy of M_end (one HBM fetch per head and step).
 template <int D>
 __global__ __launch_bounds__(256) void k_chain_split(Problem p, Split sp, WsLayout L, char* wsb) {
     constexpr int LD = D + 4;
     constexpr int MP = D * D / 4 / 256;  // float4 pieces of M per thread
     constexpr int SP = 16 * D / 4;       // float4 pieces of 16 rows
     constexpr int NTW = D / 64;          // column tiles per wave
+    constexpr int NX = D / 16;           // row blocks per head
     __shared__ __attribute__((aligned(16))) float Ms[D * LD];
     __shared__ __attribute__((aligned(16))) float Cb[2][16 * LD];
     __shared__ __attribute__((aligned(16))) float SDs[16 * LD];
-    const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int64_t heads = p.B * p.H;
+    int64_t bh;
+    int x;
+    if (heads % 8 == 0) {
+        const int64_t slot = blockIdx.x / 8;
+        bh = (slot / NX) * 8 + blockIdx.x % 8;
+        x = (int)(slot % NX);
+    } else {
+        bh = blockIdx.x / NX;
+        x = blockIdx.x % NX;
+    }
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int r0 = 16 * x;
-    const int64_t bh = (int64_t)b * p.H + h;
     const float* sdend = reinterpret_cast<const float*>(wsb + L.sdend);
     const float* mend = reinterpret_cast<const float*>(wsb + L.mend);
     float* sstart = reinterpret_cast<float*>(wsb + L.sstart);
@@ -1647,9 +1660,22 @@ __global__ __launch_bounds__(seg_threads<D>(), (seg_waves_per_eu<D, MODE>())) vo
         const int id = blockIdx.x;
         seg_body<D, MODE, 0, NV>(p, sp, L, wsb, tfrag, gates, id / sp.G, id % sp.G, sh);
     } else {
-        const int kind = blockIdx.x & 1, id = blockIdx.x >> 1;
+        // the two workgroups of a (head, segment) read the same K and T': when
+        // the pair count is a multiple of eight they are placed on one XCD
+        // (workgroups b and b + 8), so the second read hits in its L2
         const int nseg = sp.G - 1;
-        const int gseg = id % nseg;
+        const int64_t pairs = p.B * p.H * (int64_t)nseg;
+        int kind;
+        int64_t id;
+        if (pairs % 8 == 0) {
+            const int64_t r = blockIdx.x / 8;
+            kind = (int)(r & 1);
+            id = (r >> 1) * 8 + blockIdx.x % 8;
+        } else {
+            kind = blockIdx.x & 1;
+            id = blockIdx.x >> 1;
+        }
+        const int gseg = (int)(id % nseg);
         const int64_t bh = id / nseg;
         if (kind == 0) seg_body<D, MODE, 0, NV>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
         else if (gseg > 0) seg_body<D, MODE, 1, NV>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
@@ -1815,9 +1841,8 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        dim3 grid(D / 16, (unsigned)p.H, (unsigned)p.B);
         prof_begin("k_chain", st);
-        hipLaunchKernelGGL((k_chain_split<D>), grid, dim3(256), 0, st, p, sp, L, ws);
+        hipLaunchKernelGGL((k_chain_split<D>), dim3((unsigned)(heads * (D / 16))), dim3(256), 0, st, p, sp, L, ws);
         prof_end(st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
