@@ -1103,13 +1103,15 @@ struct SegShared {
 };
 
 // KIND 0: the state S (values from V); KIND 1: the scaling matrix M (V = 0,
-// identity start).
+// identity start); KIND 2 (state pass): both, waves 0 .. NWH - 1 on S and
+// NWH .. 2 NWH - 1 on M, sharing the staged chunk and the K^T fragments.
 template <int D, int MODE, int KIND, int NV>
 __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, const WsLayout& L, char* wsb,
                                          const u16x8* tfrag, const float* gates, int64_t bh, int gseg,
                                          SegShared<D, MODE>& sh) {
     constexpr bool OUT = MODE == kSegOut;
-    constexpr int NW = D / (16 * NV);  // waves; wave w owns value columns 16 NV w ..
+    constexpr int NWH = D / (16 * NV);         // waves per state; wave w owns value columns 16 NV (w % NWH) ..
+    constexpr int NW = KIND == 2 ? 2 * NWH : NWH;
     constexpr int NT = 64 * NW;
     constexpr int LDK = SegShared<D, MODE>::LDK;
     constexpr int LDO = SegShared<D, MODE>::LDO;
@@ -1123,6 +1125,8 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wv = KIND == 2 ? w % NWH : w;                      // value block of the wave
+    const bool mk = KIND == 2 ? w >= NWH : KIND == 1;           // the wave runs M
     const int l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int64_t H = p.H, T = p.T;
     const int b = (int)(bh / H), h = (int)(bh - (bh / H) * H);
@@ -1137,11 +1141,11 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     // (v = 16 (NV w + n) + c16, a = 16 tau + 4 g4 + r)
     int v[NV];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) v[n] = 16 * (NV * w + n) + c16;
+    for (int n = 0; n < NV; ++n) v[n] = 16 * (NV * wv + n) + c16;
     f32x4 Sacc[NV][TPW];
     {
         const float* src = nullptr;
-        if (KIND == 0) {
+        if (!mk) {
             if (gseg == 0) src = p.s0 ? p.s0 + bh * D * D : nullptr;
             else if (OUT) src = reinterpret_cast<const float*>(wsb + L.sstart) + (bh * sp.G + gseg) * D * D;
         }
@@ -1150,7 +1154,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
                 const int a0 = 16 * u + 4 * g4;
-                if (KIND == 1) {
+                if (mk) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Sacc[n][u][r] = v[n] == a0 + r ? 1.f : 0.f;
                 } else if (src) {
@@ -1171,7 +1175,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             const int e = tid + NT * k, t = min(e / PPR, nt - 1), c8 = e % PPR;
             const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
             kr[k] = *reinterpret_cast<const u32x4*>(kin + off);
-            if (KIND == 0) vr[k] = *reinterpret_cast<const u32x4*>(vin + off);
+            if (KIND != 1) vr[k] = *reinterpret_cast<const u32x4*>(vin + off);
             if (OUT) qr[k] = *reinterpret_cast<const u32x4*>(qin + off);
         }
         const u32x4* tp = reinterpret_cast<const u32x4*>(tfrag + (bh * p.NC + i) * kTfragPerChunk);
@@ -1187,7 +1191,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         for (int k = 0; k < KP; ++k) {
             const int e = tid + NT * k, t = e / PPR, c8 = e % PPR;
             const bool ok = t < nt;
-            *reinterpret_cast<u32x4*>(&sh.V[t * LDK + c8 * 8]) = (KIND == 0 && ok) ? vr[k] : z;
+            *reinterpret_cast<u32x4*>(&sh.V[t * LDK + c8 * 8]) = (KIND != 1 && ok) ? vr[k] : z;
             // columns 8 c8 .. +3 and +4 .. +7 of block c8 / 4 go to the
             // permuted positions 16 (c8 % 2) + 4 h and that + 8, h = (c8 % 4) / 2
             const int p0 = t * LDK + 32 * (c8 >> 2) + 16 * (c8 & 1) + 4 * ((c8 >> 1) & 1);
@@ -1389,7 +1393,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
                 f32x4 u;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float vv = KIND == 0 ? gdn_bf16_to_f32(sh.V[(16 * m + 4 * g4 + r) * LDK + v[n]]) : 0.f;
+                    const float vv = mk ? 0.f : gdn_bf16_to_f32(sh.V[(16 * m + 4 * g4 + r) * LDK + v[n]]);
                     u[r] = vv - gp[r] * X[m][n][r];
                 }
                 split4(u, uh[n][m], ul[n][m]);
@@ -1499,7 +1503,8 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     if (OUT) {
         if (gseg == sp.G - 1 && p.s_out) dst = p.s_out + bh * D * D;
     } else {
-        dst = reinterpret_cast<float*>(wsb + (KIND ? L.mend : L.sdend)) + (bh * sp.G + gseg) * D * D;
+        if (!mk || gseg > 0)  // (segment 0 needs no M)
+            dst = reinterpret_cast<float*>(wsb + (mk ? L.mend : L.sdend)) + (bh * sp.G + gseg) * D * D;
     }
     if (dst) {
 #pragma unroll
@@ -1643,16 +1648,14 @@ __global__ __launch_bounds__(256) void k_chain_split(Problem p, Split sp, WsLayo
 // products, but leave one wave per SIMD and measured slower.)
 template <int D>
 constexpr int kSegNV = 1;
-template <int D>
-constexpr int seg_threads() { return 64 * D / (16 * kSegNV<D>); }
-// The output pass runs one workgroup per CU, the state pass two.
+// threads per workgroup: one wave per value block; the state pass runs the S
+// and the M chain of a segment in one workgroup (twice the waves)
 template <int D, int MODE>
-constexpr int seg_waves_per_eu() {
-    constexpr int w = D / (64 * kSegNV<D>);
-    return (w < 1 ? 1 : w) * (MODE == kSegState ? 2 : 1);
-}
+constexpr int seg_threads() { return 64 * D / (16 * kSegNV<D>) * (MODE == kSegState ? 2 : 1); }
 template <int D, int MODE>
-__global__ __launch_bounds__(seg_threads<D>(), (seg_waves_per_eu<D, MODE>())) void k_seg(
+constexpr int seg_waves_per_eu() { return seg_threads<D, MODE>() / 256 < 1 ? 1 : seg_threads<D, MODE>() / 256; }
+template <int D, int MODE>
+__global__ __launch_bounds__((seg_threads<D, MODE>()), (seg_waves_per_eu<D, MODE>())) void k_seg(
     Problem p, Split sp, WsLayout L, char* wsb, const u16x8* tfrag, const float* gates) {
     constexpr int NV = kSegNV<D>;
     __shared__ __attribute__((aligned(16))) SegShared<D, MODE> sh;
@@ -1660,25 +1663,9 @@ __global__ __launch_bounds__(seg_threads<D>(), (seg_waves_per_eu<D, MODE>())) vo
         const int id = blockIdx.x;
         seg_body<D, MODE, 0, NV>(p, sp, L, wsb, tfrag, gates, id / sp.G, id % sp.G, sh);
     } else {
-        // the two workgroups of a (head, segment) read the same K and T': when
-        // the pair count is a multiple of eight they are placed on one XCD
-        // (workgroups b and b + 8), so the second read hits in its L2
+        // workgroup (head, segment g < G - 1)
         const int nseg = sp.G - 1;
-        const int64_t pairs = p.B * p.H * (int64_t)nseg;
-        int kind;
-        int64_t id;
-        if (pairs % 8 == 0) {
-            const int64_t r = blockIdx.x / 8;
-            kind = (int)(r & 1);
-            id = (r >> 1) * 8 + blockIdx.x % 8;
-        } else {
-            kind = blockIdx.x & 1;
-            id = blockIdx.x >> 1;
-        }
-        const int gseg = (int)(id % nseg);
-        const int64_t bh = id / nseg;
-        if (kind == 0) seg_body<D, MODE, 0, NV>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
-        else if (gseg > 0) seg_body<D, MODE, 1, NV>(p, sp, L, wsb, tfrag, gates, bh, gseg, sh);
+        seg_body<D, MODE, 2, NV>(p, sp, L, wsb, tfrag, gates, blockIdx.x / nseg, blockIdx.x % nseg, sh);
     }
 }
 
@@ -1836,7 +1823,7 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
     const int64_t heads = p.B * p.H;
     if (sp.G > 1) {
         prof_begin("k_seg_state", st);
-        hipLaunchKernelGGL((k_seg<D, kSegState>), dim3((unsigned)(heads * (sp.G - 1) * 2)), dim3(seg_threads<D>()), 0, st,
+        hipLaunchKernelGGL((k_seg<D, kSegState>), dim3((unsigned)(heads * (sp.G - 1))), dim3(seg_threads<D, kSegState>()), 0, st,
                            p, sp, L, ws, tfrag, gates);
         prof_end(st);
         hipError_t e = hipGetLastError();
@@ -1848,7 +1835,7 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
         if (e != hipSuccess) return e;
     }
     prof_begin("k_seg_out", st);
-    hipLaunchKernelGGL((k_seg<D, kSegOut>), dim3((unsigned)(heads * sp.G)), dim3(seg_threads<D>()), 0, st, p, sp, L, ws,
+    hipLaunchKernelGGL((k_seg<D, kSegOut>), dim3((unsigned)(heads * sp.G)), dim3(seg_threads<D, kSegOut>()), 0, st, p, sp, L, ws,
                        tfrag, gates);
     prof_end(st);
     return hipGetLastError();
