@@ -252,6 +252,7 @@ WHOLE = [
     (2, 16, 2000, 128, None, PTD, 0.5, 2.0),  # library schedule (7 segments)
     (1, 32, 512, 128, 4, PTD, 0.0, 6.0),     # long memory, zero start state
     (1, 32, 512, 128, 4, DTP, 0.5, -6.0),    # fast forgetting
+    (1, 20, 2048, 128, 8, PTD, 0.5, 2.0),    # head count not a multiple of 8
 ]
 
 
