@@ -1072,9 +1072,10 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 // Long sequences are cut into segments run side by side in two passes, after
 // the sequence-parallel notes (the state at a segment end is the increment
 // from a zero start plus the entry state through the scaling matrix):
-//   pass 1 (kSegState): per segment g < G-1 the increment S^D from zero
-//     (segment 0: from the true start state) and the scaling matrix M from I
-//     (the same recurrence with V = 0), end values only;
+//   pass 1 (kSegState): one workgroup per segment g < G-1 runs the increment
+//     S^D from zero (segment 0: from the true start state) on one half of its
+//     waves and the scaling matrix M from I (the same recurrence with V = 0)
+//     on the other, on the same staged chunks; end values only;
 //   the start-state chain S_start(g+1) = S^D_end(g) + S_start(g) M_end(g);
 //   pass 2 (kSegOut): every segment from its true entry state, with outputs.
 // Per chunk: X = K S^T and Z = Q S^T (S^T split hi/lo), U = V - diag(gamma') X,
