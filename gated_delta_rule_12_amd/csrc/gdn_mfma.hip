@@ -1168,21 +1168,24 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 
     // ---- staging: chunk i+1 in registers while chunk i computes
     u32x4 kr[KP], vr[KP], qr[OUT ? KP : 1], tr[TFP], gr;
-    auto issue = [&](int i) {
+    // part mask: 1 K, 2 V, 4 Q, 8 T' fragments and gate block
+    auto issue = [&](int i, int parts = 15) {
         const int64_t t0 = (int64_t)i * C;
         const int nt = (int)((T - t0) < C ? (T - t0) : C);
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
             const int e = tid + NT * k, t = min(e / PPR, nt - 1), c8 = e % PPR;
             const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
-            kr[k] = *reinterpret_cast<const u32x4*>(kin + off);
-            if (KIND != 1) vr[k] = *reinterpret_cast<const u32x4*>(vin + off);
-            if (OUT) qr[k] = *reinterpret_cast<const u32x4*>(qin + off);
+            if (parts & 1) kr[k] = *reinterpret_cast<const u32x4*>(kin + off);
+            if (KIND != 1 && (parts & 2)) vr[k] = *reinterpret_cast<const u32x4*>(vin + off);
+            if (OUT && (parts & 4)) qr[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qin + off));
         }
-        const u32x4* tp = reinterpret_cast<const u32x4*>(tfrag + (bh * p.NC + i) * kTfragPerChunk);
+        if (parts & 8) {
+            const u32x4* tp = reinterpret_cast<const u32x4*>(tfrag + (bh * p.NC + i) * kTfragPerChunk);
 #pragma unroll
-        for (int k = 0; k < TFP; ++k) tr[k] = tp[min(tid + NT * k, kTfragPerChunk - 1)];
-        gr = reinterpret_cast<const u32x4*>(gates + (bh * p.NC + i) * kGateFloats)[min(tid, GP - 1)];
+            for (int k = 0; k < TFP; ++k) tr[k] = tp[min(tid + NT * k, kTfragPerChunk - 1)];
+            gr = reinterpret_cast<const u32x4*>(gates + (bh * p.NC + i) * kGateFloats)[min(tid, GP - 1)];
+        }
     };
     auto store = [&](int i) {
         const int64_t t0 = (int64_t)i * C;
@@ -1254,7 +1257,9 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         }
     }
     // the output tile of chunk i (LDS) to HBM: 16-byte pieces of whole rows,
-    // rows past the sequence end dropped
+    // rows past the sequence end dropped.  O is written once and Q read once
+    // per forward; both go with non-temporal hints, which leaves the caches
+    // to K, V and T' (read by both passes) and measured 7 % off this pass
     auto flush = [&](int i) {
         constexpr int OPR = D / 4, OP = C * OPR / NT;
         const int64_t t0 = (int64_t)i * C;
@@ -1264,8 +1269,8 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         for (int k = 0; k < OP; ++k) {
             const int e = tid + NT * k, t = e / OPR, c4 = e % OPR;
             if (t < nt)
-                *reinterpret_cast<f32x4*>(obase + (int64_t)t * row_stride + 4 * c4) =
-                    *reinterpret_cast<const f32x4*>(&sh.O[t * LDO + 4 * c4]);
+                __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sh.O[t * LDO + 4 * c4]),
+                                            reinterpret_cast<f32x4*>(obase + (int64_t)t * row_stride + 4 * c4));
         }
     };
     if (i_begin < i_end) {
@@ -1287,10 +1292,14 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         __syncthreads();  // chunk i staged
         // the previous chunk's output and the next chunk's loads go out here,
         // overlapping this chunk's products
+        // the output pass fetches the next chunk's K and V here, its Q, T'
+        // and gates after the first product and writes the previous chunk's
+        // output tile after the second, so that the loads and stores of one
+        // chunk (about 100 KiB per CU) do not queue up at one point and stall
+        // the waves behind them
+        const bool more = i + 1 < i_end;
         if constexpr (OUT)
-            if (i > i_begin) flush(i - 1);
-        if constexpr (OUT)
-            if (i + 1 < i_end) issue(i + 1);
+            if (more) issue(i + 1, 3);
         if constexpr (OUT) scores();
         // K^T fragments by exact MFMA products with the identity: job (s', u)
         // turns token tiles 2s', 2s' + 1 of key tile u into the A fragment of
@@ -1380,7 +1389,9 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         // (the state pass fetches the next chunk only now, so that the staging
         // registers are not live across these products)
         if constexpr (!OUT)
-            if (i + 1 < i_end) issue(i + 1);
+            if (more) issue(i + 1);
+        if constexpr (OUT)
+            if (more) issue(i + 1, 12);
         // U = V - diag(gamma') X, split hi/lo; Z = Q S^T (entry state of the
         // chunk) in the same loop so that its products overlap the U arithmetic
         u16x4 uh[NV][4], ul[NV][4];
@@ -1400,6 +1411,8 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
                 split4(u, uh[n][m], ul[n][m]);
             }
         }
+        if constexpr (OUT)
+            if (i > i_begin) flush(i - 1);
         // Delta = T' U (tile m takes k-steps s <= m / 2); Delta hi/lo for the
         // output and Delta-bar = diag(gamma_C / gamma) Delta hi/lo for the state
         u16x4 dh[NV][4], dl[NV][4], dbh[NV][4], dbl[NV][4];
