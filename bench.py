@@ -11,6 +11,8 @@ run of the same number of steps.
 Default workload: main-bf16 (B=2, H=16, T=8192, dk=dv=128, chunk 64, scalar
 gate, start state N(0, 0.02^2)).  The long workload runs the sequence-parallel
 entry point (8 segments) and also reports the single-stream time beside it.
+--workload decode-bf16 times gdn_decode_step instead: one token for each of
+256 x 16 persistent states, updated in place.
 """
 from __future__ import annotations
 
@@ -135,6 +137,95 @@ def cpu_baseline(w, inp, max_threads=16, target_s=10.0):
                       f"fp64 token loop, {dt:.2f} s; tokens/s = head-tokens/s / H"}
 
 
+def decode_bytes(w) -> float:
+    """HBM bytes one decode step must move per batch: read and write every
+    state (fp32), read the token's q, k, v, alpha, beta, write o."""
+    s_in = 2 if w.dtype == "bf16" else 4
+    per_head = (8 * w.dk * w.dv + (2 * w.dk + w.dv) * s_in + 4
+                + (4 * w.dk if w.gate == "channel" else 4) + 4 * w.dv)
+    return float(per_head * w.B * w.H)
+
+
+def cpu_baseline_decode(w, inp, max_threads=16, target_s=10.0, n_pairs=1024):
+    """Time the oracle's token loop (T = 1) on a sample of (batch, head)
+    states of the decode batch."""
+    import numpy as np
+
+    import oracle
+    cores = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    g = oracle.GATE_SCALAR if w.gate == "scalar" else oracle.GATE_CHANNEL
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)][:n_pairs]
+    pick = lambda name: np.stack([inp[name][b, :, h] for b, h in sel])[:, :, None]
+    q, k, v, a, be = (pick(n) for n in ("q", "k", "v", "alpha", "beta"))
+    s0 = np.stack([inp["state0"][b, h] for b, h in sel])[:, None]
+    reps, dt = 0, 0.0
+    while dt < target_s and reps < 10000:
+        t = time.perf_counter()
+        oracle.forward(q, k, v, a, be, s0, gate=g, threads=cores)
+        dt += time.perf_counter() - t
+        reps += 1
+    return {"value": reps * len(sel) / w.H / dt, "unit": "tokens/sec", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} x {len(sel)} (batch,head) states of {w.name}, one token each, "
+                      f"fp64 token loop, {dt:.2f} s; tokens/s = head-steps/s / H"}
+
+
+def bench_decode(args, w):
+    """One step = gdn_decode_step over the whole batch, in place."""
+    import torch
+
+    from gated_delta_rule_12_amd import gdn
+    from gated_delta_rule_12_amd.workloads import make_inputs, to_device
+    inp = make_inputs(w)
+    d = to_device(inp, w, "cuda")
+    tok = {n: d[n][:, 0].contiguous() for n in ("q", "k", "v", "alpha", "beta")}
+    st = d["state0"].clone()
+    out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device="cuda")
+
+    def step():
+        gdn.decode_step(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], st,
+                        out=out, inplace=True)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gdn.gdn_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern = gdn.gdn_profile_read()
+    gdn.gdn_profile_enable(False)
+    k_us = 1e3 * kern["k_decode"][0] / kern["k_decode"][1]
+    abytes = decode_bytes(w)
+    achieved = abytes / (k_us * 1e-6) / 1e9
+    log(f"step {ms * 1e3:.1f} us, k_decode {k_us:.1f} us per launch")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(w, inp)
+    res = {"metric": "decode tokens/sec (one gated-delta token per sequence, H=16 d=128)",
+           "value": round(w.B / (ms * 1e-3), 1), "unit": "tokens/sec", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv,
+                      "gate": w.gate, "input_dtype": w.dtype, "entry": "gdn_decode_step",
+                      "state": "in place", "global_batch": w.B, "parallelism": "single-gpu"},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": stored_traffic(w.name, "k_decode"), "kernel": "k_decode",
+                        "kernel_timing": "HIP events around each launch, in a second run of the same steps after the timed region",
+                        "kernel_avg_launch_us": round(k_us, 2), "algorithmic_bytes": abytes,
+                        "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1)},
+           "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +257,9 @@ def main():
     from gated_delta_rule_12_amd.workloads import make_inputs, to_device, workload
 
     w = workload(int(args.workload) if args.workload.isdigit() else args.workload)
+    if w.name == "decode-bf16":
+        bench_decode(args, w)
+        return
     # None: gdn_chunk_fwd with the library's schedule; a count: gdn_seqpar_fwd
     G = args.segments if args.segments is not None else (w.n_segments if w.n_segments > 1 else None)
     log(f"workload {w}, segments {G if G is not None else 'library schedule'}")

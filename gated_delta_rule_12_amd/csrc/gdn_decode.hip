@@ -1,0 +1,160 @@
+// One-token step of the gated delta rule on a persistent state
+// (gdn_decode_step).
+//
+// Generation runs the fixed-size-state recurrence: each new token updates
+// the dv x dk state once and reads it once, at a cost that does not grow
+// with the history (DeltaNet illustrated notes, the part on linear attention
+// as an RNN; the per-token update is that of the Gated DeltaNet
+// GPU-parallelisation blog, section 1.2, in the notes' dv x dk orientation).
+//
+// Given the token's k, q, gate and beta, the rows r of S (value dimensions)
+// are independent:
+//   predict-then-decay:  p_r = S_r . k;  S'_r = S_r D + beta (v_r - p_r) k
+//   decay-then-predict:  S_r <- S_r D;  p_r = S_r . k;  S'_r = S_r + beta (v_r - p_r) k
+//   o_r = scale S'_r . q
+// so the step is a stream over S: 8 dk dv bytes of HBM traffic per head (read
+// and write), against 4 flops per element.  LPR lanes hold one row as float4
+// pieces (16-byte loads and stores; a wave covers 64 / LPR whole rows, which
+// are contiguous in memory), the two dot products are reduced across the
+// row's lanes with shuffles, and each thread keeps kRows rows in flight so
+// that enough bytes are outstanding per CU to cover the HBM latency.  The
+// state is read and written with non-temporal hints: each byte is touched
+// once per step, and keeping it out of the caches took a quarter less time
+// than cached accesses.
+#include "gdn_internal.h"
+#include "../../include/gdn.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 4;  // rows per thread
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
+    if constexpr (DT == 0) {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+}
+
+__device__ __forceinline__ float dot4(const float4& a, const float4& b) {
+    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+
+// sum over the LPR lanes of a row (aligned groups of LPR lanes)
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// grid (row blocks, H, B); block: 4 waves, wave w covers rows
+// rb RB + (j 4 + w) RPW + l / LPR for j < kRows
+template <int DT, int LPR>
+__global__ __launch_bounds__(kThreads) void k_decode(Problem p) {
+    constexpr int RPW = 64 / LPR;            // rows per wave and pass
+    constexpr int RB = 4 * RPW * kRows;      // rows per block
+    const int64_t b = blockIdx.z, h = blockIdx.y, H = p.H;
+    const int64_t bh = b * H + h;
+    const int dk = (int)p.dk, dv = (int)p.dv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int c = l % LPR;                   // float4 piece of the row
+    const bool col = 4 * c < dk;
+    const bool channel = p.gate == GDN_GATE_CHANNEL;
+    const bool dtp = p.order == GDN_DECAY_THEN_PREDICT;
+
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 k4 = col ? ld4<DT>(p.k, bh * dk + 4 * c) : z4;
+    const float4 q4 = col ? ld4<DT>(p.q, bh * dk + 4 * c) : z4;
+    float4 d4;
+    if (channel) {
+        d4 = col ? *reinterpret_cast<const float4*>(p.alpha + bh * dk + 4 * c) : z4;
+    } else {
+        const float a = p.alpha[bh];
+        d4 = make_float4(a, a, a, a);
+    }
+    const float beta = p.beta[bh];
+
+    int r[kRows];
+    bool on[kRows];
+    float4 s[kRows];
+    float vr[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        r[j] = blockIdx.x * RB + (j * 4 + w) * RPW + l / LPR;
+        on[j] = r[j] < dv;
+        const int64_t off = (bh * dv + r[j]) * dk + 4 * c;
+        s[j] = z4;
+        if (on[j] && col && p.s0) {
+            const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p.s0 + off));
+            s[j] = make_float4(x[0], x[1], x[2], x[3]);
+        }
+        vr[j] = on[j] ? gdn_ld<DT>(p.v, bh * dv + r[j]) : 0.f;
+    }
+    float pr[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        if (dtp) s[j] = make_float4(s[j].x * d4.x, s[j].y * d4.y, s[j].z * d4.z, s[j].w * d4.w);
+        pr[j] = dot4(s[j], k4);
+    }
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) pr[j] = row_sum<LPR>(pr[j]);
+    float o[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        const float e = beta * (vr[j] - pr[j]);
+        float4 n;
+        if (dtp) {
+            n = make_float4(s[j].x + e * k4.x, s[j].y + e * k4.y, s[j].z + e * k4.z, s[j].w + e * k4.w);
+        } else {
+            n = make_float4(s[j].x * d4.x + e * k4.x, s[j].y * d4.y + e * k4.y,
+                            s[j].z * d4.z + e * k4.z, s[j].w * d4.w + e * k4.w);
+        }
+        s[j] = n;
+        o[j] = dot4(n, q4);
+    }
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) o[j] = row_sum<LPR>(o[j]);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        if (on[j] && col) {
+            const f32x4v x = {s[j].x, s[j].y, s[j].z, s[j].w};
+            __builtin_nontemporal_store(x, reinterpret_cast<f32x4v*>(p.s_out + (bh * dv + r[j]) * dk + 4 * c));
+        }
+        if (on[j] && c == 0) p.out[bh * dv + r[j]] = p.scale * o[j];
+    }
+}
+
+template <int DT, int LPR>
+hipError_t launch_lpr(const Problem& p, hipStream_t st) {
+    constexpr int RB = 4 * (64 / LPR) * kRows;
+    const dim3 grid((unsigned)((p.dv + RB - 1) / RB), (unsigned)p.H, (unsigned)p.B);
+    hipLaunchKernelGGL((k_decode<DT, LPR>), grid, dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const Problem& p, hipStream_t st) {
+    const int64_t pieces = p.dk / 4;  // float4 pieces per row, 4 .. 32
+    if (pieces <= 4) return launch_lpr<DT, 4>(p, st);
+    if (pieces <= 8) return launch_lpr<DT, 8>(p, st);
+    if (pieces <= 16) return launch_lpr<DT, 16>(p, st);
+    return launch_lpr<DT, 32>(p, st);
+}
+
+}  // namespace
+
+hipError_t decode_step(const Problem& p, hipStream_t st) {
+    prof_begin("k_decode", st);
+    hipError_t e = p.dtype == GDN_BF16 ? launch_dt<1>(p, st) : launch_dt<0>(p, st);
+    prof_end(st);
+    return e;
+}
+
+}  // namespace gdn

@@ -5,8 +5,9 @@ kernels of libgdn.so.  PyTorch supplies device memory and the stream.  There
 is no fallback: if the library is missing or no GPU is present, calls raise.
 
 Low-level names mirror the C ABI (gdn_chunk_fwd, gdn_recurrent_ref,
-gdn_seqpar_fwd, ...); chunk_fwd / seqpar_fwd / recurrent_ref are the same
-calls taking torch tensors and allocating the outputs and the workspace.
+gdn_seqpar_fwd, gdn_decode_step, ...); chunk_fwd / seqpar_fwd / recurrent_ref /
+decode_step are the same calls taking torch tensors and allocating the
+outputs and the workspace.
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ GDN_OK, GDN_E_ARG, GDN_E_SHAPE, GDN_E_UNSUPPORTED, GDN_E_WORKSPACE, GDN_E_HIP = 
 GDN_PATH_VALU, GDN_PATH_MFMA = 0, 1
 
 # every symbol include/gdn.h declares
-EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_workspace_bytes",
+EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_step",
+           "gdn_workspace_bytes",
            "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_status_str", "gdn_abi_version",
            "gdn_profile_enable", "gdn_profile_read")
 
@@ -55,6 +57,8 @@ def lib():
     L.gdn_seqpar_fwd.restype = ctypes.c_int
     L.gdn_recurrent_ref.argtypes = shape + [i32, i32, i32, f32] + tens + [vp]
     L.gdn_recurrent_ref.restype = ctypes.c_int
+    L.gdn_decode_step.argtypes = [i64] * 4 + [i32, i32, i32, f32] + tens + [vp]
+    L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_workspace_bytes.argtypes = shape + [i32, i32, i32, i32]
     L.gdn_workspace_bytes.restype = sz
     L.gdn_validate.argtypes = shape + [i32, i32, i32, i32, i32]
@@ -88,6 +92,10 @@ def gdn_seqpar_fwd(*args):
 
 def gdn_recurrent_ref(*args):
     return lib().gdn_recurrent_ref(*args)
+
+
+def gdn_decode_step(*args):
+    return lib().gdn_decode_step(*args)
 
 
 def gdn_workspace_bytes(B, T, H, dk, dv, chunk, dtype, gate, n_segments=1) -> int:
@@ -241,4 +249,50 @@ def recurrent_ref(q, k, v, alpha, beta, state0=None, *, order=GDN_PREDICT_THEN_D
                            _ptr(out), _ptr(state_out), _stream())
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_recurrent_ref")
+    return out, state_out
+
+
+def decode_step(q, k, v, alpha, beta, state=None, *, order=GDN_PREDICT_THEN_DECAY,
+                scale=1.0, out=None, state_out=None, inplace=False):
+    """One token on a persistent state: gdn_decode_step.
+    q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), alpha [B,H] or [B,H,dk], beta
+    [B,H] fp32, state [B,H,dv,dk] fp32 or None (zero).  inplace=True writes the
+    new state over `state`.  Returns (out [B,H,dv] fp32, new state)."""
+    import torch
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [B,H,dk] and v [B,H,dv]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    tensors = [q, k, v, alpha, beta] + ([state] if state is not None else [])
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous and on the GPU")
+    for t in tensors[3:]:
+        if t.dtype != torch.float32:
+            raise TypeError("alpha, beta, state must be float32")
+    if alpha.shape == (B, H):
+        gate = GDN_GATE_SCALAR
+    elif alpha.shape == (B, H, dk):
+        gate = GDN_GATE_CHANNEL
+    else:
+        raise ValueError("alpha must be [B,H] or [B,H,dk]")
+    if beta.shape != (B, H):
+        raise ValueError("beta must be [B,H]")
+    if state is not None and state.shape != (B, H, dv, dk):
+        raise ValueError("state must be [B,H,dv,dk]")
+    if inplace:
+        if state is None:
+            raise ValueError("inplace needs a state")
+        state_out = state
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    if state_out is None:
+        state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    rc = gdn_decode_step(B, H, dk, dv, _dtype_code(q), gate, order, scale,
+                         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+                         _ptr(out), _ptr(state_out), _stream())
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode_step")
     return out, state_out

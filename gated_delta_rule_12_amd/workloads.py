@@ -65,13 +65,20 @@ WORKLOADS = [
              gate="channel", seed=1238),
 ]
 
+# One decode step (T = 1) of a serving batch: 256 sequences x 16 heads at
+# d = 128, each with a persistent fp32 state.  The pages give no decode size;
+# this batch makes the step stream 512 MiB of state (read and write), well
+# past launch latency, with the main workload's head shape and distributions.
+DECODE_WORKLOAD = Workload("decode-bf16", B=256, H=16, T=1, dk=128, dv=128, chunk=64,
+                           state0_std=0.02, seed=1239)
+
 
 def workload(key) -> Workload:
     if isinstance(key, Workload):
         return key
     if isinstance(key, int):
         return WORKLOADS[key]
-    for w in WORKLOADS:
+    for w in WORKLOADS + [DECODE_WORKLOAD]:
         if w.name == key:
             return w
     raise KeyError(key)

@@ -108,6 +108,30 @@ int gdn_recurrent_ref(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                       float* out, float* state_out, void* stream);
 
 /*
+ * gdn_decode_step — one token on a persistent state, for generation: the
+ * fixed-size-state recurrence of the DeltaNet illustrated notes' linear
+ * attention as an RNN part, with the gated delta update above.  For every
+ * (batch, head) it reads state_in, applies the update for the token
+ * (q, k, v, gate, beta) in the given order, writes the new state to
+ * state_out and the read o = scale * S q to out.  Equal to gdn_recurrent_ref
+ * with T = 1.
+ *   q, k       [B, H, dk]   bf16 or fp32 (dtype); v [B, H, dv], same dtype
+ *   alpha      [B, H] fp32 (scalar gate) or [B, H, dk] fp32 (channel)
+ *   beta       [B, H] fp32
+ *   state_in   [B, H, dv, dk] fp32, or NULL for a zero state
+ *   out        [B, H, dv] fp32
+ *   state_out  [B, H, dv, dk] fp32, required; may equal state_in (in place)
+ * Alignment: q and k on 8 bytes (bf16) or 16 bytes (fp32); state_in,
+ * state_out and a channel alpha on 16 bytes; otherwise GDN_E_ARG.  Needs no
+ * workspace.  dk, dv as for gdn_chunk_fwd; other statuses as above.
+ */
+int gdn_decode_step(int64_t B, int64_t H, int64_t dk, int64_t dv,
+                    int32_t dtype, int32_t gate, int32_t order, float scale,
+                    const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, const float* state_in,
+                    float* out, float* state_out, void* stream);
+
+/*
  * gdn_seqpar_fwd — increment-and-correct sequence parallelism (How to
  * Implement Sequence Parallelism in DeltaNet, papercache notes, sections
  * "parallel algorithm derivation" and "CP=4").  The chunks of every sequence

@@ -143,3 +143,40 @@ def test_chunk_schedule():
     assert seg(8, 4096, 16, 128, 128, 64, 1, 1) == 1       # channel gate
     assert seg(1, 256, 1, 16, 16, 16, 0, 0) == 1           # fp32 vector-ALU path
     assert seg(1, 100, 1, 60, 64, 64, 1, 0) < 0            # bad shape
+
+
+def test_decode_step_rejects_bad_arguments_before_any_launch():
+    """gdn_decode_step's checks return before anything is enqueued (fake,
+    never dereferenced pointers)."""
+    import ctypes
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    shape = (2, 4, 128, 128)
+    tail = (gdn.GDN_BF16, gdn.GDN_GATE_SCALAR, gdn.GDN_PREDICT_THEN_DECAY, 1.0)
+    ok_ptrs = [fake] * 8
+    # state_out is required
+    rc = gdn.gdn_decode_step(*shape, *tail, *ok_ptrs[:7], nul, nul)
+    assert rc == gdn.GDN_E_ARG
+    # the state moves in 16-byte pieces
+    rc = gdn.gdn_decode_step(*shape, *tail, *ok_ptrs[:5], ctypes.c_void_p(0x1008), fake, fake, nul)
+    assert rc == gdn.GDN_E_ARG
+    # bf16 q, k in 8-byte pieces; fp32 in 16-byte pieces
+    rc = gdn.gdn_decode_step(*shape, *tail, ctypes.c_void_p(0x1004), *ok_ptrs[1:], nul)
+    assert rc == gdn.GDN_E_ARG
+    rc = gdn.gdn_decode_step(*shape, gdn.GDN_F32, *tail[1:], fake, ctypes.c_void_p(0x1008),
+                             *ok_ptrs[2:], nul)
+    assert rc == gdn.GDN_E_ARG
+    # a vector gate in 16-byte pieces
+    rc = gdn.gdn_decode_step(*shape, gdn.GDN_BF16, gdn.GDN_GATE_CHANNEL, *tail[2:], fake, fake,
+                             fake, ctypes.c_void_p(0x1004), *ok_ptrs[4:], nul)
+    assert rc == gdn.GDN_E_ARG
+    # enums and sizes as for the other entry points
+    rc = gdn.gdn_decode_step(*shape, 9, *tail[1:], *ok_ptrs, nul)
+    assert rc == gdn.GDN_E_ARG
+    rc = gdn.gdn_decode_step(2, 4, 60, 128, *tail, *ok_ptrs, nul)
+    assert rc == gdn.GDN_E_UNSUPPORTED
+    rc = gdn.gdn_decode_step(-1, 4, 128, 128, *tail, *ok_ptrs, nul)
+    assert rc == gdn.GDN_E_SHAPE
+    # empty batch: nothing to do
+    rc = gdn.gdn_decode_step(0, 4, 128, 128, *tail, *([nul] * 8), nul)
+    assert rc == gdn.GDN_OK

@@ -440,3 +440,22 @@ def test_empty_sequence_returns_start_state():
                           z(1, 0, 2), S0)
     assert o.shape == (1, 0, 2, 3)
     np.testing.assert_array_equal(s, S0)
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("order", [PTD, DTP])
+def test_one_token_calls_thread_the_state(gate, order):
+    """The recurrence carries nothing but S between tokens (the fixed-size
+    state of the linear-attention-as-RNN reading): T calls of one token each,
+    each starting from the previous call's state, equal one call over the T
+    tokens.  This is what makes the oracle the reference for chains of
+    single-token decode steps."""
+    rng = np.random.default_rng(21 + gate + 2 * order)
+    q, k, v, alpha, beta, S0 = rand_seq(rng, 9, 6, 5, gate=gate)
+    o, s = run1(q, k, v, alpha, beta, S0=S0, gate=gate, order=order)
+    st = S0
+    for t in range(9):
+        o1, st = run1(q[t:t + 1], k[t:t + 1], v[t:t + 1], alpha[t:t + 1], beta[t:t + 1],
+                      S0=st, gate=gate, order=order)
+        np.testing.assert_array_equal(o1[0], o[t])
+    np.testing.assert_array_equal(st, s)
