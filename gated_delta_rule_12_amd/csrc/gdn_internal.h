@@ -49,6 +49,7 @@ struct WsLayout {
     size_t mend = 0, mend_bytes = 0;     // seq-par: per-segment end scaling matrices
     size_t sstart = 0, sstart_bytes = 0; // seq-par: per-segment true start states
     size_t sfrag = 0, sfrag_bytes = 0;   // seq-par, MFMA family: start states as bf16 hi/lo fragments
+    size_t blk = 0, blk_bytes = 0;       // seq-par, whole-head path: composed maps of blocks of segments
     size_t total = 0;
 };
 

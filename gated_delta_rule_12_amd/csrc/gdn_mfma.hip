@@ -33,7 +33,8 @@
 //   one workgroup per (batch, head, segment) holds the whole state S^T in
 //   registers, wave w the value columns 16w..16w+15; sequences cut into
 //   segments run as a state pass (increment S^D and scaling matrix M per
-//   segment), the start-state chain (k_chain_split) and an output pass from
+//   segment), the start-state chain (k_chain_rows: sequential, or a two-level
+//   scan over blocks of segments when they are many) and an output pass from
 //   the true entry states.
 // k_rec_mfma (channel gate, or too few groups): one workgroup per (batch,
 //   head, segment, 16-row slice of the state); wave w owns token rows
@@ -1530,128 +1531,238 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 }
 
 // Start-state chain of the whole-head path, S_start(g + 1) = S^D_end(g) +
-// S_start(g) M_end(g), g = 1 .. G - 2, stopping at the last segment's start
-// state (sequence-parallel notes: the state at a segment end is the
-// increment plus the entry state through the scaling matrix).  One
-// workgroup per 16 rows of one head; each step is a 16 x D x D product on
-// bf16 MFMA with both factors split hi/lo (three products, fp32 accumulate).
-// M_end(g + 1) and the rows of S^D_end(g + 1) are fetched while step g
-// computes; the start states go to HBM after the fetch is issued.
-// Workgroups are dealt to the eight XCDs round-robin; when the head count is
-// a multiple of eight, the D/16 row blocks of one head are placed on one XCD
-// so that they share its L2 copy of M_end (one HBM fetch per head and step).
-template <int D>
-__global__ __launch_bounds__(256) void k_chain_split(Problem p, Split sp, WsLayout L, char* wsb) {
+// S_start(g) M_end(g), g = 1 .. G - 2, from S_start(1) = S^D_end(0)
+// (sequence-parallel notes: the state at a segment end is the increment plus
+// the entry state through the scaling matrix).  Each map X -> X M + A is
+// affine, and affine maps compose associatively (GDN blog, section 2.3), so
+// for many segments the chain runs as a two-level scan over blocks of b
+// consecutive maps:
+//   compose  (blocks in parallel)  P_j = M(a) ... M(e - 1), Q_j the matching
+//            addend, so that S_start(e) = S_start(a) P_j + Q_j;
+//   blocks   (sequential over j)   S_start(a_{j+1}) = S_start(a_j) P_j + Q_j;
+//   expand   (blocks in parallel)  the starts inside each block, one map at a
+//            time from the block's start.
+// That is about 3 sqrt(G) dependent steps instead of G - 2; below
+// kChainBlockMin maps the plain sequential chain runs.
+// Every mode is the same row chain: X <- X Mult(s) + Add(s) for s < nsteps on
+// 16 rows of one head per workgroup (rows of the start state are independent
+// chains), each step a 16 x D x D product on bf16 MFMA with both factors split
+// hi/lo (three products, fp32 accumulate).  Mult(s + 1) and the rows of
+// Add(s + 1) are fetched while step s computes.  Workgroups are dealt to the
+// eight XCDs round-robin; when the count of groups that share their Mult
+// matrices is a multiple of eight, each group is placed on one XCD, so that it
+// shares the L2 copy (one HBM fetch per group and step).
+constexpr int kChainBlockMin = 16;
+enum { kChainSeq = 0, kChainCompose = 1, kChainBlocks = 2, kChainExpand = 3 };
+struct ChainPlan {
+    int b;   // maps per block (0: sequential chain)
+    int nb;  // blocks
+};
+// b about sqrt(n), but no more blocks than keep one workgroup per (head,
+// block, 16 rows) within the 256 CUs (the compose and expand grids run in one
+// round); the plain chain when the scan would not take fewer steps
+ChainPlan chain_plan(int G, int64_t heads, int D) {
+    const int n = G - 2;  // maps M_end(1 .. G - 2)
+    ChainPlan c{0, 0};
+    if (n < kChainBlockMin) return c;
+    int b = 1;
+    while (b * b < n) ++b;
+    const int64_t nb_cap = 256 / ((D / 16) * heads);
+    if (nb_cap >= 2 && (n + b - 1) / b > nb_cap) b = (int)((n + nb_cap - 1) / nb_cap);
+    const int nb = (n + b - 1) / b;
+    if (2 * (b - 1) + nb >= n) return c;
+    c.b = b;
+    c.nb = nb;
+    return c;
+}
+
+// NR = 2 (compose): the P and the Q rows of a block in one workgroup, sharing
+// the staged Mult(s) and its hi/lo split; NR = 1 otherwise.
+template <int D, int NR>
+__global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayout L, char* wsb, int mode,
+                                                    ChainPlan cp) {
     constexpr int LD = D + 4;
-    constexpr int MP = D * D / 4 / 256;  // float4 pieces of M per thread
+    constexpr int MP = D * D / 4 / 256;  // float4 pieces of a D x D matrix per thread
     constexpr int SP = 16 * D / 4;       // float4 pieces of 16 rows
+    constexpr int SR = (SP + 255) / 256;
     constexpr int NTW = D / 64;          // column tiles per wave
     constexpr int NX = D / 16;           // row blocks per head
+    constexpr int64_t DD = (int64_t)D * D;
     __shared__ __attribute__((aligned(16))) float Ms[D * LD];
-    __shared__ __attribute__((aligned(16))) float Cb[2][16 * LD];
+    __shared__ __attribute__((aligned(16))) float Cb[2][NR][16 * LD];
     __shared__ __attribute__((aligned(16))) float SDs[16 * LD];
     const int64_t heads = p.B * p.H;
-    int64_t bh;
+    const bool per_block = mode == kChainCompose || mode == kChainExpand;
+    const int64_t groups = heads * (per_block ? cp.nb : 1);  // workgroups of a group share Mult
+    int64_t grp;
     int x;
-    if (heads % 8 == 0) {
+    if (groups % 8 == 0) {
         const int64_t slot = blockIdx.x / 8;
-        bh = (slot / NX) * 8 + blockIdx.x % 8;
+        grp = (slot / NX) * 8 + blockIdx.x % 8;
         x = (int)(slot % NX);
     } else {
-        bh = blockIdx.x / NX;
-        x = blockIdx.x % NX;
+        grp = blockIdx.x / NX;
+        x = (int)(blockIdx.x % NX);
     }
+    const int64_t bh = per_block ? grp / cp.nb : grp;
+    const int j = per_block ? (int)(grp % cp.nb) : 0;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int r0 = 16 * x;
-    const float* sdend = reinterpret_cast<const float*>(wsb + L.sdend);
-    const float* mend = reinterpret_cast<const float*>(wsb + L.mend);
-    float* sstart = reinterpret_cast<float*>(wsb + L.sstart);
-    const int last = sp.G - 1;  // steps g = 1 .. last - 1 (none when G == 2)
+    const float* sdend = reinterpret_cast<const float*>(wsb + L.sdend) + bh * sp.G * DD;
+    const float* mend = reinterpret_cast<const float*>(wsb + L.mend) + bh * sp.G * DD;
+    float* sstart = reinterpret_cast<float*>(wsb + L.sstart) + bh * sp.G * DD;
+    float* pblk = reinterpret_cast<float*>(wsb + L.blk) + bh * cp.nb * DD;
+    float* qblk = reinterpret_cast<float*>(wsb + L.blk) + (heads + bh) * cp.nb * DD;
 
-    f32x4 mreg[MP], sreg[(SP + 255) / 256];
-    auto fetch = [&](int g) {
-        g = min(g, last - 1);
-        const f32x4* M = reinterpret_cast<const f32x4*>(mend + (bh * sp.G + g) * D * D);
+    // the job: start rows of each set, step operands Mult(s) = mult0 + s DD and
+    // Add(s) = add0 + s DD (last set only), X written before step s (pre),
+    // after it (post), at the end (fin, per set)
+    const int a = 1 + j * cp.b;                               // first map of block j
+    const int len = per_block ? min(cp.b, sp.G - 1 - a) : 0;  // its maps a .. a + len - 1
+    const float* init[NR];
+    float* fin[NR];
+    const float* mult0;
+    const float* add0 = nullptr;
+    float* pre0 = nullptr;
+    float* post0 = nullptr;
+    int64_t pre_stride = DD;
+    int nsteps;
+    fin[NR - 1] = nullptr;
+    if (mode == kChainSeq) {
+        init[0] = sdend;
+        nsteps = sp.G - 2;
+        mult0 = mend + DD;
+        add0 = sdend + DD;
+        pre0 = sstart + DD;
+        fin[0] = sstart + (sp.G - 1) * DD;
+    } else if (mode == kChainCompose) {
+        // set 0: P_j (from M(a), no addend); set NR - 1: Q_j (from S^D(a))
+        init[0] = mend + a * DD;
+        init[NR - 1] = sdend + a * DD;
+        nsteps = len - 1;
+        mult0 = mend + (a + 1) * DD;
+        add0 = sdend + (a + 1) * DD;
+        fin[0] = pblk + j * DD;
+        fin[NR - 1] = qblk + j * DD;
+    } else if (mode == kChainBlocks) {
+        init[0] = sdend;
+        nsteps = cp.nb;
+        mult0 = pblk;
+        add0 = qblk;
+        pre0 = sstart + DD;
+        pre_stride = cp.b * DD;
+        fin[0] = sstart + (sp.G - 1) * DD;
+    } else {
+        init[0] = sstart + a * DD;
+        nsteps = len - 1;
+        mult0 = mend + a * DD;
+        add0 = sdend + a * DD;
+        post0 = sstart + (a + 1) * DD;
+    }
+
+    f32x4 mreg[MP], sreg[SR];
+    auto fetch = [&](int s) {
+        const f32x4* M = reinterpret_cast<const f32x4*>(mult0 + s * DD);
 #pragma unroll
         for (int k = 0; k < MP; ++k) mreg[k] = M[tid + 256 * k];
-        const f32x4* S = reinterpret_cast<const f32x4*>(sdend + (bh * sp.G + g) * D * D + (int64_t)r0 * D);
+        const f32x4* S = reinterpret_cast<const f32x4*>(add0 + s * DD + (int64_t)r0 * D);
 #pragma unroll
-        for (int k = 0; k < (SP + 255) / 256; ++k) sreg[k] = S[min(tid + 256 * k, SP - 1)];
+        for (int k = 0; k < SR; ++k) sreg[k] = S[min(tid + 256 * k, SP - 1)];
     };
-    // S_start(1) = S^D_end(0), the true end state of segment 0
-    {
-        const f32x4* S = reinterpret_cast<const f32x4*>(sdend + (bh * sp.G + 0) * D * D + (int64_t)r0 * D);
+    auto write_rows = [&](float* dst, const float* X) {
+        float* SS = dst + (int64_t)r0 * D;
         for (int e = tid; e < SP; e += 256) {
             const int r = e / (D / 4), c4 = e % (D / 4);
-            *reinterpret_cast<f32x4*>(&Cb[0][r * LD + 4 * c4]) = S[e];
+            *reinterpret_cast<f32x4*>(&SS[r * D + 4 * c4]) = *reinterpret_cast<const f32x4*>(&X[r * LD + 4 * c4]);
+        }
+    };
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const f32x4* S = reinterpret_cast<const f32x4*>(init[r] + (int64_t)r0 * D);
+        for (int e = tid; e < SP; e += 256) {
+            const int rr = e / (D / 4), c4 = e % (D / 4);
+            *reinterpret_cast<f32x4*>(&Cb[0][r][rr * LD + 4 * c4]) = S[e];
         }
     }
-    if (last > 1) fetch(1);
+    if (nsteps > 0) fetch(0);
     int cur = 0;
-    for (int g = 1;; ++g) {
-        if (g < last) {
+    for (int s = 0;; ++s) {
+        if (s < nsteps) {
 #pragma unroll
             for (int k = 0; k < MP; ++k) {
                 const int e = tid + 256 * k, c = e / (D / 4), a4 = e % (D / 4);
                 *reinterpret_cast<f32x4*>(&Ms[c * LD + 4 * a4]) = mreg[k];
             }
 #pragma unroll
-            for (int k = 0; k < (SP + 255) / 256; ++k) {
+            for (int k = 0; k < SR; ++k) {
                 const int e = tid + 256 * k;
                 if (SP % 256 == 0 || e < SP)
                     *reinterpret_cast<f32x4*>(&SDs[(e / (D / 4)) * LD + 4 * (e % (D / 4))]) = sreg[k];
             }
         }
-        __syncthreads();  // S_start(g) complete in Cb[cur]; M(g), S^D(g) staged
-        if (g + 1 < last) fetch(g + 1);
-        {
-            float* SS = sstart + (bh * sp.G + g) * D * D + (int64_t)r0 * D;
-            for (int e = tid; e < SP; e += 256) {
-                const int r = e / (D / 4), c4 = e % (D / 4);
-                *reinterpret_cast<f32x4*>(&SS[r * D + 4 * c4]) = *reinterpret_cast<const f32x4*>(&Cb[cur][r * LD + 4 * c4]);
-            }
-        }
-        if (g == last) break;
-        // Cb[cur ^ 1] = S^D(g) + Cb[cur] M(g): wave w takes column tiles w, w + 4
-        const float* A = Cb[cur];
-        u16x8 ah[D / 32], al[D / 32];
+        __syncthreads();  // X complete in Cb[cur]; Mult(s), Add(s) staged
+        if (s + 1 < nsteps) fetch(s + 1);
+        if (s < nsteps) {
+            if (pre0) write_rows(pre0 + s * pre_stride, Cb[cur][0]);
+        } else {
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * s + 8 * g4]);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * s + 8 * g4 + 4]);
-            u16x4 h0, l0, h1, l1;
-            split4(x0, h0, l0);
-            split4(x1, h1, l1);
-            ah[s] = cat(h0, h1);
-            al[s] = cat(l0, l1);
+            for (int r = 0; r < NR; ++r)
+                if (fin[r]) write_rows(fin[r], Cb[cur][r]);
         }
+        if (s > 0 && post0) write_rows(post0 + (s - 1) * DD, Cb[cur][0]);
+        if (s == nsteps) break;
+        // Cb[cur ^ 1][r] = Cb[cur][r] Mult(s) (+ Add(s) for the last set):
+        // wave w takes column tiles w, w + 4
+        u16x8 ah[NR][D / 32], al[NR][D / 32];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int q = 0; q < D / 32; ++q) {
+                const float* A = Cb[cur][r];
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * q + 8 * g4]);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * q + 8 * g4 + 4]);
+                u16x4 h0, l0, h1, l1;
+                split4(x0, h0, l0);
+                split4(x1, h1, l1);
+                ah[r][q] = cat(h0, h1);
+                al[r][q] = cat(l0, l1);
+            }
 #pragma unroll
         for (int q = 0; q < NTW; ++q) {
             const int nt = w + 4 * q;
-            f32x4 a1, a2 = zero4(), a3 = zero4();
+            f32x4 a1[NR], a2[NR], a3[NR];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a1[i] = SDs[(4 * g4 + i) * LD + 16 * nt + c16];
+            for (int r = 0; r < NR; ++r) a1[r] = a2[r] = a3[r] = zero4();
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
+            for (int i = 0; i < 4; ++i) a1[NR - 1][i] = SDs[(4 * g4 + i) * LD + 16 * nt + c16];
+            if (NR == 1 && !add0) a1[0] = zero4();
+#pragma unroll
+            for (int k = 0; k < D / 32; ++k) {
                 f32x4 y0, y1;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    y0[e] = Ms[(32 * s + 8 * g4 + e) * LD + 16 * nt + c16];
-                    y1[e] = Ms[(32 * s + 8 * g4 + 4 + e) * LD + 16 * nt + c16];
+                    y0[e] = Ms[(32 * k + 8 * g4 + e) * LD + 16 * nt + c16];
+                    y1[e] = Ms[(32 * k + 8 * g4 + 4 + e) * LD + 16 * nt + c16];
                 }
                 u16x4 h0, l0, h1, l1;
                 split4(y0, h0, l0);
                 split4(y1, h1, l1);
                 const u16x8 bh_ = cat(h0, h1), bl_ = cat(l0, l1);
-                a1 = mfma(ah[s], bh_, a1);
-                a2 = mfma(ah[s], bl_, a2);
-                a3 = mfma(al[s], bh_, a3);
-            }
-            const f32x4 sum = a1 + a2 + a3;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Cb[cur ^ 1][(4 * g4 + i) * LD + 16 * nt + c16] = sum[i];
+                for (int r = 0; r < NR; ++r) {
+                    a1[r] = mfma(ah[r][k], bh_, a1[r]);
+                    a2[r] = mfma(ah[r][k], bl_, a2[r]);
+                    a3[r] = mfma(al[r][k], bh_, a3[r]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const f32x4 sum = a1[r] + a2[r] + a3[r];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Cb[cur ^ 1][r][(4 * g4 + i) * LD + 16 * nt + c16] = sum[i];
+            }
         }
-        __syncthreads();  // M(g), S^D(g) and S_start(g) consumed
+        __syncthreads();  // Mult(s), Add(s) and X consumed
         cur ^= 1;
     }
 }
@@ -1842,8 +1953,20 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
         prof_end(st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        const ChainPlan cp = chain_plan(sp.G, heads, D);
+        const unsigned nx = D / 16;
         prof_begin("k_chain", st);
-        hipLaunchKernelGGL((k_chain_split<D>), dim3((unsigned)(heads * (D / 16))), dim3(256), 0, st, p, sp, L, ws);
+        if (cp.nb == 0) {
+            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * nx)), dim3(256), 0, st, p, sp, L, ws,
+                               (int)kChainSeq, cp);
+        } else {
+            hipLaunchKernelGGL((k_chain_rows<D, 2>), dim3((unsigned)(heads * cp.nb * nx)), dim3(256), 0, st, p, sp,
+                               L, ws, (int)kChainCompose, cp);
+            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * nx)), dim3(256), 0, st, p, sp, L, ws,
+                               (int)kChainBlocks, cp);
+            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * cp.nb * nx)), dim3(256), 0, st, p, sp, L,
+                               ws, (int)kChainExpand, cp);
+        }
         prof_end(st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1897,6 +2020,11 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
         L.sfrag = off;
         L.sfrag_bytes = whole ? 0 : align256(2 * sizeof(uint16_t) * p.B * p.H * sp.G * p.dv * p.dk);
         off += L.sfrag_bytes;
+        // the blocked start-state chain keeps a composed map pair per block
+        const ChainPlan cp = whole ? chain_plan(sp.G, p.B * p.H, (int)p.dk) : ChainPlan{0, 0};
+        L.blk = off;
+        L.blk_bytes = align256(2 * sizeof(float) * p.B * p.H * cp.nb * p.dk * p.dk);
+        off += L.blk_bytes;
     }
     L.total = off;
     return L;

@@ -253,6 +253,10 @@ WHOLE = [
     (1, 32, 512, 128, 4, PTD, 0.0, 6.0),     # long memory, zero start state
     (1, 32, 512, 128, 4, DTP, 0.5, -6.0),    # fast forgetting
     (1, 20, 2048, 128, 8, PTD, 0.5, 2.0),    # head count not a multiple of 8
+    # 16 maps and more: the start-state chain as a two-level scan over blocks
+    (1, 16, 4608, 64, 18, PTD, 0.3, 6.0),    # 4 blocks of 4 maps, long memory
+    (1, 8, 5120, 128, 20, PTD, 0.5, 6.0),    # blocks of 5, 5, 5, 3 maps
+    (1, 4, 10240, 128, 40, DTP, 0.5, 6.0),   # blocks of 7 (x5) and 3, 4 heads
 ]
 
 
@@ -278,6 +282,20 @@ def test_full_workload_sampled(idx):
     inp = make_inputs(w)
     o, s = run(w, inp)
     check(w, inp, o, s, bh=SAMPLES[idx])
+
+
+def test_long_workload_library_schedule_sampled():
+    """The long workload through gdn_chunk_fwd: the library cuts its four
+    sequences into 64 segments (whole-head path, blocked start-state chain)."""
+    import torch
+    w = WORKLOADS[3]
+    assert gdn.gdn_chunk_segments(w.B, w.T, w.H, w.dk, w.dv, w.chunk, gdn.GDN_BF16,
+                                  gdn.GDN_GATE_SCALAR) == 64
+    inp = make_inputs(w)
+    d = to_device(inp, w)
+    o, s = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], chunk=w.chunk)
+    torch.cuda.synchronize()
+    check(w, inp, _np(o), _np(s), bh=[(0, 0), (0, 3)])
 
 
 def test_long_workload_single_stream_sampled():
