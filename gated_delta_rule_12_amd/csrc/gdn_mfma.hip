@@ -201,8 +201,10 @@ __device__ __forceinline__ void ut_inverse_store(float* AT, float* Pw, const flo
             const float v1 = up ? 0.f : AT[t * LDA + j0 + 1] * bsh[j0 + 1];
             split2(v0, v1, hi[e >> 1], lo[e >> 1]);
         }
-        dst[(slot * 2 + 0) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
-        dst[(slot * 2 + 1) * 64 + lane] = __builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
+        // (non-temporal: written once here, read by the chunk loops later;
+        // measured 5 % off stage 1 and nothing on the readers)
+        __builtin_nontemporal_store(__builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]}), &dst[(slot * 2 + 0) * 64 + lane]);
+        __builtin_nontemporal_store(__builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]}), &dst[(slot * 2 + 1) * 64 + lane]);
     }
 }
 
