@@ -257,6 +257,8 @@ WHOLE = [
     (1, 16, 4608, 64, 18, PTD, 0.3, 6.0),    # 4 blocks of 4 maps, long memory
     (1, 8, 5120, 128, 20, PTD, 0.5, 6.0),    # blocks of 5, 5, 5, 3 maps
     (1, 4, 10240, 128, 40, DTP, 0.5, 6.0),   # blocks of 7 (x5) and 3, 4 heads
+    # one chunk per segment: a scan over the per-chunk affine maps, ragged tail
+    (1, 4, 4128, 128, 65, PTD, 0.5, 6.0),
 ]
 
 
