@@ -1293,8 +1293,6 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 
     for (int i = i_begin; i < i_end; ++i) {
         __syncthreads();  // chunk i staged
-        // the previous chunk's output and the next chunk's loads go out here,
-        // overlapping this chunk's products
         // the output pass fetches the next chunk's K and V here, its Q, T'
         // and gates after the first product and writes the previous chunk's
         // output tile after the second, so that the loads and stores of one
@@ -1306,8 +1304,12 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         if constexpr (OUT) scores();
         // K^T fragments by exact MFMA products with the identity: job (s', u)
         // turns token tiles 2s', 2s' + 1 of key tile u into the A fragment of
-        // rows a = 16u + c16, k-step s' over tokens
-        for (int job = w; job < 2 * TPW; job += NW) {
+        // rows a = 16u + c16, k-step s' over tokens; every wave takes the same
+        // number of jobs
+        static_assert((2 * TPW) % NW == 0, "K^T jobs split evenly over the waves");
+#pragma unroll
+        for (int jj = 0; jj < 2 * TPW / NW; ++jj) {
+            const int job = w + NW * jj;
             const int sp_ = job & 1, u = job >> 1;
             u16x4 half[2];
 #pragma unroll
