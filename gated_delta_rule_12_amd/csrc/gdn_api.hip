@@ -84,6 +84,16 @@ void prof_drain() {
 
 int finish(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
+// The kernels move q, k, v, a per-channel gate, the states and the output in
+// 16-byte pieces; beta and a scalar gate per float.
+bool aligned(const void* ptr, uintptr_t a) { return (uintptr_t)ptr % a == 0; }
+bool forward_aligned(const void* q, const void* k, const void* v, const float* alpha, int gate,
+                     const float* beta, const float* state0, const float* out, const float* state_out) {
+    return aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(state0, 16) &&
+           aligned(out, 16) && aligned(state_out, 16) && aligned(beta, 4) &&
+           aligned(alpha, gate == GDN_GATE_CHANNEL ? 16 : 4);
+}
+
 int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
                 int32_t dtype, int32_t gate, int32_t order, float scale, int32_t n_segments,
                 const void* q, const void* k, const void* v, const float* alpha,
@@ -96,6 +106,7 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
     if (B * H == 0) return GDN_OK;
     if (n_segments == 0) n_segments = auto_segments(p);
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_E_ARG;
+    if (!forward_aligned(q, k, v, alpha, gate, beta, state0, out, state_out)) return GDN_E_ARG;
     p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
     p.s0 = state0; p.out = out; p.s_out = state_out;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -206,6 +217,7 @@ int gdn_seqpar_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int3
                    const void* q, const void* k, const void* v, const float* alpha,
                    const float* beta, const float* state0, float* out, float* state_out,
                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (n_segments < 1) return GDN_E_SHAPE;  // (0 would select the library's schedule)
     return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, n_segments, q, k, v,
                        alpha, beta, state0, out, state_out, workspace, workspace_bytes, stream);
 }
@@ -218,6 +230,7 @@ int gdn_recurrent_ref(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, i
     if (s != GDN_OK) return s;
     if (B * H == 0) return GDN_OK;
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_E_ARG;
+    if (!forward_aligned(q, k, v, alpha, gate, beta, state0, out, state_out)) return GDN_E_ARG;
     Problem p = make_problem(B, T, H, dk, dv, 16, dtype, gate, order, scale);
     p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
     p.s0 = state0; p.out = out; p.s_out = state_out;

@@ -34,6 +34,10 @@
  * the workspace must not alias any input.  Two calls that share a workspace
  * must be ordered on one stream.
  *
+ * Alignment: q, k, v, state0, out, state_out and a per-channel alpha must be
+ * 16-byte aligned, beta and a scalar alpha 4-byte aligned (fresh device
+ * allocations are); otherwise the call returns GDN_E_ARG.
+ *
  * Errors: every argument check runs on the host before anything is enqueued;
  * a failing check returns a negative status and enqueues nothing.  A HIP
  * launch error returns GDN_E_HIP.  NaN/Inf inputs are not checked; they
@@ -141,7 +145,8 @@ int gdn_decode_step(int64_t B, int64_t H, int64_t dk, int64_t dv,
  * which is M_[i](I - W^T K) with unit gates).  Start states are chained
  * S_start(g+1) = S^D_end(g) + S_start(g) M_end(g), and the correction
  * S_[i] = S^D_[i] + S_start M_[i] is applied to the outputs, which are
- * linear in the entry state.  n_segments = 1 is a single stream.  Segments
+ * linear in the entry state.  n_segments = 1 is a single stream; below 1
+ * the call returns GDN_E_SHAPE.  Segments
  * hold ceil(NC / n_segments) chunks (NC = ceil(T / chunk)); the last may be
  * shorter.  Same tensors as gdn_chunk_fwd; a larger workspace.
  */

@@ -180,3 +180,37 @@ def test_decode_step_rejects_bad_arguments_before_any_launch():
     # empty batch: nothing to do
     rc = gdn.gdn_decode_step(0, 4, 128, 128, *tail, *([nul] * 8), nul)
     assert rc == gdn.GDN_OK
+
+
+def test_forward_entry_points_check_alignment_and_segment_count():
+    """16-byte pieces: misaligned tensors are refused before any launch; a
+    segment count below one is a shape error (fake, never dereferenced
+    pointers)."""
+    import ctypes
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    odd16 = ctypes.c_void_p(0x1008)   # 8-byte, not 16-byte aligned
+    odd4 = ctypes.c_void_p(0x1002)    # not 4-byte aligned
+    shape = (1, 64, 1, 64, 64, 64, gdn.GDN_BF16, gdn.GDN_GATE_SCALAR, gdn.GDN_PREDICT_THEN_DECAY, 1.0)
+    ok = [fake] * 8
+    # an aligned call gets as far as the workspace check
+    assert gdn.gdn_chunk_fwd(*shape, *ok, fake, 16, nul) == gdn.GDN_E_WORKSPACE
+    for idx in (0, 1, 2, 5, 6, 7):            # q, k, v, state0, out, state_out
+        ptrs = list(ok)
+        ptrs[idx] = odd16
+        assert gdn.gdn_chunk_fwd(*shape, *ptrs, fake, 16, nul) == gdn.GDN_E_ARG, idx
+        assert gdn.gdn_seqpar_fwd(*shape, 2, *ptrs, fake, 16, nul) == gdn.GDN_E_ARG, idx
+        assert gdn.gdn_recurrent_ref(1, 64, 1, 64, 64, *shape[6:], *ptrs, nul) == gdn.GDN_E_ARG, idx
+    # beta and a scalar gate per float; a channel gate in 16-byte pieces
+    for idx in (3, 4):
+        ptrs = list(ok)
+        ptrs[idx] = odd4
+        assert gdn.gdn_chunk_fwd(*shape, *ptrs, fake, 16, nul) == gdn.GDN_E_ARG, idx
+    ptrs = list(ok)
+    ptrs[3] = odd16
+    assert gdn.gdn_chunk_fwd(*shape, *ptrs, fake, 16, nul) == gdn.GDN_E_WORKSPACE
+    chan = shape[:7] + (gdn.GDN_GATE_CHANNEL,) + shape[8:]
+    assert gdn.gdn_chunk_fwd(*chan, *ptrs, fake, 16, nul) == gdn.GDN_E_ARG
+    # segment counts below one
+    for n in (0, -3):
+        assert gdn.gdn_seqpar_fwd(*shape, n, *ok, fake, 1 << 30, nul) == gdn.GDN_E_SHAPE
