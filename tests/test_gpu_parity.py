@@ -274,6 +274,21 @@ def test_whole_head_path(case):
     check(w, inp, o, s, order, bh=[(0, 0), (B - 1, H // 2 + 1), (B - 1, H - 1)])
 
 
+@pytest.mark.parametrize("B,H,T,d,order", [
+    (16, 16, 700, 128, PTD),   # 256 heads: one segment, ragged last chunk
+    (8, 20, 256, 64, DTP),     # 160 heads, four chunks: too short to split
+])
+def test_whole_head_single_pass(B, H, T, d, order):
+    """Enough heads to fill the device: gdn_chunk_fwd runs stage 1 and one
+    pass of the whole-head chunk loop (no state pass, no chain)."""
+    assert gdn.gdn_chunk_segments(B, T, H, d, d, 64, gdn.GDN_BF16, gdn.GDN_GATE_SCALAR) == 1
+    assert gdn.gdn_chunk_path(d, d, 64, gdn.GDN_BF16, gdn.GDN_GATE_SCALAR) == gdn.GDN_PATH_MFMA
+    w = Workload("single-pass", B=B, H=H, T=T, dk=d, dv=d, chunk=64, state0_std=0.3, seed=T + H + d)
+    inp = make_inputs(w)
+    o, s = run(w, inp, order=order)
+    check(w, inp, o, s, order, bh=[(0, 0), (B // 2, H // 3), (B - 1, H - 1)])
+
+
 SAMPLES = {1: [(0, 0), (3, 7)], 2: [(0, 0), (1, 15), (0, 9)], 3: [(0, 0), (0, 3)],
            4: [(0, 0), (7, 15)]}
 
