@@ -204,6 +204,16 @@ def bench_decode(args, w):
     kern = gdn.gdn_profile_read()
     gdn.gdn_profile_enable(False)
     k_us = 1e3 * kern["k_decode"][0] / kern["k_decode"][1]
+    # the fused-prologue entry point on the same tensors (read as raw
+    # projections and logits): same traffic, a few more operations per head
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        gdn.decode_step(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], st,
+                        out=out, inplace=True, raw=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    raw_ms = e0.elapsed_time(e1) / args.steps
     abytes = decode_bytes(w)
     achieved = abytes / (k_us * 1e-6) / 1e9
     log(f"step {ms * 1e3:.1f} us, k_decode {k_us:.1f} us per launch")
@@ -222,7 +232,7 @@ def bench_decode(args, w):
                         "kernel_timing": "HIP events around each launch, in a second run of the same steps after the timed region",
                         "kernel_avg_launch_us": round(k_us, 2), "algorithmic_bytes": abytes,
                         "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1)},
-           "cpu_baseline": cpu}
+           "cpu_baseline": cpu, "raw_prologue_ms_per_step": round(raw_ms, 5)}
     print(json.dumps(res), flush=True)
 
 

@@ -119,6 +119,26 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
     return finish(valu_forward(p, sp, ws, st));
 }
 
+int decode_common(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,
+                  int32_t order, float scale, const void* q, const void* k, const void* v,
+                  const float* alpha, const float* beta, const float* state_in, float* out,
+                  float* state_out, bool prologue, void* stream) {
+    int s = validate(B, 1, H, dk, dv, 16, dtype, gate, order, 1);
+    if (s != GDN_OK) return s;
+    if (B * H == 0) return GDN_OK;
+    if (!q || !k || !v || !alpha || !beta || !out || !state_out) return GDN_E_ARG;
+    // the kernel moves q, k (and a vector gate) and the state rows in 16-byte
+    // (fp32) or 8-byte (bf16) pieces
+    const uintptr_t qk_align = dtype == GDN_BF16 ? 8 : 16;
+    if (((uintptr_t)q | (uintptr_t)k) % qk_align != 0) return GDN_E_ARG;
+    if (((uintptr_t)state_in | (uintptr_t)state_out) % 16 != 0) return GDN_E_ARG;
+    if (gate == GDN_GATE_CHANNEL && (uintptr_t)alpha % 16 != 0) return GDN_E_ARG;
+    Problem p = make_problem(B, 1, H, dk, dv, 16, dtype, gate, order, scale);
+    p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+    p.s0 = state_in; p.out = out; p.s_out = state_out;
+    return finish(decode_step(p, prologue, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 void prof_begin(const char* name, hipStream_t st) {
@@ -243,20 +263,16 @@ int gdn_decode_step(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dtype,
                     int32_t order, float scale, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, const float* state_in,
                     float* out, float* state_out, void* stream) {
-    int s = validate(B, 1, H, dk, dv, 16, dtype, gate, order, 1);
-    if (s != GDN_OK) return s;
-    if (B * H == 0) return GDN_OK;
-    if (!q || !k || !v || !alpha || !beta || !out || !state_out) return GDN_E_ARG;
-    // the kernel moves q, k (and a vector gate) and the state rows in 16-byte
-    // (fp32) or 8-byte (bf16) pieces
-    const uintptr_t qk_align = dtype == GDN_BF16 ? 8 : 16;
-    if (((uintptr_t)q | (uintptr_t)k) % qk_align != 0) return GDN_E_ARG;
-    if (((uintptr_t)state_in | (uintptr_t)state_out) % 16 != 0) return GDN_E_ARG;
-    if (gate == GDN_GATE_CHANNEL && (uintptr_t)alpha % 16 != 0) return GDN_E_ARG;
-    Problem p = make_problem(B, 1, H, dk, dv, 16, dtype, gate, order, scale);
-    p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
-    p.s0 = state_in; p.out = out; p.s_out = state_out;
-    return finish(decode_step(p, static_cast<hipStream_t>(stream)));
+    return decode_common(B, H, dk, dv, dtype, gate, order, scale, q, k, v, alpha, beta,
+                         state_in, out, state_out, false, stream);
+}
+
+int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,
+                        int32_t order, float scale, const void* q, const void* k, const void* v,
+                        const float* alpha_logit, const float* beta_logit, const float* state_in,
+                        float* out, float* state_out, void* stream) {
+    return decode_common(B, H, dk, dv, dtype, gate, order, scale, q, k, v, alpha_logit,
+                         beta_logit, state_in, out, state_out, true, stream);
 }
 
 int gdn_profile_enable(int on) {

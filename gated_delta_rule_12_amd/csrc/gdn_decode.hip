@@ -21,6 +21,14 @@
 // state is read and written with non-temporal hints: each byte is touched
 // once per step, and keeping it out of the caches took a quarter less time
 // than cached accesses.
+//
+// With the prologue (gdn_decode_step_raw) the kernel also forms the step's
+// inputs from the model's raw projections, as the DeltaNet block does before
+// the recurrence (DeltaNet illustrated notes, block description: per-head L2
+// normalisation of q and k; the gates through a sigmoid): q <- q / |q|,
+// k <- k / |k| (a zero vector stays zero), alpha <- sigmoid(alpha),
+// beta <- sigmoid(beta), all in fp32.  The row's lanes hold the head's q and
+// k in float4 pieces, so each norm is one more reduction over them.
 #include "gdn_internal.h"
 #include "../../include/gdn.h"
 
@@ -56,7 +64,16 @@ __device__ __forceinline__ float row_sum(float x) {
 
 // grid (row blocks, H, B); block: 4 waves, wave w covers rows
 // rb RB + (j 4 + w) RPW + l / LPR for j < kRows
-template <int DT, int LPR>
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+template <int LPR>
+__device__ __forceinline__ float4 l2_normalised(const float4& x) {
+    const float n2 = row_sum<LPR>(dot4(x, x));
+    const float r = n2 > 0.f ? 1.f / __fsqrt_rn(n2) : 0.f;
+    return make_float4(x.x * r, x.y * r, x.z * r, x.w * r);
+}
+
+template <int DT, int LPR, bool PRO>
 __global__ __launch_bounds__(kThreads) void k_decode(Problem p) {
     constexpr int RPW = 64 / LPR;            // rows per wave and pass
     constexpr int RB = 4 * RPW * kRows;      // rows per block
@@ -70,16 +87,23 @@ __global__ __launch_bounds__(kThreads) void k_decode(Problem p) {
     const bool dtp = p.order == GDN_DECAY_THEN_PREDICT;
 
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 k4 = col ? ld4<DT>(p.k, bh * dk + 4 * c) : z4;
-    const float4 q4 = col ? ld4<DT>(p.q, bh * dk + 4 * c) : z4;
+    float4 k4 = col ? ld4<DT>(p.k, bh * dk + 4 * c) : z4;
+    float4 q4 = col ? ld4<DT>(p.q, bh * dk + 4 * c) : z4;
     float4 d4;
     if (channel) {
         d4 = col ? *reinterpret_cast<const float4*>(p.alpha + bh * dk + 4 * c) : z4;
+        if (PRO && col) d4 = make_float4(sigmoid(d4.x), sigmoid(d4.y), sigmoid(d4.z), sigmoid(d4.w));
     } else {
-        const float a = p.alpha[bh];
+        float a = p.alpha[bh];
+        if (PRO) a = sigmoid(a);
         d4 = make_float4(a, a, a, a);
     }
-    const float beta = p.beta[bh];
+    float beta = p.beta[bh];
+    if (PRO) {
+        k4 = l2_normalised<LPR>(k4);
+        q4 = l2_normalised<LPR>(q4);
+        beta = sigmoid(beta);
+    }
 
     int r[kRows];
     bool on[kRows];
@@ -131,28 +155,32 @@ __global__ __launch_bounds__(kThreads) void k_decode(Problem p) {
     }
 }
 
-template <int DT, int LPR>
+template <int DT, int LPR, bool PRO>
 hipError_t launch_lpr(const Problem& p, hipStream_t st) {
     constexpr int RB = 4 * (64 / LPR) * kRows;
     const dim3 grid((unsigned)((p.dv + RB - 1) / RB), (unsigned)p.H, (unsigned)p.B);
-    hipLaunchKernelGGL((k_decode<DT, LPR>), grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((k_decode<DT, LPR, PRO>), grid, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool PRO>
 hipError_t launch_dt(const Problem& p, hipStream_t st) {
     const int64_t pieces = p.dk / 4;  // float4 pieces per row, 4 .. 32
-    if (pieces <= 4) return launch_lpr<DT, 4>(p, st);
-    if (pieces <= 8) return launch_lpr<DT, 8>(p, st);
-    if (pieces <= 16) return launch_lpr<DT, 16>(p, st);
-    return launch_lpr<DT, 32>(p, st);
+    if (pieces <= 4) return launch_lpr<DT, 4, PRO>(p, st);
+    if (pieces <= 8) return launch_lpr<DT, 8, PRO>(p, st);
+    if (pieces <= 16) return launch_lpr<DT, 16, PRO>(p, st);
+    return launch_lpr<DT, 32, PRO>(p, st);
 }
 
 }  // namespace
 
-hipError_t decode_step(const Problem& p, hipStream_t st) {
+hipError_t decode_step(const Problem& p, bool prologue, hipStream_t st) {
     prof_begin("k_decode", st);
-    hipError_t e = p.dtype == GDN_BF16 ? launch_dt<1>(p, st) : launch_dt<0>(p, st);
+    hipError_t e;
+    if (prologue)
+        e = p.dtype == GDN_BF16 ? launch_dt<1, true>(p, st) : launch_dt<0, true>(p, st);
+    else
+        e = p.dtype == GDN_BF16 ? launch_dt<1, false>(p, st) : launch_dt<0, false>(p, st);
     prof_end(st);
     return e;
 }

@@ -67,8 +67,9 @@ hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
 int mfma_auto_segments(const Problem& p);
 
 hipError_t recurrent_forward(const Problem& p, hipStream_t st);
-// One-token step on a persistent state (q, k, v, gates of one token; T = 1).
-hipError_t decode_step(const Problem& p, hipStream_t st);
+// One-token step on a persistent state (q, k, v, gates of one token; T = 1);
+// prologue: q, k L2-normalised and alpha, beta through a sigmoid first.
+hipError_t decode_step(const Problem& p, bool prologue, hipStream_t st);
 
 // Sequence-parallel tail shared by both families: chain of start states and
 // output correction (R_i S_start^T), then the final state.

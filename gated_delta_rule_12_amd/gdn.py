@@ -25,6 +25,7 @@ GDN_PATH_VALU, GDN_PATH_MFMA = 0, 1
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_step",
+           "gdn_decode_step_raw",
            "gdn_workspace_bytes",
            "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_status_str", "gdn_abi_version",
            "gdn_profile_enable", "gdn_profile_read")
@@ -59,6 +60,8 @@ def lib():
     L.gdn_recurrent_ref.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [i64] * 4 + [i32, i32, i32, f32] + tens + [vp]
     L.gdn_decode_step.restype = ctypes.c_int
+    L.gdn_decode_step_raw.argtypes = [i64] * 4 + [i32, i32, i32, f32] + tens + [vp]
+    L.gdn_decode_step_raw.restype = ctypes.c_int
     L.gdn_workspace_bytes.argtypes = shape + [i32, i32, i32, i32]
     L.gdn_workspace_bytes.restype = sz
     L.gdn_validate.argtypes = shape + [i32, i32, i32, i32, i32]
@@ -96,6 +99,10 @@ def gdn_recurrent_ref(*args):
 
 def gdn_decode_step(*args):
     return lib().gdn_decode_step(*args)
+
+
+def gdn_decode_step_raw(*args):
+    return lib().gdn_decode_step_raw(*args)
 
 
 def gdn_workspace_bytes(B, T, H, dk, dv, chunk, dtype, gate, n_segments=1) -> int:
@@ -253,11 +260,14 @@ def recurrent_ref(q, k, v, alpha, beta, state0=None, *, order=GDN_PREDICT_THEN_D
 
 
 def decode_step(q, k, v, alpha, beta, state=None, *, order=GDN_PREDICT_THEN_DECAY,
-                scale=1.0, out=None, state_out=None, inplace=False):
+                scale=1.0, out=None, state_out=None, inplace=False, raw=False):
     """One token on a persistent state: gdn_decode_step.
     q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), alpha [B,H] or [B,H,dk], beta
     [B,H] fp32, state [B,H,dv,dk] fp32 or None (zero).  inplace=True writes the
-    new state over `state`.  Returns (out [B,H,dv] fp32, new state)."""
+    new state over `state`.  raw=True calls gdn_decode_step_raw: q, k are raw
+    projections (L2-normalised in the kernel) and alpha, beta are logits
+    (passed through a sigmoid in the kernel).
+    Returns (out [B,H,dv] fp32, new state)."""
     import torch
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B,H,dk] and v [B,H,dv]")
@@ -290,9 +300,10 @@ def decode_step(q, k, v, alpha, beta, state=None, *, order=GDN_PREDICT_THEN_DECA
         out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
     if state_out is None:
         state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
-    rc = gdn_decode_step(B, H, dk, dv, _dtype_code(q), gate, order, scale,
-                         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
-                         _ptr(out), _ptr(state_out), _stream())
+    fn, name = (gdn_decode_step_raw, "gdn_decode_step_raw") if raw else (gdn_decode_step, "gdn_decode_step")
+    rc = fn(B, H, dk, dv, _dtype_code(q), gate, order, scale,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+            _ptr(out), _ptr(state_out), _stream())
     if rc != GDN_OK:
-        raise GdnError(rc, "gdn_decode_step")
+        raise GdnError(rc, name)
     return out, state_out

@@ -128,6 +128,34 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def make_raw_inputs(w: Workload, seed: int | None = None) -> dict:
+    """Raw projections for the fused-prologue entry point: q, k ~ N(0,1)
+    times a per-(batch, token, head) length drawn from U(0.2, 5), not
+    normalised, with the key of token 0 of head 0 set to zero; v ~ N(0,1);
+    alpha as logits N(mu_a, 0.5) (per token-head or per key channel); beta as
+    logits N(0,1); state0 as in make_inputs.  Same fp32 / bf16 rounding and
+    return layout as make_inputs, with alpha and beta holding logits."""
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    out = {}
+    for name in ("q", "k"):
+        x = rng.standard_normal((B, T, H, dk)) * rng.uniform(0.2, 5.0, (B, T, H, 1))
+        out[name] = x.astype(np.float32)
+    out["k"][0, 0, 0, :] = 0.0
+    out["v"] = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    ashape = (B, T, H) if w.gate == "scalar" else (B, T, H, dk)
+    out["alpha"] = rng.normal(w.alpha_mean, 0.5, ashape).astype(np.float32)
+    out["beta"] = rng.standard_normal((B, T, H)).astype(np.float32)
+    if w.state0_std > 0:
+        out["state0"] = (w.state0_std * rng.standard_normal((B, H, dv, dk))).astype(np.float32)
+    else:
+        out["state0"] = None
+    if w.dtype == "bf16":
+        for name in ("q", "k", "v"):
+            out[name] = _round_bf16(out[name])
+    return out
+
+
 def to_device(inputs: dict, w: Workload, device="cuda"):
     """Upload to torch tensors: q/k/v in the workload dtype, the rest fp32."""
     import torch

@@ -136,6 +136,22 @@ int gdn_decode_step(int64_t B, int64_t H, int64_t dk, int64_t dv,
                     float* out, float* state_out, void* stream);
 
 /*
+ * gdn_decode_step_raw — gdn_decode_step on the model's raw projections: the
+ * kernel first forms the step's inputs the way the DeltaNet block does before
+ * its delta-rule core (DeltaNet illustrated notes, block description): q and
+ * k L2-normalised per (batch, head) along their features (a zero vector stays
+ * zero), beta = sigmoid(beta_logit), and the gate alpha = sigmoid(alpha_logit)
+ * (per head, or per key channel for GDN_GATE_CHANNEL), all in fp32.  Same
+ * tensors, layouts, alignment and statuses as gdn_decode_step; alpha_logit and
+ * beta_logit take the places of alpha and beta.
+ */
+int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
+                        int32_t dtype, int32_t gate, int32_t order, float scale,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha_logit, const float* beta_logit,
+                        const float* state_in, float* out, float* state_out, void* stream);
+
+/*
  * gdn_seqpar_fwd — increment-and-correct sequence parallelism (How to
  * Implement Sequence Parallelism in DeltaNet, papercache notes, sections
  * "parallel algorithm derivation" and "CP=4").  The chunks of every sequence

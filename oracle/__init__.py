@@ -10,6 +10,9 @@ The recurrence, the two gate orderings and the two gate kinds it follows are
 stated, with the passages of the pages they come from, in the header of
 ``gdn_oracle.c``.
 
+``prologue`` forms the core's inputs from raw projections (per-head L2 norm of
+q and k, sigmoid gates), the step before the core in the DeltaNet block.
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against what
 the pages and the mathematics fix (printed worked examples, closed forms,
 affine composition, the WY identity, linearity, exact rational arithmetic on
@@ -112,3 +115,25 @@ def forward(q, k, v, alpha, beta, state0=None, *, gate: int = GATE_SCALAR,
     if rc != 0:
         raise RuntimeError(f"gdn_oracle_forward failed with status {rc}")
     return out, st
+
+
+def prologue(q, k, alpha_logit, beta_logit):
+    """The inputs of the delta-rule core from the model's raw projections, as
+    the DeltaNet block forms them (DeltaNet illustrated notes, block
+    description): q and k divided by their L2 length along the feature axis,
+    separately for every (batch, token, head) (a zero vector stays zero);
+    beta = sigmoid(beta_logit) with sigmoid(z) = 1 / (1 + exp(-z)); the gate
+    alpha through the same sigmoid.  fp64 throughout.
+
+    q, k: [..., d]; alpha_logit, beta_logit: any shape.  Returns
+    (q, k, alpha, beta) as float64 arrays of the same shapes.
+    """
+    def l2(x):
+        x = np.asarray(x, dtype=np.float64)
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+    def sigmoid(z):
+        return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+
+    return l2(q), l2(k), sigmoid(alpha_logit), sigmoid(beta_logit)

@@ -154,8 +154,12 @@ def test_decode_step_rejects_bad_arguments_before_any_launch():
     shape = (2, 4, 128, 128)
     tail = (gdn.GDN_BF16, gdn.GDN_GATE_SCALAR, gdn.GDN_PREDICT_THEN_DECAY, 1.0)
     ok_ptrs = [fake] * 8
-    # state_out is required
+    # state_out is required (both decode entry points)
     rc = gdn.gdn_decode_step(*shape, *tail, *ok_ptrs[:7], nul, nul)
+    assert rc == gdn.GDN_E_ARG
+    rc = gdn.gdn_decode_step_raw(*shape, *tail, *ok_ptrs[:7], nul, nul)
+    assert rc == gdn.GDN_E_ARG
+    rc = gdn.gdn_decode_step_raw(*shape, *tail, ctypes.c_void_p(0x1004), *ok_ptrs[1:], nul)
     assert rc == gdn.GDN_E_ARG
     # the state moves in 16-byte pieces
     rc = gdn.gdn_decode_step(*shape, *tail, *ok_ptrs[:5], ctypes.c_void_p(0x1008), fake, fake, nul)

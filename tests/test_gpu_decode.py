@@ -12,7 +12,9 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_12_amd import gdn
-from gated_delta_rule_12_amd.workloads import DECODE_WORKLOAD, Workload, make_inputs, to_device
+import oracle
+from gated_delta_rule_12_amd.workloads import (DECODE_WORKLOAD, Workload, make_inputs,
+                                              make_raw_inputs, to_device)
 from parity import TOL, oracle_on, out_err, state_err
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +39,7 @@ def token(d, name, t):
     return d[name][:, t].contiguous()
 
 
-def decode_chain(w, d, order, state, t0=0):
+def decode_chain(w, d, order, state, t0=0, raw=False):
     """Decode tokens t0 .. T-1 one at a time, in place on a copy of state.
     Returns (out [B,T-t0,H,dv], state)."""
     import torch
@@ -46,9 +48,9 @@ def decode_chain(w, d, order, state, t0=0):
     for t in range(t0, w.T):
         args = [token(d, n, t) for n in ("q", "k", "v", "alpha", "beta")]
         if st is None:
-            o, st = gdn.decode_step(*args, None, order=order)
+            o, st = gdn.decode_step(*args, None, order=order, raw=raw)
         else:
-            o, _ = gdn.decode_step(*args, st, order=order, inplace=True)
+            o, _ = gdn.decode_step(*args, st, order=order, inplace=True, raw=raw)
         outs.append(o)
     torch.cuda.synchronize()
     return _np(torch.stack(outs, dim=1)), _np(st)
@@ -156,3 +158,22 @@ def test_decode_workload_sampled():
     oo = np.stack([on[b, h][None, None] for b, h in bh])
     ss = np.stack([sn[b, h] for b, h in bh])[:, None]
     check(oo, ss, o_ref, s_ref)
+
+
+@pytest.mark.parametrize("order", [PTD, DTP])
+@pytest.mark.parametrize("dtype,gate,dk,dv", [
+    ("bf16", "scalar", 128, 128), ("f32", "channel", 64, 48),
+    ("bf16", "channel", 48, 80), ("f32", "scalar", 16, 16)])
+def test_decode_raw_prologue(dtype, gate, dk, dv, order):
+    """gdn_decode_step_raw on raw projections and gate logits: the kernel's
+    L2 norm and sigmoids against the oracle's prologue, then the token loop
+    over the same tokens (one key is zero and stays zero)."""
+    w = Workload("decode-raw", B=2, H=3, T=12, dk=dk, dv=dv, chunk=16, dtype=dtype, gate=gate,
+                 state0_std=0.3, seed=4500 + dk + dv)
+    raw = make_raw_inputs(w)
+    d = to_device(raw, w)
+    o, s = decode_chain(w, d, order, d["state0"], raw=True)
+    q, k, a, b = oracle.prologue(raw["q"], raw["k"], raw["alpha"], raw["beta"])
+    g = oracle.GATE_SCALAR if gate == "scalar" else oracle.GATE_CHANNEL
+    o_ref, s_ref = oracle.forward(q, k, raw["v"], a, b, raw["state0"], gate=g, order=order)
+    check(o, s, o_ref, s_ref)

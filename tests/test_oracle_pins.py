@@ -459,3 +459,26 @@ def test_one_token_calls_thread_the_state(gate, order):
                       S0=st, gate=gate, order=order)
         np.testing.assert_array_equal(o1[0], o[t])
     np.testing.assert_array_equal(st, s)
+
+
+def test_prologue_printed_l2_example_and_sigmoid():
+    """The notes' worked L2 example, (3, 4) -> (0.6, 0.8), per (token, head)
+    and never across tokens ((30, 40) beside it has its own length 50); the
+    sigmoid against the library's logistic function and its fixed point."""
+    from scipy.special import expit
+    q = np.array([[[3.0, 4.0]], [[30.0, 40.0]]])      # [T=2, H=1, d=2]
+    k = np.array([[[0.0, 0.0]], [[-6.0, 8.0]]])       # a zero key stays zero
+    logits = np.array([[-3.0, 0.0, 2.5], [40.0, -40.0, 1e-3]])
+    qn, kn, a, b = oracle.prologue(q, k, logits, logits[0])
+    np.testing.assert_allclose(qn[0, 0], [0.6, 0.8], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(qn[1, 0], [0.6, 0.8], rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(kn[0, 0], [0.0, 0.0])
+    np.testing.assert_allclose(kn[1, 0], [-0.6, 0.8], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(a, expit(logits), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(b, expit(logits[0]), rtol=1e-15, atol=0)
+    assert a[0, 1] == 0.5
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 3, 5, 16)) * rng.uniform(0.1, 10, (4, 3, 5, 1))
+    xn = oracle.prologue(x, x, 0.0, 0.0)[0]
+    np.testing.assert_allclose(np.linalg.norm(xn, axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(xn * np.linalg.norm(x, axis=-1, keepdims=True), x, rtol=1e-13)
