@@ -156,6 +156,47 @@ def make_raw_inputs(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def make_inputs_device(w: Workload, device="cuda") -> dict:
+    """Workloads too large to draw on the host: the same recipe as
+    make_inputs, drawn on the device by torch's seeded Philox generator (so
+    the values differ from make_inputs' for the same seed), q and k
+    L2-normalised in fp32 before the cast to the workload dtype.  Returns
+    device tensors laid out as to_device's; checkers read the uploaded values
+    of the slices they need with slice_inputs."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    res = {}
+    for name, d in (("q", dk), ("k", dk)):
+        x = torch.randn((B, T, H, d), generator=g, device=device)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True).clamp_min(1e-30)
+        res[name] = x.to(dt)
+        del x
+    res["v"] = torch.randn((B, T, H, dv), generator=g, device=device).to(dt)
+    ashape = (B, T, H) if w.gate == "scalar" else (B, T, H, dk)
+    a = torch.randn(ashape, generator=g, device=device)
+    res["alpha"] = torch.sigmoid(a * 0.5 + w.alpha_mean)
+    del a
+    res["beta"] = torch.sigmoid(torch.randn((B, T, H), generator=g, device=device))
+    res["state0"] = (w.state0_std * torch.randn((B, H, dv, dk), generator=g, device=device)
+                     if w.state0_std > 0 else None)
+    return res
+
+
+def slice_inputs(d: dict, pairs) -> dict:
+    """The uploaded values of the listed (batch, head) slices of device
+    inputs, as fp32 numpy arrays shaped like make_inputs' with B = len(pairs)
+    and H = 1."""
+    out = {}
+    for name in ("q", "k", "v", "alpha", "beta"):
+        out[name] = np.stack([d[name][b, :, h].float().cpu().numpy() for b, h in pairs])[:, :, None]
+    s0 = d.get("state0")
+    out["state0"] = None if s0 is None else np.stack([s0[b, h].cpu().numpy() for b, h in pairs])[:, None]
+    return out
+
+
 def to_device(inputs: dict, w: Workload, device="cuda"):
     """Upload to torch tensors: q/k/v in the workload dtype, the rest fp32."""
     import torch

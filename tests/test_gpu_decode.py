@@ -177,3 +177,24 @@ def test_decode_raw_prologue(dtype, gate, dk, dv, order):
     g = oracle.GATE_SCALAR if gate == "scalar" else oracle.GATE_CHANNEL
     o_ref, s_ref = oracle.forward(q, k, raw["v"], a, b, raw["state0"], gate=g, order=order)
     check(o, s, o_ref, s_ref)
+
+
+def test_decode_state_past_2_31_elements():
+    """4352 x 32 states of 128 x 128: 2.3e9 state elements; heads at the end
+    of the batch checked against the oracle."""
+    import torch
+    from gated_delta_rule_12_amd.workloads import make_inputs_device, slice_inputs
+    w = Workload("decode-large", B=4352, H=32, T=1, dk=128, dv=128, chunk=64, state0_std=0.02,
+                 seed=778)
+    assert w.B * w.H * w.dk * w.dv > 2 ** 31
+    d = make_inputs_device(w)
+    st = d["state0"]
+    pairs = [(4351, 31), (4351, 0), (2000, 5)]
+    inp = slice_inputs(d, pairs)
+    args = [token(d, n, 0) for n in ("q", "k", "v", "alpha", "beta")]
+    o, _ = gdn.decode_step(*args, st, inplace=True)
+    torch.cuda.synchronize()
+    oo = np.stack([o[b, h].cpu().numpy()[None, None] for b, h in pairs])
+    ss = np.stack([st[b, h].cpu().numpy() for b, h in pairs])[:, None]
+    o_ref, s_ref = oracle_on(inp, "scalar", PTD)
+    check(oo, ss, o_ref, s_ref)

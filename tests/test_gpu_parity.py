@@ -321,3 +321,31 @@ def test_long_workload_single_stream_sampled():
     inp = make_inputs(w)
     o, s = run(w, inp, n_segments=1)
     check(w, inp, o, s, bh=[(0, 1)])
+
+
+# --------------------------------------------------------------------------
+# maximum sizes: more than 2^31 elements per tensor (64-bit offsets)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_tensors_past_2_31_elements(gate):
+    """9 x 65536 x 32 x 128 = 2.4e9 elements in q, k, v and O (scalar gate:
+    the whole-head path, 288 heads in one pass; channel gate: the sliced
+    path); heads whose data lie past element 2^31 checked against the
+    oracle."""
+    import torch
+    from gated_delta_rule_12_amd.workloads import make_inputs_device, slice_inputs
+    w = Workload("large", B=9, H=32, T=65536, dk=128, dv=128, chunk=64, gate=gate,
+                 state0_std=0.02, seed=777)
+    assert w.B * w.T * w.H * w.dk > 2 ** 31
+    d = make_inputs_device(w)
+    o, s = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], chunk=w.chunk)
+    torch.cuda.synchronize()
+    bh = [(8, 31), (8, 0), (4, 17)]   # (8, 31) holds the last elements of every tensor
+    inp = slice_inputs(d, bh)
+    ow = np.stack([o[b, :, h].cpu().numpy() for b, h in bh])[:, :, None]
+    sw = np.stack([s[b, h].cpu().numpy() for b, h in bh])[:, None]
+    del o, s, d
+    torch.cuda.empty_cache()
+    ws = w.with_(B=len(bh), H=1)
+    check(ws, inp, ow, sw)
