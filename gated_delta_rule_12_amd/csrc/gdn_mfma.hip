@@ -1106,14 +1106,16 @@ struct SegShared {
     float O[OUT ? C * LDO : 4];
 };
 
-// KIND 0: the state S (values from V); KIND 1: the scaling matrix M (V = 0,
-// identity start); KIND 2 (state pass): both, waves 0 .. NWH - 1 on S and
-// NWH .. 2 NWH - 1 on M, sharing the staged chunk and the K^T fragments.
+// KIND 0 (output pass): the state S (values from V); KIND 2 (state pass): S
+// and the scaling matrix M (V = 0, identity start) in one workgroup, waves
+// 0 .. NWH - 1 on S and NWH .. 2 NWH - 1 on M, sharing the staged chunk and
+// the K^T fragments.
 template <int D, int MODE, int KIND, int NV>
 __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, const WsLayout& L, char* wsb,
                                          const u16x8* tfrag, const float* gates, int64_t bh, int gseg,
                                          SegShared<D, MODE>& sh) {
     constexpr bool OUT = MODE == kSegOut;
+    static_assert(KIND == 0 || KIND == 2, "S alone, or S and M together");
     constexpr int NWH = D / (16 * NV);         // waves per state; wave w owns value columns 16 NV (w % NWH) ..
     constexpr int NW = KIND == 2 ? 2 * NWH : NWH;
     constexpr int NT = 64 * NW;
@@ -1130,7 +1132,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wv = KIND == 2 ? w % NWH : w;                      // value block of the wave
-    const bool mk = KIND == 2 ? w >= NWH : KIND == 1;           // the wave runs M
+    const bool mk = KIND == 2 && w >= NWH;                      // the wave runs M
     const int l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int64_t H = p.H, T = p.T;
     const int b = (int)(bh / H), h = (int)(bh - (bh / H) * H);
@@ -1180,7 +1182,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             const int e = tid + NT * k, t = min(e / PPR, nt - 1), c8 = e % PPR;
             const int64_t off = (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8;
             if (parts & 1) kr[k] = *reinterpret_cast<const u32x4*>(kin + off);
-            if (KIND != 1 && (parts & 2)) vr[k] = *reinterpret_cast<const u32x4*>(vin + off);
+            if (parts & 2) vr[k] = *reinterpret_cast<const u32x4*>(vin + off);
             if (OUT && (parts & 4)) qr[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qin + off));
         }
         if (parts & 8) {
@@ -1198,7 +1200,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         for (int k = 0; k < KP; ++k) {
             const int e = tid + NT * k, t = e / PPR, c8 = e % PPR;
             const bool ok = t < nt;
-            *reinterpret_cast<u32x4*>(&sh.V[t * LDK + c8 * 8]) = (KIND != 1 && ok) ? vr[k] : z;
+            *reinterpret_cast<u32x4*>(&sh.V[t * LDK + c8 * 8]) = ok ? vr[k] : z;
             // columns 8 c8 .. +3 and +4 .. +7 of block c8 / 4 go to the
             // permuted positions 16 (c8 % 2) + 4 h and that + 8, h = (c8 % 4) / 2
             const int p0 = t * LDK + 32 * (c8 >> 2) + 16 * (c8 & 1) + 4 * ((c8 >> 1) & 1);
