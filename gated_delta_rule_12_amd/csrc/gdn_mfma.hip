@@ -1519,13 +1519,13 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     if constexpr (OUT)
         if (i_begin < i_end) flush(i_end - 1);
 
-    // ---- end value: final state (last segment of pass 2), S^D or M (pass 1)
+    // ---- end value: final state (last segment of pass 2), S^D (pass 1, row
+    // major) or M (pass 1, as the chain's operand fragments)
     float* dst = nullptr;
     if (OUT) {
         if (gseg == sp.G - 1 && p.s_out) dst = p.s_out + bh * D * D;
     } else {
-        if (!mk || gseg > 0)  // (segment 0 needs no M)
-            dst = reinterpret_cast<float*>(wsb + (mk ? L.mend : L.sdend)) + (bh * sp.G + gseg) * D * D;
+        if (!mk) dst = reinterpret_cast<float*>(wsb + L.sdend) + (bh * sp.G + gseg) * D * D;
     }
     if (dst) {
 #pragma unroll
@@ -1533,6 +1533,45 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 #pragma unroll
             for (int u = 0; u < TPW; ++u)
                 *reinterpret_cast<f32x4*>(&dst[(int64_t)v[n] * D + 16 * u + 4 * g4]) = Sacc[n][u];
+    }
+    if constexpr (!OUT) {
+        if (gseg > 0) {  // (segment 0 needs no M)
+            // M_end(g) goes out as the start-state chain's B operands, split
+            // hi/lo: fragment (column tile nt, k-step s) holds, for lane
+            // (g, c), rows 32 s + 8 g .. + 7 of column 16 nt + c.  An M wave
+            // owns rows v0 .. v0 + 16 NV - 1 of every column: it puts them in
+            // a private LDS tile (column-major, 16 NV floats per column) and
+            // reads back runs of 8 rows of one column, one fragment slot per
+            // lane, so each slot leaves as one 16-byte store per half.
+            constexpr int LW = 16 * NV;  // rows of M per wave
+            static_assert(sizeof(SegShared<D, MODE>) >= sizeof(float) * NWH * D * LW, "M tiles fit");
+            __syncthreads();  // the chunk loop is done with LDS
+            if (mk) {
+                float* Wt = reinterpret_cast<float*>(&sh) + wv * (D * LW);
+#pragma unroll
+                for (int n = 0; n < NV; ++n)
+#pragma unroll
+                    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Wt[(16 * u + 4 * g4 + r) * LW + 16 * n + c16] = Sacc[n][u][r];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const int v0 = LW * wv;
+                u16x8* frag = reinterpret_cast<u16x8*>(wsb + L.mend) + (bh * sp.G + gseg) * (int64_t)(D * D / 4);
+#pragma unroll
+                for (int q = l; q < 2 * LW * TPW; q += 64) {  // (u, run h, column c)
+                    const int c = q & 15, h = (q >> 4) % (LW / 8), u = q / (2 * LW);
+                    const int vr = v0 + 8 * h, s = vr >> 5, fl = 16 * ((vr & 31) >> 3) + c;
+                    const float* src = &Wt[(16 * u + c) * LW + 8 * h];
+                    u16x4 h0, l0, h1, l1;
+                    split4(*reinterpret_cast<const f32x4*>(src), h0, l0);
+                    split4(*reinterpret_cast<const f32x4*>(src + 4), h1, l1);
+                    frag[((u * KS + s) * 2 + 0) * 64 + fl] = cat(h0, h1);
+                    frag[((u * KS + s) * 2 + 1) * 64 + fl] = cat(l0, l1);
+                }
+            }
+        }
     }
 }
 
@@ -1582,21 +1621,26 @@ ChainPlan chain_plan(int G, int64_t heads, int D) {
     return c;
 }
 
-// NR = 2 (compose): the P and the Q rows of a block in one workgroup, sharing
-// the staged Mult(s) and its hi/lo split; NR = 1 otherwise.
+// Multipliers (M_end and the composed P_j) are stored as the MFMA B operands
+// of these products, split hi/lo (fragment (column tile nt, k-step s): lane
+// (g, c) holds rows 32 s + 8 g .. + 7 of column 16 nt + c), written so by the
+// state pass and by the compose step; each wave loads the fragments of its
+// column tiles for step s + 1 while step s computes, straight into registers.
+// NR = 2 (compose): the P and the Q rows of a block in one workgroup, both
+// from (I, 0) through every map of the block.
 template <int D, int NR>
 __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayout L, char* wsb, int mode,
                                                     ChainPlan cp) {
     constexpr int LD = D + 4;
-    constexpr int MP = D * D / 4 / 256;  // float4 pieces of a D x D matrix per thread
+    constexpr int KS = D / 32;           // k-steps of the product
     constexpr int SP = 16 * D / 4;       // float4 pieces of 16 rows
     constexpr int SR = (SP + 255) / 256;
     constexpr int NTW = D / 64;          // column tiles per wave
     constexpr int NX = D / 16;           // row blocks per head
     constexpr int64_t DD = (int64_t)D * D;
-    __shared__ __attribute__((aligned(16))) float Ms[D * LD];
+    constexpr int64_t FD = DD / 4;       // u16x8 per fragment matrix (hi and lo)
     __shared__ __attribute__((aligned(16))) float Cb[2][NR][16 * LD];
-    __shared__ __attribute__((aligned(16))) float SDs[16 * LD];
+    __shared__ __attribute__((aligned(16))) float SDs[2][16 * LD];
     const int64_t heads = p.B * p.H;
     const bool per_block = mode == kChainCompose || mode == kChainExpand;
     const int64_t groups = heads * (per_block ? cp.nb : 1);  // workgroups of a group share Mult
@@ -1615,62 +1659,68 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int r0 = 16 * x;
     const float* sdend = reinterpret_cast<const float*>(wsb + L.sdend) + bh * sp.G * DD;
-    const float* mend = reinterpret_cast<const float*>(wsb + L.mend) + bh * sp.G * DD;
+    const u16x8* mfr = reinterpret_cast<const u16x8*>(wsb + L.mend) + bh * sp.G * FD;
     float* sstart = reinterpret_cast<float*>(wsb + L.sstart) + bh * sp.G * DD;
-    float* pblk = reinterpret_cast<float*>(wsb + L.blk) + bh * cp.nb * DD;
+    u16x8* pfr = reinterpret_cast<u16x8*>(wsb + L.blk) + bh * cp.nb * FD;
     float* qblk = reinterpret_cast<float*>(wsb + L.blk) + (heads + bh) * cp.nb * DD;
 
-    // the job: start rows of each set, step operands Mult(s) = mult0 + s DD and
-    // Add(s) = add0 + s DD (last set only), X written before step s (pre),
-    // after it (post), at the end (fin, per set)
+    // the job: start rows of each set (nullptr: the identity for set 0, zero
+    // otherwise), step operands Mult(s) = mult0 + s FD (fragments) and Add(s)
+    // = add0 + s DD (rows, last set only), X written before step s (pre),
+    // after it (post), at the end (fin, rows; compose: P_j as fragments)
     const int a = 1 + j * cp.b;                               // first map of block j
     const int len = per_block ? min(cp.b, sp.G - 1 - a) : 0;  // its maps a .. a + len - 1
     const float* init[NR];
-    float* fin[NR];
-    const float* mult0;
-    const float* add0 = nullptr;
+    const u16x8* mult0;
+    const float* add0;
     float* pre0 = nullptr;
     float* post0 = nullptr;
+    float* fin = nullptr;
+    u16x8* fin_frag = nullptr;
     int64_t pre_stride = DD;
     int nsteps;
-    fin[NR - 1] = nullptr;
     if (mode == kChainSeq) {
         init[0] = sdend;
         nsteps = sp.G - 2;
-        mult0 = mend + DD;
+        mult0 = mfr + FD;
         add0 = sdend + DD;
         pre0 = sstart + DD;
-        fin[0] = sstart + (sp.G - 1) * DD;
+        fin = sstart + (sp.G - 1) * DD;
     } else if (mode == kChainCompose) {
-        // set 0: P_j (from M(a), no addend); set NR - 1: Q_j (from S^D(a))
-        init[0] = mend + a * DD;
-        init[NR - 1] = sdend + a * DD;
-        nsteps = len - 1;
-        mult0 = mend + (a + 1) * DD;
-        add0 = sdend + (a + 1) * DD;
-        fin[0] = pblk + j * DD;
-        fin[NR - 1] = qblk + j * DD;
+        init[0] = nullptr;
+        init[NR - 1] = nullptr;
+        nsteps = len;
+        mult0 = mfr + a * FD;
+        add0 = sdend + a * DD;
+        fin_frag = pfr + j * FD;
+        fin = qblk + j * DD;
     } else if (mode == kChainBlocks) {
         init[0] = sdend;
         nsteps = cp.nb;
-        mult0 = pblk;
+        mult0 = pfr;
         add0 = qblk;
         pre0 = sstart + DD;
         pre_stride = cp.b * DD;
-        fin[0] = sstart + (sp.G - 1) * DD;
+        fin = sstart + (sp.G - 1) * DD;
     } else {
         init[0] = sstart + a * DD;
         nsteps = len - 1;
-        mult0 = mend + a * DD;
+        mult0 = mfr + a * FD;
         add0 = sdend + a * DD;
         post0 = sstart + (a + 1) * DD;
     }
 
-    f32x4 mreg[MP], sreg[SR];
+    // B fragments of the wave's column tiles nt = w + 4 q, hi and lo
+    u16x8 fcur[NTW][KS][2], fnxt[NTW][KS][2];
+    f32x4 sreg[SR];
     auto fetch = [&](int s) {
-        const f32x4* M = reinterpret_cast<const f32x4*>(mult0 + s * DD);
+        const u16x8* F = mult0 + s * FD;
 #pragma unroll
-        for (int k = 0; k < MP; ++k) mreg[k] = M[tid + 256 * k];
+        for (int q = 0; q < NTW; ++q)
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl) fnxt[q][k][hl] = F[(((w + 4 * q) * KS + k) * 2 + hl) * 64 + l];
         const f32x4* S = reinterpret_cast<const f32x4*>(add0 + s * DD + (int64_t)r0 * D);
 #pragma unroll
         for (int k = 0; k < SR; ++k) sreg[k] = S[min(tid + 256 * k, SP - 1)];
@@ -1684,10 +1734,16 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
     };
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const f32x4* S = reinterpret_cast<const f32x4*>(init[r] + (int64_t)r0 * D);
         for (int e = tid; e < SP; e += 256) {
             const int rr = e / (D / 4), c4 = e % (D / 4);
-            *reinterpret_cast<f32x4*>(&Cb[0][r][rr * LD + 4 * c4]) = S[e];
+            f32x4 val;
+            if (init[r]) {
+                val = reinterpret_cast<const f32x4*>(init[r] + (int64_t)r0 * D)[e];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) val[i] = (r == 0 && r0 + rr == 4 * c4 + i) ? 1.f : 0.f;
+            }
+            *reinterpret_cast<f32x4*>(&Cb[0][r][rr * LD + 4 * c4]) = val;
         }
     }
     if (nsteps > 0) fetch(0);
@@ -1695,43 +1751,60 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
     for (int s = 0;; ++s) {
         if (s < nsteps) {
 #pragma unroll
-            for (int k = 0; k < MP; ++k) {
-                const int e = tid + 256 * k, c = e / (D / 4), a4 = e % (D / 4);
-                *reinterpret_cast<f32x4*>(&Ms[c * LD + 4 * a4]) = mreg[k];
-            }
+            for (int q = 0; q < NTW; ++q)
+#pragma unroll
+                for (int k = 0; k < KS; ++k)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl) fcur[q][k][hl] = fnxt[q][k][hl];
 #pragma unroll
             for (int k = 0; k < SR; ++k) {
                 const int e = tid + 256 * k;
                 if (SP % 256 == 0 || e < SP)
-                    *reinterpret_cast<f32x4*>(&SDs[(e / (D / 4)) * LD + 4 * (e % (D / 4))]) = sreg[k];
+                    *reinterpret_cast<f32x4*>(&SDs[s & 1][(e / (D / 4)) * LD + 4 * (e % (D / 4))]) = sreg[k];
             }
         }
-        __syncthreads();  // X complete in Cb[cur]; Mult(s), Add(s) staged
+        __syncthreads();  // X complete in Cb[cur]; Add(s) staged; Cb[cur ^ 1] and SDs[s ^ 1] free
         if (s + 1 < nsteps) fetch(s + 1);
         if (s < nsteps) {
             if (pre0) write_rows(pre0 + s * pre_stride, Cb[cur][0]);
         } else {
+            if (fin) write_rows(fin, Cb[cur][NR - 1]);
+            if (fin_frag) {
+                // P_j rows 16 x .. of block j as B fragments: k-step x / 2,
+                // lane groups 2 (x % 2), 2 (x % 2) + 1
+                if (tid < (D / 16) * 32) {
+                    const int nt = tid >> 5, hsel = (tid >> 4) & 1, cc = tid & 15;
+                    const int gg = 2 * (x & 1) + hsel, ks = x >> 1;
+                    f32x4 y0, y1;
 #pragma unroll
-            for (int r = 0; r < NR; ++r)
-                if (fin[r]) write_rows(fin[r], Cb[cur][r]);
+                    for (int e = 0; e < 4; ++e) {
+                        y0[e] = Cb[cur][0][(8 * hsel + e) * LD + 16 * nt + cc];
+                        y1[e] = Cb[cur][0][(8 * hsel + 4 + e) * LD + 16 * nt + cc];
+                    }
+                    u16x4 h0, l0, h1, l1;
+                    split4(y0, h0, l0);
+                    split4(y1, h1, l1);
+                    fin_frag[((nt * KS + ks) * 2 + 0) * 64 + 16 * gg + cc] = cat(h0, h1);
+                    fin_frag[((nt * KS + ks) * 2 + 1) * 64 + 16 * gg + cc] = cat(l0, l1);
+                }
+            }
         }
         if (s > 0 && post0) write_rows(post0 + (s - 1) * DD, Cb[cur][0]);
         if (s == nsteps) break;
-        // Cb[cur ^ 1][r] = Cb[cur][r] Mult(s) (+ Add(s) for the last set):
-        // wave w takes column tiles w, w + 4
-        u16x8 ah[NR][D / 32], al[NR][D / 32];
+        // Cb[cur ^ 1][r] = Cb[cur][r] Mult(s) (+ Add(s) for the last set)
+        u16x8 ah[NR][KS], al[NR][KS];
 #pragma unroll
         for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int q = 0; q < D / 32; ++q) {
+            for (int k = 0; k < KS; ++k) {
                 const float* A = Cb[cur][r];
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * q + 8 * g4]);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * q + 8 * g4 + 4]);
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * k + 8 * g4]);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(&A[c16 * LD + 32 * k + 8 * g4 + 4]);
                 u16x4 h0, l0, h1, l1;
                 split4(x0, h0, l0);
                 split4(x1, h1, l1);
-                ah[r][q] = cat(h0, h1);
-                al[r][q] = cat(l0, l1);
+                ah[r][k] = cat(h0, h1);
+                al[r][k] = cat(l0, l1);
             }
 #pragma unroll
         for (int q = 0; q < NTW; ++q) {
@@ -1740,25 +1813,14 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
 #pragma unroll
             for (int r = 0; r < NR; ++r) a1[r] = a2[r] = a3[r] = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a1[NR - 1][i] = SDs[(4 * g4 + i) * LD + 16 * nt + c16];
-            if (NR == 1 && !add0) a1[0] = zero4();
+            for (int i = 0; i < 4; ++i) a1[NR - 1][i] = SDs[s & 1][(4 * g4 + i) * LD + 16 * nt + c16];
 #pragma unroll
-            for (int k = 0; k < D / 32; ++k) {
-                f32x4 y0, y1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    y0[e] = Ms[(32 * k + 8 * g4 + e) * LD + 16 * nt + c16];
-                    y1[e] = Ms[(32 * k + 8 * g4 + 4 + e) * LD + 16 * nt + c16];
-                }
-                u16x4 h0, l0, h1, l1;
-                split4(y0, h0, l0);
-                split4(y1, h1, l1);
-                const u16x8 bh_ = cat(h0, h1), bl_ = cat(l0, l1);
+            for (int k = 0; k < KS; ++k) {
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
-                    a1[r] = mfma(ah[r][k], bh_, a1[r]);
-                    a2[r] = mfma(ah[r][k], bl_, a2[r]);
-                    a3[r] = mfma(al[r][k], bh_, a3[r]);
+                    a1[r] = mfma(ah[r][k], fcur[q][k][0], a1[r]);
+                    a2[r] = mfma(ah[r][k], fcur[q][k][1], a2[r]);
+                    a3[r] = mfma(al[r][k], fcur[q][k][0], a3[r]);
                 }
             }
 #pragma unroll
@@ -1768,7 +1830,6 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
                 for (int i = 0; i < 4; ++i) Cb[cur ^ 1][r][(4 * g4 + i) * LD + 16 * nt + c16] = sum[i];
             }
         }
-        __syncthreads();  // Mult(s), Add(s) and X consumed
         cur ^= 1;
     }
 }
