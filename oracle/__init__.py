@@ -10,6 +10,10 @@ The recurrence, the two gate orderings and the two gate kinds it follows are
 stated, with the passages of the pages they come from, in the header of
 ``gdn_oracle.c``.
 
+``backward`` is the reverse mode of ``forward``: the chain rule through the
+same token loop, run backwards over stored states (``gdn_oracle.c``, second
+half; the pages give no gradient formulas, so its header derives them).
+
 ``prologue`` forms the core's inputs from raw projections (per-head L2 norm of
 q and k, sigmoid gates), the step before the core in the DeltaNet block.
 
@@ -63,6 +67,10 @@ def _load():
                 i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                 ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
             lib.gdn_oracle_forward.restype = ctypes.c_int
+            lib.gdn_oracle_backward.argtypes = [
+                i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                ctypes.c_double] + [dp] * 14 + [ctypes.c_int]
+            lib.gdn_oracle_backward.restype = ctypes.c_int
             lib.gdn_oracle_max_threads.argtypes = []
             lib.gdn_oracle_max_threads.restype = ctypes.c_int
             _lib = lib
@@ -115,6 +123,42 @@ def forward(q, k, v, alpha, beta, state0=None, *, gate: int = GATE_SCALAR,
     if rc != 0:
         raise RuntimeError(f"gdn_oracle_forward failed with status {rc}")
     return out, st
+
+
+def backward(q, k, v, alpha, beta, state0, dout, dstate=None, *,
+             gate: int = GATE_SCALAR, order: int = PREDICT_THEN_DECAY,
+             scale: float = 1.0, threads: int = 0):
+    """Gradients of a loss L through ``forward``: given dout = dL/dout
+    [B, T, H, dv] and dstate = dL/dS_T [B, H, dv, dk] (None: zero), returns
+    (dq, dk, dv, dalpha, dbeta, dstate0) as float64 arrays shaped like
+    q, k, v, alpha, beta and the state.  fp64, token by token in reverse
+    over the states of a forward sweep.
+    """
+    q, k, v, alpha, beta, dout = (_f64(a) for a in (q, k, v, alpha, beta, dout))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    want_alpha = (B, T, H) if gate == GATE_SCALAR else (B, T, H, dk)
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or alpha.shape != want_alpha \
+            or beta.shape != (B, T, H) or dout.shape != v.shape:
+        raise ValueError("backward: inconsistent shapes")
+    s0 = None if state0 is None else _f64(state0)
+    dst = None if dstate is None else _f64(dstate)
+    for x in (s0, dst):
+        if x is not None and x.shape != (B, H, dv, dk):
+            raise ValueError("states must be [B,H,dv,dk]")
+    dq = np.zeros_like(q)
+    dkk = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    dal = np.zeros_like(alpha)
+    dbe = np.zeros_like(beta)
+    ds0 = np.zeros((B, H, dv, dk), dtype=np.float64)
+    rc = _load().gdn_oracle_backward(B, T, H, dk, dv, int(gate), int(order), float(scale),
+                                     _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(s0), _ptr(dout), _ptr(dst), _ptr(dq), _ptr(dkk),
+                                     _ptr(dvv), _ptr(dal), _ptr(dbe), _ptr(ds0), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"gdn_oracle_backward failed with status {rc}")
+    return dq, dkk, dvv, dal, dbe, ds0
 
 
 def prologue(q, k, alpha_logit, beta_logit):
