@@ -275,6 +275,48 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dt
                          beta_logit, state_in, out, state_out, true, stream);
 }
 
+size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
+    if (validate(B, T, H, dk, dv, 16, GDN_F32, GDN_GATE_SCALAR, GDN_PREDICT_THEN_DECAY, 1) != GDN_OK)
+        return 0;
+    return backward_workspace(B, T, H, dk, dv);
+}
+
+int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,
+                 int32_t order, float scale, const void* q, const void* k, const void* v,
+                 const float* alpha, const float* beta, const float* state0, const float* grad_out,
+                 const float* grad_state_out, float* grad_q, float* grad_k, float* grad_v,
+                 float* grad_alpha, float* grad_beta, float* grad_state0, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    int s = validate(B, T, H, dk, dv, 16, dtype, gate, order, 1);
+    if (s != GDN_OK) return s;
+    if (B * H == 0) return GDN_OK;
+    // one workgroup per (batch, head, block of at least 16 state rows)
+    if (B * H * (dv / 16) > ((int64_t)1 << 31) - 1) return GDN_E_SHAPE;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !grad_out || !grad_q || !grad_k || !grad_v ||
+                  !grad_alpha || !grad_beta))
+        return GDN_E_ARG;
+    // q, k move in 8-byte (bf16) or 16-byte (fp32) pieces, a channel gate and
+    // the states in 16-byte pieces, everything else per element
+    const uintptr_t qk_align = dtype == GDN_BF16 ? 8 : 16;
+    if (!aligned(q, qk_align) || !aligned(k, qk_align) || !aligned(state0, 16) ||
+        !aligned(grad_state_out, 16) || !aligned(grad_state0, 16) ||
+        !aligned(alpha, gate == GDN_GATE_CHANNEL ? 16 : 4) || !aligned(beta, 4) || !aligned(v, 2) ||
+        !aligned(grad_out, 4) || !aligned(grad_q, 4) || !aligned(grad_k, 4) || !aligned(grad_v, 4) ||
+        !aligned(grad_alpha, 4) || !aligned(grad_beta, 4))
+        return GDN_E_ARG;
+    const size_t need = backward_workspace(B, T, H, dk, dv);
+    if (T > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
+    BwdProblem a{};
+    a.p = make_problem(B, T, H, dk, dv, 16, dtype, gate, order, scale);
+    a.p.q = q; a.p.k = k; a.p.v = v; a.p.alpha = alpha; a.p.beta = beta; a.p.s0 = state0;
+    a.dout = grad_out;
+    a.ds_out = grad_state_out;
+    a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dalpha = grad_alpha; a.dbeta = grad_beta;
+    a.ds0 = grad_state0;
+    a.ckpt = static_cast<float*>(workspace);
+    return finish(backward(a, static_cast<hipStream_t>(stream)));
+}
+
 int gdn_profile_enable(int on) {
     if (!on) {
         prof_drain();

@@ -1,0 +1,404 @@
+// Backward pass of the gated delta rule (gdn_backward): gradients of a loss
+// through the forward recurrence, for both gate orderings and gate kinds.
+//
+// The pages give the recurrence, not its gradient (the Gated DeltaNet
+// GPU-parallelisation blog, section 1.2, and the DeltaNet illustrated notes
+// fix the forward; training through it is mentioned, not derived).  Here the
+// chain rule is applied to one token step, row by row: rows r of the dv x dk
+// state evolve independently given the token's k, gate d and beta, so with
+// X_r = S_r (predict-then-decay) or S_r * d (decay-then-predict),
+// p_r = X_r . k, e_r = beta (v_r - p_r) and G_r = dL/dS'_r + scale do_r q,
+// gk_r = G_r . k:
+//   dv_r = beta gk_r                 dbeta += gk_r (v_r - p_r)
+//   dk  += e_r G_r - beta gk_r X_r   dq    += scale do_r S'_r
+//   predict-then-decay: dL/dS_r = G_r * d - beta gk_r k,  dd += G_r * S_r
+//   decay-then-predict: dX_r = G_r - beta gk_r k,  dL/dS_r = dX_r * d,
+//                       dd += dX_r * S_r
+// (dalpha = dd for a channel gate, its sum over channels for a scalar gate).
+//
+// Schedule (recompute from boundary-state checkpoints): a workgroup owns a
+// block of state rows of one (batch, head).  Phase A runs the recurrence
+// forward over the sequence and stores its rows of the state every kCk
+// tokens in the workspace.  Phase B walks the checkpoint intervals backwards:
+// it recomputes the interval forward from its checkpoint, keeping the state
+// at every kSub-th token in LDS, then for each run of kSub tokens (last
+// first) recomputes the kSub states into registers and carries dL/dS back
+// through them.  The per-token sums over rows (dq, dk, dalpha, dbeta) are
+// reduced within the workgroup through LDS and added into the outputs with
+// fp32 atomics (one add per workgroup and element, so the order of the row
+// blocks' contributions, and with it the last bits, may vary between runs).
+// dv is row-local and written directly, as is dL/dS_0.
+//
+// Every thread holds kRows rows as float4 pieces, LPR lanes per row (the
+// layout of the decode step); a row's dot products are shuffle sums over its
+// lanes.
+#include <algorithm>
+
+#include "gdn_internal.h"
+#include "../../include/gdn.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 2;    // rows per thread
+constexpr int kCk = 64;     // tokens between stored checkpoints
+constexpr int kSub = 16;    // tokens recomputed into registers at a time
+constexpr int kSubs = kCk / kSub;
+constexpr int kMaxD = 128;
+
+template <int DT>
+__device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
+    if constexpr (DT == 0) {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+}
+
+__device__ __forceinline__ float dot4(const float4& a, const float4& b) {
+    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+__device__ __forceinline__ float4 mul4(const float4& a, const float4& b) {
+    return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ float4 axpy4(float s, const float4& x, const float4& y) {  // s x + y
+    return make_float4(s * x.x + y.x, s * x.y + y.y, s * x.z + y.z, s * x.w + y.w);
+}
+__device__ __forceinline__ float4 add4(const float4& a, const float4& b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// sum over the LPR lanes of a row (aligned groups of LPR lanes)
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+// sum over the row groups of a wave (lanes equal modulo LPR)
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = LPR; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+template <int LPR>
+__device__ __forceinline__ float4 group_sum4(float4 x) {
+    return make_float4(group_sum<LPR>(x.x), group_sum<LPR>(x.y), group_sum<LPR>(x.z),
+                       group_sum<LPR>(x.w));
+}
+
+// one token's inputs as a thread sees them
+struct Tok {
+    float4 k, q, d;
+    float beta;
+    float v[kRows];
+};
+
+template <int DT, int LPR, bool CH, bool DTPO>
+struct Bwd {
+    static constexpr int RPW = 64 / LPR;             // rows per wave and pass
+    static constexpr int RB = 4 * RPW * kRows;       // rows per workgroup
+    const BwdProblem& a;
+    int64_t b, h, bh;
+    int c, w, l;
+    bool col;
+    int r[kRows];
+    bool on[kRows];
+
+    __device__ Bwd(const BwdProblem& a_, int64_t bh_, int rb) : a(a_) {
+        const Problem& p = a.p;
+        bh = bh_;
+        b = bh / p.H;
+        h = bh - b * p.H;
+        const int tid = threadIdx.x;
+        w = tid >> 6;
+        l = tid & 63;
+        c = l % LPR;
+        col = 4 * c < p.dk;
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+            r[j] = rb * RB + (j * 4 + w) * RPW + l / LPR;
+            on[j] = r[j] < p.dv;
+        }
+    }
+
+    __device__ Tok load(int64_t t) const {
+        const Problem& p = a.p;
+        const int64_t th = (b * p.T + t) * p.H + h;  // token-head index
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        Tok x;
+        x.k = col ? ld4<DT>(p.k, th * p.dk + 4 * c) : z4;
+        x.q = col ? ld4<DT>(p.q, th * p.dk + 4 * c) : z4;
+        if constexpr (CH) {
+            x.d = col ? *reinterpret_cast<const float4*>(p.alpha + th * p.dk + 4 * c) : z4;
+        } else {
+            const float g = p.alpha[th];
+            x.d = make_float4(g, g, g, g);
+        }
+        x.beta = p.beta[th];
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) x.v[j] = on[j] ? gdn_ld<DT>(p.v, th * p.dv + r[j]) : 0.f;
+        return x;
+    }
+
+    // the state after the token, from the state before it (rows of the thread)
+    __device__ void step(const float4 (&S)[kRows], float4 (&Sn)[kRows], const Tok& x) const {
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+            const float4 X = DTPO ? mul4(S[j], x.d) : S[j];
+            const float pr = row_sum<LPR>(dot4(X, x.k));
+            const float e = x.beta * (x.v[j] - pr);
+            Sn[j] = axpy4(e, x.k, DTPO ? X : mul4(S[j], x.d));
+        }
+    }
+
+    // the thread's piece of row j: in a [B, H, dv, dk] state tensor, and in
+    // one head's state (the checkpoints)
+    __device__ int64_t off(int j) const { return (bh * a.p.dv + r[j]) * a.p.dk + 4 * c; }
+    __device__ int64_t roff(int j) const { return (int64_t)r[j] * a.p.dk + 4 * c; }
+};
+
+// per-token partial sums of the workgroup: [wave][token of the run][dq | dk | dd][dk]
+struct BwdShared {
+    float4 vec[4][kSub][3][kMaxD / 4];
+    float sc[4][kSub][2];                 // dbeta, dalpha (scalar gate)
+    float4 sub[kSubs][kRows][kThreads];   // states at the runs' starts
+};
+
+template <int DT, int LPR, bool CH, bool DTPO>
+__global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
+    using K = Bwd<DT, LPR, CH, DTPO>;
+    __shared__ BwdShared sh;
+    const Problem& p = a.p;
+    const int64_t bh = blockIdx.x / nrb;
+    const int rb = (int)(blockIdx.x % nrb);
+    const K k(a, bh, rb);
+    const int tid = threadIdx.x;
+    const int64_t T = p.T;
+    const int64_t NCk = (T + kCk - 1) / kCk;
+    const int64_t DD = p.dv * p.dk;
+    float* ckpt = a.ckpt + bh * NCk * DD;
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    // ---- phase A: forward, a checkpoint of the rows every kCk tokens
+    float4 S[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j)
+        S[j] = (k.on[j] && k.col && p.s0) ? *reinterpret_cast<const float4*>(p.s0 + k.off(j)) : z4;
+    {
+        Tok nx = T > 0 ? k.load(0) : Tok{};
+        for (int64_t t = 0; t < T; ++t) {
+            const Tok x = nx;
+            if (t + 1 < T) nx = k.load(t + 1);
+            if (t % kCk == 0) {
+#pragma unroll
+                for (int j = 0; j < kRows; ++j)
+                    if (k.on[j] && k.col)
+                        *reinterpret_cast<float4*>(ckpt + (t / kCk) * DD + k.roff(j)) = S[j];
+            }
+            float4 Sn[kRows];
+            k.step(S, Sn, x);
+#pragma unroll
+            for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
+        }
+    }
+
+    // ---- phase B: dL/dS carried back from the end
+    float4 Gd[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j)
+        Gd[j] = (k.on[j] && k.col && a.ds_out) ? *reinterpret_cast<const float4*>(a.ds_out + k.off(j)) : z4;
+
+    for (int64_t ck = NCk - 1; ck >= 0; --ck) {
+        const int64_t t0 = ck * kCk;
+        const int n = (int)min<int64_t>(kCk, T - t0);
+        // the interval forward from its checkpoint (each thread reads back
+        // the elements it wrote), the run starts into LDS
+#pragma unroll
+        for (int j = 0; j < kRows; ++j)
+            S[j] = (k.on[j] && k.col) ? *reinterpret_cast<const float4*>(ckpt + ck * DD + k.roff(j)) : z4;
+        const int nsub = (n + kSub - 1) / kSub;
+        const int last = (nsub - 1) * kSub;  // first token of the last run
+        for (int u = 0;; ++u) {
+            if (u % kSub == 0) {
+#pragma unroll
+                for (int j = 0; j < kRows; ++j) sh.sub[u / kSub][j][tid] = S[j];
+            }
+            if (u == last) break;  // (the last run's states are recomputed below)
+            float4 Sn[kRows];
+            k.step(S, Sn, k.load(t0 + u));
+#pragma unroll
+            for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
+        }
+        for (int sb = nsub - 1; sb >= 0; --sb) {
+            const int64_t ts = t0 + (int64_t)sb * kSub;
+            const int m = min(kSub, n - sb * kSub);
+            // the run's states, St[u] before token ts + u
+            float4 St[kSub + 1][kRows];
+#pragma unroll
+            for (int j = 0; j < kRows; ++j) St[0][j] = sh.sub[sb][j][tid];
+#pragma unroll
+            for (int u = 0; u < kSub; ++u) {
+                if (u < m) {
+                    k.step(St[u], St[u + 1], k.load(ts + u));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < kRows; ++j) St[u + 1][j] = St[u][j];
+                }
+            }
+#pragma unroll
+            for (int u = kSub - 1; u >= 0; --u) {
+                if (u >= m) continue;
+                const int64_t t = ts + u;
+                const int64_t th = (k.b * T + t) * p.H + k.h;
+                const Tok x = k.load(t);
+                float4 dkp = z4, dqp = z4, ddp = z4;
+                float dbp = 0.f;
+#pragma unroll
+                for (int j = 0; j < kRows; ++j) {
+                    const float dor = k.on[j] ? a.dout[th * p.dv + k.r[j]] : 0.f;
+                    const float4 X = DTPO ? mul4(St[u][j], x.d) : St[u][j];
+                    const float pr = row_sum<LPR>(dot4(X, x.k));
+                    const float e = x.beta * (x.v[j] - pr);
+                    const float4 G = axpy4(p.scale * dor, x.q, Gd[j]);
+                    const float gk = row_sum<LPR>(dot4(G, x.k));
+                    if (k.on[j] && k.c == 0) a.dv[th * p.dv + k.r[j]] = x.beta * gk;
+                    dbp += gk * (x.v[j] - pr);
+                    dkp = add4(dkp, axpy4(e, G, make_float4(-x.beta * gk * X.x, -x.beta * gk * X.y,
+                                                            -x.beta * gk * X.z, -x.beta * gk * X.w)));
+                    dqp = axpy4(p.scale * dor, St[u + 1][j], dqp);
+                    const float4 bk = make_float4(x.beta * gk * x.k.x, x.beta * gk * x.k.y,
+                                                  x.beta * gk * x.k.z, x.beta * gk * x.k.w);
+                    if constexpr (!DTPO) {
+                        ddp = add4(ddp, mul4(G, St[u][j]));
+                        Gd[j] = make_float4(G.x * x.d.x - bk.x, G.y * x.d.y - bk.y, G.z * x.d.z - bk.z,
+                                            G.w * x.d.w - bk.w);
+                    } else {
+                        const float4 dX = make_float4(G.x - bk.x, G.y - bk.y, G.z - bk.z, G.w - bk.w);
+                        ddp = add4(ddp, mul4(dX, St[u][j]));
+                        Gd[j] = mul4(dX, x.d);
+                    }
+                }
+                // the wave's sums over its rows: lanes c of the first row group
+                dkp = group_sum4<LPR>(dkp);
+                dqp = group_sum4<LPR>(dqp);
+                if constexpr (CH) ddp = group_sum4<LPR>(ddp);
+                // dbp is equal on the lanes of a row: sum over row groups only
+                dbp = group_sum<LPR>(dbp);
+                float das = 0.f;
+                if constexpr (!CH) das = group_sum<LPR>(row_sum<LPR>(ddp.x + ddp.y + ddp.z + ddp.w));
+                if (k.l < LPR) {
+                    sh.vec[k.w][u][0][k.c] = dqp;
+                    sh.vec[k.w][u][1][k.c] = dkp;
+                    if constexpr (CH) sh.vec[k.w][u][2][k.c] = ddp;
+                    if (k.l == 0) {
+                        sh.sc[k.w][u][0] = dbp;
+                        sh.sc[k.w][u][1] = das;
+                    }
+                }
+            }
+            __syncthreads();  // the run's partial sums complete
+            // workgroup sums into the outputs: (token, vector, piece) jobs
+            const int P4 = (int)(p.dk / 4);
+            const int nv = CH ? 3 : 2;
+            for (int e = tid; e < m * (nv * P4 + 1); e += kThreads) {
+                const int u = e / (nv * P4 + 1), f = e % (nv * P4 + 1);
+                const int64_t th = (k.b * T + ts + u) * p.H + k.h;
+                if (f == nv * P4) {
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) {
+                        s0 += sh.sc[ww][u][0];
+                        s1 += sh.sc[ww][u][1];
+                    }
+                    atomicAdd(a.dbeta + th, s0);
+                    if constexpr (!CH) atomicAdd(a.dalpha + th, s1);
+                } else {
+                    const int vi = f / P4, c4 = f % P4;
+                    float4 s = sh.vec[0][u][vi][c4];
+#pragma unroll
+                    for (int ww = 1; ww < 4; ++ww) s = add4(s, sh.vec[ww][u][vi][c4]);
+                    float* dst = (vi == 0 ? a.dq : vi == 1 ? a.dk : a.dalpha) + th * p.dk + 4 * c4;
+                    atomicAdd(dst + 0, s.x);
+                    atomicAdd(dst + 1, s.y);
+                    atomicAdd(dst + 2, s.z);
+                    atomicAdd(dst + 3, s.w);
+                }
+            }
+            __syncthreads();  // partial sums read; LDS free for the next run
+        }
+    }
+    if (a.ds0) {
+#pragma unroll
+        for (int j = 0; j < kRows; ++j)
+            if (k.on[j] && k.col) *reinterpret_cast<float4*>(a.ds0 + k.off(j)) = Gd[j];
+    }
+}
+
+__global__ void k_zero(float* p, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
+}
+
+hipError_t zero(float* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+template <int DT, int LPR, bool CH, bool DTPO>
+hipError_t launch4(const BwdProblem& a, hipStream_t st) {
+    constexpr int RB = Bwd<DT, LPR, CH, DTPO>::RB;
+    const int nrb = (int)((a.p.dv + RB - 1) / RB);
+    const int64_t grid = a.p.B * a.p.H * nrb;
+    hipLaunchKernelGGL((k_backward<DT, LPR, CH, DTPO>), dim3((unsigned)grid), dim3(kThreads), 0, st, a,
+                       nrb);
+    return hipGetLastError();
+}
+
+template <int DT, int LPR>
+hipError_t launch_lpr(const BwdProblem& a, hipStream_t st) {
+    const bool ch = a.p.gate == GDN_GATE_CHANNEL, dtp = a.p.order == GDN_DECAY_THEN_PREDICT;
+    if (ch) return dtp ? launch4<DT, LPR, true, true>(a, st) : launch4<DT, LPR, true, false>(a, st);
+    return dtp ? launch4<DT, LPR, false, true>(a, st) : launch4<DT, LPR, false, false>(a, st);
+}
+
+template <int DT>
+hipError_t launch_dt(const BwdProblem& a, hipStream_t st) {
+    const int64_t pieces = a.p.dk / 4;  // float4 pieces per row, 4 .. 32
+    if (pieces <= 4) return launch_lpr<DT, 4>(a, st);
+    if (pieces <= 8) return launch_lpr<DT, 8>(a, st);
+    if (pieces <= 16) return launch_lpr<DT, 16>(a, st);
+    return launch_lpr<DT, 32>(a, st);
+}
+
+}  // namespace
+
+size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
+    const int64_t NCk = (T + kCk - 1) / kCk;
+    return align256(sizeof(float) * (size_t)(B * H * NCk) * (size_t)(dk * dv));
+}
+
+hipError_t backward(const BwdProblem& a, hipStream_t st) {
+    const Problem& p = a.p;
+    const int64_t th = p.B * p.T * p.H;
+    hipError_t e;
+    prof_begin("k_bwd_zero", st);
+    if ((e = zero(a.dq, th * p.dk, st)) != hipSuccess) return e;
+    if ((e = zero(a.dk, th * p.dk, st)) != hipSuccess) return e;
+    if ((e = zero(a.dalpha, th * (p.gate == GDN_GATE_CHANNEL ? p.dk : 1), st)) != hipSuccess) return e;
+    if ((e = zero(a.dbeta, th, st)) != hipSuccess) return e;
+    prof_end(st);
+    prof_begin("k_backward", st);
+    e = p.dtype == GDN_BF16 ? launch_dt<1>(a, st) : launch_dt<0>(a, st);
+    prof_end(st);
+    return e;
+}
+
+}  // namespace gdn

@@ -82,6 +82,23 @@ hipError_t seqpar_chain(const Problem& p, const Split& sp, char* ws, const WsLay
 hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLayout& L,
                         hipStream_t st);
 
+// Backward pass (gdn_backward): the forward problem plus the incoming
+// gradients, the gradient outputs and the checkpoint workspace.
+struct BwdProblem {
+    Problem p;
+    const float* dout;    // [B, T, H, dv]
+    const float* ds_out;  // [B, H, dv, dk] or null (zero)
+    float* dq;            // [B, T, H, dk]
+    float* dk;            // [B, T, H, dk]
+    float* dv;            // [B, T, H, dv]
+    float* dalpha;        // shaped as alpha
+    float* dbeta;         // [B, T, H]
+    float* ds0;           // [B, H, dv, dk] or null
+    float* ckpt;          // workspace: states every 64 tokens
+};
+size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+hipError_t backward(const BwdProblem& a, hipStream_t st);
+
 // Start state copy/zero for empty sequences (T == 0).
 hipError_t copy_state(const Problem& p, hipStream_t st);
 

@@ -25,7 +25,7 @@ GDN_PATH_VALU, GDN_PATH_MFMA = 0, 1
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_step",
-           "gdn_decode_step_raw",
+           "gdn_decode_step_raw", "gdn_backward", "gdn_backward_workspace_bytes",
            "gdn_workspace_bytes",
            "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_status_str", "gdn_abi_version",
            "gdn_profile_enable", "gdn_profile_read")
@@ -62,6 +62,10 @@ def lib():
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step_raw.argtypes = [i64] * 4 + [i32, i32, i32, f32] + tens + [vp]
     L.gdn_decode_step_raw.restype = ctypes.c_int
+    L.gdn_backward.argtypes = shape + [i32, i32, i32, f32] + [vp] * 14 + [vp, sz, vp]
+    L.gdn_backward.restype = ctypes.c_int
+    L.gdn_backward_workspace_bytes.argtypes = shape
+    L.gdn_backward_workspace_bytes.restype = sz
     L.gdn_workspace_bytes.argtypes = shape + [i32, i32, i32, i32]
     L.gdn_workspace_bytes.restype = sz
     L.gdn_validate.argtypes = shape + [i32, i32, i32, i32, i32]
@@ -103,6 +107,14 @@ def gdn_decode_step(*args):
 
 def gdn_decode_step_raw(*args):
     return lib().gdn_decode_step_raw(*args)
+
+
+def gdn_backward(*args):
+    return lib().gdn_backward(*args)
+
+
+def gdn_backward_workspace_bytes(B, T, H, dk, dv) -> int:
+    return int(lib().gdn_backward_workspace_bytes(B, T, H, dk, dv))
 
 
 def gdn_workspace_bytes(B, T, H, dk, dv, chunk, dtype, gate, n_segments=1) -> int:
@@ -257,6 +269,43 @@ def recurrent_ref(q, k, v, alpha, beta, state0=None, *, order=GDN_PREDICT_THEN_D
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_recurrent_ref")
     return out, state_out
+
+
+def backward(q, k, v, alpha, beta, state0, grad_out, grad_state_out=None, *,
+             order=GDN_PREDICT_THEN_DECAY, scale=1.0, want_grad_state0=True, workspace=None):
+    """Gradients through the forward pass: gdn_backward.
+    grad_out [B,T,H,dv] fp32 = dL/d out; grad_state_out [B,H,dv,dk] fp32 =
+    dL/d S_T or None (zero).  Returns (dq, dk, dv, dalpha, dbeta, dstate0),
+    fp32, shaped like q, k, v, alpha, beta and the state (dstate0 None when
+    not wanted)."""
+    import torch
+    B, T, H, dk, dv, gate = _check(q, k, v, alpha, beta, state0)
+    for t in (grad_out, grad_state_out):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32):
+            raise ValueError("gradients must be contiguous float32 GPU tensors")
+    if grad_out.shape != (B, T, H, dv):
+        raise ValueError("grad_out must be [B,T,H,dv]")
+    if grad_state_out is not None and grad_state_out.shape != (B, H, dv, dk):
+        raise ValueError("grad_state_out must be [B,H,dv,dk]")
+    dev = q.device
+    f32 = torch.float32
+    dq = torch.empty((B, T, H, dk), dtype=f32, device=dev)
+    dkk = torch.empty((B, T, H, dk), dtype=f32, device=dev)
+    dvv = torch.empty((B, T, H, dv), dtype=f32, device=dev)
+    dal = torch.empty(alpha.shape, dtype=f32, device=dev)
+    dbe = torch.empty((B, T, H), dtype=f32, device=dev)
+    ds0 = torch.empty((B, H, dv, dk), dtype=f32, device=dev) if want_grad_state0 else None
+    if workspace is None:
+        n = gdn_backward_workspace_bytes(B, T, H, dk, dv)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    rc = gdn_backward(B, T, H, dk, dv, _dtype_code(q), gate, order, scale,
+                      _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state0),
+                      _ptr(grad_out), _ptr(grad_state_out), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                      _ptr(dal), _ptr(dbe), _ptr(ds0), _ptr(workspace), workspace.numel(),
+                      _stream())
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_backward")
+    return dq, dkk, dvv, dal, dbe, ds0
 
 
 def decode_step(q, k, v, alpha, beta, state=None, *, order=GDN_PREDICT_THEN_DECAY,

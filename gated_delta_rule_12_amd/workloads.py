@@ -156,6 +156,16 @@ def make_raw_inputs(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def make_grads(w: Workload, seed: int | None = None, with_state: bool = True) -> dict:
+    """Upstream gradients for a backward pass over workload w: dout
+    ~ N(0, 1) [B,T,H,dv] and, with_state, dstate ~ N(0, 1) [B,H,dv,dk]
+    (else None); fp32, from their own PCG64 stream (seed + 1 by default)."""
+    rng = np.random.Generator(np.random.PCG64((w.seed + 1) if seed is None else seed))
+    dout = rng.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
+    ds = rng.standard_normal((w.B, w.H, w.dv, w.dk)).astype(np.float32) if with_state else None
+    return {"dout": dout, "dstate": ds}
+
+
 def make_inputs_device(w: Workload, device="cuda") -> dict:
     """Workloads too large to draw on the host: the same recipe as
     make_inputs, drawn on the device by torch's seeded Philox generator (so

@@ -152,6 +152,44 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
                         const float* state_in, float* out, float* state_out, void* stream);
 
 /*
+ * gdn_backward — gradients of a scalar loss L through the forward pass (the
+ * token recurrence of either order and gate kind above): given
+ * grad_out = dL/d out and grad_state_out = dL/d S_T (NULL: zero), it writes
+ * dL/dq, dL/dk, dL/dv, dL/dalpha, dL/dbeta and grad_state0 = dL/d S_0 (NULL:
+ * not wanted).  The pages fix the forward recurrence only; the gradients are
+ * its chain rule, token by token in reverse.  The forward states are
+ * recomputed from boundary-state checkpoints every 64 tokens that the call
+ * itself stores in the workspace.
+ *   q, k, v, alpha, beta, state0  as for gdn_chunk_fwd (state0 NULL: zero)
+ *   grad_out        [B, T, H, dv] fp32
+ *   grad_state_out  [B, H, dv, dk] fp32 or NULL
+ *   grad_q, grad_k  [B, T, H, dk] fp32;  grad_v [B, T, H, dv] fp32
+ *   grad_alpha      shaped as alpha, fp32;  grad_beta [B, T, H] fp32
+ *   grad_state0     [B, H, dv, dk] fp32 or NULL
+ *   workspace       at least gdn_backward_workspace_bytes(B, T, H, dk, dv)
+ *                   bytes (4 dk dv ceil(T / 64) per (batch, head)); may be
+ *                   NULL when T = 0
+ * The gradient outputs must not alias any input or each other.  dq, dk,
+ * dalpha and dbeta are sums over state rows that several workgroups add into
+ * with fp32 atomics, so their last bits may differ between runs.
+ * Alignment: q and k on 8 bytes (bf16) or 16 bytes (fp32); state0,
+ * grad_state_out, grad_state0 and a channel alpha on 16 bytes; the rest on
+ * their element size; otherwise GDN_E_ARG.  dk, dv as for gdn_chunk_fwd;
+ * other statuses as above.
+ */
+int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                 int32_t dtype, int32_t gate, int32_t order, float scale,
+                 const void* q, const void* k, const void* v,
+                 const float* alpha, const float* beta, const float* state0,
+                 const float* grad_out, const float* grad_state_out,
+                 float* grad_q, float* grad_k, float* grad_v, float* grad_alpha,
+                 float* grad_beta, float* grad_state0,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes gdn_backward needs (0 for an invalid or unsupported shape). */
+size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+
+/*
  * gdn_seqpar_fwd — increment-and-correct sequence parallelism (How to
  * Implement Sequence Parallelism in DeltaNet, papercache notes, sections
  * "parallel algorithm derivation" and "CP=4").  The chunks of every sequence

@@ -218,3 +218,56 @@ def test_forward_entry_points_check_alignment_and_segment_count():
     # segment counts below one
     for n in (0, -3):
         assert gdn.gdn_seqpar_fwd(*shape, n, *ok, fake, 1 << 30, nul) == gdn.GDN_E_SHAPE
+
+
+def test_backward_rejects_bad_arguments_before_any_launch():
+    """gdn_backward's checks return before anything is enqueued (fake, never
+    dereferenced pointers): required tensors, alignment, workspace size,
+    enums and shapes."""
+    import ctypes
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    odd16 = ctypes.c_void_p(0x1008)
+    odd4 = ctypes.c_void_p(0x1002)
+    B, T, H, dk, dv = 1, 100, 2, 64, 64
+    head = (B, T, H, dk, dv, gdn.GDN_BF16, gdn.GDN_GATE_SCALAR, gdn.GDN_PREDICT_THEN_DECAY, 1.0)
+    need = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv)
+    assert need == 4 * dk * dv * 2 * B * H  # two checkpoints of 64 tokens per (batch, head)
+    assert gdn.gdn_backward_workspace_bytes(B, T, H, 60, dv) == 0
+    ok = [fake] * 14  # q k v alpha beta state0 dout dstate dq dk dv dalpha dbeta dstate0
+
+    def call(ptrs, ws=fake, nbytes=need, head=head):
+        return gdn.gdn_backward(*head, *ptrs, ws, nbytes, nul)
+
+    # an aligned call gets past every check but the workspace size
+    assert call(ok, nbytes=need - 1) == gdn.GDN_E_WORKSPACE
+    assert call(ok, ws=nul) == gdn.GDN_E_WORKSPACE
+    # required tensors (state0, dstate and dstate0 are optional)
+    for idx in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):
+        ptrs = list(ok)
+        ptrs[idx] = nul
+        assert call(ptrs) == gdn.GDN_E_ARG, idx
+    # 16-byte pieces: states; 8-byte: bf16 q, k; per element: the rest
+    for idx in (5, 7, 13):
+        ptrs = list(ok)
+        ptrs[idx] = odd16
+        assert call(ptrs) == gdn.GDN_E_ARG, idx
+    for idx in (0, 1):
+        ptrs = list(ok)
+        ptrs[idx] = ctypes.c_void_p(0x1004)
+        assert call(ptrs) == gdn.GDN_E_ARG, idx
+    for idx in (3, 4, 6, 8, 9, 10, 11, 12):
+        ptrs = list(ok)
+        ptrs[idx] = odd4
+        assert call(ptrs) == gdn.GDN_E_ARG, idx
+    chan = head[:6] + (gdn.GDN_GATE_CHANNEL,) + head[7:]
+    ptrs = list(ok)
+    ptrs[3] = odd16
+    assert call(ptrs, head=chan) == gdn.GDN_E_ARG
+    # enums and sizes
+    assert call(ok, head=head[:5] + (7,) + head[6:]) == gdn.GDN_E_ARG
+    assert call(ok, head=head[:7] + (5,) + head[8:]) == gdn.GDN_E_ARG
+    assert call(ok, head=(1, 100, 2, 72, 64) + head[5:]) == gdn.GDN_E_UNSUPPORTED
+    assert call(ok, head=(1, -1, 2, 64, 64) + head[5:]) == gdn.GDN_E_SHAPE
+    # empty batch: nothing to do
+    assert gdn.gdn_backward(0, T, H, dk, dv, *head[5:], *([nul] * 14), nul, 0, nul) == gdn.GDN_OK
