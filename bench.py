@@ -12,7 +12,8 @@ Default workload: main-bf16 (B=2, H=16, T=8192, dk=dv=128, chunk 64, scalar
 gate, start state N(0, 0.02^2)).  The long workload runs the sequence-parallel
 entry point (8 segments) and also reports the single-stream time beside it.
 --workload decode-bf16 times gdn_decode_step instead: one token for each of
-256 x 16 persistent states, updated in place.
+256 x 16 persistent states, updated in place.  --backward times gdn_backward
+(gradients through the recurrence) on the workload.
 """
 from __future__ import annotations
 
@@ -236,6 +237,106 @@ def bench_decode(args, w):
     print(json.dumps(res), flush=True)
 
 
+def backward_bytes(w) -> float:
+    """HBM bytes gdn_backward must move: read q, k, v, the gates, beta and
+    dL/dout, write dq, dk, dv, dalpha, dbeta (per head-token); read the start
+    state and dL/dS_T and write dL/dS_0 (per head)."""
+    s_in = 2 if w.dtype == "bf16" else 4
+    gate = 4 * w.dk if w.gate == "channel" else 4
+    per_tok = ((2 * w.dk + w.dv) * s_in + gate + 4 + 4 * w.dv
+               + 8 * w.dk + 4 * w.dv + gate + 4)
+    return float(per_tok * w.B * w.T * w.H + 12 * w.dk * w.dv * w.B * w.H)
+
+
+def cpu_baseline_backward(w, inp, gr, max_threads=16, target_s=10.0):
+    """Time the oracle's backward on (batch, head) slices of the workload,
+    the first n_tok tokens of each."""
+    import numpy as np
+
+    import oracle
+    cores = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    g = oracle.GATE_SCALAR if w.gate == "scalar" else oracle.GATE_CHANNEL
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)][:cores]
+    n_tok = min(w.T, 1024)
+    pick = lambda x: np.stack([x[b, :n_tok, h] for b, h in sel])[:, :, None]
+    args = [pick(inp[n]) for n in ("q", "k", "v", "alpha", "beta")]
+    s0 = np.stack([inp["state0"][b, h] for b, h in sel])[:, None]
+    ds = np.stack([gr["dstate"][b, h] for b, h in sel])[:, None]
+    dout = pick(gr["dout"])
+    reps, dt = 0, 0.0
+    while dt < target_s and reps < 1000:
+        t = time.perf_counter()
+        oracle.backward(*args, s0, dout, ds, gate=g, threads=cores)
+        dt += time.perf_counter() - t
+        reps += 1
+    return {"value": reps * len(sel) * n_tok / w.H / dt, "unit": "tokens/sec", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} x {len(sel)} (batch,head) slices x {n_tok} tokens of {w.name}, "
+                      f"fp64 backward over stored states, {dt:.2f} s; tokens/s = head-tokens/s / H"}
+
+
+def bench_backward(args, w):
+    """One step = gdn_backward over the whole batch (dL/dout and dL/dS_T
+    given, dL/dS_0 wanted)."""
+    import torch
+
+    from gated_delta_rule_12_amd import gdn
+    from gated_delta_rule_12_amd.workloads import make_grads, make_inputs, to_device
+    inp = make_inputs(w)
+    gr = make_grads(w)
+    d = to_device(inp, w, "cuda")
+    g_out = torch.from_numpy(gr["dout"]).cuda()
+    g_st = torch.from_numpy(gr["dstate"]).cuda()
+    ws = torch.empty(max(1, gdn.gdn_backward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], g_out, g_st,
+                     workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gdn.gdn_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern = gdn.gdn_profile_read()
+    gdn.gdn_profile_enable(False)
+    k_us = 1e3 * kern["k_backward"][0] / kern["k_backward"][1]
+    abytes = backward_bytes(w)
+    achieved = abytes / (k_us * 1e-6) / 1e9
+    log(f"step {ms * 1e3:.1f} us, k_backward {k_us:.1f} us per launch")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, inp, gr)
+    res = {"metric": "backward tokens/sec (gradients through the gated-delta recurrence, H=16 d=128 T=8K)",
+           "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/sec", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                      "gate": w.gate, "input_dtype": w.dtype, "entry": "gdn_backward",
+                      "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": stored_traffic(w.name + "-backward", "k_backward"),
+                        "kernel": "k_backward",
+                        "kernel_timing": "HIP events around each launch, in a second run of the same steps after the timed region",
+                        "kernel_avg_launch_us": round(k_us, 2), "algorithmic_bytes": abytes,
+                        "kernel_us_per_step": {n: round(1e3 * v[0] / args.steps, 2)
+                                               for n, v in kern.items()},
+                        "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1)},
+           "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +348,8 @@ def main():
     ap.add_argument("--segments", type=int, default=None,
                     help="sequence-parallel segments (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time gdn_backward on the workload instead of the forward")
     ap.add_argument("--no-single-stream", action="store_true",
                     help="sequence parallel: skip the single-stream comparison (for kernel traces)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -269,6 +372,9 @@ def main():
     w = workload(int(args.workload) if args.workload.isdigit() else args.workload)
     if w.name == "decode-bf16":
         bench_decode(args, w)
+        return
+    if args.backward:
+        bench_backward(args, w)
         return
     # None: gdn_chunk_fwd with the library's schedule; a count: gdn_seqpar_fwd
     G = args.segments if args.segments is not None else (w.n_segments if w.n_segments > 1 else None)

@@ -17,13 +17,15 @@
 // (dalpha = dd for a channel gate, its sum over channels for a scalar gate).
 //
 // Schedule (recompute from boundary-state checkpoints): a workgroup owns a
-// block of state rows of one (batch, head).  Phase A runs the recurrence
-// forward over the sequence and stores its rows of the state every kCk
-// tokens in the workspace.  Phase B walks the checkpoint intervals backwards:
-// it recomputes the interval forward from its checkpoint, keeping the state
-// at every kSub-th token in LDS, then for each run of kSub tokens (last
-// first) recomputes the kSub states into registers and carries dL/dS back
-// through them.  The per-token sums over rows (dq, dk, dalpha, dbeta) are
+// block of state rows of one (batch, head) and works in runs of kSub tokens,
+// whose inputs (q, k, gates, beta and the block's v and dL/dout) are staged
+// into LDS by one coalesced load of the whole workgroup, issued while the
+// previous run computes.  Phase A runs the recurrence forward over the
+// sequence and stores its rows of the state every kCk tokens in the
+// workspace.  Phase B walks the checkpoint intervals backwards: it
+// recomputes the interval forward from its checkpoint, keeping the state at
+// every run start in LDS, then for each run (last first) recomputes the
+// run's states into registers and carries dL/dS back through them.  The per-token sums over rows (dq, dk, dalpha, dbeta) are
 // reduced within the workgroup through LDS and added into the outputs with
 // fp32 atomics (one add per workgroup and element, so the order of the row
 // blocks' contributions, and with it the last bits, may vary between runs).
@@ -96,52 +98,131 @@ struct Tok {
     float4 k, q, d;
     float beta;
     float v[kRows];
+    float dout[kRows];
+};
+
+// LDS of a workgroup: the inputs of one run of kSub tokens (fp32), the
+// per-token partial sums of a run, and the states at the runs' starts
+template <int LPR, int RB>
+struct BwdShared {
+    static constexpr int KD = 4 * LPR;  // largest dk of this lane layout
+    float tq[kSub][KD], tk[kSub][KD], td[kSub][KD];
+    float tbeta[kSub], talpha[kSub];
+    float tv[kSub][RB], tdo[kSub][RB];
+    float4 vec[4][kSub][3][LPR];        // [wave][token][dq | dk | dd][piece]
+    float sc[4][kSub][2];               // dbeta, dalpha (scalar gate)
+    float4 sub[kSubs][kRows][kThreads];
 };
 
 template <int DT, int LPR, bool CH, bool DTPO>
 struct Bwd {
     static constexpr int RPW = 64 / LPR;             // rows per wave and pass
     static constexpr int RB = 4 * RPW * kRows;       // rows per workgroup
+    static constexpr int KD = 4 * LPR;
+    static constexpr int QP = (kSub * KD / 4 + kThreads - 1) / kThreads;  // staged pieces per thread
+    static constexpr int VP = (kSub * RB + kThreads - 1) / kThreads;
+    using Sh = BwdShared<LPR, RB>;
     const BwdProblem& a;
+    Sh& sh;
     int64_t b, h, bh;
-    int c, w, l;
+    int rb, c, w, l, tid;
     bool col;
-    int r[kRows];
+    int r[kRows], rr[kRows];
     bool on[kRows];
 
-    __device__ Bwd(const BwdProblem& a_, int64_t bh_, int rb) : a(a_) {
+    __device__ Bwd(const BwdProblem& a_, Sh& sh_, int64_t bh_, int rb_) : a(a_), sh(sh_) {
         const Problem& p = a.p;
         bh = bh_;
+        rb = rb_;
         b = bh / p.H;
         h = bh - b * p.H;
-        const int tid = threadIdx.x;
+        tid = threadIdx.x;
         w = tid >> 6;
         l = tid & 63;
         c = l % LPR;
         col = 4 * c < p.dk;
 #pragma unroll
         for (int j = 0; j < kRows; ++j) {
-            r[j] = rb * RB + (j * 4 + w) * RPW + l / LPR;
+            rr[j] = (j * 4 + w) * RPW + l / LPR;
+            r[j] = rb * RB + rr[j];
             on[j] = r[j] < p.dv;
         }
     }
 
-    __device__ Tok load(int64_t t) const {
+    // ---- staging of a run's inputs: loads into registers, then LDS
+    struct Stage {
+        float4 q[QP], k[QP], d[QP];
+        float beta, alpha;
+        float v[VP], dout[VP];
+    };
+    __device__ void stage_load(Stage& s, int64_t ts, int m) const {
         const Problem& p = a.p;
-        const int64_t th = (b * p.T + t) * p.H + h;  // token-head index
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int P4 = KD / 4;
+#pragma unroll
+        for (int i = 0; i < QP; ++i) {
+            const int e = tid + kThreads * i, u = e / P4, c4 = e % P4;
+            const bool ok = e < kSub * P4 && u < m && 4 * c4 < p.dk;
+            const int64_t th = (b * p.T + ts + u) * p.H + h;
+            s.q[i] = ok ? ld4<DT>(p.q, th * p.dk + 4 * c4) : z4;
+            s.k[i] = ok ? ld4<DT>(p.k, th * p.dk + 4 * c4) : z4;
+            if constexpr (CH) s.d[i] = ok ? *reinterpret_cast<const float4*>(p.alpha + th * p.dk + 4 * c4) : z4;
+        }
+        const int64_t th0 = (b * p.T + ts + (tid < m ? tid : 0)) * p.H + h;
+        s.beta = tid < m ? p.beta[th0] : 0.f;
+        s.alpha = (!CH && tid < m) ? p.alpha[th0] : 0.f;
+#pragma unroll
+        for (int i = 0; i < VP; ++i) {
+            const int e = tid + kThreads * i, u = e / RB, q = e % RB;
+            const bool ok = e < kSub * RB && u < m && rb * RB + q < p.dv;
+            const int64_t th = (b * p.T + ts + u) * p.H + h;
+            s.v[i] = ok ? gdn_ld<DT>(p.v, th * p.dv + rb * RB + q) : 0.f;
+            s.dout[i] = ok ? a.dout[th * p.dv + rb * RB + q] : 0.f;
+        }
+    }
+    __device__ void stage_store(const Stage& s) const {
+        const int P4 = KD / 4;
+#pragma unroll
+        for (int i = 0; i < QP; ++i) {
+            const int e = tid + kThreads * i;
+            if (e < kSub * P4) {
+                const int u = e / P4, c4 = e % P4;
+                *reinterpret_cast<float4*>(&sh.tq[u][4 * c4]) = s.q[i];
+                *reinterpret_cast<float4*>(&sh.tk[u][4 * c4]) = s.k[i];
+                if constexpr (CH) *reinterpret_cast<float4*>(&sh.td[u][4 * c4]) = s.d[i];
+            }
+        }
+        if (tid < kSub) {
+            sh.tbeta[tid] = s.beta;
+            sh.talpha[tid] = s.alpha;
+        }
+#pragma unroll
+        for (int i = 0; i < VP; ++i) {
+            const int e = tid + kThreads * i;
+            if (e < kSub * RB) {
+                sh.tv[e / RB][e % RB] = s.v[i];
+                sh.tdo[e / RB][e % RB] = s.dout[i];
+            }
+        }
+    }
+
+    // token u of the staged run
+    __device__ Tok tok(int u) const {
         Tok x;
-        x.k = col ? ld4<DT>(p.k, th * p.dk + 4 * c) : z4;
-        x.q = col ? ld4<DT>(p.q, th * p.dk + 4 * c) : z4;
+        x.k = *reinterpret_cast<const float4*>(&sh.tk[u][4 * c]);
+        x.q = *reinterpret_cast<const float4*>(&sh.tq[u][4 * c]);
         if constexpr (CH) {
-            x.d = col ? *reinterpret_cast<const float4*>(p.alpha + th * p.dk + 4 * c) : z4;
+            x.d = *reinterpret_cast<const float4*>(&sh.td[u][4 * c]);
         } else {
-            const float g = p.alpha[th];
+            const float g = sh.talpha[u];
             x.d = make_float4(g, g, g, g);
         }
-        x.beta = p.beta[th];
+        x.beta = sh.tbeta[u];
 #pragma unroll
-        for (int j = 0; j < kRows; ++j) x.v[j] = on[j] ? gdn_ld<DT>(p.v, th * p.dv + r[j]) : 0.f;
+        for (int j = 0; j < kRows; ++j) {
+            x.v[j] = sh.tv[u][rr[j]];
+            x.dout[j] = sh.tdo[u][rr[j]];
+        }
         return x;
     }
 
@@ -162,89 +243,129 @@ struct Bwd {
     __device__ int64_t roff(int j) const { return (int64_t)r[j] * a.p.dk + 4 * c; }
 };
 
-// per-token partial sums of the workgroup: [wave][token of the run][dq | dk | dd][dk]
-struct BwdShared {
-    float4 vec[4][kSub][3][kMaxD / 4];
-    float sc[4][kSub][2];                 // dbeta, dalpha (scalar gate)
-    float4 sub[kSubs][kRows][kThreads];   // states at the runs' starts
+// The order in which a workgroup visits runs of kSub tokens (R = run index):
+// phase A, R = 0 .. NR - 1 forward; then for every checkpoint interval ck,
+// last first, with nsub runs: forward over its runs 0 .. nsub - 2 (storing
+// the run starts), then backward over runs nsub - 1 .. 0.
+struct Visit {
+    int kind;    // 0 phase A, 1 forward inside an interval, 2 backward
+    int64_t R;   // run
+    int pos;     // run within its interval
+    int64_t ck;  // interval
 };
+__device__ __forceinline__ Visit visit_of(int64_t vi, int64_t T) {
+    const int64_t NR = (T + kSub - 1) / kSub, NCk = (T + kCk - 1) / kCk;
+    Visit v;
+    if (vi < NR) {
+        v.kind = 0;
+        v.R = vi;
+        v.pos = (int)(vi % kSubs);
+        v.ck = vi / kSubs;
+        return v;
+    }
+    int64_t j = vi - NR;
+    const int64_t ckl = NCk - 1;
+    const int nsl = (int)((T - ckl * kCk + kSub - 1) / kSub);
+    int nsub, local;
+    if (j < 2 * nsl - 1) {
+        v.ck = ckl;
+        nsub = nsl;
+        local = (int)j;
+    } else {
+        j -= 2 * nsl - 1;
+        v.ck = ckl - 1 - j / (2 * kSubs - 1);
+        nsub = kSubs;
+        local = (int)(j % (2 * kSubs - 1));
+    }
+    if (local < nsub - 1) {
+        v.kind = 1;
+        v.pos = local;
+    } else {
+        v.kind = 2;
+        v.pos = 2 * (nsub - 1) - local;
+    }
+    v.R = v.ck * kSubs + v.pos;
+    return v;
+}
 
 template <int DT, int LPR, bool CH, bool DTPO>
 __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
     using K = Bwd<DT, LPR, CH, DTPO>;
-    __shared__ BwdShared sh;
+    __shared__ typename K::Sh sh;
     const Problem& p = a.p;
     const int64_t bh = blockIdx.x / nrb;
-    const int rb = (int)(blockIdx.x % nrb);
-    const K k(a, bh, rb);
+    const K k(a, sh, bh, (int)(blockIdx.x % nrb));
     const int tid = threadIdx.x;
     const int64_t T = p.T;
-    const int64_t NCk = (T + kCk - 1) / kCk;
+    const int64_t NR = (T + kSub - 1) / kSub, NCk = (T + kCk - 1) / kCk;
+    const int64_t NV = T > 0 ? NR + (2 * ((T - (NCk - 1) * kCk + kSub - 1) / kSub) - 1) + (2 * kSubs - 1) * (NCk - 1) : 0;
     const int64_t DD = p.dv * p.dk;
     float* ckpt = a.ckpt + bh * NCk * DD;
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    // ---- phase A: forward, a checkpoint of the rows every kCk tokens
-    float4 S[kRows];
+    float4 S[kRows], Gd[kRows];
 #pragma unroll
-    for (int j = 0; j < kRows; ++j)
+    for (int j = 0; j < kRows; ++j) {
         S[j] = (k.on[j] && k.col && p.s0) ? *reinterpret_cast<const float4*>(p.s0 + k.off(j)) : z4;
-    {
-        Tok nx = T > 0 ? k.load(0) : Tok{};
-        for (int64_t t = 0; t < T; ++t) {
-            const Tok x = nx;
-            if (t + 1 < T) nx = k.load(t + 1);
-            if (t % kCk == 0) {
+        Gd[j] = (k.on[j] && k.col && a.ds_out) ? *reinterpret_cast<const float4*>(a.ds_out + k.off(j)) : z4;
+    }
+    typename K::Stage stg;
+    if (NV > 0) {
+        const Visit v0 = visit_of(0, T);
+        k.stage_load(stg, v0.R * kSub, (int)min<int64_t>(kSub, T - v0.R * kSub));
+        k.stage_store(stg);
+    }
+    __syncthreads();
+    for (int64_t vi = 0; vi < NV; ++vi) {
+        const Visit v = visit_of(vi, T);
+        const int64_t ts = v.R * kSub;
+        const int m = (int)min<int64_t>(kSub, T - ts);
+        // the next visit's inputs are fetched while this one computes
+        if (vi + 1 < NV) {
+            const Visit nv = visit_of(vi + 1, T);
+            k.stage_load(stg, nv.R * kSub, (int)min<int64_t>(kSub, T - nv.R * kSub));
+        }
+        if (v.kind == 0) {
+            // phase A: checkpoints every kCk tokens
+            if (v.pos == 0) {
 #pragma unroll
                 for (int j = 0; j < kRows; ++j)
-                    if (k.on[j] && k.col)
-                        *reinterpret_cast<float4*>(ckpt + (t / kCk) * DD + k.roff(j)) = S[j];
+                    if (k.on[j] && k.col) *reinterpret_cast<float4*>(ckpt + v.ck * DD + k.roff(j)) = S[j];
             }
-            float4 Sn[kRows];
-            k.step(S, Sn, x);
+            for (int u = 0; u < m; ++u) {
+                float4 Sn[kRows];
+                k.step(S, Sn, k.tok(u));
 #pragma unroll
-            for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
-        }
-    }
-
-    // ---- phase B: dL/dS carried back from the end
-    float4 Gd[kRows];
-#pragma unroll
-    for (int j = 0; j < kRows; ++j)
-        Gd[j] = (k.on[j] && k.col && a.ds_out) ? *reinterpret_cast<const float4*>(a.ds_out + k.off(j)) : z4;
-
-    for (int64_t ck = NCk - 1; ck >= 0; --ck) {
-        const int64_t t0 = ck * kCk;
-        const int n = (int)min<int64_t>(kCk, T - t0);
-        // the interval forward from its checkpoint (each thread reads back
-        // the elements it wrote), the run starts into LDS
-#pragma unroll
-        for (int j = 0; j < kRows; ++j)
-            S[j] = (k.on[j] && k.col) ? *reinterpret_cast<const float4*>(ckpt + ck * DD + k.roff(j)) : z4;
-        const int nsub = (n + kSub - 1) / kSub;
-        const int last = (nsub - 1) * kSub;  // first token of the last run
-        for (int u = 0;; ++u) {
-            if (u % kSub == 0) {
-#pragma unroll
-                for (int j = 0; j < kRows; ++j) sh.sub[u / kSub][j][tid] = S[j];
+                for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
             }
-            if (u == last) break;  // (the last run's states are recomputed below)
-            float4 Sn[kRows];
-            k.step(S, Sn, k.load(t0 + u));
+        } else if (v.kind == 1) {
+            // forward inside an interval (each thread reads back the
+            // elements it wrote): the start of the next run into LDS
+            if (v.pos == 0) {
 #pragma unroll
-            for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
-        }
-        for (int sb = nsub - 1; sb >= 0; --sb) {
-            const int64_t ts = t0 + (int64_t)sb * kSub;
-            const int m = min(kSub, n - sb * kSub);
-            // the run's states, St[u] before token ts + u
+                for (int j = 0; j < kRows; ++j)
+                    S[j] = (k.on[j] && k.col) ? *reinterpret_cast<const float4*>(ckpt + v.ck * DD + k.roff(j)) : z4;
+            }
+            for (int u = 0; u < m; ++u) {
+                float4 Sn[kRows];
+                k.step(S, Sn, k.tok(u));
+#pragma unroll
+                for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
+            }
+#pragma unroll
+            for (int j = 0; j < kRows; ++j) sh.sub[v.pos + 1][j][tid] = S[j];
+        } else {
+            // backward over the run: its states into registers, St[u] before
+            // token ts + u, then dL/dS carried back through them
             float4 St[kSub + 1][kRows];
 #pragma unroll
-            for (int j = 0; j < kRows; ++j) St[0][j] = sh.sub[sb][j][tid];
+            for (int j = 0; j < kRows; ++j)
+                St[0][j] = v.pos == 0 ? ((k.on[j] && k.col) ? *reinterpret_cast<const float4*>(ckpt + v.ck * DD + k.roff(j)) : z4)
+                                      : sh.sub[v.pos][j][tid];
 #pragma unroll
             for (int u = 0; u < kSub; ++u) {
                 if (u < m) {
-                    k.step(St[u], St[u + 1], k.load(ts + u));
+                    k.step(St[u], St[u + 1], k.tok(u));
                 } else {
 #pragma unroll
                     for (int j = 0; j < kRows; ++j) St[u + 1][j] = St[u][j];
@@ -253,14 +374,13 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
 #pragma unroll
             for (int u = kSub - 1; u >= 0; --u) {
                 if (u >= m) continue;
-                const int64_t t = ts + u;
-                const int64_t th = (k.b * T + t) * p.H + k.h;
-                const Tok x = k.load(t);
+                const int64_t th = (k.b * T + ts + u) * p.H + k.h;
+                const Tok x = k.tok(u);
                 float4 dkp = z4, dqp = z4, ddp = z4;
                 float dbp = 0.f;
 #pragma unroll
                 for (int j = 0; j < kRows; ++j) {
-                    const float dor = k.on[j] ? a.dout[th * p.dv + k.r[j]] : 0.f;
+                    const float dor = x.dout[j];
                     const float4 X = DTPO ? mul4(St[u][j], x.d) : St[u][j];
                     const float pr = row_sum<LPR>(dot4(X, x.k));
                     const float e = x.beta * (x.v[j] - pr);
@@ -268,17 +388,17 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
                     const float gk = row_sum<LPR>(dot4(G, x.k));
                     if (k.on[j] && k.c == 0) a.dv[th * p.dv + k.r[j]] = x.beta * gk;
                     dbp += gk * (x.v[j] - pr);
-                    dkp = add4(dkp, axpy4(e, G, make_float4(-x.beta * gk * X.x, -x.beta * gk * X.y,
-                                                            -x.beta * gk * X.z, -x.beta * gk * X.w)));
+                    const float bg = x.beta * gk;
+                    dkp = add4(dkp, make_float4(e * G.x - bg * X.x, e * G.y - bg * X.y, e * G.z - bg * X.z,
+                                                e * G.w - bg * X.w));
                     dqp = axpy4(p.scale * dor, St[u + 1][j], dqp);
-                    const float4 bk = make_float4(x.beta * gk * x.k.x, x.beta * gk * x.k.y,
-                                                  x.beta * gk * x.k.z, x.beta * gk * x.k.w);
                     if constexpr (!DTPO) {
                         ddp = add4(ddp, mul4(G, St[u][j]));
-                        Gd[j] = make_float4(G.x * x.d.x - bk.x, G.y * x.d.y - bk.y, G.z * x.d.z - bk.z,
-                                            G.w * x.d.w - bk.w);
+                        Gd[j] = make_float4(G.x * x.d.x - bg * x.k.x, G.y * x.d.y - bg * x.k.y,
+                                            G.z * x.d.z - bg * x.k.z, G.w * x.d.w - bg * x.k.w);
                     } else {
-                        const float4 dX = make_float4(G.x - bk.x, G.y - bk.y, G.z - bk.z, G.w - bk.w);
+                        const float4 dX = make_float4(G.x - bg * x.k.x, G.y - bg * x.k.y, G.z - bg * x.k.z,
+                                                      G.w - bg * x.k.w);
                         ddp = add4(ddp, mul4(dX, St[u][j]));
                         Gd[j] = mul4(dX, x.d);
                     }
@@ -318,18 +438,22 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
                     atomicAdd(a.dbeta + th, s0);
                     if constexpr (!CH) atomicAdd(a.dalpha + th, s1);
                 } else {
-                    const int vi = f / P4, c4 = f % P4;
-                    float4 s = sh.vec[0][u][vi][c4];
+                    const int vi2 = f / P4, c4 = f % P4;
+                    float4 s = sh.vec[0][u][vi2][c4];
 #pragma unroll
-                    for (int ww = 1; ww < 4; ++ww) s = add4(s, sh.vec[ww][u][vi][c4]);
-                    float* dst = (vi == 0 ? a.dq : vi == 1 ? a.dk : a.dalpha) + th * p.dk + 4 * c4;
+                    for (int ww = 1; ww < 4; ++ww) s = add4(s, sh.vec[ww][u][vi2][c4]);
+                    float* dst = (vi2 == 0 ? a.dq : vi2 == 1 ? a.dk : a.dalpha) + th * p.dk + 4 * c4;
                     atomicAdd(dst + 0, s.x);
                     atomicAdd(dst + 1, s.y);
                     atomicAdd(dst + 2, s.z);
                     atomicAdd(dst + 3, s.w);
                 }
             }
-            __syncthreads();  // partial sums read; LDS free for the next run
+        }
+        __syncthreads();  // the staged run (and partial sums) read
+        if (vi + 1 < NV) {
+            k.stage_store(stg);
+            __syncthreads();
         }
     }
     if (a.ds0) {
