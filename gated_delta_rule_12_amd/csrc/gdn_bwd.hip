@@ -60,6 +60,15 @@ __device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
     }
 }
 
+// a 16-byte load from global memory, typed so: a conditional load must not
+// become a load through a pointer chosen between this address and a
+// zero-filled stack slot (a generic load, which every LDS wait then waits for)
+typedef float f32x4g __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ldg4(const float* p) {
+    const f32x4g x = *(const __attribute__((address_space(1))) f32x4g*)(p);
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+
 __device__ __forceinline__ float dot4(const float4& a, const float4& b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
@@ -150,7 +159,9 @@ struct Bwd {
     static constexpr int QP = (kSub * KD / 4 + kThreads - 1) / kThreads;  // staged pieces per thread
     static constexpr int VP = (kSub * RB + kThreads - 1) / kThreads;
     using Sh = BwdShared<LPR, RB>;
-    const BwdProblem& a;
+    // (by value: a reference to the kernel argument would put it in scratch
+    // memory and turn every pointer read from it into a generic one)
+    const BwdProblem a;
     Sh& sh;
     int64_t b, h, bh;
     int rb, c, w, l, tid;
@@ -334,8 +345,8 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
     float4 S[kRows], Gd[kRows];
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
-        S[j] = (k.on[j] && k.col && p.s0) ? *reinterpret_cast<const float4*>(p.s0 + k.off(j)) : z4;
-        Gd[j] = (k.on[j] && k.col && a.ds_out) ? *reinterpret_cast<const float4*>(a.ds_out + k.off(j)) : z4;
+        S[j] = (k.on[j] && k.col && p.s0) ? ldg4(p.s0 + k.off(j)) : z4;
+        Gd[j] = (k.on[j] && k.col && a.ds_out) ? ldg4(a.ds_out + k.off(j)) : z4;
     }
     typename K::Stage stg;
     if (NV > 0) {
@@ -348,6 +359,17 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
         const Visit v = visit_of(vi, T);
         const int64_t ts = v.R * kSub;
         const int m = (int)min<int64_t>(kSub, T - ts);
+        // the visit's start state (from a checkpoint: read before the next
+        // visit's inputs are requested, so that waiting for it does not wait
+        // for them)
+        if (v.kind != 0 && v.pos == 0) {
+#pragma unroll
+            for (int j = 0; j < kRows; ++j)
+                S[j] = (k.on[j] && k.col) ? ldg4(ckpt + v.ck * DD + k.roff(j)) : z4;
+        } else if (v.kind == 2) {
+#pragma unroll
+            for (int j = 0; j < kRows; ++j) S[j] = sh.sub[v.pos][j][tid];
+        }
         // the next visit's inputs are fetched while this one computes
         if (vi + 1 < NV) {
             const Visit nv = visit_of(vi + 1, T);
@@ -367,13 +389,9 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
                 for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
             }
         } else if (v.kind == 1) {
-            // forward inside an interval (each thread reads back the
-            // elements it wrote): the start of the next run into LDS
-            if (v.pos == 0) {
-#pragma unroll
-                for (int j = 0; j < kRows; ++j)
-                    S[j] = (k.on[j] && k.col) ? *reinterpret_cast<const float4*>(ckpt + v.ck * DD + k.roff(j)) : z4;
-            }
+            // forward inside an interval (from the checkpoint, which each
+            // thread reads back where it wrote it): the start of the next run
+            // into LDS
             for (int u = 0; u < m; ++u) {
                 float4 Sn[kRows];
                 k.step(S, Sn, k.tok(u));
@@ -387,9 +405,7 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb) {
             // token ts + u, then dL/dS carried back through them
             float4 St[kSub + 1][kRows];
 #pragma unroll
-            for (int j = 0; j < kRows; ++j)
-                St[0][j] = v.pos == 0 ? ((k.on[j] && k.col) ? *reinterpret_cast<const float4*>(ckpt + v.ck * DD + k.roff(j)) : z4)
-                                      : sh.sub[v.pos][j][tid];
+            for (int j = 0; j < kRows; ++j) St[0][j] = S[j];
 #pragma unroll
             for (int u = 0; u < kSub; ++u) {
                 if (u < m) {
