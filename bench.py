@@ -287,7 +287,8 @@ def bench_backward(args, w):
     d = to_device(inp, w, "cuda")
     g_out = torch.from_numpy(gr["dout"]).cuda()
     g_st = torch.from_numpy(gr["dstate"]).cuda()
-    ws = torch.empty(max(1, gdn.gdn_backward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)),
+    gate = gdn.GDN_GATE_SCALAR if w.gate == "scalar" else gdn.GDN_GATE_CHANNEL
+    ws = torch.empty(max(1, gdn.gdn_backward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, gate)),
                      dtype=torch.uint8, device="cuda")
 
     def step():

@@ -275,10 +275,10 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dt
                          beta_logit, state_in, out, state_out, true, stream);
 }
 
-size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
-    if (validate(B, T, H, dk, dv, 16, GDN_F32, GDN_GATE_SCALAR, GDN_PREDICT_THEN_DECAY, 1) != GDN_OK)
-        return 0;
-    return backward_workspace(B, T, H, dk, dv);
+size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                    int32_t gate) {
+    if (validate(B, T, H, dk, dv, 16, GDN_F32, gate, GDN_PREDICT_THEN_DECAY, 1) != GDN_OK) return 0;
+    return backward_workspace(B, T, H, dk, dv, gate);
 }
 
 int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,
@@ -304,7 +304,7 @@ int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_
         !aligned(grad_out, 4) || !aligned(grad_q, 4) || !aligned(grad_k, 4) || !aligned(grad_v, 4) ||
         !aligned(grad_alpha, 4) || !aligned(grad_beta, 4))
         return GDN_E_ARG;
-    const size_t need = backward_workspace(B, T, H, dk, dv);
+    const size_t need = backward_workspace(B, T, H, dk, dv, gate);
     if (T > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
     BwdProblem a{};
     a.p = make_problem(B, T, H, dk, dv, 16, dtype, gate, order, scale);
@@ -314,6 +314,7 @@ int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_
     a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dalpha = grad_alpha; a.dbeta = grad_beta;
     a.ds0 = grad_state0;
     a.ckpt = static_cast<float*>(workspace);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_ckpt_bytes(B, T, H, dk, dv));
     return finish(backward(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -95,8 +95,10 @@ struct BwdProblem {
     float* dbeta;         // [B, T, H]
     float* ds0;           // [B, H, dv, dk] or null
     float* ckpt;          // workspace: states every 64 tokens
+    float* part;          // workspace: per (row block, token) partial sums
 };
-size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+size_t backward_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate);
 hipError_t backward(const BwdProblem& a, hipStream_t st);
 
 // Start state copy/zero for empty sequences (T == 0).

@@ -64,7 +64,7 @@ def lib():
     L.gdn_decode_step_raw.restype = ctypes.c_int
     L.gdn_backward.argtypes = shape + [i32, i32, i32, f32] + [vp] * 14 + [vp, sz, vp]
     L.gdn_backward.restype = ctypes.c_int
-    L.gdn_backward_workspace_bytes.argtypes = shape
+    L.gdn_backward_workspace_bytes.argtypes = shape + [i32]
     L.gdn_backward_workspace_bytes.restype = sz
     L.gdn_workspace_bytes.argtypes = shape + [i32, i32, i32, i32]
     L.gdn_workspace_bytes.restype = sz
@@ -113,8 +113,8 @@ def gdn_backward(*args):
     return lib().gdn_backward(*args)
 
 
-def gdn_backward_workspace_bytes(B, T, H, dk, dv) -> int:
-    return int(lib().gdn_backward_workspace_bytes(B, T, H, dk, dv))
+def gdn_backward_workspace_bytes(B, T, H, dk, dv, gate=GDN_GATE_SCALAR) -> int:
+    return int(lib().gdn_backward_workspace_bytes(B, T, H, dk, dv, gate))
 
 
 def gdn_workspace_bytes(B, T, H, dk, dv, chunk, dtype, gate, n_segments=1) -> int:
@@ -296,7 +296,7 @@ def backward(q, k, v, alpha, beta, state0, grad_out, grad_state_out=None, *,
     dbe = torch.empty((B, T, H), dtype=f32, device=dev)
     ds0 = torch.empty((B, H, dv, dk), dtype=f32, device=dev) if want_grad_state0 else None
     if workspace is None:
-        n = gdn_backward_workspace_bytes(B, T, H, dk, dv)
+        n = gdn_backward_workspace_bytes(B, T, H, dk, dv, gate)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     rc = gdn_backward(B, T, H, dk, dv, _dtype_code(q), gate, order, scale,
                       _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state0),

@@ -159,19 +159,22 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
  * not wanted).  The pages fix the forward recurrence only; the gradients are
  * its chain rule, token by token in reverse.  The forward states are
  * recomputed from boundary-state checkpoints every 64 tokens that the call
- * itself stores in the workspace.
+ * itself stores in the workspace; the sums over state rows go through the
+ * workspace too (one record per block of rows and token), so the outputs are
+ * written once, in a fixed order.
  *   q, k, v, alpha, beta, state0  as for gdn_chunk_fwd (state0 NULL: zero)
  *   grad_out        [B, T, H, dv] fp32
  *   grad_state_out  [B, H, dv, dk] fp32 or NULL
  *   grad_q, grad_k  [B, T, H, dk] fp32;  grad_v [B, T, H, dv] fp32
  *   grad_alpha      shaped as alpha, fp32;  grad_beta [B, T, H] fp32
  *   grad_state0     [B, H, dv, dk] fp32 or NULL
- *   workspace       at least gdn_backward_workspace_bytes(B, T, H, dk, dv)
- *                   bytes (4 dk dv ceil(T / 64) per (batch, head)); may be
- *                   NULL when T = 0
- * The gradient outputs must not alias any input or each other.  dq, dk,
- * dalpha and dbeta are sums over state rows that several workgroups add into
- * with fp32 atomics, so their last bits may differ between runs.
+ *   workspace       at least gdn_backward_workspace_bytes(B, T, H, dk, dv,
+ *                   gate) bytes (per (batch, head): 4 dk dv ceil(T / 64) of
+ *                   checkpoints and 4 T (2 dk + 4) per block of state rows of
+ *                   sums, 3 dk + 4 for a channel gate; 2.4 GiB on a batch of
+ *                   2 x 16 heads of 8192 tokens at d = 128); may be NULL when
+ *                   T = 0
+ * The gradient outputs must not alias any input or each other.
  * Alignment: q and k on 8 bytes (bf16) or 16 bytes (fp32); state0,
  * grad_state_out, grad_state0 and a channel alpha on 16 bytes; the rest on
  * their element size; otherwise GDN_E_ARG.  dk, dv as for gdn_chunk_fwd;
@@ -186,8 +189,10 @@ int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                  float* grad_beta, float* grad_state0,
                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes gdn_backward needs (0 for an invalid or unsupported shape). */
-size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+/* Workspace bytes gdn_backward needs for that shape and gate kind (0 for an
+ * invalid or unsupported shape or gate). */
+size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                    int32_t gate);
 
 /*
  * gdn_seqpar_fwd — increment-and-correct sequence parallelism (How to

@@ -231,9 +231,17 @@ def test_backward_rejects_bad_arguments_before_any_launch():
     odd4 = ctypes.c_void_p(0x1002)
     B, T, H, dk, dv = 1, 100, 2, 64, 64
     head = (B, T, H, dk, dv, gdn.GDN_BF16, gdn.GDN_GATE_SCALAR, gdn.GDN_PREDICT_THEN_DECAY, 1.0)
-    need = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv)
-    assert need == 4 * dk * dv * 2 * B * H  # two checkpoints of 64 tokens per (batch, head)
-    assert gdn.gdn_backward_workspace_bytes(B, T, H, 60, dv) == 0
+    need = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, gdn.GDN_GATE_SCALAR)
+    # two checkpoints of 64 tokens per (batch, head), and per block of 32 rows
+    # (16 lanes a row at dk = 64) a record of 2 dk + 4 floats per token
+    ckpt = 4 * dk * dv * 2 * B * H
+    part = 4 * B * H * (dv // 32) * T * (2 * dk + 4)
+    align = lambda x: (x + 255) // 256 * 256
+    assert need == align(ckpt) + align(part)
+    chan = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, gdn.GDN_GATE_CHANNEL)
+    assert chan == align(ckpt) + align(4 * B * H * (dv // 32) * T * (3 * dk + 4))
+    assert gdn.gdn_backward_workspace_bytes(B, T, H, 60, dv, 0) == 0
+    assert gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, 5) == 0
     ok = [fake] * 14  # q k v alpha beta state0 dout dstate dq dk dv dalpha dbeta dstate0
 
     def call(ptrs, ws=fake, nbytes=need, head=head):
@@ -260,10 +268,12 @@ def test_backward_rejects_bad_arguments_before_any_launch():
         ptrs = list(ok)
         ptrs[idx] = odd4
         assert call(ptrs) == gdn.GDN_E_ARG, idx
-    chan = head[:6] + (gdn.GDN_GATE_CHANNEL,) + head[7:]
+    chan_head = head[:6] + (gdn.GDN_GATE_CHANNEL,) + head[7:]
     ptrs = list(ok)
     ptrs[3] = odd16
-    assert call(ptrs, head=chan) == gdn.GDN_E_ARG
+    assert call(ptrs, head=chan_head, nbytes=chan) == gdn.GDN_E_ARG
+    # a channel gate needs the larger workspace
+    assert call(ok, head=chan_head, nbytes=need) == gdn.GDN_E_WORKSPACE
     # enums and sizes
     assert call(ok, head=head[:5] + (7,) + head[6:]) == gdn.GDN_E_ARG
     assert call(ok, head=head[:7] + (5,) + head[8:]) == gdn.GDN_E_ARG
