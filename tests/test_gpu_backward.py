@@ -114,3 +114,21 @@ def test_backward_long_sequence_sampled():
                  seed=5401)
     got, ref = run(w, PTD)
     check(got, ref)
+
+
+def test_backward_is_deterministic():
+    """The row blocks' sums are combined in a fixed order: two calls give
+    bit-identical gradients."""
+    import torch
+    w = Workload("bwd-det", B=2, H=2, T=300, dk=128, dv=128, chunk=64, gate="channel",
+                 state0_std=0.3, seed=5501)
+    inp = make_inputs(w)
+    gr = make_grads(w)
+    d = to_device(inp, w)
+    g_out = torch.from_numpy(gr["dout"]).cuda()
+    g_st = torch.from_numpy(gr["dstate"]).cuda()
+    r1 = gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], g_out, g_st)
+    r2 = gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], g_out, g_st)
+    torch.cuda.synchronize()
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
