@@ -334,7 +334,8 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb, in
     using K = Bwd<DT, LPR, CH, DTPO>;
     __shared__ typename K::Sh sh;
     const Problem& p = a.p;
-    const int64_t bh = blockIdx.x / nrb;
+    const int64_t bl = blockIdx.x / nrb;  // (batch, head) pair within the launch
+    const int64_t bh = a.bh0 + bl;
     const K k(a, sh, bh, (int)(blockIdx.x % nrb));
     const int tid = threadIdx.x;
     const int64_t T = p.T;
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb, in
             const int nv = CH ? 3 : 2;
             for (int e = tid; e < m * (nv * P4 + 1); e += kThreads) {
                 const int u = e / (nv * P4 + 1), f = e % (nv * P4 + 1);
-                float* rec = a.part + ((bh * nrb + k.rb) * T + ts + u) * RS;
+                float* rec = a.part + ((bl * nrb + k.rb) * T + ts + u) * RS;
                 if (f == nv * P4) {
                     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -511,12 +512,12 @@ __global__ void k_bwd_reduce(BwdProblem a, int nrb, int RS) {
     const bool ch = p.gate == GDN_GATE_CHANNEL;
     const int nv = ch ? 3 : 2;
     const int P4 = RS / 4;
-    const int64_t n = p.B * p.H * p.T * P4;
+    const int64_t n = a.nbh * p.T * P4;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int f = (int)(i % P4);
-        const int64_t ht = i / P4, bh = ht / p.T, t = ht % p.T;
-        const float* src = a.part + (bh * nrb * p.T + t) * RS + 4 * f;
+        const int64_t ht = i / P4, bl = ht / p.T, t = ht % p.T, bh = a.bh0 + bl;
+        const float* src = a.part + (bl * nrb * p.T + t) * RS + 4 * f;
         float4 s = *reinterpret_cast<const float4*>(src);
         for (int r = 1; r < nrb; ++r) s = add4(s, *reinterpret_cast<const float4*>(src + (int64_t)r * p.T * RS));
         const int64_t b = bh / p.H, h = bh % p.H;
@@ -545,7 +546,7 @@ template <int DT, int LPR, bool CH, bool DTPO>
 hipError_t launch4(const BwdProblem& a, hipStream_t st) {
     constexpr int RB = Bwd<DT, LPR, CH, DTPO>::RB;
     const int nrb = (int)((a.p.dv + RB - 1) / RB);
-    const int64_t grid = a.p.B * a.p.H * nrb;
+    const int64_t grid = a.nbh * nrb;
     static_assert(RB == 4 * (64 / LPR) * kRows, "rows_per_block");
     hipLaunchKernelGGL((k_backward<DT, LPR, CH, DTPO>), dim3((unsigned)grid), dim3(kThreads), 0, st, a,
                        nrb, record_stride(a.p.dk, a.p.gate));
@@ -576,29 +577,50 @@ size_t backward_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
     return align256(sizeof(float) * (size_t)(B * H * NCk) * (size_t)(dk * dv));
 }
 
-size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate) {
+// The records of the row blocks' sums of (batch, head) pairs in a launch;
+// larger batches run in groups of pairs, one launch pair (kernel and
+// reduction) per group, so that this part of the workspace stays within
+// kPartCap however large the batch.
+constexpr size_t kPartCap = size_t(8) << 30;
+size_t part_bytes_per_head(int64_t T, int64_t dk, int64_t dv, int gate) {
     const int RB = rows_per_block(dk);
     const int64_t nrb = (dv + RB - 1) / RB;
-    const size_t part = sizeof(float) * (size_t)(B * H * nrb) * (size_t)T * (size_t)record_stride(dk, gate);
+    return sizeof(float) * (size_t)nrb * (size_t)T * (size_t)record_stride(dk, gate);
+}
+int64_t heads_per_launch(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate) {
+    const size_t per = part_bytes_per_head(T, dk, dv, gate);
+    const int64_t g = per > 0 ? (int64_t)(kPartCap / per) : B * H;
+    return std::max<int64_t>(1, std::min<int64_t>(B * H, g));
+}
+
+size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate) {
+    const size_t part = part_bytes_per_head(T, dk, dv, gate) * (size_t)heads_per_launch(B, T, H, dk, dv, gate);
     return backward_ckpt_bytes(B, T, H, dk, dv) + align256(part);
 }
 
 hipError_t backward(const BwdProblem& a, hipStream_t st) {
     const Problem& p = a.p;
-    prof_begin("k_backward", st);
-    hipError_t e = p.dtype == GDN_BF16 ? launch_dt<1>(a, st) : launch_dt<0>(a, st);
-    prof_end(st);
-    if (e != hipSuccess) return e;
     const int RB = rows_per_block(p.dk);
     const int nrb = (int)((p.dv + RB - 1) / RB);
     const int RS = record_stride(p.dk, p.gate);
-    const int64_t n = p.B * p.H * p.T * (RS / 4);
-    if (n == 0) return hipSuccess;
-    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
-    prof_begin("k_bwd_reduce", st);
-    hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)blocks), dim3(256), 0, st, a, nrb, RS);
-    prof_end(st);
-    return hipGetLastError();
+    const int64_t BH = p.B * p.H, gsz = heads_per_launch(p.B, p.T, p.H, p.dk, p.dv, p.gate);
+    for (int64_t bh0 = 0; bh0 < BH; bh0 += gsz) {
+        BwdProblem g = a;
+        g.bh0 = bh0;
+        g.nbh = std::min<int64_t>(gsz, BH - bh0);
+        prof_begin("k_backward", st);
+        hipError_t e = p.dtype == GDN_BF16 ? launch_dt<1>(g, st) : launch_dt<0>(g, st);
+        prof_end(st);
+        if (e != hipSuccess) return e;
+        const int64_t n = g.nbh * p.T * (RS / 4);
+        if (n == 0) continue;
+        const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+        prof_begin("k_bwd_reduce", st);
+        hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)blocks), dim3(256), 0, st, g, nrb, RS);
+        prof_end(st);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gdn

@@ -195,6 +195,17 @@ def make_inputs_device(w: Workload, device="cuda") -> dict:
     return res
 
 
+def make_grads_device(w: Workload, device="cuda", with_state: bool = True) -> dict:
+    """make_grads' recipe drawn on the device (torch's seeded Philox
+    generator, seed + 1), for workloads too large to draw on the host."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed + 1)
+    dout = torch.randn((w.B, w.T, w.H, w.dv), generator=g, device=device)
+    ds = torch.randn((w.B, w.H, w.dv, w.dk), generator=g, device=device) if with_state else None
+    return {"dout": dout, "dstate": ds}
+
+
 def slice_inputs(d: dict, pairs) -> dict:
     """The uploaded values of the listed (batch, head) slices of device
     inputs, as fp32 numpy arrays shaped like make_inputs' with B = len(pairs)

@@ -172,8 +172,9 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
  *                   gate) bytes (per (batch, head): 4 dk dv ceil(T / 64) of
  *                   checkpoints and 4 T (2 dk + 4) per block of state rows of
  *                   sums, 3 dk + 4 for a channel gate; 2.4 GiB on a batch of
- *                   2 x 16 heads of 8192 tokens at d = 128); may be NULL when
- *                   T = 0
+ *                   2 x 16 heads of 8192 tokens at d = 128); the sums' part
+ *                   is capped at 8 GiB (larger batches run in groups of
+ *                   heads, one after the other); may be NULL when T = 0
  * The gradient outputs must not alias any input or each other.
  * Alignment: q and k on 8 bytes (bf16) or 16 bytes (fp32); state0,
  * grad_state_out, grad_state0 and a channel alpha on 16 bytes; the rest on

@@ -132,3 +132,25 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(r1, r2):
         assert torch.equal(x, y)
+
+
+def test_backward_past_2_31_elements():
+    """2049 x 256 tokens x 32 heads at d = 128: q, k, dq and dk of 2.15e9
+    elements (the sums run in groups of heads within the 8 GiB cap); heads at
+    the end of the batch checked against the oracle."""
+    import torch
+    from gated_delta_rule_12_amd.workloads import make_grads_device, make_inputs_device, slice_inputs
+    w = Workload("bwd-large", B=2049, H=32, T=256, dk=128, dv=128, chunk=64, seed=779)
+    assert w.B * w.T * w.H * w.dk > 2 ** 31
+    print(f"case {w.name} B={w.B} H={w.H} T={w.T}", flush=True)
+    d = make_inputs_device(w)
+    g = make_grads_device(w, with_state=False)
+    pairs = [(2048, 31), (2048, 0), (1000, 5)]
+    inp = slice_inputs(d, pairs)
+    dout = np.stack([g["dout"][b, :, h].cpu().numpy() for b, h in pairs])[:, :, None]
+    res = gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], None, g["dout"], None)
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, dout, None)
+    got = [np.stack([x[b, :, h].cpu().numpy() for b, h in pairs])[:, :, None] for x in res[:5]]
+    got.append(np.stack([res[5][b, h].cpu().numpy() for b, h in pairs])[:, None])
+    check(got, ref)
