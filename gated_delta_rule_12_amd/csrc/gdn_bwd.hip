@@ -84,48 +84,6 @@ __device__ __forceinline__ float4 add4(const float4& a, const float4& b) {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// Cross-lane sums on the vector ALU (DPP and the lane-swap instructions),
-// not through the LDS crossbar: each step pairs lanes symmetrically, so every
-// lane of a group ends with the same sum.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-// x + (x with 16-lane rows 0 <-> 1 and 2 <-> 3 exchanged)
-__device__ __forceinline__ float xor16_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// x + (x with the two 32-lane halves exchanged)
-__device__ __forceinline__ float xor32_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141; // within 8 lanes, i <-> 7 - i
-constexpr int kDppMirror = 0x140;     // within 16 lanes, i <-> 15 - i
-constexpr int kDppRor4 = 0x124;       // within 16 lanes, rotate by 4
-constexpr int kDppRor8 = 0x128;       // within 16 lanes, rotate by 8
-
-// sum over the LPR lanes of a row (aligned groups of LPR lanes)
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
-    if constexpr (LPR >= 2) x += dpp<kDppXor1>(x);
-    if constexpr (LPR >= 4) x += dpp<kDppXor2>(x);
-    if constexpr (LPR >= 8) x += dpp<kDppHalfMirror>(x);
-    if constexpr (LPR >= 16) x += dpp<kDppMirror>(x);
-    if constexpr (LPR >= 32) x = xor16_sum(x);
-    return x;
-}
-// sum over the row groups of a wave (lanes equal modulo LPR)
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-    if constexpr (LPR <= 4) x += dpp<kDppRor4>(x);
-    if constexpr (LPR <= 8) x += dpp<kDppRor8>(x);
-    if constexpr (LPR <= 16) x = xor16_sum(x);
-    return xor32_sum(x);
-}
 template <int LPR>
 __device__ __forceinline__ float4 group_sum4(float4 x) {
     return make_float4(group_sum<LPR>(x.x), group_sum<LPR>(x.y), group_sum<LPR>(x.z),

@@ -16,7 +16,7 @@
 // and write), against 4 flops per element.  LPR lanes hold one row as float4
 // pieces (16-byte loads and stores; a wave covers 64 / LPR whole rows, which
 // are contiguous in memory), the two dot products are reduced across the
-// row's lanes with shuffles, and each thread keeps kRows rows in flight so
+// row's lanes by vector-ALU butterflies (row_sum), and each thread keeps kRows rows in flight so
 // that enough bytes are outstanding per CU to cover the HBM latency.  The
 // state is read and written with non-temporal hints: each byte is touched
 // once per step, and keeping it out of the caches took a quarter less time
@@ -54,13 +54,6 @@ __device__ __forceinline__ float dot4(const float4& a, const float4& b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
-// sum over the LPR lanes of a row (aligned groups of LPR lanes)
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-    return x;
-}
 
 // grid (row blocks, H, B); block: 4 waves, wave w covers rows
 // rb RB + (j 4 + w) RPW + l / LPR for j < kRows
