@@ -1109,14 +1109,16 @@ struct SegShared {
 // KIND 0 (output pass): the state S (values from V); KIND 2 (state pass): S
 // and the scaling matrix M (V = 0, identity start) in one workgroup, waves
 // 0 .. NWH - 1 on S and NWH .. 2 NWH - 1 on M, sharing the staged chunk and
-// the K^T fragments.
+// the K^T fragments; KIND 3 (state pass, NV = 2): every wave holds the same
+// value columns of S (slot 0) and of M (slot 1).
 template <int D, int MODE, int KIND, int NV>
 __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, const WsLayout& L, char* wsb,
                                          const u16x8* tfrag, const float* gates, int64_t bh, int gseg,
                                          SegShared<D, MODE>& sh) {
     constexpr bool OUT = MODE == kSegOut;
-    static_assert(KIND == 0 || KIND == 2, "S alone, or S and M together");
-    constexpr int NWH = D / (16 * NV);         // waves per state; wave w owns value columns 16 NV (w % NWH) ..
+    static_assert(KIND == 0 || KIND == 2 || (KIND == 3 && NV == 2), "S alone, or S and M together");
+    // KIND 3: each wave holds the same value columns of S (slot 0) and M (slot 1)
+    constexpr int NWH = KIND == 3 ? D / 16 : D / (16 * NV);  // waves per state; wave w owns value columns 16 NV (w % NWH) ..
     constexpr int NW = KIND == 2 ? 2 * NWH : NWH;
     constexpr int NT = 64 * NW;
     constexpr int LDK = SegShared<D, MODE>::LDK;
@@ -1133,6 +1135,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wv = KIND == 2 ? w % NWH : w;                      // value block of the wave
     const bool mk = KIND == 2 && w >= NWH;                      // the wave runs M
+    auto is_m = [&](int n) { return KIND == 3 ? n == 1 : mk; };  // slot n holds M
     const int l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int64_t H = p.H, T = p.T;
     const int b = (int)(bh / H), h = (int)(bh - (bh / H) * H);
@@ -1147,7 +1150,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     // (v = 16 (NV w + n) + c16, a = 16 tau + 4 g4 + r)
     int v[NV];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) v[n] = 16 * (NV * wv + n) + c16;
+    for (int n = 0; n < NV; ++n) v[n] = KIND == 3 ? 16 * wv + c16 : 16 * (NV * wv + n) + c16;
     f32x4 Sacc[NV][TPW];
     {
         const float* src = nullptr;
@@ -1160,7 +1163,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
                 const int a0 = 16 * u + 4 * g4;
-                if (mk) {
+                if (is_m(n)) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Sacc[n][u][r] = v[n] == a0 + r ? 1.f : 0.f;
                 } else if (src) {
@@ -1412,7 +1415,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
                 f32x4 u;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float vv = mk ? 0.f : gdn_bf16_to_f32(sh.V[(16 * m + 4 * g4 + r) * LDK + v[n]]);
+                    const float vv = is_m(n) ? 0.f : gdn_bf16_to_f32(sh.V[(16 * m + 4 * g4 + r) * LDK + v[n]]);
                     u[r] = vv - gp[r] * X[m][n][r];
                 }
                 split4(u, uh[n][m], ul[n][m]);
@@ -1530,9 +1533,11 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     if (dst) {
 #pragma unroll
         for (int n = 0; n < NV; ++n)
+            if (!is_m(n)) {
 #pragma unroll
-            for (int u = 0; u < TPW; ++u)
-                *reinterpret_cast<f32x4*>(&dst[(int64_t)v[n] * D + 16 * u + 4 * g4]) = Sacc[n][u];
+                for (int u = 0; u < TPW; ++u)
+                    *reinterpret_cast<f32x4*>(&dst[(int64_t)v[n] * D + 16 * u + 4 * g4]) = Sacc[n][u];
+            }
     }
     if constexpr (!OUT) {
         if (gseg > 0) {  // (segment 0 needs no M)
@@ -1543,17 +1548,20 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             // a private LDS tile (column-major, 16 NV floats per column) and
             // reads back runs of 8 rows of one column, one fragment slot per
             // lane, so each slot leaves as one 16-byte store per half.
-            constexpr int LW = 16 * NV;  // rows of M per wave
+            constexpr int LW = KIND == 3 ? 16 : 16 * NV;  // rows of M per wave
             static_assert(sizeof(SegShared<D, MODE>) >= sizeof(float) * NWH * D * LW, "M tiles fit");
             __syncthreads();  // the chunk loop is done with LDS
-            if (mk) {
+            if (KIND == 3 || mk) {
                 float* Wt = reinterpret_cast<float*>(&sh) + wv * (D * LW);
 #pragma unroll
                 for (int n = 0; n < NV; ++n)
+                    if (is_m(n)) {
+                        const int col = KIND == 3 ? 0 : 16 * n;
 #pragma unroll
-                    for (int u = 0; u < TPW; ++u)
+                        for (int u = 0; u < TPW; ++u)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) Wt[(16 * u + 4 * g4 + r) * LW + 16 * n + c16] = Sacc[n][u][r];
+                            for (int r = 0; r < 4; ++r) Wt[(16 * u + 4 * g4 + r) * LW + col + c16] = Sacc[n][u][r];
+                    }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1842,8 +1850,17 @@ template <int D>
 constexpr int kSegNV = 1;
 // threads per workgroup: one wave per value block; the state pass runs the S
 // and the M chain of a segment in one workgroup (twice the waves)
+// The state pass at D = 128 pairs S^D and M in every wave (KIND 3): eight
+// waves, each with the same 16 value columns of both, so that every shared A
+// fragment read from LDS feeds two products (88.5 against 94.1 us on the main
+// workload, with half the LDS operand traffic and two waves per SIMD instead
+// of four).  At D = 64 the sixteen-wave form (KIND 2) stays faster.
+template <int D>
+constexpr bool kSegPaired = D == 128;
 template <int D, int MODE>
-constexpr int seg_threads() { return 64 * D / (16 * kSegNV<D>) * (MODE == kSegState ? 2 : 1); }
+constexpr int seg_threads() {
+    return 64 * D / (16 * kSegNV<D>) * (MODE == kSegState && !kSegPaired<D> ? 2 : 1);
+}
 template <int D, int MODE>
 constexpr int seg_waves_per_eu() { return seg_threads<D, MODE>() / 256 < 1 ? 1 : seg_threads<D, MODE>() / 256; }
 template <int D, int MODE>
@@ -1857,7 +1874,10 @@ __global__ __launch_bounds__((seg_threads<D, MODE>()), (seg_waves_per_eu<D, MODE
     } else {
         // workgroup (head, segment g < G - 1)
         const int nseg = sp.G - 1;
-        seg_body<D, MODE, 2, NV>(p, sp, L, wsb, tfrag, gates, blockIdx.x / nseg, blockIdx.x % nseg, sh);
+        if constexpr (kSegPaired<D>)
+            seg_body<D, MODE, 3, 2>(p, sp, L, wsb, tfrag, gates, blockIdx.x / nseg, blockIdx.x % nseg, sh);
+        else
+            seg_body<D, MODE, 2, NV>(p, sp, L, wsb, tfrag, gates, blockIdx.x / nseg, blockIdx.x % nseg, sh);
     }
 }
 
