@@ -1849,7 +1849,8 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
 template <int D>
 constexpr int kSegNV = 1;
 // threads per workgroup: one wave per value block; the state pass runs the S
-// and the M chain of a segment in one workgroup (twice the waves)
+// and the M chain of a segment in one workgroup (twice the waves, unless
+// every wave carries both, see kSegPaired)
 // The state pass at D = 128 pairs S^D and M in every wave (KIND 3): eight
 // waves, each with the same 16 value columns of both, so that every shared A
 // fragment read from LDS feeds two products (88.5 against 94.1 us on the main
