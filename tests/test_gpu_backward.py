@@ -80,6 +80,9 @@ CASES = [
     ("bf16", "scalar", DTP, 32, 48, 2, 1, 65, 0.3, 2.0),
     ("bf16", "channel", PTD, 128, 128, 1, 2, 96, 0.3, 6.0),   # long memory
     ("f32", "scalar", PTD, 64, 128, 1, 2, 5, 0.3, 2.0),       # shorter than one run
+    ("f32", "channel", DTP, 128, 64, 1, 2, 190, 0.3, 2.0),    # fp32 at d = 128, dk > dv
+    ("bf16", "scalar", PTD, 64, 128, 2, 2, 129, 0.3, 6.0),    # dk < dv, long memory, 2 intervals + 1 token
+    ("bf16", "channel", DTP, 128, 128, 1, 3, 250, 0.0, 2.0),  # no start state, three intervals + ragged run
 ]
 
 
