@@ -295,14 +295,16 @@ int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !grad_out || !grad_q || !grad_k || !grad_v ||
                   !grad_alpha || !grad_beta))
         return GDN_E_ARG;
-    // q, k move in 8-byte (bf16) or 16-byte (fp32) pieces, a channel gate and
-    // the states in 16-byte pieces, everything else per element
+    // q, k move in 8-byte (bf16) or 16-byte (fp32) pieces; a channel gate, the
+    // states, dq, dk, a channel dalpha and the workspace in 16-byte pieces;
+    // everything else per element
     const uintptr_t qk_align = dtype == GDN_BF16 ? 8 : 16;
+    const uintptr_t gate_align = gate == GDN_GATE_CHANNEL ? 16 : 4;
     if (!aligned(q, qk_align) || !aligned(k, qk_align) || !aligned(state0, 16) ||
-        !aligned(grad_state_out, 16) || !aligned(grad_state0, 16) ||
-        !aligned(alpha, gate == GDN_GATE_CHANNEL ? 16 : 4) || !aligned(beta, 4) || !aligned(v, 2) ||
-        !aligned(grad_out, 4) || !aligned(grad_q, 4) || !aligned(grad_k, 4) || !aligned(grad_v, 4) ||
-        !aligned(grad_alpha, 4) || !aligned(grad_beta, 4))
+        !aligned(grad_state_out, 16) || !aligned(grad_state0, 16) || !aligned(alpha, gate_align) ||
+        !aligned(beta, 4) || !aligned(v, 2) || !aligned(grad_out, 4) || !aligned(grad_q, 16) ||
+        !aligned(grad_k, 16) || !aligned(grad_v, 4) || !aligned(grad_alpha, gate_align) ||
+        !aligned(grad_beta, 4) || !aligned(workspace, 16))
         return GDN_E_ARG;
     const size_t need = backward_workspace(B, T, H, dk, dv, gate);
     if (T > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;

@@ -177,8 +177,9 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
  *                   heads, one after the other); may be NULL when T = 0
  * The gradient outputs must not alias any input or each other.
  * Alignment: q and k on 8 bytes (bf16) or 16 bytes (fp32); state0,
- * grad_state_out, grad_state0 and a channel alpha on 16 bytes; the rest on
- * their element size; otherwise GDN_E_ARG.  dk, dv as for gdn_chunk_fwd;
+ * grad_state_out, grad_state0, grad_q, grad_k, a channel alpha and its
+ * grad_alpha, and the workspace on 16 bytes; the rest on their element size;
+ * otherwise GDN_E_ARG.  dk, dv as for gdn_chunk_fwd;
  * other statuses as above.
  */
 int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

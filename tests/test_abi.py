@@ -255,11 +255,13 @@ def test_backward_rejects_bad_arguments_before_any_launch():
         ptrs = list(ok)
         ptrs[idx] = nul
         assert call(ptrs) == gdn.GDN_E_ARG, idx
-    # 16-byte pieces: states; 8-byte: bf16 q, k; per element: the rest
-    for idx in (5, 7, 13):
+    # 16-byte pieces: states, dq, dk and the workspace; 8-byte: bf16 q, k;
+    # per element: the rest
+    for idx in (5, 7, 8, 9, 13):
         ptrs = list(ok)
         ptrs[idx] = odd16
         assert call(ptrs) == gdn.GDN_E_ARG, idx
+    assert call(ok, ws=odd16) == gdn.GDN_E_ARG
     for idx in (0, 1):
         ptrs = list(ok)
         ptrs[idx] = ctypes.c_void_p(0x1004)
@@ -271,6 +273,9 @@ def test_backward_rejects_bad_arguments_before_any_launch():
     chan_head = head[:6] + (gdn.GDN_GATE_CHANNEL,) + head[7:]
     ptrs = list(ok)
     ptrs[3] = odd16
+    assert call(ptrs, head=chan_head, nbytes=chan) == gdn.GDN_E_ARG
+    ptrs = list(ok)
+    ptrs[11] = odd16  # a channel gate's gradient goes out in 16-byte pieces too
     assert call(ptrs, head=chan_head, nbytes=chan) == gdn.GDN_E_ARG
     # a channel gate needs the larger workspace
     assert call(ok, head=chan_head, nbytes=need) == gdn.GDN_E_WORKSPACE
