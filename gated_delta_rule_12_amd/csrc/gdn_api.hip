@@ -114,6 +114,7 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
     const Split sp = make_split(p.NC, n_segments);
     const WsLayout L = layout_for(p, sp);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return GDN_E_WORKSPACE;
+    if (!aligned(workspace, 16)) return GDN_E_ARG;  // (moved in 16-byte pieces)
     char* ws = static_cast<char*>(workspace);
     if (mfma_supported(dk, dv, chunk, dtype, gate)) return finish(mfma_forward(p, sp, ws, st));
     return finish(valu_forward(p, sp, ws, st));

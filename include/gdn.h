@@ -34,9 +34,9 @@
  * the workspace must not alias any input.  Two calls that share a workspace
  * must be ordered on one stream.
  *
- * Alignment: q, k, v, state0, out, state_out and a per-channel alpha must be
- * 16-byte aligned, beta and a scalar alpha 4-byte aligned (fresh device
- * allocations are); otherwise the call returns GDN_E_ARG.
+ * Alignment: q, k, v, state0, out, state_out, a per-channel alpha and the
+ * workspace must be 16-byte aligned, beta and a scalar alpha 4-byte aligned
+ * (fresh device allocations are); otherwise the call returns GDN_E_ARG.
  *
  * Errors: every argument check runs on the host before anything is enqueued;
  * a failing check returns a negative status and enqueues nothing.  A HIP

@@ -215,6 +215,8 @@ def test_forward_entry_points_check_alignment_and_segment_count():
     assert gdn.gdn_chunk_fwd(*shape, *ptrs, fake, 16, nul) == gdn.GDN_E_WORKSPACE
     chan = shape[:7] + (gdn.GDN_GATE_CHANNEL,) + shape[8:]
     assert gdn.gdn_chunk_fwd(*chan, *ptrs, fake, 16, nul) == gdn.GDN_E_ARG
+    # the workspace moves in 16-byte pieces too
+    assert gdn.gdn_chunk_fwd(*shape, *ok, odd16, 1 << 30, nul) == gdn.GDN_E_ARG
     # segment counts below one
     for n in (0, -3):
         assert gdn.gdn_seqpar_fwd(*shape, n, *ok, fake, 1 << 30, nul) == gdn.GDN_E_SHAPE
