@@ -317,7 +317,7 @@ int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_
     a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dalpha = grad_alpha; a.dbeta = grad_beta;
     a.ds0 = grad_state0;
     a.ckpt = static_cast<float*>(workspace);
-    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_ckpt_bytes(B, T, H, dk, dv));
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_ckpt_bytes(B, T, H, dk, dv, gate));
     return finish(backward(a, static_cast<hipStream_t>(stream)));
 }
 

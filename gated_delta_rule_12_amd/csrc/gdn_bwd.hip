@@ -21,11 +21,11 @@
 // whose inputs (q, k, gates, beta and the block's v and dL/dout) are staged
 // into LDS by one coalesced load of the whole workgroup, issued while the
 // previous run computes.  Phase A runs the recurrence forward over the
-// sequence and stores its rows of the state every kCk tokens in the
-// workspace.  Phase B walks the checkpoint intervals backwards: it
-// recomputes the interval forward from its checkpoint, keeping the state at
-// every run start in LDS, then for each run (last first) recomputes the
-// run's states into registers and carries dL/dS back through them.  The
+// sequence and stores its rows of the state at every run start in the
+// workspace.  Phase B walks the runs backwards: it recomputes each run's
+// states from its checkpoint into registers and carries dL/dS back through
+// them.  (Checkpoints every 64 tokens, with the run starts recomputed per
+// interval, took 14 % more time for a quarter of the workspace.)  The
 // per-token sums over rows (dq, dk, dalpha, dbeta) are reduced within the
 // workgroup through LDS and stored as one record per (row block, token) in
 // the workspace; k_bwd_reduce then sums a head's row blocks into the outputs
@@ -46,9 +46,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRows = 2;    // rows per thread
-constexpr int kCk = 64;     // tokens between stored checkpoints
 constexpr int kSub = 16;    // tokens recomputed into registers at a time
-constexpr int kSubs = kCk / kSub;
 constexpr int kMaxD = 128;
 
 template <int DT>
@@ -108,7 +106,6 @@ struct BwdShared {
     float tv[kSub][RB], tdo[kSub][RB];
     float4 vec[4][kSub][3][LPR];        // [wave][token][dq | dk | dd][piece]
     float sc[4][kSub][2];               // dbeta, dalpha (scalar gate)
-    float4 sub[kSubs][kRows][kThreads];
 };
 
 template <int DT, int LPR, bool CH, bool DTPO>
@@ -242,50 +239,9 @@ struct Bwd {
     __device__ int64_t roff(int j) const { return (int64_t)r[j] * a.p.dk + 4 * c; }
 };
 
-// The order in which a workgroup visits runs of kSub tokens (R = run index):
-// phase A, R = 0 .. NR - 1 forward; then for every checkpoint interval ck,
-// last first, with nsub runs: forward over its runs 0 .. nsub - 2 (storing
-// the run starts), then backward over runs nsub - 1 .. 0.
-struct Visit {
-    int kind;    // 0 phase A, 1 forward inside an interval, 2 backward
-    int64_t R;   // run
-    int pos;     // run within its interval
-    int64_t ck;  // interval
-};
-__device__ __forceinline__ Visit visit_of(int64_t vi, int64_t T) {
-    const int64_t NR = (T + kSub - 1) / kSub, NCk = (T + kCk - 1) / kCk;
-    Visit v;
-    if (vi < NR) {
-        v.kind = 0;
-        v.R = vi;
-        v.pos = (int)(vi % kSubs);
-        v.ck = vi / kSubs;
-        return v;
-    }
-    int64_t j = vi - NR;
-    const int64_t ckl = NCk - 1;
-    const int nsl = (int)((T - ckl * kCk + kSub - 1) / kSub);
-    int nsub, local;
-    if (j < 2 * nsl - 1) {
-        v.ck = ckl;
-        nsub = nsl;
-        local = (int)j;
-    } else {
-        j -= 2 * nsl - 1;
-        v.ck = ckl - 1 - j / (2 * kSubs - 1);
-        nsub = kSubs;
-        local = (int)(j % (2 * kSubs - 1));
-    }
-    if (local < nsub - 1) {
-        v.kind = 1;
-        v.pos = local;
-    } else {
-        v.kind = 2;
-        v.pos = 2 * (nsub - 1) - local;
-    }
-    v.R = v.ck * kSubs + v.pos;
-    return v;
-}
+// Visits of runs of kSub tokens: phase A over runs 0 .. NR - 1, then the
+// backward over runs NR - 1 .. 0.
+__device__ __forceinline__ int64_t run_of(int64_t vi, int64_t NR) { return vi < NR ? vi : 2 * NR - 1 - vi; }
 
 template <int DT, int LPR, bool CH, bool DTPO>
 __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb, int RS) {
@@ -297,10 +253,9 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb, in
     const K k(a, sh, bh, (int)(blockIdx.x % nrb));
     const int tid = threadIdx.x;
     const int64_t T = p.T;
-    const int64_t NR = (T + kSub - 1) / kSub, NCk = (T + kCk - 1) / kCk;
-    const int64_t NV = T > 0 ? NR + (2 * ((T - (NCk - 1) * kCk + kSub - 1) / kSub) - 1) + (2 * kSubs - 1) * (NCk - 1) : 0;
+    const int64_t NR = (T + kSub - 1) / kSub, NV = 2 * NR;
     const int64_t DD = p.dv * p.dk;
-    float* ckpt = a.ckpt + bh * NCk * DD;
+    float* ckpt = a.ckpt + bl * NR * DD;  // (the launch's own checkpoint region)
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 
     float4 S[kRows], Gd[kRows];
@@ -311,56 +266,37 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdProblem a, int nrb, in
     }
     typename K::Stage stg;
     if (NV > 0) {
-        const Visit v0 = visit_of(0, T);
-        k.stage_load(stg, v0.R * kSub, (int)min<int64_t>(kSub, T - v0.R * kSub));
+        k.stage_load(stg, 0, (int)min<int64_t>(kSub, T));
         k.stage_store(stg);
     }
     __syncthreads();
     for (int64_t vi = 0; vi < NV; ++vi) {
-        const Visit v = visit_of(vi, T);
-        const int64_t ts = v.R * kSub;
+        const bool fwd = vi < NR;
+        const int64_t R = run_of(vi, NR), ts = R * kSub;
         const int m = (int)min<int64_t>(kSub, T - ts);
-        // the visit's start state (from a checkpoint: read before the next
-        // visit's inputs are requested, so that waiting for it does not wait
-        // for them)
-        if (v.kind != 0 && v.pos == 0) {
+        // a backward visit starts from its run's checkpoint (each thread reads
+        // back what it wrote; read before the next visit's inputs are
+        // requested, so that waiting for it does not wait for them)
+        if (!fwd) {
 #pragma unroll
-            for (int j = 0; j < kRows; ++j)
-                S[j] = (k.on[j] && k.col) ? ldg4(ckpt + v.ck * DD + k.roff(j)) : z4;
-        } else if (v.kind == 2) {
-#pragma unroll
-            for (int j = 0; j < kRows; ++j) S[j] = sh.sub[v.pos][j][tid];
+            for (int j = 0; j < kRows; ++j) S[j] = (k.on[j] && k.col) ? ldg4(ckpt + R * DD + k.roff(j)) : z4;
         }
         // the next visit's inputs are fetched while this one computes
         if (vi + 1 < NV) {
-            const Visit nv = visit_of(vi + 1, T);
-            k.stage_load(stg, nv.R * kSub, (int)min<int64_t>(kSub, T - nv.R * kSub));
+            const int64_t nR = run_of(vi + 1, NR);
+            k.stage_load(stg, nR * kSub, (int)min<int64_t>(kSub, T - nR * kSub));
         }
-        if (v.kind == 0) {
-            // phase A: checkpoints every kCk tokens
-            if (v.pos == 0) {
+        if (fwd) {
+            // phase A: the run's start state, then its tokens
 #pragma unroll
-                for (int j = 0; j < kRows; ++j)
-                    if (k.on[j] && k.col) *reinterpret_cast<float4*>(ckpt + v.ck * DD + k.roff(j)) = S[j];
-            }
+            for (int j = 0; j < kRows; ++j)
+                if (k.on[j] && k.col) *reinterpret_cast<float4*>(ckpt + R * DD + k.roff(j)) = S[j];
             for (int u = 0; u < m; ++u) {
                 float4 Sn[kRows];
                 k.step(S, Sn, k.tok(u));
 #pragma unroll
                 for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
             }
-        } else if (v.kind == 1) {
-            // forward inside an interval (from the checkpoint, which each
-            // thread reads back where it wrote it): the start of the next run
-            // into LDS
-            for (int u = 0; u < m; ++u) {
-                float4 Sn[kRows];
-                k.step(S, Sn, k.tok(u));
-#pragma unroll
-                for (int j = 0; j < kRows; ++j) S[j] = Sn[j];
-            }
-#pragma unroll
-            for (int j = 0; j < kRows; ++j) sh.sub[v.pos + 1][j][tid] = S[j];
         } else {
             // backward over the run: its states into registers, St[u] before
             // token ts + u, then dL/dS carried back through them
@@ -530,30 +466,33 @@ hipError_t launch_dt(const BwdProblem& a, hipStream_t st) {
 
 }  // namespace
 
-size_t backward_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
-    const int64_t NCk = (T + kCk - 1) / kCk;
-    return align256(sizeof(float) * (size_t)(B * H * NCk) * (size_t)(dk * dv));
-}
 
-// The records of the row blocks' sums of (batch, head) pairs in a launch;
-// larger batches run in groups of pairs, one launch pair (kernel and
-// reduction) per group, so that this part of the workspace stays within
-// kPartCap however large the batch.
-constexpr size_t kPartCap = size_t(8) << 30;
+// The workspace of a launch: per (batch, head) pair the checkpoints (the
+// state at every run start) and the records of the row blocks' sums.  Larger
+// batches run in groups of pairs, one launch pair (kernel and reduction) per
+// group, so that the workspace stays within kWsCap however large the batch.
+constexpr size_t kWsCap = size_t(8) << 30;
+size_t ckpt_bytes_per_head(int64_t T, int64_t dk, int64_t dv) {
+    return sizeof(float) * (size_t)((T + kSub - 1) / kSub) * (size_t)(dk * dv);
+}
 size_t part_bytes_per_head(int64_t T, int64_t dk, int64_t dv, int gate) {
     const int RB = rows_per_block(dk);
     const int64_t nrb = (dv + RB - 1) / RB;
     return sizeof(float) * (size_t)nrb * (size_t)T * (size_t)record_stride(dk, gate);
 }
 int64_t heads_per_launch(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate) {
-    const size_t per = part_bytes_per_head(T, dk, dv, gate);
-    const int64_t g = per > 0 ? (int64_t)(kPartCap / per) : B * H;
+    const size_t per = ckpt_bytes_per_head(T, dk, dv) + part_bytes_per_head(T, dk, dv, gate);
+    const int64_t g = per > 0 ? (int64_t)(kWsCap / per) : B * H;
     return std::max<int64_t>(1, std::min<int64_t>(B * H, g));
+}
+
+size_t backward_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate) {
+    return align256(ckpt_bytes_per_head(T, dk, dv) * (size_t)heads_per_launch(B, T, H, dk, dv, gate));
 }
 
 size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate) {
     const size_t part = part_bytes_per_head(T, dk, dv, gate) * (size_t)heads_per_launch(B, T, H, dk, dv, gate);
-    return backward_ckpt_bytes(B, T, H, dk, dv) + align256(part);
+    return backward_ckpt_bytes(B, T, H, dk, dv, gate) + align256(part);
 }
 
 hipError_t backward(const BwdProblem& a, hipStream_t st) {

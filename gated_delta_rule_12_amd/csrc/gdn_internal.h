@@ -94,11 +94,11 @@ struct BwdProblem {
     float* dalpha;        // shaped as alpha
     float* dbeta;         // [B, T, H]
     float* ds0;           // [B, H, dv, dk] or null
-    float* ckpt;          // workspace: states every 64 tokens
+    float* ckpt;          // workspace: states at every 16-token run start
     float* part;          // workspace: per (row block, token) partial sums
     int64_t bh0, nbh;     // the (batch, head) pairs of one launch
 };
-size_t backward_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+size_t backward_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate);
 size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate);
 hipError_t backward(const BwdProblem& a, hipStream_t st);
 

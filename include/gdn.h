@@ -158,7 +158,7 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
  * dL/dq, dL/dk, dL/dv, dL/dalpha, dL/dbeta and grad_state0 = dL/d S_0 (NULL:
  * not wanted).  The pages fix the forward recurrence only; the gradients are
  * its chain rule, token by token in reverse.  The forward states are
- * recomputed from boundary-state checkpoints every 64 tokens that the call
+ * recomputed from boundary-state checkpoints every 16 tokens that the call
  * itself stores in the workspace; the sums over state rows go through the
  * workspace too (one record per block of rows and token), so the outputs are
  * written once, in a fixed order.
@@ -169,12 +169,12 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
  *   grad_alpha      shaped as alpha, fp32;  grad_beta [B, T, H] fp32
  *   grad_state0     [B, H, dv, dk] fp32 or NULL
  *   workspace       at least gdn_backward_workspace_bytes(B, T, H, dk, dv,
- *                   gate) bytes (per (batch, head): 4 dk dv ceil(T / 64) of
+ *                   gate) bytes (per (batch, head): 4 dk dv ceil(T / 16) of
  *                   checkpoints and 4 T (2 dk + 4) per block of state rows of
- *                   sums, 3 dk + 4 for a channel gate; 2.4 GiB on a batch of
- *                   2 x 16 heads of 8192 tokens at d = 128); the sums' part
- *                   is capped at 8 GiB (larger batches run in groups of
- *                   heads, one after the other); may be NULL when T = 0
+ *                   sums, 3 dk + 4 for a channel gate; 3.2 GiB on a batch of
+ *                   2 x 16 heads of 8192 tokens at d = 128), capped at about
+ *                   8 GiB (larger batches run in groups of heads, one after
+ *                   the other); may be NULL when T = 0
  * The gradient outputs must not alias any input or each other.
  * Alignment: q and k on 8 bytes (bf16) or 16 bytes (fp32); state0,
  * grad_state_out, grad_state0, grad_q, grad_k, a channel alpha and its

@@ -234,9 +234,10 @@ def test_backward_rejects_bad_arguments_before_any_launch():
     B, T, H, dk, dv = 1, 100, 2, 64, 64
     head = (B, T, H, dk, dv, gdn.GDN_BF16, gdn.GDN_GATE_SCALAR, gdn.GDN_PREDICT_THEN_DECAY, 1.0)
     need = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, gdn.GDN_GATE_SCALAR)
-    # two checkpoints of 64 tokens per (batch, head), and per block of 32 rows
-    # (16 lanes a row at dk = 64) a record of 2 dk + 4 floats per token
-    ckpt = 4 * dk * dv * 2 * B * H
+    # a checkpoint at every 16-token run start per (batch, head), and per block
+    # of 32 rows (16 lanes a row at dk = 64) a record of 2 dk + 4 floats per
+    # token
+    ckpt = 4 * dk * dv * 7 * B * H
     part = 4 * B * H * (dv // 32) * T * (2 * dk + 4)
     align = lambda x: (x + 255) // 256 * 256
     assert need == align(ckpt) + align(part)
