@@ -1368,8 +1368,9 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 #pragma unroll
             for (int m = 0; m < 4; ++m) times_state(sh.K, m, X[m]);
         } else {
-            // k-step outer, one accumulator per tile (the state pass runs two
-            // workgroups per CU, whose waves hide the dependent products)
+            // k-step outer, one accumulator per tile (the other waves of the
+            // SIMD hide the dependent products; this keeps the state pass's
+            // registers low)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
