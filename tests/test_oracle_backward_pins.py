@@ -9,7 +9,10 @@ oracle's forward pass alone, by central finite differences in fp64:
 * random directions on larger shapes (long-memory gates, unequal dk and dv);
 * special cases that fix single terms: beta = 0 makes v irrelevant (dv = 0),
   a zero dout and dstate give zero gradients everywhere, and with T = 0 the
-  start-state gradient is the final-state gradient itself.
+  start-state gradient is the final-state gradient itself;
+* and by a second, independent route: PyTorch's reverse mode through a plain
+  fp64 token loop written in the test from the recurrence (agreement to
+  1e-12).
 
 A dropped term, a wrong sign, a transposed state or a gate on the wrong axis
 in the backward changes at least one of these derivatives by far more than
@@ -103,3 +106,43 @@ def test_special_cases():
     xe = [a[:, :0] if a.ndim >= 3 and i < 5 else a for i, a in enumerate(x)]
     g = oracle.backward(*xe, do[:, :0], ds)
     assert np.array_equal(g[5], ds)
+
+
+@pytest.mark.parametrize("gate", [SC, CH])
+@pytest.mark.parametrize("order", [PTD, DTP])
+def test_against_autograd_of_a_plain_loop(gate, order):
+    """A second, independent route to the same gradients: PyTorch's reverse
+    mode through a plain fp64 token loop written here from the recurrence
+    (the update as the pages state it, not the oracle's code), on every input
+    at once."""
+    import torch
+    rng = np.random.default_rng(30 + 2 * gate + order)
+    x, do, ds = inputs(rng, B=1, T=24, H=2, dk=6, dv=5, gate=gate)
+    scale = 1.3
+    t = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in x]
+    q, k, v, al, be, s0 = t
+    B, T, H, dk = q.shape
+    outs = []
+    states = []
+    for h in range(H):
+        S = s0[0, h]
+        o_h = []
+        for tt in range(T):
+            kt, qt, vt, b = k[0, tt, h], q[0, tt, h], v[0, tt, h], be[0, tt, h]
+            d = al[0, tt, h] * torch.ones(dk, dtype=torch.float64) if gate == SC else al[0, tt, h]
+            if order == PTD:
+                S = S * d + b * torch.outer(vt - S @ kt, kt)
+            else:
+                Sb = S * d
+                S = Sb + b * torch.outer(vt - Sb @ kt, kt)
+            o_h.append(scale * (S @ qt))
+        outs.append(torch.stack(o_h))
+        states.append(S)
+    out = torch.stack(outs, dim=1)[None]   # [1, T, H, dv]
+    st = torch.stack(states)[None]         # [1, H, dv, dk]
+    L = (out * torch.tensor(do)).sum() + (st * torch.tensor(ds)).sum()
+    L.backward()
+    g = oracle.backward(*x, do, ds, gate=gate, order=order, scale=scale)
+    for name, a, ref in zip(["q", "k", "v", "alpha", "beta", "state0"], g, t):
+        r = ref.grad.numpy()
+        assert np.abs(a - r).max() <= 1e-12 * max(1.0, np.abs(r).max()), name
