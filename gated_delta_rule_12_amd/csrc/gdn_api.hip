@@ -1,12 +1,56 @@
 // C ABI of libgdn: argument validation, workspace sizing, dispatch between
-// the MFMA and vector-ALU kernel families, and optional per-kernel timing.
+// the MFMA and vector-ALU kernel families, and optional per-kernel timing
+// through a caller-owned timer.
 #include <string.h>
+
+#include <new>
 
 #include <string>
 #include <vector>
 
 #include "gdn_internal.h"
 #include "../../include/gdn.h"
+
+// A caller-owned per-kernel timer: one record per distinct kernel name, the
+// HIP event pairs not yet read, and a pool of spare events.  Touched only by
+// the calls it is passed to.
+struct gdn_timer {
+    struct Ev { int kernel; hipEvent_t a, b; };
+    std::vector<std::string> names;
+    std::vector<Ev> events;
+    std::vector<hipEvent_t> pool;
+    std::vector<double> ms;
+    std::vector<int64_t> cnt;
+    int open = -1;
+    hipEvent_t open_a = nullptr;
+
+    hipEvent_t get() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    void drain() {
+        for (auto& ev : events) {
+            float t = 0.f;
+            if (hipEventSynchronize(ev.b) == hipSuccess && hipEventElapsedTime(&t, ev.a, ev.b) == hipSuccess) {
+                ms[ev.kernel] += t;
+                cnt[ev.kernel] += 1;
+            }
+            pool.push_back(ev.a);
+            pool.push_back(ev.b);
+        }
+        events.clear();
+    }
+    ~gdn_timer() {
+        drain();
+        for (hipEvent_t e : pool) hipEventDestroy(e);
+    }
+};
 
 namespace gdn {
 namespace {
@@ -47,41 +91,6 @@ int auto_segments(const Problem& p) {
     return mfma_supported(p.dk, p.dv, p.C, p.dtype, p.gate) ? mfma_auto_segments(p) : 1;
 }
 
-// ---- profiling record ------------------------------------------------------
-struct ProfEvent { int kernel; hipEvent_t a, b; };
-bool g_prof_on = false;
-std::vector<std::string> g_prof_names;
-std::vector<ProfEvent> g_prof_events;
-std::vector<hipEvent_t> g_prof_pool;
-std::vector<double> g_prof_ms;
-std::vector<int64_t> g_prof_cnt;
-int g_prof_open = -1;
-hipEvent_t g_prof_open_a = nullptr;
-
-hipEvent_t pool_get() {
-    if (!g_prof_pool.empty()) {
-        hipEvent_t e = g_prof_pool.back();
-        g_prof_pool.pop_back();
-        return e;
-    }
-    hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    return e;
-}
-
-void prof_drain() {
-    for (auto& ev : g_prof_events) {
-        float ms = 0.f;
-        if (hipEventSynchronize(ev.b) == hipSuccess && hipEventElapsedTime(&ms, ev.a, ev.b) == hipSuccess) {
-            g_prof_ms[ev.kernel] += ms;
-            g_prof_cnt[ev.kernel] += 1;
-        }
-        g_prof_pool.push_back(ev.a);
-        g_prof_pool.push_back(ev.b);
-    }
-    g_prof_events.clear();
-}
-
 int finish(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 // The kernels move q, k, v, a per-channel gate, the states and the output in
@@ -98,7 +107,7 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
                 int32_t dtype, int32_t gate, int32_t order, float scale, int32_t n_segments,
                 const void* q, const void* k, const void* v, const float* alpha,
                 const float* beta, const float* state0, float* out, float* state_out,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream, gdn_timer* timer) {
     // n_segments == 0: the library picks the schedule (gdn_chunk_fwd)
     int s = validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments > 0 ? n_segments : 1);
     if (s != GDN_OK) return s;
@@ -109,6 +118,7 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
     if (!forward_aligned(q, k, v, alpha, gate, beta, state0, out, state_out)) return GDN_E_ARG;
     p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
     p.s0 = state0; p.out = out; p.s_out = state_out;
+    p.timer = timer;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p.NC == 0) return finish(copy_state(p, st));
     const Split sp = make_split(p.NC, n_segments);
@@ -123,7 +133,7 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
 int decode_common(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,
                   int32_t order, float scale, const void* q, const void* k, const void* v,
                   const float* alpha, const float* beta, const float* state_in, float* out,
-                  float* state_out, bool prologue, void* stream) {
+                  float* state_out, bool prologue, void* stream, gdn_timer* timer) {
     int s = validate(B, 1, H, dk, dv, 16, dtype, gate, order, 1);
     if (s != GDN_OK) return s;
     if (B * H == 0) return GDN_OK;
@@ -137,42 +147,85 @@ int decode_common(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dtype, i
     Problem p = make_problem(B, 1, H, dk, dv, 16, dtype, gate, order, scale);
     p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
     p.s0 = state_in; p.out = out; p.s_out = state_out;
+    p.timer = timer;
     return finish(decode_step(p, prologue, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
 
-void prof_begin(const char* name, hipStream_t st) {
-    if (!g_prof_on) return;
+void prof_begin(gdn_timer* t, const char* name, hipStream_t st) {
+    if (!t) return;
     int idx = -1;
-    for (size_t i = 0; i < g_prof_names.size(); ++i)
-        if (g_prof_names[i] == name) idx = (int)i;
+    for (size_t i = 0; i < t->names.size(); ++i)
+        if (t->names[i] == name) idx = (int)i;
     if (idx < 0) {
-        g_prof_names.emplace_back(name);
-        g_prof_ms.push_back(0.0);
-        g_prof_cnt.push_back(0);
-        idx = (int)g_prof_names.size() - 1;
+        t->names.emplace_back(name);
+        t->ms.push_back(0.0);
+        t->cnt.push_back(0);
+        idx = (int)t->names.size() - 1;
     }
-    g_prof_open = idx;
-    g_prof_open_a = pool_get();
-    if (g_prof_open_a) hipEventRecord(g_prof_open_a, st);
+    t->open = idx;
+    t->open_a = t->get();
+    if (t->open_a) hipEventRecord(t->open_a, st);
 }
 
-void prof_end(hipStream_t st) {
-    if (!g_prof_on || g_prof_open < 0 || !g_prof_open_a) return;
-    hipEvent_t b = pool_get();
+void prof_end(gdn_timer* t, hipStream_t st) {
+    if (!t || t->open < 0 || !t->open_a) return;
+    hipEvent_t b = t->get();
     if (b) {
         hipEventRecord(b, st);
-        g_prof_events.push_back({g_prof_open, g_prof_open_a, b});
+        t->events.push_back({t->open, t->open_a, b});
     }
-    g_prof_open = -1;
-    g_prof_open_a = nullptr;
-    if (g_prof_events.size() > 4096) prof_drain();
+    t->open = -1;
+    t->open_a = nullptr;
+    if (t->events.size() > 4096) t->drain();
 }
 
 }  // namespace gdn
 
 using namespace gdn;
+
+static int backward_common(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,
+                 int32_t order, float scale, const void* q, const void* k, const void* v,
+                 const float* alpha, const float* beta, const float* state0, const float* grad_out,
+                 const float* grad_state_out, float* grad_q, float* grad_k, float* grad_v,
+                 float* grad_alpha, float* grad_beta, float* grad_state0, void* workspace,
+                 size_t workspace_bytes, void* stream, gdn_timer* timer) {
+    int s = validate(B, T, H, dk, dv, 16, dtype, gate, order, 1);
+    if (s != GDN_OK) return s;
+    if (B * H == 0) return GDN_OK;
+    // one workgroup per (batch, head, block of at least 16 state rows)
+    if (B * H * (dv / 16) > ((int64_t)1 << 31) - 1) return GDN_E_SHAPE;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !grad_out || !grad_q || !grad_k || !grad_v ||
+                  !grad_alpha || !grad_beta))
+        return GDN_E_ARG;
+    // q, k move in 8-byte (bf16) or 16-byte (fp32) pieces; a channel gate, the
+    // states, dq, dk, a channel dalpha and the workspace in 16-byte pieces;
+    // everything else per element
+    const uintptr_t qk_align = dtype == GDN_BF16 ? 8 : 16;
+    const uintptr_t gate_align = gate == GDN_GATE_CHANNEL ? 16 : 4;
+    if (!aligned(q, qk_align) || !aligned(k, qk_align) || !aligned(state0, 16) ||
+        !aligned(grad_state_out, 16) || !aligned(grad_state0, 16) || !aligned(alpha, gate_align) ||
+        !aligned(beta, 4) || !aligned(v, 2) || !aligned(grad_out, 4) || !aligned(grad_q, 16) ||
+        !aligned(grad_k, 16) || !aligned(grad_v, 4) || !aligned(grad_alpha, gate_align) ||
+        !aligned(grad_beta, 4) || !aligned(workspace, 16))
+        return GDN_E_ARG;
+    const size_t need = backward_workspace(B, T, H, dk, dv, gate);
+    if (T > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
+    BwdProblem a{};
+    a.p = make_problem(B, T, H, dk, dv, 16, dtype, gate, order, scale);
+    a.p.q = q; a.p.k = k; a.p.v = v; a.p.alpha = alpha; a.p.beta = beta; a.p.s0 = state0;
+    a.p.timer = timer;
+    a.dout = grad_out;
+    a.ds_out = grad_state_out;
+    a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dalpha = grad_alpha; a.dbeta = grad_beta;
+    a.ds0 = grad_state0;
+    a.ckpt = static_cast<float*>(workspace);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_ckpt_bytes(B, T, H, dk, dv, gate));
+    return finish(backward(a, static_cast<hipStream_t>(stream)));
+}
+
+
 
 extern "C" {
 
@@ -230,7 +283,16 @@ int gdn_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32
                   const float* beta, const float* state0, float* out, float* state_out,
                   void* workspace, size_t workspace_bytes, void* stream) {
     return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, 0, q, k, v, alpha,
-                       beta, state0, out, state_out, workspace, workspace_bytes, stream);
+                       beta, state0, out, state_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int gdn_chunk_fwd_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                        int32_t dtype, int32_t gate, int32_t order, float scale,
+                        const void* q, const void* k, const void* v, const float* alpha,
+                        const float* beta, const float* state0, float* out, float* state_out,
+                        void* workspace, size_t workspace_bytes, void* stream, gdn_timer* timer) {
+    return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, 0, q, k, v, alpha,
+                       beta, state0, out, state_out, workspace, workspace_bytes, stream, timer);
 }
 
 int gdn_seqpar_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
@@ -240,7 +302,19 @@ int gdn_seqpar_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int3
                    void* workspace, size_t workspace_bytes, void* stream) {
     if (n_segments < 1) return GDN_E_SHAPE;  // (0 would select the library's schedule)
     return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, n_segments, q, k, v,
-                       alpha, beta, state0, out, state_out, workspace, workspace_bytes, stream);
+                       alpha, beta, state0, out, state_out, workspace, workspace_bytes, stream,
+                       nullptr);
+}
+
+int gdn_seqpar_fwd_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                         int32_t dtype, int32_t gate, int32_t order, float scale, int32_t n_segments,
+                         const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* state0, float* out, float* state_out,
+                         void* workspace, size_t workspace_bytes, void* stream, gdn_timer* timer) {
+    if (n_segments < 1) return GDN_E_SHAPE;
+    return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, n_segments, q, k, v,
+                       alpha, beta, state0, out, state_out, workspace, workspace_bytes, stream,
+                       timer);
 }
 
 int gdn_recurrent_ref(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t dtype,
@@ -265,7 +339,15 @@ int gdn_decode_step(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dtype,
                     const float* alpha, const float* beta, const float* state_in,
                     float* out, float* state_out, void* stream) {
     return decode_common(B, H, dk, dv, dtype, gate, order, scale, q, k, v, alpha, beta,
-                         state_in, out, state_out, false, stream);
+                         state_in, out, state_out, false, stream, nullptr);
+}
+
+int gdn_decode_step_timed(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,
+                          int32_t order, float scale, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, const float* state_in,
+                          float* out, float* state_out, void* stream, gdn_timer* timer) {
+    return decode_common(B, H, dk, dv, dtype, gate, order, scale, q, k, v, alpha, beta,
+                         state_in, out, state_out, false, stream, timer);
 }
 
 int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,
@@ -273,7 +355,7 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dt
                         const float* alpha_logit, const float* beta_logit, const float* state_in,
                         float* out, float* state_out, void* stream) {
     return decode_common(B, H, dk, dv, dtype, gate, order, scale, q, k, v, alpha_logit,
-                         beta_logit, state_in, out, state_out, true, stream);
+                         beta_logit, state_in, out, state_out, true, stream, nullptr);
 }
 
 size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
@@ -288,59 +370,45 @@ int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_
                  const float* grad_state_out, float* grad_q, float* grad_k, float* grad_v,
                  float* grad_alpha, float* grad_beta, float* grad_state0, void* workspace,
                  size_t workspace_bytes, void* stream) {
-    int s = validate(B, T, H, dk, dv, 16, dtype, gate, order, 1);
-    if (s != GDN_OK) return s;
-    if (B * H == 0) return GDN_OK;
-    // one workgroup per (batch, head, block of at least 16 state rows)
-    if (B * H * (dv / 16) > ((int64_t)1 << 31) - 1) return GDN_E_SHAPE;
-    if (T > 0 && (!q || !k || !v || !alpha || !beta || !grad_out || !grad_q || !grad_k || !grad_v ||
-                  !grad_alpha || !grad_beta))
-        return GDN_E_ARG;
-    // q, k move in 8-byte (bf16) or 16-byte (fp32) pieces; a channel gate, the
-    // states, dq, dk, a channel dalpha and the workspace in 16-byte pieces;
-    // everything else per element
-    const uintptr_t qk_align = dtype == GDN_BF16 ? 8 : 16;
-    const uintptr_t gate_align = gate == GDN_GATE_CHANNEL ? 16 : 4;
-    if (!aligned(q, qk_align) || !aligned(k, qk_align) || !aligned(state0, 16) ||
-        !aligned(grad_state_out, 16) || !aligned(grad_state0, 16) || !aligned(alpha, gate_align) ||
-        !aligned(beta, 4) || !aligned(v, 2) || !aligned(grad_out, 4) || !aligned(grad_q, 16) ||
-        !aligned(grad_k, 16) || !aligned(grad_v, 4) || !aligned(grad_alpha, gate_align) ||
-        !aligned(grad_beta, 4) || !aligned(workspace, 16))
-        return GDN_E_ARG;
-    const size_t need = backward_workspace(B, T, H, dk, dv, gate);
-    if (T > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
-    BwdProblem a{};
-    a.p = make_problem(B, T, H, dk, dv, 16, dtype, gate, order, scale);
-    a.p.q = q; a.p.k = k; a.p.v = v; a.p.alpha = alpha; a.p.beta = beta; a.p.s0 = state0;
-    a.dout = grad_out;
-    a.ds_out = grad_state_out;
-    a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dalpha = grad_alpha; a.dbeta = grad_beta;
-    a.ds0 = grad_state0;
-    a.ckpt = static_cast<float*>(workspace);
-    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_ckpt_bytes(B, T, H, dk, dv, gate));
-    return finish(backward(a, static_cast<hipStream_t>(stream)));
+    return backward_common(B, T, H, dk, dv, dtype, gate, order, scale, q, k, v, alpha, beta, state0,
+                           grad_out, grad_state_out, grad_q, grad_k, grad_v, grad_alpha, grad_beta,
+                           grad_state0, workspace, workspace_bytes, stream, nullptr);
 }
 
-int gdn_profile_enable(int on) {
-    if (!on) {
-        prof_drain();
-        g_prof_names.clear();
-        g_prof_ms.clear();
-        g_prof_cnt.clear();
-    }
-    g_prof_on = on != 0;
+int gdn_backward_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t dtype,
+                       int32_t gate, int32_t order, float scale, const void* q, const void* k,
+                       const void* v, const float* alpha, const float* beta, const float* state0,
+                       const float* grad_out, const float* grad_state_out, float* grad_q,
+                       float* grad_k, float* grad_v, float* grad_alpha, float* grad_beta,
+                       float* grad_state0, void* workspace, size_t workspace_bytes, void* stream,
+                       gdn_timer* timer) {
+    return backward_common(B, T, H, dk, dv, dtype, gate, order, scale, q, k, v, alpha, beta, state0,
+                           grad_out, grad_state_out, grad_q, grad_k, grad_v, grad_alpha, grad_beta,
+                           grad_state0, workspace, workspace_bytes, stream, timer);
+}
+
+int gdn_timer_create(gdn_timer** timer) {
+    if (!timer) return GDN_E_ARG;
+    *timer = new (std::nothrow) gdn_timer();
+    return *timer ? GDN_OK : GDN_E_HIP;
+}
+
+int gdn_timer_destroy(gdn_timer* timer) {
+    delete timer;
     return GDN_OK;
 }
 
-int gdn_profile_read(int index, char* name, size_t name_len, double* total_ms, int64_t* count) {
-    prof_drain();
-    if (index < 0 || index >= (int)g_prof_names.size()) return GDN_E_ARG;
+int gdn_timer_read(gdn_timer* timer, int index, char* name, size_t name_len, double* total_ms,
+                   int64_t* count) {
+    if (!timer) return GDN_E_ARG;
+    timer->drain();
+    if (index < 0 || index >= (int)timer->names.size()) return GDN_E_ARG;
     if (name && name_len > 0) {
-        strncpy(name, g_prof_names[index].c_str(), name_len - 1);
+        strncpy(name, timer->names[index].c_str(), name_len - 1);
         name[name_len - 1] = '\0';
     }
-    if (total_ms) *total_ms = g_prof_ms[index];
-    if (count) *count = g_prof_cnt[index];
+    if (total_ms) *total_ms = timer->ms[index];
+    if (count) *count = timer->cnt[index];
     return GDN_OK;
 }
 

@@ -505,16 +505,16 @@ hipError_t backward(const BwdProblem& a, hipStream_t st) {
         BwdProblem g = a;
         g.bh0 = bh0;
         g.nbh = std::min<int64_t>(gsz, BH - bh0);
-        prof_begin("k_backward", st);
+        prof_begin(p.timer, "k_backward", st);
         hipError_t e = p.dtype == GDN_BF16 ? launch_dt<1>(g, st) : launch_dt<0>(g, st);
-        prof_end(st);
+        prof_end(p.timer, st);
         if (e != hipSuccess) return e;
         const int64_t n = g.nbh * p.T * (RS / 4);
         if (n == 0) continue;
         const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
-        prof_begin("k_bwd_reduce", st);
+        prof_begin(p.timer, "k_bwd_reduce", st);
         hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)blocks), dim3(256), 0, st, g, nrb, RS);
-        prof_end(st);
+        prof_end(p.timer, st);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -168,13 +168,13 @@ hipError_t launch_dt(const Problem& p, hipStream_t st) {
 }  // namespace
 
 hipError_t decode_step(const Problem& p, bool prologue, hipStream_t st) {
-    prof_begin("k_decode", st);
+    prof_begin(p.timer, "k_decode", st);
     hipError_t e;
     if (prologue)
         e = p.dtype == GDN_BF16 ? launch_dt<1, true>(p, st) : launch_dt<0, true>(p, st);
     else
         e = p.dtype == GDN_BF16 ? launch_dt<1, false>(p, st) : launch_dt<0, false>(p, st);
-    prof_end(st);
+    prof_end(p.timer, st);
     return e;
 }
 

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+struct gdn_timer;  // caller-owned per-kernel timer (include/gdn.h)
+
 namespace gdn {
 
 // One forward problem, as the entry points received it (already validated).
@@ -25,6 +27,7 @@ struct Problem {
     const float* s0;
     float* out;
     float* s_out;
+    gdn_timer* timer;  // host object, null: no timing (never read by a kernel)
 };
 
 // Sequence-parallel split of the NC chunks of every sequence.
@@ -105,9 +108,10 @@ hipError_t backward(const BwdProblem& a, hipStream_t st);
 // Start state copy/zero for empty sequences (T == 0).
 hipError_t copy_state(const Problem& p, hipStream_t st);
 
-// Profiling hooks (gdn_profile_enable): bracket a launch with events.
-void prof_begin(const char* name, hipStream_t st);
-void prof_end(hipStream_t st);
+// Timing hooks: with a caller's timer, bracket a launch with HIP events on
+// the launch stream (nothing otherwise).
+void prof_begin(gdn_timer* t, const char* name, hipStream_t st);
+void prof_end(gdn_timer* t, hipStream_t st);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

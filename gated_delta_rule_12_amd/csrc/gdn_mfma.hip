@@ -1152,11 +1152,18 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
 #pragma unroll
     for (int n = 0; n < NV; ++n) v[n] = KIND == 3 ? 16 * wv + c16 : 16 * (NV * wv + n) + c16;
     f32x4 Sacc[NV][TPW];
+    // Entry states: the caller's start state for segment 0 of a single pass;
+    // with segments, every segment of the output pass reads its slot of the
+    // workspace's start states (segment 0's copied there by the state pass),
+    // so the start state may be the buffer the last segment's final state
+    // goes to (in-place streaming) with no ordering between the workgroups
+    // of the output pass.
+    float* const sstart_ws = reinterpret_cast<float*>(wsb + L.sstart) + (bh * sp.G + gseg) * D * D;
     {
         const float* src = nullptr;
         if (!mk) {
-            if (gseg == 0) src = p.s0 ? p.s0 + bh * D * D : nullptr;
-            else if (OUT) src = reinterpret_cast<const float*>(wsb + L.sstart) + (bh * sp.G + gseg) * D * D;
+            if (OUT && sp.G > 1) src = sstart_ws;
+            else if (gseg == 0) src = p.s0 ? p.s0 + bh * D * D : nullptr;
         }
 #pragma unroll
         for (int n = 0; n < NV; ++n)
@@ -1172,6 +1179,15 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
                     Sacc[n][u] = zero4();
                 }
             }
+        if (!OUT && gseg == 0) {
+#pragma unroll
+            for (int n = 0; n < NV; ++n)
+                if (!is_m(n)) {
+#pragma unroll
+                    for (int u = 0; u < TPW; ++u)
+                        *reinterpret_cast<f32x4*>(sstart_ws + (int64_t)v[n] * D + 16 * u + 4 * g4) = Sacc[n][u];
+                }
+        }
     }
 
     // ---- staging: chunk i+1 in registers while chunk i computes
@@ -1993,12 +2009,12 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
     float* gates = reinterpret_cast<float*>(ws + L.prep + (CH ? 2 : 1) * fbytes);
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
-        prof_begin("k_prep_mfma", st);
+        prof_begin(p.timer, "k_prep_mfma", st);
         if constexpr (CH)
             hipLaunchKernelGGL((k_prep_channel<D>), grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
         else
             hipLaunchKernelGGL((k_prep_scalar<D>), grid, dim3(kThreads), 0, st, p, tfrag, gates);
-        prof_end(st);
+        prof_end(p.timer, st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -2007,10 +2023,10 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
         const int64_t heads = p.B * p.H * sp.G;
         const int64_t nwork = heads * ntiles;
         const int remap = (heads % 8 == 0) ? 1 : 0;
-        prof_begin("k_rec_mfma", st);
+        prof_begin(p.timer, "k_rec_mfma", st);
         hipLaunchKernelGGL((k_rec_mfma<D, CH>), dim3((unsigned)nwork), dim3(kRecThreads), 0, st, p, sp, L,
                            ws, tfrag, pfrag, gates, ntiles, remap);
-        prof_end(st);
+        prof_end(p.timer, st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -2028,23 +2044,23 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
     float* gates = reinterpret_cast<float*>(ws + L.prep + fbytes);
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
-        prof_begin("k_prep_mfma", st);
+        prof_begin(p.timer, "k_prep_mfma", st);
         hipLaunchKernelGGL((k_prep_scalar<D>), grid, dim3(kThreads), 0, st, p, tfrag, gates);
-        prof_end(st);
+        prof_end(p.timer, st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t heads = p.B * p.H;
     if (sp.G > 1) {
-        prof_begin("k_seg_state", st);
+        prof_begin(p.timer, "k_seg_state", st);
         hipLaunchKernelGGL((k_seg<D, kSegState>), dim3((unsigned)(heads * (sp.G - 1))), dim3(seg_threads<D, kSegState>()), 0, st,
                            p, sp, L, ws, tfrag, gates);
-        prof_end(st);
+        prof_end(p.timer, st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const ChainPlan cp = chain_plan(sp.G, heads, D);
         const unsigned nx = D / 16;
-        prof_begin("k_chain", st);
+        prof_begin(p.timer, "k_chain", st);
         if (cp.nb == 0) {
             hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * nx)), dim3(256), 0, st, p, sp, L, ws,
                                (int)kChainSeq, cp);
@@ -2056,14 +2072,14 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
             hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * cp.nb * nx)), dim3(256), 0, st, p, sp, L,
                                ws, (int)kChainExpand, cp);
         }
-        prof_end(st);
+        prof_end(p.timer, st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    prof_begin("k_seg_out", st);
+    prof_begin(p.timer, "k_seg_out", st);
     hipLaunchKernelGGL((k_seg<D, kSegOut>), dim3((unsigned)(heads * sp.G)), dim3(seg_threads<D, kSegOut>()), 0, st, p, sp, L, ws,
                        tfrag, gates);
-    prof_end(st);
+    prof_end(p.timer, st);
     return hipGetLastError();
 }
 
@@ -2123,12 +2139,12 @@ hipError_t mfma_correct(const Problem& p, const Split& sp, char* ws, const WsLay
                         hipStream_t st) {
     const int runs = (sp.per + kCorrChunks - 1) / kCorrChunks;  // runs of chunks per segment
     dim3 grid((unsigned)((sp.G - 1) * runs), (unsigned)p.H, (unsigned)p.B);
-    prof_begin("k_correct_mfma", st);
+    prof_begin(p.timer, "k_correct_mfma", st);
     if (p.dk == 128)
         hipLaunchKernelGGL(k_correct_mfma<128>, grid, dim3(512), 0, st, p, sp, L, ws, runs);
     else
         hipLaunchKernelGGL(k_correct_mfma<64>, grid, dim3(512), 0, st, p, sp, L, ws, runs);
-    prof_end(st);
+    prof_end(p.timer, st);
     return hipGetLastError();
 }
 

@@ -106,9 +106,9 @@ hipError_t launch_dt(const Problem& p, hipStream_t st) {
 }  // namespace
 
 hipError_t recurrent_forward(const Problem& p, hipStream_t st) {
-    prof_begin("k_recurrent", st);
+    prof_begin(p.timer, "k_recurrent", st);
     hipError_t e = p.dtype == GDN_BF16 ? launch_dt<1>(p, st) : launch_dt<0>(p, st);
-    prof_end(st);
+    prof_end(p.timer, st);
     return e;
 }
 

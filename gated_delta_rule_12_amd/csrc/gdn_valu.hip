@@ -316,12 +316,12 @@ hipError_t valu_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
         const size_t kw = (size_t)(dk > C ? dk : C) + 1;
         const size_t lds = sizeof(float) * ((size_t)C * kw + (size_t)C * (C + 1) + 3 * C);
-        prof_begin("k_prep_valu", st);
+        prof_begin(p.timer, "k_prep_valu", st);
         if (p.dtype == GDN_BF16)
             hipLaunchKernelGGL(k_prep_valu<1>, grid, dim3(kThreads), lds, st, p, w, wsp);
         else
             hipLaunchKernelGGL(k_prep_valu<0>, grid, dim3(kThreads), lds, st, p, w, wsp);
-        prof_end(st);
+        prof_end(p.timer, st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -329,12 +329,12 @@ hipError_t valu_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
         const int ntiles = dv / kRows + (sp.G > 1 ? dk / kRows : 0);
         dim3 grid(ntiles, (unsigned)(p.H * sp.G), (unsigned)p.B);
         const size_t lds = sizeof(float) * ((size_t)kRows * (dk + 1) + 2 * (size_t)C * (kRows + 1));
-        prof_begin("k_rec_valu", st);
+        prof_begin(p.timer, "k_rec_valu", st);
         if (p.dtype == GDN_BF16)
             hipLaunchKernelGGL(k_rec_valu<1>, grid, dim3(kThreads), lds, st, p, w, wsp, sp, L, ws);
         else
             hipLaunchKernelGGL(k_rec_valu<0>, grid, dim3(kThreads), lds, st, p, w, wsp, sp, L, ws);
-        prof_end(st);
+        prof_end(p.timer, st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -512,10 +512,10 @@ hipError_t seqpar_chain(const Problem& p, const Split& sp, char* ws, const WsLay
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    prof_begin("k_chain", st);
+    prof_begin(p.timer, "k_chain", st);
     hipLaunchKernelGGL(k_chain, grid, dim3(kThreads), lds, st, p, sp, L, ws, write_frag ? 1 : 0,
                        final_step ? 1 : 0);
-    prof_end(st);
+    prof_end(p.timer, st);
     return hipGetLastError();
 }
 
@@ -528,9 +528,9 @@ hipError_t seqpar_finish(const Problem& p, const Split& sp, char* ws, const WsLa
     if (mfma) return mfma_correct(p, sp, ws, L, st);
     {
         dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
-        prof_begin("k_correct", st);
+        prof_begin(p.timer, "k_correct", st);
         hipLaunchKernelGGL(k_correct, grid, dim3(kThreads), 0, st, p, sp, L, ws);
-        prof_end(st);
+        prof_end(p.timer, st);
         return hipGetLastError();
     }
 }
@@ -540,9 +540,9 @@ hipError_t copy_state(const Problem& p, hipStream_t st) {
     const int64_t n = p.B * p.H * p.dv * p.dk;
     if (n == 0) return hipSuccess;
     const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-    prof_begin("k_copy_state", st);
+    prof_begin(p.timer, "k_copy_state", st);
     hipLaunchKernelGGL(k_copy_state, dim3(blocks), dim3(256), 0, st, p);
-    prof_end(st);
+    prof_end(p.timer, st);
     return hipGetLastError();
 }
 

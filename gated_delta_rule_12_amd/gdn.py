@@ -28,7 +28,8 @@ EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_s
            "gdn_decode_step_raw", "gdn_backward", "gdn_backward_workspace_bytes",
            "gdn_workspace_bytes",
            "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_status_str", "gdn_abi_version",
-           "gdn_profile_enable", "gdn_profile_read")
+           "gdn_timer_create", "gdn_timer_destroy", "gdn_timer_read", "gdn_chunk_fwd_timed",
+           "gdn_seqpar_fwd_timed", "gdn_decode_step_timed", "gdn_backward_timed")
 
 _lib = None
 
@@ -78,11 +79,18 @@ def lib():
     L.gdn_status_str.restype = ctypes.c_char_p
     L.gdn_abi_version.argtypes = []
     L.gdn_abi_version.restype = ctypes.c_int
-    L.gdn_profile_enable.argtypes = [ctypes.c_int]
-    L.gdn_profile_enable.restype = ctypes.c_int
-    L.gdn_profile_read.argtypes = [ctypes.c_int, ctypes.c_char_p, sz,
-                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
-    L.gdn_profile_read.restype = ctypes.c_int
+    L.gdn_timer_create.argtypes = [ctypes.POINTER(vp)]
+    L.gdn_timer_create.restype = ctypes.c_int
+    L.gdn_timer_destroy.argtypes = [vp]
+    L.gdn_timer_destroy.restype = ctypes.c_int
+    L.gdn_timer_read.argtypes = [vp, ctypes.c_int, ctypes.c_char_p, sz,
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    L.gdn_timer_read.restype = ctypes.c_int
+    # the *_timed variants: the same arguments plus the timer
+    for name in ("gdn_chunk_fwd", "gdn_seqpar_fwd", "gdn_decode_step", "gdn_backward"):
+        f = getattr(L, name + "_timed")
+        f.argtypes = getattr(L, name).argtypes + [vp]
+        f.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -144,22 +152,50 @@ def gdn_abi_version() -> int:
     return int(lib().gdn_abi_version())
 
 
-def gdn_profile_enable(on: bool) -> int:
-    return int(lib().gdn_profile_enable(1 if on else 0))
+class Timer:
+    """A caller-owned per-kernel timer (gdn_timer_create / gdn_timer_read /
+    gdn_timer_destroy).  Pass it as timer= to the torch-level helpers; they
+    then call the *_timed entry points, which bracket each kernel with HIP
+    events on the launch stream."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        rc = lib().gdn_timer_create(ctypes.byref(h))
+        if rc != GDN_OK:
+            raise GdnError(rc, "gdn_timer_create")
+        self.handle = h
+
+    def read(self):
+        """Every kernel timed so far: {name: (total ms, launches)}."""
+        res = {}
+        buf = ctypes.create_string_buffer(128)
+        i = 0
+        while True:
+            ms, cnt = ctypes.c_double(), ctypes.c_int64()
+            if lib().gdn_timer_read(self.handle, i, buf, 128, ctypes.byref(ms),
+                                    ctypes.byref(cnt)) != GDN_OK:
+                break
+            res[buf.value.decode()] = (ms.value, cnt.value)
+            i += 1
+        return res
+
+    def close(self):
+        if self.handle is not None:
+            lib().gdn_timer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
-def gdn_profile_read():
-    """All kernels recorded since profiling was enabled: {name: (ms, count)}."""
-    res = {}
-    i = 0
-    buf = ctypes.create_string_buffer(128)
-    while True:
-        ms, cnt = ctypes.c_double(), ctypes.c_int64()
-        if lib().gdn_profile_read(i, buf, 128, ctypes.byref(ms), ctypes.byref(cnt)) != GDN_OK:
-            break
-        res[buf.value.decode()] = (ms.value, cnt.value)
-        i += 1
-    return res
+def _call(name, args, timer):
+    """The entry point `name`, or its *_timed variant with the timer."""
+    if timer is None:
+        return getattr(lib(), name)(*args)
+    return getattr(lib(), name + "_timed")(*args, timer.handle)
 
 
 # ---- torch-level helpers -------------------------------------------------------
@@ -223,10 +259,10 @@ def workspace_for(q, v, alpha, chunk=64, n_segments=None):
 
 def chunk_fwd(q, k, v, alpha, beta, state0=None, *, chunk=64,
               order=GDN_PREDICT_THEN_DECAY, scale=1.0, n_segments=None,
-              out=None, state_out=None, workspace=None):
+              out=None, state_out=None, workspace=None, timer=None):
     """Chunkwise forward: gdn_chunk_fwd (the library's schedule) when
     n_segments is None, else gdn_seqpar_fwd with that many segments (1: a
-    single stream).
+    single stream).  timer: a Timer (the *_timed entry point) or None.
     Returns (out [B,T,H,dv] fp32, final state [B,H,dv,dk] fp32)."""
     import torch
     B, T, H, dk, dv, gate = _check(q, k, v, alpha, beta, state0)
@@ -241,11 +277,11 @@ def chunk_fwd(q, k, v, alpha, beta, state0=None, *, chunk=64,
             _ptr(out), _ptr(state_out)]
     tail = [_ptr(workspace), workspace.numel(), _stream()]
     if n_segments is None:
-        rc = gdn_chunk_fwd(*args, *tens, *tail)
         where = "gdn_chunk_fwd"
+        rc = _call(where, [*args, *tens, *tail], timer)
     else:
-        rc = gdn_seqpar_fwd(*args, n_segments, *tens, *tail)
         where = "gdn_seqpar_fwd"
+        rc = _call(where, [*args, n_segments, *tens, *tail], timer)
     if rc != GDN_OK:
         raise GdnError(rc, where)
     return out, state_out
@@ -272,7 +308,8 @@ def recurrent_ref(q, k, v, alpha, beta, state0=None, *, order=GDN_PREDICT_THEN_D
 
 
 def backward(q, k, v, alpha, beta, state0, grad_out, grad_state_out=None, *,
-             order=GDN_PREDICT_THEN_DECAY, scale=1.0, want_grad_state0=True, workspace=None):
+             order=GDN_PREDICT_THEN_DECAY, scale=1.0, want_grad_state0=True, workspace=None,
+             timer=None):
     """Gradients through the forward pass: gdn_backward.
     grad_out [B,T,H,dv] fp32 = dL/d out; grad_state_out [B,H,dv,dk] fp32 =
     dL/d S_T or None (zero).  Returns (dq, dk, dv, dalpha, dbeta, dstate0),
@@ -298,18 +335,19 @@ def backward(q, k, v, alpha, beta, state0, grad_out, grad_state_out=None, *,
     if workspace is None:
         n = gdn_backward_workspace_bytes(B, T, H, dk, dv, gate)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-    rc = gdn_backward(B, T, H, dk, dv, _dtype_code(q), gate, order, scale,
-                      _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state0),
-                      _ptr(grad_out), _ptr(grad_state_out), _ptr(dq), _ptr(dkk), _ptr(dvv),
-                      _ptr(dal), _ptr(dbe), _ptr(ds0), _ptr(workspace), workspace.numel(),
-                      _stream())
+    rc = _call("gdn_backward",
+               [B, T, H, dk, dv, _dtype_code(q), gate, order, scale,
+                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state0),
+                _ptr(grad_out), _ptr(grad_state_out), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                _ptr(dal), _ptr(dbe), _ptr(ds0), _ptr(workspace), workspace.numel(),
+                _stream()], timer)
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_backward")
     return dq, dkk, dvv, dal, dbe, ds0
 
 
 def decode_step(q, k, v, alpha, beta, state=None, *, order=GDN_PREDICT_THEN_DECAY,
-                scale=1.0, out=None, state_out=None, inplace=False, raw=False):
+                scale=1.0, out=None, state_out=None, inplace=False, raw=False, timer=None):
     """One token on a persistent state: gdn_decode_step.
     q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), alpha [B,H] or [B,H,dk], beta
     [B,H] fp32, state [B,H,dv,dk] fp32 or None (zero).  inplace=True writes the
@@ -349,10 +387,12 @@ def decode_step(q, k, v, alpha, beta, state=None, *, order=GDN_PREDICT_THEN_DECA
         out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
     if state_out is None:
         state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
-    fn, name = (gdn_decode_step_raw, "gdn_decode_step_raw") if raw else (gdn_decode_step, "gdn_decode_step")
-    rc = fn(B, H, dk, dv, _dtype_code(q), gate, order, scale,
-            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
-            _ptr(out), _ptr(state_out), _stream())
+    if raw and timer is not None:
+        raise ValueError("the raw decode step has no timed variant")
+    name = "gdn_decode_step_raw" if raw else "gdn_decode_step"
+    rc = _call(name, [B, H, dk, dv, _dtype_code(q), gate, order, scale,
+                      _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+                      _ptr(out), _ptr(state_out), _stream()], timer)
     if rc != GDN_OK:
         raise GdnError(rc, name)
     return out, state_out

@@ -26,8 +26,10 @@
  *   state_out  [B, H, dv, dk] fp32, or NULL if not wanted
  *   workspace  device scratch of at least gdn_workspace_bytes(...) bytes
  *
- * Ownership and lifetime: the library allocates no memory and keeps no state
- * between calls (except the optional profiling record below).  Buffers are
+ * Ownership and lifetime: the library allocates no device memory and keeps no
+ * state between calls (it has no mutable globals, so calls on different
+ * streams or threads may run concurrently; the optional timer below is an
+ * object the caller owns and passes in).  Buffers are
  * borrowed only for the work the call enqueues on `stream` (a hipStream_t;
  * NULL is the null stream).  Calls return after enqueueing; the caller
  * synchronises.  state_out may equal state0 (in-place continuation); out and
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
 enum gdn_gate { GDN_GATE_SCALAR = 0, GDN_GATE_CHANNEL = 1 };
@@ -249,17 +251,57 @@ const char* gdn_status_str(int status);
 int gdn_abi_version(void);
 
 /*
- * Optional per-kernel timing.  gdn_profile_enable(1) makes the entry points
- * bracket every kernel they launch with HIP events recorded on the call's
- * stream (no work is skipped or reordered); gdn_profile_enable(0) stops and
- * discards the record.  gdn_profile_read(i, name, name_len, &ms, &count)
- * synchronises the recorded events and returns, for the i-th distinct kernel
- * seen (0-based), its name, total milliseconds and launch count; it returns
- * GDN_E_ARG past the last kernel.  Process-global; not thread-safe.
+ * Optional per-kernel timing through a caller-owned timer.  The *_timed entry
+ * points below are the entry points of the same name without the suffix,
+ * plus a timer: they bracket every kernel they launch with HIP events
+ * recorded on the call's stream and add the elapsed times to the timer's
+ * record (no work is skipped or reordered; the events cost a few microseconds
+ * of GPU time between kernels).  timer may be NULL (no timing).
+ *
+ * gdn_timer_create makes an empty timer (host memory; its HIP events are
+ * created on first use, on the device current then, and destroyed with it).
+ * gdn_timer_read(t, i, name, name_len, &ms, &count) waits for the recorded
+ * events and returns, for the i-th distinct kernel seen (0-based), its name,
+ * total milliseconds and launch count, or GDN_E_ARG past the last kernel.
+ * A timer must not be used by two calls at once; distinct timers are
+ * independent.  gdn_timer_destroy(NULL) is a no-op.
  */
-int gdn_profile_enable(int on);
-int gdn_profile_read(int index, char* name, size_t name_len, double* total_ms,
-                     int64_t* count);
+typedef struct gdn_timer gdn_timer;
+int gdn_timer_create(gdn_timer** timer);
+int gdn_timer_destroy(gdn_timer* timer);
+int gdn_timer_read(gdn_timer* timer, int index, char* name, size_t name_len,
+                   double* total_ms, int64_t* count);
+
+int gdn_chunk_fwd_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                        int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
+                        float scale,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, const float* state0,
+                        float* out, float* state_out,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        gdn_timer* timer);
+int gdn_seqpar_fwd_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                         int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
+                         float scale, int32_t n_segments,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta, const float* state0,
+                         float* out, float* state_out,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         gdn_timer* timer);
+int gdn_decode_step_timed(int64_t B, int64_t H, int64_t dk, int64_t dv,
+                          int32_t dtype, int32_t gate, int32_t order, float scale,
+                          const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, const float* state_in,
+                          float* out, float* state_out, void* stream, gdn_timer* timer);
+int gdn_backward_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                       int32_t dtype, int32_t gate, int32_t order, float scale,
+                       const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, const float* state0,
+                       const float* grad_out, const float* grad_state_out,
+                       float* grad_q, float* grad_k, float* grad_v, float* grad_alpha,
+                       float* grad_beta, float* grad_state0,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       gdn_timer* timer);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_abi_version() == 2
     for s in (gdn.GDN_OK, gdn.GDN_E_ARG, gdn.GDN_E_SHAPE, gdn.GDN_E_UNSUPPORTED,
               gdn.GDN_E_WORKSPACE, gdn.GDN_E_HIP):
         assert gdn.gdn_status_str(s).startswith("GDN_")
@@ -289,3 +289,34 @@ def test_backward_rejects_bad_arguments_before_any_launch():
     assert call(ok, head=(1, -1, 2, 64, 64) + head[5:]) == gdn.GDN_E_SHAPE
     # empty batch: nothing to do
     assert gdn.gdn_backward(0, T, H, dk, dv, *head[5:], *([nul] * 14), nul, 0, nul) == gdn.GDN_OK
+
+
+def test_timer_is_a_caller_owned_object():
+    """Per-kernel timing lives in a timer the caller creates, passes to the
+    *_timed entry points and destroys; an empty timer reads nothing, a
+    timed call that fails its argument checks records nothing."""
+    t = gdn.Timer()
+    assert t.read() == {}
+    L = gdn.lib()
+    # bad dtype: rejected on the host before any launch or event
+    rc = L.gdn_chunk_fwd_timed(1, 64, 1, 64, 64, 64, 7, 0, 0, 1.0, None, None, None, None, None,
+                               None, None, None, None, 0, None, t.handle)
+    assert rc == gdn.GDN_E_ARG
+    assert t.read() == {}
+    t2 = gdn.Timer()
+    assert t2.handle.value != t.handle.value
+    t.close()
+    t2.close()
+    assert L.gdn_timer_destroy(None) == gdn.GDN_OK
+    assert L.gdn_timer_read(None, 0, None, 0, None, None) == gdn.GDN_E_ARG
+
+
+def test_no_mutable_globals_in_the_library():
+    """The library keeps no state between calls: its writable data sections
+    hold no objects of the library's own, only what the HIP runtime
+    registers (code-object handles and the host stubs of the kernels)."""
+    out = subprocess.run(["nm", "-C", "--defined-only", gdn.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    own = [ln for ln in out.splitlines()
+           if re.search(r"\s[bBdD]\s", ln) and "gdn" in ln and "(" not in ln]
+    assert not own, own
