@@ -2,9 +2,15 @@
 
 One step = one full forward (every kernel of the path) over one batch of the
 workload, inputs already resident in HBM.  Prints ONE JSON line on stdout;
-diagnostics go to stderr.  The timed region holds only the steps; per-kernel
-durations (for the roofline) come from the library's HIP events in a second
-run of the same number of steps.
+diagnostics go to stderr.  After the W warmup steps, untimed steps run for a
+settle period (--settle-ms, default 500 ms: the GPU clock takes tens to
+hundreds of milliseconds of load to reach its working frequency), reported
+as settle_ms / settle_steps.  The timed region holds only the K steps.
+roofline.achieved / frac are the whole step's algorithmic bytes over the
+step's time; per-kernel durations (the dominant kernel's figures) come from
+HIP events the library records on the launch stream into a caller-owned
+timer, in a second run of the same number of steps.  Achievable peaks (a
+device copy and an MFMA loop) are measured in the same run.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main-bf16]
 
@@ -81,6 +87,105 @@ def stored_traffic(workload_name, kernel):
     return None if k is None else round(k["read_bytes"] + k["write_bytes"])
 
 
+def settle(step, settle_ms: float):
+    """Untimed steps until settle_ms of wall time have passed (at least one
+    step); returns (milliseconds, steps)."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step()
+        n += 1
+        if n % 8 == 0 or settle_ms <= 0:
+            torch.cuda.synchronize()
+            el = (time.perf_counter() - t0) * 1e3
+            if el >= settle_ms:
+                return round(el, 1), n
+
+
+def measure_peaks():
+    """Achievable peaks on this device, for fractions beside the vendor ones:
+    a plain 1 GiB device copy (bytes read + written per second) and eight
+    independent chains of 16x16x32 bf16 MFMAs on two waves per SIMD."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "gated_delta_rule_12_amd", "libgdn_peaks.so")
+    L = ctypes.CDLL(path)
+    L.gdn_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.gdn_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    cp = lambda: L.gdn_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                 nbytes, sp)
+    for _ in range(3):
+        assert cp() == 0
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        cp()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    blocks, iters = 2 * 256, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2 * 4 * blocks, dtype=torch.int64, device="cuda")
+    mf = {}
+    for shape, name, flop in ((0, "16x16x32", 16384), (1, "32x32x16", 32768)):
+        run = lambda: L.gdn_peak_mfma(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(clk.data_ptr()),
+                                      shape, blocks, iters, sp)
+        assert run() == 0
+        e0.record(stream)
+        for _ in range(3):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tfs = 3 * blocks * 4 * 8 * iters * flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        c = clk.view(-1, 2).double().mean(0)
+        mf[name] = {"TFs": round(tfs, 1),
+                    # two waves share a SIMD: its cycles per MFMA
+                    "cycles_per_mfma_per_simd": round(float(c[0]) / (8 * iters * 2), 2),
+                    "shader_clock_GHz": round(float(c[0]) / (float(c[1]) / 1e8) / 1e9, 3)}
+    best = max(v["TFs"] for v in mf.values())
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBs": round(copy_gbs, 1), "mfma_bf16_TFs": best, "mfma_bf16_shapes": mf,
+            "how": "1 GiB device copy (16-byte non-temporal loads and stores), read + write bytes; "
+                   "8 independent bf16 MFMA chains per wave, 2 waves per SIMD, best shape"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores() -> int:
+    """Cores this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when the environment sets it (the share of the host a
+    one-GPU job is given)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return n
+
+
+def host_info() -> dict:
+    return {"nproc": len(os.sched_getaffinity(0)), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "cpu_model": cpu_model()}
+
+
 def copy_calibration(mbytes: int, reps: int = 5):
     """A plain device copy of known size, for scaling the FETCH_SIZE and
     WRITE_SIZE counters: each rep reads and writes mbytes MiB."""
@@ -95,12 +200,13 @@ def copy_calibration(mbytes: int, reps: int = 5):
     print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}), flush=True)
 
 
-def cpu_baseline(w, inp, max_threads=16, target_s=10.0):
-    """Time the oracle on a bounded sample of (batch, head) slices."""
+def cpu_baseline(w, inp, target_s=10.0):
+    """Time the oracle on a bounded sample of (batch, head) slices, with
+    min(host cores, B * H) threads (OpenMP over the slices)."""
     import numpy as np
 
     import oracle
-    cores = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    cores = max(1, host_cores())
     pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
     g = oracle.GATE_SCALAR if w.gate == "scalar" else oracle.GATE_CHANNEL
 
@@ -133,7 +239,7 @@ def cpu_baseline(w, inp, max_threads=16, target_s=10.0):
     head_tokens = reps * n_pairs * n_tok
     tok_per_s = head_tokens / dt / w.H   # tokens of the workload (all H heads) per second
     return {"value": tok_per_s, "unit": "tokens/sec", "cores": min(cores, n_pairs),
-            "kind": "oracle",
+            "kind": "oracle", **host_info(),
             "sample": f"{reps} x {n_pairs} (batch,head) slices x {n_tok} tokens of {w.name}, "
                       f"fp64 token loop, {dt:.2f} s; tokens/s = head-tokens/s / H"}
 
@@ -147,13 +253,13 @@ def decode_bytes(w) -> float:
     return float(per_head * w.B * w.H)
 
 
-def cpu_baseline_decode(w, inp, max_threads=16, target_s=10.0, n_pairs=1024):
+def cpu_baseline_decode(w, inp, target_s=10.0, n_pairs=1024):
     """Time the oracle's token loop (T = 1) on a sample of (batch, head)
-    states of the decode batch."""
+    states of the decode batch, one thread per host core."""
     import numpy as np
 
     import oracle
-    cores = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    cores = max(1, host_cores())
     g = oracle.GATE_SCALAR if w.gate == "scalar" else oracle.GATE_CHANNEL
     sel = [(b, h) for b in range(w.B) for h in range(w.H)][:n_pairs]
     pick = lambda name: np.stack([inp[name][b, :, h] for b, h in sel])[:, :, None]
@@ -166,7 +272,7 @@ def cpu_baseline_decode(w, inp, max_threads=16, target_s=10.0, n_pairs=1024):
         dt += time.perf_counter() - t
         reps += 1
     return {"value": reps * len(sel) / w.H / dt, "unit": "tokens/sec", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", **host_info(),
             "sample": f"{reps} x {len(sel)} (batch,head) states of {w.name}, one token each, "
                       f"fp64 token loop, {dt:.2f} s; tokens/s = head-steps/s / H"}
 
@@ -189,6 +295,7 @@ def bench_decode(args, w):
 
     for _ in range(args.warmup):
         step()
+    settle_ms, settle_steps = settle(step, args.settle_ms)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -198,12 +305,13 @@ def bench_decode(args, w):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    gdn.gdn_profile_enable(True)
+    timer = gdn.Timer()
     for _ in range(args.steps):
-        step()
+        gdn.decode_step(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], st,
+                        out=out, inplace=True, timer=timer)
     torch.cuda.synchronize()
-    kern = gdn.gdn_profile_read()
-    gdn.gdn_profile_enable(False)
+    kern = timer.read()
+    timer.close()
     k_us = 1e3 * kern["k_decode"][0] / kern["k_decode"][1]
     # the fused-prologue entry point on the same tensors (read as raw
     # projections and logits): same traffic, a few more operations per head
@@ -221,7 +329,8 @@ def bench_decode(args, w):
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(w, inp)
     res = {"metric": "decode tokens/sec (one gated-delta token per sequence, H=16 d=128)",
            "value": round(w.B / (ms * 1e-3), 1), "unit": "tokens/sec", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": settle_ms,
+           "settle_steps": settle_steps, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f32", "data": "synthetic",
            "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv,
@@ -232,7 +341,8 @@ def bench_decode(args, w):
                         "traffic": stored_traffic(w.name, "k_decode"), "kernel": "k_decode",
                         "kernel_timing": "HIP events around each launch, in a second run of the same steps after the timed region",
                         "kernel_avg_launch_us": round(k_us, 2), "algorithmic_bytes": abytes,
-                        "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1)},
+                        "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
+                        "step_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
            "cpu_baseline": cpu, "raw_prologue_ms_per_step": round(raw_ms, 5)}
     print(json.dumps(res), flush=True)
 
@@ -248,13 +358,13 @@ def backward_bytes(w) -> float:
     return float(per_tok * w.B * w.T * w.H + 12 * w.dk * w.dv * w.B * w.H)
 
 
-def cpu_baseline_backward(w, inp, gr, max_threads=16, target_s=10.0):
+def cpu_baseline_backward(w, inp, gr, target_s=10.0):
     """Time the oracle's backward on (batch, head) slices of the workload,
-    the first n_tok tokens of each."""
+    the first n_tok tokens of each, one slice per host core."""
     import numpy as np
 
     import oracle
-    cores = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    cores = max(1, host_cores())
     g = oracle.GATE_SCALAR if w.gate == "scalar" else oracle.GATE_CHANNEL
     sel = [(b, h) for b in range(w.B) for h in range(w.H)][:cores]
     n_tok = min(w.T, 1024)
@@ -269,8 +379,8 @@ def cpu_baseline_backward(w, inp, gr, max_threads=16, target_s=10.0):
         oracle.backward(*args, s0, dout, ds, gate=g, threads=cores)
         dt += time.perf_counter() - t
         reps += 1
-    return {"value": reps * len(sel) * n_tok / w.H / dt, "unit": "tokens/sec", "cores": cores,
-            "kind": "oracle",
+    return {"value": reps * len(sel) * n_tok / w.H / dt, "unit": "tokens/sec",
+            "cores": min(cores, len(sel)), "kind": "oracle", **host_info(),
             "sample": f"{reps} x {len(sel)} (batch,head) slices x {n_tok} tokens of {w.name}, "
                       f"fp64 backward over stored states, {dt:.2f} s; tokens/s = head-tokens/s / H"}
 
@@ -297,6 +407,7 @@ def bench_backward(args, w):
 
     for _ in range(args.warmup):
         step()
+    settle_ms, settle_steps = settle(step, args.settle_ms)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -306,12 +417,13 @@ def bench_backward(args, w):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    gdn.gdn_profile_enable(True)
+    timer = gdn.Timer()
     for _ in range(args.steps):
-        step()
+        gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], g_out, g_st,
+                     workspace=ws, timer=timer)
     torch.cuda.synchronize()
-    kern = gdn.gdn_profile_read()
-    gdn.gdn_profile_enable(False)
+    kern = timer.read()
+    timer.close()
     k_us = 1e3 * kern["k_backward"][0] / kern["k_backward"][1]
     abytes = backward_bytes(w)
     achieved = abytes / (k_us * 1e-6) / 1e9
@@ -319,7 +431,8 @@ def bench_backward(args, w):
     cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, inp, gr)
     res = {"metric": "backward tokens/sec (gradients through the gated-delta recurrence, H=16 d=128 T=8K)",
            "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/sec", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": settle_ms,
+           "settle_steps": settle_steps, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f32", "data": "synthetic",
            "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
@@ -333,7 +446,8 @@ def bench_backward(args, w):
                         "kernel_avg_launch_us": round(k_us, 2), "algorithmic_bytes": abytes,
                         "kernel_us_per_step": {n: round(1e3 * v[0] / args.steps, 2)
                                                for n, v in kern.items()},
-                        "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1)},
+                        "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
+                        "step_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
            "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
@@ -342,9 +456,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # the GPU clock takes tens of milliseconds of load to settle: 200 untimed
-    # steps (about 0.1 s on the main workload) before the timed region
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    # the GPU clock takes tens to hundreds of milliseconds of load to reach
+    # its working frequency: untimed steps for this long after the warmup
+    ap.add_argument("--settle-ms", type=float, default=500.0)
     ap.add_argument("--workload", default="main-bf16")
     ap.add_argument("--segments", type=int, default=None,
                     help="sequence-parallel segments (default: the workload's)")
@@ -391,19 +506,19 @@ def main():
     st = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
     ws = gdn.workspace_for(d["q"], d["v"], d["alpha"], w.chunk, G)
 
-    def step(nseg=G):
+    def step(nseg=G, timer=None):
         gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
                       chunk=w.chunk, n_segments=nseg, out=out, state_out=st,
-                      workspace=ws if nseg == G else None)
+                      workspace=ws if nseg == G else None, timer=timer)
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    log("warmup done")
+    settle_ms, settle_steps = settle(step, args.settle_ms)
+    log(f"warmup done ({args.warmup} steps, then {settle_steps} steps in {settle_ms} ms to settle)")
 
     # timed region: events on the stream the kernels are launched on, and no
     # per-kernel events inside it (each costs a few microseconds of GPU time
-    # between kernels: ~28 us per step on the main workload)
+    # between kernels)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -413,16 +528,15 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    # per-kernel durations: the same number of steps again, each kernel
-    # bracketed by the library's HIP events on the launch stream
-    gdn.gdn_profile_enable(True)
+    # per-kernel durations: the same number of steps again through the timed
+    # entry point, each kernel bracketed by HIP events on the launch stream
+    timer = gdn.Timer()
     for _ in range(args.steps):
-        step()
+        step(timer=timer)
     torch.cuda.synchronize()
-    kern = gdn.gdn_profile_read()
-    gdn.gdn_profile_enable(False)
-    # per step: total time of each kernel (several launches per step when the
-    # path is pipelined over chunk slabs) and its launches
+    kern = timer.read()
+    timer.close()
+    # per step: total time of each kernel and its launches
     per_kernel_us = {k: 1e3 * v[0] / args.steps for k, v in kern.items()}
     launches = {k: v[1] / args.steps for k, v in kern.items()}
     dominant = max(per_kernel_us, key=per_kernel_us.get) if per_kernel_us else None
@@ -433,24 +547,37 @@ def main():
     value = tokens / (ms * 1e-3)
     abytes = algorithmic_bytes(w)
     aflops = algorithmic_flops(w)
-    # dominant kernel: each launch covers an equal share of the head-tokens and
-    # their algorithmic bytes, so bytes per launch / average launch time equals
-    # bytes per step / that kernel's time per step
-    dom_us = per_kernel_us[dominant]
-    achieved = abytes / (dom_us * 1e-6) / 1e9
+    peaks = measure_peaks()
+    log(f"achievable peaks: {peaks}")
+    # the roofline is the whole step's: its algorithmic bytes over its time
     step_achieved = abytes / (ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(w.name, dominant) if args.segments is None else None,
-            "kernel": dominant,
-            "kernel_timing": "HIP events around each launch, in a second run of the same steps after the timed region",
-            "kernel_launches_per_step": launches[dominant],
-            "kernel_avg_launch_us": round(dom_us / launches[dominant], 2),
-            "kernel_us_per_step": {k: round(v, 2) for k, v in per_kernel_us.items()},
+    # counted HBM traffic of the step: every kernel's stored counters (only
+    # while they were taken on the current kernel sources)
+    traffic = None
+    if args.segments is None:
+        parts = [stored_traffic(w.name, k) for k in per_kernel_us]
+        traffic = None if any(t_ is None for t_ in parts) else int(sum(parts))
+    # the dominant kernel (longest per step): each launch covers every
+    # head-token, so the step's algorithmic bytes over its average launch
+    dom_us = per_kernel_us[dominant]
+    dom_launch_us = dom_us / launches[dominant]
+    dom_achieved = abytes / (dom_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(step_achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(step_achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "whole step: " + " + ".join(per_kernel_us),
             "algorithmic_bytes": abytes,
-            "step_achieved": round(step_achieved, 1),
-            "step_frac": round(step_achieved / HBM_PEAK_GBS, 4),
-            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+            "frac_of_achievable_copy": round(step_achieved / peaks["hbm_copy_GBs"], 4),
+            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_of_achievable": round(aflops / (ms * 1e-3) / 1e12 / peaks["mfma_bf16_TFs"], 4),
+            "kernel_us_per_step": {k: round(v, 2) for k, v in per_kernel_us.items()},
+            "kernel_timing": "HIP events around each launch (caller-owned timer), in a second run of the same steps after the timed region",
+            "dominant_kernel": {
+                "kernel": dominant, "launches_per_step": launches[dominant],
+                "avg_launch_us": round(dom_launch_us, 2),
+                "achieved": round(dom_achieved, 1), "frac": round(dom_achieved / HBM_PEAK_GBS, 4),
+                "traffic": stored_traffic(w.name, dominant) if args.segments is None else None},
+            "achievable_peaks": peaks}
 
     extra = {}
     if G is not None and G > 1 and not args.no_single_stream:
@@ -473,7 +600,8 @@ def main():
         log(f"cpu baseline: {cpu}")
 
     res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/sec", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": settle_ms,
+           "settle_steps": settle_steps, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16" if path == gdn.GDN_PATH_MFMA else "f32",
            "data": "synthetic",

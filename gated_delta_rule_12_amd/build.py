@@ -11,6 +11,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
+# achievable-peak probes for the benchmark (a library of their own)
+PEAKS_SRC = os.path.join(HERE, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(HERE, "libgdn_peaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: hipcc must not emit packed fp32 ALU instructions.
@@ -38,8 +41,11 @@ def build(verbose: bool = False) -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = PEAKS_LIB + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, *FLAGS, "-shared", "-o", tmp, PEAKS_SRC], check=True)
+    os.replace(tmp, PEAKS_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PEAKS_LIB)
     return LIB
 
 
