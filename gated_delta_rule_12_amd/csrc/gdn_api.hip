@@ -239,6 +239,7 @@ const char* gdn_status_str(int status) {
         case GDN_E_UNSUPPORTED: return "GDN_E_UNSUPPORTED: dk/dv must be multiples of 16 up to 128, chunk 16, 32 or 64";
         case GDN_E_WORKSPACE: return "GDN_E_WORKSPACE: workspace missing or smaller than gdn_workspace_bytes()";
         case GDN_E_HIP: return "GDN_E_HIP: a HIP runtime call or kernel launch failed";
+        case GDN_E_SCRATCH: return "GDN_E_SCRATCH: the problem needs more workspace than gdn_chunk_fwd_noalloc's static scratch (GDN_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown gdn status";
     }
 }

@@ -21,6 +21,8 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_SCALAR, GDN_GATE_CHANNEL = 0, 1
 GDN_PREDICT_THEN_DECAY, GDN_DECAY_THEN_PREDICT = 0, 1
 GDN_OK, GDN_E_ARG, GDN_E_SHAPE, GDN_E_UNSUPPORTED, GDN_E_WORKSPACE, GDN_E_HIP = 0, -1, -2, -3, -4, -5
+GDN_E_SCRATCH = -6
+GDN_NOALLOC_SCRATCH_BYTES = 128 << 20
 GDN_PATH_VALU, GDN_PATH_MFMA = 0, 1
 
 # every symbol include/gdn.h declares
@@ -29,7 +31,8 @@ EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_s
            "gdn_workspace_bytes",
            "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_status_str", "gdn_abi_version",
            "gdn_timer_create", "gdn_timer_destroy", "gdn_timer_read", "gdn_chunk_fwd_timed",
-           "gdn_seqpar_fwd_timed", "gdn_decode_step_timed", "gdn_backward_timed")
+           "gdn_seqpar_fwd_timed", "gdn_decode_step_timed", "gdn_backward_timed",
+           "gdn_chunk_fwd_noalloc")
 
 _lib = None
 
@@ -55,6 +58,8 @@ def lib():
     tens = [vp] * 8
     L.gdn_chunk_fwd.argtypes = shape + [i32, i32, i32, i32, f32] + tens + [vp, sz, vp]
     L.gdn_chunk_fwd.restype = ctypes.c_int
+    L.gdn_chunk_fwd_noalloc.argtypes = shape + [i32, i32, i32, i32, f32] + tens + [vp]
+    L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     L.gdn_seqpar_fwd.argtypes = shape + [i32, i32, i32, i32, f32, i32] + tens + [vp, sz, vp]
     L.gdn_seqpar_fwd.restype = ctypes.c_int
     L.gdn_recurrent_ref.argtypes = shape + [i32, i32, i32, f32] + tens + [vp]
@@ -284,6 +289,25 @@ def chunk_fwd(q, k, v, alpha, beta, state0=None, *, chunk=64,
         rc = _call(where, [*args, n_segments, *tens, *tail], timer)
     if rc != GDN_OK:
         raise GdnError(rc, where)
+    return out, state_out
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, beta, state0=None, *, chunk=64,
+                      order=GDN_PREDICT_THEN_DECAY, scale=1.0, out=None, state_out=None):
+    """gdn_chunk_fwd_noalloc: the forward with the library's static device
+    scratch as its workspace (the call itself allocates nothing; out and
+    state_out are allocated here when not given)."""
+    import torch
+    B, T, H, dk, dv, gate = _check(q, k, v, alpha, beta, state0)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    if state_out is None:
+        state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    rc = lib().gdn_chunk_fwd_noalloc(B, T, H, dk, dv, chunk, _dtype_code(q), gate, order, scale,
+                                     _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(state0), _ptr(out), _ptr(state_out), _stream())
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd_noalloc")
     return out, state_out
 
 

@@ -29,7 +29,8 @@
  * Ownership and lifetime: the library allocates no device memory and keeps no
  * state between calls (it has no mutable globals, so calls on different
  * streams or threads may run concurrently; the optional timer below is an
- * object the caller owns and passes in).  Buffers are
+ * object the caller owns and passes in; gdn_chunk_fwd_noalloc alone keeps
+ * the address of its static scratch array per device).  Buffers are
  * borrowed only for the work the call enqueues on `stream` (a hipStream_t;
  * NULL is the null stream).  Calls return after enqueueing; the caller
  * synchronises.  state_out may equal state0 (in-place continuation); out and
@@ -73,7 +74,8 @@ enum gdn_status {
     GDN_E_SHAPE = -2,        /* negative or inconsistent size */
     GDN_E_UNSUPPORTED = -3,  /* valid but not built (dk, dv, chunk) */
     GDN_E_WORKSPACE = -4,    /* workspace NULL or smaller than required */
-    GDN_E_HIP = -5           /* a HIP call failed */
+    GDN_E_HIP = -5,          /* a HIP call failed */
+    GDN_E_SCRATCH = -6       /* larger than gdn_chunk_fwd_noalloc's static scratch */
 };
 enum gdn_path { GDN_PATH_VALU = 0, GDN_PATH_MFMA = 1 };
 
@@ -100,6 +102,30 @@ int gdn_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                   const float* alpha, const float* beta, const float* state0,
                   float* out, float* state_out,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_chunk_fwd_noalloc — gdn_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same call without a workspace argument, running
+ * the same kernels with the same results.  Its workspace is a static device
+ * array of GDN_NOALLOC_SCRATCH_BYTES (128 MiB) that every GPU this entry point
+ * runs on holds until the process ends; the first call on a device looks up
+ * the array's address there (the only state the library keeps between
+ * calls).  It allocates nothing and makes no hipMalloc/hipFree call.
+ * Problems whose gdn_workspace_bytes(..., n_segments = 1) exceed that size
+ * return GDN_E_SCRATCH before anything is enqueued (the main workload,
+ * 2 x 16 heads x 8192 tokens at d = 128, needs 100.25 MiB).  Every call on a
+ * GPU shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, threads or processes sharing the device) race and must be
+ * ordered by the caller.  Other statuses as for gdn_chunk_fwd.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdn_chunk_fwd_noalloc(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                          int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
+                          float scale,
+                          const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, const float* state0,
+                          float* out, float* state_out, void* stream);
 
 /*
  * gdn_recurrent_ref — the token-by-token recurrence on the GPU (fp32 state

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version_and_status_strings():
     assert gdn.gdn_abi_version() == 2
     for s in (gdn.GDN_OK, gdn.GDN_E_ARG, gdn.GDN_E_SHAPE, gdn.GDN_E_UNSUPPORTED,
-              gdn.GDN_E_WORKSPACE, gdn.GDN_E_HIP):
+              gdn.GDN_E_WORKSPACE, gdn.GDN_E_HIP, gdn.GDN_E_SCRATCH):
         assert gdn.gdn_status_str(s).startswith("GDN_")
     assert "unknown" in gdn.gdn_status_str(42)
 
@@ -313,10 +313,28 @@ def test_timer_is_a_caller_owned_object():
 
 def test_no_mutable_globals_in_the_library():
     """The library keeps no state between calls: its writable data sections
-    hold no objects of the library's own, only what the HIP runtime
-    registers (code-object handles and the host stubs of the kernels)."""
+    hold only what the HIP runtime registers (code-object handles and the
+    host stubs of the kernels) and, for gdn_chunk_fwd_noalloc, the host-side
+    stand-in of its static device scratch and the per-device cache of that
+    array's device address."""
     out = subprocess.run(["nm", "-C", "--defined-only", gdn.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
-    own = [ln for ln in out.splitlines()
-           if re.search(r"\s[bBdD]\s", ln) and "gdn" in ln and "(" not in ln]
-    assert not own, own
+    runtime = re.compile(r"^(__hip_|__do_init|__do_fini|__dso_handle|__init|__fini|_DYNAMIC|"
+                         r"_GLOBAL_OFFSET_TABLE_|DW\.ref\.)")
+    own = []
+    for ln in out.splitlines():
+        parts = ln.split(None, 2)
+        if len(parts) < 3 or parts[1] not in "bBdD" or "(" in parts[2].replace("(anonymous namespace)", ""):
+            continue
+        if not runtime.match(parts[2]):
+            own.append(parts[2])
+    assert sorted(own) == ["(anonymous namespace)::g_scratch_addr", "(anonymous namespace)::scratch"], own
+
+
+def test_noalloc_refuses_problems_past_the_scratch_on_the_host():
+    """The size check runs on the host before any HIP call (no GPU needed)."""
+    rc = gdn.lib().gdn_chunk_fwd_noalloc(8, 4096, 16, 128, 128, 64, gdn.GDN_BF16,
+                                         gdn.GDN_GATE_CHANNEL, 0, 1.0, None, None, None, None,
+                                         None, None, None, None, None)
+    assert rc == gdn.GDN_E_SCRATCH
+    assert gdn.gdn_workspace_bytes(2, 8192, 16, 128, 128, 64, gdn.GDN_BF16, 0, 1) <= gdn.GDN_NOALLOC_SCRATCH_BYTES
