@@ -464,6 +464,9 @@ def main():
     ap.add_argument("--segments", type=int, default=None,
                     help="sequence-parallel segments (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--raw", action="store_true",
+                    help="time gdn_chunk_fwd_raw (raw q, k and gate / beta logits, the block's "
+                         "prologue fused in) on the workload's shapes")
     ap.add_argument("--backward", action="store_true",
                     help="time gdn_backward on the workload instead of the forward")
     ap.add_argument("--no-single-stream", action="store_true",
@@ -496,7 +499,11 @@ def main():
     G = args.segments if args.segments is not None else (w.n_segments if w.n_segments > 1 else None)
     log(f"workload {w}, segments {G if G is not None else 'library schedule'}")
     t = time.time()
-    inp = make_inputs(w)
+    if args.raw:
+        from gated_delta_rule_12_amd.workloads import make_raw_inputs
+        inp = make_raw_inputs(w)
+    else:
+        inp = make_inputs(w)
     d = to_device(inp, w, "cuda")
     log(f"inputs ready in {time.time() - t:.1f} s")
     dt_code = gdn.GDN_BF16 if w.dtype == "bf16" else gdn.GDN_F32
@@ -505,8 +512,18 @@ def main():
     out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
     st = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
     ws = gdn.workspace_for(d["q"], d["v"], d["alpha"], w.chunk, G)
+    ws_raw = None
+    if args.raw:
+        if G is not None:
+            raise SystemExit("--raw runs the library's schedule (gdn_chunk_fwd_raw); no --segments")
+        ws_raw = torch.empty(max(1, gdn.lib().gdn_raw_workspace_bytes(
+            w.B, w.T, w.H, w.dk, w.dv, w.chunk, dt_code, gate_code)), dtype=torch.uint8, device="cuda")
 
     def step(nseg=G, timer=None):
+        if args.raw:
+            gdn.chunk_fwd_raw(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
+                              chunk=w.chunk, out=out, state_out=st, workspace=ws_raw)
+            return
         gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
                       chunk=w.chunk, n_segments=nseg, out=out, state_out=st,
                       workspace=ws if nseg == G else None, timer=timer)
@@ -530,12 +547,16 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     # per-kernel durations: the same number of steps again through the timed
     # entry point, each kernel bracketed by HIP events on the launch stream
-    timer = gdn.Timer()
-    for _ in range(args.steps):
-        step(timer=timer)
-    torch.cuda.synchronize()
-    kern = timer.read()
-    timer.close()
+    # (the raw entry point has no timed variant: its line carries the step's
+    # figures only, and per-kernel times come from rocprofv3)
+    kern = {}
+    if not args.raw:
+        timer = gdn.Timer()
+        for _ in range(args.steps):
+            step(timer=timer)
+        torch.cuda.synchronize()
+        kern = timer.read()
+        timer.close()
     # per step: total time of each kernel and its launches
     per_kernel_us = {k: 1e3 * v[0] / args.steps for k, v in kern.items()}
     launches = {k: v[1] / args.steps for k, v in kern.items()}
@@ -554,29 +575,30 @@ def main():
     # counted HBM traffic of the step: every kernel's stored counters (only
     # while they were taken on the current kernel sources)
     traffic = None
-    if args.segments is None:
+    if args.segments is None and per_kernel_us:
         parts = [stored_traffic(w.name, k) for k in per_kernel_us]
         traffic = None if any(t_ is None for t_ in parts) else int(sum(parts))
     # the dominant kernel (longest per step): each launch covers every
     # head-token, so the step's algorithmic bytes over its average launch
-    dom_us = per_kernel_us[dominant]
-    dom_launch_us = dom_us / launches[dominant]
-    dom_achieved = abytes / (dom_us * 1e-6) / 1e9
+    dom = None
+    if dominant is not None:
+        dom_us = per_kernel_us[dominant]
+        dom_achieved = abytes / (dom_us * 1e-6) / 1e9
+        dom = {"kernel": dominant, "launches_per_step": launches[dominant],
+               "avg_launch_us": round(dom_us / launches[dominant], 2),
+               "achieved": round(dom_achieved, 1), "frac": round(dom_achieved / HBM_PEAK_GBS, 4),
+               "traffic": stored_traffic(w.name, dominant) if args.segments is None else None}
     roof = {"bound": "hbm", "achieved": round(step_achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(step_achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "whole step: " + " + ".join(per_kernel_us),
+            "kernel": "whole step: " + (" + ".join(per_kernel_us) if per_kernel_us else "gdn_chunk_fwd_raw"),
             "algorithmic_bytes": abytes,
             "frac_of_achievable_copy": round(step_achieved / peaks["hbm_copy_GBs"], 4),
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "mfma_frac_of_achievable": round(aflops / (ms * 1e-3) / 1e12 / peaks["mfma_bf16_TFs"], 4),
             "kernel_us_per_step": {k: round(v, 2) for k, v in per_kernel_us.items()},
             "kernel_timing": "HIP events around each launch (caller-owned timer), in a second run of the same steps after the timed region",
-            "dominant_kernel": {
-                "kernel": dominant, "launches_per_step": launches[dominant],
-                "avg_launch_us": round(dom_launch_us, 2),
-                "achieved": round(dom_achieved, 1), "frac": round(dom_achieved / HBM_PEAK_GBS, 4),
-                "traffic": stored_traffic(w.name, dominant) if args.segments is None else None},
+            "dominant_kernel": dom,
             "achievable_peaks": peaks}
 
     extra = {}
@@ -607,7 +629,8 @@ def main():
            "data": "synthetic",
            "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                       "chunk": w.chunk, "gate": w.gate, "input_dtype": w.dtype,
-                      "entry": "gdn_seqpar_fwd" if G is not None else "gdn_chunk_fwd",
+                      "entry": "gdn_chunk_fwd_raw" if args.raw else (
+                          "gdn_seqpar_fwd" if G is not None else "gdn_chunk_fwd"),
                       "segments": G if G is not None else gdn.gdn_chunk_segments(
                           w.B, w.T, w.H, w.dk, w.dv, w.chunk, dt_code, gate_code),
                       "global_batch": w.B, "seq_len": w.T,

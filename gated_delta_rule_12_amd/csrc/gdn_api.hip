@@ -107,7 +107,8 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
                 int32_t dtype, int32_t gate, int32_t order, float scale, int32_t n_segments,
                 const void* q, const void* k, const void* v, const float* alpha,
                 const float* beta, const float* state0, float* out, float* state_out,
-                void* workspace, size_t workspace_bytes, void* stream, gdn_timer* timer) {
+                void* workspace, size_t workspace_bytes, void* stream, gdn_timer* timer,
+                bool raw = false) {
     // n_segments == 0: the library picks the schedule (gdn_chunk_fwd)
     int s = validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments > 0 ? n_segments : 1);
     if (s != GDN_OK) return s;
@@ -119,9 +120,26 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
     p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
     p.s0 = state0; p.out = out; p.s_out = state_out;
     p.timer = timer;
+    p.raw = raw ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p.NC == 0) return finish(copy_state(p, st));
     const Split sp = make_split(p.NC, n_segments);
+    if (raw && !mfma_supported(dk, dv, chunk, dtype, gate)) {
+        // vector-ALU family: the prologue writes normalised fp32 inputs into
+        // the workspace (after the forward's own part), then the fp32 forward
+        Problem pf = p;
+        pf.dtype = GDN_F32;
+        pf.raw = 0;
+        const size_t base = align256(valu_layout(pf, sp).total);
+        if (!workspace || workspace_bytes < base + raw_inputs_bytes(p)) return GDN_E_WORKSPACE;
+        if (!aligned(workspace, 16)) return GDN_E_ARG;
+        char* ws = static_cast<char*>(workspace);
+        const RawInputs r = raw_inputs_at(p, ws + base);
+        const hipError_t e = raw_prologue(p, r, st);
+        if (e != hipSuccess) return GDN_E_HIP;
+        pf.q = r.q; pf.k = r.k; pf.v = r.v; pf.alpha = r.alpha; pf.beta = r.beta;
+        return finish(valu_forward(pf, sp, ws, st));
+    }
     const WsLayout L = layout_for(p, sp);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return GDN_E_WORKSPACE;
     if (!aligned(workspace, 16)) return GDN_E_ARG;  // (moved in 16-byte pieces)
@@ -294,6 +312,26 @@ int gdn_chunk_fwd_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                         void* workspace, size_t workspace_bytes, void* stream, gdn_timer* timer) {
     return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, 0, q, k, v, alpha,
                        beta, state0, out, state_out, workspace, workspace_bytes, stream, timer);
+}
+
+int gdn_chunk_fwd_raw(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                      int32_t dtype, int32_t gate, int32_t order, float scale,
+                      const void* q, const void* k, const void* v, const float* alpha_logit,
+                      const float* beta_logit, const float* state0, float* out, float* state_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, 0, q, k, v, alpha_logit,
+                       beta_logit, state0, out, state_out, workspace, workspace_bytes, stream, nullptr,
+                       true);
+}
+
+size_t gdn_raw_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                               int32_t chunk, int32_t dtype, int32_t gate) {
+    if (validate(B, T, H, dk, dv, chunk, dtype, gate, 0, 1) != GDN_OK) return 0;
+    if (mfma_supported(dk, dv, chunk, dtype, gate))
+        return gdn_workspace_bytes(B, T, H, dk, dv, chunk, dtype, gate, 1);
+    Problem p = make_problem(B, T, H, dk, dv, chunk, GDN_F32, gate, 0, 1.f);
+    if (p.NC == 0 || B * H == 0) return 0;
+    return align256(valu_layout(p, make_split(p.NC, 1)).total) + raw_inputs_bytes(p);
 }
 
 int gdn_seqpar_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,

@@ -18,6 +18,8 @@ struct Problem {
     int dtype;    // GDN_F32 / GDN_BF16
     int gate;     // GDN_GATE_SCALAR / GDN_GATE_CHANNEL
     int order;    // GDN_PREDICT_THEN_DECAY / GDN_DECAY_THEN_PREDICT
+    int raw;      // 1: q, k raw projections (L2-normalised on the fly, as fp32
+                  // row factors) and alpha, beta logits (through a sigmoid)
     float scale;
     const void* q;
     const void* k;
@@ -105,6 +107,20 @@ size_t backward_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
 size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate);
 hipError_t backward(const BwdProblem& a, hipStream_t st);
 
+// Raw projections on the vector-ALU family: the prologue's fp32 outputs in
+// the workspace (raw_inputs_bytes of it, at raw_inputs_at), then the forward
+// runs on them as fp32 inputs.
+struct RawInputs {
+    float* q;
+    float* k;
+    float* v;
+    float* alpha;
+    float* beta;
+};
+size_t raw_inputs_bytes(const Problem& p);
+RawInputs raw_inputs_at(const Problem& p, char* base);
+hipError_t raw_prologue(const Problem& p, const RawInputs& r, hipStream_t st);
+
 // Start state copy/zero for empty sequences (T == 0).
 hipError_t copy_state(const Problem& p, hipStream_t st);
 
@@ -118,6 +134,16 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace gdn
 
 // Device helpers -----------------------------------------------------------
+
+// The block's gate and beta from logits: sigmoid(x) = 1 / (1 + e^-x) and its
+// logarithm log sigmoid(x) = -log(1 + e^-x), formed without overflow for
+// either sign of x.
+__device__ __forceinline__ float gdn_sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float gdn_log_sigmoid(float x) {
+    return x >= 0.f ? -log1pf(expf(-x)) : x - log1pf(expf(x));
+}
+// 1 / |x| for an L2 length squared, 0 for a zero vector (it stays zero)
+__device__ __forceinline__ float gdn_inv_len(float sumsq) { return sumsq > 0.f ? rsqrtf(sumsq) : 0.f; }
 
 __device__ __forceinline__ float gdn_bf16_to_f32(uint16_t x) {
     return __uint_as_float(uint32_t(x) << 16);

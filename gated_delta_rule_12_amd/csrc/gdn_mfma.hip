@@ -112,8 +112,16 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
 // stage 1: T' and the gate block per chunk-head
 // ---------------------------------------------------------------------------
 // Gate block (floats): [0,64) gamma_t, [64,128) gamma'_t, [128,192)
-// gamma_C / gamma_t, [192,256) g_t, [256] gamma_C.
-constexpr int kGateFloats = 272;
+// gamma_C / gamma_t, [192,256) g_t, [256] gamma_C; for raw projections
+// (gdn_chunk_fwd_raw) the row factors of the L2 norm are folded in:
+// gamma_t / |q_t|, gamma'_t / |k_t|, (gamma_C / gamma_t) / |k_t|, and
+// [272,336) 1 / |q_t|, [336,400) 1 / |k_t| for the scores.
+constexpr int kGateFloats = 400;
+constexpr int kGateRq = 272, kGateRk = 336;
+constexpr int kGatePieces = 272 / 4, kGatePiecesRaw = kGateFloats / 4;  // 16-byte pieces read
+// Channel gate: the C x D log2-prefix table, then (raw) 1 / |q_t|, 1 / |k_t|.
+template <int D>
+constexpr int kChanFloats = C * D + 2 * C;
 // T' fragments kept per chunk: (m, s) with s <= m / 2 (T' is lower triangular)
 constexpr int kTslots = 6;
 constexpr int kTfragPerChunk = kTslots * 2 * 64;  // [slot][hi/lo][lane] of u16x8
@@ -251,7 +259,42 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
         kv[k] = u32x4{0, 0, 0, 0};
         if (t < nt) kv[k] = *reinterpret_cast<const u32x4*>(kin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
     }
-    if (w == 0) bsh[l] = l < nt ? p.beta[((int64_t)b * T + t0 + l) * H + h] : 0.f;
+    if (w == 0) {
+        float bt = 0.f;
+        if (l < nt) {
+            bt = p.beta[((int64_t)b * T + t0 + l) * H + h];
+            if (p.raw) bt = gdn_sigmoid(bt);
+        }
+        bsh[l] = bt;
+    }
+    // raw projections: 1 / |k_t| and 1 / |q_t| (each row's pieces sit on PPR
+    // consecutive lanes); otherwise ones
+    __shared__ float rqsh[C], rksh[C];
+    if (p.raw) {
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
+            u32x4 qv = u32x4{0, 0, 0, 0};
+            if (t < nt) qv = *reinterpret_cast<const u32x4*>(qin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                const float x = gdn_bf16_to_f32(__builtin_bit_cast(u16x8, kv[k])[e2]);
+                const float y = gdn_bf16_to_f32(__builtin_bit_cast(u16x8, qv)[e2]);
+                sk += x * x;
+                sq += y * y;
+            }
+            sk = row_sum<PPR>(sk);
+            sq = row_sum<PPR>(sq);
+            if (c8 == 0) {
+                rksh[t] = gdn_inv_len(sk);
+                rqsh[t] = gdn_inv_len(sq);
+            }
+        }
+    } else if (w == 0) {
+        rksh[l] = 1.f;
+        rqsh[l] = 1.f;
+    }
     // log2 prefix lam[t][a] = sum_{s <= t} log2 alpha_sa (padding tokens add
     // zero): thread (group, a4) scans TPG tokens of four channels in
     // registers, then adds the totals of the earlier groups
@@ -266,7 +309,13 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
         if (t < nt) {
             const f32x4 av = *reinterpret_cast<const f32x4*>(
                 p.alpha + (((int64_t)b * T + t0 + t) * H + h) * D + 4 * a4);
-            run += f32x4{__log2f(av[0]), __log2f(av[1]), __log2f(av[2]), __log2f(av[3])};
+            if (p.raw) {
+                constexpr float kLog2e = 1.4426950408889634f;
+                run += kLog2e * f32x4{gdn_log_sigmoid(av[0]), gdn_log_sigmoid(av[1]), gdn_log_sigmoid(av[2]),
+                                      gdn_log_sigmoid(av[3])};
+            } else {
+                run += f32x4{__log2f(av[0]), __log2f(av[1]), __log2f(av[2]), __log2f(av[3])};
+            }
         }
         vals[u] = run;
     }
@@ -288,11 +337,15 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
     // the prefix table for the chunk loop (after the K rows, whose wait on
     // the vector-memory counter would otherwise include these stores)
     {
-        float* gdst = gates + ch * (int64_t)C * D;
+        float* gdst = gates + ch * (int64_t)kChanFloats<D>;
 #pragma unroll
         for (int u = 0; u < TPG; ++u) {
             const int t = grp * TPG + u;
             *reinterpret_cast<f32x4*>(&gdst[t * D + 4 * a4]) = *reinterpret_cast<const f32x4*>(&gt[t][4 * a4]);
+        }
+        if (p.raw && w == 0) {
+            gdst[C * D + l] = rqsh[l];
+            gdst[C * D + C + l] = rksh[l];
         }
     }
     __syncthreads();
@@ -308,6 +361,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
     const int pa = 16 * w - 1, t = 16 * w + c16;
     const int tp = ptd ? t - 1 : t;  // row of lam' (-1: zero)
     const f32x4 z4 = zero4();
+    const float rq_t = rqsh[t], rk_t = rksh[t];
     u16x8 qh[D / 32], ql[D / 32], lh[D / 32], ll[D / 32];
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
@@ -330,8 +384,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
             for (int u = 0; u < 2; ++u) {
                 const int ee = e + u;
                 const float g_p = ee < 4 ? gp0[ee] : gp1[ee - 4];
-                xq[u] = gdn_bf16_to_f32(qt[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gt0[ee] : gt1[ee - 4]) - g_p);
-                xl[u] = gdn_bf16_to_f32(kt_[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gq0[ee] : gq1[ee - 4]) - g_p);
+                xq[u] = rq_t * gdn_bf16_to_f32(qt[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gt0[ee] : gt1[ee - 4]) - g_p);
+                xl[u] = rk_t * gdn_bf16_to_f32(kt_[ee]) * __builtin_amdgcn_exp2f((ee < 4 ? gq0[ee] : gq1[ee - 4]) - g_p);
             }
             split2(xq[0], xq[1], h1[e >> 1], l1[e >> 1]);
             split2(xl[0], xl[1], h2[e >> 1], l2[e >> 1]);
@@ -375,11 +429,12 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
                         sl += gdn_bf16_to_f32(Ks[t * LDK + a]) * kj * __builtin_amdgcn_exp2f(lq - gt[jj][a]);
                     }
                 }
-                aP[r] = sp;
-                aL[r] = sl;
+                aP[r] = rq_t * rksh[jj] * sp;
+                aL[r] = rk_t * rksh[jj] * sl;
             }
         } else {
             f32x4 aP2 = zero4(), aL2 = zero4();
+            const float rk_j = rksh[j];
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
                 const int a0 = 32 * s + 8 * g4;
@@ -395,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfr
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         const int ee = e + u;
-                        xa[u] = gdn_bf16_to_f32(kj[ee]) *
+                        xa[u] = rk_j * gdn_bf16_to_f32(kj[ee]) *
                                 __builtin_amdgcn_exp2f((ee < 4 ? gp0[ee] : gp1[ee - 4]) - (ee < 4 ? gj0[ee] : gj1[ee - 4]));
                     }
                     split2(xa[0], xa[1], ah[e >> 1], al[e >> 1]);
@@ -457,6 +512,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
     __shared__ float Pscr[4][16 * 17];  // per-wave scratch of the diagonal inverse
     __shared__ float gsh[C], gpsh[C], bsh[C];
+    __shared__ float rqsh[C], rksh[C];  // 1 / |q_t|, 1 / |k_t| (raw projections; else ones)
 
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
@@ -486,8 +542,13 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
         float la = 0.f, bt = 0.f;
         if (l < nt) {
             const int64_t row = ((int64_t)b * T + t0 + l) * H + h;
-            la = __logf(p.alpha[row]);
-            bt = p.beta[row];
+            if (p.raw) {
+                la = gdn_log_sigmoid(p.alpha[row]);
+                bt = gdn_sigmoid(p.beta[row]);
+            } else {
+                la = __logf(p.alpha[row]);
+                bt = p.beta[row];
+            }
         }
         const float gv = wave_incl_scan(la, l);
         float gprev = __shfl_up(gv, 1, 64);
@@ -502,17 +563,50 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
         const int e = tid + kThreads * k, t = e / PPR, c8 = e % PPR;
         *reinterpret_cast<u32x4*>(&Ks[t * LDK + c8 * 8]) = t < nt ? kv[k] : u32x4{0, 0, 0, 0};
     }
-    __syncthreads();  // K rows and the gate prefix visible
+    // raw projections: 1 / |k_t| and 1 / |q_t| (each row's pieces sit on PPR
+    // consecutive lanes; padding rows are zero); otherwise ones
+    if (p.raw) {
+        const unsigned short* qin = static_cast<const unsigned short*>(p.q);
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int e = tid + kThreads * k, t = min(e / PPR, nt - 1), c8 = e % PPR;
+            const u32x4 qv = *reinterpret_cast<const u32x4*>(qin + (((int64_t)b * T + t0 + t) * H + h) * D + c8 * 8);
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                const float x = gdn_bf16_to_f32(__builtin_bit_cast(u16x8, kv[k])[e2]);
+                const float y = gdn_bf16_to_f32(__builtin_bit_cast(u16x8, qv)[e2]);
+                sk += x * x;
+                sq += y * y;
+            }
+            sk = row_sum<PPR>(sk);
+            sq = row_sum<PPR>(sq);
+            if (c8 == 0) {
+                const bool real = e / PPR < nt;
+                rksh[e / PPR] = real ? gdn_inv_len(sk) : 0.f;
+                rqsh[e / PPR] = real ? gdn_inv_len(sq) : 0.f;
+            }
+        }
+    } else if (w == 0) {
+        rksh[l] = 1.f;
+        rqsh[l] = 1.f;
+    }
+    __syncthreads();  // K rows, the gate prefix and the row factors visible
     // the gate block for the chunk loop (after the K rows, whose wait on the
     // vector-memory counter would otherwise include these stores)
     if (w == 0) {
         const float gv = gsh[l], gpv = gpsh[l], gC = gsh[C - 1];
+        const float rq = rqsh[l], rk = rksh[l];
         float* gb = gates + ch * kGateFloats;
-        gb[l] = __expf(gv);
-        gb[64 + l] = __expf(gpv);
-        gb[128 + l] = __expf(gC - gv);
+        gb[l] = rq * __expf(gv);
+        gb[64 + l] = rk * __expf(gpv);
+        gb[128 + l] = rk * __expf(gC - gv);
         gb[192 + l] = gv;
         if (l == 0) gb[256] = __expf(gC);
+        if (p.raw) {
+            gb[kGateRq + l] = rq;
+            gb[kGateRk + l] = rk;
+        }
     }
     auto krow = [&](int m, int s) { return *reinterpret_cast<const u16x8*>(&Ks[(16 * m + c16) * LDK + 32 * s + 8 * g4]); };
     // Gram blocks (m, nb), nb <= m, dealt 3, 3, 2, 2 over the waves
@@ -539,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * m + 4 * g4 + r;
-            a[r] = j < t ? bsh[t] * __expf(gpsh[t] - gsh[j]) * acc[q][r] : 0.f;
+            a[r] = j < t ? bsh[t] * rksh[t] * rksh[j] * __expf(gpsh[t] - gsh[j]) * acc[q][r] : 0.f;
         }
         if (nb < m) {
             // A_tj stored at (j, t): upper triangle
@@ -580,6 +674,7 @@ struct RecShared {
     unsigned short V[2][C * 16];
     // gate block, or the C x D log2-prefix table (rows padded to D + 4 floats)
     float G[2][CH ? C * (D + 4) : kGateFloats];
+    float RQK[2][CH ? 2 * C : 1];  // channel gate, raw projections: 1 / |q_t|, 1 / |k_t|
     u16x4 Sf[KS][2][2][64];  // S^T fragments: [k-step][tile half][hi/lo][lane]
     u16x4 Xf[2][2][2][64];
     u16x4 Df[2][2][2][64];
@@ -608,6 +703,8 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
     constexpr int KQP = C * PPR / kThreads;
     constexpr int GP = CH ? C * D / 4 : kGateFloats / 4;  // 16-byte pieces of gate data
     constexpr int GPT = (GP + 255) / 256;                  // pieces per output thread
+    // scalar gate: the pieces actually read (the row factors only for raw projections)
+    const int gp_n = CH ? GP : (p.raw ? kGatePiecesRaw : kGatePieces);
     // (the scalar gate also hands P fragments over through LDS)
     __shared__ __attribute__((aligned(16))) std::conditional_t<CH, RecShared<D, CH>, RecSharedP<D>> sh;
     const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
@@ -673,12 +770,12 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
     const int64_t kq_base = (((int64_t)b * T + trow) * H + h) * D + c8 * 8;
     const int vrow = otid >> 1, vhf = otid & 1;
     const int64_t v_base = (((int64_t)b * T + vrow) * H + h) * D + r0 + 8 * vhf;
-    constexpr int GSTRIDE = CH ? C * D : kGateFloats;  // gate floats per chunk-head
+    constexpr int GSTRIDE = CH ? kChanFloats<D> : kGateFloats;  // gate floats per chunk-head
     constexpr int LDG = D + 4;                           // LDS row stride of the channel table
     static_assert(!CH || (GP % 256 == 0 && 256 % (D / 4) == 0), "channel table staging");
     const float* g_base = gates + bh * p.NC * GSTRIDE;
     uint4 kreg[KQP], qreg[KQP], vreg;
-    u32x4 greg[GPT];
+    u32x4 greg[GPT], rqk;
     auto issue_loads = [&](int i) {
         const int64_t t0 = (int64_t)i * C;
         const int nt = (int)((T - t0) < C ? (T - t0) : C);
@@ -696,7 +793,8 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
         const u32x4* gsrc = reinterpret_cast<const u32x4*>(g_base + (int64_t)i * GSTRIDE) + otid;
 #pragma unroll
         for (int k = 0; k < GPT; ++k)
-            if (GP % 256 == 0 || otid + 256 * k < GP) greg[k] = gsrc[256 * k];
+            if (otid + 256 * k < gp_n) greg[k] = gsrc[256 * k];
+        if (CH && p.raw && otid < 2 * C / 4) rqk = gsrc[C * D / 4];
     };
     auto store_loads = [&](int buf) {
 #pragma unroll
@@ -711,11 +809,12 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 #pragma unroll
             for (int k = 0; k < GPT; ++k)
                 *reinterpret_cast<u32x4*>(gdst + k * (256 / (D / 4)) * LDG) = greg[k];
+            if (p.raw && otid < 2 * C / 4) reinterpret_cast<u32x4*>(sh.RQK[buf])[otid] = rqk;
         } else {
             u32x4* gdst = reinterpret_cast<u32x4*>(sh.G[buf]) + otid;
 #pragma unroll
             for (int k = 0; k < GPT; ++k)
-                if (GP % 256 == 0 || otid + 256 * k < GP) gdst[256 * k] = greg[k];
+                if (otid + 256 * k < gp_n) gdst[256 * k] = greg[k];
         }
     };
     float* corr = reinterpret_cast<float*>(wsb + L.corr);
@@ -756,6 +855,11 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
             for (int r = 0; r < 4; ++r) {
                 const int j = 16 * c + 4 * g4 + r;
                 pt[r] = j <= t ? acc[r] * __expf(gt - gj[r]) : 0.f;
+            }
+            if (p.raw) {
+                const float rq = G[kGateRq + t];
+                const f32x4 rk = *reinterpret_cast<const f32x4*>(&G[kGateRk + 16 * c + 4 * g4]);
+                pt = rq * (pt * rk);
             }
             u16x4 hi, lo;
             split4(pt, hi, lo);
@@ -806,7 +910,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 
     // channel gate: rows of src scaled by 2^{lam[grow]} (grow = -1: by one),
     // split hi/lo, times S^T (hi/lo): 16 x 16 tile of rows 16w.. of the chunk
-    auto gated_rows = [&](const unsigned short* src, const float* G, int grow) {
+    auto gated_rows = [&](const unsigned short* src, const float* G, int grow, float rowf) {
         f32x4 A1 = zero4(), A2 = zero4(), A3 = zero4();
         const int t = 16 * w + c16;
 #pragma unroll
@@ -823,8 +927,8 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
             uint32_t ah[4], al[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float x0 = gdn_bf16_to_f32(raw[e]) * __builtin_amdgcn_exp2f(e < 4 ? g0[e] : g1[e - 4]);
-                const float x1 = gdn_bf16_to_f32(raw[e + 1]) * __builtin_amdgcn_exp2f(e < 4 ? g0[e + 1] : g1[e - 3]);
+                const float x0 = rowf * gdn_bf16_to_f32(raw[e]) * __builtin_amdgcn_exp2f(e < 4 ? g0[e] : g1[e - 4]);
+                const float x1 = rowf * gdn_bf16_to_f32(raw[e + 1]) * __builtin_amdgcn_exp2f(e < 4 ? g0[e + 1] : g1[e - 3]);
                 split2(x0, x1, ah[e >> 1], al[e >> 1]);
             }
             const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
@@ -894,7 +998,8 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                 }
                 Xc = A1 + A2;
             } else {
-                Xc = gated_rows(sh.K[cur], G, ptd ? 16 * w + c16 - 1 : 16 * w + c16);
+                Xc = gated_rows(sh.K[cur], G, ptd ? 16 * w + c16 - 1 : 16 * w + c16,
+                                p.raw ? sh.RQK[cur][C + 16 * w + c16] : 1.f);
             }
             {
                 f32x4 gamp = f32x4{1.f, 1.f, 1.f, 1.f};
@@ -956,8 +1061,10 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 #pragma unroll
                         for (int e = 0; e < 8; e += 2) {
                             const int j0 = 32 * s + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-                            const float x0 = gdn_bf16_to_f32(sh.K[cur][j0 * LDK + a]) * __builtin_amdgcn_exp2f(gC - G[j0 * LDG + a]);
-                            const float x1 = gdn_bf16_to_f32(sh.K[cur][(j0 + 1) * LDK + a]) *
+                            const float f0 = p.raw ? sh.RQK[cur][C + j0] : 1.f;
+                            const float f1 = p.raw ? sh.RQK[cur][C + j0 + 1] : 1.f;
+                            const float x0 = f0 * gdn_bf16_to_f32(sh.K[cur][j0 * LDK + a]) * __builtin_amdgcn_exp2f(gC - G[j0 * LDG + a]);
+                            const float x1 = f1 * gdn_bf16_to_f32(sh.K[cur][(j0 + 1) * LDK + a]) *
                                              __builtin_amdgcn_exp2f(gC - G[(j0 + 1) * LDG + a]);
                             split2(x0, x1, kh[e >> 1], kl[e >> 1]);
                         }
@@ -1043,7 +1150,7 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
                 }
                 Zc = A1 + A2;
             } else {
-                Zc = gated_rows(sh.Q[cur], G, 16 * w + c16);
+                Zc = gated_rows(sh.Q[cur], G, 16 * w + c16, p.raw ? sh.RQK[cur][16 * w + c16] : 1.f);
             }
             if constexpr (CH) load_pfrag(i);
             __syncthreads();  // B2
@@ -1130,6 +1237,8 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
     constexpr int TFP = (kTfragPerChunk + NT - 1) / NT;
     constexpr int GP = kGateFloats / 4;
     static_assert(C * PPR % NT == 0 && GP <= NT, "staging split");
+    // the gate pieces read: the row factors only for raw projections
+    const int gp_n = p.raw ? kGatePiecesRaw : kGatePieces;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1208,7 +1317,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             const u32x4* tp = reinterpret_cast<const u32x4*>(tfrag + (bh * p.NC + i) * kTfragPerChunk);
 #pragma unroll
             for (int k = 0; k < TFP; ++k) tr[k] = tp[min(tid + NT * k, kTfragPerChunk - 1)];
-            gr = reinterpret_cast<const u32x4*>(gates + (bh * p.NC + i) * kGateFloats)[min(tid, GP - 1)];
+            gr = reinterpret_cast<const u32x4*>(gates + (bh * p.NC + i) * kGateFloats)[min(tid, gp_n - 1)];
         }
     };
     auto store = [&](int i) {
@@ -1236,7 +1345,7 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         for (int k = 0; k < TFP; ++k)
             if (kTfragPerChunk % NT == 0 || tid + NT * k < kTfragPerChunk)
                 reinterpret_cast<u32x4*>(sh.Tf)[tid + NT * k] = tr[k];
-        if (tid < GP) reinterpret_cast<u32x4*>(sh.G)[tid] = gr;
+        if (tid < gp_n) reinterpret_cast<u32x4*>(sh.G)[tid] = gr;
     };
 
     // ---- P blocks (m, c), c <= m, dealt over the waves: rows j of tile c,
@@ -1261,6 +1370,11 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
             for (int r = 0; r < 4; ++r) {
                 const int j = 16 * c + 4 * g4 + r;
                 pt[r] = j <= t ? acc[r] * __expf(gt - gj[r]) : 0.f;
+            }
+            if (p.raw) {
+                const float rq = sh.G[kGateRq + t];
+                const f32x4 rk = *reinterpret_cast<const f32x4*>(&sh.G[kGateRk + 16 * c + 4 * g4]);
+                pt = rq * (pt * rk);
             }
             u16x4 hi, lo;
             split4(pt, hi, lo);
@@ -2102,7 +2216,7 @@ WsLayout mfma_layout(const Problem& p, const Split& sp) {
     WsLayout L;
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
     L.prep = 0;
-    const size_t gate_floats = p.gate == GDN_GATE_CHANNEL ? (size_t)C * p.dk : kGateFloats;
+    const size_t gate_floats = p.gate == GDN_GATE_CHANNEL ? (size_t)C * p.dk + 2 * C : kGateFloats;
     L.prep_bytes = (p.gate == GDN_GATE_CHANNEL ? 2 : 1) * align256((size_t)nch * kTfragPerChunk * sizeof(u16x8)) +
                    align256((size_t)nch * gate_floats * sizeof(float));
     size_t off = L.prep_bytes;

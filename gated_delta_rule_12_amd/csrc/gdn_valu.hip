@@ -25,6 +25,8 @@
 // DeltaNet illustrated notes (stay-hungry-time.github.io/deltanet).  Every
 // gate ratio is evaluated as exp(g_t - g_j) with g the chunk-local log
 // prefix and t >= j, so no factor exceeds one.
+#include <algorithm>
+
 #include "gdn_internal.h"
 #include "../../include/gdn.h"
 
@@ -533,6 +535,80 @@ hipError_t seqpar_finish(const Problem& p, const Split& sp, char* ws, const WsLa
         prof_end(p.timer, st);
         return hipGetLastError();
     }
+}
+
+// The block's prologue for raw projections on the vector-ALU family: q and k
+// L2-normalised per (batch, token, head) along their features (a zero vector
+// stays zero), v converted to fp32, alpha = sigmoid(alpha_logit) (per head or
+// per key channel), beta = sigmoid(beta_logit), written as fp32 [B, T, H, .]
+// for the forward kernels (DeltaNet illustrated notes, block description).
+// One wave per (batch, token, head) row, lanes over the features.
+template <int DT>
+__global__ __launch_bounds__(256) void k_raw_prologue(Problem p, RawInputs r) {
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = p.B * p.T * p.H;
+    const int dk = (int)p.dk, dv = (int)p.dv;
+    const bool chan = p.gate == GDN_GATE_CHANNEL;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4) {
+        float sq = 0.f, sk = 0.f;
+        for (int a = lane; a < dk; a += 64) {
+            const float x = gdn_ld<DT>(p.q, row * dk + a), y = gdn_ld<DT>(p.k, row * dk + a);
+            sq += x * x;
+            sk += y * y;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            sq += __shfl_xor(sq, o, 64);
+            sk += __shfl_xor(sk, o, 64);
+        }
+        const float rq = gdn_inv_len(sq), rk = gdn_inv_len(sk);
+        for (int a = lane; a < dk; a += 64) {
+            r.q[row * dk + a] = rq * gdn_ld<DT>(p.q, row * dk + a);
+            r.k[row * dk + a] = rk * gdn_ld<DT>(p.k, row * dk + a);
+            if (chan) r.alpha[row * dk + a] = gdn_sigmoid(p.alpha[row * dk + a]);
+        }
+        for (int a = lane; a < dv; a += 64) r.v[row * dv + a] = gdn_ld<DT>(p.v, row * dv + a);
+        if (lane == 0) {
+            if (!chan) r.alpha[row] = gdn_sigmoid(p.alpha[row]);
+            r.beta[row] = gdn_sigmoid(p.beta[row]);
+        }
+    }
+}
+
+size_t raw_inputs_bytes(const Problem& p) {
+    const int64_t rows = p.B * p.T * p.H;
+    return align256(sizeof(float) * rows * p.dk) * 2 + align256(sizeof(float) * rows * p.dv) +
+           align256(sizeof(float) * rows * (p.gate == GDN_GATE_CHANNEL ? p.dk : 1)) +
+           align256(sizeof(float) * rows);
+}
+
+RawInputs raw_inputs_at(const Problem& p, char* base) {
+    const int64_t rows = p.B * p.T * p.H;
+    RawInputs r;
+    size_t off = 0;
+    r.q = reinterpret_cast<float*>(base + off);
+    off += align256(sizeof(float) * rows * p.dk);
+    r.k = reinterpret_cast<float*>(base + off);
+    off += align256(sizeof(float) * rows * p.dk);
+    r.v = reinterpret_cast<float*>(base + off);
+    off += align256(sizeof(float) * rows * p.dv);
+    r.alpha = reinterpret_cast<float*>(base + off);
+    off += align256(sizeof(float) * rows * (p.gate == GDN_GATE_CHANNEL ? p.dk : 1));
+    r.beta = reinterpret_cast<float*>(base + off);
+    return r;
+}
+
+hipError_t raw_prologue(const Problem& p, const RawInputs& r, hipStream_t st) {
+    const int64_t rows = p.B * p.T * p.H;
+    if (rows == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 8192);
+    prof_begin(p.timer, "k_raw_prologue", st);
+    if (p.dtype == GDN_BF16)
+        hipLaunchKernelGGL(k_raw_prologue<1>, dim3((unsigned)blocks), dim3(256), 0, st, p, r);
+    else
+        hipLaunchKernelGGL(k_raw_prologue<0>, dim3((unsigned)blocks), dim3(256), 0, st, p, r);
+    prof_end(p.timer, st);
+    return hipGetLastError();
 }
 
 hipError_t copy_state(const Problem& p, hipStream_t st) {

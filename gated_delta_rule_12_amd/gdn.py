@@ -32,7 +32,7 @@ EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_s
            "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_status_str", "gdn_abi_version",
            "gdn_timer_create", "gdn_timer_destroy", "gdn_timer_read", "gdn_chunk_fwd_timed",
            "gdn_seqpar_fwd_timed", "gdn_decode_step_timed", "gdn_backward_timed",
-           "gdn_chunk_fwd_noalloc")
+           "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_raw", "gdn_raw_workspace_bytes")
 
 _lib = None
 
@@ -58,6 +58,10 @@ def lib():
     tens = [vp] * 8
     L.gdn_chunk_fwd.argtypes = shape + [i32, i32, i32, i32, f32] + tens + [vp, sz, vp]
     L.gdn_chunk_fwd.restype = ctypes.c_int
+    L.gdn_chunk_fwd_raw.argtypes = shape + [i32, i32, i32, i32, f32] + tens + [vp, sz, vp]
+    L.gdn_chunk_fwd_raw.restype = ctypes.c_int
+    L.gdn_raw_workspace_bytes.argtypes = shape + [i32, i32, i32]
+    L.gdn_raw_workspace_bytes.restype = sz
     L.gdn_chunk_fwd_noalloc.argtypes = shape + [i32, i32, i32, i32, f32] + tens + [vp]
     L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     L.gdn_seqpar_fwd.argtypes = shape + [i32, i32, i32, i32, f32, i32] + tens + [vp, sz, vp]
@@ -289,6 +293,30 @@ def chunk_fwd(q, k, v, alpha, beta, state0=None, *, chunk=64,
         rc = _call(where, [*args, n_segments, *tens, *tail], timer)
     if rc != GDN_OK:
         raise GdnError(rc, where)
+    return out, state_out
+
+
+def chunk_fwd_raw(q, k, v, alpha_logit, beta_logit, state0=None, *, chunk=64,
+                  order=GDN_PREDICT_THEN_DECAY, scale=1.0, out=None, state_out=None,
+                  workspace=None):
+    """gdn_chunk_fwd_raw: the forward on raw projections q, k (L2-normalised
+    in the kernels) and gate / beta logits (through a sigmoid in the
+    kernels).  Returns (out [B,T,H,dv] fp32, final state [B,H,dv,dk])."""
+    import torch
+    B, T, H, dk, dv, gate = _check(q, k, v, alpha_logit, beta_logit, state0)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    if state_out is None:
+        state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = int(lib().gdn_raw_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q), gate))
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    rc = lib().gdn_chunk_fwd_raw(B, T, H, dk, dv, chunk, _dtype_code(q), gate, order, scale,
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(alpha_logit), _ptr(beta_logit),
+                                 _ptr(state0), _ptr(out), _ptr(state_out), _ptr(workspace),
+                                 workspace.numel(), _stream())
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd_raw")
     return out, state_out
 
 

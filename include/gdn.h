@@ -104,6 +104,36 @@ int gdn_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_chunk_fwd_raw — gdn_chunk_fwd on the model's raw projections, with the
+ * step before the delta-rule core fused in (DeltaNet illustrated notes, block
+ * description; the Gated DeltaNet GPU-parallelisation blog's projection
+ * stage): q and k L2-normalised per (batch, token, head) along their
+ * features (a zero vector stays zero), beta = sigmoid(beta_logit) and the
+ * gate alpha = sigmoid(alpha_logit) (per head, or per key channel for
+ * GDN_GATE_CHANNEL), then the forward.  The MFMA kernels keep the raw bf16 q
+ * and k as exact matrix operands and apply 1/|q_t| and 1/|k_t| as fp32 row
+ * factors beside the gate factors, and form log alpha = -softplus(-logit)
+ * in stage 1 (no normalised copy is written); the vector-ALU family writes
+ * the normalised fp32 inputs into the workspace first.  Same tensors, layouts,
+ * alignment and statuses as gdn_chunk_fwd, with alpha_logit and beta_logit in
+ * the places of alpha and beta; the workspace must hold
+ * gdn_raw_workspace_bytes(...) bytes.  Raw q and k rows
+ * must have L2 lengths between 2^-60 and 2^60 (or be zero).
+ */
+int gdn_chunk_fwd_raw(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                      int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
+                      float scale,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha_logit, const float* beta_logit, const float* state0,
+                      float* out, float* state_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes gdn_chunk_fwd_raw needs for these arguments (0 when they do
+ * not validate).  Host only. */
+size_t gdn_raw_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                               int32_t chunk, int32_t dtype, int32_t gate);
+
+/*
  * gdn_chunk_fwd_noalloc — gdn_chunk_fwd for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same call without a workspace argument, running
