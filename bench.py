@@ -71,22 +71,6 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload_name, kernel):
-    """HBM bytes (read + write) of one launch of `kernel` from
-    profiles/traffic_<workload>.json (FETCH_SIZE and WRITE_SIZE per dispatch,
-    scaled by the plain-copy calibration), or None when absent, taken on
-    other kernel sources, or not recorded for that kernel."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    k = rec.get("per_kernel", {}).get(kernel)
-    return None if k is None else round(k["read_bytes"] + k["write_bytes"])
-
-
 def settle(step, settle_ms: float):
     """Untimed steps until settle_ms of wall time have passed (at least one
     step); returns (milliseconds, steps)."""
@@ -184,6 +168,24 @@ def host_cores() -> int:
 def host_info() -> dict:
     return {"nproc": len(os.sched_getaffinity(0)), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "cpu_model": cpu_model()}
+
+
+def stored_step_traffic(tag, kernels=None):
+    """HBM bytes per step of the listed kernels (None: every kernel the
+    record holds) from profiles/traffic_<tag>.json, or None when absent,
+    taken on other kernel sources, or missing one of them."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    per = rec.get("per_kernel", {})
+    names = list(per) if kernels is None else list(kernels)
+    if not names or any(k not in per for k in names):
+        return None
+    return round(sum(per[k]["read_bytes"] + per[k]["write_bytes"] for k in names))
 
 
 def copy_calibration(mbytes: int, reps: int = 5):
@@ -336,13 +338,16 @@ def bench_decode(args, w):
            "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv,
                       "gate": w.gate, "input_dtype": w.dtype, "entry": "gdn_decode_step",
                       "state": "in place", "global_batch": w.B, "parallelism": "single-gpu"},
-           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": stored_traffic(w.name, "k_decode"), "kernel": "k_decode",
-                        "kernel_timing": "HIP events around each launch, in a second run of the same steps after the timed region",
-                        "kernel_avg_launch_us": round(k_us, 2), "algorithmic_bytes": abytes,
-                        "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
-                        "step_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "roofline": {"bound": "hbm", "achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": stored_step_traffic(w.name, ["k_decode"]),
+                        "kernel": "whole step: k_decode", "algorithmic_bytes": abytes,
+                        "kernel_timing": "HIP events around each launch (caller-owned timer), in a second run of the same steps after the timed region",
+                        "dominant_kernel": {"kernel": "k_decode", "launches_per_step": 1,
+                                            "avg_launch_us": round(k_us, 2), "achieved": round(achieved, 1),
+                                            "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                            "traffic": stored_step_traffic(w.name, ["k_decode"])}},
            "cpu_baseline": cpu, "raw_prologue_ms_per_step": round(raw_ms, 5)}
     print(json.dumps(res), flush=True)
 
@@ -438,16 +443,19 @@ def bench_backward(args, w):
            "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                       "gate": w.gate, "input_dtype": w.dtype, "entry": "gdn_backward",
                       "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"},
-           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": stored_traffic(w.name + "-backward", "k_backward"),
-                        "kernel": "k_backward",
-                        "kernel_timing": "HIP events around each launch, in a second run of the same steps after the timed region",
-                        "kernel_avg_launch_us": round(k_us, 2), "algorithmic_bytes": abytes,
+           "roofline": {"bound": "hbm", "achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": stored_step_traffic(w.name + "-backward", list(kern)),
+                        "kernel": "whole step: " + " + ".join(kern), "algorithmic_bytes": abytes,
+                        "kernel_timing": "HIP events around each launch (caller-owned timer), in a second run of the same steps after the timed region",
                         "kernel_us_per_step": {n: round(1e3 * v[0] / args.steps, 2)
                                                for n, v in kern.items()},
-                        "step_achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
-                        "step_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                        "dominant_kernel": {"kernel": "k_backward",
+                                            "launches_per_step": kern["k_backward"][1] / args.steps,
+                                            "avg_launch_us": round(k_us, 2), "achieved": round(achieved, 1),
+                                            "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                            "traffic": stored_step_traffic(w.name + "-backward", ["k_backward"])}},
            "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
@@ -463,7 +471,12 @@ def main():
     ap.add_argument("--workload", default="main-bf16")
     ap.add_argument("--segments", type=int, default=None,
                     help="sequence-parallel segments (default: the workload's)")
+    ap.add_argument("--library-schedule", action="store_true",
+                    help="gdn_chunk_fwd with the library's own schedule even where the workload "
+                         "names a segment count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak probes (profiler runs)")
     ap.add_argument("--raw", action="store_true",
                     help="time gdn_chunk_fwd_raw (raw q, k and gate / beta logits, the block's "
                          "prologue fused in) on the workload's shapes")
@@ -497,6 +510,8 @@ def main():
         return
     # None: gdn_chunk_fwd with the library's schedule; a count: gdn_seqpar_fwd
     G = args.segments if args.segments is not None else (w.n_segments if w.n_segments > 1 else None)
+    if args.library_schedule:
+        G = None
     log(f"workload {w}, segments {G if G is not None else 'library schedule'}")
     t = time.time()
     if args.raw:
@@ -568,16 +583,19 @@ def main():
     value = tokens / (ms * 1e-3)
     abytes = algorithmic_bytes(w)
     aflops = algorithmic_flops(w)
-    peaks = measure_peaks()
-    log(f"achievable peaks: {peaks}")
+    peaks = None if args.no_peaks else measure_peaks()
+    if peaks:
+        log(f"achievable peaks: {peaks}")
     # the roofline is the whole step's: its algorithmic bytes over its time
     step_achieved = abytes / (ms * 1e-3) / 1e9
     # counted HBM traffic of the step: every kernel's stored counters (only
     # while they were taken on the current kernel sources)
+    # (the counters were taken on the default command of each record: the
+    # workload's own segments, the library schedule, or the raw entry point)
+    rec_tag = w.name + ("-raw" if args.raw else "-library" if args.library_schedule else "")
     traffic = None
-    if args.segments is None and per_kernel_us:
-        parts = [stored_traffic(w.name, k) for k in per_kernel_us]
-        traffic = None if any(t_ is None for t_ in parts) else int(sum(parts))
+    if args.segments is None:
+        traffic = stored_step_traffic(rec_tag, list(per_kernel_us) or None)
     # the dominant kernel (longest per step): each launch covers every
     # head-token, so the step's algorithmic bytes over its average launch
     dom = None
@@ -587,15 +605,15 @@ def main():
         dom = {"kernel": dominant, "launches_per_step": launches[dominant],
                "avg_launch_us": round(dom_us / launches[dominant], 2),
                "achieved": round(dom_achieved, 1), "frac": round(dom_achieved / HBM_PEAK_GBS, 4),
-               "traffic": stored_traffic(w.name, dominant) if args.segments is None else None}
+               "traffic": stored_step_traffic(rec_tag, [dominant]) if args.segments is None else None}
     roof = {"bound": "hbm", "achieved": round(step_achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(step_achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": "whole step: " + (" + ".join(per_kernel_us) if per_kernel_us else "gdn_chunk_fwd_raw"),
             "algorithmic_bytes": abytes,
-            "frac_of_achievable_copy": round(step_achieved / peaks["hbm_copy_GBs"], 4),
+            "frac_of_achievable_copy": round(step_achieved / peaks["hbm_copy_GBs"], 4) if peaks else None,
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "mfma_frac_of_achievable": round(aflops / (ms * 1e-3) / 1e12 / peaks["mfma_bf16_TFs"], 4),
+            "mfma_frac_of_achievable": round(aflops / (ms * 1e-3) / 1e12 / peaks["mfma_bf16_TFs"], 4) if peaks else None,
             "kernel_us_per_step": {k: round(v, 2) for k, v in per_kernel_us.items()},
             "kernel_timing": "HIP events around each launch (caller-owned timer), in a second run of the same steps after the timed region",
             "dominant_kernel": dom,

@@ -224,7 +224,7 @@ __device__ __forceinline__ void ut_inverse_store(float* AT, float* Pw, const flo
 // anchor token, per 16-token row block (the secondary chunking of the GLA
 // gating section).
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_prep_channel(Problem p, u16x8* tfrag, u16x8* pfrag,
+__global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* tfrag, u16x8* pfrag,
                                                            float* gates) {
     constexpr int LDA = C + 4;
     constexpr int LDK = D + 8;
