@@ -1477,20 +1477,17 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         // rows 16m.. of src times S^T for every value block of the wave: lane
         // (column v, rows t = 16m + 4 g4 + r); each A fragment read once
         auto times_state = [&](const unsigned short* src, int m, f32x4 (&res)[NV]) {
-            f32x4 x1[NV], x2[NV];
 #pragma unroll
-            for (int n = 0; n < NV; ++n) x1[n] = x2[n] = zero4();
+            for (int n = 0; n < NV; ++n) res[n] = zero4();
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const u16x8 ra = *reinterpret_cast<const u16x8*>(&src[(16 * m + c16) * LDK + 32 * s + 8 * g4]);
 #pragma unroll
                 for (int n = 0; n < NV; ++n) {
-                    x1[n] = mfma(ra, sbh[n][s], x1[n]);
-                    x2[n] = mfma(ra, sbl[n][s], x2[n]);
+                    res[n] = mfma(ra, sbh[n][s], res[n]);
+                    res[n] = mfma(ra, sbl[n][s], res[n]);
                 }
             }
-#pragma unroll
-            for (int n = 0; n < NV; ++n) res[n] = x1[n] + x2[n];
         };
         // X = K S^T
         f32x4 X[4][NV];
@@ -1559,9 +1556,9 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         u16x4 dh[NV][4], dl[NV][4], dbh[NV][4], dbl[NV][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            f32x4 d1[NV], d2[NV], d3[NV];
+            f32x4 d1[NV];
 #pragma unroll
-            for (int n = 0; n < NV; ++n) d1[n] = d2[n] = d3[n] = zero4();
+            for (int n = 0; n < NV; ++n) d1[n] = zero4();
 #pragma unroll
             for (int s = 0; s <= (m >> 1); ++s) {
                 const u16x8 th = sh.Tf[(tslot(m, s) * 2 + 0) * 64 + l];
@@ -1570,21 +1567,15 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
                 for (int n = 0; n < NV; ++n) {
                     const u16x8 xh = cat(uh[n][2 * s], uh[n][2 * s + 1]);
                     const u16x8 xl = cat(ul[n][2 * s], ul[n][2 * s + 1]);
-                    if constexpr (OUT) {
-                        d1[n] = mfma(th, xh, d1[n]);
-                        d2[n] = mfma(th, xl, d2[n]);
-                        d3[n] = mfma(tl, xh, d3[n]);
-                    } else {
-                        d1[n] = mfma(th, xh, d1[n]);
-                        d1[n] = mfma(th, xl, d1[n]);
-                        d1[n] = mfma(tl, xh, d1[n]);
-                    }
+                    d1[n] = mfma(th, xh, d1[n]);
+                    d1[n] = mfma(th, xl, d1[n]);
+                    d1[n] = mfma(tl, xh, d1[n]);
                 }
             }
             const f32x4 rat = *reinterpret_cast<const f32x4*>(&sh.G[128 + 16 * m + 4 * g4]);
 #pragma unroll
             for (int n = 0; n < NV; ++n) {
-                const f32x4 dd = OUT ? d1[n] + d2[n] + d3[n] : d1[n];
+                const f32x4 dd = d1[n];
                 if constexpr (OUT) split4(dd, dh[n][m], dl[n][m]);
                 split4(rat * dd, dbh[n][m], dbl[n][m]);
             }
@@ -1596,24 +1587,20 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         const float gC = sh.G[256];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
-            f32x4 acc[NV], acc2[NV];
+            f32x4 acc[NV];
 #pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                acc[n] = gC * Sacc[n][u];
-                acc2[n] = zero4();
-            }
+            for (int n = 0; n < NV; ++n) acc[n] = gC * Sacc[n][u];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const u16x8 ka = sh.KtF[u][s][l];
 #pragma unroll
                 for (int n = 0; n < NV; ++n) {
                     acc[n] = mfma(ka, cat(dbh[n][2 * s], dbh[n][2 * s + 1]), acc[n]);
-                    if constexpr (OUT) acc2[n] = mfma(ka, cat(dbl[n][2 * s], dbl[n][2 * s + 1]), acc2[n]);
-                    else acc[n] = mfma(ka, cat(dbl[n][2 * s], dbl[n][2 * s + 1]), acc[n]);
+                    acc[n] = mfma(ka, cat(dbl[n][2 * s], dbl[n][2 * s + 1]), acc[n]);
                 }
             }
 #pragma unroll
-            for (int n = 0; n < NV; ++n) Sacc[n][u] = OUT ? acc[n] + acc2[n] : acc[n];
+            for (int n = 0; n < NV; ++n) Sacc[n][u] = acc[n];
         }
 
         // O = scale (diag(gamma) Z + P Delta) into the LDS output tile; it goes
@@ -1622,9 +1609,9 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
         if constexpr (OUT) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                f32x4 o1[NV], o2[NV], o3[NV];
+                f32x4 o1[NV];
 #pragma unroll
-                for (int n = 0; n < NV; ++n) o1[n] = o2[n] = o3[n] = zero4();
+                for (int n = 0; n < NV; ++n) o1[n] = zero4();
 #pragma unroll
                 for (int s = 0; s <= (m >> 1); ++s) {
                     const u16x8 ph = sh.Pf[m][s][0][l];
@@ -1634,14 +1621,14 @@ __device__ __forceinline__ void seg_body(const Problem& p, const Split& sp, cons
                         const u16x8 xh = cat(dh[n][2 * s], dh[n][2 * s + 1]);
                         const u16x8 xl = cat(dl[n][2 * s], dl[n][2 * s + 1]);
                         o1[n] = mfma(ph, xh, o1[n]);
-                        o2[n] = mfma(ph, xl, o2[n]);
-                        o3[n] = mfma(pl, xh, o3[n]);
+                        o1[n] = mfma(ph, xl, o1[n]);
+                        o1[n] = mfma(pl, xh, o1[n]);
                     }
                 }
                 const f32x4 gam = *reinterpret_cast<const f32x4*>(&sh.G[16 * m + 4 * g4]);
 #pragma unroll
                 for (int n = 0; n < NV; ++n) {
-                    const f32x4 o = p.scale * (gam * Z[m][n] + o1[n] + o2[n] + o3[n]);
+                    const f32x4 o = p.scale * (gam * Z[m][n] + o1[n]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sh.O[(16 * m + 4 * g4 + r) * LDO + v[n]] = o[r];
                 }
