@@ -16,7 +16,8 @@ device copy and an MFMA loop) are measured in the same run.
 
 Default workload: main-bf16 (B=2, H=16, T=8192, dk=dv=128, chunk 64, scalar
 gate, start state N(0, 0.02^2)).  The long workload runs the sequence-parallel
-entry point (8 segments) and also reports the single-stream time beside it.
+entry point (8 segments, which the library cuts finer to fill the device:
+see gdn_seqpar_segments) and also reports the single-stream time beside it.
 --workload decode-bf16 times gdn_decode_step instead: one token for each of
 256 x 16 persistent states, updated in place.  --backward times gdn_backward
 (gradients through the recurrence) on the workload.
@@ -512,7 +513,9 @@ def main():
     G = args.segments if args.segments is not None else (w.n_segments if w.n_segments > 1 else None)
     if args.library_schedule:
         G = None
-    log(f"workload {w}, segments {G if G is not None else 'library schedule'}")
+    log(f"workload {w}, segments {G if G is not None else 'library schedule'}"
+        + (f" (run as {gdn.gdn_seqpar_segments(w.B, w.T, w.H, w.dk, w.dv, w.chunk, 1 if w.dtype == 'bf16' else 0, 0 if w.gate == 'scalar' else 1, G)})"
+           if G is not None else ""))
     t = time.time()
     if args.raw:
         from gated_delta_rule_12_amd.workloads import make_raw_inputs
@@ -650,6 +653,10 @@ def main():
                       "entry": "gdn_chunk_fwd_raw" if args.raw else (
                           "gdn_seqpar_fwd" if G is not None else "gdn_chunk_fwd"),
                       "segments": G if G is not None else gdn.gdn_chunk_segments(
+                          w.B, w.T, w.H, w.dk, w.dv, w.chunk, dt_code, gate_code),
+                      "segments_run": gdn.gdn_seqpar_segments(
+                          w.B, w.T, w.H, w.dk, w.dv, w.chunk, dt_code, gate_code, G)
+                      if G is not None else gdn.gdn_chunk_segments(
                           w.B, w.T, w.H, w.dk, w.dv, w.chunk, dt_code, gate_code),
                       "global_batch": w.B, "seq_len": w.T,
                       "parallelism": "single-gpu",

@@ -91,6 +91,11 @@ int auto_segments(const Problem& p) {
     return mfma_supported(p.dk, p.dv, p.C, p.dtype, p.gate) ? mfma_auto_segments(p) : 1;
 }
 
+// the segments an explicit request of n runs in (n, or a multiple of it)
+int run_segments(const Problem& p, int n) {
+    return mfma_supported(p.dk, p.dv, p.C, p.dtype, p.gate) ? mfma_refine_segments(p, n) : n;
+}
+
 int finish(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 // The kernels move q, k, v, a per-channel gate, the states and the output in
@@ -114,7 +119,7 @@ int run_chunked(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t
     if (s != GDN_OK) return s;
     Problem p = make_problem(B, T, H, dk, dv, chunk, dtype, gate, order, scale);
     if (B * H == 0) return GDN_OK;
-    if (n_segments == 0) n_segments = auto_segments(p);
+    n_segments = n_segments == 0 ? auto_segments(p) : run_segments(p, n_segments);
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_E_ARG;
     if (!forward_aligned(q, k, v, alpha, gate, beta, state0, out, state_out)) return GDN_E_ARG;
     p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
@@ -282,12 +287,21 @@ int gdn_chunk_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, 
     return make_split(p.NC, auto_segments(p)).G;
 }
 
+int gdn_seqpar_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                        int32_t dtype, int32_t gate, int32_t n_segments) {
+    int s = validate(B, T, H, dk, dv, chunk, dtype, gate, 0, n_segments);
+    if (s != GDN_OK) return s;
+    Problem p = make_problem(B, T, H, dk, dv, chunk, dtype, gate, 0, 1.f);
+    if (p.NC == 0 || B * H == 0) return 1;
+    return make_split(p.NC, run_segments(p, n_segments)).G;
+}
+
 size_t gdn_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                            int32_t chunk, int32_t dtype, int32_t gate, int32_t n_segments) {
     if (validate(B, T, H, dk, dv, chunk, dtype, gate, 0, n_segments) != GDN_OK) return 0;
     Problem p = make_problem(B, T, H, dk, dv, chunk, dtype, gate, 0, 1.f);
     if (p.NC == 0 || B * H == 0) return 0;
-    size_t bytes = layout_for(p, make_split(p.NC, n_segments)).total;
+    size_t bytes = layout_for(p, make_split(p.NC, run_segments(p, n_segments))).total;
     if (n_segments == 1) {
         // also covers gdn_chunk_fwd, whose schedule may cut sequences into segments
         const size_t a = layout_for(p, make_split(p.NC, auto_segments(p))).total;

@@ -70,6 +70,9 @@ hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
 // workgroups to occupy the device, at least kMinSegChunks chunks each; 1 for
 // paths without the whole-head chunk loop.
 int mfma_auto_segments(const Problem& p);
+// Segments the MFMA family runs an explicit request of G in: G, or a multiple
+// of it when only a finer cut fills the device with the whole-head loop.
+int mfma_refine_segments(const Problem& p, int G);
 
 hipError_t recurrent_forward(const Problem& p, hipStream_t st);
 // One-token step on a persistent state (q, k, v, gates of one token; T = 1);

@@ -2257,6 +2257,27 @@ hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
     return ch ? launch<64, 1>(p, sp, ws, L, st) : launch<64, 0>(p, sp, ws, L, st);
 }
 
+// Segments for an explicit request of G: when (batch, head, segment) groups
+// are too few for the whole-head loop, each segment is cut into k equal runs
+// (k G segments in all, about kTargetGroups groups, at least kMinSegChunks
+// chunks each), so that the whole-head loop, whose correction is fused with
+// the outputs, takes it; a request that cannot reach kWholeHeadMinGroups so
+// stays as it is (the sliced loop).
+int mfma_refine_segments(const Problem& p, int G) {
+    constexpr int64_t kTargetGroups = 256;
+    constexpr int kMinSegChunks = 4;
+    if (G <= 1 || !mfma_supported(p.dk, p.dv, p.C, p.dtype, p.gate) || p.gate != GDN_GATE_SCALAR) return G;
+    const Split sp = make_split(p.NC, G);
+    const int64_t heads = p.B * p.H;
+    if (heads <= 0 || whole_head(p, sp)) return G;
+    int64_t k = (kTargetGroups + heads * sp.G - 1) / (heads * sp.G);
+    const int64_t kmax = p.NC / ((int64_t)kMinSegChunks * sp.G);
+    if (k > kmax) k = kmax;
+    if (k < 2) return G;
+    const Split fine = make_split(p.NC, (int)(k * sp.G));
+    return whole_head(p, fine) ? fine.G : G;
+}
+
 int mfma_auto_segments(const Problem& p) {
     constexpr int kTargetGroups = 256;  // compute units of a gfx950 device
     constexpr int kMinSegChunks = 4;

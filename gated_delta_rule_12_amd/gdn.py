@@ -29,7 +29,8 @@ GDN_PATH_VALU, GDN_PATH_MFMA = 0, 1
 EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_step",
            "gdn_decode_step_raw", "gdn_backward", "gdn_backward_workspace_bytes",
            "gdn_workspace_bytes",
-           "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_status_str", "gdn_abi_version",
+           "gdn_validate", "gdn_chunk_path", "gdn_chunk_segments", "gdn_seqpar_segments",
+           "gdn_status_str", "gdn_abi_version",
            "gdn_timer_create", "gdn_timer_destroy", "gdn_timer_read", "gdn_chunk_fwd_timed",
            "gdn_seqpar_fwd_timed", "gdn_decode_step_timed", "gdn_backward_timed",
            "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_raw", "gdn_raw_workspace_bytes")
@@ -84,6 +85,8 @@ def lib():
     L.gdn_chunk_path.restype = ctypes.c_int
     L.gdn_chunk_segments.argtypes = shape + [i32, i32, i32]
     L.gdn_chunk_segments.restype = ctypes.c_int
+    L.gdn_seqpar_segments.argtypes = shape + [i32, i32, i32, i32]
+    L.gdn_seqpar_segments.restype = ctypes.c_int
     L.gdn_status_str.argtypes = [ctypes.c_int]
     L.gdn_status_str.restype = ctypes.c_char_p
     L.gdn_abi_version.argtypes = []
@@ -148,6 +151,10 @@ def gdn_chunk_path(dk, dv, chunk, dtype, gate) -> int:
 
 def gdn_chunk_segments(B, T, H, dk, dv, chunk, dtype, gate) -> int:
     return int(lib().gdn_chunk_segments(B, T, H, dk, dv, chunk, dtype, gate))
+
+
+def gdn_seqpar_segments(B, T, H, dk, dv, chunk, dtype, gate, n_segments) -> int:
+    return int(lib().gdn_seqpar_segments(B, T, H, dk, dv, chunk, dtype, gate, n_segments))
 
 
 def gdn_status_str(status: int) -> str:

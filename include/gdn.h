@@ -267,7 +267,12 @@ size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk,
  * linear in the entry state.  n_segments = 1 is a single stream; below 1
  * the call returns GDN_E_SHAPE.  Segments
  * hold ceil(NC / n_segments) chunks (NC = ceil(T / chunk)); the last may be
- * shorter.  Same tensors as gdn_chunk_fwd; a larger workspace.
+ * shorter.  When B * H * n_segments (batch, head, segment) groups are too few
+ * to fill the device with the MFMA family's whole-head loop (scalar gate),
+ * each segment is cut further into k equal runs (k * n_segments segments in
+ * all, at least 4 chunks each), as each of n_segments devices would split
+ * its own share; the results are the same up to floating-point rounding.
+ * Same tensors as gdn_chunk_fwd; a larger workspace.
  */
 int gdn_seqpar_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                    int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
@@ -299,6 +304,12 @@ int gdn_chunk_path(int64_t dk, int64_t dv, int32_t chunk, int32_t dtype,
  * arguments (1: a single stream), or a negative status.  Host only. */
 int gdn_chunk_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                        int32_t chunk, int32_t dtype, int32_t gate);
+
+/* Number of segments gdn_seqpar_fwd with n_segments runs each sequence in
+ * (n_segments, or a multiple of it: see gdn_seqpar_fwd), or a negative
+ * status.  Host only. */
+int gdn_seqpar_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                        int32_t chunk, int32_t dtype, int32_t gate, int32_t n_segments);
 
 /* Static string naming a status code. */
 const char* gdn_status_str(int status);

@@ -145,6 +145,25 @@ def test_chunk_schedule():
     assert seg(1, 100, 1, 60, 64, 64, 1, 0) < 0            # bad shape
 
 
+def test_seqpar_schedule():
+    # an explicit split runs as asked, or, when its (batch, head, segment)
+    # groups are too few for the whole-head MFMA loop, each segment cut into
+    # k equal runs (about 256 groups, at least 4 chunks a segment)
+    seg = gdn.gdn_seqpar_segments
+    assert seg(1, 65536, 4, 128, 128, 64, 1, 0, 8) == 64     # 32 groups -> 8 x 8 segments
+    assert seg(1, 65536, 4, 128, 128, 64, 1, 0, 64) == 64    # already 256 groups
+    assert seg(2, 8192, 16, 128, 128, 64, 1, 0, 8) == 8      # 256 groups
+    assert seg(2, 8192, 16, 128, 128, 64, 1, 0, 2) == 8      # 64 groups -> 2 x 4
+    assert seg(1, 65536, 4, 128, 128, 64, 1, 0, 1) == 1      # a single stream stays one
+    assert seg(1, 1000, 2, 64, 64, 64, 1, 0, 3) == 3         # 16 chunks: no finer cut
+    assert seg(8, 4096, 16, 128, 128, 64, 1, 1, 4) == 4      # channel gate: as asked
+    assert seg(1, 256, 1, 16, 16, 16, 0, 0, 4) == 4          # fp32 vector-ALU path
+    assert seg(1, 100, 1, 60, 64, 64, 1, 0, 2) < 0           # bad shape
+    # the workspace follows the segments actually run
+    assert gdn.gdn_workspace_bytes(1, 65536, 4, 128, 128, 64, 1, 0, 8) == \
+        gdn.gdn_workspace_bytes(1, 65536, 4, 128, 128, 64, 1, 0, 64)
+
+
 def test_decode_step_rejects_bad_arguments_before_any_launch():
     """gdn_decode_step's checks return before anything is enqueued (fake,
     never dereferenced pointers)."""
