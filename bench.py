@@ -540,7 +540,7 @@ def main():
     def step(nseg=G, timer=None):
         if args.raw:
             gdn.chunk_fwd_raw(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
-                              chunk=w.chunk, out=out, state_out=st, workspace=ws_raw)
+                              chunk=w.chunk, out=out, state_out=st, workspace=ws_raw, timer=timer)
             return
         gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
                       chunk=w.chunk, n_segments=nseg, out=out, state_out=st,
@@ -565,16 +565,12 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     # per-kernel durations: the same number of steps again through the timed
     # entry point, each kernel bracketed by HIP events on the launch stream
-    # (the raw entry point has no timed variant: its line carries the step's
-    # figures only, and per-kernel times come from rocprofv3)
-    kern = {}
-    if not args.raw:
-        timer = gdn.Timer()
-        for _ in range(args.steps):
-            step(timer=timer)
-        torch.cuda.synchronize()
-        kern = timer.read()
-        timer.close()
+    timer = gdn.Timer()
+    for _ in range(args.steps):
+        step(timer=timer)
+    torch.cuda.synchronize()
+    kern = timer.read()
+    timer.close()
     # per step: total time of each kernel and its launches
     per_kernel_us = {k: 1e3 * v[0] / args.steps for k, v in kern.items()}
     launches = {k: v[1] / args.steps for k, v in kern.items()}

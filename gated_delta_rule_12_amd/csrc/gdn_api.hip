@@ -338,6 +338,16 @@ int gdn_chunk_fwd_raw(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, i
                        true);
 }
 
+int gdn_chunk_fwd_raw_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t chunk,
+                            int32_t dtype, int32_t gate, int32_t order, float scale,
+                            const void* q, const void* k, const void* v, const float* alpha_logit,
+                            const float* beta_logit, const float* state0, float* out, float* state_out,
+                            void* workspace, size_t workspace_bytes, void* stream, gdn_timer* timer) {
+    return run_chunked(B, T, H, dk, dv, chunk, dtype, gate, order, scale, 0, q, k, v, alpha_logit,
+                       beta_logit, state0, out, state_out, workspace, workspace_bytes, stream, timer,
+                       true);
+}
+
 size_t gdn_raw_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                int32_t chunk, int32_t dtype, int32_t gate) {
     if (validate(B, T, H, dk, dv, chunk, dtype, gate, 0, 1) != GDN_OK) return 0;

@@ -202,12 +202,14 @@ __device__ __forceinline__ void ut_inverse_store(float* AT, float* Pw, const flo
         const int t = 16 * m + (lane & 15), gg = lane >> 4;
         uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const int j0 = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
+        for (int hf = 0; hf < 2; ++hf) {
+            // columns j0 .. j0 + 3 of row t (16-byte pieces of the tile and of beta)
+            const int j0 = 32 * s + 16 * hf + 4 * gg;
             const bool up = (j0 >> 4) > m;
-            const float v0 = up ? 0.f : AT[t * LDA + j0] * bsh[j0];
-            const float v1 = up ? 0.f : AT[t * LDA + j0 + 1] * bsh[j0 + 1];
-            split2(v0, v1, hi[e >> 1], lo[e >> 1]);
+            f32x4 v = *reinterpret_cast<const f32x4*>(&AT[t * LDA + j0]) * *reinterpret_cast<const f32x4*>(&bsh[j0]);
+            if (up) v = zero4();
+            split2(v[0], v[1], hi[2 * hf], lo[2 * hf]);
+            split2(v[2], v[3], hi[2 * hf + 1], lo[2 * hf + 1]);
         }
         // (non-temporal: written once here, read by the chunk loops later;
         // measured 5 % off stage 1 and nothing on the readers)
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* 
     // one 64 x 68 fp32 tile holds in turn the prefix scan's partials, the K
     // rows (bf16, row stride LDK) and then A and T as in the scalar kernel
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
-    __shared__ float bsh[C];
+    __shared__ __attribute__((aligned(16))) float bsh[C];
     // channel log2 prefix, rows padded by 16 bytes against bank conflicts;
     // once the scores are formed it is the inverse's per-wave scratch
     __shared__ __attribute__((aligned(16))) float gt[C][D + 4];
@@ -511,8 +513,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
     constexpr int LDA = C + 4;
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
     __shared__ float Pscr[4][16 * 17];  // per-wave scratch of the diagonal inverse
-    __shared__ float gsh[C], gpsh[C], bsh[C];
-    __shared__ float rqsh[C], rksh[C];  // 1 / |q_t|, 1 / |k_t| (raw projections; else ones)
+    __shared__ __attribute__((aligned(16))) float gsh[C], gpsh[C], bsh[C];
+    __shared__ __attribute__((aligned(16))) float rqsh[C], rksh[C];  // 1 / |q_t|, 1 / |k_t| (raw projections; else ones)
 
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
@@ -629,11 +631,16 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
         if (q >= nbk) continue;
         const int m = bm[q], nb = bn[q];
         const int j = 16 * nb + c16;
+        const int t0 = 16 * m + 4 * g4;
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(&bsh[t0]);
+        const f32x4 rkt = *reinterpret_cast<const f32x4*>(&rksh[t0]);
+        const f32x4 gpt = *reinterpret_cast<const f32x4*>(&gpsh[t0]);
+        const float gj = gsh[j], rkj = rksh[j];
         f32x4 a;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * m + 4 * g4 + r;
-            a[r] = j < t ? bsh[t] * rksh[t] * rksh[j] * __expf(gpsh[t] - gsh[j]) * acc[q][r] : 0.f;
+            const int t = t0 + r;
+            a[r] = j < t ? bt[r] * rkt[r] * rkj * __expf(gpt[r] - gj) * acc[q][r] : 0.f;
         }
         if (nb < m) {
             // A_tj stored at (j, t): upper triangle

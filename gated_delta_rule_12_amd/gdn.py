@@ -33,7 +33,8 @@ EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_s
            "gdn_status_str", "gdn_abi_version",
            "gdn_timer_create", "gdn_timer_destroy", "gdn_timer_read", "gdn_chunk_fwd_timed",
            "gdn_seqpar_fwd_timed", "gdn_decode_step_timed", "gdn_backward_timed",
-           "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_raw", "gdn_raw_workspace_bytes")
+           "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_raw", "gdn_chunk_fwd_raw_timed",
+           "gdn_raw_workspace_bytes")
 
 _lib = None
 
@@ -99,7 +100,8 @@ def lib():
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     L.gdn_timer_read.restype = ctypes.c_int
     # the *_timed variants: the same arguments plus the timer
-    for name in ("gdn_chunk_fwd", "gdn_seqpar_fwd", "gdn_decode_step", "gdn_backward"):
+    for name in ("gdn_chunk_fwd", "gdn_chunk_fwd_raw", "gdn_seqpar_fwd", "gdn_decode_step",
+                 "gdn_backward"):
         f = getattr(L, name + "_timed")
         f.argtypes = getattr(L, name).argtypes + [vp]
         f.restype = ctypes.c_int
@@ -305,10 +307,11 @@ def chunk_fwd(q, k, v, alpha, beta, state0=None, *, chunk=64,
 
 def chunk_fwd_raw(q, k, v, alpha_logit, beta_logit, state0=None, *, chunk=64,
                   order=GDN_PREDICT_THEN_DECAY, scale=1.0, out=None, state_out=None,
-                  workspace=None):
+                  workspace=None, timer=None):
     """gdn_chunk_fwd_raw: the forward on raw projections q, k (L2-normalised
     in the kernels) and gate / beta logits (through a sigmoid in the
-    kernels).  Returns (out [B,T,H,dv] fp32, final state [B,H,dv,dk])."""
+    kernels); timer: a Timer (gdn_chunk_fwd_raw_timed) or None.
+    Returns (out [B,T,H,dv] fp32, final state [B,H,dv,dk])."""
     import torch
     B, T, H, dk, dv, gate = _check(q, k, v, alpha_logit, beta_logit, state0)
     if out is None:
@@ -318,10 +321,11 @@ def chunk_fwd_raw(q, k, v, alpha_logit, beta_logit, state0=None, *, chunk=64,
     if workspace is None:
         n = int(lib().gdn_raw_workspace_bytes(B, T, H, dk, dv, chunk, _dtype_code(q), gate))
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
-    rc = lib().gdn_chunk_fwd_raw(B, T, H, dk, dv, chunk, _dtype_code(q), gate, order, scale,
-                                 _ptr(q), _ptr(k), _ptr(v), _ptr(alpha_logit), _ptr(beta_logit),
-                                 _ptr(state0), _ptr(out), _ptr(state_out), _ptr(workspace),
-                                 workspace.numel(), _stream())
+    rc = _call("gdn_chunk_fwd_raw",
+               [B, T, H, dk, dv, chunk, _dtype_code(q), gate, order, scale,
+                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha_logit), _ptr(beta_logit),
+                _ptr(state0), _ptr(out), _ptr(state_out), _ptr(workspace),
+                workspace.numel(), _stream()], timer)
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd_raw")
     return out, state_out

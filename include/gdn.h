@@ -347,6 +347,14 @@ int gdn_chunk_fwd_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                         float* out, float* state_out,
                         void* workspace, size_t workspace_bytes, void* stream,
                         gdn_timer* timer);
+int gdn_chunk_fwd_raw_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                            int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
+                            float scale,
+                            const void* q, const void* k, const void* v,
+                            const float* alpha_logit, const float* beta_logit,
+                            const float* state0, float* out, float* state_out,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            gdn_timer* timer);
 int gdn_seqpar_fwd_timed(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                          int32_t chunk, int32_t dtype, int32_t gate, int32_t order,
                          float scale, int32_t n_segments,
