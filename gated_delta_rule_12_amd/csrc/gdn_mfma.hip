@@ -1761,14 +1761,20 @@ ChainPlan chain_plan(int G, int64_t heads, int D) {
 // column tiles for step s + 1 while step s computes, straight into registers.
 // NR = 2 (compose): the P and the Q rows of a block in one workgroup, both
 // from (I, 0) through every map of the block.
+// One wave per 16-column tile of the product (D / 16 waves: two per SIMD at
+// D = 128, so the matrix cores run at the two-wave rate); each step's
+// multiplier fragments and addend rows are fetched two steps ahead into three
+// rotating register sets.
+template <int D>
+constexpr int chain_threads() { return 64 * (D / 16); }
 template <int D, int NR>
-__global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayout L, char* wsb, int mode,
-                                                    ChainPlan cp) {
+__global__ __launch_bounds__(chain_threads<D>()) void k_chain_rows(Problem p, Split sp, WsLayout L, char* wsb,
+                                                                  int mode, ChainPlan cp) {
     constexpr int LD = D + 4;
     constexpr int KS = D / 32;           // k-steps of the product
+    constexpr int NT = chain_threads<D>();
     constexpr int SP = 16 * D / 4;       // float4 pieces of 16 rows
-    constexpr int SR = (SP + 255) / 256;
-    constexpr int NTW = D / 64;          // column tiles per wave
+    constexpr int SR = (SP + NT - 1) / NT;
     constexpr int NX = D / 16;           // row blocks per head
     constexpr int64_t DD = (int64_t)D * D;
     constexpr int64_t FD = DD / 4;       // u16x8 per fragment matrix (hi and lo)
@@ -1789,7 +1795,8 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
     }
     const int64_t bh = per_block ? grp / cp.nb : grp;
     const int j = per_block ? (int)(grp % cp.nb) : 0;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int nt = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave's column tile
     const int r0 = 16 * x;
     const float* sdend = reinterpret_cast<const float*>(wsb + L.sdend) + bh * sp.G * DD;
     const u16x8* mfr = reinterpret_cast<const u16x8*>(wsb + L.mend) + bh * sp.G * FD;
@@ -1843,31 +1850,30 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
         post0 = sstart + (a + 1) * DD;
     }
 
-    // B fragments of the wave's column tiles nt = w + 4 q, hi and lo
-    u16x8 fcur[NTW][KS][2], fnxt[NTW][KS][2];
-    f32x4 sreg[SR];
-    auto fetch = [&](int s) {
-        const u16x8* F = mult0 + s * FD;
+    // register sets: B fragments of the wave's column tile (hi and lo) and the
+    // thread's pieces of the addend rows
+    typedef u16x8 Frag[KS][2];
+    typedef f32x4 Rows[SR];
+    auto fetch = [&](int s, Frag& F, Rows& S) {
+        const u16x8* M = mult0 + s * FD;
 #pragma unroll
-        for (int q = 0; q < NTW; ++q)
+        for (int k = 0; k < KS; ++k)
 #pragma unroll
-            for (int k = 0; k < KS; ++k)
+            for (int hl = 0; hl < 2; ++hl) F[k][hl] = M[((nt * KS + k) * 2 + hl) * 64 + l];
+        const f32x4* A = reinterpret_cast<const f32x4*>(add0 + s * DD + (int64_t)r0 * D);
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl) fnxt[q][k][hl] = F[(((w + 4 * q) * KS + k) * 2 + hl) * 64 + l];
-        const f32x4* S = reinterpret_cast<const f32x4*>(add0 + s * DD + (int64_t)r0 * D);
-#pragma unroll
-        for (int k = 0; k < SR; ++k) sreg[k] = S[min(tid + 256 * k, SP - 1)];
+        for (int k = 0; k < SR; ++k) S[k] = A[min(tid + NT * k, SP - 1)];
     };
     auto write_rows = [&](float* dst, const float* X) {
         float* SS = dst + (int64_t)r0 * D;
-        for (int e = tid; e < SP; e += 256) {
+        for (int e = tid; e < SP; e += NT) {
             const int r = e / (D / 4), c4 = e % (D / 4);
             *reinterpret_cast<f32x4*>(&SS[r * D + 4 * c4]) = *reinterpret_cast<const f32x4*>(&X[r * LD + 4 * c4]);
         }
     };
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        for (int e = tid; e < SP; e += 256) {
+        for (int e = tid; e < SP; e += NT) {
             const int rr = e / (D / 4), c4 = e % (D / 4);
             f32x4 val;
             if (init[r]) {
@@ -1879,52 +1885,54 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
             *reinterpret_cast<f32x4*>(&Cb[0][r][rr * LD + 4 * c4]) = val;
         }
     }
-    if (nsteps > 0) fetch(0);
+    // the end values from X in Cb[c]
+    auto finish = [&](int c) {
+        if (fin) write_rows(fin, Cb[c][NR - 1]);
+        if (fin_frag) {
+            // P_j rows 16 x .. of block j as B fragments: k-step x / 2, lane
+            // groups 2 (x % 2), 2 (x % 2) + 1
+            if (tid < (D / 16) * 32) {
+                const int ft = tid >> 5, hsel = (tid >> 4) & 1, cc = tid & 15;
+                const int gg = 2 * (x & 1) + hsel, ks = x >> 1;
+                f32x4 y0, y1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y0[e] = Cb[c][0][(8 * hsel + e) * LD + 16 * ft + cc];
+                    y1[e] = Cb[c][0][(8 * hsel + 4 + e) * LD + 16 * ft + cc];
+                }
+                u16x4 h0, l0, h1, l1;
+                split4(y0, h0, l0);
+                split4(y1, h1, l1);
+                fin_frag[((ft * KS + ks) * 2 + 0) * 64 + 16 * gg + cc] = cat(h0, h1);
+                fin_frag[((ft * KS + ks) * 2 + 1) * 64 + 16 * gg + cc] = cat(l0, l1);
+            }
+        }
+    };
     int cur = 0;
-    for (int s = 0;; ++s) {
+    // step s with its operands in (F, S); the operands of step s + 2 go to
+    // (Fn, Sn), the set step s - 1 used; false once the chain is done
+    auto step = [&](int s, const Frag& F, const Rows& S, Frag& Fn, Rows& Sn) {
+        // every step issues a fetch (the last step's operands again near the
+        // end), so that the waits below count the loads in flight exactly
+        fetch(min(s + 2, nsteps - 1), Fn, Sn);
         if (s < nsteps) {
 #pragma unroll
-            for (int q = 0; q < NTW; ++q)
-#pragma unroll
-                for (int k = 0; k < KS; ++k)
-#pragma unroll
-                    for (int hl = 0; hl < 2; ++hl) fcur[q][k][hl] = fnxt[q][k][hl];
-#pragma unroll
             for (int k = 0; k < SR; ++k) {
-                const int e = tid + 256 * k;
-                if (SP % 256 == 0 || e < SP)
-                    *reinterpret_cast<f32x4*>(&SDs[s & 1][(e / (D / 4)) * LD + 4 * (e % (D / 4))]) = sreg[k];
+                const int e = tid + NT * k;
+                if (SP % NT == 0 || e < SP)
+                    *reinterpret_cast<f32x4*>(&SDs[s & 1][(e / (D / 4)) * LD + 4 * (e % (D / 4))]) = S[k];
             }
         }
         __syncthreads();  // X complete in Cb[cur]; Add(s) staged; Cb[cur ^ 1] and SDs[s ^ 1] free
-        if (s + 1 < nsteps) fetch(s + 1);
         if (s < nsteps) {
             if (pre0) write_rows(pre0 + s * pre_stride, Cb[cur][0]);
         } else {
-            if (fin) write_rows(fin, Cb[cur][NR - 1]);
-            if (fin_frag) {
-                // P_j rows 16 x .. of block j as B fragments: k-step x / 2,
-                // lane groups 2 (x % 2), 2 (x % 2) + 1
-                if (tid < (D / 16) * 32) {
-                    const int nt = tid >> 5, hsel = (tid >> 4) & 1, cc = tid & 15;
-                    const int gg = 2 * (x & 1) + hsel, ks = x >> 1;
-                    f32x4 y0, y1;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        y0[e] = Cb[cur][0][(8 * hsel + e) * LD + 16 * nt + cc];
-                        y1[e] = Cb[cur][0][(8 * hsel + 4 + e) * LD + 16 * nt + cc];
-                    }
-                    u16x4 h0, l0, h1, l1;
-                    split4(y0, h0, l0);
-                    split4(y1, h1, l1);
-                    fin_frag[((nt * KS + ks) * 2 + 0) * 64 + 16 * gg + cc] = cat(h0, h1);
-                    fin_frag[((nt * KS + ks) * 2 + 1) * 64 + 16 * gg + cc] = cat(l0, l1);
-                }
-            }
+            finish(cur);
         }
         if (s > 0 && post0) write_rows(post0 + (s - 1) * DD, Cb[cur][0]);
-        if (s == nsteps) break;
-        // Cb[cur ^ 1][r] = Cb[cur][r] Mult(s) (+ Add(s) for the last set)
+        if (s == nsteps) return false;
+        // Cb[cur ^ 1][r] = Cb[cur][r] Mult(s) (+ Add(s) for the last set) on
+        // the wave's column tile
         u16x8 ah[NR][KS], al[NR][KS];
 #pragma unroll
         for (int r = 0; r < NR; ++r)
@@ -1939,31 +1947,39 @@ __global__ __launch_bounds__(256) void k_chain_rows(Problem p, Split sp, WsLayou
                 ah[r][k] = cat(h0, h1);
                 al[r][k] = cat(l0, l1);
             }
+        f32x4 acc[NR];
 #pragma unroll
-        for (int q = 0; q < NTW; ++q) {
-            const int nt = w + 4 * q;
-            f32x4 a1[NR], a2[NR], a3[NR];
+        for (int r = 0; r < NR; ++r) acc[r] = zero4();
 #pragma unroll
-            for (int r = 0; r < NR; ++r) a1[r] = a2[r] = a3[r] = zero4();
+        for (int i = 0; i < 4; ++i) acc[NR - 1][i] = SDs[s & 1][(4 * g4 + i) * LD + 16 * nt + c16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a1[NR - 1][i] = SDs[s & 1][(4 * g4 + i) * LD + 16 * nt + c16];
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-#pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    a1[r] = mfma(ah[r][k], fcur[q][k][0], a1[r]);
-                    a2[r] = mfma(ah[r][k], fcur[q][k][1], a2[r]);
-                    a3[r] = mfma(al[r][k], fcur[q][k][0], a3[r]);
-                }
-            }
+        for (int k = 0; k < KS; ++k)
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                const f32x4 sum = a1[r] + a2[r] + a3[r];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Cb[cur ^ 1][r][(4 * g4 + i) * LD + 16 * nt + c16] = sum[i];
+                acc[r] = mfma(ah[r][k], F[k][0], acc[r]);
+                acc[r] = mfma(ah[r][k], F[k][1], acc[r]);
+                acc[r] = mfma(al[r][k], F[k][0], acc[r]);
             }
-        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Cb[cur ^ 1][r][(4 * g4 + i) * LD + 16 * nt + c16] = acc[r][i];
         cur ^= 1;
+        return true;
+    };
+    Frag f0, f1, f2;
+    Rows s0, s1, s2;
+    if (nsteps <= 0) {  // no map: the end values are the start rows
+        __syncthreads();
+        finish(0);
+        return;
+    }
+    fetch(0, f0, s0);
+    fetch(min(1, nsteps - 1), f1, s1);
+    for (int s = 0;; s += 3) {
+        if (!step(s, f0, s0, f2, s2)) break;
+        if (!step(s + 1, f1, s1, f0, s0)) break;
+        if (!step(s + 2, f2, s2, f1, s1)) break;
     }
 }
 
@@ -2170,15 +2186,15 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
         const unsigned nx = D / 16;
         prof_begin(p.timer, "k_chain", st);
         if (cp.nb == 0) {
-            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * nx)), dim3(256), 0, st, p, sp, L, ws,
-                               (int)kChainSeq, cp);
+            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * nx)), dim3(chain_threads<D>()), 0, st, p, sp,
+                               L, ws, (int)kChainSeq, cp);
         } else {
-            hipLaunchKernelGGL((k_chain_rows<D, 2>), dim3((unsigned)(heads * cp.nb * nx)), dim3(256), 0, st, p, sp,
-                               L, ws, (int)kChainCompose, cp);
-            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * nx)), dim3(256), 0, st, p, sp, L, ws,
-                               (int)kChainBlocks, cp);
-            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * cp.nb * nx)), dim3(256), 0, st, p, sp, L,
-                               ws, (int)kChainExpand, cp);
+            hipLaunchKernelGGL((k_chain_rows<D, 2>), dim3((unsigned)(heads * cp.nb * nx)), dim3(chain_threads<D>()), 0,
+                               st, p, sp, L, ws, (int)kChainCompose, cp);
+            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * nx)), dim3(chain_threads<D>()), 0, st, p, sp,
+                               L, ws, (int)kChainBlocks, cp);
+            hipLaunchKernelGGL((k_chain_rows<D, 1>), dim3((unsigned)(heads * cp.nb * nx)), dim3(chain_threads<D>()), 0,
+                               st, p, sp, L, ws, (int)kChainExpand, cp);
         }
         prof_end(p.timer, st);
         e = hipGetLastError();
