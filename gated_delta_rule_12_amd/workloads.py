@@ -141,7 +141,8 @@ def make_raw_inputs(w: Workload, seed: int | None = None) -> dict:
     for name in ("q", "k"):
         x = rng.standard_normal((B, T, H, dk)) * rng.uniform(0.2, 5.0, (B, T, H, 1))
         out[name] = x.astype(np.float32)
-    out["k"][0, 0, 0, :] = 0.0
+    if T > 0:
+        out["k"][0, 0, 0, :] = 0.0
     out["v"] = rng.standard_normal((B, T, H, dv)).astype(np.float32)
     ashape = (B, T, H) if w.gate == "scalar" else (B, T, H, dk)
     out["alpha"] = rng.normal(w.alpha_mean, 0.5, ashape).astype(np.float32)

@@ -26,13 +26,27 @@ def _gpu():
     gdn.lib()
 
 
-def run_and_check(w, order=PTD):
+def run_and_check(w, order=PTD, edit=None, in_place=False):
+    """edit(raw) may change the drawn inputs in place before the call;
+    in_place: state_out is the start state's buffer."""
     import torch
     raw = make_raw_inputs(w)
+    if edit is not None:
+        edit(raw)
     d = to_device(raw, w)
-    o, s = gdn.chunk_fwd_raw(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
-                             chunk=w.chunk, order=order)
+    s0 = d["state0"]
+    so = None
+    if in_place:
+        s0 = s0.clone()
+        so = s0
+    o, s = gdn.chunk_fwd_raw(d["q"], d["k"], d["v"], d["alpha"], d["beta"], s0,
+                             chunk=w.chunk, order=order, state_out=so)
     torch.cuda.synchronize()
+    if T_empty(w):
+        assert o.shape[1] == 0
+        ref = raw["state0"] if raw["state0"] is not None else np.zeros((w.B, w.H, w.dv, w.dk), np.float32)
+        assert np.array_equal(s.cpu().numpy(), ref)
+        return
     q, k, a, b = oracle.prologue(raw["q"], raw["k"], raw["alpha"], raw["beta"])
     g = oracle.GATE_SCALAR if w.gate == "scalar" else oracle.GATE_CHANNEL
     o_ref, s_ref = oracle.forward(q, k, raw["v"], a, b, raw["state0"], gate=g, order=order)
@@ -42,6 +56,10 @@ def run_and_check(w, order=PTD):
     print(f"  {w.name}: out err {eo:.3e} (tol {to}), state err {es:.3e} (tol {ts})", flush=True)
     assert np.isfinite(o).all() and np.isfinite(s).all()
     assert eo <= to and es <= ts, (eo, es)
+
+
+def T_empty(w):
+    return w.T == 0
 
 
 CASES = [
@@ -92,3 +110,51 @@ def test_raw_equals_normalised_inputs_for_unit_rows():
     torch.cuda.synchronize()
     assert (o1 - o2).abs().max().item() <= 1e-5 * o1.abs().max().item()
     assert (s1 - s2).abs().max().item() <= 1e-5 * s1.abs().max().item()
+
+
+@pytest.mark.parametrize("T", [0, 1, 63, 65])
+@pytest.mark.parametrize("H", [32, 2])
+def test_raw_short_and_empty(T, H):
+    """Empty and short sequences on the whole-head shape (32 heads) and the
+    sliced one (2 heads)."""
+    w = Workload("raw-short", B=1, H=H, T=T, dk=128, dv=128, chunk=64, state0_std=0.3,
+                 seed=500 + T + H)
+    run_and_check(w)
+
+
+def test_raw_zero_rows_and_saturated_logits():
+    """Zero q and k rows (a zero vector stays zero) and gate / beta logits
+    far in both tails of the sigmoid."""
+    w = Workload("raw-edges", B=1, H=32, T=700, dk=128, dv=128, chunk=64, state0_std=0.3, seed=61)
+
+    def edit(raw):
+        raw["q"][0, 5:70:7] = 0.0
+        raw["k"][0, 3:300:11] = 0.0
+        raw["alpha"][0, 100:160] = 30.0     # gate 1 (no decay) over a chunk
+        raw["alpha"][0, 400:410] = -30.0    # gate e^-30: the state is forgotten
+        raw["beta"][0, 200:230] = -30.0     # no write
+        raw["beta"][0, 500:530] = 30.0      # full write
+    run_and_check(w, edit=edit)
+
+
+@pytest.mark.parametrize("H", [32, 2])
+def test_raw_in_place_state(H):
+    w = Workload("raw-inplace", B=1, H=H, T=900, dk=128, dv=128, chunk=64, state0_std=0.3,
+                 seed=70 + H)
+    run_and_check(w, in_place=True)
+
+
+def test_raw_timed_equals_plain():
+    """gdn_chunk_fwd_raw_timed gives bit for bit the plain call's results and
+    names the kernels it ran."""
+    import torch
+    w = Workload("raw-timed", B=1, H=32, T=1000, dk=128, dv=128, chunk=64, state0_std=0.3, seed=81)
+    d = to_device(make_raw_inputs(w), w)
+    o1, s1 = gdn.chunk_fwd_raw(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"])
+    timer = gdn.Timer()
+    o2, s2 = gdn.chunk_fwd_raw(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], timer=timer)
+    torch.cuda.synchronize()
+    names = set(timer.read())
+    timer.close()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert {"k_prep_mfma", "k_seg_out"} <= names, names
