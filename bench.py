@@ -329,6 +329,7 @@ def bench_decode(args, w):
     abytes = decode_bytes(w)
     achieved = abytes / (k_us * 1e-6) / 1e9
     log(f"step {ms * 1e3:.1f} us, k_decode {k_us:.1f} us per launch")
+    peaks = None if args.no_peaks else measure_peaks()
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(w, inp)
     res = {"metric": "decode tokens/sec (one gated-delta token per sequence, H=16 d=128)",
            "value": round(w.B / (ms * 1e-3), 1), "unit": "tokens/sec", "n_gpus": 1,
@@ -348,7 +349,10 @@ def bench_decode(args, w):
                         "dominant_kernel": {"kernel": "k_decode", "launches_per_step": 1,
                                             "avg_launch_us": round(k_us, 2), "achieved": round(achieved, 1),
                                             "frac": round(achieved / HBM_PEAK_GBS, 4),
-                                            "traffic": stored_step_traffic(w.name, ["k_decode"])}},
+                                            "traffic": stored_step_traffic(w.name, ["k_decode"])},
+                        "frac_of_achievable_copy": round(abytes / (ms * 1e-3) / 1e9 / peaks["hbm_copy_GBs"], 4)
+                        if peaks else None,
+                        "achievable_peaks": peaks},
            "cpu_baseline": cpu, "raw_prologue_ms_per_step": round(raw_ms, 5)}
     print(json.dumps(res), flush=True)
 
@@ -434,6 +438,7 @@ def bench_backward(args, w):
     abytes = backward_bytes(w)
     achieved = abytes / (k_us * 1e-6) / 1e9
     log(f"step {ms * 1e3:.1f} us, k_backward {k_us:.1f} us per launch")
+    peaks = None if args.no_peaks else measure_peaks()
     cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, inp, gr)
     res = {"metric": "backward tokens/sec (gradients through the gated-delta recurrence, H=16 d=128 T=8K)",
            "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/sec", "n_gpus": 1,
@@ -456,7 +461,10 @@ def bench_backward(args, w):
                                             "launches_per_step": kern["k_backward"][1] / args.steps,
                                             "avg_launch_us": round(k_us, 2), "achieved": round(achieved, 1),
                                             "frac": round(achieved / HBM_PEAK_GBS, 4),
-                                            "traffic": stored_step_traffic(w.name + "-backward", ["k_backward"])}},
+                                            "traffic": stored_step_traffic(w.name + "-backward", ["k_backward"])},
+                        "frac_of_achievable_copy": round(abytes / (ms * 1e-3) / 1e9 / peaks["hbm_copy_GBs"], 4)
+                        if peaks else None,
+                        "achievable_peaks": peaks},
            "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
