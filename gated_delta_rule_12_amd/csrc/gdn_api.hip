@@ -233,7 +233,10 @@ static int backward_common(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
         !aligned(grad_k, 16) || !aligned(grad_v, 4) || !aligned(grad_alpha, gate_align) ||
         !aligned(grad_beta, 4) || !aligned(workspace, 16))
         return GDN_E_ARG;
-    const size_t need = backward_workspace(B, T, H, dk, dv, gate);
+    const bool chunked = chunked_backward_supported(dk, dv, gate);
+    // the chunked path reads dL/d out in 16-byte pieces
+    if (chunked && !aligned(grad_out, 16)) return GDN_E_ARG;
+    const size_t need = chunked ? chunked_backward_workspace(B, T, H, dk) : backward_workspace(B, T, H, dk, dv, gate);
     if (T > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
     BwdProblem a{};
     a.p = make_problem(B, T, H, dk, dv, 16, dtype, gate, order, scale);
@@ -243,6 +246,7 @@ static int backward_common(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
     a.ds_out = grad_state_out;
     a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dalpha = grad_alpha; a.dbeta = grad_beta;
     a.ds0 = grad_state0;
+    if (chunked) return finish(backward_chunked(a, workspace, static_cast<hipStream_t>(stream)));
     a.ckpt = static_cast<float*>(workspace);
     a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_ckpt_bytes(B, T, H, dk, dv, gate));
     return finish(backward(a, static_cast<hipStream_t>(stream)));
@@ -424,7 +428,14 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv, int32_t dt
 size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                     int32_t gate) {
     if (validate(B, T, H, dk, dv, 16, GDN_F32, gate, GDN_PREDICT_THEN_DECAY, 1) != GDN_OK) return 0;
+    if (chunked_backward_supported(dk, dv, gate)) return chunked_backward_workspace(B, T, H, dk);
     return backward_workspace(B, T, H, dk, dv, gate);
+}
+
+int gdn_backward_path(int64_t dk, int64_t dv, int32_t gate) {
+    if (validate(1, 1, 1, dk, dv, 16, GDN_F32, gate, GDN_PREDICT_THEN_DECAY, 1) != GDN_OK)
+        return validate(1, 1, 1, dk, dv, 16, GDN_F32, gate, GDN_PREDICT_THEN_DECAY, 1);
+    return chunked_backward_supported(dk, dv, gate) ? GDN_BWD_CHUNKED : GDN_BWD_TOKEN;
 }
 
 int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int32_t dtype, int32_t gate,

@@ -1,0 +1,897 @@
+// Chunked backward of the gated delta rule (gdn_backward with a scalar gate,
+// dk = dv = D in {64, 128}; the channel gate and other shapes take the token
+// kernel of gdn_bwd.hip).
+//
+// The pages fix the forward only (the DeltaNet illustrated notes, WY/UT
+// section: UT transform, chunk state passing, output; the scalar gate of the
+// Gated DeltaNet paragraph); these are the chain rule through its chunk
+// form.  Per chunk of C = 64 tokens with entry state S (dv x dk), chunk-local
+// log-gate prefix l_t (gamma_t = e^{l_t}), prediction prefix l'_t (l_{t-1}
+// predict-then-decay, l_t decay-then-predict), R_t = e^{l_{C-1} - l_t}:
+//   A_tj = beta_t e^{l'_t - l_j} k_t.k_j (j < t),  T = (I + A)^{-1}
+//   X = K S^T,  U = V - diag(gamma') X,  Delta = T diag(beta) U
+//   O = scale (diag(gamma) Q S^T + P Delta),  P_tj = e^{l_t - l_j} q_t.k_j (j <= t)
+//   S_end = gamma_{C-1} S + Delta^T diag(R) K
+// and, with dO and dS_end given:
+//   dDelta = scale P^T dO + diag(R) K dS_end^T,  dU' = T^T dDelta,  dV = diag(beta) dU'
+//   dS = gamma_{C-1} dS_end + scale dO^T diag(gamma) Q - dU'^T diag(gamma' beta) K
+//   dP = scale dO Delta^T (j <= t),  dT = dDelta U^T diag(beta),  dA = -T^T dT T^T (j < t)
+//   dQ = scale diag(gamma) dO S + (dP o M) K,         M_tj = e^{l_t - l_j}
+//   dK = (dP o M)^T Q - diag(gamma' beta) dU' S + diag(R) Delta dS_end + (W + W^T) K,
+//        W_tj = beta_t dA_tj e^{l'_t - l_j}
+//   dbeta_t = dU'_t . U_t + sum_j dA_tj Atilde_tj,     Atilde = A / beta
+// The gate gradient is taken pair by pair: every product of gates above is a
+// ratio e^{l_b - l_a} over the tokens a < s <= b (a = -1: from the chunk
+// start), whose derivative in log alpha_s is the term itself, so
+//   dlog alpha_s = sum over terms whose range holds s   (dalpha_s = that / alpha_s),
+// summed as a two-dimensional prefix over a matrix V[b][a + 1] of the terms
+// (pair terms dP o P, dA o A at their ranges; the boundary terms q_t.dQ_S0,
+// k_t.dK_S0, gamma_{C-1} <dS_end, S> and k_j.dK_dS at theirs, the last two
+// formed from the S and dS_end parts of dQ and dK).  Every addend of a sum
+// for s then carries the factor alpha_s, so the division loses nothing
+// where a gate is small.  l is kept as a compensated pair (hi + lo, each
+// step of the prefix an error-free addition), so every ratio's exponent
+// (hi_b - hi_a) + (lo_b - lo_a) is accurate to the fp32 rounding of its own
+// value, not of the prefix.
+//
+// Three kernels, all fp32 MFMA (16 x 16 x 4, the layout of gdn_mfma_common.h;
+// bf16 inputs are exact in fp32), fp32 accumulation:
+//   k_bprep, one workgroup per chunk: gate prefix, Gram K K^T and Q K^T, A,
+//     T by the in-LDS UT inverse; T, T^T and P^T in the workspace, with K
+//     and Q as transposed fragments (K[16 tb + 4 g + q][16 m + c] per lane).
+//   k_bchain, one workgroup per (head, 16-row slice of the state) and
+//     direction: the forward chain carries S over the chunks and stores each
+//     chunk's entry state, U and Delta; the reverse chain carries dS back and
+//     stores each chunk's dS_end, dDelta and dU' and writes dv and dS_0.  Rows
+//     of the state are independent given T, K and the gates, so a slice holds
+//     its 16 rows in registers; wave w owns key tiles of it, the token tiles
+//     of the chunk products are dealt over the waves and exchanged in LDS.
+//   k_bgrad, one workgroup per chunk: everything else from the stored pieces.
+#include <type_traits>
+
+#include "gdn_internal.h"
+#include "gdn_mfma_common.h"
+#include "../../include/gdn.h"
+
+namespace gdn {
+namespace {
+
+constexpr int LDA = C + 4;  // row stride of C x C fp32 tiles in LDS
+
+// acc += A B over a 16 x 16 x 16 block: a = A[c][4g .. 4g + 3] (the lane's
+// row c, four consecutive contraction indices), b = B[4g .. 4g + 3][c].  An
+// accumulator tile of M serves as b for M as it stands; one of M^T as a.
+__device__ __forceinline__ f32x4 blk(const f32x4& a, const f32x4& b, f32x4 acc) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = mfma_f32(a[q], b[q], acc);
+    return acc;
+}
+
+// four consecutive input elements (q, k: 8 bytes bf16 or 16 bytes fp32)
+template <int DT>
+__device__ __forceinline__ f32x4 ld4in(const void* base, int64_t i) {
+    if constexpr (DT == GDN_BF16) {
+        const u32x2 u = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i);
+        return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xFFFF0000u),
+                     __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xFFFF0000u)};
+    } else {
+        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
+    }
+}
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ float dot4(const f32x4& x, const f32x4& y) {
+    return x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+}
+// lower block (m, nb), nb <= m, of the 10 of a C x C tile, by index
+__device__ __forceinline__ int blk_m(int i) { return i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0; }
+__device__ __forceinline__ int blk_n(int i) { const int m = blk_m(i); return i - m * (m + 1) / 2; }
+__device__ __forceinline__ void st4f(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+
+__device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
+    s = a + b;
+    const float bb = s - a;
+    e = (a - (s - bb)) + (b - bb);
+}
+
+// Chunk gates on one wave (lane t = token t of the chunk; past the sequence
+// end alpha = 1, beta = 0): the log-gate prefix as hi + lo, the prediction
+// prefix, beta and alpha.
+struct Gate {
+    float hi, lo, phi, plo, beta, alpha;
+};
+__device__ __forceinline__ Gate chunk_gate(const Problem& p, int64_t row0, int nt, int lane) {
+    Gate g;
+    g.alpha = 1.f;
+    g.beta = 0.f;
+    if (lane < nt) {
+        g.alpha = p.alpha[row0 + (int64_t)lane * p.H];
+        g.beta = p.beta[row0 + (int64_t)lane * p.H];
+    }
+    float hi = lane < nt ? logf(g.alpha) : 0.f, lo = 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float h2 = __shfl_up(hi, o, 64), l2 = __shfl_up(lo, o, 64);
+        if (lane >= o) {
+            float s, e;
+            two_sum(hi, h2, s, e);
+            hi = s;
+            lo = (lo + l2) + e;
+        }
+    }
+    g.hi = hi;
+    g.lo = lo;
+    if (p.order == GDN_PREDICT_THEN_DECAY) {
+        g.phi = __shfl_up(hi, 1, 64);
+        g.plo = __shfl_up(lo, 1, 64);
+        if (lane == 0) g.phi = g.plo = 0.f;
+    } else {
+        g.phi = hi;
+        g.plo = lo;
+    }
+    return g;
+}
+
+// e^{(hb - ha) + (lb - la)}
+__device__ __forceinline__ float ratio(float hb, float lb, float ha, float la) {
+    return __expf((hb - ha) + (lb - la));
+}
+
+// Per-chunk records of the workspace.  Fragment sets: [m][tb][lane] of
+// f32x4 = X[16 tb + 4 g + q][16 m + c] (q = 0..3) for X = K, Q; state
+// fragments [vb][db][lane] of f32x4 = S[16 vb + 4 g + q][16 db + c].
+template <int D>
+struct Rec {
+    static constexpr int NB = D / 16;
+    static constexpr size_t kTile = (size_t)C * C;          // T, T^T, P^T (floats)
+    static constexpr size_t kFrag = (size_t)NB * 4 * 64 * 4;  // K^T, Q^T fragments
+    static constexpr size_t kState = (size_t)NB * NB * 64 * 4;
+    static constexpr size_t kRows = (size_t)C * D;          // U, Delta, dDelta, dU'
+};
+
+struct CbWs {
+    float *T, *TT, *PT;        // [chunk][C][C]
+    float *KTf, *QTf;          // [chunk][fragment set]
+    float *Sf, *dSf;           // [chunk][state fragments]
+    float *U, *Dl, *dDl, *dUp; // [chunk][C][D]
+};
+
+// ---------------------------------------------------------------------------
+// k_bprep: T, T^T, P^T and the K^T, Q^T fragments of one chunk
+// ---------------------------------------------------------------------------
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
+    using E = std::conditional_t<DT == GDN_BF16, uint16_t, float>;
+    constexpr int NB = D / 16;
+    constexpr int LDK = D + (DT == GDN_BF16 ? 8 : 4);
+    constexpr int EP = 16 / sizeof(E);  // elements per 16-byte piece
+    constexpr int PPR = D / EP;         // pieces per row
+    __shared__ __attribute__((aligned(16))) float AT[C * LDA];
+    __shared__ __attribute__((aligned(16))) E Ks[C * LDK];
+    __shared__ __attribute__((aligned(16))) E Qs[C * LDK];
+    __shared__ float Pscr[4][16 * 17];
+    __shared__ float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C];
+
+    const Problem& p = a.p;
+    const int64_t ci = blockIdx.x;
+    const int64_t bl = ci / p.NC;
+    const int c = (int)(ci - bl * p.NC);
+    const int64_t bh = a.bh0 + bl, b = bh / p.H, h = bh - b * p.H;
+    const int64_t t0 = (int64_t)c * C;
+    const int nt = (int)min<int64_t>(C, p.T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+
+    // K and Q rows into LDS (rows past the sequence end zero)
+    constexpr int KP = C * PPR / kThreads;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+        const int e = tid + kThreads * i, t = e / PPR, pc = e % PPR;
+        const int64_t src = ((b * p.T + t0 + min(t, nt - 1)) * p.H + h) * D + pc * EP;
+        u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(p.k) + src);
+        u32x4 qv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(p.q) + src);
+        if (t >= nt) kv = qv = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(&Ks[t * LDK + pc * EP]) = kv;
+        *reinterpret_cast<u32x4*>(&Qs[t * LDK + pc * EP]) = qv;
+    }
+    if (w == 0) {
+        const Gate g = chunk_gate(p, (b * p.T + t0) * p.H + h, nt, l);
+        ghi[l] = g.hi;
+        glo[l] = g.lo;
+        gphi[l] = g.phi;
+        gplo[l] = g.plo;
+        gbeta[l] = g.beta;
+    }
+    __syncthreads();
+
+    auto row4 = [&](const E* X, int t, int d0) -> f32x4 {
+        if constexpr (DT == GDN_BF16) return ld4in<DT>(X, t * LDK + d0);
+        else return ld4f(X + t * LDK + d0);
+    };
+    // Gram blocks (m, nb) and Q K^T blocks, nb <= m: 20 jobs over 4 waves
+    for (int job = w; job < 20; job += 4) {
+        const int kind = job / 10, m = blk_m(job % 10), nb = blk_n(job % 10);
+        const E* X = kind == 0 ? Ks : Qs;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+            acc = blk(row4(X, 16 * m + c16, 16 * kb + 4 * g4), row4(Ks, 16 * nb + c16, 16 * kb + 4 * g4), acc);
+        const int j = 16 * nb + c16;
+        if (kind == 0) {
+            // A_tj = beta_t e^{l'_t - l_j} k_t.k_j (j < t), in the inverse's layout
+            f32x4 av;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * m + 4 * g4 + r;
+                av[r] = j < t ? gbeta[t] * ratio(gphi[t], gplo[t], ghi[j], glo[j]) * acc[r] : 0.f;
+            }
+            if (nb < m) {
+                st4f(&AT[j * LDA + 16 * m + 4 * g4], av);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) AT[(16 * m + 4 * g4 + r) * LDA + j] = av[r];
+            }
+        } else {
+            // P_tj = e^{l_t - l_j} q_t.k_j (j <= t), stored as P^T[j][t]
+            f32x4 pv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * m + 4 * g4 + r;
+                pv[r] = j <= t ? ratio(ghi[t], glo[t], ghi[j], glo[j]) * acc[r] : 0.f;
+            }
+            st4f(ws.PT + ci * Rec<D>::kTile + j * C + 16 * m + 4 * g4, pv);
+        }
+    }
+    __syncthreads();
+    ut_inverse_lds(AT, Pscr[w]);
+
+    // T and T^T, row-major, zero above (below) the diagonal
+    float* Tg = ws.T + ci * Rec<D>::kTile;
+    float* TTg = ws.TT + ci * Rec<D>::kTile;
+    for (int e = tid; e < C * C / 4; e += kThreads) {
+        const int r0 = e >> 4, c0 = (e & 15) * 4;
+        f32x4 x, y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = c0 + i <= r0 ? AT[r0 * LDA + c0 + i] : 0.f;   // T[r0][c0 + i]
+            y[i] = r0 <= c0 + i ? AT[(c0 + i) * LDA + r0] : 0.f; // T^T[r0][c0 + i] = T[c0 + i][r0]
+        }
+        st4f(Tg + r0 * C + c0, x);
+        st4f(TTg + r0 * C + c0, y);
+    }
+    // K^T and Q^T fragments
+    for (int f = tid; f < NB * 4 * 64; f += kThreads) {
+        const int ln = f & 63, mt = f >> 6, m = mt >> 2, tb = mt & 3;
+        const int gg = ln >> 4, cc = ln & 15;
+        f32x4 kx, qx;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = 16 * tb + 4 * gg + q, d = 16 * m + cc;
+            if constexpr (DT == GDN_BF16) {
+                kx[q] = gdn_bf16_to_f32(Ks[t * LDK + d]);
+                qx[q] = gdn_bf16_to_f32(Qs[t * LDK + d]);
+            } else {
+                kx[q] = Ks[t * LDK + d];
+                qx[q] = Qs[t * LDK + d];
+            }
+        }
+        st4f(ws.KTf + ci * Rec<D>::kFrag + (size_t)f * 4, kx);
+        st4f(ws.QTf + ci * Rec<D>::kFrag + (size_t)f * 4, qx);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_bchain: the forward state chain and the reverse adjoint chain
+// ---------------------------------------------------------------------------
+// Per-wave LDS gate rows of the current chunk.
+struct ChainShared {
+    f32x4 red[4][4][64];  // [wave][token tile][lane]: partial K S^T (or K dS^T)
+    f32x4 xch[4][64];     // [token tile][lane]: Delta R (forward) / dDelta (reverse)
+    f32x4 xch2[4][64];    // reverse: -gamma' beta dU'
+    float g[4][6][C];     // [wave][hi, lo, phi, plo, beta, -][token]
+};
+
+// Token-row factors of the chunk from the wave's gate rows.
+struct RowF {
+    const float* g;  // [6][C]
+    __device__ float gam(int t) const { return __expf(g[0 * C + t] + g[1 * C + t]); }
+    __device__ float gamp(int t) const { return __expf(g[2 * C + t] + g[3 * C + t]); }
+    __device__ float R(int t) const {
+        return ratio(g[0 * C + C - 1], g[1 * C + C - 1], g[0 * C + t], g[1 * C + t]);
+    }
+    __device__ float gC() const { return __expf(g[0 * C + C - 1] + g[1 * C + C - 1]); }
+    __device__ float beta(int t) const { return g[4 * C + t]; }
+};
+
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void k_bchain(BwdProblem a, CbWs ws) {
+    constexpr int NB = D / 16, MT = D / 64;
+    __shared__ ChainShared sh;
+    const Problem& p = a.p;
+    const int NS = NB;  // 16-row slices per head
+    const int64_t nsl = a.nbh * NS;
+    const bool rev = blockIdx.x < nsl;
+    const int64_t idx = rev ? blockIdx.x : blockIdx.x - nsl;
+    const int64_t bl = idx / NS;
+    const int rho = (int)(idx - bl * NS), r0 = 16 * rho;
+    const int64_t bh = a.bh0 + bl, b = bh / p.H, h = bh - b * p.H;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int NC = p.NC;
+    float* gw = &sh.g[w][0][0];
+    const RowF rf{gw};
+
+    // the slice's state rows as accumulator tiles of S^T: tile mi holds
+    // S[r0 + c16][16 (w MT + mi) + 4 g4 + r]
+    f32x4 St[MT];
+    const float* init = rev ? a.ds_out : p.s0;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+        const int m = w * MT + mi;
+        St[mi] = init ? ld4f(init + ((bh * D + r0 + c16) * D) + 16 * m + 4 * g4) : zero4();
+    }
+
+    for (int step = 0; step < NC; ++step) {
+        const int c = rev ? NC - 1 - step : step;
+        const int64_t ci = bl * NC + c;
+        const int64_t t0 = (int64_t)c * C;
+        const int nt = (int)min<int64_t>(C, p.T - t0);
+        const int64_t row0 = (b * p.T + t0) * p.H + h;  // (batch, token t0, head)
+        {
+            const Gate g = chunk_gate(p, row0, nt, l);
+            gw[0 * C + l] = g.hi;
+            gw[1 * C + l] = g.lo;
+            gw[2 * C + l] = g.phi;
+            gw[3 * C + l] = g.plo;
+            gw[4 * C + l] = g.beta;
+        }
+        // the state this chunk starts from (forward) or ends with (reverse),
+        // as the gradient kernel's state fragments
+        {
+            float* dst = (rev ? ws.dSf : ws.Sf) + ci * Rec<D>::kState;
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                const int m = w * MT + mi;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[((size_t)(rho * NB + m) * 64 + 16 * (c16 >> 2) + 4 * g4 + r) * 4 + (c16 & 3)] = St[mi][r];
+            }
+        }
+        // partial K S^T over the wave's key tiles, every token tile
+#pragma unroll
+        for (int at = 0; at < 4; ++at) {
+            const int t = 16 * at + c16;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                const int m = w * MT + mi;
+                f32x4 kx = ld4in<DT>(p.k, (row0 + (int64_t)min(t, nt - 1) * p.H) * D + 16 * m + 4 * g4);
+                if (t >= nt) kx = zero4();
+                acc = blk(kx, St[mi], acc);
+            }
+            sh.red[w][at][l] = acc;
+        }
+        if (!rev) {
+            __syncthreads();
+            // U' tiles jb <= w and the Delta tile w: Delta_w = sum_jb T[w][jb] U'[jb]
+            f32x4 dl = zero4();
+            for (int jb = 0; jb <= w; ++jb) {
+                const f32x4 X = sh.red[0][jb][l] + sh.red[1][jb][l] + sh.red[2][jb][l] + sh.red[3][jb][l];
+                f32x4 U, Up;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * jb + 4 * g4 + r;
+                    const float vv = t < nt ? gdn_ld<DT>(p.v, (row0 + (int64_t)t * p.H) * D + r0 + c16) : 0.f;
+                    U[r] = vv - rf.gamp(t) * X[r];
+                    Up[r] = rf.beta(t) * U[r];
+                }
+                if (jb == w) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ws.U[ci * Rec<D>::kRows + (16 * w + 4 * g4 + r) * D + r0 + c16] = U[r];
+                }
+                dl = blk(ld4f(ws.T + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4), Up, dl);
+            }
+            f32x4 rd;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * w + 4 * g4 + r;
+                ws.Dl[ci * Rec<D>::kRows + t * D + r0 + c16] = dl[r];
+                rd[r] = rf.R(t) * dl[r];
+            }
+            sh.xch[w][l] = rd;
+            __syncthreads();
+            // S^T <- gamma_C S^T + K^T diag(R) Delta
+            const float gC = rf.gC();
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                const int m = w * MT + mi;
+                f32x4 acc = gC * St[mi];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    acc = blk(ld4f(ws.KTf + ci * Rec<D>::kFrag + ((size_t)(m * 4 + tb) * 64 + l) * 4), sh.xch[tb][l], acc);
+                St[mi] = acc;
+            }
+        } else {
+            // state-independent pieces: E_w = scale P^T[w][.] dO and
+            // scale Q^T diag(gamma) dO over the wave's key tiles
+            f32x4 dob[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int t = 16 * tb + 4 * g4 + q;
+                    dob[tb][q] = t < nt ? a.dout[(row0 + (int64_t)t * p.H) * D + r0 + c16] : 0.f;
+                }
+            }
+            f32x4 E = zero4();
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                if (tb >= w)
+                    E = blk(ld4f(ws.PT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * tb + 4 * g4), dob[tb], E);
+            E = p.scale * E;
+            f32x4 QD[MT];
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) QD[mi] = zero4();
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 sg;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sg[q] = p.scale * rf.gam(16 * tb + 4 * g4 + q) * dob[tb][q];
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi) {
+                    const int m = w * MT + mi;
+                    QD[mi] = blk(ld4f(ws.QTf + ci * Rec<D>::kFrag + ((size_t)(m * 4 + tb) * 64 + l) * 4), sg, QD[mi]);
+                }
+            }
+            __syncthreads();
+            // dDelta tile w = diag(R) K dS^T + E_w
+            {
+                const f32x4 Y = sh.red[0][w][l] + sh.red[1][w][l] + sh.red[2][w][l] + sh.red[3][w][l];
+                f32x4 dd;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * w + 4 * g4 + r;
+                    dd[r] = rf.R(t) * Y[r] + E[r];
+                    ws.dDl[ci * Rec<D>::kRows + t * D + r0 + c16] = dd[r];
+                }
+                sh.xch[w][l] = dd;
+            }
+            __syncthreads();
+            // dU' tile w = sum_{jb >= w} T^T[w][jb] dDelta[jb]; dv = beta dU'
+            f32x4 du = zero4();
+            for (int jb = w; jb < 4; ++jb)
+                du = blk(ld4f(ws.TT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4), sh.xch[jb][l], du);
+            f32x4 bk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * w + 4 * g4 + r;
+                ws.dUp[ci * Rec<D>::kRows + t * D + r0 + c16] = du[r];
+                if (t < nt) a.dv[(row0 + (int64_t)t * p.H) * D + r0 + c16] = rf.beta(t) * du[r];
+                bk[r] = -rf.gamp(t) * rf.beta(t) * du[r];
+            }
+            sh.xch2[w][l] = bk;
+            __syncthreads();
+            // dS^T <- gamma_C dS^T + scale Q^T diag(gamma) dO - K^T diag(gamma' beta) dU'
+            const float gC = rf.gC();
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                const int m = w * MT + mi;
+                f32x4 acc = gC * St[mi] + QD[mi];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    acc = blk(ld4f(ws.KTf + ci * Rec<D>::kFrag + ((size_t)(m * 4 + tb) * 64 + l) * 4), sh.xch2[tb][l], acc);
+                St[mi] = acc;
+            }
+        }
+    }
+    if (rev && a.ds0) {
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            const int m = w * MT + mi;
+            st4f(a.ds0 + ((bh * D + r0 + c16) * D) + 16 * m + 4 * g4, St[mi]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_bgrad: dq, dk, dbeta and dalpha of one chunk
+// ---------------------------------------------------------------------------
+struct GradShared {
+    float dPm[C * LDA];   // dP o M (lower triangle, zero above)
+    float At[C * LDA];    // Atilde (strictly lower); then W + W^T (full)
+    float dT[C * LDA];    // dT (lower triangle)
+    float Vm[C * LDA];    // gate terms V[b][a + 1]; then their prefix along a
+    float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C], galpha[C];
+    float db1[C];         // dU'_t . U_t
+    float db2[4][C];      // per wave: sum_j dA_tj Atilde_tj
+    float vo[4][C], vx[4][C], vr[4][C];  // per wave: q.dQ_S0, k.dK_S0, k.dK_dS
+    float sd[4];          // per wave: <dS_end, S>
+};
+
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void k_bgrad(BwdProblem a, CbWs ws) {
+    constexpr int NB = D / 16, MT = D / 64;
+    __shared__ __attribute__((aligned(16))) GradShared sh;
+    const Problem& p = a.p;
+    const int64_t ci = blockIdx.x;
+    const int64_t bl = ci / p.NC;
+    const int c = (int)(ci - bl * p.NC);
+    const int64_t bh = a.bh0 + bl, b = bh / p.H, h = bh - b * p.H;
+    const int64_t t0 = (int64_t)c * C;
+    const int nt = (int)min<int64_t>(C, p.T - t0);
+    const int64_t row0 = (b * p.T + t0) * p.H + h;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const float* U = ws.U + ci * Rec<D>::kRows;
+    const float* Dl = ws.Dl + ci * Rec<D>::kRows;
+    const float* dDl = ws.dDl + ci * Rec<D>::kRows;
+    const float* dUp = ws.dUp + ci * Rec<D>::kRows;
+    const float* Tg = ws.T + ci * Rec<D>::kTile;
+    const float* TTg = ws.TT + ci * Rec<D>::kTile;
+    const float* KTf = ws.KTf + ci * Rec<D>::kFrag;
+    const float* QTf = ws.QTf + ci * Rec<D>::kFrag;
+    auto rowaddr = [&](int t) { return (row0 + (int64_t)min(t, nt - 1) * p.H) * D; };
+
+    // ---- phase 0: gates, dU'.U, cleared sums
+    if (w == 0) {
+        const Gate g = chunk_gate(p, row0, nt, l);
+        sh.ghi[l] = g.hi;
+        sh.glo[l] = g.lo;
+        sh.gphi[l] = g.phi;
+        sh.gplo[l] = g.plo;
+        sh.gbeta[l] = g.beta;
+        sh.galpha[l] = g.alpha;
+    }
+    {
+        const int t = tid >> 2, part = tid & 3;
+        float s = 0.f;
+#pragma unroll 4
+        for (int d = 4 * part; d < D; d += 16) s += dot4(ld4f(dUp + t * D + d), ld4f(U + t * D + d));
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (part == 0) sh.db1[t] = s;
+    }
+    for (int e = tid; e < C * LDA; e += kThreads) sh.Vm[e] = 0.f;
+    for (int e = tid; e < 4 * C; e += kThreads) (&sh.db2[0][0])[e] = 0.f;
+    __syncthreads();
+    auto ex = [&](int tb_, int ja) { return ratio(sh.ghi[tb_], sh.glo[tb_], sh.ghi[ja], sh.glo[ja]); };
+    auto exp_ = [&](int tb_, int ja) { return ratio(sh.gphi[tb_], sh.gplo[tb_], sh.ghi[ja], sh.glo[ja]); };
+
+    // ---- phase 1: C x C products on the lower blocks
+    for (int job = w; job < 20; job += 4) {
+        const int kind = job / 10, tb = blk_m(job % 10), jb = blk_n(job % 10);
+        const int ta = 16 * tb + c16, ja = 16 * jb + c16;  // A-operand row, B-operand row
+        f32x4 x1 = zero4(), x2 = zero4();
+        if (kind == 0) {
+            // dP = scale dO Delta^T and Q K^T
+            const float ok = ta < nt ? 1.f : 0.f;
+#pragma unroll 4
+            for (int vb = 0; vb < NB; ++vb)
+                x1 = blk(ok * ld4f(a.dout + rowaddr(ta) + 16 * vb + 4 * g4), ld4f(Dl + ja * D + 16 * vb + 4 * g4), x1);
+            const float okj = ja < nt ? 1.f : 0.f;
+#pragma unroll 4
+            for (int db = 0; db < NB; ++db)
+                x2 = blk(ok * ld4in<DT>(p.q, rowaddr(ta) + 16 * db + 4 * g4),
+                         okj * ld4in<DT>(p.k, rowaddr(ja) + 16 * db + 4 * g4), x2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tb + 4 * g4 + r, j = 16 * jb + c16;
+                const float M = j <= t ? ex(t, j) : 0.f;
+                const float dpm = p.scale * x1[r] * M;
+                sh.dPm[t * LDA + j] = dpm;
+                sh.Vm[t * LDA + 1 + j] = j < t ? dpm * x2[r] : 0.f;
+            }
+        } else {
+            // Gram K K^T and dT = dDelta U^T diag(beta)
+            const float ok = ta < nt ? 1.f : 0.f, okj = ja < nt ? 1.f : 0.f;
+#pragma unroll 4
+            for (int db = 0; db < NB; ++db)
+                x1 = blk(ok * ld4in<DT>(p.k, rowaddr(ta) + 16 * db + 4 * g4),
+                         okj * ld4in<DT>(p.k, rowaddr(ja) + 16 * db + 4 * g4), x1);
+#pragma unroll 4
+            for (int vb = 0; vb < NB; ++vb)
+                x2 = blk(ld4f(dDl + ta * D + 16 * vb + 4 * g4), ld4f(U + ja * D + 16 * vb + 4 * g4), x2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tb + 4 * g4 + r, j = 16 * jb + c16;
+                sh.At[t * LDA + j] = j < t ? exp_(t, j) * x1[r] : 0.f;
+                sh.dT[t * LDA + j] = j <= t ? x2[r] * sh.gbeta[j] : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: dA = -T^T (dT T^T), column block bb = w.  Atilde of an
+    // entry is read and replaced by W + W^T in the same lane: the lower entry
+    // (ar, bc) takes W, the upper one (bc, ar), never read as Atilde, its
+    // transpose, the diagonal zero
+    {
+        const int bb = w;
+        f32x4 Z[4];
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+            Z[ib] = zero4();
+            if (ib < bb) continue;
+            for (int jb = 0; jb <= bb; ++jb)
+                Z[ib] = blk(ld4f(&sh.dT[(16 * ib + c16) * LDA + 16 * jb + 4 * g4]),
+                            ld4f(Tg + (16 * bb + c16) * C + 16 * jb + 4 * g4), Z[ib]);
+        }
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab) {
+            if (ab < bb) continue;
+            f32x4 dA = zero4();
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+                if (ib >= ab) dA = blk(ld4f(TTg + (16 * ab + c16) * C + 16 * ib + 4 * g4), Z[ib], dA);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ar = 16 * ab + 4 * g4 + r, bc = 16 * bb + c16;
+                const bool lower = ar > bc;
+                const float da = -dA[r];
+                const float at = lower ? sh.At[ar * LDA + bc] : 0.f;
+                const float bt = sh.gbeta[ar];
+                if (lower) {
+                    const int row = p.order == GDN_DECAY_THEN_PREDICT ? ar : ar - 1;
+                    sh.Vm[row * LDA + 1 + bc] += da * bt * at;
+                    const float wk = bt * da * exp_(ar, bc);
+                    sh.At[ar * LDA + bc] = wk;
+                    sh.At[bc * LDA + ar] = wk;
+                } else if (ar == bc) {
+                    sh.At[ar * LDA + bc] = 0.f;
+                }
+                const float rs = row_sum<16>(lower ? da * at : 0.f);
+                if (c16 == 0) sh.db2[w][ar] = rs;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: dQ and dK, value-column blocks db = w MT + mi
+    f32x4 aQ[4][MT], aK1[4][MT], aK2[4][MT];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) aQ[tb][mi] = aK1[tb][mi] = aK2[tb][mi] = zero4();
+    float sdot = 0.f;
+    {
+        float fo[4], fu[4], fr[4], okr[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int t = 16 * tb + c16;
+            okr[tb] = t < nt ? 1.f : 0.f;
+            fo[tb] = p.scale * __expf(sh.ghi[t] + sh.glo[t]);
+            fu[tb] = -__expf(sh.gphi[t] + sh.gplo[t]) * sh.gbeta[t];
+            fr[tb] = ratio(sh.ghi[C - 1], sh.glo[C - 1], sh.ghi[t], sh.glo[t]);
+        }
+        for (int vb = 0; vb < NB; ++vb) {
+            f32x4 sf[MT], dsf[MT];
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                const int db = w * MT + mi;
+                const size_t fo_ = ((size_t)(vb * NB + db) * 64 + l) * 4;
+                sf[mi] = ld4f(ws.Sf + ci * Rec<D>::kState + fo_);
+                dsf[mi] = ld4f(ws.dSf + ci * Rec<D>::kState + fo_);
+                sdot += dot4(sf[mi], dsf[mi]);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + c16;
+                const f32x4 Ao = (okr[tb] * fo[tb]) * ld4f(a.dout + rowaddr(t) + 16 * vb + 4 * g4);
+                const f32x4 Au = fu[tb] * ld4f(dUp + t * D + 16 * vb + 4 * g4);
+                const f32x4 Ad = fr[tb] * ld4f(Dl + t * D + 16 * vb + 4 * g4);
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi) {
+                    aQ[tb][mi] = blk(Ao, sf[mi], aQ[tb][mi]);
+                    aK1[tb][mi] = blk(Au, sf[mi], aK1[tb][mi]);
+                    aK2[tb][mi] = blk(Ad, dsf[mi], aK2[tb][mi]);
+                }
+            }
+        }
+    }
+    // boundary terms: q_t . dQ_S0, k_t . dK_S0, k_t . dK_dS (rows of the tiles)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        float so[4] = {0.f, 0.f, 0.f, 0.f}, sx[4] = {0.f, 0.f, 0.f, 0.f}, sr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tb + 4 * g4 + r;
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                const int d = 16 * (w * MT + mi) + c16;
+                const float qv = t < nt ? gdn_ld<DT>(p.q, rowaddr(t) + d) : 0.f;
+                const float kv = t < nt ? gdn_ld<DT>(p.k, rowaddr(t) + d) : 0.f;
+                so[r] += qv * aQ[tb][mi][r];
+                sx[r] += kv * aK1[tb][mi][r];
+                sr[r] += kv * aK2[tb][mi][r];
+            }
+            so[r] = row_sum<16>(so[r]);
+            sx[r] = row_sum<16>(sx[r]);
+            sr[r] = row_sum<16>(sr[r]);
+            if (c16 == 0) {
+                sh.vo[w][t] = so[r];
+                sh.vx[w][t] = sx[r];
+                sh.vr[w][t] = sr[r];
+            }
+        }
+    }
+    {
+        float s = sdot;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (l == 0) sh.sd[w] = s;
+    }
+    // dQ += (dP o M) K,  dK += (dP o M)^T Q + (W + W^T) K
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            const int db = w * MT + mi;
+            f32x4 q = aQ[tb][mi], kk = aK1[tb][mi] + aK2[tb][mi];
+            for (int jb = 0; jb <= tb; ++jb)
+                q = blk(ld4f(&sh.dPm[(16 * tb + c16) * LDA + 16 * jb + 4 * g4]),
+                        ld4f(KTf + ((size_t)(db * 4 + jb) * 64 + l) * 4), q);
+            // row tile tb of dK: (dP o M)^T over token tiles s >= tb, W over all
+            for (int sb = tb; sb < 4; ++sb) {
+                f32x4 at;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) at[qq] = sh.dPm[(16 * sb + 4 * g4 + qq) * LDA + 16 * tb + c16];
+                kk = blk(at, ld4f(QTf + ((size_t)(db * 4 + sb) * 64 + l) * 4), kk);
+            }
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+                kk = blk(ld4f(&sh.At[(16 * tb + c16) * LDA + 16 * ib + 4 * g4]),
+                         ld4f(KTf + ((size_t)(db * 4 + ib) * 64 + l) * 4), kk);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tb + 4 * g4 + r;
+                if (t < nt) {
+                    const int64_t o = (row0 + (int64_t)t * p.H) * D + 16 * db + c16;
+                    a.dq[o] = q[r];
+                    a.dk[o] = kk[r];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 4: boundary terms into V, then dlog alpha_s = sum_{b >= s}
+    // sum_{a' <= s} V[b][a'], dalpha = that / alpha, dbeta
+    if (w == 0) {
+        const int t = l;
+        const float vo = sh.vo[0][t] + sh.vo[1][t] + sh.vo[2][t] + sh.vo[3][t];
+        const int tx = p.order == GDN_DECAY_THEN_PREDICT ? t : t + 1;  // k_tx . dK_S0 lands in row t
+        const float vx = tx < C ? sh.vx[0][tx] + sh.vx[1][tx] + sh.vx[2][tx] + sh.vx[3][tx] : 0.f;
+        float c0 = vo + vx;
+        if (t == C - 1) {
+            const float sd = sh.sd[0] + sh.sd[1] + sh.sd[2] + sh.sd[3];
+            c0 += __expf(sh.ghi[C - 1] + sh.glo[C - 1]) * sd;
+        }
+        sh.Vm[t * LDA] += c0;
+        if (t < C - 1) sh.Vm[(C - 1) * LDA + 1 + t] += sh.vr[0][t] + sh.vr[1][t] + sh.vr[2][t] + sh.vr[3][t];
+    }
+    __syncthreads();
+    {
+        // inclusive prefix along each row over a' = 0 .. 63: four threads a
+        // row (consecutive lanes), 16 entries each, then the parts' offsets
+        const int bro = tid >> 2, part = tid & 3;
+        float* row = &sh.Vm[bro * LDA + 16 * part];
+        float s = 0.f;
+        float pre[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s += row[i];
+            pre[i] = s;
+        }
+        const float s1 = __shfl_up(s, 1, 64), s2 = __shfl_up(s, 2, 64), s3 = __shfl_up(s, 3, 64);
+        const float off = (part >= 1 ? s1 : 0.f) + (part >= 2 ? s2 : 0.f) + (part >= 3 ? s3 : 0.f);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) row[i] = pre[i] + off;
+    }
+    __syncthreads();
+    {
+        const int s = tid >> 2, part = tid & 3;
+        float acc = 0.f;
+        for (int bro = max(16 * part, s); bro < 16 * part + 16; ++bro) acc += sh.Vm[bro * LDA + s];
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        if (part == 0 && s < nt) {
+            const int64_t o = row0 + (int64_t)s * p.H;
+            a.dalpha[o] = acc / sh.galpha[s];
+            a.dbeta[o] = sh.db1[s] + sh.db2[0][s] + sh.db2[1][s] + sh.db2[2][s] + sh.db2[3][s];
+        }
+    }
+}
+
+template <int D, int DT>
+hipError_t launch_chunked(const BwdProblem& a, const CbWs& ws, hipStream_t st) {
+    const int64_t nch = a.nbh * a.p.NC;
+    prof_begin(a.p.timer, "k_bprep", st);
+    hipLaunchKernelGGL((k_bprep<D, DT>), dim3((unsigned)nch), dim3(kThreads), 0, st, a, ws);
+    prof_end(a.p.timer, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prof_begin(a.p.timer, "k_bchain", st);
+    hipLaunchKernelGGL((k_bchain<D, DT>), dim3((unsigned)(2 * a.nbh * (D / 16))), dim3(kThreads), 0, st, a, ws);
+    prof_end(a.p.timer, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    prof_begin(a.p.timer, "k_bgrad", st);
+    hipLaunchKernelGGL((k_bgrad<D, DT>), dim3((unsigned)nch), dim3(kThreads), 0, st, a, ws);
+    prof_end(a.p.timer, st);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunked_backward_supported(int64_t dk, int64_t dv, int gate) {
+    return gate == GDN_GATE_SCALAR && dk == dv && (dk == 64 || dk == 128);
+}
+
+// Workspace bytes per (batch, head) of the chunked backward; larger batches
+// run in groups of heads so that the workspace stays within the cap.
+static size_t chunked_bytes_per_head(int64_t T, int64_t D) {
+    const size_t nc = (size_t)((T + C - 1) / C);
+    const size_t nb = (size_t)(D / 16);
+    const size_t per_chunk = sizeof(float) * (3 * (size_t)C * C + 2 * nb * 4 * 64 * 4 + 2 * nb * nb * 64 * 4 +
+                                              4 * (size_t)C * D);
+    return nc * per_chunk;
+}
+constexpr size_t kChunkedWsCap = size_t(8) << 30;
+static int64_t chunked_heads_per_launch(int64_t B, int64_t T, int64_t H, int64_t D) {
+    const size_t per = chunked_bytes_per_head(T, D);
+    const int64_t g = per > 0 ? (int64_t)(kChunkedWsCap / per) : B * H;
+    return std::max<int64_t>(1, std::min<int64_t>(B * H, g));
+}
+
+size_t chunked_backward_workspace(int64_t B, int64_t T, int64_t H, int64_t D) {
+    // eleven pieces, each 256-byte aligned
+    return chunked_bytes_per_head(T, D) * (size_t)chunked_heads_per_launch(B, T, H, D) + 11 * 256;
+}
+
+hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t st) {
+    BwdProblem a0 = a_in;
+    a0.p.C = C;
+    a0.p.NC = (int)((a0.p.T + C - 1) / C);
+    const Problem& p = a0.p;
+    const int64_t D = p.dk, BH = p.B * p.H;
+    if (p.T == 0) {
+        // dS_0 = dS_T: the reverse chain with no chunks
+        BwdProblem g = a0;
+        g.bh0 = 0;
+        g.nbh = BH;
+        CbWs ws{};
+        hipLaunchKernelGGL((D == 64 ? k_bchain<64, GDN_BF16> : k_bchain<128, GDN_BF16>),
+                           dim3((unsigned)(BH * (D / 16))), dim3(kThreads), 0, st, g, ws);
+        return hipGetLastError();
+    }
+    const int64_t gsz = chunked_heads_per_launch(p.B, p.T, p.H, D);
+    const size_t nch = (size_t)gsz * (size_t)p.NC;
+    const size_t nb = (size_t)(D / 16);
+    char* base = static_cast<char*>(workspace);
+    size_t off = 0;
+    auto take = [&](size_t floats) {
+        float* q = reinterpret_cast<float*>(base + off);
+        off += align256(floats * sizeof(float));
+        return q;
+    };
+    CbWs ws;
+    ws.T = take(nch * C * C);
+    ws.TT = take(nch * C * C);
+    ws.PT = take(nch * C * C);
+    ws.KTf = take(nch * nb * 4 * 64 * 4);
+    ws.QTf = take(nch * nb * 4 * 64 * 4);
+    ws.Sf = take(nch * nb * nb * 64 * 4);
+    ws.dSf = take(nch * nb * nb * 64 * 4);
+    ws.U = take(nch * C * D);
+    ws.Dl = take(nch * C * D);
+    ws.dDl = take(nch * C * D);
+    ws.dUp = take(nch * C * D);
+    for (int64_t bh0 = 0; bh0 < BH; bh0 += gsz) {
+        BwdProblem g = a0;
+        g.bh0 = bh0;
+        g.nbh = std::min<int64_t>(gsz, BH - bh0);
+        hipError_t e;
+        if (D == 64) e = p.dtype == GDN_BF16 ? launch_chunked<64, GDN_BF16>(g, ws, st) : launch_chunked<64, GDN_F32>(g, ws, st);
+        else e = p.dtype == GDN_BF16 ? launch_chunked<128, GDN_BF16>(g, ws, st) : launch_chunked<128, GDN_F32>(g, ws, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace gdn

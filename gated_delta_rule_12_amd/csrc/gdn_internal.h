@@ -109,6 +109,11 @@ struct BwdProblem {
 size_t backward_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate);
 size_t backward_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate);
 hipError_t backward(const BwdProblem& a, hipStream_t st);
+// Chunked backward (gdn_bwd_chunk.hip): scalar gate, dk = dv in {64, 128};
+// its own workspace layout, given whole.
+bool chunked_backward_supported(int64_t dk, int64_t dv, int gate);
+size_t chunked_backward_workspace(int64_t B, int64_t T, int64_t H, int64_t D);
+hipError_t backward_chunked(const BwdProblem& a, void* workspace, hipStream_t st);
 
 // Raw projections on the vector-ALU family: the prologue's fp32 outputs in
 // the workspace (raw_inputs_bytes of it, at raw_inputs_at), then the forward

@@ -44,20 +44,11 @@
 #include <type_traits>
 
 #include "gdn_internal.h"
+#include "gdn_mfma_common.h"
 #include "../../include/gdn.h"
 
 namespace gdn {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int C = 64;
-constexpr int kThreads = 256;
 
 __device__ __forceinline__ f32x4 mfma(const u16x8& a, const u16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -97,17 +88,6 @@ __device__ __forceinline__ u16x8 cat(const u16x4& a, const u16x4& b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    return x;
-}
-
 // ---------------------------------------------------------------------------
 // stage 1: T' and the gate block per chunk-head
 // ---------------------------------------------------------------------------
@@ -127,70 +107,16 @@ constexpr int kTslots = 6;
 constexpr int kTfragPerChunk = kTslots * 2 * 64;  // [slot][hi/lo][lane] of u16x8
 __host__ __device__ constexpr int tslot(int m, int s) { return m < 2 ? m : 2 + 2 * (m - 2) + s; }
 
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// The UT inverse T = (I + A)^{-1} (fp32) and T' = T diag(beta) written as
-// A-operand fragments, for both stage-1 kernels.  AT (row stride C + 4)
-// holds A's strictly lower off-diagonal blocks transposed (block (i, k) at
-// rows of block k, columns of block i) and A's diagonal blocks in place; T
-// replaces the diagonal blocks and fills the lower triangle.  Called by all
-// threads of the workgroup (it contains barriers); Pw is 16 x 17 floats of
-// scratch for the calling wave.
-//   diagonal block w: (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
-//     (N^16 = 0), three rounds of P <- P P, X <- X + X P on fp32 MFMA;
-//     accumulators (lane: column c16, rows 4 g4 + i) serve as B operands as
-//     they stand (instruction s contracts the indices 4G + s, G = lane / 16);
-//   off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
+// The UT inverse T = (I + A)^{-1} (fp32, ut_inverse_lds: AT holds A's
+// strictly lower off-diagonal blocks transposed and its diagonal blocks in
+// place; T replaces the diagonal blocks and fills the lower triangle) and
+// T' = T diag(beta) written as A-operand fragments, for both stage-1 kernels.
+// Called by all threads of the workgroup (it contains barriers); Pw is
+// 16 x 17 floats of scratch for the calling wave.
 __device__ __forceinline__ void ut_inverse_store(float* AT, float* Pw, const float* bsh, u16x8* dst) {
     constexpr int LDA = C + 4;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
-    {
-        float* Xb = &AT[(16 * w) * LDA + 16 * w];
-        f32x4 pm, xm;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pm[r] = -Xb[(4 * g4 + r) * LDA + c16];
-            xm[r] = (4 * g4 + r == c16 ? 1.f : 0.f) + pm[r];
-        }
-#pragma unroll
-        for (int round = 0; round < 3; ++round) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Pw[(4 * g4 + r) * 17 + c16] = pm[r];
-            f32x4 np = zero4();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) np = mfma_f32(Pw[c16 * 17 + 4 * g4 + q], pm[q], np);
-            pm = np;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
-            f32x4 nx = xm;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) nx = mfma_f32(Xb[c16 * LDA + 4 * g4 + q], pm[q], nx);
-            xm = nx;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
-    }
-    __syncthreads();
-    for (int d = 1; d < 4; ++d) {
-        if (w < 4 - d) {
-            const int jb = w, ib = w + d;
-            f32x4 X = zero4();
-            for (int kb = jb; kb < ib; ++kb) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    X = mfma_f32(AT[(16 * kb + 4 * g4 + q) * LDA + 16 * ib + c16],   // A_ib,kb (transposed)
-                                 AT[(16 * kb + 4 * g4 + q) * LDA + 16 * jb + c16], X);  // T_kb,jb
-            }
-            f32x4 Tij = zero4();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) Tij = mfma_f32(AT[(16 * ib + c16) * LDA + 16 * ib + 4 * g4 + q], X[q], Tij);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) AT[(16 * ib + 4 * g4 + r) * LDA + 16 * jb + c16] = -Tij[r];
-        }
-        __syncthreads();
-    }
+    const int tid = threadIdx.x;
+    ut_inverse_lds(AT, Pw);
     // T' = T diag(beta): [slot(m, s)][hi/lo][lane] of 8 bf16; lane (row
     // 16m + lane % 16, group g), slot e -> column 32s + 4g + e (e < 4) or
     // 32s + 16 + 4g + e - 4; entries above the block diagonal are zero (the

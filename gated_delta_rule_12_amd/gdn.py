@@ -24,6 +24,7 @@ GDN_OK, GDN_E_ARG, GDN_E_SHAPE, GDN_E_UNSUPPORTED, GDN_E_WORKSPACE, GDN_E_HIP = 
 GDN_E_SCRATCH = -6
 GDN_NOALLOC_SCRATCH_BYTES = 128 << 20
 GDN_PATH_VALU, GDN_PATH_MFMA = 0, 1
+GDN_BWD_TOKEN, GDN_BWD_CHUNKED = 0, 1
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_step",
@@ -34,7 +35,7 @@ EXPORTS = ("gdn_chunk_fwd", "gdn_recurrent_ref", "gdn_seqpar_fwd", "gdn_decode_s
            "gdn_timer_create", "gdn_timer_destroy", "gdn_timer_read", "gdn_chunk_fwd_timed",
            "gdn_seqpar_fwd_timed", "gdn_decode_step_timed", "gdn_backward_timed",
            "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_raw", "gdn_chunk_fwd_raw_timed",
-           "gdn_raw_workspace_bytes")
+           "gdn_raw_workspace_bytes", "gdn_backward_path")
 
 _lib = None
 
@@ -84,6 +85,8 @@ def lib():
     L.gdn_validate.restype = ctypes.c_int
     L.gdn_chunk_path.argtypes = [i64, i64, i32, i32, i32]
     L.gdn_chunk_path.restype = ctypes.c_int
+    L.gdn_backward_path.argtypes = [i64, i64, i32]
+    L.gdn_backward_path.restype = ctypes.c_int
     L.gdn_chunk_segments.argtypes = shape + [i32, i32, i32]
     L.gdn_chunk_segments.restype = ctypes.c_int
     L.gdn_seqpar_segments.argtypes = shape + [i32, i32, i32, i32]
@@ -149,6 +152,10 @@ def gdn_validate(B, T, H, dk, dv, chunk, dtype, gate, order, n_segments=1) -> in
 
 def gdn_chunk_path(dk, dv, chunk, dtype, gate) -> int:
     return int(lib().gdn_chunk_path(dk, dv, chunk, dtype, gate))
+
+
+def gdn_backward_path(dk, dv, gate) -> int:
+    return int(lib().gdn_backward_path(dk, dv, gate))
 
 
 def gdn_chunk_segments(B, T, H, dk, dv, chunk, dtype, gate) -> int:

@@ -78,6 +78,8 @@ enum gdn_status {
     GDN_E_SCRATCH = -6       /* larger than gdn_chunk_fwd_noalloc's static scratch */
 };
 enum gdn_path { GDN_PATH_VALU = 0, GDN_PATH_MFMA = 1 };
+/* Backward algorithm (gdn_backward_path). */
+enum gdn_bwd_path { GDN_BWD_TOKEN = 0, GDN_BWD_CHUNKED = 1 };
 
 /*
  * gdn_chunk_fwd — chunkwise-parallel forward.
@@ -215,30 +217,38 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
  * grad_out = dL/d out and grad_state_out = dL/d S_T (NULL: zero), it writes
  * dL/dq, dL/dk, dL/dv, dL/dalpha, dL/dbeta and grad_state0 = dL/d S_0 (NULL:
  * not wanted).  The pages fix the forward recurrence only; the gradients are
- * its chain rule, token by token in reverse.  The forward states are
- * recomputed from boundary-state checkpoints every 16 tokens that the call
- * itself stores in the workspace; the sums over state rows go through the
- * workspace too (one record per block of rows and token), so the outputs are
- * written once, in a fixed order.
- *   q, k, v, alpha, beta, state0  as for gdn_chunk_fwd (state0 NULL: zero)
+ * its chain rule.  Two algorithms (gdn_backward_path says which runs):
+ *   chunked (scalar gate, dk = dv in {64, 128}): the chain rule through the
+ *     chunk form of the forward (DeltaNet illustrated notes, WY/UT section)
+ *     with chunks of 64 tokens on fp32 matrix cores: per-chunk UT inverses
+ *     and gated scores, a forward chain of chunk entry states and a reverse
+ *     chain of state gradients, then every chunk's gradients in parallel;
+ *   token (otherwise): the token recurrence run backwards, its states
+ *     recomputed from boundary-state checkpoints every 16 tokens.
+ * Both compute in fp32 and write every output once, in a fixed order
+ * (repeated calls give identical results).
+ *   q, k, v, alpha, beta, state0  as for gdn_chunk_fwd (state0 NULL: zero);
+ *                   alpha > 0 (the chunked path takes its logarithm)
  *   grad_out        [B, T, H, dv] fp32
  *   grad_state_out  [B, H, dv, dk] fp32 or NULL
  *   grad_q, grad_k  [B, T, H, dk] fp32;  grad_v [B, T, H, dv] fp32
  *   grad_alpha      shaped as alpha, fp32;  grad_beta [B, T, H] fp32
  *   grad_state0     [B, H, dv, dk] fp32 or NULL
  *   workspace       at least gdn_backward_workspace_bytes(B, T, H, dk, dv,
- *                   gate) bytes (per (batch, head): 4 dk dv ceil(T / 16) of
- *                   checkpoints and 4 T (2 dk + 4) per block of state rows of
- *                   sums, 3 dk + 4 for a channel gate; 3.2 GiB on a batch of
- *                   2 x 16 heads of 8192 tokens at d = 128), capped at about
- *                   8 GiB (larger batches run in groups of heads, one after
- *                   the other); may be NULL when T = 0
+ *                   gate) bytes; chunked: per (batch, head) and chunk of 64
+ *                   tokens 4 (3 * 64^2 + 6 * 64 dk + 2 dk^2) bytes
+ *                   (1.4 GiB on a batch of 2 x 16 heads of 8192 tokens at
+ *                   d = 128); token: per (batch, head) 4 dk dv ceil(T / 16)
+ *                   of checkpoints and 4 T (2 dk + 4) per block of state rows
+ *                   of sums, 3 dk + 4 for a channel gate; both capped at
+ *                   about 8 GiB (larger batches run in groups of heads, one
+ *                   after the other); may be NULL when T = 0
  * The gradient outputs must not alias any input or each other.
  * Alignment: q and k on 8 bytes (bf16) or 16 bytes (fp32); state0,
  * grad_state_out, grad_state0, grad_q, grad_k, a channel alpha and its
- * grad_alpha, and the workspace on 16 bytes; the rest on their element size;
- * otherwise GDN_E_ARG.  dk, dv as for gdn_chunk_fwd;
- * other statuses as above.
+ * grad_alpha, and the workspace on 16 bytes; grad_out on 16 bytes for the
+ * chunked path; the rest on their element size; otherwise GDN_E_ARG.  dk, dv
+ * as for gdn_chunk_fwd; other statuses as above.
  */
 int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                  int32_t dtype, int32_t gate, int32_t order, float scale,
@@ -253,6 +263,10 @@ int gdn_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
  * invalid or unsupported shape or gate). */
 size_t gdn_backward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                     int32_t gate);
+
+/* Which algorithm gdn_backward runs for these feature sizes and gate kind
+ * (GDN_BWD_TOKEN or GDN_BWD_CHUNKED), or a negative status.  Host only. */
+int gdn_backward_path(int64_t dk, int64_t dv, int32_t gate);
 
 /*
  * gdn_seqpar_fwd — increment-and-correct sequence parallelism (How to

@@ -252,15 +252,32 @@ def test_backward_rejects_bad_arguments_before_any_launch():
     odd4 = ctypes.c_void_p(0x1002)
     B, T, H, dk, dv = 1, 100, 2, 64, 64
     head = (B, T, H, dk, dv, gdn.GDN_BF16, gdn.GDN_GATE_SCALAR, gdn.GDN_PREDICT_THEN_DECAY, 1.0)
-    need = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, gdn.GDN_GATE_SCALAR)
-    # a checkpoint at every 16-token run start per (batch, head), and per block
-    # of 32 rows (16 lanes a row at dk = 64) a record of 2 dk + 4 floats per
-    # token
-    ckpt = 4 * dk * dv * 7 * B * H
-    part = 4 * B * H * (dv // 32) * T * (2 * dk + 4)
+    S, CH = gdn.GDN_GATE_SCALAR, gdn.GDN_GATE_CHANNEL
+    # which algorithm runs: chunked for a scalar gate at dk = dv in {64, 128}
+    assert gdn.gdn_backward_path(64, 64, S) == gdn.GDN_BWD_CHUNKED
+    assert gdn.gdn_backward_path(128, 128, S) == gdn.GDN_BWD_CHUNKED
+    assert gdn.gdn_backward_path(64, 128, S) == gdn.GDN_BWD_TOKEN
+    assert gdn.gdn_backward_path(32, 32, S) == gdn.GDN_BWD_TOKEN
+    assert gdn.gdn_backward_path(64, 64, CH) == gdn.GDN_BWD_TOKEN
+    assert gdn.gdn_backward_path(60, 64, S) < 0
+    assert gdn.gdn_backward_path(64, 64, 5) < 0
+    need = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, S)
+    # chunked: per (batch, head) and chunk of 64 tokens T, T^T, P^T (64 x 64),
+    # K^T and Q^T fragments (64 x dk each), the entry state and the state
+    # gradient (dk x dv each) and U, Delta, dDelta, dU' (64 x dv each), fp32;
+    # eleven pieces
+    nc = (T + 63) // 64
+    assert need == 4 * B * H * nc * (3 * 64 * 64 + 2 * 64 * dk + 2 * dk * dv + 4 * 64 * dv) + 11 * 256
+    # token: a checkpoint at every 16-token run start per (batch, head), and
+    # per block of 32 rows (16 lanes a row at dk = 64) a record of 2 dk + 4
+    # floats per token
     align = lambda x: (x + 255) // 256 * 256
-    assert need == align(ckpt) + align(part)
-    chan = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, gdn.GDN_GATE_CHANNEL)
+    dv2 = 128
+    ckpt = 4 * dk * dv2 * 7 * B * H
+    part = 4 * B * H * (dv2 // 32) * T * (2 * dk + 4)
+    assert gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv2, S) == align(ckpt) + align(part)
+    chan = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, CH)
+    ckpt = 4 * dk * dv * 7 * B * H
     assert chan == align(ckpt) + align(4 * B * H * (dv // 32) * T * (3 * dk + 4))
     assert gdn.gdn_backward_workspace_bytes(B, T, H, 60, dv, 0) == 0
     assert gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, 5) == 0
@@ -299,8 +316,13 @@ def test_backward_rejects_bad_arguments_before_any_launch():
     ptrs = list(ok)
     ptrs[11] = odd16  # a channel gate's gradient goes out in 16-byte pieces too
     assert call(ptrs, head=chan_head, nbytes=chan) == gdn.GDN_E_ARG
-    # a channel gate needs the larger workspace
-    assert call(ok, head=chan_head, nbytes=need) == gdn.GDN_E_WORKSPACE
+    # a channel gate needs its own workspace
+    assert call(ok, head=chan_head, nbytes=chan - 1) == gdn.GDN_E_WORKSPACE
+    # the chunked path reads dL/d out in 16-byte pieces, the token path per float
+    ptrs = list(ok)
+    ptrs[6] = odd16
+    assert call(ptrs) == gdn.GDN_E_ARG
+    assert call(ptrs, head=chan_head, nbytes=chan - 1) == gdn.GDN_E_WORKSPACE
     # enums and sizes
     assert call(ok, head=head[:5] + (7,) + head[6:]) == gdn.GDN_E_ARG
     assert call(ok, head=head[:7] + (5,) + head[8:]) == gdn.GDN_E_ARG
