@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "tokens/sec + % MFMA/HBM roofline, gated-delta chunk fwd H=16 d=128 T=8K"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, vendor figure
 
 
 def log(*a):
@@ -368,6 +369,27 @@ def backward_bytes(w) -> float:
     return float(per_tok * w.B * w.T * w.H + 12 * w.dk * w.dv * w.B * w.H)
 
 
+def backward_chunk_flops(w) -> dict:
+    """Algorithmic flops of the chunked backward per step, by kernel: per
+    (batch, head) and chunk of C = 64 tokens at d = dk = dv, the products of
+    the chunk-form chain rule with their triangular structure (a lower-
+    triangular C x C operand counts half):
+      k_bprep   K K^T, Q K^T (C^2 d / 2 each), the UT inverse (C^3 / 6)
+      k_bchain  forward: K S^T, S update (C d^2 each), T U' (C^2 d / 2);
+                reverse: K dS^T, Q^T dO, K^T dU' (C d^2 each), P^T dO,
+                T^T dDelta (C^2 d / 2 each)
+      k_bgrad   dO S, dU' S, Delta dS (C d^2 each); dO Delta^T, dDelta U^T,
+                (dP o M) K, (dP o M)^T Q (C^2 d / 2 each), (W + W^T) K (C^2 d),
+                T^T dT T^T (C^3 / 3)
+    as multiply-adds, two flops each."""
+    C, d = 64, w.dk
+    n = w.B * w.H * ((w.T + C - 1) // C)
+    mac = {"k_bprep": C * C * d + C ** 3 / 6,
+           "k_bchain": 5 * C * d * d + 1.5 * C * C * d,
+           "k_bgrad": 3 * C * d * d + 3 * C * C * d + C ** 3 / 3}
+    return {k: 2.0 * v * n for k, v in mac.items()}
+
+
 def cpu_baseline_backward(w, inp, gr, target_s=10.0):
     """Time the oracle's backward on (batch, head) slices of the workload,
     the first n_tok tokens of each, one slice per host core."""
@@ -434,12 +456,48 @@ def bench_backward(args, w):
     torch.cuda.synchronize()
     kern = timer.read()
     timer.close()
-    k_us = 1e3 * kern["k_backward"][0] / kern["k_backward"][1]
-    abytes = backward_bytes(w)
-    achieved = abytes / (k_us * 1e-6) / 1e9
-    log(f"step {ms * 1e3:.1f} us, k_backward {k_us:.1f} us per launch")
+    chunked = gdn.gdn_backward_path(w.dk, w.dv, gate) == gdn.GDN_BWD_CHUNKED
+    dom = max(kern, key=lambda n: kern[n][0])
+    k_us = 1e3 * kern[dom][0] / kern[dom][1]
+    log(f"step {ms * 1e3:.1f} us, " + ", ".join(f"{n} {1e3 * v[0] / args.steps:.1f} us" for n, v in kern.items())
+        + " per step")
     peaks = None if args.no_peaks else measure_peaks()
     cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, inp, gr)
+    abytes = backward_bytes(w)
+    kernel_us = {n: round(1e3 * v[0] / args.steps, 2) for n, v in kern.items()}
+    timing = "HIP events around each launch (caller-owned timer), in a second run of the same steps after the timed region"
+    if chunked:
+        fl = backward_chunk_flops(w)
+        step_tf = sum(fl.values()) / (ms * 1e-3) / 1e12
+        dom_tf = fl[dom] / kern[dom][1] * args.steps / (k_us * 1e-6) / 1e12 if dom in fl else None
+        roof = {"bound": "mfma", "achieved": round(step_tf, 2), "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(step_tf / MFMA_F32_PEAK_TFLOPS, 4),
+                "traffic": stored_step_traffic(w.name + "-backward", list(kern)),
+                "kernel": "whole step: " + " + ".join(kern), "algorithmic_flops": sum(fl.values()),
+                "algorithmic_flops_by_kernel": fl, "mfma_dtype": "fp32 (16x16x4)",
+                "hbm_bytes_moved_min": abytes,
+                "kernel_timing": timing, "kernel_us_per_step": kernel_us,
+                "dominant_kernel": {"kernel": dom, "launches_per_step": kern[dom][1] / args.steps,
+                                    "avg_launch_us": round(k_us, 2),
+                                    "achieved": round(dom_tf, 2) if dom_tf else None,
+                                    "frac": round(dom_tf / MFMA_F32_PEAK_TFLOPS, 4) if dom_tf else None,
+                                    "traffic": stored_step_traffic(w.name + "-backward", [dom])},
+                "achievable_peaks": peaks}
+    else:
+        achieved = abytes / (k_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": stored_step_traffic(w.name + "-backward", list(kern)),
+                "kernel": "whole step: " + " + ".join(kern), "algorithmic_bytes": abytes,
+                "kernel_timing": timing, "kernel_us_per_step": kernel_us,
+                "dominant_kernel": {"kernel": dom, "launches_per_step": kern[dom][1] / args.steps,
+                                    "avg_launch_us": round(k_us, 2), "achieved": round(achieved, 1),
+                                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                    "traffic": stored_step_traffic(w.name + "-backward", [dom])},
+                "frac_of_achievable_copy": round(abytes / (ms * 1e-3) / 1e9 / peaks["hbm_copy_GBs"], 4)
+                if peaks else None,
+                "achievable_peaks": peaks}
     res = {"metric": "backward tokens/sec (gradients through the gated-delta recurrence, H=16 d=128 T=8K)",
            "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/sec", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "settle_ms": settle_ms,
@@ -448,23 +506,9 @@ def bench_backward(args, w):
            "dtype": "f32", "data": "synthetic",
            "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                       "gate": w.gate, "input_dtype": w.dtype, "entry": "gdn_backward",
+                      "algorithm": "chunked" if chunked else "token",
                       "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"},
-           "roofline": {"bound": "hbm", "achieved": round(abytes / (ms * 1e-3) / 1e9, 1),
-                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "traffic": stored_step_traffic(w.name + "-backward", list(kern)),
-                        "kernel": "whole step: " + " + ".join(kern), "algorithmic_bytes": abytes,
-                        "kernel_timing": "HIP events around each launch (caller-owned timer), in a second run of the same steps after the timed region",
-                        "kernel_us_per_step": {n: round(1e3 * v[0] / args.steps, 2)
-                                               for n, v in kern.items()},
-                        "dominant_kernel": {"kernel": "k_backward",
-                                            "launches_per_step": kern["k_backward"][1] / args.steps,
-                                            "avg_launch_us": round(k_us, 2), "achieved": round(achieved, 1),
-                                            "frac": round(achieved / HBM_PEAK_GBS, 4),
-                                            "traffic": stored_step_traffic(w.name + "-backward", ["k_backward"])},
-                        "frac_of_achievable_copy": round(abytes / (ms * 1e-3) / 1e9 / peaks["hbm_copy_GBs"], 4)
-                        if peaks else None,
-                        "achievable_peaks": peaks},
+           "roofline": roof,
            "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 

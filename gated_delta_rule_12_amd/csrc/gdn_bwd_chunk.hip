@@ -67,16 +67,28 @@ __device__ __forceinline__ f32x4 blk(const f32x4& a, const f32x4& b, f32x4 acc) 
     return acc;
 }
 
-// four consecutive input elements (q, k: 8 bytes bf16 or 16 bytes fp32)
+// four consecutive input-typed elements (q, k and their fragments: 8 bytes
+// bf16 or 16 bytes fp32), kept as loaded until used
 template <int DT>
-__device__ __forceinline__ f32x4 ld4in(const void* base, int64_t i) {
+using R4 = std::conditional_t<DT == GDN_BF16, u32x2, f32x4>;
+template <int DT>
+using InE = std::conditional_t<DT == GDN_BF16, uint16_t, float>;
+template <int DT>
+__device__ __forceinline__ R4<DT> ldr(const void* base, int64_t i) {
+    return *reinterpret_cast<const R4<DT>*>(static_cast<const InE<DT>*>(base) + i);
+}
+template <int DT>
+__device__ __forceinline__ f32x4 cvt(const R4<DT>& u) {
     if constexpr (DT == GDN_BF16) {
-        const u32x2 u = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i);
         return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xFFFF0000u),
                      __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xFFFF0000u)};
     } else {
-        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
+        return u;
     }
+}
+template <int DT>
+__device__ __forceinline__ f32x4 ld4in(const void* base, int64_t i) {
+    return cvt<DT>(ldr<DT>(base, i));
 }
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ float dot4(const f32x4& x, const f32x4& y) {
@@ -99,14 +111,10 @@ __device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
 struct Gate {
     float hi, lo, phi, plo, beta, alpha;
 };
-__device__ __forceinline__ Gate chunk_gate(const Problem& p, int64_t row0, int nt, int lane) {
+__device__ __forceinline__ Gate gate_from(float alpha, float beta, int nt, int order, int lane) {
     Gate g;
-    g.alpha = 1.f;
-    g.beta = 0.f;
-    if (lane < nt) {
-        g.alpha = p.alpha[row0 + (int64_t)lane * p.H];
-        g.beta = p.beta[row0 + (int64_t)lane * p.H];
-    }
+    g.alpha = lane < nt ? alpha : 1.f;
+    g.beta = lane < nt ? beta : 0.f;
     float hi = lane < nt ? logf(g.alpha) : 0.f, lo = 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -120,7 +128,7 @@ __device__ __forceinline__ Gate chunk_gate(const Problem& p, int64_t row0, int n
     }
     g.hi = hi;
     g.lo = lo;
-    if (p.order == GDN_PREDICT_THEN_DECAY) {
+    if (order == GDN_PREDICT_THEN_DECAY) {
         g.phi = __shfl_up(hi, 1, 64);
         g.plo = __shfl_up(lo, 1, 64);
         if (lane == 0) g.phi = g.plo = 0.f;
@@ -129,6 +137,12 @@ __device__ __forceinline__ Gate chunk_gate(const Problem& p, int64_t row0, int n
         g.plo = lo;
     }
     return g;
+}
+// (token rows past the sequence end are read at the last real row and
+// replaced by the defaults)
+__device__ __forceinline__ Gate chunk_gate(const Problem& p, int64_t row0, int nt, int lane) {
+    const int64_t r = row0 + (int64_t)min(lane, nt - 1) * p.H;
+    return gate_from(p.alpha[r], p.beta[r], nt, p.order, lane);
 }
 
 // e^{(hb - ha) + (lb - la)}
@@ -150,7 +164,7 @@ struct Rec {
 
 struct CbWs {
     float *T, *TT, *PT;        // [chunk][C][C]
-    float *KTf, *QTf;          // [chunk][fragment set]
+    void *KTf, *QTf;           // [chunk][fragment set], input-typed
     float *Sf, *dSf;           // [chunk][state fragments]
     float *U, *Dl, *dDl, *dUp; // [chunk][C][D]
 };
@@ -257,24 +271,24 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
         st4f(Tg + r0 * C + c0, x);
         st4f(TTg + r0 * C + c0, y);
     }
-    // K^T and Q^T fragments
+    // K^T and Q^T fragments (input-typed)
     for (int f = tid; f < NB * 4 * 64; f += kThreads) {
         const int ln = f & 63, mt = f >> 6, m = mt >> 2, tb = mt & 3;
         const int gg = ln >> 4, cc = ln & 15;
-        f32x4 kx, qx;
+        E kx[4], qx[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int t = 16 * tb + 4 * gg + q, d = 16 * m + cc;
-            if constexpr (DT == GDN_BF16) {
-                kx[q] = gdn_bf16_to_f32(Ks[t * LDK + d]);
-                qx[q] = gdn_bf16_to_f32(Qs[t * LDK + d]);
-            } else {
-                kx[q] = Ks[t * LDK + d];
-                qx[q] = Qs[t * LDK + d];
-            }
+            kx[q] = Ks[t * LDK + d];
+            qx[q] = Qs[t * LDK + d];
         }
-        st4f(ws.KTf + ci * Rec<D>::kFrag + (size_t)f * 4, kx);
-        st4f(ws.QTf + ci * Rec<D>::kFrag + (size_t)f * 4, qx);
+        E* kd = static_cast<E*>(ws.KTf) + ci * Rec<D>::kFrag + (size_t)f * 4;
+        E* qd = static_cast<E*>(ws.QTf) + ci * Rec<D>::kFrag + (size_t)f * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            kd[q] = kx[q];
+            qd[q] = qx[q];
+        }
     }
 }
 
@@ -301,193 +315,306 @@ struct RowF {
     __device__ float beta(int t) const { return g[4 * C + t]; }
 };
 
+// Operands of a chain step, fetched ahead: the "early" ones of the next
+// chunk while the current one computes, the "late" ones (used after the
+// chunk's first or second barrier) at the start of the chunk itself.  Rows
+// past the sequence end are read at the last real row and zeroed at use.
 template <int D, int DT>
-__global__ __launch_bounds__(kThreads) void k_bchain(BwdProblem a, CbWs ws) {
+struct ChainIn {
+    static constexpr int MT = D / 64;
+    R4<DT> kx[4][MT];  // K[16 at + c16][16 m + 4 g4 ..], the K S^T operand
+    float al, be;      // lane t: alpha_t, beta_t
+};
+
+template <int D, int DT>
+struct ChainCtx {
+    static constexpr int NB = D / 16, MT = D / 64;
+    const BwdProblem& a;
+    const CbWs& ws;
+    int64_t bl, b, h, bh;
+    int rho, r0, w, l, g4, c16, NC;
+    __device__ int64_t row0(int c) const { return (b * a.p.T + (int64_t)c * C) * a.p.H + h; }
+    __device__ int ntok(int c) const { return (int)min<int64_t>(C, a.p.T - (int64_t)c * C); }
+    // early operands of chunk c (clamped to a real chunk)
+    __device__ void load_early(ChainIn<D, DT>& x, int c) const {
+        c = min(max(c, 0), NC - 1);
+        const int64_t r = row0(c);
+        const int nt = ntok(c);
+        const int64_t rl = r + (int64_t)min(l, nt - 1) * a.p.H;
+        x.al = a.p.alpha[rl];
+        x.be = a.p.beta[rl];
+#pragma unroll
+        for (int at = 0; at < 4; ++at)
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi)
+                x.kx[at][mi] = ldr<DT>(a.p.k, (r + (int64_t)min(16 * at + c16, nt - 1) * a.p.H) * D +
+                                                  16 * (w * MT + mi) + 4 * g4);
+    }
+    // partial K S^T over the wave's key tiles for every token tile, to LDS
+    __device__ void partial_KS(ChainShared& sh, const ChainIn<D, DT>& x, const f32x4 (&St)[MT], int nt) const {
+#pragma unroll
+        for (int at = 0; at < 4; ++at) {
+            f32x4 acc = zero4();
+            const float ok = 16 * at + c16 < nt ? 1.f : 0.f;
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) acc = blk(ok * cvt<DT>(x.kx[at][mi]), St[mi], acc);
+            sh.red[w][at][l] = acc;
+        }
+    }
+    // the state as the gradient kernel's fragments
+    __device__ void store_state(float* dst, const f32x4 (&St)[MT]) const {
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            const int m = w * MT + mi;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[((size_t)(rho * NB + m) * 64 + 16 * (c16 >> 2) + 4 * g4 + r) * 4 + (c16 & 3)] = St[mi][r];
+        }
+    }
+    __device__ void gates_to_lds(float* gw, const ChainIn<D, DT>& x, int nt) const {
+        const Gate g = gate_from(x.al, x.be, nt, a.p.order, l);
+        gw[0 * C + l] = g.hi;
+        gw[1 * C + l] = g.lo;
+        gw[2 * C + l] = g.phi;
+        gw[3 * C + l] = g.plo;
+        gw[4 * C + l] = g.beta;
+    }
+};
+
+template <int D, int DT>
+__device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 (&St)[D / 64]) {
+    constexpr int MT = D / 64;
+    const BwdProblem& a = cx.a;
+    const CbWs& ws = cx.ws;
+    const int w = cx.w, l = cx.l, g4 = cx.g4, c16 = cx.c16, r0 = cx.r0;
+    float* gw = &sh.g[w][0][0];
+    const RowF rf{gw};
+    ChainIn<D, DT> cur, nxt;
+    cx.load_early(cur, 0);
+    for (int c = 0; c < cx.NC; ++c) {
+        const int64_t ci = cx.bl * cx.NC + c;
+        const int nt = cx.ntok(c);
+        const int64_t r = cx.row0(c);
+        // late operands of this chunk: V rows, T rows, K^T fragments
+        float vv[4][4];
+        f32x4 tr[4];
+        R4<DT> kt[MT][4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                vv[jb][q] = gdn_ld<DT>(a.p.v, (r + (int64_t)min(16 * jb + 4 * g4 + q, nt - 1) * a.p.H) * D + r0 + c16);
+            tr[jb] = ld4f(ws.T + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                kt[mi][tb] = ldr<DT>(ws.KTf, ci * Rec<D>::kFrag + ((int64_t)((w * MT + mi) * 4 + tb) * 64 + l) * 4);
+        cx.load_early(nxt, c + 1);
+        cx.gates_to_lds(gw, cur, nt);
+        cx.store_state(ws.Sf + ci * Rec<D>::kState, St);
+        cx.partial_KS(sh, cur, St, nt);
+        __syncthreads();
+        // U' tiles jb <= w and the Delta tile w = sum_jb T[w][jb] U'[jb]
+        f32x4 dl = zero4();
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            if (jb > w) continue;
+            const f32x4 X = sh.red[0][jb][l] + sh.red[1][jb][l] + sh.red[2][jb][l] + sh.red[3][jb][l];
+            f32x4 U, Up;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = 16 * jb + 4 * g4 + q;
+                U[q] = (t < nt ? vv[jb][q] : 0.f) - rf.gamp(t) * X[q];
+                Up[q] = rf.beta(t) * U[q];
+            }
+            if (jb == w) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ws.U[ci * Rec<D>::kRows + (16 * w + 4 * g4 + q) * D + r0 + c16] = U[q];
+            }
+            dl = blk(tr[jb], Up, dl);
+        }
+        f32x4 rd;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = 16 * w + 4 * g4 + q;
+            ws.Dl[ci * Rec<D>::kRows + t * D + r0 + c16] = dl[q];
+            rd[q] = rf.R(t) * dl[q];
+        }
+        sh.xch[w][l] = rd;
+        __syncthreads();
+        // S^T <- gamma_C S^T + K^T diag(R) Delta
+        const float gC = rf.gC();
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            f32x4 acc = gC * St[mi];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc = blk(cvt<DT>(kt[mi][tb]), sh.xch[tb][l], acc);
+            St[mi] = acc;
+        }
+        cur = nxt;
+    }
+}
+
+template <int D, int DT>
+__device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 (&St)[D / 64]) {
+    constexpr int MT = D / 64;
+    const BwdProblem& a = cx.a;
+    const Problem& p = a.p;
+    const CbWs& ws = cx.ws;
+    const int w = cx.w, l = cx.l, g4 = cx.g4, c16 = cx.c16, r0 = cx.r0;
+    float* gw = &sh.g[w][0][0];
+    const RowF rf{gw};
+    // early operands beyond the K rows: dO of the slice, P^T rows, Q^T fragments
+    struct RevIn {
+        float dob[4][4];
+        f32x4 pr[4];
+        R4<DT> qt[MT][4];
+    };
+    auto load_rev = [&](RevIn& x, int c) {
+        c = min(max(c, 0), cx.NC - 1);
+        const int64_t ci = cx.bl * cx.NC + c;
+        const int64_t r = cx.row0(c);
+        const int nt = cx.ntok(c);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                x.dob[tb][q] = a.dout[(r + (int64_t)min(16 * tb + 4 * g4 + q, nt - 1) * p.H) * D + r0 + c16];
+            x.pr[tb] = ld4f(ws.PT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * tb + 4 * g4);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                x.qt[mi][tb] = ldr<DT>(ws.QTf, ci * Rec<D>::kFrag + ((int64_t)((w * MT + mi) * 4 + tb) * 64 + l) * 4);
+    };
+    ChainIn<D, DT> cur, nxt;
+    RevIn rcur, rnxt;
+    cx.load_early(cur, cx.NC - 1);
+    load_rev(rcur, cx.NC - 1);
+    for (int c = cx.NC - 1; c >= 0; --c) {
+        const int64_t ci = cx.bl * cx.NC + c;
+        const int nt = cx.ntok(c);
+        const int64_t r = cx.row0(c);
+        // late operands of this chunk: T^T rows, K^T fragments
+        f32x4 tt[4];
+        R4<DT> kt[MT][4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) tt[jb] = ld4f(ws.TT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                kt[mi][tb] = ldr<DT>(ws.KTf, ci * Rec<D>::kFrag + ((int64_t)((w * MT + mi) * 4 + tb) * 64 + l) * 4);
+        cx.load_early(nxt, c - 1);
+        load_rev(rnxt, c - 1);
+        cx.gates_to_lds(gw, cur, nt);
+        cx.store_state(ws.dSf + ci * Rec<D>::kState, St);
+        cx.partial_KS(sh, cur, St, nt);
+        // state-independent pieces: E_w = scale P^T[w][.] dO and
+        // scale Q^T diag(gamma) dO over the wave's key tiles
+        f32x4 dob[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dob[tb][q] = 16 * tb + 4 * g4 + q < nt ? rcur.dob[tb][q] : 0.f;
+        f32x4 E = zero4();
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+            if (tb >= w) E = blk(rcur.pr[tb], dob[tb], E);
+        E = p.scale * E;
+        f32x4 QD[MT];
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) QD[mi] = zero4();
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 sg;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sg[q] = p.scale * rf.gam(16 * tb + 4 * g4 + q) * dob[tb][q];
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) QD[mi] = blk(cvt<DT>(rcur.qt[mi][tb]), sg, QD[mi]);
+        }
+        __syncthreads();
+        // dDelta tile w = diag(R) K dS^T + E_w
+        {
+            const f32x4 Y = sh.red[0][w][l] + sh.red[1][w][l] + sh.red[2][w][l] + sh.red[3][w][l];
+            f32x4 dd;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = 16 * w + 4 * g4 + q;
+                dd[q] = rf.R(t) * Y[q] + E[q];
+                ws.dDl[ci * Rec<D>::kRows + t * D + r0 + c16] = dd[q];
+            }
+            sh.xch[w][l] = dd;
+        }
+        __syncthreads();
+        // dU' tile w = sum_{jb >= w} T^T[w][jb] dDelta[jb]; dv = beta dU'
+        f32x4 du = zero4();
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            if (jb >= w) du = blk(tt[jb], sh.xch[jb][l], du);
+        f32x4 bk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = 16 * w + 4 * g4 + q;
+            ws.dUp[ci * Rec<D>::kRows + t * D + r0 + c16] = du[q];
+            if (t < nt) a.dv[(r + (int64_t)t * p.H) * D + r0 + c16] = rf.beta(t) * du[q];
+            bk[q] = -rf.gamp(t) * rf.beta(t) * du[q];
+        }
+        sh.xch2[w][l] = bk;
+        __syncthreads();
+        // dS^T <- gamma_C dS^T + scale Q^T diag(gamma) dO - K^T diag(gamma' beta) dU'
+        const float gC = rf.gC();
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            f32x4 acc = gC * St[mi] + QD[mi];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc = blk(cvt<DT>(kt[mi][tb]), sh.xch2[tb][l], acc);
+            St[mi] = acc;
+        }
+        cur = nxt;
+        rcur = rnxt;
+    }
+}
+
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads, 2) void k_bchain(BwdProblem a, CbWs ws) {
     constexpr int NB = D / 16, MT = D / 64;
     __shared__ ChainShared sh;
     const Problem& p = a.p;
-    const int NS = NB;  // 16-row slices per head
-    const int64_t nsl = a.nbh * NS;
+    const int64_t nsl = a.nbh * NB;  // (head, 16-row slice) pairs per direction
     const bool rev = blockIdx.x < nsl;
     const int64_t idx = rev ? blockIdx.x : blockIdx.x - nsl;
-    const int64_t bl = idx / NS;
-    const int rho = (int)(idx - bl * NS), r0 = 16 * rho;
-    const int64_t bh = a.bh0 + bl, b = bh / p.H, h = bh - b * p.H;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
-    const int NC = p.NC;
-    float* gw = &sh.g[w][0][0];
-    const RowF rf{gw};
-
+    ChainCtx<D, DT> cx{a, ws};
+    cx.bl = idx / NB;
+    cx.rho = (int)(idx - cx.bl * NB);
+    cx.r0 = 16 * cx.rho;
+    cx.bh = a.bh0 + cx.bl;
+    cx.b = cx.bh / p.H;
+    cx.h = cx.bh - cx.b * p.H;
+    const int tid = threadIdx.x;
+    cx.w = tid >> 6;
+    cx.l = tid & 63;
+    cx.g4 = cx.l >> 4;
+    cx.c16 = cx.l & 15;
+    cx.NC = p.NC;
     // the slice's state rows as accumulator tiles of S^T: tile mi holds
     // S[r0 + c16][16 (w MT + mi) + 4 g4 + r]
     f32x4 St[MT];
     const float* init = rev ? a.ds_out : p.s0;
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-        const int m = w * MT + mi;
-        St[mi] = init ? ld4f(init + ((bh * D + r0 + c16) * D) + 16 * m + 4 * g4) : zero4();
-    }
-
-    for (int step = 0; step < NC; ++step) {
-        const int c = rev ? NC - 1 - step : step;
-        const int64_t ci = bl * NC + c;
-        const int64_t t0 = (int64_t)c * C;
-        const int nt = (int)min<int64_t>(C, p.T - t0);
-        const int64_t row0 = (b * p.T + t0) * p.H + h;  // (batch, token t0, head)
-        {
-            const Gate g = chunk_gate(p, row0, nt, l);
-            gw[0 * C + l] = g.hi;
-            gw[1 * C + l] = g.lo;
-            gw[2 * C + l] = g.phi;
-            gw[3 * C + l] = g.plo;
-            gw[4 * C + l] = g.beta;
-        }
-        // the state this chunk starts from (forward) or ends with (reverse),
-        // as the gradient kernel's state fragments
-        {
-            float* dst = (rev ? ws.dSf : ws.Sf) + ci * Rec<D>::kState;
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                const int m = w * MT + mi;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[((size_t)(rho * NB + m) * 64 + 16 * (c16 >> 2) + 4 * g4 + r) * 4 + (c16 & 3)] = St[mi][r];
-            }
-        }
-        // partial K S^T over the wave's key tiles, every token tile
-#pragma unroll
-        for (int at = 0; at < 4; ++at) {
-            const int t = 16 * at + c16;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                const int m = w * MT + mi;
-                f32x4 kx = ld4in<DT>(p.k, (row0 + (int64_t)min(t, nt - 1) * p.H) * D + 16 * m + 4 * g4);
-                if (t >= nt) kx = zero4();
-                acc = blk(kx, St[mi], acc);
-            }
-            sh.red[w][at][l] = acc;
-        }
-        if (!rev) {
-            __syncthreads();
-            // U' tiles jb <= w and the Delta tile w: Delta_w = sum_jb T[w][jb] U'[jb]
-            f32x4 dl = zero4();
-            for (int jb = 0; jb <= w; ++jb) {
-                const f32x4 X = sh.red[0][jb][l] + sh.red[1][jb][l] + sh.red[2][jb][l] + sh.red[3][jb][l];
-                f32x4 U, Up;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * jb + 4 * g4 + r;
-                    const float vv = t < nt ? gdn_ld<DT>(p.v, (row0 + (int64_t)t * p.H) * D + r0 + c16) : 0.f;
-                    U[r] = vv - rf.gamp(t) * X[r];
-                    Up[r] = rf.beta(t) * U[r];
-                }
-                if (jb == w) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        ws.U[ci * Rec<D>::kRows + (16 * w + 4 * g4 + r) * D + r0 + c16] = U[r];
-                }
-                dl = blk(ld4f(ws.T + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4), Up, dl);
-            }
-            f32x4 rd;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * g4 + r;
-                ws.Dl[ci * Rec<D>::kRows + t * D + r0 + c16] = dl[r];
-                rd[r] = rf.R(t) * dl[r];
-            }
-            sh.xch[w][l] = rd;
-            __syncthreads();
-            // S^T <- gamma_C S^T + K^T diag(R) Delta
-            const float gC = rf.gC();
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                const int m = w * MT + mi;
-                f32x4 acc = gC * St[mi];
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    acc = blk(ld4f(ws.KTf + ci * Rec<D>::kFrag + ((size_t)(m * 4 + tb) * 64 + l) * 4), sh.xch[tb][l], acc);
-                St[mi] = acc;
-            }
-        } else {
-            // state-independent pieces: E_w = scale P^T[w][.] dO and
-            // scale Q^T diag(gamma) dO over the wave's key tiles
-            f32x4 dob[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int t = 16 * tb + 4 * g4 + q;
-                    dob[tb][q] = t < nt ? a.dout[(row0 + (int64_t)t * p.H) * D + r0 + c16] : 0.f;
-                }
-            }
-            f32x4 E = zero4();
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                if (tb >= w)
-                    E = blk(ld4f(ws.PT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * tb + 4 * g4), dob[tb], E);
-            E = p.scale * E;
-            f32x4 QD[MT];
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) QD[mi] = zero4();
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                f32x4 sg;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) sg[q] = p.scale * rf.gam(16 * tb + 4 * g4 + q) * dob[tb][q];
-#pragma unroll
-                for (int mi = 0; mi < MT; ++mi) {
-                    const int m = w * MT + mi;
-                    QD[mi] = blk(ld4f(ws.QTf + ci * Rec<D>::kFrag + ((size_t)(m * 4 + tb) * 64 + l) * 4), sg, QD[mi]);
-                }
-            }
-            __syncthreads();
-            // dDelta tile w = diag(R) K dS^T + E_w
-            {
-                const f32x4 Y = sh.red[0][w][l] + sh.red[1][w][l] + sh.red[2][w][l] + sh.red[3][w][l];
-                f32x4 dd;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * w + 4 * g4 + r;
-                    dd[r] = rf.R(t) * Y[r] + E[r];
-                    ws.dDl[ci * Rec<D>::kRows + t * D + r0 + c16] = dd[r];
-                }
-                sh.xch[w][l] = dd;
-            }
-            __syncthreads();
-            // dU' tile w = sum_{jb >= w} T^T[w][jb] dDelta[jb]; dv = beta dU'
-            f32x4 du = zero4();
-            for (int jb = w; jb < 4; ++jb)
-                du = blk(ld4f(ws.TT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4), sh.xch[jb][l], du);
-            f32x4 bk;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * g4 + r;
-                ws.dUp[ci * Rec<D>::kRows + t * D + r0 + c16] = du[r];
-                if (t < nt) a.dv[(row0 + (int64_t)t * p.H) * D + r0 + c16] = rf.beta(t) * du[r];
-                bk[r] = -rf.gamp(t) * rf.beta(t) * du[r];
-            }
-            sh.xch2[w][l] = bk;
-            __syncthreads();
-            // dS^T <- gamma_C dS^T + scale Q^T diag(gamma) dO - K^T diag(gamma' beta) dU'
-            const float gC = rf.gC();
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                const int m = w * MT + mi;
-                f32x4 acc = gC * St[mi] + QD[mi];
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    acc = blk(ld4f(ws.KTf + ci * Rec<D>::kFrag + ((size_t)(m * 4 + tb) * 64 + l) * 4), sh.xch2[tb][l], acc);
-                St[mi] = acc;
-            }
-        }
+    for (int mi = 0; mi < MT; ++mi)
+        St[mi] = init ? ld4f(init + ((cx.bh * D + cx.r0 + cx.c16) * D) + 16 * (cx.w * MT + mi) + 4 * cx.g4) : zero4();
+    if (p.NC > 0) {
+        if (rev) chain_reverse<D, DT>(cx, sh, St);
+        else chain_forward<D, DT>(cx, sh, St);
     }
     if (rev && a.ds0) {
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-            const int m = w * MT + mi;
-            st4f(a.ds0 + ((bh * D + r0 + c16) * D) + 16 * m + 4 * g4, St[mi]);
-        }
+        for (int mi = 0; mi < MT; ++mi)
+            st4f(a.ds0 + ((cx.bh * D + cx.r0 + cx.c16) * D) + 16 * (cx.w * MT + mi) + 4 * cx.g4, St[mi]);
     }
 }
 
@@ -507,7 +634,7 @@ struct GradShared {
 };
 
 template <int D, int DT>
-__global__ __launch_bounds__(kThreads) void k_bgrad(BwdProblem a, CbWs ws) {
+__global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
     constexpr int NB = D / 16, MT = D / 64;
     __shared__ __attribute__((aligned(16))) GradShared sh;
     const Problem& p = a.p;
@@ -525,8 +652,8 @@ __global__ __launch_bounds__(kThreads) void k_bgrad(BwdProblem a, CbWs ws) {
     const float* dUp = ws.dUp + ci * Rec<D>::kRows;
     const float* Tg = ws.T + ci * Rec<D>::kTile;
     const float* TTg = ws.TT + ci * Rec<D>::kTile;
-    const float* KTf = ws.KTf + ci * Rec<D>::kFrag;
-    const float* QTf = ws.QTf + ci * Rec<D>::kFrag;
+    const InE<DT>* KTf = static_cast<const InE<DT>*>(ws.KTf) + ci * Rec<D>::kFrag;
+    const InE<DT>* QTf = static_cast<const InE<DT>*>(ws.QTf) + ci * Rec<D>::kFrag;
     auto rowaddr = [&](int t) { return (row0 + (int64_t)min(t, nt - 1) * p.H) * D; };
 
     // ---- phase 0: gates, dU'.U, cleared sums
@@ -726,18 +853,18 @@ __global__ __launch_bounds__(kThreads) void k_bgrad(BwdProblem a, CbWs ws) {
             f32x4 q = aQ[tb][mi], kk = aK1[tb][mi] + aK2[tb][mi];
             for (int jb = 0; jb <= tb; ++jb)
                 q = blk(ld4f(&sh.dPm[(16 * tb + c16) * LDA + 16 * jb + 4 * g4]),
-                        ld4f(KTf + ((size_t)(db * 4 + jb) * 64 + l) * 4), q);
+                        ld4in<DT>(KTf, ((int64_t)(db * 4 + jb) * 64 + l) * 4), q);
             // row tile tb of dK: (dP o M)^T over token tiles s >= tb, W over all
             for (int sb = tb; sb < 4; ++sb) {
                 f32x4 at;
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) at[qq] = sh.dPm[(16 * sb + 4 * g4 + qq) * LDA + 16 * tb + c16];
-                kk = blk(at, ld4f(QTf + ((size_t)(db * 4 + sb) * 64 + l) * 4), kk);
+                kk = blk(at, ld4in<DT>(QTf, ((int64_t)(db * 4 + sb) * 64 + l) * 4), kk);
             }
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib)
                 kk = blk(ld4f(&sh.At[(16 * tb + c16) * LDA + 16 * ib + 4 * g4]),
-                         ld4f(KTf + ((size_t)(db * 4 + ib) * 64 + l) * 4), kk);
+                         ld4in<DT>(KTf, ((int64_t)(db * 4 + ib) * 64 + l) * 4), kk);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tb + 4 * g4 + r;
@@ -874,7 +1001,7 @@ hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t
     ws.T = take(nch * C * C);
     ws.TT = take(nch * C * C);
     ws.PT = take(nch * C * C);
-    ws.KTf = take(nch * nb * 4 * 64 * 4);
+    ws.KTf = take(nch * nb * 4 * 64 * 4);  // (sized for fp32 inputs)
     ws.QTf = take(nch * nb * 4 * 64 * 4);
     ws.Sf = take(nch * nb * nb * 64 * 4);
     ws.dSf = take(nch * nb * nb * 64 * 4);

@@ -86,6 +86,19 @@ CASES = [
 ]
 
 
+# scalar gate at dk = dv in {64, 128}: the chunked algorithm (64-token chunks)
+CHUNKED_CASES = [
+    ("bf16", "scalar", DTP, 128, 128, 1, 2, 200, 0.3, 2.0),   # 3 chunks + 8 tokens
+    ("bf16", "scalar", PTD, 64, 64, 2, 2, 130, 0.3, 2.0),     # 2 chunks + 2 tokens
+    ("bf16", "scalar", DTP, 64, 64, 1, 2, 64, 0.3, -3.0),     # exactly one chunk, small gates
+    ("bf16", "scalar", PTD, 128, 128, 2, 1, 65, 0.3, -1.0),   # one chunk + one token
+    ("bf16", "scalar", PTD, 128, 128, 1, 2, 63, 0.0, 6.0),    # shorter than a chunk, no start state
+    ("f32", "scalar", PTD, 128, 128, 1, 2, 100, 0.3, 2.0),    # fp32 inputs
+    ("f32", "scalar", DTP, 64, 64, 1, 3, 1, 0.5, 2.0),        # a single token
+    ("bf16", "scalar", DTP, 128, 128, 1, 2, 1000, 0.02, 2.0), # 16 chunks, ragged
+]
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_backward_matches_oracle(case):
     dtype, gate, order, dk, dv, B, H, T, std, am = case
@@ -93,6 +106,54 @@ def test_backward_matches_oracle(case):
                  state0_std=std, alpha_mean=am, seed=5100 + dk + dv + T)
     got, ref = run(w, order, scale=0.8)
     check(got, ref)
+
+
+@pytest.mark.parametrize("case", CHUNKED_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_chunked_backward_matches_oracle(case):
+    dtype, gate, order, dk, dv, B, H, T, std, am = case
+    assert gdn.gdn_backward_path(dk, dv, gdn.GDN_GATE_SCALAR) == gdn.GDN_BWD_CHUNKED
+    w = Workload("bwd-chunked", B=B, H=H, T=T, dk=dk, dv=dv, chunk=64, dtype=dtype, gate=gate,
+                 state0_std=std, alpha_mean=am, seed=5600 + dk + T)
+    got, ref = run(w, order, scale=0.7)
+    check(got, ref)
+
+
+def test_chunked_backward_main_workload_sampled():
+    """The training shape the benchmark times (2 x 16 heads of 8192 tokens at
+    d = 128, bf16, scalar gate): the whole batch through gdn_backward, two
+    (batch, head) slices against the oracle over all 8192 tokens."""
+    import torch
+    from gated_delta_rule_12_amd.workloads import WORKLOADS, make_grads
+    w = WORKLOADS[2]
+    inp = make_inputs(w)
+    gr = make_grads(w)
+    d = to_device(inp, w)
+    print(f"case {w.name} B={w.B} H={w.H} T={w.T}", flush=True)
+    res = gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
+                       torch.from_numpy(gr["dout"]).cuda(), torch.from_numpy(gr["dstate"]).cuda())
+    torch.cuda.synchronize()
+    for b, h in ((0, 3), (1, 15)):
+        sl = lambda x: x[b:b + 1, :, h:h + 1]
+        ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]), sl(inp["beta"]),
+                              inp["state0"][b:b + 1, h:h + 1], sl(gr["dout"]), gr["dstate"][b:b + 1, h:h + 1])
+        got = [sl(x).cpu().numpy() for x in res[:5]] + [res[5][b:b + 1, h:h + 1].cpu().numpy()]
+        check(got, ref)
+
+
+def test_chunked_backward_is_deterministic():
+    """Every output of the chunked path is written once, in a fixed order."""
+    import torch
+    w = Workload("bwd-det-chunked", B=1, H=3, T=300, dk=128, dv=128, chunk=64, state0_std=0.3, seed=5502)
+    inp = make_inputs(w)
+    gr = make_grads(w)
+    d = to_device(inp, w)
+    g_out = torch.from_numpy(gr["dout"]).cuda()
+    g_st = torch.from_numpy(gr["dstate"]).cuda()
+    r1 = gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], g_out, g_st, order=DTP)
+    r2 = gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], g_out, g_st, order=DTP)
+    torch.cuda.synchronize()
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
 
 
 def test_backward_without_optional_tensors():
