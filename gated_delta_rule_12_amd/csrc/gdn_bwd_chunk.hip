@@ -156,14 +156,14 @@ __device__ __forceinline__ float ratio(float hb, float lb, float ha, float la) {
 template <int D>
 struct Rec {
     static constexpr int NB = D / 16;
-    static constexpr size_t kTile = (size_t)C * C;          // T, T^T, P^T (floats)
+    static constexpr size_t kTile = (size_t)C * C;          // T, T^T, P^T, Atilde^T (floats)
     static constexpr size_t kFrag = (size_t)NB * 4 * 64 * 4;  // K^T, Q^T fragments
     static constexpr size_t kState = (size_t)NB * NB * 64 * 4;
     static constexpr size_t kRows = (size_t)C * D;          // U, Delta, dDelta, dU'
 };
 
 struct CbWs {
-    float *T, *TT, *PT;        // [chunk][C][C]
+    float *T, *TT, *PT, *AtT;  // [chunk][C][C]
     void *KTf, *QTf;           // [chunk][fragment set], input-typed
     float *Sf, *dSf;           // [chunk][state fragments]
     float *U, *Dl, *dDl, *dUp; // [chunk][C][D]
@@ -230,13 +230,16 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
             acc = blk(row4(X, 16 * m + c16, 16 * kb + 4 * g4), row4(Ks, 16 * nb + c16, 16 * kb + 4 * g4), acc);
         const int j = 16 * nb + c16;
         if (kind == 0) {
-            // A_tj = beta_t e^{l'_t - l_j} k_t.k_j (j < t), in the inverse's layout
-            f32x4 av;
+            // Atilde_tj = e^{l'_t - l_j} k_t.k_j (j < t), stored as Atilde^T[j][t];
+            // A = diag(beta) Atilde in the inverse's layout
+            f32x4 av, tv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * m + 4 * g4 + r;
-                av[r] = j < t ? gbeta[t] * ratio(gphi[t], gplo[t], ghi[j], glo[j]) * acc[r] : 0.f;
+                tv[r] = j < t ? ratio(gphi[t], gplo[t], ghi[j], glo[j]) * acc[r] : 0.f;
+                av[r] = gbeta[t] * tv[r];
             }
+            st4f(ws.AtT + ci * Rec<D>::kTile + j * C + 16 * m + 4 * g4, tv);
             if (nb < m) {
                 st4f(&AT[j * LDA + 16 * m + 4 * g4], av);
             } else {
@@ -622,8 +625,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bchain(BwdProblem a, CbWs ws) {
 // k_bgrad: dq, dk, dbeta and dalpha of one chunk
 // ---------------------------------------------------------------------------
 struct GradShared {
-    float dPm[C * LDA];   // dP o M (lower triangle, zero above)
-    float At[C * LDA];    // Atilde (strictly lower); then W + W^T (full)
+    float dPm[C * LDA];   // dP o M (lower triangle with the diagonal, zero above)
+    float W[C * LDA];     // W + W^T
     float dT[C * LDA];    // dT (lower triangle)
     float Vm[C * LDA];    // gate terms V[b][a + 1]; then their prefix along a
     float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C], galpha[C];
@@ -633,6 +636,10 @@ struct GradShared {
     float sd[4];          // per wave: <dS_end, S>
 };
 
+// Global operands are fetched ahead of their use throughout: a job's or a
+// block's whole set at once, the next phase's before the barrier that ends
+// the current one, the state products' next value block while the current
+// one multiplies.
 template <int D, int DT>
 __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
     constexpr int NB = D / 16, MT = D / 64;
@@ -652,6 +659,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
     const float* dUp = ws.dUp + ci * Rec<D>::kRows;
     const float* Tg = ws.T + ci * Rec<D>::kTile;
     const float* TTg = ws.TT + ci * Rec<D>::kTile;
+    const float* PTg = ws.PT + ci * Rec<D>::kTile;
+    const float* AtTg = ws.AtT + ci * Rec<D>::kTile;
+    const float* Sf = ws.Sf + ci * Rec<D>::kState;
+    const float* dSf = ws.dSf + ci * Rec<D>::kState;
     const InE<DT>* KTf = static_cast<const InE<DT>*>(ws.KTf) + ci * Rec<D>::kFrag;
     const InE<DT>* QTf = static_cast<const InE<DT>*>(ws.QTf) + ci * Rec<D>::kFrag;
     auto rowaddr = [&](int t) { return (row0 + (int64_t)min(t, nt - 1) * p.H) * D; };
@@ -668,9 +679,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
     }
     {
         const int t = tid >> 2, part = tid & 3;
+        f32x4 x[NB / 2], y[NB / 2];
+#pragma unroll
+        for (int i = 0; i < NB / 2; ++i) {
+            x[i] = ld4f(dUp + t * D + 4 * part + 16 * i);
+            y[i] = ld4f(U + t * D + 4 * part + 16 * i);
+        }
         float s = 0.f;
-#pragma unroll 4
-        for (int d = 4 * part; d < D; d += 16) s += dot4(ld4f(dUp + t * D + d), ld4f(U + t * D + d));
+#pragma unroll
+        for (int i = 0; i < NB / 2; ++i) s += dot4(x[i], y[i]);
+#pragma unroll
+        for (int i = 0; i < NB / 2; ++i) {
+            x[i] = ld4f(dUp + t * D + 4 * part + 16 * (i + NB / 2));
+            y[i] = ld4f(U + t * D + 4 * part + 16 * (i + NB / 2));
+        }
+#pragma unroll
+        for (int i = 0; i < NB / 2; ++i) s += dot4(x[i], y[i]);
         s += __shfl_xor(s, 1, 64);
         s += __shfl_xor(s, 2, 64);
         if (part == 0) sh.db1[t] = s;
@@ -681,64 +705,59 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
     auto ex = [&](int tb_, int ja) { return ratio(sh.ghi[tb_], sh.glo[tb_], sh.ghi[ja], sh.glo[ja]); };
     auto exp_ = [&](int tb_, int ja) { return ratio(sh.gphi[tb_], sh.gplo[tb_], sh.ghi[ja], sh.glo[ja]); };
 
-    // ---- phase 1: C x C products on the lower blocks
+    // ---- phase 1: dP = scale dO Delta^T and dT = dDelta U^T diag(beta) on
+    // the lower blocks (10 each), all operands of a job fetched at once
     for (int job = w; job < 20; job += 4) {
         const int kind = job / 10, tb = blk_m(job % 10), jb = blk_n(job % 10);
         const int ta = 16 * tb + c16, ja = 16 * jb + c16;  // A-operand row, B-operand row
-        f32x4 x1 = zero4(), x2 = zero4();
-        if (kind == 0) {
-            // dP = scale dO Delta^T and Q K^T
-            const float ok = ta < nt ? 1.f : 0.f;
-#pragma unroll 4
-            for (int vb = 0; vb < NB; ++vb)
-                x1 = blk(ok * ld4f(a.dout + rowaddr(ta) + 16 * vb + 4 * g4), ld4f(Dl + ja * D + 16 * vb + 4 * g4), x1);
-            const float okj = ja < nt ? 1.f : 0.f;
-#pragma unroll 4
-            for (int db = 0; db < NB; ++db)
-                x2 = blk(ok * ld4in<DT>(p.q, rowaddr(ta) + 16 * db + 4 * g4),
-                         okj * ld4in<DT>(p.k, rowaddr(ja) + 16 * db + 4 * g4), x2);
+        const float* Ar = kind == 0 ? a.dout + rowaddr(ta) : dDl + ta * D;
+        const float* Br = (kind == 0 ? Dl : U) + ja * D;
+        const float ok = (kind == 0 && ta >= nt) ? 0.f : 1.f;
+        f32x4 av[NB], bv[NB];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tb + 4 * g4 + r, j = 16 * jb + c16;
-                const float M = j <= t ? ex(t, j) : 0.f;
-                const float dpm = p.scale * x1[r] * M;
-                sh.dPm[t * LDA + j] = dpm;
-                sh.Vm[t * LDA + 1 + j] = j < t ? dpm * x2[r] : 0.f;
-            }
-        } else {
-            // Gram K K^T and dT = dDelta U^T diag(beta)
-            const float ok = ta < nt ? 1.f : 0.f, okj = ja < nt ? 1.f : 0.f;
-#pragma unroll 4
-            for (int db = 0; db < NB; ++db)
-                x1 = blk(ok * ld4in<DT>(p.k, rowaddr(ta) + 16 * db + 4 * g4),
-                         okj * ld4in<DT>(p.k, rowaddr(ja) + 16 * db + 4 * g4), x1);
-#pragma unroll 4
-            for (int vb = 0; vb < NB; ++vb)
-                x2 = blk(ld4f(dDl + ta * D + 16 * vb + 4 * g4), ld4f(U + ja * D + 16 * vb + 4 * g4), x2);
+        for (int vb = 0; vb < NB; ++vb) {
+            av[vb] = ld4f(Ar + 16 * vb + 4 * g4);
+            bv[vb] = ld4f(Br + 16 * vb + 4 * g4);
+        }
+        const f32x4 pv = kind == 0 ? ld4f(PTg + ja * C + 16 * tb + 4 * g4) : zero4();  // P[t][j], r = 0..3
+        f32x4 x = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tb + 4 * g4 + r, j = 16 * jb + c16;
-                sh.At[t * LDA + j] = j < t ? exp_(t, j) * x1[r] : 0.f;
-                sh.dT[t * LDA + j] = j <= t ? x2[r] * sh.gbeta[j] : 0.f;
+        for (int vb = 0; vb < NB; ++vb) x = blk(ok * av[vb], bv[vb], x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tb + 4 * g4 + r, j = ja;
+            if (kind == 0) {
+                const float dp = p.scale * x[r];
+                sh.dPm[t * LDA + j] = j <= t ? dp * ex(t, j) : 0.f;
+                sh.Vm[t * LDA + 1 + j] = j < t ? dp * pv[r] : 0.f;
+            } else {
+                sh.dT[t * LDA + j] = j <= t ? x[r] * sh.gbeta[j] : 0.f;
             }
         }
     }
+    // phase 2's operands: rows of T (block bb = w), of T^T and Atilde^T
+    const int bb = w;
+    f32x4 trow[4], ttrow[4][4], atr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        trow[i] = ld4f(Tg + (16 * bb + c16) * C + 16 * i + 4 * g4);
+        atr[i] = ld4f(AtTg + (16 * bb + c16) * C + 16 * i + 4 * g4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ttrow[i][k] = ld4f(TTg + (16 * i + c16) * C + 16 * k + 4 * g4);
+    }
     __syncthreads();
 
-    // ---- phase 2: dA = -T^T (dT T^T), column block bb = w.  Atilde of an
-    // entry is read and replaced by W + W^T in the same lane: the lower entry
-    // (ar, bc) takes W, the upper one (bc, ar), never read as Atilde, its
-    // transpose, the diagonal zero
+    // ---- phase 2: dA = -T^T (dT T^T), column block bb = w.  W + W^T: the
+    // lower entry (ar, bc) and its transpose, the diagonal zero
     {
-        const int bb = w;
         f32x4 Z[4];
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
             Z[ib] = zero4();
-            if (ib < bb) continue;
-            for (int jb = 0; jb <= bb; ++jb)
-                Z[ib] = blk(ld4f(&sh.dT[(16 * ib + c16) * LDA + 16 * jb + 4 * g4]),
-                            ld4f(Tg + (16 * bb + c16) * C + 16 * jb + 4 * g4), Z[ib]);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                if (ib >= bb && jb <= bb)
+                    Z[ib] = blk(ld4f(&sh.dT[(16 * ib + c16) * LDA + 16 * jb + 4 * g4]), trow[jb], Z[ib]);
         }
 #pragma unroll
         for (int ab = 0; ab < 4; ++ab) {
@@ -746,95 +765,154 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
             f32x4 dA = zero4();
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib)
-                if (ib >= ab) dA = blk(ld4f(TTg + (16 * ab + c16) * C + 16 * ib + 4 * g4), Z[ib], dA);
+                if (ib >= ab) dA = blk(ttrow[ab][ib], Z[ib], dA);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int ar = 16 * ab + 4 * g4 + r, bc = 16 * bb + c16;
                 const bool lower = ar > bc;
                 const float da = -dA[r];
-                const float at = lower ? sh.At[ar * LDA + bc] : 0.f;
+                const float at = lower ? atr[ab][r] : 0.f;
                 const float bt = sh.gbeta[ar];
                 if (lower) {
                     const int row = p.order == GDN_DECAY_THEN_PREDICT ? ar : ar - 1;
                     sh.Vm[row * LDA + 1 + bc] += da * bt * at;
                     const float wk = bt * da * exp_(ar, bc);
-                    sh.At[ar * LDA + bc] = wk;
-                    sh.At[bc * LDA + ar] = wk;
+                    sh.W[ar * LDA + bc] = wk;
+                    sh.W[bc * LDA + ar] = wk;
                 } else if (ar == bc) {
-                    sh.At[ar * LDA + bc] = 0.f;
+                    sh.W[ar * LDA + bc] = 0.f;
                 }
                 const float rs = row_sum<16>(lower ? da * at : 0.f);
                 if (c16 == 0) sh.db2[w][ar] = rs;
             }
         }
     }
+
+    // ---- phase 3: dQ and dK, value-column blocks db = w MT + mi.  State
+    // products first, in two passes over the value blocks vb (S with dO and
+    // dU', then dS_end with Delta), each fetching block vb + 1 while block vb
+    // multiplies
+    float fo[4], fu[4], fr[4], okr[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int t = 16 * tb + c16;
+        okr[tb] = t < nt ? 1.f : 0.f;
+        fo[tb] = p.scale * __expf(sh.ghi[t] + sh.glo[t]);
+        fu[tb] = -__expf(sh.gphi[t] + sh.gplo[t]) * sh.gbeta[t];
+        fr[tb] = ratio(sh.ghi[C - 1], sh.glo[C - 1], sh.ghi[t], sh.glo[t]);
+    }
+    struct PassA {
+        f32x4 sf[MT], ao[4], au[4];
+    };
+    struct PassB {
+        f32x4 sf[MT], dsf[MT], ad[4];
+    };
+    auto fidx = [&](int vb, int mi) { return ((size_t)(vb * NB + w * MT + mi) * 64 + l) * 4; };
+    auto loadA = [&](PassA& x, int vb) {
+        vb = min(vb, NB - 1);
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) x.sf[mi] = ld4f(Sf + fidx(vb, mi));
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            x.ao[tb] = ld4f(a.dout + rowaddr(16 * tb + c16) + 16 * vb + 4 * g4);
+            x.au[tb] = ld4f(dUp + (16 * tb + c16) * D + 16 * vb + 4 * g4);
+        }
+    };
+    auto loadB = [&](PassB& x, int vb) {
+        vb = min(vb, NB - 1);
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            x.sf[mi] = ld4f(Sf + fidx(vb, mi));
+            x.dsf[mi] = ld4f(dSf + fidx(vb, mi));
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) x.ad[tb] = ld4f(Dl + (16 * tb + c16) * D + 16 * vb + 4 * g4);
+    };
+    PassA pa, pa2;
+    loadA(pa, 0);
     __syncthreads();
 
-    // ---- phase 3: dQ and dK, value-column blocks db = w MT + mi
     f32x4 aQ[4][MT], aK1[4][MT], aK2[4][MT];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) aQ[tb][mi] = aK1[tb][mi] = aK2[tb][mi] = zero4();
-    float sdot = 0.f;
-    {
-        float fo[4], fu[4], fr[4], okr[4];
+        for (int mi = 0; mi < MT; ++mi) aQ[tb][mi] = aK1[tb][mi] = zero4();
+#pragma unroll 1
+    for (int vb = 0; vb < NB; ++vb) {
+        loadA(pa2, vb + 1);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            const int t = 16 * tb + c16;
-            okr[tb] = t < nt ? 1.f : 0.f;
-            fo[tb] = p.scale * __expf(sh.ghi[t] + sh.glo[t]);
-            fu[tb] = -__expf(sh.gphi[t] + sh.gplo[t]) * sh.gbeta[t];
-            fr[tb] = ratio(sh.ghi[C - 1], sh.glo[C - 1], sh.ghi[t], sh.glo[t]);
-        }
-        for (int vb = 0; vb < NB; ++vb) {
-            f32x4 sf[MT], dsf[MT];
+            const f32x4 Ao = (okr[tb] * fo[tb]) * pa.ao[tb];
+            const f32x4 Au = fu[tb] * pa.au[tb];
 #pragma unroll
             for (int mi = 0; mi < MT; ++mi) {
-                const int db = w * MT + mi;
-                const size_t fo_ = ((size_t)(vb * NB + db) * 64 + l) * 4;
-                sf[mi] = ld4f(ws.Sf + ci * Rec<D>::kState + fo_);
-                dsf[mi] = ld4f(ws.dSf + ci * Rec<D>::kState + fo_);
-                sdot += dot4(sf[mi], dsf[mi]);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const int t = 16 * tb + c16;
-                const f32x4 Ao = (okr[tb] * fo[tb]) * ld4f(a.dout + rowaddr(t) + 16 * vb + 4 * g4);
-                const f32x4 Au = fu[tb] * ld4f(dUp + t * D + 16 * vb + 4 * g4);
-                const f32x4 Ad = fr[tb] * ld4f(Dl + t * D + 16 * vb + 4 * g4);
-#pragma unroll
-                for (int mi = 0; mi < MT; ++mi) {
-                    aQ[tb][mi] = blk(Ao, sf[mi], aQ[tb][mi]);
-                    aK1[tb][mi] = blk(Au, sf[mi], aK1[tb][mi]);
-                    aK2[tb][mi] = blk(Ad, dsf[mi], aK2[tb][mi]);
-                }
+                aQ[tb][mi] = blk(Ao, pa.sf[mi], aQ[tb][mi]);
+                aK1[tb][mi] = blk(Au, pa.sf[mi], aK1[tb][mi]);
             }
         }
+        pa = pa2;
     }
+    float sdot = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) aK2[tb][mi] = zero4();
+    {
+        PassB pb, pb2;
+        loadB(pb, 0);
+#pragma unroll 1
+        for (int vb = 0; vb < NB; ++vb) {
+            loadB(pb2, vb + 1);
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) sdot += dot4(pb.sf[mi], pb.dsf[mi]);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const f32x4 Ad = fr[tb] * pb.ad[tb];
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi) aK2[tb][mi] = blk(Ad, pb.dsf[mi], aK2[tb][mi]);
+            }
+            pb = pb2;
+        }
+    }
+    // K^T and Q^T fragments of the wave's value blocks, for the rest of dQ, dK
+    R4<DT> kf[MT][4], qf[MT][4];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kf[mi][i] = ldr<DT>(KTf, ((int64_t)((w * MT + mi) * 4 + i) * 64 + l) * 4);
+            qf[mi][i] = ldr<DT>(QTf, ((int64_t)((w * MT + mi) * 4 + i) * 64 + l) * 4);
+        }
     // boundary terms: q_t . dQ_S0, k_t . dK_S0, k_t . dK_dS (rows of the tiles)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-        float so[4] = {0.f, 0.f, 0.f, 0.f}, sx[4] = {0.f, 0.f, 0.f, 0.f}, sr[4] = {0.f, 0.f, 0.f, 0.f};
+        float qv[4][MT], kv[4][MT];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                const int t = 16 * tb + 4 * g4 + r, d = 16 * (w * MT + mi) + c16;
+                qv[r][mi] = gdn_ld<DT>(p.q, rowaddr(t) + d);
+                kv[r][mi] = gdn_ld<DT>(p.k, rowaddr(t) + d);
+            }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * tb + 4 * g4 + r;
+            float so = 0.f, sx = 0.f, sr = 0.f;
 #pragma unroll
             for (int mi = 0; mi < MT; ++mi) {
-                const int d = 16 * (w * MT + mi) + c16;
-                const float qv = t < nt ? gdn_ld<DT>(p.q, rowaddr(t) + d) : 0.f;
-                const float kv = t < nt ? gdn_ld<DT>(p.k, rowaddr(t) + d) : 0.f;
-                so[r] += qv * aQ[tb][mi][r];
-                sx[r] += kv * aK1[tb][mi][r];
-                sr[r] += kv * aK2[tb][mi][r];
+                so += qv[r][mi] * aQ[tb][mi][r];
+                sx += kv[r][mi] * aK1[tb][mi][r];
+                sr += kv[r][mi] * aK2[tb][mi][r];
             }
-            so[r] = row_sum<16>(so[r]);
-            sx[r] = row_sum<16>(sx[r]);
-            sr[r] = row_sum<16>(sr[r]);
+            // (rows past the sequence end: their accumulators are zero or unused)
+            so = row_sum<16>(t < nt ? so : 0.f);
+            sx = row_sum<16>(t < nt ? sx : 0.f);
+            sr = row_sum<16>(t < nt ? sr : 0.f);
             if (c16 == 0) {
-                sh.vo[w][t] = so[r];
-                sh.vx[w][t] = sx[r];
-                sh.vr[w][t] = sr[r];
+                sh.vo[w][t] = so;
+                sh.vx[w][t] = sx;
+                sh.vr[w][t] = sr;
             }
         }
     }
@@ -851,20 +929,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
         for (int mi = 0; mi < MT; ++mi) {
             const int db = w * MT + mi;
             f32x4 q = aQ[tb][mi], kk = aK1[tb][mi] + aK2[tb][mi];
+#pragma unroll
             for (int jb = 0; jb <= tb; ++jb)
-                q = blk(ld4f(&sh.dPm[(16 * tb + c16) * LDA + 16 * jb + 4 * g4]),
-                        ld4in<DT>(KTf, ((int64_t)(db * 4 + jb) * 64 + l) * 4), q);
-            // row tile tb of dK: (dP o M)^T over token tiles s >= tb, W over all
+                q = blk(ld4f(&sh.dPm[(16 * tb + c16) * LDA + 16 * jb + 4 * g4]), cvt<DT>(kf[mi][jb]), q);
+#pragma unroll
             for (int sb = tb; sb < 4; ++sb) {
                 f32x4 at;
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) at[qq] = sh.dPm[(16 * sb + 4 * g4 + qq) * LDA + 16 * tb + c16];
-                kk = blk(at, ld4in<DT>(QTf, ((int64_t)(db * 4 + sb) * 64 + l) * 4), kk);
+                kk = blk(at, cvt<DT>(qf[mi][sb]), kk);
             }
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib)
-                kk = blk(ld4f(&sh.At[(16 * tb + c16) * LDA + 16 * ib + 4 * g4]),
-                         ld4in<DT>(KTf, ((int64_t)(db * 4 + ib) * 64 + l) * 4), kk);
+                kk = blk(ld4f(&sh.W[(16 * tb + c16) * LDA + 16 * ib + 4 * g4]), cvt<DT>(kf[mi][ib]), kk);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tb + 4 * g4 + r;
@@ -955,7 +1032,7 @@ bool chunked_backward_supported(int64_t dk, int64_t dv, int gate) {
 static size_t chunked_bytes_per_head(int64_t T, int64_t D) {
     const size_t nc = (size_t)((T + C - 1) / C);
     const size_t nb = (size_t)(D / 16);
-    const size_t per_chunk = sizeof(float) * (3 * (size_t)C * C + 2 * nb * 4 * 64 * 4 + 2 * nb * nb * 64 * 4 +
+    const size_t per_chunk = sizeof(float) * (4 * (size_t)C * C + 2 * nb * 4 * 64 * 4 + 2 * nb * nb * 64 * 4 +
                                               4 * (size_t)C * D);
     return nc * per_chunk;
 }
@@ -967,8 +1044,8 @@ static int64_t chunked_heads_per_launch(int64_t B, int64_t T, int64_t H, int64_t
 }
 
 size_t chunked_backward_workspace(int64_t B, int64_t T, int64_t H, int64_t D) {
-    // eleven pieces, each 256-byte aligned
-    return chunked_bytes_per_head(T, D) * (size_t)chunked_heads_per_launch(B, T, H, D) + 11 * 256;
+    // twelve pieces, each 256-byte aligned
+    return chunked_bytes_per_head(T, D) * (size_t)chunked_heads_per_launch(B, T, H, D) + 12 * 256;
 }
 
 hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t st) {
@@ -1001,6 +1078,7 @@ hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t
     ws.T = take(nch * C * C);
     ws.TT = take(nch * C * C);
     ws.PT = take(nch * C * C);
+    ws.AtT = take(nch * C * C);
     ws.KTf = take(nch * nb * 4 * 64 * 4);  // (sized for fp32 inputs)
     ws.QTf = take(nch * nb * 4 * 64 * 4);
     ws.Sf = take(nch * nb * nb * 64 * 4);
