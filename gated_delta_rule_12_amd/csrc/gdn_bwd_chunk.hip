@@ -90,6 +90,39 @@ template <int DT>
 __device__ __forceinline__ f32x4 ld4in(const void* base, int64_t i) {
     return cvt<DT>(ldr<DT>(base, i));
 }
+// eight consecutive input-typed elements (16 bytes bf16, 32 bytes fp32)
+template <int DT>
+struct R8 {
+    R4<DT> h[2];
+};
+template <int DT>
+__device__ __forceinline__ R8<DT> ldr8(const void* base, int64_t i) {
+    R8<DT> x;
+    if constexpr (DT == GDN_BF16) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + i);
+        x.h[0] = u32x2{u[0], u[1]};
+        x.h[1] = u32x2{u[2], u[3]};
+    } else {
+        x.h[0] = ldr<DT>(base, i);
+        x.h[1] = ldr<DT>(base, i + 4);
+    }
+    return x;
+}
+
+// Key (dk) index of row i (0..15) of key tile mi (of MT = D / 64) of wave w.
+// A wave's tiles interleave in runs of four, so that a lane's rows of all of
+// them are 4 MT consecutive keys and come in one load; every tiling of the
+// key axis below (state tiles, K^T and Q^T fragments, the gradient kernel's
+// output columns) uses this order.  Column block db of the whole axis is
+// tile db % MT of wave db / MT.
+template <int D>
+__device__ __forceinline__ int key_of(int w, int mi, int i) {
+    return (D / 4) * w + 4 * (D / 64) * (i >> 2) + 4 * mi + (i & 3);
+}
+template <int D>
+__device__ __forceinline__ int key_col(int db, int i) {
+    return key_of<D>(db / (D / 64), db % (D / 64), i);
+}
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ float dot4(const f32x4& x, const f32x4& y) {
     return x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
@@ -150,16 +183,17 @@ __device__ __forceinline__ float ratio(float hb, float lb, float ha, float la) {
     return __expf((hb - ha) + (lb - la));
 }
 
-// Per-chunk records of the workspace.  Fragment sets: [m][tb][lane] of
-// f32x4 = X[16 tb + 4 g + q][16 m + c] (q = 0..3) for X = K, Q; state
-// fragments [vb][db][lane] of f32x4 = S[16 vb + 4 g + q][16 db + c].
+// Per-chunk records of the workspace.  Fragment sets: [m][tp][lane][8] =
+// X[16 (2 tp + e) + 4 g + q][key_col(m, c)] (e = 0, 1; q = 0..3) for X = K,
+// Q; state fragments [vb][db][lane] of f32x4 = S[16 vb + 4 g + q][key_col(db, c)].
 template <int D>
 struct Rec {
     static constexpr int NB = D / 16;
     static constexpr size_t kTile = (size_t)C * C;          // T, T^T, P^T, Atilde^T (floats)
     static constexpr size_t kFrag = (size_t)NB * 4 * 64 * 4;  // K^T, Q^T fragments
     static constexpr size_t kState = (size_t)NB * NB * 64 * 4;
-    static constexpr size_t kRows = (size_t)C * D;          // U, Delta, dDelta, dU'
+    static constexpr size_t kRows = (size_t)C * D;          // U, Delta, dDelta, dU'; E fragments
+    static constexpr size_t kHf = (size_t)D * D;            // H fragments
 };
 
 struct CbWs {
@@ -167,6 +201,8 @@ struct CbWs {
     void *KTf, *QTf;           // [chunk][fragment set], input-typed
     float *Sf, *dSf;           // [chunk][state fragments]
     float *U, *Dl, *dDl, *dUp; // [chunk][C][D]
+    float *Ef, *Hf;            // [chunk][vb][jb or m][lane] of f32x4: E = scale P^T dO,
+                               // H = scale Q^T diag(gamma) dO as accumulator tiles
 };
 
 // ---------------------------------------------------------------------------
@@ -182,8 +218,10 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
     __shared__ __attribute__((aligned(16))) E Ks[C * LDK];
     __shared__ __attribute__((aligned(16))) E Qs[C * LDK];
+    __shared__ __attribute__((aligned(16))) float PTs[C * LDA];        // P^T
+    __shared__ __attribute__((aligned(16))) float dOs[C * (D + 4)];    // dL/d out rows
     __shared__ float Pscr[4][16 * 17];
-    __shared__ float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C];
+    __shared__ float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C], ggam[C];
 
     const Problem& p = a.p;
     const int64_t ci = blockIdx.x;
@@ -206,6 +244,14 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
         *reinterpret_cast<u32x4*>(&Ks[t * LDK + pc * EP]) = kv;
         *reinterpret_cast<u32x4*>(&Qs[t * LDK + pc * EP]) = qv;
     }
+    constexpr int LDD = D + 4, OP = C * (D / 4) / kThreads;
+#pragma unroll
+    for (int i = 0; i < OP; ++i) {
+        const int e = tid + kThreads * i, t = e / (D / 4), pc = e % (D / 4);
+        f32x4 x = ld4f(a.dout + ((b * p.T + t0 + min(t, nt - 1)) * p.H + h) * D + 4 * pc);
+        if (t >= nt) x = zero4();
+        st4f(&dOs[t * LDD + 4 * pc], x);
+    }
     if (w == 0) {
         const Gate g = chunk_gate(p, (b * p.T + t0) * p.H + h, nt, l);
         ghi[l] = g.hi;
@@ -213,6 +259,7 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
         gphi[l] = g.phi;
         gplo[l] = g.plo;
         gbeta[l] = g.beta;
+        ggam[l] = __expf(g.hi + g.lo);
     }
     __syncthreads();
 
@@ -255,9 +302,53 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
                 pv[r] = j <= t ? ratio(ghi[t], glo[t], ghi[j], glo[j]) * acc[r] : 0.f;
             }
             st4f(ws.PT + ci * Rec<D>::kTile + j * C + 16 * m + 4 * g4, pv);
+            st4f(&PTs[j * LDA + 16 * m + 4 * g4], pv);
         }
     }
     __syncthreads();
+    // E = scale P^T dO (value blocks vb = w MT + mi, every token block jb) and
+    // H = scale Q^T diag(gamma) dO (key blocks m = w MT + mi, every vb), the
+    // reverse chain's state-independent terms, as accumulator tiles
+    {
+        constexpr int MT = D / 64;
+        f32x4 qa[MT][4];  // A operand Q^T[16 m + c16][16 tb + 4 g4 + q]
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const E x = Qs[(16 * tb + 4 * g4 + q) * LDK + key_of<D>(w, mi, c16)];
+                    if constexpr (DT == GDN_BF16) qa[mi][tb][q] = gdn_bf16_to_f32(x);
+                    else qa[mi][tb][q] = x;
+                }
+        for (int vb = 0; vb < NB; ++vb) {
+            f32x4 db[4], gb[4];  // B operands dO[16 tb + 4 g4 + q][16 vb + c16], and scale gamma_t times it
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) db[tb][q] = dOs[(16 * tb + 4 * g4 + q) * LDD + 16 * vb + c16];
+                gb[tb] = p.scale * *reinterpret_cast<const f32x4*>(&ggam[16 * tb + 4 * g4]) * db[tb];
+            }
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc = blk(qa[mi][tb], gb[tb], acc);
+                st4f(ws.Hf + ci * Rec<D>::kHf + ((size_t)(vb * NB + w * MT + mi) * 64 + l) * 4, acc);
+            }
+            if (vb / MT == w) {
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+                        if (tb >= jb) acc = blk(ld4f(&PTs[(16 * jb + c16) * LDA + 16 * tb + 4 * g4]), db[tb], acc);
+                    st4f(ws.Ef + ci * Rec<D>::kRows + ((size_t)(vb * 4 + jb) * 64 + l) * 4, p.scale * acc);
+                }
+            }
+        }
+    }
     ut_inverse_lds(AT, Pscr[w]);
 
     // T and T^T, row-major, zero above (below) the diagonal
@@ -274,23 +365,33 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
         st4f(Tg + r0 * C + c0, x);
         st4f(TTg + r0 * C + c0, y);
     }
-    // K^T and Q^T fragments (input-typed)
-    for (int f = tid; f < NB * 4 * 64; f += kThreads) {
-        const int ln = f & 63, mt = f >> 6, m = mt >> 2, tb = mt & 3;
-        const int gg = ln >> 4, cc = ln & 15;
-        E kx[4], qx[4];
+    // K^T and Q^T fragments (input-typed), two token blocks a lane
+    for (int f = tid; f < NB * 2 * 64; f += kThreads) {
+        const int ln = f & 63, mt = f >> 6, m = mt >> 1, tp = mt & 1;
+        const int gg = ln >> 4, d = key_col<D>(m, ln & 15);
+        E kx[8], qx[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = 16 * tb + 4 * gg + q, d = 16 * m + cc;
-            kx[q] = Ks[t * LDK + d];
-            qx[q] = Qs[t * LDK + d];
+        for (int e = 0; e < 8; ++e) {
+            const int t = 16 * (2 * tp + (e >> 2)) + 4 * gg + (e & 3);
+            kx[e] = Ks[t * LDK + d];
+            qx[e] = Qs[t * LDK + d];
         }
-        E* kd = static_cast<E*>(ws.KTf) + ci * Rec<D>::kFrag + (size_t)f * 4;
-        E* qd = static_cast<E*>(ws.QTf) + ci * Rec<D>::kFrag + (size_t)f * 4;
+        E* kd = static_cast<E*>(ws.KTf) + ci * Rec<D>::kFrag + (size_t)f * 8;
+        E* qd = static_cast<E*>(ws.QTf) + ci * Rec<D>::kFrag + (size_t)f * 8;
+        if constexpr (DT == GDN_BF16) {
+            u16x8 kv, qv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            kd[q] = kx[q];
-            qd[q] = qx[q];
+            for (int e = 0; e < 8; ++e) {
+                kv[e] = kx[e];
+                qv[e] = qx[e];
+            }
+            *reinterpret_cast<u16x8*>(kd) = kv;
+            *reinterpret_cast<u16x8*>(qd) = qv;
+        } else {
+            st4f(kd, f32x4{kx[0], kx[1], kx[2], kx[3]});
+            st4f(kd + 4, f32x4{kx[4], kx[5], kx[6], kx[7]});
+            st4f(qd, f32x4{qx[0], qx[1], qx[2], qx[3]});
+            st4f(qd + 4, f32x4{qx[4], qx[5], qx[6], qx[7]});
         }
     }
 }
@@ -303,30 +404,45 @@ struct ChainShared {
     f32x4 red[4][4][64];  // [wave][token tile][lane]: partial K S^T (or K dS^T)
     f32x4 xch[4][64];     // [token tile][lane]: Delta R (forward) / dDelta (reverse)
     f32x4 xch2[4][64];    // reverse: -gamma' beta dU'
-    float g[4][6][C];     // [wave][hi, lo, phi, plo, beta, -][token]
+    float vs[2][16][C + 4];      // forward: V of the slice, [chunk parity][value][token]
+    float tp[4][5][16][20];      // per wave: 16 x 16 tiles being transposed for stores
+    float g[4][2][8][C];  // [wave][chunk parity][row kG*][token]
 };
 
-// Token-row factors of the chunk from the wave's gate rows.
+// Token-row factors of a chunk, formed once per wave (lane t: token t) in
+// LDS: the gate prefix pair, beta, gamma_t, gamma'_t and R_t = gamma_C / gamma_t.
+enum { kGhi, kGlo, kGphi, kGplo, kGbeta, kGgam, kGgamp, kGR };
 struct RowF {
-    const float* g;  // [6][C]
-    __device__ float gam(int t) const { return __expf(g[0 * C + t] + g[1 * C + t]); }
-    __device__ float gamp(int t) const { return __expf(g[2 * C + t] + g[3 * C + t]); }
-    __device__ float R(int t) const {
-        return ratio(g[0 * C + C - 1], g[1 * C + C - 1], g[0 * C + t], g[1 * C + t]);
-    }
-    __device__ float gC() const { return __expf(g[0 * C + C - 1] + g[1 * C + C - 1]); }
-    __device__ float beta(int t) const { return g[4 * C + t]; }
+    const float* g;  // [8][C]
+    // rows of four consecutive tokens t0 .. t0 + 3
+    __device__ f32x4 v4(int row, int t0) const { return *reinterpret_cast<const f32x4*>(g + row * C + t0); }
+    __device__ float gC() const { return g[kGgam * C + C - 1]; }
 };
 
-// Operands of a chain step, fetched ahead: the "early" ones of the next
-// chunk while the current one computes, the "late" ones (used after the
-// chunk's first or second barrier) at the start of the chunk itself.  Rows
-// past the sequence end are read at the last real row and zeroed at use.
+// Operands of a chain step, all fetched one chunk ahead (the next chunk's
+// while the current one computes); rows past the sequence end are read at
+// the last real row and zeroed at use.  A chunk's workspace stores are
+// issued at the start of the next chunk, so that neither they nor the
+// fetches are waited for before a whole step has passed.  Stores go out in
+// 16-byte pieces after a transpose through the wave's own LDS tiles.
 template <int D, int DT>
-struct ChainIn {
+struct FwdIn {
     static constexpr int MT = D / 64;
-    R4<DT> kx[4][MT];  // K[16 at + c16][16 m + 4 g4 ..], the K S^T operand
-    float al, be;      // lane t: alpha_t, beta_t
+    R4<DT> kx[4][MT];    // K[16 at + c16][key_of(w, mi, 4 g4 ..)]: the K S^T operand
+    float al, be;        // lane t: alpha_t, beta_t
+    R4<DT> vr;           // V[t][r0 + 4 p ..] of this thread's (t, p) = (tid / 4, tid % 4)
+    f32x4 tr[4];         // T[16 w + c16][16 jb + 4 g4 ..]
+    R8<DT> kt[MT][2];    // K^T fragments of the wave's key tiles, token blocks in pairs
+};
+template <int D, int DT>
+struct RevIn {
+    static constexpr int MT = D / 64;
+    R4<DT> kx[4][MT];
+    float al, be;
+    f32x4 ef;            // E tile w of the slice
+    f32x4 hf[MT];        // H tiles of the wave's key tiles
+    f32x4 tt[4];         // T^T[16 w + c16][16 jb + 4 g4 ..]
+    R8<DT> kt[MT][2];
 };
 
 template <int D, int DT>
@@ -335,26 +451,61 @@ struct ChainCtx {
     const BwdProblem& a;
     const CbWs& ws;
     int64_t bl, b, h, bh;
-    int rho, r0, w, l, g4, c16, NC;
+    int rho, r0, w, l, g4, c16, NC, tid;
     __device__ int64_t row0(int c) const { return (b * a.p.T + (int64_t)c * C) * a.p.H + h; }
     __device__ int ntok(int c) const { return (int)min<int64_t>(C, a.p.T - (int64_t)c * C); }
-    // early operands of chunk c (clamped to a real chunk)
-    __device__ void load_early(ChainIn<D, DT>& x, int c) const {
-        c = min(max(c, 0), NC - 1);
+    __device__ int64_t cidx(int c) const { return bl * NC + c; }
+    template <class In>
+    __device__ void load_common(In& x, int c) const {
         const int64_t r = row0(c);
         const int nt = ntok(c);
+        const int64_t ci = cidx(c);
         const int64_t rl = r + (int64_t)min(l, nt - 1) * a.p.H;
         x.al = a.p.alpha[rl];
         x.be = a.p.beta[rl];
 #pragma unroll
-        for (int at = 0; at < 4; ++at)
+        for (int at = 0; at < 4; ++at) {
+            const int64_t o = (r + (int64_t)min(16 * at + c16, nt - 1) * a.p.H) * D + key_of<D>(w, 0, 4 * g4);
+            if constexpr (MT == 2) {
+                const R8<DT> k8 = ldr8<DT>(a.p.k, o);
+                x.kx[at][0] = k8.h[0];
+                x.kx[at][MT - 1] = k8.h[1];
+            } else {
+                x.kx[at][0] = ldr<DT>(a.p.k, o);
+            }
+        }
 #pragma unroll
-            for (int mi = 0; mi < MT; ++mi)
-                x.kx[at][mi] = ldr<DT>(a.p.k, (r + (int64_t)min(16 * at + c16, nt - 1) * a.p.H) * D +
-                                                  16 * (w * MT + mi) + 4 * g4);
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+                x.kt[mi][tp] = ldr8<DT>(ws.KTf, ci * Rec<D>::kFrag + ((int64_t)((w * MT + mi) * 2 + tp) * 64 + l) * 8);
     }
+    __device__ void load(FwdIn<D, DT>& x, int c) const {
+        c = min(max(c, 0), NC - 1);
+        load_common(x, c);
+        const int64_t r = row0(c), ci = cidx(c);
+        const int nt = ntok(c);
+        x.vr = ldr<DT>(a.p.v, (r + (int64_t)min(tid >> 2, nt - 1) * a.p.H) * D + r0 + 4 * (tid & 3));
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) x.tr[jb] = ld4f(ws.T + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
+    }
+    __device__ void load(RevIn<D, DT>& x, int c) const {
+        c = min(max(c, 0), NC - 1);
+        load_common(x, c);
+        const int64_t ci = cidx(c);
+        x.ef = ld4f(ws.Ef + ci * Rec<D>::kRows + ((size_t)(rho * 4 + w) * 64 + l) * 4);
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+            x.hf[mi] = ld4f(ws.Hf + ci * Rec<D>::kHf + ((size_t)(rho * NB + w * MT + mi) * 64 + l) * 4);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) x.tt[jb] = ld4f(ws.TT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
+    }
+    // K^T fragment of key tile mi, token block tb
+    template <class In>
+    __device__ f32x4 ktf(const In& x, int mi, int tb) const { return cvt<DT>(x.kt[mi][tb >> 1].h[tb & 1]); }
     // partial K S^T over the wave's key tiles for every token tile, to LDS
-    __device__ void partial_KS(ChainShared& sh, const ChainIn<D, DT>& x, const f32x4 (&St)[MT], int nt) const {
+    template <class In>
+    __device__ void partial_KS(ChainShared& sh, const In& x, const f32x4 (&St)[MT], int nt) const {
 #pragma unroll
         for (int at = 0; at < 4; ++at) {
             f32x4 acc = zero4();
@@ -364,59 +515,74 @@ struct ChainCtx {
             sh.red[w][at][l] = acc;
         }
     }
-    // the state as the gradient kernel's fragments
-    __device__ void store_state(float* dst, const f32x4 (&St)[MT]) const {
+    // the state as the gradient kernel's fragments: lane (g, c) holds
+    // S[r0 + c][key_of(w, mi, 4 g + r)], the fragment lane 16 (c / 4) + 4 g + r
+    // wants it in element c % 4; transposed through the wave's tile
+    __device__ void store_state(ChainShared& sh, float* dst, const f32x4 (&St)[MT]) const {
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
-            const int m = w * MT + mi;
+            float(*X)[20] = sh.tp[w][mi];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dst[((size_t)(rho * NB + m) * 64 + 16 * (c16 >> 2) + 4 * g4 + r) * 4 + (c16 & 3)] = St[mi][r];
+            for (int r = 0; r < 4; ++r) X[4 * g4 + r][c16] = St[mi][r];
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&X[c16][4 * g4]);
+            st4f(dst + ((size_t)(rho * NB + w * MT + mi) * 64 + l) * 4, v);
         }
     }
-    __device__ void gates_to_lds(float* gw, const ChainIn<D, DT>& x, int nt) const {
+    // a token tile w of a C x D row block (rows 16 w + 4 g4 + q, column
+    // r0 + c16) as 16-byte row pieces: lane l takes row l / 4, columns
+    // r0 + 4 (l % 4) ..; base points at row 0, column 0, rows ld apart
+    __device__ void store_rows(ChainShared& sh, int slot, float* base, int64_t ld, const f32x4& x, int nvalid) const {
+        float(*X)[20] = sh.tp[w][slot];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) X[4 * g4 + q][c16] = x[q];
+        const int i = l >> 2, j = l & 3;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&X[i][4 * j]);
+        if (16 * w + i < nvalid) st4f(base + (int64_t)(16 * w + i) * ld + r0 + 4 * j, v);
+    }
+    template <class In>
+    __device__ void gates_to_lds(float* gw, const In& x, int nt) const {
         const Gate g = gate_from(x.al, x.be, nt, a.p.order, l);
-        gw[0 * C + l] = g.hi;
-        gw[1 * C + l] = g.lo;
-        gw[2 * C + l] = g.phi;
-        gw[3 * C + l] = g.plo;
-        gw[4 * C + l] = g.beta;
+        const float hC = __shfl(g.hi, C - 1, 64), lC = __shfl(g.lo, C - 1, 64);
+        gw[kGhi * C + l] = g.hi;
+        gw[kGlo * C + l] = g.lo;
+        gw[kGphi * C + l] = g.phi;
+        gw[kGplo * C + l] = g.plo;
+        gw[kGbeta * C + l] = g.beta;
+        gw[kGgam * C + l] = __expf(g.hi + g.lo);
+        gw[kGgamp * C + l] = __expf(g.phi + g.plo);
+        gw[kGR * C + l] = ratio(hC, lC, g.hi, g.lo);
+    }
+    // the slice of V (this thread's four values of one token) into LDS,
+    // transposed to [value][token]
+    __device__ void v_to_lds(ChainShared& sh, int buf, const FwdIn<D, DT>& x, int nt) const {
+        const int t = tid >> 2, j = tid & 3;
+        const f32x4 v = t < nt ? cvt<DT>(x.vr) : zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sh.vs[buf][4 * j + e][t] = v[e];
     }
 };
 
 template <int D, int DT>
 __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 (&St)[D / 64]) {
     constexpr int MT = D / 64;
-    const BwdProblem& a = cx.a;
     const CbWs& ws = cx.ws;
-    const int w = cx.w, l = cx.l, g4 = cx.g4, c16 = cx.c16, r0 = cx.r0;
-    float* gw = &sh.g[w][0][0];
-    const RowF rf{gw};
-    ChainIn<D, DT> cur, nxt;
-    cx.load_early(cur, 0);
+    const int w = cx.w, l = cx.l, g4 = cx.g4, c16 = cx.c16;
+    FwdIn<D, DT> cur, nxt;
+    cx.load(cur, 0);
+    cx.gates_to_lds(&sh.g[w][0][0][0], cur, cx.ntok(0));
+    cx.v_to_lds(sh, 0, cur, cx.ntok(0));
+    // the previous chunk's U and Delta tiles, stored at the next chunk's start
+    // (chunk 0's slots first take zeros, overwritten in order by the same lane)
+    f32x4 pU = zero4(), pD = zero4();
+    int64_t pci = cx.cidx(0);
     for (int c = 0; c < cx.NC; ++c) {
-        const int64_t ci = cx.bl * cx.NC + c;
+        const RowF rf{&sh.g[w][c & 1][0][0]};
+        const int64_t ci = cx.cidx(c);
         const int nt = cx.ntok(c);
-        const int64_t r = cx.row0(c);
-        // late operands of this chunk: V rows, T rows, K^T fragments
-        float vv[4][4];
-        f32x4 tr[4];
-        R4<DT> kt[MT][4];
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                vv[jb][q] = gdn_ld<DT>(a.p.v, (r + (int64_t)min(16 * jb + 4 * g4 + q, nt - 1) * a.p.H) * D + r0 + c16);
-            tr[jb] = ld4f(ws.T + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
-        }
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                kt[mi][tb] = ldr<DT>(ws.KTf, ci * Rec<D>::kFrag + ((int64_t)((w * MT + mi) * 4 + tb) * 64 + l) * 4);
-        cx.load_early(nxt, c + 1);
-        cx.gates_to_lds(gw, cur, nt);
-        cx.store_state(ws.Sf + ci * Rec<D>::kState, St);
+        cx.load(nxt, c + 1);
+        cx.store_rows(sh, 2, ws.U + pci * Rec<D>::kRows, D, pU, C);
+        cx.store_rows(sh, 3, ws.Dl + pci * Rec<D>::kRows, D, pD, C);
+        cx.store_state(sh, ws.Sf + ci * Rec<D>::kState, St);
         cx.partial_KS(sh, cur, St, nt);
         __syncthreads();
         // U' tiles jb <= w and the Delta tile w = sum_jb T[w][jb] U'[jb]
@@ -425,27 +591,14 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
         for (int jb = 0; jb < 4; ++jb) {
             if (jb > w) continue;
             const f32x4 X = sh.red[0][jb][l] + sh.red[1][jb][l] + sh.red[2][jb][l] + sh.red[3][jb][l];
-            f32x4 U, Up;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int t = 16 * jb + 4 * g4 + q;
-                U[q] = (t < nt ? vv[jb][q] : 0.f) - rf.gamp(t) * X[q];
-                Up[q] = rf.beta(t) * U[q];
-            }
-            if (jb == w) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) ws.U[ci * Rec<D>::kRows + (16 * w + 4 * g4 + q) * D + r0 + c16] = U[q];
-            }
-            dl = blk(tr[jb], Up, dl);
+            const f32x4 gp = rf.v4(kGgamp, 16 * jb + 4 * g4), bt = rf.v4(kGbeta, 16 * jb + 4 * g4);
+            const f32x4 U = *reinterpret_cast<const f32x4*>(&sh.vs[c & 1][c16][16 * jb + 4 * g4]) - gp * X;
+            if (jb == w) pU = U;
+            dl = blk(cur.tr[jb], bt * U, dl);
         }
-        f32x4 rd;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = 16 * w + 4 * g4 + q;
-            ws.Dl[ci * Rec<D>::kRows + t * D + r0 + c16] = dl[q];
-            rd[q] = rf.R(t) * dl[q];
-        }
-        sh.xch[w][l] = rd;
+        pD = dl;
+        pci = ci;
+        sh.xch[w][l] = rf.v4(kGR, 16 * w + 4 * g4) * dl;
         __syncthreads();
         // S^T <- gamma_C S^T + K^T diag(R) Delta
         const float gC = rf.gC();
@@ -453,11 +606,19 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
         for (int mi = 0; mi < MT; ++mi) {
             f32x4 acc = gC * St[mi];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc = blk(cvt<DT>(kt[mi][tb]), sh.xch[tb][l], acc);
+            for (int tb = 0; tb < 4; ++tb) acc = blk(cx.ktf(cur, mi, tb), sh.xch[tb][l], acc);
             St[mi] = acc;
         }
+        // the next chunk's gate rows and V slice while the update multiplies
+        // (every wave is past this chunk's first barrier, the last reader of
+        // the V buffer written here)
+        const int nn = cx.ntok(min(c + 1, cx.NC - 1));
+        cx.gates_to_lds(&sh.g[w][(c + 1) & 1][0][0], nxt, nn);
+        cx.v_to_lds(sh, (c + 1) & 1, nxt, nn);
         cur = nxt;
     }
+    cx.store_rows(sh, 2, ws.U + pci * Rec<D>::kRows, D, pU, C);
+    cx.store_rows(sh, 3, ws.Dl + pci * Rec<D>::kRows, D, pD, C);
 }
 
 template <int D, int DT>
@@ -466,120 +627,61 @@ __device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     const BwdProblem& a = cx.a;
     const Problem& p = a.p;
     const CbWs& ws = cx.ws;
-    const int w = cx.w, l = cx.l, g4 = cx.g4, c16 = cx.c16, r0 = cx.r0;
-    float* gw = &sh.g[w][0][0];
-    const RowF rf{gw};
-    // early operands beyond the K rows: dO of the slice, P^T rows, Q^T fragments
-    struct RevIn {
-        float dob[4][4];
-        f32x4 pr[4];
-        R4<DT> qt[MT][4];
-    };
-    auto load_rev = [&](RevIn& x, int c) {
-        c = min(max(c, 0), cx.NC - 1);
-        const int64_t ci = cx.bl * cx.NC + c;
-        const int64_t r = cx.row0(c);
-        const int nt = cx.ntok(c);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                x.dob[tb][q] = a.dout[(r + (int64_t)min(16 * tb + 4 * g4 + q, nt - 1) * p.H) * D + r0 + c16];
-            x.pr[tb] = ld4f(ws.PT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * tb + 4 * g4);
-        }
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                x.qt[mi][tb] = ldr<DT>(ws.QTf, ci * Rec<D>::kFrag + ((int64_t)((w * MT + mi) * 4 + tb) * 64 + l) * 4);
-    };
-    ChainIn<D, DT> cur, nxt;
-    RevIn rcur, rnxt;
-    cx.load_early(cur, cx.NC - 1);
-    load_rev(rcur, cx.NC - 1);
+    const int w = cx.w, l = cx.l, g4 = cx.g4;
+    RevIn<D, DT> cur, nxt;
+    cx.load(cur, cx.NC - 1);
+    cx.gates_to_lds(&sh.g[w][(cx.NC - 1) & 1][0][0], cur, cx.ntok(cx.NC - 1));
+    // the previous step's dDelta, dU' and dv tiles, stored at the next step's
+    // start (the first step's slots first take zeros, then the real values)
+    f32x4 pdD = zero4(), pdU = zero4(), pdv = zero4();
+    int64_t pci = cx.cidx(cx.NC - 1), prow = cx.row0(cx.NC - 1);
+    int pnt = 0;
     for (int c = cx.NC - 1; c >= 0; --c) {
-        const int64_t ci = cx.bl * cx.NC + c;
+        const RowF rf{&sh.g[w][c & 1][0][0]};
+        const int64_t ci = cx.cidx(c);
         const int nt = cx.ntok(c);
-        const int64_t r = cx.row0(c);
-        // late operands of this chunk: T^T rows, K^T fragments
-        f32x4 tt[4];
-        R4<DT> kt[MT][4];
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) tt[jb] = ld4f(ws.TT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                kt[mi][tb] = ldr<DT>(ws.KTf, ci * Rec<D>::kFrag + ((int64_t)((w * MT + mi) * 4 + tb) * 64 + l) * 4);
-        cx.load_early(nxt, c - 1);
-        load_rev(rnxt, c - 1);
-        cx.gates_to_lds(gw, cur, nt);
-        cx.store_state(ws.dSf + ci * Rec<D>::kState, St);
+        cx.load(nxt, c - 1);
+        cx.store_rows(sh, 2, ws.dDl + pci * Rec<D>::kRows, D, pdD, C);
+        cx.store_rows(sh, 3, ws.dUp + pci * Rec<D>::kRows, D, pdU, C);
+        cx.store_rows(sh, 4, a.dv + prow * D, p.H * D, pdv, pnt);
+        cx.store_state(sh, ws.dSf + ci * Rec<D>::kState, St);
         cx.partial_KS(sh, cur, St, nt);
-        // state-independent pieces: E_w = scale P^T[w][.] dO and
-        // scale Q^T diag(gamma) dO over the wave's key tiles
-        f32x4 dob[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dob[tb][q] = 16 * tb + 4 * g4 + q < nt ? rcur.dob[tb][q] : 0.f;
-        f32x4 E = zero4();
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-            if (tb >= w) E = blk(rcur.pr[tb], dob[tb], E);
-        E = p.scale * E;
-        f32x4 QD[MT];
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) QD[mi] = zero4();
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            f32x4 sg;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sg[q] = p.scale * rf.gam(16 * tb + 4 * g4 + q) * dob[tb][q];
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) QD[mi] = blk(cvt<DT>(rcur.qt[mi][tb]), sg, QD[mi]);
-        }
         __syncthreads();
         // dDelta tile w = diag(R) K dS^T + E_w
-        {
-            const f32x4 Y = sh.red[0][w][l] + sh.red[1][w][l] + sh.red[2][w][l] + sh.red[3][w][l];
-            f32x4 dd;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int t = 16 * w + 4 * g4 + q;
-                dd[q] = rf.R(t) * Y[q] + E[q];
-                ws.dDl[ci * Rec<D>::kRows + t * D + r0 + c16] = dd[q];
-            }
-            sh.xch[w][l] = dd;
-        }
+        const f32x4 Y = sh.red[0][w][l] + sh.red[1][w][l] + sh.red[2][w][l] + sh.red[3][w][l];
+        const f32x4 dd = rf.v4(kGR, 16 * w + 4 * g4) * Y + cur.ef;
+        sh.xch[w][l] = dd;
+        pdD = dd;
         __syncthreads();
         // dU' tile w = sum_{jb >= w} T^T[w][jb] dDelta[jb]; dv = beta dU'
         f32x4 du = zero4();
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
-            if (jb >= w) du = blk(tt[jb], sh.xch[jb][l], du);
-        f32x4 bk;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = 16 * w + 4 * g4 + q;
-            ws.dUp[ci * Rec<D>::kRows + t * D + r0 + c16] = du[q];
-            if (t < nt) a.dv[(r + (int64_t)t * p.H) * D + r0 + c16] = rf.beta(t) * du[q];
-            bk[q] = -rf.gamp(t) * rf.beta(t) * du[q];
-        }
-        sh.xch2[w][l] = bk;
+            if (jb >= w) du = blk(cur.tt[jb], sh.xch[jb][l], du);
+        const f32x4 bt = rf.v4(kGbeta, 16 * w + 4 * g4);
+        sh.xch2[w][l] = -(rf.v4(kGgamp, 16 * w + 4 * g4) * bt) * du;
+        pdU = du;
+        pdv = bt * du;
+        pci = ci;
+        prow = cx.row0(c);
+        pnt = nt;
         __syncthreads();
         // dS^T <- gamma_C dS^T + scale Q^T diag(gamma) dO - K^T diag(gamma' beta) dU'
         const float gC = rf.gC();
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
-            f32x4 acc = gC * St[mi] + QD[mi];
+            f32x4 acc = gC * St[mi] + cur.hf[mi];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc = blk(cvt<DT>(kt[mi][tb]), sh.xch2[tb][l], acc);
+            for (int tb = 0; tb < 4; ++tb) acc = blk(cx.ktf(cur, mi, tb), sh.xch2[tb][l], acc);
             St[mi] = acc;
         }
+        // the next chunk's gate rows while the update multiplies
+        cx.gates_to_lds(&sh.g[w][(c + 1) & 1][0][0], nxt, cx.ntok(max(c - 1, 0)));
         cur = nxt;
-        rcur = rnxt;
     }
+    cx.store_rows(sh, 2, ws.dDl + pci * Rec<D>::kRows, D, pdD, C);
+    cx.store_rows(sh, 3, ws.dUp + pci * Rec<D>::kRows, D, pdU, C);
+    cx.store_rows(sh, 4, a.dv + prow * D, p.H * D, pdv, pnt);
 }
 
 template <int D, int DT>
@@ -587,29 +689,36 @@ __global__ __launch_bounds__(kThreads, 2) void k_bchain(BwdProblem a, CbWs ws) {
     constexpr int NB = D / 16, MT = D / 64;
     __shared__ ChainShared sh;
     const Problem& p = a.p;
-    const int64_t nsl = a.nbh * NB;  // (head, 16-row slice) pairs per direction
-    const bool rev = blockIdx.x < nsl;
-    const int64_t idx = rev ? blockIdx.x : blockIdx.x - nsl;
+    // workgroups go to the eight XCDs in turn; the logical order (head,
+    // direction, slice) is laid over them so that consecutive logical
+    // indices, the 2 NB workgroups of a head that read the same chunk
+    // operands, share an XCD and its L2
+    const int64_t N = 2 * a.nbh * NB;
+    const int64_t lin = N % 8 == 0 ? (blockIdx.x % 8) * (N / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int64_t head = lin / (2 * NB);
+    const int rem = (int)(lin - head * 2 * NB);
+    const bool rev = rem < NB;
     ChainCtx<D, DT> cx{a, ws};
-    cx.bl = idx / NB;
-    cx.rho = (int)(idx - cx.bl * NB);
+    cx.bl = head;
+    cx.rho = rev ? rem : rem - NB;
     cx.r0 = 16 * cx.rho;
     cx.bh = a.bh0 + cx.bl;
     cx.b = cx.bh / p.H;
     cx.h = cx.bh - cx.b * p.H;
     const int tid = threadIdx.x;
+    cx.tid = tid;
     cx.w = tid >> 6;
     cx.l = tid & 63;
     cx.g4 = cx.l >> 4;
     cx.c16 = cx.l & 15;
     cx.NC = p.NC;
     // the slice's state rows as accumulator tiles of S^T: tile mi holds
-    // S[r0 + c16][16 (w MT + mi) + 4 g4 + r]
+    // S[r0 + c16][key_of(w, mi, 4 g4 + r)]
     f32x4 St[MT];
     const float* init = rev ? a.ds_out : p.s0;
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
-        St[mi] = init ? ld4f(init + ((cx.bh * D + cx.r0 + cx.c16) * D) + 16 * (cx.w * MT + mi) + 4 * cx.g4) : zero4();
+        St[mi] = init ? ld4f(init + ((cx.bh * D + cx.r0 + cx.c16) * D) + key_of<D>(cx.w, mi, 4 * cx.g4)) : zero4();
     if (p.NC > 0) {
         if (rev) chain_reverse<D, DT>(cx, sh, St);
         else chain_forward<D, DT>(cx, sh, St);
@@ -617,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bchain(BwdProblem a, CbWs ws) {
     if (rev && a.ds0) {
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi)
-            st4f(a.ds0 + ((cx.bh * D + cx.r0 + cx.c16) * D) + 16 * (cx.w * MT + mi) + 4 * cx.g4, St[mi]);
+            st4f(a.ds0 + ((cx.bh * D + cx.r0 + cx.c16) * D) + key_of<D>(cx.w, mi, 4 * cx.g4), St[mi]);
     }
 }
 
@@ -875,13 +984,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
         }
     }
     // K^T and Q^T fragments of the wave's value blocks, for the rest of dQ, dK
-    R4<DT> kf[MT][4], qf[MT][4];
+    R8<DT> kf[MT][2], qf[MT][2];
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kf[mi][i] = ldr<DT>(KTf, ((int64_t)((w * MT + mi) * 4 + i) * 64 + l) * 4);
-            qf[mi][i] = ldr<DT>(QTf, ((int64_t)((w * MT + mi) * 4 + i) * 64 + l) * 4);
+        for (int i = 0; i < 2; ++i) {
+            kf[mi][i] = ldr8<DT>(KTf, ((int64_t)((w * MT + mi) * 2 + i) * 64 + l) * 8);
+            qf[mi][i] = ldr8<DT>(QTf, ((int64_t)((w * MT + mi) * 2 + i) * 64 + l) * 8);
         }
     // boundary terms: q_t . dQ_S0, k_t . dK_S0, k_t . dK_dS (rows of the tiles)
 #pragma unroll
@@ -891,7 +1000,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int mi = 0; mi < MT; ++mi) {
-                const int t = 16 * tb + 4 * g4 + r, d = 16 * (w * MT + mi) + c16;
+                const int t = 16 * tb + 4 * g4 + r, d = key_col<D>(w * MT + mi, c16);
                 qv[r][mi] = gdn_ld<DT>(p.q, rowaddr(t) + d);
                 kv[r][mi] = gdn_ld<DT>(p.k, rowaddr(t) + d);
             }
@@ -931,22 +1040,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
             f32x4 q = aQ[tb][mi], kk = aK1[tb][mi] + aK2[tb][mi];
 #pragma unroll
             for (int jb = 0; jb <= tb; ++jb)
-                q = blk(ld4f(&sh.dPm[(16 * tb + c16) * LDA + 16 * jb + 4 * g4]), cvt<DT>(kf[mi][jb]), q);
+                q = blk(ld4f(&sh.dPm[(16 * tb + c16) * LDA + 16 * jb + 4 * g4]), cvt<DT>(kf[mi][jb >> 1].h[jb & 1]), q);
 #pragma unroll
             for (int sb = tb; sb < 4; ++sb) {
                 f32x4 at;
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) at[qq] = sh.dPm[(16 * sb + 4 * g4 + qq) * LDA + 16 * tb + c16];
-                kk = blk(at, cvt<DT>(qf[mi][sb]), kk);
+                kk = blk(at, cvt<DT>(qf[mi][sb >> 1].h[sb & 1]), kk);
             }
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib)
-                kk = blk(ld4f(&sh.W[(16 * tb + c16) * LDA + 16 * ib + 4 * g4]), cvt<DT>(kf[mi][ib]), kk);
+                kk = blk(ld4f(&sh.W[(16 * tb + c16) * LDA + 16 * ib + 4 * g4]), cvt<DT>(kf[mi][ib >> 1].h[ib & 1]), kk);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tb + 4 * g4 + r;
                 if (t < nt) {
-                    const int64_t o = (row0 + (int64_t)t * p.H) * D + 16 * db + c16;
+                    const int64_t o = (row0 + (int64_t)t * p.H) * D + key_col<D>(db, c16);
                     a.dq[o] = q[r];
                     a.dk[o] = kk[r];
                 }
@@ -1033,7 +1142,7 @@ static size_t chunked_bytes_per_head(int64_t T, int64_t D) {
     const size_t nc = (size_t)((T + C - 1) / C);
     const size_t nb = (size_t)(D / 16);
     const size_t per_chunk = sizeof(float) * (4 * (size_t)C * C + 2 * nb * 4 * 64 * 4 + 2 * nb * nb * 64 * 4 +
-                                              4 * (size_t)C * D);
+                                              5 * (size_t)C * D + (size_t)D * D);
     return nc * per_chunk;
 }
 constexpr size_t kChunkedWsCap = size_t(8) << 30;
@@ -1044,8 +1153,8 @@ static int64_t chunked_heads_per_launch(int64_t B, int64_t T, int64_t H, int64_t
 }
 
 size_t chunked_backward_workspace(int64_t B, int64_t T, int64_t H, int64_t D) {
-    // twelve pieces, each 256-byte aligned
-    return chunked_bytes_per_head(T, D) * (size_t)chunked_heads_per_launch(B, T, H, D) + 12 * 256;
+    // fourteen pieces, each 256-byte aligned
+    return chunked_bytes_per_head(T, D) * (size_t)chunked_heads_per_launch(B, T, H, D) + 14 * 256;
 }
 
 hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t st) {
@@ -1055,13 +1164,14 @@ hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t
     const Problem& p = a0.p;
     const int64_t D = p.dk, BH = p.B * p.H;
     if (p.T == 0) {
-        // dS_0 = dS_T: the reverse chain with no chunks
+        // dS_0 = dS_T: the chain kernel with no chunks (its whole grid, both
+        // directions, as the block order assumes; the forward half does nothing)
         BwdProblem g = a0;
         g.bh0 = 0;
         g.nbh = BH;
         CbWs ws{};
         hipLaunchKernelGGL((D == 64 ? k_bchain<64, GDN_BF16> : k_bchain<128, GDN_BF16>),
-                           dim3((unsigned)(BH * (D / 16))), dim3(kThreads), 0, st, g, ws);
+                           dim3((unsigned)(2 * BH * (D / 16))), dim3(kThreads), 0, st, g, ws);
         return hipGetLastError();
     }
     const int64_t gsz = chunked_heads_per_launch(p.B, p.T, p.H, D);
@@ -1087,6 +1197,8 @@ hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t
     ws.Dl = take(nch * C * D);
     ws.dDl = take(nch * C * D);
     ws.dUp = take(nch * C * D);
+    ws.Ef = take(nch * C * D);
+    ws.Hf = take(nch * D * D);
     for (int64_t bh0 = 0; bh0 < BH; bh0 += gsz) {
         BwdProblem g = a0;
         g.bh0 = bh0;
