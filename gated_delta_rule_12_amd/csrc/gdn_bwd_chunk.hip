@@ -206,22 +206,32 @@ struct CbWs {
 };
 
 // ---------------------------------------------------------------------------
-// k_bprep: T, T^T, P^T and the K^T, Q^T fragments of one chunk
+// k_bprep: per chunk T, T^T, P^T, Atilde^T, the K^T and Q^T fragments, and
+// the reverse chain's state-independent terms E = scale P^T dO and
+// H = scale Q^T diag(gamma) dO as accumulator tiles
 // ---------------------------------------------------------------------------
+// Work of wave w: the Gram row block m = w (tiles (w, nb), nb <= w) and the
+// Q K^T column block jb = w (tiles (tb, w), tb >= w), five tiles either way;
+// the P tiles it holds are the A operands of E's block row w as they stand
+// (a lane holds P[16 tb + 4 g + r][16 w + c] = P^T[16 w + c][16 tb + 4 g + r]).
+// LDS: the K and Q rows, later dL/d out over them; the UT system.
 template <int D, int DT>
-__global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
+__global__ __launch_bounds__(kThreads, 2) void k_bprep(BwdProblem a, CbWs ws) {
     using E = std::conditional_t<DT == GDN_BF16, uint16_t, float>;
-    constexpr int NB = D / 16;
+    constexpr int NB = D / 16, MT = D / 64;
     constexpr int LDK = D + (DT == GDN_BF16 ? 8 : 4);
+    constexpr int LDD = D + 4;
     constexpr int EP = 16 / sizeof(E);  // elements per 16-byte piece
     constexpr int PPR = D / EP;         // pieces per row
+    constexpr int KQB = 2 * C * LDK * (int)sizeof(E);
+    static_assert(C * LDD * 4 <= KQB, "dL/d out fits over the K and Q rows");
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
-    __shared__ __attribute__((aligned(16))) E Ks[C * LDK];
-    __shared__ __attribute__((aligned(16))) E Qs[C * LDK];
-    __shared__ __attribute__((aligned(16))) float PTs[C * LDA];        // P^T
-    __shared__ __attribute__((aligned(16))) float dOs[C * (D + 4)];    // dL/d out rows
+    __shared__ __attribute__((aligned(16))) unsigned char kq[KQB];
     __shared__ float Pscr[4][16 * 17];
-    __shared__ float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C], ggam[C];
+    __shared__ __attribute__((aligned(16))) float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C], ggam[C];
+    E* Ks = reinterpret_cast<E*>(kq);
+    E* Qs = Ks + C * LDK;
+    float* dOs = reinterpret_cast<float*>(kq);
 
     const Problem& p = a.p;
     const int64_t ci = blockIdx.x;
@@ -230,6 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
     const int64_t bh = a.bh0 + bl, b = bh / p.H, h = bh - b * p.H;
     const int64_t t0 = (int64_t)c * C;
     const int nt = (int)min<int64_t>(C, p.T - t0);
+    const int64_t row0 = (b * p.T + t0) * p.H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
 
     // K and Q rows into LDS (rows past the sequence end zero)
@@ -237,23 +248,15 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
         const int e = tid + kThreads * i, t = e / PPR, pc = e % PPR;
-        const int64_t src = ((b * p.T + t0 + min(t, nt - 1)) * p.H + h) * D + pc * EP;
+        const int64_t src = (row0 + (int64_t)min(t, nt - 1) * p.H) * D + pc * EP;
         u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(p.k) + src);
         u32x4 qv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(p.q) + src);
         if (t >= nt) kv = qv = u32x4{0, 0, 0, 0};
         *reinterpret_cast<u32x4*>(&Ks[t * LDK + pc * EP]) = kv;
         *reinterpret_cast<u32x4*>(&Qs[t * LDK + pc * EP]) = qv;
     }
-    constexpr int LDD = D + 4, OP = C * (D / 4) / kThreads;
-#pragma unroll
-    for (int i = 0; i < OP; ++i) {
-        const int e = tid + kThreads * i, t = e / (D / 4), pc = e % (D / 4);
-        f32x4 x = ld4f(a.dout + ((b * p.T + t0 + min(t, nt - 1)) * p.H + h) * D + 4 * pc);
-        if (t >= nt) x = zero4();
-        st4f(&dOs[t * LDD + 4 * pc], x);
-    }
     if (w == 0) {
-        const Gate g = chunk_gate(p, (b * p.T + t0) * p.H + h, nt, l);
+        const Gate g = chunk_gate(p, row0, nt, l);
         ghi[l] = g.hi;
         glo[l] = g.lo;
         gphi[l] = g.phi;
@@ -267,103 +270,48 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
         if constexpr (DT == GDN_BF16) return ld4in<DT>(X, t * LDK + d0);
         else return ld4f(X + t * LDK + d0);
     };
-    // Gram blocks (m, nb) and Q K^T blocks, nb <= m: 20 jobs over 4 waves
-    for (int job = w; job < 20; job += 4) {
-        const int kind = job / 10, m = blk_m(job % 10), nb = blk_n(job % 10);
-        const E* X = kind == 0 ? Ks : Qs;
+    // Gram row block m = w: A_tj = beta_t Atilde_tj, Atilde_tj = e^{l'_t - l_j}
+    // k_t.k_j (j < t), Atilde^T[j][t] to the workspace, A in the inverse's layout
+    for (int nb = 0; nb <= w; ++nb) {
+        const int m = w;
         f32x4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
-            acc = blk(row4(X, 16 * m + c16, 16 * kb + 4 * g4), row4(Ks, 16 * nb + c16, 16 * kb + 4 * g4), acc);
+            acc = blk(row4(Ks, 16 * m + c16, 16 * kb + 4 * g4), row4(Ks, 16 * nb + c16, 16 * kb + 4 * g4), acc);
         const int j = 16 * nb + c16;
-        if (kind == 0) {
-            // Atilde_tj = e^{l'_t - l_j} k_t.k_j (j < t), stored as Atilde^T[j][t];
-            // A = diag(beta) Atilde in the inverse's layout
-            f32x4 av, tv;
+        f32x4 av, tv;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * m + 4 * g4 + r;
-                tv[r] = j < t ? ratio(gphi[t], gplo[t], ghi[j], glo[j]) * acc[r] : 0.f;
-                av[r] = gbeta[t] * tv[r];
-            }
-            st4f(ws.AtT + ci * Rec<D>::kTile + j * C + 16 * m + 4 * g4, tv);
-            if (nb < m) {
-                st4f(&AT[j * LDA + 16 * m + 4 * g4], av);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) AT[(16 * m + 4 * g4 + r) * LDA + j] = av[r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * m + 4 * g4 + r;
+            tv[r] = j < t ? ratio(gphi[t], gplo[t], ghi[j], glo[j]) * acc[r] : 0.f;
+            av[r] = gbeta[t] * tv[r];
+        }
+        st4f(ws.AtT + ci * Rec<D>::kTile + j * C + 16 * m + 4 * g4, tv);
+        if (nb < m) {
+            st4f(&AT[j * LDA + 16 * m + 4 * g4], av);
         } else {
-            // P_tj = e^{l_t - l_j} q_t.k_j (j <= t), stored as P^T[j][t]
-            f32x4 pv;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * m + 4 * g4 + r;
-                pv[r] = j <= t ? ratio(ghi[t], glo[t], ghi[j], glo[j]) * acc[r] : 0.f;
-            }
-            st4f(ws.PT + ci * Rec<D>::kTile + j * C + 16 * m + 4 * g4, pv);
-            st4f(&PTs[j * LDA + 16 * m + 4 * g4], pv);
+            for (int r = 0; r < 4; ++r) AT[(16 * m + 4 * g4 + r) * LDA + j] = av[r];
         }
     }
-    __syncthreads();
-    // E = scale P^T dO (value blocks vb = w MT + mi, every token block jb) and
-    // H = scale Q^T diag(gamma) dO (key blocks m = w MT + mi, every vb), the
-    // reverse chain's state-independent terms, as accumulator tiles
-    {
-        constexpr int MT = D / 64;
-        f32x4 qa[MT][4];  // A operand Q^T[16 m + c16][16 tb + 4 g4 + q]
+    // Q K^T column block jb = w: P_tj = e^{l_t - l_j} q_t.k_j (j <= t), kept
+    // (pk[tb], tb >= w) and stored as P^T[j][t]
+    f32x4 pk[4];
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
+    for (int tb = 0; tb < 4; ++tb) {
+        pk[tb] = zero4();
+        if (tb < w) continue;
+        f32x4 acc = zero4();
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+        for (int kb = 0; kb < NB; ++kb)
+            acc = blk(row4(Qs, 16 * tb + c16, 16 * kb + 4 * g4), row4(Ks, 16 * w + c16, 16 * kb + 4 * g4), acc);
+        const int j = 16 * w + c16;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const E x = Qs[(16 * tb + 4 * g4 + q) * LDK + key_of<D>(w, mi, c16)];
-                    if constexpr (DT == GDN_BF16) qa[mi][tb][q] = gdn_bf16_to_f32(x);
-                    else qa[mi][tb][q] = x;
-                }
-        for (int vb = 0; vb < NB; ++vb) {
-            f32x4 db[4], gb[4];  // B operands dO[16 tb + 4 g4 + q][16 vb + c16], and scale gamma_t times it
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) db[tb][q] = dOs[(16 * tb + 4 * g4 + q) * LDD + 16 * vb + c16];
-                gb[tb] = p.scale * *reinterpret_cast<const f32x4*>(&ggam[16 * tb + 4 * g4]) * db[tb];
-            }
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) acc = blk(qa[mi][tb], gb[tb], acc);
-                st4f(ws.Hf + ci * Rec<D>::kHf + ((size_t)(vb * NB + w * MT + mi) * 64 + l) * 4, acc);
-            }
-            if (vb / MT == w) {
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    f32x4 acc = zero4();
-#pragma unroll
-                    for (int tb = 0; tb < 4; ++tb)
-                        if (tb >= jb) acc = blk(ld4f(&PTs[(16 * jb + c16) * LDA + 16 * tb + 4 * g4]), db[tb], acc);
-                    st4f(ws.Ef + ci * Rec<D>::kRows + ((size_t)(vb * 4 + jb) * 64 + l) * 4, p.scale * acc);
-                }
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tb + 4 * g4 + r;
+            pk[tb][r] = j <= t ? ratio(ghi[t], glo[t], ghi[j], glo[j]) * acc[r] : 0.f;
         }
-    }
-    ut_inverse_lds(AT, Pscr[w]);
-
-    // T and T^T, row-major, zero above (below) the diagonal
-    float* Tg = ws.T + ci * Rec<D>::kTile;
-    float* TTg = ws.TT + ci * Rec<D>::kTile;
-    for (int e = tid; e < C * C / 4; e += kThreads) {
-        const int r0 = e >> 4, c0 = (e & 15) * 4;
-        f32x4 x, y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = c0 + i <= r0 ? AT[r0 * LDA + c0 + i] : 0.f;   // T[r0][c0 + i]
-            y[i] = r0 <= c0 + i ? AT[(c0 + i) * LDA + r0] : 0.f; // T^T[r0][c0 + i] = T[c0 + i][r0]
-        }
-        st4f(Tg + r0 * C + c0, x);
-        st4f(TTg + r0 * C + c0, y);
+        st4f(ws.PT + ci * Rec<D>::kTile + j * C + 16 * tb + 4 * g4, pk[tb]);
     }
     // K^T and Q^T fragments (input-typed), two token blocks a lane
     for (int f = tid; f < NB * 2 * 64; f += kThreads) {
@@ -394,6 +342,67 @@ __global__ __launch_bounds__(kThreads) void k_bprep(BwdProblem a, CbWs ws) {
             st4f(qd + 4, f32x4{qx[4], qx[5], qx[6], qx[7]});
         }
     }
+    // H's A operand Q^T[key_of(w, mi, c16)][16 tb + 4 g4 + q], before dL/d out
+    // takes the Q rows' place
+    f32x4 qa[MT][4];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const E x = Qs[(16 * tb + 4 * g4 + q) * LDK + key_of<D>(w, mi, c16)];
+                if constexpr (DT == GDN_BF16) qa[mi][tb][q] = gdn_bf16_to_f32(x);
+                else qa[mi][tb][q] = x;
+            }
+    __syncthreads();  // the K and Q rows are dead
+    constexpr int OP = C * (D / 4) / kThreads;
+#pragma unroll
+    for (int i = 0; i < OP; ++i) {
+        const int e = tid + kThreads * i, t = e / (D / 4), pc = e % (D / 4);
+        f32x4 x = ld4f(a.dout + (row0 + (int64_t)min(t, nt - 1) * p.H) * D + 4 * pc);
+        if (t >= nt) x = zero4();
+        st4f(&dOs[t * LDD + 4 * pc], x);
+    }
+    __syncthreads();
+    // E block row w (all value blocks) and H of the wave's key tiles
+    for (int vb = 0; vb < NB; ++vb) {
+        f32x4 db[4], gb[4];  // B operands dO[16 tb + 4 g4 + q][16 vb + c16], and scale gamma_t times it
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) db[tb][q] = dOs[(16 * tb + 4 * g4 + q) * LDD + 16 * vb + c16];
+            gb[tb] = p.scale * *reinterpret_cast<const f32x4*>(&ggam[16 * tb + 4 * g4]) * db[tb];
+        }
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc = blk(qa[mi][tb], gb[tb], acc);
+            st4f(ws.Hf + ci * Rec<D>::kHf + ((size_t)(vb * NB + w * MT + mi) * 64 + l) * 4, acc);
+        }
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+            if (tb >= w) acc = blk(pk[tb], db[tb], acc);
+        st4f(ws.Ef + ci * Rec<D>::kRows + ((size_t)(vb * 4 + w) * 64 + l) * 4, p.scale * acc);
+    }
+    ut_inverse_lds(AT, Pscr[w]);
+
+    // T and T^T, row-major, zero above (below) the diagonal
+    float* Tg = ws.T + ci * Rec<D>::kTile;
+    float* TTg = ws.TT + ci * Rec<D>::kTile;
+    for (int e = tid; e < C * C / 4; e += kThreads) {
+        const int r0 = e >> 4, c0 = (e & 15) * 4;
+        f32x4 x, y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = c0 + i <= r0 ? AT[r0 * LDA + c0 + i] : 0.f;   // T[r0][c0 + i]
+            y[i] = r0 <= c0 + i ? AT[(c0 + i) * LDA + r0] : 0.f; // T^T[r0][c0 + i] = T[c0 + i][r0]
+        }
+        st4f(Tg + r0 * C + c0, x);
+        st4f(TTg + r0 * C + c0, y);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -420,25 +429,30 @@ struct RowF {
 };
 
 // Operands of a chain step, all fetched one chunk ahead (the next chunk's
-// while the current one computes); rows past the sequence end are read at
-// the last real row and zeroed at use.  A chunk's workspace stores are
-// issued at the start of the next chunk, so that neither they nor the
-// fetches are waited for before a whole step has passed.  Stores go out in
-// 16-byte pieces after a transpose through the wave's own LDS tiles.
+// while the current one computes), the gates and the V slice two ahead (they
+// are turned into LDS rows at the end of the step before their chunk's);
+// rows past the sequence end are read at the last real row and zeroed at
+// use.  A chunk's workspace stores are issued at the start of the next chunk.
+// Nothing a step waits for was fetched in that step: vector memory results
+// count down in issue order, so waiting for a fresh fetch would wait for the
+// whole prefetch.  Stores go out in 16-byte pieces after a transpose through
+// the wave's own LDS tiles.
 template <int D, int DT>
 struct FwdIn {
     static constexpr int MT = D / 64;
     R4<DT> kx[4][MT];    // K[16 at + c16][key_of(w, mi, 4 g4 ..)]: the K S^T operand
-    float al, be;        // lane t: alpha_t, beta_t
-    R4<DT> vr;           // V[t][r0 + 4 p ..] of this thread's (t, p) = (tid / 4, tid % 4)
     f32x4 tr[4];         // T[16 w + c16][16 jb + 4 g4 ..]
     R8<DT> kt[MT][2];    // K^T fragments of the wave's key tiles, token blocks in pairs
+};
+template <int DT>
+struct GateIn {
+    float al, be;        // lane t: alpha_t, beta_t
+    R4<DT> vr;           // forward: V[t][r0 + 4 p ..] of this thread's (t, p) = (tid / 4, tid % 4)
 };
 template <int D, int DT>
 struct RevIn {
     static constexpr int MT = D / 64;
     R4<DT> kx[4][MT];
-    float al, be;
     f32x4 ef;            // E tile w of the slice
     f32x4 hf[MT];        // H tiles of the wave's key tiles
     f32x4 tt[4];         // T^T[16 w + c16][16 jb + 4 g4 ..]
@@ -455,14 +469,21 @@ struct ChainCtx {
     __device__ int64_t row0(int c) const { return (b * a.p.T + (int64_t)c * C) * a.p.H + h; }
     __device__ int ntok(int c) const { return (int)min<int64_t>(C, a.p.T - (int64_t)c * C); }
     __device__ int64_t cidx(int c) const { return bl * NC + c; }
+    // gates (and, forward, the V slice) of chunk c, clamped to a real chunk
+    __device__ void load_gate(GateIn<DT>& x, int c, bool fwd) const {
+        c = min(max(c, 0), NC - 1);
+        const int64_t r = row0(c);
+        const int nt = ntok(c);
+        const int64_t rl = r + (int64_t)min(l, nt - 1) * a.p.H;
+        x.al = a.p.alpha[rl];
+        x.be = a.p.beta[rl];
+        if (fwd) x.vr = ldr<DT>(a.p.v, (r + (int64_t)min(tid >> 2, nt - 1) * a.p.H) * D + r0 + 4 * (tid & 3));
+    }
     template <class In>
     __device__ void load_common(In& x, int c) const {
         const int64_t r = row0(c);
         const int nt = ntok(c);
         const int64_t ci = cidx(c);
-        const int64_t rl = r + (int64_t)min(l, nt - 1) * a.p.H;
-        x.al = a.p.alpha[rl];
-        x.be = a.p.beta[rl];
 #pragma unroll
         for (int at = 0; at < 4; ++at) {
             const int64_t o = (r + (int64_t)min(16 * at + c16, nt - 1) * a.p.H) * D + key_of<D>(w, 0, 4 * g4);
@@ -483,9 +504,7 @@ struct ChainCtx {
     __device__ void load(FwdIn<D, DT>& x, int c) const {
         c = min(max(c, 0), NC - 1);
         load_common(x, c);
-        const int64_t r = row0(c), ci = cidx(c);
-        const int nt = ntok(c);
-        x.vr = ldr<DT>(a.p.v, (r + (int64_t)min(tid >> 2, nt - 1) * a.p.H) * D + r0 + 4 * (tid & 3));
+        const int64_t ci = cidx(c);
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) x.tr[jb] = ld4f(ws.T + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
     }
@@ -539,8 +558,7 @@ struct ChainCtx {
         const f32x4 v = *reinterpret_cast<const f32x4*>(&X[i][4 * j]);
         if (16 * w + i < nvalid) st4f(base + (int64_t)(16 * w + i) * ld + r0 + 4 * j, v);
     }
-    template <class In>
-    __device__ void gates_to_lds(float* gw, const In& x, int nt) const {
+    __device__ void gates_to_lds(float* gw, const GateIn<DT>& x, int nt) const {
         const Gate g = gate_from(x.al, x.be, nt, a.p.order, l);
         const float hC = __shfl(g.hi, C - 1, 64), lC = __shfl(g.lo, C - 1, 64);
         gw[kGhi * C + l] = g.hi;
@@ -554,7 +572,7 @@ struct ChainCtx {
     }
     // the slice of V (this thread's four values of one token) into LDS,
     // transposed to [value][token]
-    __device__ void v_to_lds(ChainShared& sh, int buf, const FwdIn<D, DT>& x, int nt) const {
+    __device__ void v_to_lds(ChainShared& sh, int buf, const GateIn<DT>& x, int nt) const {
         const int t = tid >> 2, j = tid & 3;
         const f32x4 v = t < nt ? cvt<DT>(x.vr) : zero4();
 #pragma unroll
@@ -567,19 +585,28 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     constexpr int MT = D / 64;
     const CbWs& ws = cx.ws;
     const int w = cx.w, l = cx.l, g4 = cx.g4, c16 = cx.c16;
-    FwdIn<D, DT> cur, nxt;
-    cx.load(cur, 0);
-    cx.gates_to_lds(&sh.g[w][0][0][0], cur, cx.ntok(0));
-    cx.v_to_lds(sh, 0, cur, cx.ntok(0));
+    // two operand sets and two gate sets that trade roles every step (no
+    // copies between them, so a step waits only for the previous step's
+    // fetches)
+    FwdIn<D, DT> xa, xb;
+    GateIn<DT> ga, gb;
+    cx.load(xa, 0);
+    cx.load_gate(ga, 0, true);
+    cx.gates_to_lds(&sh.g[w][0][0][0], ga, cx.ntok(0));
+    cx.v_to_lds(sh, 0, ga, cx.ntok(0));
+    cx.load_gate(ga, 1, true);
     // the previous chunk's U and Delta tiles, stored at the next chunk's start
     // (chunk 0's slots first take zeros, overwritten in order by the same lane)
     f32x4 pU = zero4(), pD = zero4();
     int64_t pci = cx.cidx(0);
-    for (int c = 0; c < cx.NC; ++c) {
+    // chunk c from cur; fetches chunk c + 1 into nxt and the gates of chunk
+    // c + 2 into g2; turns g1 (chunk c + 1) into LDS rows at the end
+    auto step = [&](int c, const FwdIn<D, DT>& cur, FwdIn<D, DT>& nxt, const GateIn<DT>& g1, GateIn<DT>& g2) {
         const RowF rf{&sh.g[w][c & 1][0][0]};
         const int64_t ci = cx.cidx(c);
         const int nt = cx.ntok(c);
         cx.load(nxt, c + 1);
+        cx.load_gate(g2, c + 2, true);
         cx.store_rows(sh, 2, ws.U + pci * Rec<D>::kRows, D, pU, C);
         cx.store_rows(sh, 3, ws.Dl + pci * Rec<D>::kRows, D, pD, C);
         cx.store_state(sh, ws.Sf + ci * Rec<D>::kState, St);
@@ -613,10 +640,15 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
         // (every wave is past this chunk's first barrier, the last reader of
         // the V buffer written here)
         const int nn = cx.ntok(min(c + 1, cx.NC - 1));
-        cx.gates_to_lds(&sh.g[w][(c + 1) & 1][0][0], nxt, nn);
-        cx.v_to_lds(sh, (c + 1) & 1, nxt, nn);
-        cur = nxt;
+        cx.gates_to_lds(&sh.g[w][(c + 1) & 1][0][0], g1, nn);
+        cx.v_to_lds(sh, (c + 1) & 1, g1, nn);
+    };
+    int c = 0;
+    for (; c + 1 < cx.NC; c += 2) {
+        step(c, xa, xb, ga, gb);
+        step(c + 1, xb, xa, gb, ga);
     }
+    if (c < cx.NC) step(c, xa, xb, ga, gb);
     cx.store_rows(sh, 2, ws.U + pci * Rec<D>::kRows, D, pU, C);
     cx.store_rows(sh, 3, ws.Dl + pci * Rec<D>::kRows, D, pD, C);
 }
@@ -628,19 +660,25 @@ __device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     const Problem& p = a.p;
     const CbWs& ws = cx.ws;
     const int w = cx.w, l = cx.l, g4 = cx.g4;
-    RevIn<D, DT> cur, nxt;
-    cx.load(cur, cx.NC - 1);
-    cx.gates_to_lds(&sh.g[w][(cx.NC - 1) & 1][0][0], cur, cx.ntok(cx.NC - 1));
+    RevIn<D, DT> xa, xb;
+    GateIn<DT> ga, gb;
+    cx.load(xa, cx.NC - 1);
+    cx.load_gate(ga, cx.NC - 1, false);
+    cx.gates_to_lds(&sh.g[w][(cx.NC - 1) & 1][0][0], ga, cx.ntok(cx.NC - 1));
+    cx.load_gate(ga, cx.NC - 2, false);
     // the previous step's dDelta, dU' and dv tiles, stored at the next step's
     // start (the first step's slots first take zeros, then the real values)
     f32x4 pdD = zero4(), pdU = zero4(), pdv = zero4();
     int64_t pci = cx.cidx(cx.NC - 1), prow = cx.row0(cx.NC - 1);
     int pnt = 0;
-    for (int c = cx.NC - 1; c >= 0; --c) {
+    // chunk c from cur; fetches chunk c - 1 into nxt and the gates of chunk
+    // c - 2 into g2; turns g1 (chunk c - 1) into LDS rows at the end
+    auto step = [&](int c, const RevIn<D, DT>& cur, RevIn<D, DT>& nxt, const GateIn<DT>& g1, GateIn<DT>& g2) {
         const RowF rf{&sh.g[w][c & 1][0][0]};
         const int64_t ci = cx.cidx(c);
         const int nt = cx.ntok(c);
         cx.load(nxt, c - 1);
+        cx.load_gate(g2, c - 2, false);
         cx.store_rows(sh, 2, ws.dDl + pci * Rec<D>::kRows, D, pdD, C);
         cx.store_rows(sh, 3, ws.dUp + pci * Rec<D>::kRows, D, pdU, C);
         cx.store_rows(sh, 4, a.dv + prow * D, p.H * D, pdv, pnt);
@@ -676,9 +714,14 @@ __device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
             St[mi] = acc;
         }
         // the next chunk's gate rows while the update multiplies
-        cx.gates_to_lds(&sh.g[w][(c + 1) & 1][0][0], nxt, cx.ntok(max(c - 1, 0)));
-        cur = nxt;
+        cx.gates_to_lds(&sh.g[w][(c + 1) & 1][0][0], g1, cx.ntok(max(c - 1, 0)));
+    };
+    int c = cx.NC - 1;
+    for (; c >= 1; c -= 2) {
+        step(c, xa, xb, ga, gb);
+        step(c - 1, xb, xa, gb, ga);
     }
+    if (c == 0) step(0, xa, xb, ga, gb);
     cx.store_rows(sh, 2, ws.dDl + pci * Rec<D>::kRows, D, pdD, C);
     cx.store_rows(sh, 3, ws.dUp + pci * Rec<D>::kRows, D, pdU, C);
     cx.store_rows(sh, 4, a.dv + prow * D, p.H * D, pdv, pnt);
