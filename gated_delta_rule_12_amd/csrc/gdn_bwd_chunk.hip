@@ -1035,27 +1035,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
             kf[mi][i] = ldr8<DT>(KTf, ((int64_t)((w * MT + mi) * 2 + i) * 64 + l) * 8);
             qf[mi][i] = ldr8<DT>(QTf, ((int64_t)((w * MT + mi) * 2 + i) * 64 + l) * 8);
         }
-    // boundary terms: q_t . dQ_S0, k_t . dK_S0, k_t . dK_dS (rows of the tiles)
+    // boundary terms: q_t . dQ_S0, k_t . dK_S0, k_t . dK_dS (rows of the
+    // tiles; the Q^T and K^T fragments hold q and k in the accumulator layout:
+    // Q[16 tb + 4 g4 + r][key_col(db, c16)] in element r)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-        float qv[4][MT], kv[4][MT];
+        f32x4 qv[MT], kv[MT];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                const int t = 16 * tb + 4 * g4 + r, d = key_col<D>(w * MT + mi, c16);
-                qv[r][mi] = gdn_ld<DT>(p.q, rowaddr(t) + d);
-                kv[r][mi] = gdn_ld<DT>(p.k, rowaddr(t) + d);
-            }
+        for (int mi = 0; mi < MT; ++mi) {
+            qv[mi] = cvt<DT>(qf[mi][tb >> 1].h[tb & 1]);
+            kv[mi] = cvt<DT>(kf[mi][tb >> 1].h[tb & 1]);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * tb + 4 * g4 + r;
             float so = 0.f, sx = 0.f, sr = 0.f;
 #pragma unroll
             for (int mi = 0; mi < MT; ++mi) {
-                so += qv[r][mi] * aQ[tb][mi][r];
-                sx += kv[r][mi] * aK1[tb][mi][r];
-                sr += kv[r][mi] * aK2[tb][mi][r];
+                so += qv[mi][r] * aQ[tb][mi][r];
+                sx += kv[mi][r] * aK1[tb][mi][r];
+                sr += kv[mi][r] * aK2[tb][mi][r];
             }
             // (rows past the sequence end: their accumulators are zero or unused)
             so = row_sum<16>(t < nt ? so : 0.f);
