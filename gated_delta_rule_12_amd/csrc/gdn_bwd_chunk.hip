@@ -178,6 +178,10 @@ __device__ __forceinline__ Gate chunk_gate(const Problem& p, int64_t row0, int n
     return gate_from(p.alpha[r], p.beta[r], nt, p.order, lane);
 }
 
+// Rows of a chunk's token factors (lane t: token t): the gate prefix pair,
+// the prediction prefix pair, beta, gamma_t, gamma'_t and R_t = gamma_C / gamma_t.
+enum { kGhi, kGlo, kGphi, kGplo, kGbeta, kGgam, kGgamp, kGR };
+
 // e^{(hb - ha) + (lb - la)}
 __device__ __forceinline__ float ratio(float hb, float lb, float ha, float la) {
     return __expf((hb - ha) + (lb - la));
@@ -194,6 +198,7 @@ struct Rec {
     static constexpr size_t kState = (size_t)NB * NB * 64 * 4;
     static constexpr size_t kRows = (size_t)C * D;          // U, Delta, dDelta, dU'; E fragments
     static constexpr size_t kHf = (size_t)D * D;            // H fragments
+    static constexpr size_t kGr = 8 * (size_t)C;            // gate rows
 };
 
 struct CbWs {
@@ -203,6 +208,7 @@ struct CbWs {
     float *U, *Dl, *dDl, *dUp; // [chunk][C][D]
     float *Ef, *Hf;            // [chunk][vb][jb or m][lane] of f32x4: E = scale P^T dO,
                                // H = scale Q^T diag(gamma) dO as accumulator tiles
+    float* Gr;                 // [chunk][8][C]: the chunk's gate rows (kG*)
 };
 
 // ---------------------------------------------------------------------------
@@ -263,6 +269,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_bprep(BwdProblem a, CbWs ws) {
         gplo[l] = g.plo;
         gbeta[l] = g.beta;
         ggam[l] = __expf(g.hi + g.lo);
+        // the chain kernel's gate rows
+        const float hC = __shfl(g.hi, C - 1, 64), lC = __shfl(g.lo, C - 1, 64);
+        float* gr = ws.Gr + ci * Rec<D>::kGr;
+        gr[kGhi * C + l] = g.hi;
+        gr[kGlo * C + l] = g.lo;
+        gr[kGphi * C + l] = g.phi;
+        gr[kGplo * C + l] = g.plo;
+        gr[kGbeta * C + l] = g.beta;
+        gr[kGgam * C + l] = __expf(g.hi + g.lo);
+        gr[kGgamp * C + l] = __expf(g.phi + g.plo);
+        gr[kGR * C + l] = ratio(hC, lC, g.hi, g.lo);
     }
     __syncthreads();
 
@@ -415,12 +432,11 @@ struct ChainShared {
     f32x4 xch2[4][64];    // reverse: -gamma' beta dU'
     float vs[2][16][C + 4];      // forward: V of the slice, [chunk parity][value][token]
     float tp[4][5][16][20];      // per wave: 16 x 16 tiles being transposed for stores
-    float g[4][2][8][C];  // [wave][chunk parity][row kG*][token]
+    float g[2][8][C];     // [chunk parity][row kG*][token]: gate rows
 };
 
-// Token-row factors of a chunk, formed once per wave (lane t: token t) in
-// LDS: the gate prefix pair, beta, gamma_t, gamma'_t and R_t = gamma_C / gamma_t.
-enum { kGhi, kGlo, kGphi, kGplo, kGbeta, kGgam, kGgamp, kGR };
+// A chunk's gate rows in LDS (written by the preparation kernel, staged
+// by the workgroup).
 struct RowF {
     const float* g;  // [8][C]
     // rows of four consecutive tokens t0 .. t0 + 3
@@ -446,7 +462,7 @@ struct FwdIn {
 };
 template <int DT>
 struct GateIn {
-    float al, be;        // lane t: alpha_t, beta_t
+    f32x2 gr;            // gate rows: row tid / 32, tokens 2 (tid % 32) ..
     R4<DT> vr;           // forward: V[t][r0 + 4 p ..] of this thread's (t, p) = (tid / 4, tid % 4)
 };
 template <int D, int DT>
@@ -469,14 +485,12 @@ struct ChainCtx {
     __device__ int64_t row0(int c) const { return (b * a.p.T + (int64_t)c * C) * a.p.H + h; }
     __device__ int ntok(int c) const { return (int)min<int64_t>(C, a.p.T - (int64_t)c * C); }
     __device__ int64_t cidx(int c) const { return bl * NC + c; }
-    // gates (and, forward, the V slice) of chunk c, clamped to a real chunk
+    // gate rows (and, forward, the V slice) of chunk c, clamped to a real chunk
     __device__ void load_gate(GateIn<DT>& x, int c, bool fwd) const {
         c = min(max(c, 0), NC - 1);
         const int64_t r = row0(c);
         const int nt = ntok(c);
-        const int64_t rl = r + (int64_t)min(l, nt - 1) * a.p.H;
-        x.al = a.p.alpha[rl];
-        x.be = a.p.beta[rl];
+        x.gr = *reinterpret_cast<const f32x2*>(ws.Gr + cidx(c) * Rec<D>::kGr + 2 * tid);
         if (fwd) x.vr = ldr<DT>(a.p.v, (r + (int64_t)min(tid >> 2, nt - 1) * a.p.H) * D + r0 + 4 * (tid & 3));
     }
     template <class In>
@@ -558,17 +572,9 @@ struct ChainCtx {
         const f32x4 v = *reinterpret_cast<const f32x4*>(&X[i][4 * j]);
         if (16 * w + i < nvalid) st4f(base + (int64_t)(16 * w + i) * ld + r0 + 4 * j, v);
     }
-    __device__ void gates_to_lds(float* gw, const GateIn<DT>& x, int nt) const {
-        const Gate g = gate_from(x.al, x.be, nt, a.p.order, l);
-        const float hC = __shfl(g.hi, C - 1, 64), lC = __shfl(g.lo, C - 1, 64);
-        gw[kGhi * C + l] = g.hi;
-        gw[kGlo * C + l] = g.lo;
-        gw[kGphi * C + l] = g.phi;
-        gw[kGplo * C + l] = g.plo;
-        gw[kGbeta * C + l] = g.beta;
-        gw[kGgam * C + l] = __expf(g.hi + g.lo);
-        gw[kGgamp * C + l] = __expf(g.phi + g.plo);
-        gw[kGR * C + l] = ratio(hC, lC, g.hi, g.lo);
+    // this thread's two gate-row entries into a parity's LDS rows
+    __device__ void gates_to_lds(float* gw, const GateIn<DT>& x) const {
+        *reinterpret_cast<f32x2*>(gw + 2 * tid) = x.gr;
     }
     // the slice of V (this thread's four values of one token) into LDS,
     // transposed to [value][token]
@@ -592,7 +598,7 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     GateIn<DT> ga, gb;
     cx.load(xa, 0);
     cx.load_gate(ga, 0, true);
-    cx.gates_to_lds(&sh.g[w][0][0][0], ga, cx.ntok(0));
+    cx.gates_to_lds(&sh.g[0][0][0], ga);
     cx.v_to_lds(sh, 0, ga, cx.ntok(0));
     cx.load_gate(ga, 1, true);
     // the previous chunk's U and Delta tiles, stored at the next chunk's start
@@ -602,7 +608,7 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     // chunk c from cur; fetches chunk c + 1 into nxt and the gates of chunk
     // c + 2 into g2; turns g1 (chunk c + 1) into LDS rows at the end
     auto step = [&](int c, const FwdIn<D, DT>& cur, FwdIn<D, DT>& nxt, const GateIn<DT>& g1, GateIn<DT>& g2) {
-        const RowF rf{&sh.g[w][c & 1][0][0]};
+        const RowF rf{&sh.g[c & 1][0][0]};
         const int64_t ci = cx.cidx(c);
         const int nt = cx.ntok(c);
         cx.load(nxt, c + 1);
@@ -638,9 +644,9 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
         }
         // the next chunk's gate rows and V slice while the update multiplies
         // (every wave is past this chunk's first barrier, the last reader of
-        // the V buffer written here)
+        // the buffers written here)
         const int nn = cx.ntok(min(c + 1, cx.NC - 1));
-        cx.gates_to_lds(&sh.g[w][(c + 1) & 1][0][0], g1, nn);
+        cx.gates_to_lds(&sh.g[(c + 1) & 1][0][0], g1);
         cx.v_to_lds(sh, (c + 1) & 1, g1, nn);
     };
     int c = 0;
@@ -664,7 +670,7 @@ __device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     GateIn<DT> ga, gb;
     cx.load(xa, cx.NC - 1);
     cx.load_gate(ga, cx.NC - 1, false);
-    cx.gates_to_lds(&sh.g[w][(cx.NC - 1) & 1][0][0], ga, cx.ntok(cx.NC - 1));
+    cx.gates_to_lds(&sh.g[(cx.NC - 1) & 1][0][0], ga);
     cx.load_gate(ga, cx.NC - 2, false);
     // the previous step's dDelta, dU' and dv tiles, stored at the next step's
     // start (the first step's slots first take zeros, then the real values)
@@ -674,7 +680,7 @@ __device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     // chunk c from cur; fetches chunk c - 1 into nxt and the gates of chunk
     // c - 2 into g2; turns g1 (chunk c - 1) into LDS rows at the end
     auto step = [&](int c, const RevIn<D, DT>& cur, RevIn<D, DT>& nxt, const GateIn<DT>& g1, GateIn<DT>& g2) {
-        const RowF rf{&sh.g[w][c & 1][0][0]};
+        const RowF rf{&sh.g[c & 1][0][0]};
         const int64_t ci = cx.cidx(c);
         const int nt = cx.ntok(c);
         cx.load(nxt, c - 1);
@@ -713,8 +719,9 @@ __device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
             for (int tb = 0; tb < 4; ++tb) acc = blk(cx.ktf(cur, mi, tb), sh.xch2[tb][l], acc);
             St[mi] = acc;
         }
-        // the next chunk's gate rows while the update multiplies
-        cx.gates_to_lds(&sh.g[w][(c + 1) & 1][0][0], g1, cx.ntok(max(c - 1, 0)));
+        // the next chunk's gate rows while the update multiplies (every wave
+        // is past this chunk's first barrier, the last reader of the buffer)
+        cx.gates_to_lds(&sh.g[(c + 1) & 1][0][0], g1);
     };
     int c = cx.NC - 1;
     for (; c >= 1; c -= 2) {
@@ -1184,7 +1191,7 @@ static size_t chunked_bytes_per_head(int64_t T, int64_t D) {
     const size_t nc = (size_t)((T + C - 1) / C);
     const size_t nb = (size_t)(D / 16);
     const size_t per_chunk = sizeof(float) * (4 * (size_t)C * C + 2 * nb * 4 * 64 * 4 + 2 * nb * nb * 64 * 4 +
-                                              5 * (size_t)C * D + (size_t)D * D);
+                                              5 * (size_t)C * D + (size_t)D * D + 8 * (size_t)C);
     return nc * per_chunk;
 }
 constexpr size_t kChunkedWsCap = size_t(8) << 30;
@@ -1195,8 +1202,8 @@ static int64_t chunked_heads_per_launch(int64_t B, int64_t T, int64_t H, int64_t
 }
 
 size_t chunked_backward_workspace(int64_t B, int64_t T, int64_t H, int64_t D) {
-    // fourteen pieces, each 256-byte aligned
-    return chunked_bytes_per_head(T, D) * (size_t)chunked_heads_per_launch(B, T, H, D) + 14 * 256;
+    // fifteen pieces, each 256-byte aligned
+    return chunked_bytes_per_head(T, D) * (size_t)chunked_heads_per_launch(B, T, H, D) + 15 * 256;
 }
 
 hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t st) {
@@ -1241,6 +1248,7 @@ hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t
     ws.dUp = take(nch * C * D);
     ws.Ef = take(nch * C * D);
     ws.Hf = take(nch * D * D);
+    ws.Gr = take(nch * 8 * C);
     for (int64_t bh0 = 0; bh0 < BH; bh0 += gsz) {
         BwdProblem g = a0;
         g.bh0 = bh0;

@@ -56,7 +56,6 @@ __device__ __forceinline__ f32x4 mfma(const u16x8& a, const u16x8& b, const f32x
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Two fp32 values -> bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {

@@ -236,7 +236,7 @@ int gdn_decode_step_raw(int64_t B, int64_t H, int64_t dk, int64_t dv,
  *   grad_state0     [B, H, dv, dk] fp32 or NULL
  *   workspace       at least gdn_backward_workspace_bytes(B, T, H, dk, dv,
  *                   gate) bytes; chunked: per (batch, head) and chunk of 64
- *                   tokens 4 (4 * 64^2 + 7 * 64 dk + 3 dk^2) bytes
+ *                   tokens 4 (4 * 64^2 + 7 * 64 dk + 3 dk^2 + 8 * 64) bytes
  *                   (1.9 GiB on a batch of 2 x 16 heads of 8192 tokens at
  *                   d = 128); token: per (batch, head) 4 dk dv ceil(T / 16)
  *                   of checkpoints and 4 T (2 dk + 4) per block of state rows

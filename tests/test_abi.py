@@ -264,10 +264,11 @@ def test_backward_rejects_bad_arguments_before_any_launch():
     need = gdn.gdn_backward_workspace_bytes(B, T, H, dk, dv, S)
     # chunked: per (batch, head) and chunk of 64 tokens T, T^T, P^T, Atilde^T
     # (64 x 64), K^T and Q^T fragments (64 x dk each), the entry state, the
-    # state gradient and scale Q^T diag(gamma) dO (dk x dv each), and U,
-    # Delta, dDelta, dU', scale P^T dO (64 x dv each), fp32; fourteen pieces
+    # state gradient and scale Q^T diag(gamma) dO (dk x dv each), U, Delta,
+    # dDelta, dU', scale P^T dO (64 x dv each) and eight gate rows of 64, fp32;
+    # fifteen pieces
     nc = (T + 63) // 64
-    assert need == 4 * B * H * nc * (4 * 64 * 64 + 2 * 64 * dk + 3 * dk * dv + 5 * 64 * dv) + 14 * 256
+    assert need == 4 * B * H * nc * (4 * 64 * 64 + 2 * 64 * dk + 3 * dk * dv + 5 * 64 * dv + 8 * 64) + 15 * 256
     # token: a checkpoint at every 16-token run start per (batch, head), and
     # per block of 32 rows (16 lanes a row at dk = 64) a record of 2 dk + 4
     # floats per token
