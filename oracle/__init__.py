@@ -17,6 +17,11 @@ half; the pages give no gradient formulas, so its header derives them).
 ``prologue`` forms the core's inputs from raw projections (per-head L2 norm of
 q and k, sigmoid gates), the step before the core in the DeltaNet block.
 
+``chunked.chunk_backward`` (``oracle/chunked.py``, fp64 numpy) writes the same
+gradients (scalar gate) through the chunk form of the forward, the equations
+the chunked backward kernels follow; it is pinned to ``backward`` by
+``tests/test_oracle_chunk_backward.py``.
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against what
 the pages and the mathematics fix (printed worked examples, closed forms,
 affine composition, the WY identity, linearity, exact rational arithmetic on
