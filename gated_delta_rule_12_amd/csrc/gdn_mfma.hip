@@ -1104,6 +1104,435 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 }
 
 // ---------------------------------------------------------------------------
+// Head-shared chunk loop for per-key-channel gates
+// ---------------------------------------------------------------------------
+// With a channel gate every key column decays at its own rate, so the row
+// operands of the state products carry per-element factors (log2 prefix lam,
+// lam' its prediction row, lam_C the chunk's last row):
+//   X = (K o 2^{lam'}) S^T,   Z = (Q o 2^{lam}) S^T,
+//   S^T <- diag(2^{lam_C}) S^T + (K o 2^{lam_C - lam})^T Delta
+// (GLA gating section; the diagonal decay of the KDA paragraph).  The gated
+// rows are the same for every value column of the head, so here they are
+// formed once per chunk into LDS (bf16 hi/lo, row factors of raw projections
+// folded in) and shared by the waves, where the sliced loop forms them again
+// for each 16-column slice.  Two workgroups per (batch, head) split the value
+// columns, so that 128 heads occupy 256 compute units; each of the two forms
+// the gated rows itself.  One pass, no segments.
+// Eight waves in two roles, one of each per SIMD, so that the vector-ALU
+// work of one overlaps the matrix-core work of the other:
+//   consumers (waves 0-3) hold 16 value columns of S^T each for every key
+//     row (as in k_seg) and run the products;
+//   producers (waves 4-7) load the next chunks' inputs and form their gated
+//     operands, each a chunk ahead of the consumers.
+// Per chunk i, four barriers:
+//   B0 .. B1   consumers: K^T fragments from the transposed-rows tile by exact
+//              identity products, X, Z, U = V - X, Delta = T' U; producers:
+//              the gated operands of chunk i + 1 into registers;
+//   B1 .. B1b  consumers: the fragments over the dead transposed rows;
+//              producers: K and Q rows, V and T' of chunk i + 1 to LDS;
+//   B1b .. B2  consumers: state update and outputs; producers: the loads of
+//              chunk i + 2;
+//   B2 .. B0   producers: the transposed rows, P and the decay of chunk i + 1.
+template <int D>
+struct ChanShared {
+    static constexpr int LDK = D + 8;      // row stride (bf16) of the gated rows, permuted columns
+    static constexpr int LDV = D / 2 + 8;  // row stride of the workgroup's value columns
+    unsigned short Kg[2][C * LDK];         // K o 2^{lam'} (row factor 1/|k| for raw projections), hi / lo
+    unsigned short Qg[2][C * LDK];         // Q o 2^{lam} (1/|q|), hi / lo
+    union {
+        unsigned short Kt[2][C * LDK];     // K o 2^{lam_C - lam} (1/|k|), hi / lo
+        u16x8 KtF[D / 16][2][2][64];       // the same transposed: [key tile][token k-step][hi/lo][lane]
+    } t;
+    unsigned short V[C * LDV];
+    u16x8 Tf[kTfragPerChunk];
+    u16x8 Pf[kTfragPerChunk];
+    float dec[D];                          // 2^{lam_C}
+};
+
+template <int D>
+constexpr int chan_threads() { return 4 * D; }  // D / 32 consumer waves of 16 value columns, as many producers
+
+template <int D, bool RAW>
+__global__ __launch_bounds__(chan_threads<D>(), 2) void k_chan_head(Problem p, const u16x8* tfrag,
+                                                                    const u16x8* pfrag, const float* gates,
+                                                                    int xcd_remap) {
+    constexpr int NP = chan_threads<D>() / 2;  // threads per role
+    constexpr int NW = NP / 64;
+    constexpr int LDK = ChanShared<D>::LDK;
+    constexpr int LDV = ChanShared<D>::LDV;
+    constexpr int KS = D / 32;         // k-steps over the key dimension
+    constexpr int TPW = D / 16;        // 16-row key tiles of S^T per value block
+    constexpr int GPR = D / 8;         // 16-byte groups per stored row
+    constexpr int RUN = C * GPR / NP;  // consecutive tokens per producer thread
+    constexpr int VP = C * (D / 2) / 8 / NP;  // 16-byte value pieces per producer thread
+    constexpr int TFP = kTfragPerChunk / NP;  // fragment pieces per producer thread
+    static_assert(NW == 4 && RUN == 4 && VP * NP * 8 == C * D / 2 && TFP * NP == kTfragPerChunk,
+                  "staging split");
+    __shared__ __attribute__((aligned(16))) ChanShared<D> sh;
+
+    // (batch, head, value half); with xcd_remap both halves of a head land on
+    // one XCD (workgroups are dealt to the 8 XCDs round-robin)
+    int id = blockIdx.x, half;
+    if (xcd_remap) {
+        const int xcd = id & 7, slot = id >> 3;
+        half = slot & 1;
+        id = (slot >> 1) * 8 + xcd;
+    } else {
+        half = id & 1;
+        id >>= 1;
+    }
+    const int64_t bh = id;
+    const int64_t H = p.H, T = p.T;
+    const int b = (int)(bh / H), h = (int)(bh - (bh / H) * H);
+    const int64_t row_stride = H * D;
+    const int NC = p.NC;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    if (wave >= NW) {
+        // ================= producers =================
+        const int tid = threadIdx.x - NP;
+        const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
+        const unsigned short* kin = static_cast<const unsigned short*>(p.k);
+        const unsigned short* qin = static_cast<const unsigned short*>(p.q);
+        const unsigned short* vin = static_cast<const unsigned short*>(p.v);
+        // Rows are stored with the columns of every 32-column block permuted,
+        // 16 hh + 4 g + r -> 8 g + 4 hh + r, so that a lane group's eight
+        // k-slots of a k-step are 16 contiguous bytes.  Thread (run, q) takes
+        // tokens RUN run .. + RUN - 1 and stored group q (key columns
+        // a0 = 32 (q / 4) + 4 (q % 4) .. + 3 and a1 = a0 + 16 .. + 3), so each
+        // formed group is one 16-byte store and the 16 groups of a row span
+        // every LDS bank; the log2-prefix rows from one before the run (the
+        // prediction rows of predict-then-decay) and the chunk's last row.
+        const int q = tid % GPR, run = tid / GPR, t0r = RUN * run;
+        const int a0 = 32 * (q >> 2) + 4 * (q & 3), a1 = a0 + 16;
+        u32x2 kr[RUN][2], qr[RUN][2];
+        u32x4 vr[VP], tr[TFP], pr[TFP], pn[TFP];
+        f32x4 lam[RUN + 1][2], lamC[2], rq4, rk4;
+        // loads of chunk i (all but P)
+        auto issue = [&](int i) {
+            const int64_t t0 = (int64_t)i * C;
+            const int nt = (int)((T - t0) < C ? (T - t0) : C);
+            const int64_t base = ((int64_t)b * T + t0) * row_stride + (int64_t)h * D;
+#pragma unroll
+            for (int j = 0; j < RUN; ++j) {
+                const int t = t0r + j;
+                kr[j][0] = kr[j][1] = qr[j][0] = qr[j][1] = u32x2{0, 0};
+                if (t < nt) {
+                    kr[j][0] = ld_g<u32x2>(kin + base + t * row_stride + a0);
+                    kr[j][1] = ld_g<u32x2>(kin + base + t * row_stride + a1);
+                    qr[j][0] = ld_g<u32x2>(qin + base + t * row_stride + a0);
+                    qr[j][1] = ld_g<u32x2>(qin + base + t * row_stride + a1);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < VP; ++k) {
+                const int e = tid + NP * k, t = e / (D / 16), c = e % (D / 16);
+                vr[k] = u32x4{0, 0, 0, 0};
+                if (t < nt) vr[k] = ld_g<u32x4>(vin + base + t * row_stride + (D / 2) * half + 8 * c);
+            }
+            const float* g = gates + (bh * NC + i) * kChanFloats<D>;
+#pragma unroll
+            for (int j = 0; j <= RUN; ++j) {
+                const int t = t0r + j - 1;
+                lam[j][0] = lam[j][1] = zero4();
+                if (t >= 0 && (ptd || j > 0)) {
+                    lam[j][0] = ld_g<f32x4>(g + t * D + a0);
+                    lam[j][1] = ld_g<f32x4>(g + t * D + a1);
+                }
+            }
+            lamC[0] = ld_g<f32x4>(g + (C - 1) * D + a0);
+            lamC[1] = ld_g<f32x4>(g + (C - 1) * D + a1);
+            if constexpr (RAW) {
+                rq4 = ld_g<f32x4>(g + C * D + t0r);
+                rk4 = ld_g<f32x4>(g + C * D + C + t0r);
+            }
+            const u32x4* tp = reinterpret_cast<const u32x4*>(tfrag + (bh * NC + i) * kTfragPerChunk);
+#pragma unroll
+            for (int k = 0; k < TFP; ++k) tr[k] = ld_g<u32x4>(tp + tid + NP * k);
+        };
+        // P of chunk i into pn (pr holds the P still to be stored)
+        auto issue_p = [&](int i) {
+            const u32x4* pp = reinterpret_cast<const u32x4*>(pfrag + (bh * NC + i) * kTfragPerChunk);
+#pragma unroll
+            for (int k = 0; k < TFP; ++k) pn[k] = ld_g<u32x4>(pp + tid + NP * k);
+        };
+        // element e of a stored group: column a0 + e (e < 4) or a1 + e - 4
+        auto el = [](const f32x4 (&x)[2], int e) { return e < 4 ? x[0][e] : x[1][e - 4]; };
+        auto elb = [](const u32x2 (&x)[2], int e) {
+            return gdn_bf16_to_f32(__builtin_bit_cast(u16x4, x[e >> 2])[e & 3]);
+        };
+        // the three gated operands of the staged chunk, split hi/lo
+        u32x4 kg[RUN][2], qg[RUN][2], kt[RUN][2];
+        f32x4 dec[2];
+        auto form = [&]() {
+            float eprev[8];  // 2^{lam} of the row before (predict-then-decay)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) eprev[e] = __builtin_amdgcn_exp2f(el(lam[0], e));
+#pragma unroll
+            for (int j = 0; j < RUN; ++j) {
+                uint32_t kh[4], kl[4], qh[4], ql[4], th[4], tl[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float yk[2], yq[2], yt[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int ee = e + u;
+                        const float lt = el(lam[j + 1], ee);
+                        const float et = __builtin_amdgcn_exp2f(lt);
+                        const float ft = __builtin_amdgcn_exp2f(el(lamC, ee) - lt);
+                        float kf = elb(kr[j], ee), qf = elb(qr[j], ee);
+                        if constexpr (RAW) {
+                            kf *= rk4[j];
+                            qf *= rq4[j];
+                        }
+                        yk[u] = kf * (ptd ? eprev[ee] : et);
+                        yq[u] = qf * et;
+                        yt[u] = kf * ft;
+                        eprev[ee] = et;
+                    }
+                    split2(yk[0], yk[1], kh[e >> 1], kl[e >> 1]);
+                    split2(yq[0], yq[1], qh[e >> 1], ql[e >> 1]);
+                    split2(yt[0], yt[1], th[e >> 1], tl[e >> 1]);
+                }
+                kg[j][0] = u32x4{kh[0], kh[1], kh[2], kh[3]};
+                kg[j][1] = u32x4{kl[0], kl[1], kl[2], kl[3]};
+                qg[j][0] = u32x4{qh[0], qh[1], qh[2], qh[3]};
+                qg[j][1] = u32x4{ql[0], ql[1], ql[2], ql[3]};
+                kt[j][0] = u32x4{th[0], th[1], th[2], th[3]};
+                kt[j][1] = u32x4{tl[0], tl[1], tl[2], tl[3]};
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dec[0][e] = __builtin_amdgcn_exp2f(lamC[0][e]);
+                dec[1][e] = __builtin_amdgcn_exp2f(lamC[1][e]);
+            }
+        };
+        // K and Q rows, V and T' (their tiles are free from B1 on)
+        auto store_a = [&]() {
+#pragma unroll
+            for (int j = 0; j < RUN; ++j) {
+                const int o = (t0r + j) * LDK + 8 * q;
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl) {
+                    *reinterpret_cast<u32x4*>(&sh.Kg[hl][o]) = kg[j][hl];
+                    *reinterpret_cast<u32x4*>(&sh.Qg[hl][o]) = qg[j][hl];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < VP; ++k) {
+                const int e = tid + NP * k, t = e / (D / 16), c = e % (D / 16);
+                *reinterpret_cast<u32x4*>(&sh.V[t * LDV + 8 * c]) = vr[k];
+            }
+#pragma unroll
+            for (int k = 0; k < TFP; ++k) reinterpret_cast<u32x4*>(sh.Tf)[tid + NP * k] = tr[k];
+        };
+        // the transposed operand's rows, P and the decay (free from B2 on)
+        auto store_b = [&]() {
+#pragma unroll
+            for (int j = 0; j < RUN; ++j) {
+                const int o = (t0r + j) * LDK + 8 * q;
+                *reinterpret_cast<u32x4*>(&sh.t.Kt[0][o]) = kt[j][0];
+                *reinterpret_cast<u32x4*>(&sh.t.Kt[1][o]) = kt[j][1];
+            }
+#pragma unroll
+            for (int k = 0; k < TFP; ++k) reinterpret_cast<u32x4*>(sh.Pf)[tid + NP * k] = pr[k];
+            if (run == 0) {
+                *reinterpret_cast<f32x4*>(&sh.dec[a0]) = dec[0];
+                *reinterpret_cast<f32x4*>(&sh.dec[a1]) = dec[1];
+            }
+        };
+        // chunks past the last reload it: every step stays branch-free and
+        // its results are never read
+        auto clampc = [&](int i) { return i < NC ? i : NC - 1; };
+        auto take_p = [&]() {
+#pragma unroll
+            for (int k = 0; k < TFP; ++k) pr[k] = pn[k];
+        };
+        if (NC > 0) {
+            issue(0);
+            issue_p(0);
+            take_p();
+            form();
+            store_a();
+            store_b();
+            issue(clampc(1));
+            issue_p(clampc(1));
+            take_p();
+        }
+        // the loads go out while the consumers run the state update and the
+        // outputs, so that no barrier waits on their issue (the compiler is
+        // free to sink the formation towards the stores, which measured
+        // faster than holding it before B1: the loads then have longer to
+        // arrive)
+        for (int i = 0; i < NC; ++i) {
+            __syncthreads();  // B0
+            form();           // chunk i + 1
+            __syncthreads();  // B1
+            store_a();
+            __syncthreads();  // B1b
+            issue(clampc(i + 2));
+            issue_p(clampc(i + 2));
+            __syncthreads();  // B2
+            store_b();
+            take_p();
+        }
+        return;
+    }
+
+    // ================= consumers =================
+    const int tid = threadIdx.x;
+    const int w = wave;
+    const int l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int vcol = (D / 2) * half + 16 * w + c16;  // the lane's value column
+
+    // state: S^T tile u, lane (v = vcol, a = 16 u + 4 g4 + r)
+    f32x4 Sacc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+        Sacc[u] = p.s0 ? ld_g<f32x4>(p.s0 + (bh * D + vcol) * D + 16 * u + 4 * g4) : zero4();
+
+    for (int i = 0; i < NC; ++i) {
+        const int64_t t0 = (int64_t)i * C;
+        const int nt = (int)((T - t0) < C ? (T - t0) : C);
+        __syncthreads();  // B0: chunk i staged
+
+        // K^T fragments: job (hl, s', u) turns token tiles 2s', 2s' + 1 of the
+        // transposed rows (hi or lo) into the A fragment of key rows 16u + c16
+        // by the identity selecting that key tile; wave w takes hl = w % 2,
+        // s' = w / 2 and every u
+        const int hl = w & 1, sj = w >> 1;
+        u16x8 ktf[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            u16x8 idf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                idf[e] = ((e >> 2) == (u & 1) && 4 * g4 + (e & 3) == c16) ? (unsigned short)0x3F80 : (unsigned short)0;
+            u16x4 hv[2];
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int m = 2 * sj + qq;
+                const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.t.Kt[hl][(16 * m + c16) * LDK + 32 * (u >> 1) + 8 * g4]);
+                const f32x4 d = mfma(ka, idf, zero4());
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hv[qq][r] = (unsigned short)(__float_as_uint(d[r]) >> 16);
+            }
+            ktf[u] = cat(hv[0], hv[1]);
+        }
+
+        // S^T as B operands of every k-step, split hi/lo
+        u16x8 sbh[KS], sbl[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u16x4 h0, l0, h1, l1;
+            split4(Sacc[2 * s], h0, l0);
+            split4(Sacc[2 * s + 1], h1, l1);
+            sbh[s] = cat(h0, h1);
+            sbl[s] = cat(l0, l1);
+        }
+        // X = Kg S^T, Z = Qg S^T (both operands split: three products)
+        f32x4 X[4], Z[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) X[m] = Z[m] = zero4();
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int o = (16 * m + c16) * LDK + 32 * s + 8 * g4;
+                const u16x8 kh = *reinterpret_cast<const u16x8*>(&sh.Kg[0][o]);
+                const u16x8 kl = *reinterpret_cast<const u16x8*>(&sh.Kg[1][o]);
+                X[m] = mfma(kh, sbh[s], X[m]);
+                X[m] = mfma(kh, sbl[s], X[m]);
+                X[m] = mfma(kl, sbh[s], X[m]);
+                const u16x8 qh = *reinterpret_cast<const u16x8*>(&sh.Qg[0][o]);
+                const u16x8 ql = *reinterpret_cast<const u16x8*>(&sh.Qg[1][o]);
+                Z[m] = mfma(qh, sbh[s], Z[m]);
+                Z[m] = mfma(qh, sbl[s], Z[m]);
+                Z[m] = mfma(ql, sbh[s], Z[m]);
+            }
+        // U = V - X, split hi/lo
+        u16x4 uh[4], ul[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                x[r] = gdn_bf16_to_f32(sh.V[(16 * m + 4 * g4 + r) * LDV + 16 * w + c16]) - X[m][r];
+            split4(x, uh[m], ul[m]);
+        }
+        // Delta = T' U (tile m takes k-steps s <= m / 2), split hi/lo
+        u16x4 dh[4], dl[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 d1 = zero4();
+#pragma unroll
+            for (int s = 0; s <= (m >> 1); ++s) {
+                const u16x8 th = sh.Tf[(tslot(m, s) * 2 + 0) * 64 + l];
+                const u16x8 tl = sh.Tf[(tslot(m, s) * 2 + 1) * 64 + l];
+                const u16x8 xh = cat(uh[2 * s], uh[2 * s + 1]);
+                const u16x8 xl = cat(ul[2 * s], ul[2 * s + 1]);
+                d1 = mfma(th, xh, d1);
+                d1 = mfma(th, xl, d1);
+                d1 = mfma(tl, xh, d1);
+            }
+            split4(d1, dh[m], dl[m]);
+        }
+        __syncthreads();  // B1: the gated and transposed rows, V and T' of chunk i are read
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) sh.t.KtF[u][sj][hl][l] = ktf[u];
+        __syncthreads();  // B1b: K^T fragments complete
+
+        // S^T <- diag(2^{lam_C}) S^T + K^T Delta (A rows a = 16 u + c16)
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            f32x4 acc = *reinterpret_cast<const f32x4*>(&sh.dec[16 * u + 4 * g4]) * Sacc[u];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const u16x8 kh = sh.t.KtF[u][s][0][l];
+                const u16x8 kl = sh.t.KtF[u][s][1][l];
+                const u16x8 bh_ = cat(dh[2 * s], dh[2 * s + 1]);
+                const u16x8 bl_ = cat(dl[2 * s], dl[2 * s + 1]);
+                acc = mfma(kh, bh_, acc);
+                acc = mfma(kh, bl_, acc);
+                acc = mfma(kl, bh_, acc);
+            }
+            Sacc[u] = acc;
+        }
+        // O = scale (Z + P Delta), rows past the sequence end dropped
+        {
+            float* obase = p.out + ((int64_t)b * T + t0) * row_stride + (int64_t)h * D + vcol;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 o1 = zero4();
+#pragma unroll
+                for (int s = 0; s <= (m >> 1); ++s) {
+                    const u16x8 ph = sh.Pf[(tslot(m, s) * 2 + 0) * 64 + l];
+                    const u16x8 pl = sh.Pf[(tslot(m, s) * 2 + 1) * 64 + l];
+                    const u16x8 xh = cat(dh[2 * s], dh[2 * s + 1]);
+                    const u16x8 xl = cat(dl[2 * s], dl[2 * s + 1]);
+                    o1 = mfma(ph, xh, o1);
+                    o1 = mfma(ph, xl, o1);
+                    o1 = mfma(pl, xh, o1);
+                }
+                const f32x4 o = p.scale * (Z[m] + o1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * m + 4 * g4 + r;
+                    if (t < nt) st_g<float>(obase + (int64_t)t * row_stride, o[r]);
+                }
+            }
+        }
+        __syncthreads();  // B2: K^T fragments, P and the decay of chunk i are read
+    }
+
+    if (p.s_out) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+            st_g<f32x4>(p.s_out + (bh * D + vcol) * D + 16 * u + 4 * g4, Sacc[u]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Whole-head chunk loop (scalar gate)
 // ---------------------------------------------------------------------------
 // One workgroup per (batch, head, segment) keeps the whole state S^T (D x D,
@@ -2083,6 +2512,36 @@ hipError_t launch(const Problem& p, const Split& sp, char* ws, const WsLayout& L
     return hipSuccess;
 }
 
+// Channel gate with enough heads: stage 1, then the head-shared chunk loop
+// (two workgroups per head, one pass).
+template <int D>
+hipError_t launch_chan(const Problem& p, char* ws, const WsLayout& L, hipStream_t st) {
+    u16x8* tfrag = reinterpret_cast<u16x8*>(ws + L.prep);
+    const int64_t nch = p.B * p.H * (int64_t)p.NC;
+    const size_t fbytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8));
+    u16x8* pfrag = reinterpret_cast<u16x8*>(ws + L.prep + fbytes);
+    float* gates = reinterpret_cast<float*>(ws + L.prep + 2 * fbytes);
+    if (p.NC > 0) {
+        dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
+        prof_begin(p.timer, "k_prep_mfma", st);
+        hipLaunchKernelGGL((k_prep_channel<D>), grid, dim3(kThreads), 0, st, p, tfrag, pfrag, gates);
+        prof_end(p.timer, st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t heads = p.B * p.H;
+    const int remap = heads % 8 == 0 ? 1 : 0;
+    prof_begin(p.timer, "k_chan_head", st);
+    if (p.raw)
+        hipLaunchKernelGGL((k_chan_head<D, true>), dim3((unsigned)(2 * heads)), dim3(chan_threads<D>()), 0, st, p,
+                           tfrag, pfrag, gates, remap);
+    else
+        hipLaunchKernelGGL((k_chan_head<D, false>), dim3((unsigned)(2 * heads)), dim3(chan_threads<D>()), 0, st, p,
+                           tfrag, pfrag, gates, remap);
+    prof_end(p.timer, st);
+    return hipGetLastError();
+}
+
 // Scalar gate: stage 1, then the whole-head chunk loop (two passes and the
 // start-state chain when the sequence is cut into segments).
 template <int D>
@@ -2140,6 +2599,13 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
 constexpr int64_t kWholeHeadMinGroups = 128;
 static bool whole_head(const Problem& p, const Split& sp) {
     return p.gate == GDN_GATE_SCALAR && p.B * p.H * (int64_t)sp.G >= kWholeHeadMinGroups;
+}
+// The channel gate's head-shared loop (two workgroups per head, one pass) at
+// dk = 128 once there are enough heads; the sliced loop otherwise and for
+// segmented runs.
+constexpr int64_t kChanHeadMinHeads = 64;
+static bool chan_head(const Problem& p, const Split& sp) {
+    return p.gate == GDN_GATE_CHANNEL && p.dk == 128 && sp.G == 1 && p.B * p.H >= kChanHeadMinHeads;
 }
 
 bool mfma_supported(int64_t dk, int64_t dv, int C_, int dtype, int gate) {
@@ -2201,6 +2667,7 @@ hipError_t mfma_forward(const Problem& p, const Split& sp, char* ws, hipStream_t
     const WsLayout L = mfma_layout(p, sp);
     const bool ch = p.gate == GDN_GATE_CHANNEL;
     if (whole_head(p, sp)) return p.dk == 128 ? launch_seg<128>(p, sp, ws, L, st) : launch_seg<64>(p, sp, ws, L, st);
+    if (chan_head(p, sp)) return launch_chan<128>(p, ws, L, st);
     if (p.dk == 128) return ch ? launch<128, 1>(p, sp, ws, L, st) : launch<128, 0>(p, sp, ws, L, st);
     return ch ? launch<64, 1>(p, sp, ws, L, st) : launch<64, 0>(p, sp, ws, L, st);
 }

@@ -23,6 +23,20 @@ constexpr int kThreads = 256;  // four waves
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Loads and stores through the global address space.  Where the compiler
+// cannot prove that a generic pointer is global it emits flat instructions,
+// which count on the LDS counter too, so that every later wait for an LDS
+// access (each barrier included) also waits for them to come back from
+// memory; these casts keep such accesses global.
+template <typename V>
+__device__ __forceinline__ V ld_g(const void* p) {
+    return *(const __attribute__((address_space(1))) V*)p;
+}
+template <typename V>
+__device__ __forceinline__ void st_g(void* p, const V& x) {
+    *(__attribute__((address_space(1))) V*)p = x;
+}
+
 // D += A B on a 16 x 16 x 4 fp32 tile.  Lane l = 16 g + c supplies A[c][g]
 // and B[g][c]; the accumulator holds D[4 g + r][c] in element r.
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {

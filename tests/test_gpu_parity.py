@@ -201,19 +201,20 @@ def test_streaming_equals_one_call():
     assert (s2 - s).abs().max().item() <= 1e-5 * s.abs().max().item()
 
 
-@pytest.mark.parametrize("B,H,T,d,G", [
-    (1, 2, 300, 64, None),     # sliced path, one stream
-    (1, 2, 1000, 64, 3),       # sliced path, increment-and-correct
-    (1, 32, 1000, 128, None),  # whole-head path, library schedule (4 segments)
-    (1, 32, 2000, 64, 8),      # whole-head path, 8 segments, d = 64
-    (16, 16, 700, 128, None),  # whole-head path, one pass
+@pytest.mark.parametrize("B,H,T,d,G,gate", [
+    (1, 2, 300, 64, None, "scalar"),     # sliced path, one stream
+    (1, 2, 1000, 64, 3, "scalar"),       # sliced path, increment-and-correct
+    (1, 32, 1000, 128, None, "scalar"),  # whole-head path, library schedule (4 segments)
+    (1, 32, 2000, 64, 8, "scalar"),      # whole-head path, 8 segments, d = 64
+    (16, 16, 700, 128, None, "scalar"),  # whole-head path, one pass
+    (4, 16, 700, 128, None, "channel"),  # channel gate, head-shared loop
 ])
-def test_in_place_state(B, H, T, d, G):
+def test_in_place_state(B, H, T, d, G, gate):
     """state_out == state0 (in-place streaming) on every path: the last
     segment's final state may not overwrite the start state before segment 0
     has read it."""
     import torch
-    w = Workload("inplace", B=B, H=H, T=T, dk=d, dv=d, chunk=64, state0_std=0.3, seed=13 + T)
+    w = Workload("inplace", B=B, H=H, T=T, dk=d, dv=d, chunk=64, state0_std=0.3, gate=gate, seed=13 + T)
     inp = make_inputs(w)
     d_ = to_device(inp, w)
     st = d_["state0"].clone()
@@ -352,6 +353,42 @@ def test_whole_head_single_pass(B, H, T, d, order):
     check(w, inp, o, s, order)
 
 
+# --------------------------------------------------------------------------
+# head-shared chunk loop (channel gate, dk = 128, at least 64 heads, one
+# pass): two workgroups per head, each forming the gated rows once per chunk
+# for its four waves of 16 value columns
+# --------------------------------------------------------------------------
+
+CHAN_HEAD = [
+    # B, H, T, order, state0_std, alpha_mean
+    (4, 16, 300, PTD, 0.5, 2.0),     # ragged tail; 64 heads, XCD placement
+    (2, 32, 257, DTP, 0.5, 2.0),     # one token in the last chunk
+    (5, 13, 130, PTD, 0.3, 2.0),     # 65 heads, not a multiple of 8
+    (8, 8, 64, DTP, 0.0, 6.0),       # exactly one chunk, zero start state, long memory
+    (1, 64, 1, PTD, 0.5, 2.0),       # one token
+    (4, 16, 512, PTD, 0.5, -3.0),    # fast forgetting
+    (4, 16, 512, DTP, 0.5, -6.0),    # stage 1 sums the diagonal blocks directly
+]
+
+
+@pytest.mark.parametrize("case", CHAN_HEAD, ids=lambda c: "-".join(map(str, c)))
+def test_channel_head_shared(case):
+    import torch
+    B, H, T, order, std, am = case
+    w = Workload("chan-head", B=B, H=H, T=T, dk=128, dv=128, chunk=64, gate="channel",
+                 state0_std=std, alpha_mean=am, seed=31 + T + H)
+    inp = make_inputs(w)
+    d = to_device(inp, w)
+    t = gdn.Timer()
+    o, s = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"], chunk=64,
+                         order=order, timer=t)
+    torch.cuda.synchronize()
+    rec = t.read()
+    t.close()
+    assert set(rec) == {"k_prep_mfma", "k_chan_head"}, rec
+    check(w, inp, _np(o), _np(s), order)
+
+
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
 def test_full_workload(idx):
     """The workloads at full size, every (batch, head) slice."""
@@ -390,9 +427,9 @@ def test_long_workload_single_stream():
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 def test_tensors_past_2_31_elements(gate):
     """9 x 65536 x 32 x 128 = 2.4e9 elements in q, k, v and O (scalar gate:
-    the whole-head path, 288 heads in one pass; channel gate: the sliced
-    path); heads whose data lie past element 2^31 checked against the
-    oracle."""
+    the whole-head path, 288 heads in one pass; channel gate: the
+    head-shared path); heads whose data lie past element 2^31 checked
+    against the oracle."""
     import torch
     from gated_delta_rule_12_amd.workloads import make_inputs_device, slice_inputs
     w = Workload("large", B=9, H=32, T=65536, dk=128, dv=128, chunk=64, gate=gate,

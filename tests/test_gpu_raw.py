@@ -72,6 +72,8 @@ CASES = [
     (1, 3, 449, 128, 128, 64, "bf16", "channel", PTD, 0.5, 2.0),    # sliced loop, channel gate
     (2, 2, 320, 64, 64, 64, "bf16", "channel", DTP, 0.5, 6.0),
     (1, 2, 512, 128, 128, 64, "bf16", "channel", PTD, 0.5, -6.0),   # direct diagonal blocks
+    (4, 16, 300, 128, 128, 64, "bf16", "channel", DTP, 0.5, 2.0),   # head-shared loop, channel gate
+    (2, 32, 200, 128, 128, 64, "bf16", "channel", PTD, 0.3, -3.0),
     (1, 1, 256, 16, 16, 16, "f32", "scalar", PTD, 0.0, 2.0),        # vector-ALU family
     (2, 3, 100, 96, 112, 32, "bf16", "scalar", DTP, 0.5, 2.0),
     (1, 2, 133, 32, 48, 32, "f32", "channel", PTD, 0.5, 2.0),
@@ -88,8 +90,8 @@ def test_chunk_fwd_raw(case):
 
 @pytest.mark.parametrize("idx", [2, 4])
 def test_chunk_fwd_raw_full_workload(idx):
-    """The main (whole-head path, 8 segments) and channel-gate (sliced path)
-    workloads at full size on raw projections and logits."""
+    """The main (whole-head path, 8 segments) and channel-gate (head-shared
+    path) workloads at full size on raw projections and logits."""
     run_and_check(WORKLOADS[idx].with_(name=WORKLOADS[idx].name + "-raw"))
 
 
