@@ -284,18 +284,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* 
     // Row factors are at most one, key factors too off the diagonal block;
     // on it they grow with the decay across the block.  All gated operands
     // are split hi/lo; accumulators are transposed (rows j, columns t).
-    // While the chunk decays by less than 2^96 on every channel (the prefix
-    // falls monotonically, so its last row bounds it) one anchor at the
-    // chunk start serves every block: row factors 2^{lam_t} >= 2^-96 and key
-    // factors 2^{-lam_j} <= 2^96 stay normal numbers in fp32 and bf16, and
-    // each gated key block is formed once instead of once per row block.
-    float lmin = 0.f;
-    for (int a = l; a < D; a += 64) lmin = fminf(lmin, gt[C - 1][a]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) lmin = fminf(lmin, __shfl_xor(lmin, o, 64));
-    const bool one_anchor = lmin > -96.f;
     const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
-    const int pa = one_anchor ? -1 : 16 * w - 1, t = 16 * w + c16;
+    const int pa = 16 * w - 1, t = 16 * w + c16;
     const int tp = ptd ? t - 1 : t;  // row of lam' (-1: zero)
     const f32x4 z4 = zero4();
     const float rq_t = rqsh[t], rk_t = rksh[t];
@@ -339,44 +329,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* 
     for (int a = l; a < D; a += 64) span = fmaxf(span, (pa >= 0 ? gt[pa][a] : 0.f) - gt[16 * w + 15][a]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
-    const bool direct = !one_anchor && span > 92.f;
-
-    // one anchor: wave w forms key block w, and the four go to the prefix
-    // table's tile as A fragments [block][k-step][hi/lo][lane] once every
-    // wave has read the table
-    u16x8* kfr = reinterpret_cast<u16x8*>(&gt[0][0]);
-    static_assert(4 * (D / 32) * 2 * 64 * 16 <= C * (D + 4) * 4, "key blocks fit the prefix tile");
-    if (one_anchor) {
-        u16x8 fh[D / 32], fl[D / 32];
-        const float rk_j = rksh[t];
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            const int a0 = 32 * s + 8 * g4;
-            const u16x8 kj = *reinterpret_cast<const u16x8*>(&Ks[t * LDK + a0]);
-            const f32x4 gj0 = *reinterpret_cast<const f32x4*>(&gt[t][a0]);
-            const f32x4 gj1 = *reinterpret_cast<const f32x4*>(&gt[t][a0 + 4]);
-            uint32_t ah[4], al[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float xa[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int ee = e + u;
-                    xa[u] = rk_j * gdn_bf16_to_f32(kj[ee]) * __builtin_amdgcn_exp2f(-(ee < 4 ? gj0[ee] : gj1[ee - 4]));
-                }
-                split2(xa[0], xa[1], ah[e >> 1], al[e >> 1]);
-            }
-            fh[s] = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
-            fl[s] = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
-        }
-        __syncthreads();  // every wave has read the prefix table
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            kfr[((w * (D / 32) + s) * 2 + 0) * 64 + l] = fh[s];
-            kfr[((w * (D / 32) + s) * 2 + 1) * 64 + l] = fl[s];
-        }
-        __syncthreads();
-    }
+    const bool direct = span > 92.f;
 
     // P blocks go out as fragment pairs as soon as a pair is complete; the A
     // blocks (rows j, column t) stay in registers until K is dead
@@ -411,32 +364,26 @@ __global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* 
             const float rk_j = rksh[j];
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
-                u16x8 Ah, Al;
-                if (one_anchor) {
-                    Ah = kfr[((c * (D / 32) + s) * 2 + 0) * 64 + l];
-                    Al = kfr[((c * (D / 32) + s) * 2 + 1) * 64 + l];
-                } else {
-                    const int a0 = 32 * s + 8 * g4;
-                    const u16x8 kj = *reinterpret_cast<const u16x8*>(&Ks[j * LDK + a0]);
-                    const f32x4 gp0 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0]) : z4;
-                    const f32x4 gp1 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0 + 4]) : z4;
-                    const f32x4 gj0 = *reinterpret_cast<const f32x4*>(&gt[j][a0]);
-                    const f32x4 gj1 = *reinterpret_cast<const f32x4*>(&gt[j][a0 + 4]);
-                    uint32_t ah[4], al[4];
+                const int a0 = 32 * s + 8 * g4;
+                const u16x8 kj = *reinterpret_cast<const u16x8*>(&Ks[j * LDK + a0]);
+                const f32x4 gp0 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0]) : z4;
+                const f32x4 gp1 = pa >= 0 ? *reinterpret_cast<const f32x4*>(&gt[pa][a0 + 4]) : z4;
+                const f32x4 gj0 = *reinterpret_cast<const f32x4*>(&gt[j][a0]);
+                const f32x4 gj1 = *reinterpret_cast<const f32x4*>(&gt[j][a0 + 4]);
+                uint32_t ah[4], al[4];
 #pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        float xa[2];
+                for (int e = 0; e < 8; e += 2) {
+                    float xa[2];
 #pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const int ee = e + u;
-                            xa[u] = rk_j * gdn_bf16_to_f32(kj[ee]) *
-                                    __builtin_amdgcn_exp2f((ee < 4 ? gp0[ee] : gp1[ee - 4]) - (ee < 4 ? gj0[ee] : gj1[ee - 4]));
-                        }
-                        split2(xa[0], xa[1], ah[e >> 1], al[e >> 1]);
+                    for (int u = 0; u < 2; ++u) {
+                        const int ee = e + u;
+                        xa[u] = rk_j * gdn_bf16_to_f32(kj[ee]) *
+                                __builtin_amdgcn_exp2f((ee < 4 ? gp0[ee] : gp1[ee - 4]) - (ee < 4 ? gj0[ee] : gj1[ee - 4]));
                     }
-                    Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
-                    Al = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
+                    split2(xa[0], xa[1], ah[e >> 1], al[e >> 1]);
                 }
+                const u16x8 Ah = __builtin_bit_cast(u16x8, uint4{ah[0], ah[1], ah[2], ah[3]});
+                const u16x8 Al = __builtin_bit_cast(u16x8, uint4{al[0], al[1], al[2], al[3]});
                 aP = mfma(Ah, qh[s], aP);
                 aP2 = mfma(Ah, ql[s], aP2);
                 aP = mfma(Al, qh[s], aP);
