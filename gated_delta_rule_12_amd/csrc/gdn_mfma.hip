@@ -1124,14 +1124,14 @@ __global__ __launch_bounds__(kRecThreads) void k_rec_mfma(Problem p, Split sp, W
 //     row (as in k_seg) and run the products;
 //   producers (waves 4-7) load the next chunks' inputs and form their gated
 //     operands, each a chunk ahead of the consumers.
-// Per chunk i, four barriers:
-//   B0 .. B1   consumers: K^T fragments from the transposed-rows tile by exact
-//              identity products, X, Z, U = V - X, Delta = T' U; producers:
-//              the gated operands of chunk i + 1 into registers;
-//   B1 .. B1b  consumers: the fragments over the dead transposed rows;
-//              producers: K and Q rows, V and T' of chunk i + 1 to LDS;
-//   B1b .. B2  consumers: state update and outputs; producers: the loads of
-//              chunk i + 2;
+// Per chunk i, three barriers:
+//   B0 .. B1   consumers: X, Z, U = V - X, Delta = T' U; producers: K^T
+//              fragments of chunk i from the transposed rows by exact identity
+//              products (matrix-core work off the consumers' chain), written
+//              in place over those rows, then the gated operands of chunk
+//              i + 1 into registers;
+//   B1 .. B2   consumers: state update and outputs; producers: K and Q rows,
+//              V and T' of chunk i + 1 to LDS, then the loads of chunk i + 2;
 //   B2 .. B0   producers: the transposed rows, P and the decay of chunk i + 1.
 template <int D>
 struct ChanShared {
@@ -1139,15 +1139,23 @@ struct ChanShared {
     static constexpr int LDV = D / 2 + 8;  // row stride of the workgroup's value columns
     unsigned short Kg[2][C * LDK];         // K o 2^{lam'} (row factor 1/|k| for raw projections), hi / lo
     unsigned short Qg[2][C * LDK];         // Q o 2^{lam} (1/|q|), hi / lo
-    union {
-        unsigned short Kt[2][C * LDK];     // K o 2^{lam_C - lam} (1/|k|), hi / lo
-        u16x8 KtF[D / 16][2][2][64];       // the same transposed: [key tile][token k-step][hi/lo][lane]
-    } t;
+    // K o 2^{lam_C - lam} (1/|k|), hi / lo; from B0 to B1 of a chunk each
+    // 16-byte piece is overwritten by one lane's K^T fragment (chan_ktf_off)
+    unsigned short Kt[2][C * LDK];
     unsigned short V[C * LDV];
     u16x8 Tf[kTfragPerChunk];
     u16x8 Pf[kTfragPerChunk];
     float dec[D];                          // 2^{lam_C}
 };
+
+// Where the K^T A-fragment of key tile u, token k-step s, lane l sits in a
+// transposed-rows tile: in the 16-byte piece that lane loads as its operand
+// for token tile 2 s + (u % 2) and key block u / 2, so that the fragments of
+// the two key tiles of a block replace exactly the pieces they were made from.
+template <int D>
+__device__ __forceinline__ int chan_ktf_off(int u, int s, int l) {
+    return (32 * s + 16 * (u & 1) + (l & 15)) * ChanShared<D>::LDK + 32 * (u >> 1) + 8 * (l >> 4);
+}
 
 template <int D>
 constexpr int chan_threads() { return 4 * D; }  // D / 32 consumer waves of 16 value columns, as many producers
@@ -1191,6 +1199,7 @@ __global__ __launch_bounds__(chan_threads<D>(), 2) void k_chan_head(Problem p, c
     if (wave >= NW) {
         // ================= producers =================
         const int tid = threadIdx.x - NP;
+        const int pw = tid >> 6;  // the producer wave
         const bool ptd = p.order == GDN_PREDICT_THEN_DECAY;
         const unsigned short* kin = static_cast<const unsigned short*>(p.k);
         const unsigned short* qin = static_cast<const unsigned short*>(p.q);
@@ -1331,8 +1340,8 @@ __global__ __launch_bounds__(chan_threads<D>(), 2) void k_chan_head(Problem p, c
 #pragma unroll
             for (int j = 0; j < RUN; ++j) {
                 const int o = (t0r + j) * LDK + 8 * q;
-                *reinterpret_cast<u32x4*>(&sh.t.Kt[0][o]) = kt[j][0];
-                *reinterpret_cast<u32x4*>(&sh.t.Kt[1][o]) = kt[j][1];
+                *reinterpret_cast<u32x4*>(&sh.Kt[0][o]) = kt[j][0];
+                *reinterpret_cast<u32x4*>(&sh.Kt[1][o]) = kt[j][1];
             }
 #pragma unroll
             for (int k = 0; k < TFP; ++k) reinterpret_cast<u32x4*>(sh.Pf)[tid + NP * k] = pr[k];
@@ -1364,12 +1373,45 @@ __global__ __launch_bounds__(chan_threads<D>(), 2) void k_chan_head(Problem p, c
         // free to sink the formation towards the stores, which measured
         // faster than holding it before B1: the loads then have longer to
         // arrive)
+        // K^T fragments of chunk i: producer wave pw takes the hi (pw even) or
+        // lo rows of token tiles 2 s', 2 s' + 1 (s' = pw / 2); per key block
+        // v the lane loads one piece of each token tile, and the identity
+        // selecting key tile 2 v + uu turns them into that tile's A fragment
+        // (exact), which goes back over the piece of token tile 2 s' + uu.
+        // Only this wave reads these rows, and every store depends on all
+        // the wave's loads of its block through the products.
+        const int l = tid & 63, g4 = l >> 4, c16 = l & 15;
+        const int hl = pw & 1, sj = pw >> 1;
+        auto jobs = [&]() {
+#pragma unroll
+            for (int v = 0; v < TPW / 2; ++v) {
+                u16x8 ka[2];
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq)
+                    ka[qq] = *reinterpret_cast<const u16x8*>(&sh.Kt[hl][chan_ktf_off<D>(2 * v + qq, sj, l)]);
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    u16x8 idf;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        idf[e] = ((e >> 2) == uu && 4 * g4 + (e & 3) == c16) ? (unsigned short)0x3F80 : (unsigned short)0;
+                    u16x4 hv[2];
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        const f32x4 d = mfma(ka[qq], idf, zero4());
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) hv[qq][r] = (unsigned short)(__float_as_uint(d[r]) >> 16);
+                    }
+                    *reinterpret_cast<u16x8*>(&sh.Kt[hl][chan_ktf_off<D>(2 * v + uu, sj, l)]) = cat(hv[0], hv[1]);
+                }
+            }
+        };
         for (int i = 0; i < NC; ++i) {
             __syncthreads();  // B0
+            jobs();           // chunk i
             form();           // chunk i + 1
             __syncthreads();  // B1
             store_a();
-            __syncthreads();  // B1b
             issue(clampc(i + 2));
             issue_p(clampc(i + 2));
             __syncthreads();  // B2
@@ -1395,30 +1437,6 @@ __global__ __launch_bounds__(chan_threads<D>(), 2) void k_chan_head(Problem p, c
         const int64_t t0 = (int64_t)i * C;
         const int nt = (int)((T - t0) < C ? (T - t0) : C);
         __syncthreads();  // B0: chunk i staged
-
-        // K^T fragments: job (hl, s', u) turns token tiles 2s', 2s' + 1 of the
-        // transposed rows (hi or lo) into the A fragment of key rows 16u + c16
-        // by the identity selecting that key tile; wave w takes hl = w % 2,
-        // s' = w / 2 and every u
-        const int hl = w & 1, sj = w >> 1;
-        u16x8 ktf[TPW];
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            u16x8 idf;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                idf[e] = ((e >> 2) == (u & 1) && 4 * g4 + (e & 3) == c16) ? (unsigned short)0x3F80 : (unsigned short)0;
-            u16x4 hv[2];
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                const int m = 2 * sj + qq;
-                const u16x8 ka = *reinterpret_cast<const u16x8*>(&sh.t.Kt[hl][(16 * m + c16) * LDK + 32 * (u >> 1) + 8 * g4]);
-                const f32x4 d = mfma(ka, idf, zero4());
-#pragma unroll
-                for (int r = 0; r < 4; ++r) hv[qq][r] = (unsigned short)(__float_as_uint(d[r]) >> 16);
-            }
-            ktf[u] = cat(hv[0], hv[1]);
-        }
 
         // S^T as B operands of every k-step, split hi/lo
         u16x8 sbh[KS], sbl[KS];
@@ -1477,10 +1495,7 @@ __global__ __launch_bounds__(chan_threads<D>(), 2) void k_chan_head(Problem p, c
             }
             split4(d1, dh[m], dl[m]);
         }
-        __syncthreads();  // B1: the gated and transposed rows, V and T' of chunk i are read
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) sh.t.KtF[u][sj][hl][l] = ktf[u];
-        __syncthreads();  // B1b: K^T fragments complete
+        __syncthreads();  // B1: the gated rows, V and T' of chunk i are read, K^T fragments complete
 
         // S^T <- diag(2^{lam_C}) S^T + K^T Delta (A rows a = 16 u + c16)
 #pragma unroll
@@ -1488,8 +1503,8 @@ __global__ __launch_bounds__(chan_threads<D>(), 2) void k_chan_head(Problem p, c
             f32x4 acc = *reinterpret_cast<const f32x4*>(&sh.dec[16 * u + 4 * g4]) * Sacc[u];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const u16x8 kh = sh.t.KtF[u][s][0][l];
-                const u16x8 kl = sh.t.KtF[u][s][1][l];
+                const u16x8 kh = *reinterpret_cast<const u16x8*>(&sh.Kt[0][chan_ktf_off<D>(u, s, l)]);
+                const u16x8 kl = *reinterpret_cast<const u16x8*>(&sh.Kt[1][chan_ktf_off<D>(u, s, l)]);
                 const u16x8 bh_ = cat(dh[2 * s], dh[2 * s + 1]);
                 const u16x8 bl_ = cat(dl[2 * s], dl[2 * s + 1]);
                 acc = mfma(kh, bh_, acc);
