@@ -233,7 +233,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_bprep(BwdProblem a, CbWs ws) {
     static_assert(C * LDD * 4 <= KQB, "dL/d out fits over the K and Q rows");
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
     __shared__ __attribute__((aligned(16))) unsigned char kq[KQB];
-    __shared__ float Pscr[4][16 * 17];
     __shared__ __attribute__((aligned(16))) float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C], ggam[C];
     E* Ks = reinterpret_cast<E*>(kq);
     E* Qs = Ks + C * LDK;
@@ -404,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bprep(BwdProblem a, CbWs ws) {
             if (tb >= w) acc = blk(pk[tb], db[tb], acc);
         st4f(ws.Ef + ci * Rec<D>::kRows + ((size_t)(vb * 4 + w) * 64 + l) * 4, p.scale * acc);
     }
-    ut_inverse_lds(AT, Pscr[w]);
+    ut_inverse_lds(AT);
 
     // T and T^T, row-major, zero above (below) the diagonal
     float* Tg = ws.T + ci * Rec<D>::kTile;

@@ -110,12 +110,11 @@ __host__ __device__ constexpr int tslot(int m, int s) { return m < 2 ? m : 2 + 2
 // strictly lower off-diagonal blocks transposed and its diagonal blocks in
 // place; T replaces the diagonal blocks and fills the lower triangle) and
 // T' = T diag(beta) written as A-operand fragments, for both stage-1 kernels.
-// Called by all threads of the workgroup (it contains barriers); Pw is
-// 16 x 17 floats of scratch for the calling wave.
-__device__ __forceinline__ void ut_inverse_store(float* AT, float* Pw, const float* bsh, u16x8* dst) {
+// Called by all threads of the workgroup (it contains barriers).
+__device__ __forceinline__ void ut_inverse_store(float* AT, const float* bsh, u16x8* dst) {
     constexpr int LDA = C + 4;
     const int tid = threadIdx.x;
-    ut_inverse_lds(AT, Pw);
+    ut_inverse_lds(AT);
     // T' = T diag(beta): [slot(m, s)][hi/lo][lane] of 8 bf16; lane (row
     // 16m + lane % 16, group g), slot e -> column 32s + 4g + e (e < 4) or
     // 32s + 16 + 4g + e - 4; entries above the block diagonal are zero (the
@@ -161,10 +160,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* 
     // rows (bf16, row stride LDK) and then A and T as in the scalar kernel
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
     __shared__ __attribute__((aligned(16))) float bsh[C];
-    // channel log2 prefix, rows padded by 16 bytes against bank conflicts;
-    // once the scores are formed it is the inverse's per-wave scratch
+    // channel log2 prefix, rows padded by 16 bytes against bank conflicts
     __shared__ __attribute__((aligned(16))) float gt[C][D + 4];
-    static_assert(C * (D + 4) >= 4 * 16 * 17, "inverse scratch fits the prefix table");
     unsigned short* Ks = reinterpret_cast<unsigned short*>(AT);
 
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -425,11 +422,13 @@ __global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* 
     }
     __syncthreads();
 
-    ut_inverse_store(AT, &gt[0][0] + w * 16 * 17, bsh, tfrag + ch * kTfragPerChunk);
+    ut_inverse_store(AT, bsh, tfrag + ch * kTfragPerChunk);
 }
 
-// Scalar gate, stage 1 with a small LDS footprint (about 22 KiB, so about
-// seven workgroups share a CU): one 64 x 68 fp32 tile first holds the K rows
+// Scalar gate, stage 1 with a small LDS footprint (18.3 KiB, so eight
+// workgroups of four waves share a CU, and the chunk-heads of a head count
+// that is a multiple of 512 take whole rounds of the compute units): one
+// 64 x 68 fp32 tile first holds the K rows
 // (bf16) for the Gram product, then both the UT system A (strictly lower
 // blocks stored transposed in the upper triangle, diagonal blocks in place
 // until their inverse replaces them) and T = (I + A)^{-1} (lower triangle).
@@ -437,7 +436,6 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfrag, float* gates) {
     constexpr int LDA = C + 4;
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
-    __shared__ float Pscr[4][16 * 17];  // per-wave scratch of the diagonal inverse
     __shared__ __attribute__((aligned(16))) float gsh[C], gpsh[C], bsh[C];
     __shared__ __attribute__((aligned(16))) float rqsh[C], rksh[C];  // 1 / |q_t|, 1 / |k_t| (raw projections; else ones)
 
@@ -577,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
     }
     __syncthreads();
 
-    ut_inverse_store(AT, Pscr[w], bsh, tfrag + ch * kTfragPerChunk);
+    ut_inverse_store(AT, bsh, tfrag + ch * kTfragPerChunk);
 }
 
 // ---------------------------------------------------------------------------

@@ -59,18 +59,22 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
 // diagonal blocks and the lower triangle hold T (unit lower triangular, exact
 // zeros above the diagonal inside the diagonal blocks) and the upper
 // off-diagonal blocks still hold A transposed.  Called by all threads of a
-// four-wave workgroup (it contains barriers); Pw is 16 x 17 floats of scratch
-// for the calling wave.
+// four-wave workgroup (it contains barriers).  The strictly lower
+// off-diagonal blocks are free until the off-diagonal phase fills them, so
+// the diagonal phase keeps each wave's power of N in one of them (row stride
+// C + 4 spreads a lane group's column writes over every bank).
 //   diagonal block w: (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
 //     (N^16 = 0), three rounds of P <- P P, X <- X + X P on fp32 MFMA;
 //     accumulators (lane: column c16, rows 4 g4 + i) serve as B operands as
 //     they stand (instruction s contracts the indices 4G + s, G = lane / 16);
 //   off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
-__device__ __forceinline__ void ut_inverse_lds(float* AT, float* Pw) {
+__device__ __forceinline__ void ut_inverse_lds(float* AT) {
     constexpr int LDA = C + 4;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
     {
         float* Xb = &AT[(16 * w) * LDA + 16 * w];
+        // scratch block (1, 0), (2, 0), (3, 0) or (3, 1) for waves 0 .. 3
+        float* Pw = &AT[(16 * (w < 3 ? w + 1 : 3)) * LDA + 16 * (w < 3 ? 0 : 1)];
         f32x4 pm, xm;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -80,10 +84,10 @@ __device__ __forceinline__ void ut_inverse_lds(float* AT, float* Pw) {
 #pragma unroll
         for (int round = 0; round < 3; ++round) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Pw[(4 * g4 + r) * 17 + c16] = pm[r];
+            for (int r = 0; r < 4; ++r) Pw[(4 * g4 + r) * LDA + c16] = pm[r];
             f32x4 np = zero4();
 #pragma unroll
-            for (int q = 0; q < 4; ++q) np = mfma_f32(Pw[c16 * 17 + 4 * g4 + q], pm[q], np);
+            for (int q = 0; q < 4; ++q) np = mfma_f32(Pw[c16 * LDA + 4 * g4 + q], pm[q], np);
             pm = np;
 #pragma unroll
             for (int r = 0; r < 4; ++r) Xb[(4 * g4 + r) * LDA + c16] = xm[r];
