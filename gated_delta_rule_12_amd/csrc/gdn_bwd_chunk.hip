@@ -220,22 +220,29 @@ struct CbWs {
 // Q K^T column block jb = w (tiles (tb, w), tb >= w), five tiles either way;
 // the P tiles it holds are the A operands of E's block row w as they stand
 // (a lane holds P[16 tb + 4 g + r][16 w + c] = P^T[16 w + c][16 tb + 4 g + r]).
-// LDS: the K and Q rows, later dL/d out over them; the UT system.
+// LDS: the K and Q rows, later dL/d out over them; the UT system.  With
+// bf16 inputs the K rows sit in the UT tile itself (A goes there once the
+// Gram products are done) and dL/d out comes in two column halves, which
+// keeps the workgroup at 36 KiB, four per compute unit.
 template <int D, int DT>
-__global__ __launch_bounds__(kThreads, 2) void k_bprep(BwdProblem a, CbWs ws) {
+__global__ __launch_bounds__(kThreads, DT == GDN_BF16 ? 4 : 2) void k_bprep(BwdProblem a, CbWs ws) {
     using E = std::conditional_t<DT == GDN_BF16, uint16_t, float>;
     constexpr int NB = D / 16, MT = D / 64;
     constexpr int LDK = D + (DT == GDN_BF16 ? 8 : 4);
-    constexpr int LDD = D + 4;
+    constexpr bool KIN = DT == GDN_BF16;  // K rows in the UT tile
+    constexpr int NH = KIN ? 2 : 1;       // column parts of dL/d out
+    constexpr int DH = D / NH;
+    constexpr int LDD = DH + 4;
     constexpr int EP = 16 / sizeof(E);  // elements per 16-byte piece
     constexpr int PPR = D / EP;         // pieces per row
-    constexpr int KQB = 2 * C * LDK * (int)sizeof(E);
-    static_assert(C * LDD * 4 <= KQB, "dL/d out fits over the K and Q rows");
+    constexpr int KQB = (KIN ? 1 : 2) * C * LDK * (int)sizeof(E);
+    static_assert(C * LDD * 4 <= KQB, "dL/d out fits over the Q (and K) rows");
+    static_assert(!KIN || C * LDK * (int)sizeof(E) <= C * LDA * 4, "K rows fit the UT tile");
     __shared__ __attribute__((aligned(16))) float AT[C * LDA];
     __shared__ __attribute__((aligned(16))) unsigned char kq[KQB];
     __shared__ __attribute__((aligned(16))) float ghi[C], glo[C], gphi[C], gplo[C], gbeta[C], ggam[C];
-    E* Ks = reinterpret_cast<E*>(kq);
-    E* Qs = Ks + C * LDK;
+    E* Ks = KIN ? reinterpret_cast<E*>(AT) : reinterpret_cast<E*>(kq);
+    E* Qs = KIN ? reinterpret_cast<E*>(kq) : Ks + C * LDK;
     float* dOs = reinterpret_cast<float*>(kq);
 
     const Problem& p = a.p;
@@ -287,28 +294,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_bprep(BwdProblem a, CbWs ws) {
         else return ld4f(X + t * LDK + d0);
     };
     // Gram row block m = w: A_tj = beta_t Atilde_tj, Atilde_tj = e^{l'_t - l_j}
-    // k_t.k_j (j < t), Atilde^T[j][t] to the workspace, A in the inverse's layout
-    for (int nb = 0; nb <= w; ++nb) {
+    // k_t.k_j (j < t), Atilde^T[j][t] to the workspace; A goes to the tile in
+    // the inverse's layout once the K rows are dead (tiles nb <= w kept)
+    f32x4 av[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        av[nb] = zero4();
+        if (nb > w) continue;
         const int m = w;
         f32x4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
             acc = blk(row4(Ks, 16 * m + c16, 16 * kb + 4 * g4), row4(Ks, 16 * nb + c16, 16 * kb + 4 * g4), acc);
         const int j = 16 * nb + c16;
-        f32x4 av, tv;
+        f32x4 tv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * m + 4 * g4 + r;
             tv[r] = j < t ? ratio(gphi[t], gplo[t], ghi[j], glo[j]) * acc[r] : 0.f;
-            av[r] = gbeta[t] * tv[r];
+            av[nb][r] = gbeta[t] * tv[r];
         }
         st4f(ws.AtT + ci * Rec<D>::kTile + j * C + 16 * m + 4 * g4, tv);
-        if (nb < m) {
-            st4f(&AT[j * LDA + 16 * m + 4 * g4], av);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) AT[(16 * m + 4 * g4 + r) * LDA + j] = av[r];
-        }
     }
     // Q K^T column block jb = w: P_tj = e^{l_t - l_j} q_t.k_j (j <= t), kept
     // (pk[tb], tb >= w) and stored as P^T[j][t]
@@ -371,23 +377,56 @@ __global__ __launch_bounds__(kThreads, 2) void k_bprep(BwdProblem a, CbWs ws) {
                 if constexpr (DT == GDN_BF16) qa[mi][tb][q] = gdn_bf16_to_f32(x);
                 else qa[mi][tb][q] = x;
             }
-    __syncthreads();  // the K and Q rows are dead
-    constexpr int OP = C * (D / 4) / kThreads;
+    // dL/d out columns DH hh .. + DH - 1 into registers (rows past the end zero)
+    constexpr int OP = C * (DH / 4) / kThreads;
+    f32x4 dov[OP];
+    auto fetch_dout = [&](int hh) {
 #pragma unroll
-    for (int i = 0; i < OP; ++i) {
-        const int e = tid + kThreads * i, t = e / (D / 4), pc = e % (D / 4);
-        f32x4 x = ld4f(a.dout + (row0 + (int64_t)min(t, nt - 1) * p.H) * D + 4 * pc);
-        if (t >= nt) x = zero4();
-        st4f(&dOs[t * LDD + 4 * pc], x);
+        for (int i = 0; i < OP; ++i) {
+            const int e = tid + kThreads * i, t = e / (DH / 4), pc = e % (DH / 4);
+            dov[i] = ld4f(a.dout + (row0 + (int64_t)min(t, nt - 1) * p.H) * D + DH * hh + 4 * pc);
+            if (t >= nt) dov[i] = zero4();
+        }
+    };
+    auto store_dout = [&]() {
+#pragma unroll
+        for (int i = 0; i < OP; ++i) {
+            const int e = tid + kThreads * i, t = e / (DH / 4), pc = e % (DH / 4);
+            st4f(&dOs[t * LDD + 4 * pc], dov[i]);
+        }
+    };
+    __syncthreads();  // the K and Q rows are dead
+    // A into the tile: blocks left of the diagonal transposed into the upper
+    // triangle (A_tj at (j, t)), the diagonal block in place
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        if (nb > w) continue;
+        const int j = 16 * nb + c16;
+        if (nb < w) {
+            st4f(&AT[j * LDA + 16 * w + 4 * g4], av[nb]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) AT[(16 * w + 4 * g4 + r) * LDA + j] = av[nb][r];
+        }
     }
+    fetch_dout(0);
+    store_dout();
     __syncthreads();
     // E block row w (all value blocks) and H of the wave's key tiles
     for (int vb = 0; vb < NB; ++vb) {
+        if (NH == 2 && vb == NB / 2) {
+            // the second column half over the first
+            fetch_dout(1);
+            __syncthreads();
+            store_dout();
+            __syncthreads();
+        }
+        const int vc = 16 * (vb % (NB / NH));  // column of the value block in the staged part
         f32x4 db[4], gb[4];  // B operands dO[16 tb + 4 g4 + q][16 vb + c16], and scale gamma_t times it
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) db[tb][q] = dOs[(16 * tb + 4 * g4 + q) * LDD + 16 * vb + c16];
+            for (int q = 0; q < 4; ++q) db[tb][q] = dOs[(16 * tb + 4 * g4 + q) * LDD + vc + c16];
             gb[tb] = p.scale * *reinterpret_cast<const f32x4*>(&ggam[16 * tb + 4 * g4]) * db[tb];
         }
 #pragma unroll
