@@ -39,8 +39,8 @@
 //   k_bprep, one workgroup per chunk: gate prefix, Gram K K^T and Q K^T, A,
 //     T by the in-LDS UT inverse; T, T^T and P^T in the workspace, with K
 //     and Q as transposed fragments (K[16 tb + 4 g + q][16 m + c] per lane).
-//   k_bchain, one workgroup per (head, 16-row slice of the state) and
-//     direction: the forward chain carries S over the chunks and stores each
+//   k_bchain, one workgroup per (head, one or two 16-row slices of the
+//     state) and direction: the forward chain carries S over the chunks and stores each
 //     chunk's entry state, U and Delta; the reverse chain carries dS back and
 //     stores each chunk's dS_end, dDelta and dU' and writes dv and dS_0.  Rows
 //     of the state are independent given T, K and the gates, so a slice holds
@@ -463,14 +463,15 @@ __global__ __launch_bounds__(kThreads, DT == GDN_BF16 ? 4 : 2) void k_bprep(BwdP
 // ---------------------------------------------------------------------------
 // k_bchain: the forward state chain and the reverse adjoint chain
 // ---------------------------------------------------------------------------
-// Per-wave LDS gate rows of the current chunk.
+// LDS of a chain workgroup carrying NS adjacent 16-row slices of the state.
+template <int NS>
 struct ChainShared {
-    f32x4 red[4][4][64];  // [wave][token tile][lane]: partial K S^T (or K dS^T)
-    f32x4 xch[4][64];     // [token tile][lane]: Delta R (forward) / dDelta (reverse)
-    f32x4 xch2[4][64];    // reverse: -gamma' beta dU'
-    float vs[2][16][C + 4];      // forward: V of the slice, [chunk parity][value][token]
-    float tp[4][5][16][20];      // per wave: 16 x 16 tiles being transposed for stores
-    float g[2][8][C];     // [chunk parity][row kG*][token]: gate rows
+    f32x4 red[NS][4][4][64];  // [slice][wave][token tile][lane]: partial K S^T (or K dS^T)
+    f32x4 xch[NS][4][64];     // [slice][token tile][lane]: Delta R (forward) / dDelta (reverse)
+    f32x4 xch2[NS][4][64];    // reverse: -gamma' beta dU'
+    float vs[2][16 * NS][C + 4];  // forward: V of the slices, [chunk parity][value][token]
+    float tp[4][5][16][20];   // per wave: 16 x 16 tiles being transposed for stores
+    float g[2][8][C];         // [chunk parity][row kG*][token]: gate rows
 };
 
 // A chunk's gate rows in LDS (written by the preparation kernel, staged
@@ -483,7 +484,7 @@ struct RowF {
 };
 
 // Operands of a chain step, all fetched one chunk ahead (the next chunk's
-// while the current one computes), the gates and the V slice two ahead (they
+// while the current one computes), the gates and the V slices two ahead (they
 // are turned into LDS rows at the end of the step before their chunk's);
 // rows past the sequence end are read at the last real row and zeroed at
 // use.  A chunk's workspace stores are issued at the start of the next chunk.
@@ -495,7 +496,9 @@ struct RowF {
 // issued at the start, its twenty-odd loads of every wave of the compute
 // unit queued in the vector-memory path ahead of the step's first products
 // (cycle stamps: ≈3 000 cycles of a ≈14 500-cycle step; the chain measured
-// 9 % faster with the later issue).
+// 9 % faster with the later issue).  The K, K^T and T operands serve every
+// slice of the workgroup: with two slices a workgroup, the compute unit
+// issues half the loads for the same products.
 template <int D, int DT>
 struct FwdIn {
     static constexpr int MT = D / 64;
@@ -503,38 +506,43 @@ struct FwdIn {
     f32x4 tr[4];         // T[16 w + c16][16 jb + 4 g4 ..]
     R8<DT> kt[MT][2];    // K^T fragments of the wave's key tiles, token blocks in pairs
 };
-template <int DT>
+template <int DT, int NS>
 struct GateIn {
     f32x2 gr;            // gate rows: row tid / 32, tokens 2 (tid % 32) ..
-    R4<DT> vr;           // forward: V[t][r0 + 4 p ..] of this thread's (t, p) = (tid / 4, tid % 4)
+    R4<DT> vr[NS];       // forward: V[t][r0 + 16 s + 4 p ..] of this thread's (t, p) = (tid / 4, tid % 4)
 };
-template <int D, int DT>
+template <int D, int DT, int NS>
 struct RevIn {
     static constexpr int MT = D / 64;
     R4<DT> kx[4][MT];
-    f32x4 ef;            // E tile w of the slice
-    f32x4 hf[MT];        // H tiles of the wave's key tiles
+    f32x4 ef[NS];        // E tile w of each slice
+    f32x4 hf[NS][MT];    // H tiles of the wave's key tiles, each slice
     f32x4 tt[4];         // T^T[16 w + c16][16 jb + 4 g4 ..]
     R8<DT> kt[MT][2];
 };
 
-template <int D, int DT>
+template <int D, int DT, int NS>
 struct ChainCtx {
     static constexpr int NB = D / 16, MT = D / 64;
+    using Sh = ChainShared<NS>;
     const BwdProblem& a;
     const CbWs& ws;
     int64_t bl, b, h, bh;
-    int rho, r0, w, l, g4, c16, NC, tid;
+    int rho, r0, w, l, g4, c16, NC, tid;  // rho: the first slice (rows r0 = 16 rho ..)
     __device__ int64_t row0(int c) const { return (b * a.p.T + (int64_t)c * C) * a.p.H + h; }
     __device__ int ntok(int c) const { return (int)min<int64_t>(C, a.p.T - (int64_t)c * C); }
     __device__ int64_t cidx(int c) const { return bl * NC + c; }
-    // gate rows (and, forward, the V slice) of chunk c, clamped to a real chunk
-    __device__ void load_gate(GateIn<DT>& x, int c, bool fwd) const {
+    // gate rows (and, forward, the V slices) of chunk c, clamped to a real chunk
+    __device__ void load_gate(GateIn<DT, NS>& x, int c, bool fwd) const {
         c = min(max(c, 0), NC - 1);
         const int64_t r = row0(c);
         const int nt = ntok(c);
         x.gr = *reinterpret_cast<const f32x2*>(ws.Gr + cidx(c) * Rec<D>::kGr + 2 * tid);
-        if (fwd) x.vr = ldr<DT>(a.p.v, (r + (int64_t)min(tid >> 2, nt - 1) * a.p.H) * D + r0 + 4 * (tid & 3));
+        if (fwd) {
+            const int64_t o = (r + (int64_t)min(tid >> 2, nt - 1) * a.p.H) * D + r0 + 4 * (tid & 3);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) x.vr[s] = ldr<DT>(a.p.v, o + 16 * s);
+        }
     }
     template <class In>
     __device__ void load_common(In& x, int c) const {
@@ -565,72 +573,88 @@ struct ChainCtx {
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) x.tr[jb] = ld4f(ws.T + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
     }
-    __device__ void load(RevIn<D, DT>& x, int c) const {
+    __device__ void load(RevIn<D, DT, NS>& x, int c) const {
         c = min(max(c, 0), NC - 1);
         load_common(x, c);
         const int64_t ci = cidx(c);
-        x.ef = ld4f(ws.Ef + ci * Rec<D>::kRows + ((size_t)(rho * 4 + w) * 64 + l) * 4);
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-            x.hf[mi] = ld4f(ws.Hf + ci * Rec<D>::kHf + ((size_t)(rho * NB + w * MT + mi) * 64 + l) * 4);
+        for (int s = 0; s < NS; ++s) {
+            x.ef[s] = ld4f(ws.Ef + ci * Rec<D>::kRows + ((size_t)((rho + s) * 4 + w) * 64 + l) * 4);
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi)
+                x.hf[s][mi] = ld4f(ws.Hf + ci * Rec<D>::kHf + ((size_t)((rho + s) * NB + w * MT + mi) * 64 + l) * 4);
+        }
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) x.tt[jb] = ld4f(ws.TT + ci * Rec<D>::kTile + (16 * w + c16) * C + 16 * jb + 4 * g4);
     }
     // K^T fragment of key tile mi, token block tb
     template <class In>
     __device__ f32x4 ktf(const In& x, int mi, int tb) const { return cvt<DT>(x.kt[mi][tb >> 1].h[tb & 1]); }
-    // partial K S^T over the wave's key tiles for every token tile, to LDS
+    // partial K S^T over the wave's key tiles for every token tile and slice,
+    // to LDS (each K operand converted once for every slice)
     template <class In>
-    __device__ void partial_KS(ChainShared& sh, const In& x, const f32x4 (&St)[MT], int nt) const {
+    __device__ void partial_KS(Sh& sh, const In& x, const f32x4 (&St)[NS][MT], int nt) const {
 #pragma unroll
         for (int at = 0; at < 4; ++at) {
-            f32x4 acc = zero4();
+            f32x4 acc[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) acc[s] = zero4();
             const float ok = 16 * at + c16 < nt ? 1.f : 0.f;
 #pragma unroll
-            for (int mi = 0; mi < MT; ++mi) acc = blk(ok * cvt<DT>(x.kx[at][mi]), St[mi], acc);
-            sh.red[w][at][l] = acc;
+            for (int mi = 0; mi < MT; ++mi) {
+                const f32x4 ka = ok * cvt<DT>(x.kx[at][mi]);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) acc[s] = blk(ka, St[s][mi], acc[s]);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) sh.red[s][w][at][l] = acc[s];
         }
     }
     // the state as the gradient kernel's fragments: lane (g, c) holds
-    // S[r0 + c][key_of(w, mi, 4 g + r)], the fragment lane 16 (c / 4) + 4 g + r
+    // S[r0 + 16 s + c][key_of(w, mi, 4 g + r)], the fragment lane 16 (c / 4) + 4 g + r
     // wants it in element c % 4; transposed through the wave's tile
-    __device__ void store_state(ChainShared& sh, float* dst, const f32x4 (&St)[MT]) const {
+    __device__ void store_state(Sh& sh, float* dst, const f32x4 (&St)[NS][MT]) const {
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-            float(*X)[20] = sh.tp[w][mi];
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) X[4 * g4 + r][c16] = St[mi][r];
-            const f32x4 v = *reinterpret_cast<const f32x4*>(&X[c16][4 * g4]);
-            st4f(dst + ((size_t)(rho * NB + w * MT + mi) * 64 + l) * 4, v);
-        }
+            for (int mi = 0; mi < MT; ++mi) {
+                float(*X)[20] = sh.tp[w][mi];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) X[4 * g4 + r][c16] = St[s][mi][r];
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&X[c16][4 * g4]);
+                st4f(dst + ((size_t)((rho + s) * NB + w * MT + mi) * 64 + l) * 4, v);
+            }
     }
     // a token tile w of a C x D row block (rows 16 w + 4 g4 + q, column
-    // r0 + c16) as 16-byte row pieces: lane l takes row l / 4, columns
-    // r0 + 4 (l % 4) ..; base points at row 0, column 0, rows ld apart
-    __device__ void store_rows(ChainShared& sh, int slot, float* base, int64_t ld, const f32x4& x, int nvalid) const {
+    // r0 + 16 s + c16) as 16-byte row pieces: lane l takes row l / 4, columns
+    // r0 + 16 s + 4 (l % 4) ..; base points at row 0, column 0, rows ld apart
+    __device__ void store_rows(Sh& sh, int slot, float* base, int64_t ld, const f32x4& x, int nvalid, int s) const {
         float(*X)[20] = sh.tp[w][slot];
 #pragma unroll
         for (int q = 0; q < 4; ++q) X[4 * g4 + q][c16] = x[q];
         const int i = l >> 2, j = l & 3;
         const f32x4 v = *reinterpret_cast<const f32x4*>(&X[i][4 * j]);
-        if (16 * w + i < nvalid) st4f(base + (int64_t)(16 * w + i) * ld + r0 + 4 * j, v);
+        if (16 * w + i < nvalid) st4f(base + (int64_t)(16 * w + i) * ld + r0 + 16 * s + 4 * j, v);
     }
     // this thread's two gate-row entries into a parity's LDS rows
-    __device__ void gates_to_lds(float* gw, const GateIn<DT>& x) const {
+    __device__ void gates_to_lds(float* gw, const GateIn<DT, NS>& x) const {
         *reinterpret_cast<f32x2*>(gw + 2 * tid) = x.gr;
     }
-    // the slice of V (this thread's four values of one token) into LDS,
-    // transposed to [value][token]
-    __device__ void v_to_lds(ChainShared& sh, int buf, const GateIn<DT>& x, int nt) const {
+    // the slices of V (this thread's four values of one token per slice)
+    // into LDS, transposed to [value][token]
+    __device__ void v_to_lds(Sh& sh, int buf, const GateIn<DT, NS>& x, int nt) const {
         const int t = tid >> 2, j = tid & 3;
-        const f32x4 v = t < nt ? cvt<DT>(x.vr) : zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sh.vs[buf][4 * j + e][t] = v[e];
+        for (int s = 0; s < NS; ++s) {
+            const f32x4 v = t < nt ? cvt<DT>(x.vr[s]) : zero4();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sh.vs[buf][16 * s + 4 * j + e][t] = v[e];
+        }
     }
 };
 
-template <int D, int DT>
-__device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 (&St)[D / 64]) {
+template <int D, int DT, int NS>
+__device__ void chain_forward(const ChainCtx<D, DT, NS>& cx, ChainShared<NS>& sh, f32x4 (&St)[NS][D / 64]) {
     constexpr int MT = D / 64;
     const CbWs& ws = cx.ws;
     const int w = cx.w, l = cx.l, g4 = cx.g4, c16 = cx.c16;
@@ -638,7 +662,7 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     // copies between them, so a step waits only for the previous step's
     // fetches)
     FwdIn<D, DT> xa, xb;
-    GateIn<DT> ga, gb;
+    GateIn<DT, NS> ga, gb;
     cx.load(xa, 0);
     cx.load_gate(ga, 0, true);
     cx.gates_to_lds(&sh.g[0][0][0], ga);
@@ -646,33 +670,47 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
     cx.load_gate(ga, 1, true);
     // the previous chunk's U and Delta tiles, stored at the next chunk's start
     // (chunk 0's slots first take zeros, overwritten in order by the same lane)
-    f32x4 pU = zero4(), pD = zero4();
+    f32x4 pU[NS], pD[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) pU[s] = pD[s] = zero4();
     int64_t pci = cx.cidx(0);
     // chunk c from cur; fetches chunk c + 1 into nxt and the gates of chunk
     // c + 2 into g2; turns g1 (chunk c + 1) into LDS rows at the end
-    auto step = [&](int c, const FwdIn<D, DT>& cur, FwdIn<D, DT>& nxt, const GateIn<DT>& g1, GateIn<DT>& g2) {
+    auto step = [&](int c, const FwdIn<D, DT>& cur, FwdIn<D, DT>& nxt, const GateIn<DT, NS>& g1, GateIn<DT, NS>& g2) {
         const RowF rf{&sh.g[c & 1][0][0]};
         const int64_t ci = cx.cidx(c);
         const int nt = cx.ntok(c);
-        cx.store_rows(sh, 2, ws.U + pci * Rec<D>::kRows, D, pU, C);
-        cx.store_rows(sh, 3, ws.Dl + pci * Rec<D>::kRows, D, pD, C);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            cx.store_rows(sh, 2, ws.U + pci * Rec<D>::kRows, D, pU[s], C, s);
+            cx.store_rows(sh, 3, ws.Dl + pci * Rec<D>::kRows, D, pD[s], C, s);
+        }
         cx.store_state(sh, ws.Sf + ci * Rec<D>::kState, St);
         cx.partial_KS(sh, cur, St, nt);
         __syncthreads();
         // U' tiles jb <= w and the Delta tile w = sum_jb T[w][jb] U'[jb]
-        f32x4 dl = zero4();
+        f32x4 dl[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) dl[s] = zero4();
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             if (jb > w) continue;
-            const f32x4 X = sh.red[0][jb][l] + sh.red[1][jb][l] + sh.red[2][jb][l] + sh.red[3][jb][l];
             const f32x4 gp = rf.v4(kGgamp, 16 * jb + 4 * g4), bt = rf.v4(kGbeta, 16 * jb + 4 * g4);
-            const f32x4 U = *reinterpret_cast<const f32x4*>(&sh.vs[c & 1][c16][16 * jb + 4 * g4]) - gp * X;
-            if (jb == w) pU = U;
-            dl = blk(cur.tr[jb], bt * U, dl);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const f32x4 X = sh.red[s][0][jb][l] + sh.red[s][1][jb][l] + sh.red[s][2][jb][l] + sh.red[s][3][jb][l];
+                const f32x4 U = *reinterpret_cast<const f32x4*>(&sh.vs[c & 1][16 * s + c16][16 * jb + 4 * g4]) - gp * X;
+                if (jb == w) pU[s] = U;
+                dl[s] = blk(cur.tr[jb], bt * U, dl[s]);
+            }
         }
-        pD = dl;
+        const f32x4 Rw = rf.v4(kGR, 16 * w + 4 * g4);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            pD[s] = dl[s];
+            sh.xch[s][w][l] = Rw * dl[s];
+        }
         pci = ci;
-        sh.xch[w][l] = rf.v4(kGR, 16 * w + 4 * g4) * dl;
         __syncthreads();
         cx.load(nxt, c + 1);
         cx.load_gate(g2, c + 2, true);
@@ -680,12 +718,19 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
         const float gC = rf.gC();
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
-            f32x4 acc = gC * St[mi];
+            f32x4 acc[NS];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc = blk(cx.ktf(cur, mi, tb), sh.xch[tb][l], acc);
-            St[mi] = acc;
+            for (int s = 0; s < NS; ++s) acc[s] = gC * St[s][mi];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const f32x4 ka = cx.ktf(cur, mi, tb);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) acc[s] = blk(ka, sh.xch[s][tb][l], acc[s]);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) St[s][mi] = acc[s];
         }
-        // the next chunk's gate rows and V slice while the update multiplies
+        // the next chunk's gate rows and V slices while the update multiplies
         // (every wave is past this chunk's first barrier, the last reader of
         // the buffers written here)
         const int nn = cx.ntok(min(c + 1, cx.NC - 1));
@@ -698,57 +743,79 @@ __device__ void chain_forward(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
         step(c + 1, xb, xa, gb, ga);
     }
     if (c < cx.NC) step(c, xa, xb, ga, gb);
-    cx.store_rows(sh, 2, ws.U + pci * Rec<D>::kRows, D, pU, C);
-    cx.store_rows(sh, 3, ws.Dl + pci * Rec<D>::kRows, D, pD, C);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        cx.store_rows(sh, 2, ws.U + pci * Rec<D>::kRows, D, pU[s], C, s);
+        cx.store_rows(sh, 3, ws.Dl + pci * Rec<D>::kRows, D, pD[s], C, s);
+    }
 }
 
-template <int D, int DT>
-__device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 (&St)[D / 64]) {
+template <int D, int DT, int NS>
+__device__ void chain_reverse(const ChainCtx<D, DT, NS>& cx, ChainShared<NS>& sh, f32x4 (&St)[NS][D / 64]) {
     constexpr int MT = D / 64;
     const BwdProblem& a = cx.a;
     const Problem& p = a.p;
     const CbWs& ws = cx.ws;
     const int w = cx.w, l = cx.l, g4 = cx.g4;
-    RevIn<D, DT> xa, xb;
-    GateIn<DT> ga, gb;
+    RevIn<D, DT, NS> xa, xb;
+    GateIn<DT, NS> ga, gb;
     cx.load(xa, cx.NC - 1);
     cx.load_gate(ga, cx.NC - 1, false);
     cx.gates_to_lds(&sh.g[(cx.NC - 1) & 1][0][0], ga);
     cx.load_gate(ga, cx.NC - 2, false);
     // the previous step's dDelta, dU' and dv tiles, stored at the next step's
     // start (the first step's slots first take zeros, then the real values)
-    f32x4 pdD = zero4(), pdU = zero4(), pdv = zero4();
+    f32x4 pdD[NS], pdU[NS], pdv[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) pdD[s] = pdU[s] = pdv[s] = zero4();
     int64_t pci = cx.cidx(cx.NC - 1), prow = cx.row0(cx.NC - 1);
     int pnt = 0;
     // chunk c from cur; fetches chunk c - 1 into nxt and the gates of chunk
     // c - 2 into g2; turns g1 (chunk c - 1) into LDS rows at the end
-    auto step = [&](int c, const RevIn<D, DT>& cur, RevIn<D, DT>& nxt, const GateIn<DT>& g1, GateIn<DT>& g2) {
+    auto step = [&](int c, const RevIn<D, DT, NS>& cur, RevIn<D, DT, NS>& nxt, const GateIn<DT, NS>& g1,
+                    GateIn<DT, NS>& g2) {
         const RowF rf{&sh.g[c & 1][0][0]};
         const int64_t ci = cx.cidx(c);
         const int nt = cx.ntok(c);
-        cx.store_rows(sh, 2, ws.dDl + pci * Rec<D>::kRows, D, pdD, C);
-        cx.store_rows(sh, 3, ws.dUp + pci * Rec<D>::kRows, D, pdU, C);
-        cx.store_rows(sh, 4, a.dv + prow * D, p.H * D, pdv, pnt);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            cx.store_rows(sh, 2, ws.dDl + pci * Rec<D>::kRows, D, pdD[s], C, s);
+            cx.store_rows(sh, 3, ws.dUp + pci * Rec<D>::kRows, D, pdU[s], C, s);
+            cx.store_rows(sh, 4, a.dv + prow * D, p.H * D, pdv[s], pnt, s);
+        }
         cx.store_state(sh, ws.dSf + ci * Rec<D>::kState, St);
         cx.partial_KS(sh, cur, St, nt);
         __syncthreads();
         // dDelta tile w = diag(R) K dS^T + E_w
-        const f32x4 Y = sh.red[0][w][l] + sh.red[1][w][l] + sh.red[2][w][l] + sh.red[3][w][l];
-        const f32x4 dd = rf.v4(kGR, 16 * w + 4 * g4) * Y + cur.ef;
-        sh.xch[w][l] = dd;
-        pdD = dd;
+        const f32x4 Rw = rf.v4(kGR, 16 * w + 4 * g4);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const f32x4 Y = sh.red[s][0][w][l] + sh.red[s][1][w][l] + sh.red[s][2][w][l] + sh.red[s][3][w][l];
+            const f32x4 dd = Rw * Y + cur.ef[s];
+            sh.xch[s][w][l] = dd;
+            pdD[s] = dd;
+        }
         __syncthreads();
         cx.load(nxt, c - 1);
         cx.load_gate(g2, c - 2, false);
         // dU' tile w = sum_{jb >= w} T^T[w][jb] dDelta[jb]; dv = beta dU'
-        f32x4 du = zero4();
+        f32x4 du[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) du[s] = zero4();
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
-            if (jb >= w) du = blk(cur.tt[jb], sh.xch[jb][l], du);
+            if (jb >= w) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) du[s] = blk(cur.tt[jb], sh.xch[s][jb][l], du[s]);
+            }
         const f32x4 bt = rf.v4(kGbeta, 16 * w + 4 * g4);
-        sh.xch2[w][l] = -(rf.v4(kGgamp, 16 * w + 4 * g4) * bt) * du;
-        pdU = du;
-        pdv = bt * du;
+        const f32x4 mgb = -(rf.v4(kGgamp, 16 * w + 4 * g4) * bt);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            sh.xch2[s][w][l] = mgb * du[s];
+            pdU[s] = du[s];
+            pdv[s] = bt * du[s];
+        }
         pci = ci;
         prow = cx.row0(c);
         pnt = nt;
@@ -757,10 +824,17 @@ __device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
         const float gC = rf.gC();
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
-            f32x4 acc = gC * St[mi] + cur.hf[mi];
+            f32x4 acc[NS];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc = blk(cx.ktf(cur, mi, tb), sh.xch2[tb][l], acc);
-            St[mi] = acc;
+            for (int s = 0; s < NS; ++s) acc[s] = gC * St[s][mi] + cur.hf[s][mi];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const f32x4 ka = cx.ktf(cur, mi, tb);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) acc[s] = blk(ka, sh.xch2[s][tb][l], acc[s]);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) St[s][mi] = acc[s];
         }
         // the next chunk's gate rows while the update multiplies (every wave
         // is past this chunk's first barrier, the last reader of the buffer)
@@ -772,28 +846,34 @@ __device__ void chain_reverse(const ChainCtx<D, DT>& cx, ChainShared& sh, f32x4 
         step(c - 1, xb, xa, gb, ga);
     }
     if (c == 0) step(0, xa, xb, ga, gb);
-    cx.store_rows(sh, 2, ws.dDl + pci * Rec<D>::kRows, D, pdD, C);
-    cx.store_rows(sh, 3, ws.dUp + pci * Rec<D>::kRows, D, pdU, C);
-    cx.store_rows(sh, 4, a.dv + prow * D, p.H * D, pdv, pnt);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        cx.store_rows(sh, 2, ws.dDl + pci * Rec<D>::kRows, D, pdD[s], C, s);
+        cx.store_rows(sh, 3, ws.dUp + pci * Rec<D>::kRows, D, pdU[s], C, s);
+        cx.store_rows(sh, 4, a.dv + prow * D, p.H * D, pdv[s], pnt, s);
+    }
 }
 
-template <int D, int DT>
-__global__ __launch_bounds__(kThreads, 2) void k_bchain(BwdProblem a, CbWs ws) {
+// NS adjacent 16-row slices of a head's state per workgroup and direction:
+// two on heads x slices that fill the compute units that way, one otherwise.
+template <int D, int DT, int NS>
+__global__ __launch_bounds__(kThreads, NS == 1 ? 2 : 1) void k_bchain(BwdProblem a, CbWs ws) {
     constexpr int NB = D / 16, MT = D / 64;
-    __shared__ ChainShared sh;
+    constexpr int NSL = NB / NS;  // workgroups per head and direction
+    __shared__ ChainShared<NS> sh;
     const Problem& p = a.p;
     // workgroups go to the eight XCDs in turn; the logical order (head,
-    // direction, slice) is laid over them so that consecutive logical
-    // indices, the 2 NB workgroups of a head that read the same chunk
+    // direction, slice group) is laid over them so that consecutive logical
+    // indices, the 2 NSL workgroups of a head that read the same chunk
     // operands, share an XCD and its L2
-    const int64_t N = 2 * a.nbh * NB;
+    const int64_t N = 2 * a.nbh * NSL;
     const int64_t lin = N % 8 == 0 ? (blockIdx.x % 8) * (N / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int64_t head = lin / (2 * NB);
-    const int rem = (int)(lin - head * 2 * NB);
-    const bool rev = rem < NB;
-    ChainCtx<D, DT> cx{a, ws};
+    const int64_t head = lin / (2 * NSL);
+    const int rem = (int)(lin - head * 2 * NSL);
+    const bool rev = rem < NSL;
+    ChainCtx<D, DT, NS> cx{a, ws};
     cx.bl = head;
-    cx.rho = rev ? rem : rem - NB;
+    cx.rho = NS * (rev ? rem : rem - NSL);
     cx.r0 = 16 * cx.rho;
     cx.bh = a.bh0 + cx.bl;
     cx.b = cx.bh / p.H;
@@ -805,23 +885,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_bchain(BwdProblem a, CbWs ws) {
     cx.g4 = cx.l >> 4;
     cx.c16 = cx.l & 15;
     cx.NC = p.NC;
-    // the slice's state rows as accumulator tiles of S^T: tile mi holds
-    // S[r0 + c16][key_of(w, mi, 4 g4 + r)]
-    f32x4 St[MT];
+    // the slices' state rows as accumulator tiles of S^T: tile mi of slice s
+    // holds S[r0 + 16 s + c16][key_of(w, mi, 4 g4 + r)]
+    f32x4 St[NS][MT];
     const float* init = rev ? a.ds_out : p.s0;
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-        St[mi] = init ? ld4f(init + ((cx.bh * D + cx.r0 + cx.c16) * D) + key_of<D>(cx.w, mi, 4 * cx.g4)) : zero4();
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+            St[s][mi] = init ? ld4f(init + ((cx.bh * D + cx.r0 + 16 * s + cx.c16) * D) + key_of<D>(cx.w, mi, 4 * cx.g4))
+                             : zero4();
     if (p.NC > 0) {
-        if (rev) chain_reverse<D, DT>(cx, sh, St);
-        else chain_forward<D, DT>(cx, sh, St);
+        if (rev) chain_reverse<D, DT, NS>(cx, sh, St);
+        else chain_forward<D, DT, NS>(cx, sh, St);
     }
     if (rev && a.ds0) {
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-            st4f(a.ds0 + ((cx.bh * D + cx.r0 + cx.c16) * D) + key_of<D>(cx.w, mi, 4 * cx.g4), St[mi]);
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi)
+                st4f(a.ds0 + ((cx.bh * D + cx.r0 + 16 * s + cx.c16) * D) + key_of<D>(cx.w, mi, 4 * cx.g4), St[s][mi]);
     }
 }
+
+// Slices per chain workgroup: two once the heads' slice pairs and both
+// directions still give a workgroup to every compute unit.
+inline int chain_slices(int64_t nbh, int64_t D) { return nbh * (D / 16) >= 256 ? 2 : 1; }
 
 // ---------------------------------------------------------------------------
 // k_bgrad: dq, dk, dbeta and dalpha of one chunk
@@ -1213,7 +1302,10 @@ hipError_t launch_chunked(const BwdProblem& a, const CbWs& ws, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_begin(a.p.timer, "k_bchain", st);
-    hipLaunchKernelGGL((k_bchain<D, DT>), dim3((unsigned)(2 * a.nbh * (D / 16))), dim3(kThreads), 0, st, a, ws);
+    if (chain_slices(a.nbh, D) == 2)
+        hipLaunchKernelGGL((k_bchain<D, DT, 2>), dim3((unsigned)(a.nbh * (D / 16))), dim3(kThreads), 0, st, a, ws);
+    else
+        hipLaunchKernelGGL((k_bchain<D, DT, 1>), dim3((unsigned)(2 * a.nbh * (D / 16))), dim3(kThreads), 0, st, a, ws);
     prof_end(a.p.timer, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     prof_begin(a.p.timer, "k_bgrad", st);
@@ -1262,7 +1354,7 @@ hipError_t backward_chunked(const BwdProblem& a_in, void* workspace, hipStream_t
         g.bh0 = 0;
         g.nbh = BH;
         CbWs ws{};
-        hipLaunchKernelGGL((D == 64 ? k_bchain<64, GDN_BF16> : k_bchain<128, GDN_BF16>),
+        hipLaunchKernelGGL((D == 64 ? k_bchain<64, GDN_BF16, 1> : k_bchain<128, GDN_BF16, 1>),
                            dim3((unsigned)(2 * BH * (D / 16))), dim3(kThreads), 0, st, g, ws);
         return hipGetLastError();
     }

@@ -96,6 +96,10 @@ CHUNKED_CASES = [
     ("f32", "scalar", PTD, 128, 128, 1, 2, 100, 0.3, 2.0),    # fp32 inputs
     ("f32", "scalar", DTP, 64, 64, 1, 3, 1, 0.5, 2.0),        # a single token
     ("bf16", "scalar", DTP, 128, 128, 1, 2, 1000, 0.02, 2.0), # 16 chunks, ragged
+    # heads x 16-row slices >= 256: two slices per chain workgroup
+    ("bf16", "scalar", PTD, 128, 128, 2, 16, 200, 0.3, 2.0),  # 32 heads, 3 chunks + 8 tokens
+    ("bf16", "scalar", DTP, 64, 64, 4, 16, 130, 0.3, 6.0),    # 64 heads at d = 64, long memory
+    ("f32", "scalar", PTD, 128, 128, 1, 32, 70, 0.0, -1.0),   # fp32 inputs, one chunk + 6 tokens
 ]
 
 
