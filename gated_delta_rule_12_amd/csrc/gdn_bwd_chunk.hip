@@ -1080,9 +1080,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
     }
 
     // ---- phase 3: dQ and dK, value-column blocks db = w MT + mi.  State
-    // products first, in two passes over the value blocks vb (S with dO and
-    // dU', then dS_end with Delta), each fetching block vb + 1 while block vb
-    // multiplies
+    // products first, in one pass over the value blocks vb (S with dO and
+    // dU', dS_end with Delta, and <dS_end, S>), fetching block vb + 1 while
+    // block vb multiplies: every state fragment is read once
     float fo[4], fu[4], fr[4], okr[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -1092,24 +1092,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
         fu[tb] = -__expf(sh.gphi[t] + sh.gplo[t]) * sh.gbeta[t];
         fr[tb] = ratio(sh.ghi[C - 1], sh.glo[C - 1], sh.ghi[t], sh.glo[t]);
     }
-    struct PassA {
-        f32x4 sf[MT], ao[4], au[4];
-    };
-    struct PassB {
-        f32x4 sf[MT], dsf[MT], ad[4];
+    struct PassIn {
+        f32x4 sf[MT], dsf[MT], ao[4], au[4], ad[4];
     };
     auto fidx = [&](int vb, int mi) { return ((size_t)(vb * NB + w * MT + mi) * 64 + l) * 4; };
-    auto loadA = [&](PassA& x, int vb) {
-        vb = min(vb, NB - 1);
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) x.sf[mi] = ld4f(Sf + fidx(vb, mi));
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            x.ao[tb] = ld4f(a.dout + rowaddr(16 * tb + c16) + 16 * vb + 4 * g4);
-            x.au[tb] = ld4f(dUp + (16 * tb + c16) * D + 16 * vb + 4 * g4);
-        }
-    };
-    auto loadB = [&](PassB& x, int vb) {
+    auto load_pass = [&](PassIn& x, int vb) {
         vb = min(vb, NB - 1);
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
@@ -1117,53 +1104,40 @@ __global__ __launch_bounds__(kThreads, 2) void k_bgrad(BwdProblem a, CbWs ws) {
             x.dsf[mi] = ld4f(dSf + fidx(vb, mi));
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) x.ad[tb] = ld4f(Dl + (16 * tb + c16) * D + 16 * vb + 4 * g4);
+        for (int tb = 0; tb < 4; ++tb) {
+            x.ao[tb] = ld4f(a.dout + rowaddr(16 * tb + c16) + 16 * vb + 4 * g4);
+            x.au[tb] = ld4f(dUp + (16 * tb + c16) * D + 16 * vb + 4 * g4);
+            x.ad[tb] = ld4f(Dl + (16 * tb + c16) * D + 16 * vb + 4 * g4);
+        }
     };
-    PassA pa, pa2;
-    loadA(pa, 0);
+    PassIn pa, pa2;
+    load_pass(pa, 0);
     __syncthreads();
 
     f32x4 aQ[4][MT], aK1[4][MT], aK2[4][MT];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) aQ[tb][mi] = aK1[tb][mi] = zero4();
+        for (int mi = 0; mi < MT; ++mi) aQ[tb][mi] = aK1[tb][mi] = aK2[tb][mi] = zero4();
+    float sdot = 0.f;
 #pragma unroll 1
     for (int vb = 0; vb < NB; ++vb) {
-        loadA(pa2, vb + 1);
+        load_pass(pa2, vb + 1);
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) sdot += dot4(pa.sf[mi], pa.dsf[mi]);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             const f32x4 Ao = (okr[tb] * fo[tb]) * pa.ao[tb];
             const f32x4 Au = fu[tb] * pa.au[tb];
+            const f32x4 Ad = fr[tb] * pa.ad[tb];
 #pragma unroll
             for (int mi = 0; mi < MT; ++mi) {
                 aQ[tb][mi] = blk(Ao, pa.sf[mi], aQ[tb][mi]);
                 aK1[tb][mi] = blk(Au, pa.sf[mi], aK1[tb][mi]);
+                aK2[tb][mi] = blk(Ad, pa.dsf[mi], aK2[tb][mi]);
             }
         }
         pa = pa2;
-    }
-    float sdot = 0.f;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) aK2[tb][mi] = zero4();
-    {
-        PassB pb, pb2;
-        loadB(pb, 0);
-#pragma unroll 1
-        for (int vb = 0; vb < NB; ++vb) {
-            loadB(pb2, vb + 1);
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) sdot += dot4(pb.sf[mi], pb.dsf[mi]);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const f32x4 Ad = fr[tb] * pb.ad[tb];
-#pragma unroll
-                for (int mi = 0; mi < MT; ++mi) aK2[tb][mi] = blk(Ad, pb.dsf[mi], aK2[tb][mi]);
-            }
-            pb = pb2;
-        }
     }
     // K^T and Q^T fragments of the wave's value blocks, for the rest of dQ, dK
     R8<DT> kf[MT][2], qf[MT][2];
