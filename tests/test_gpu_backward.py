@@ -122,10 +122,11 @@ def test_chunked_backward_matches_oracle(case):
     check(got, ref)
 
 
-def test_chunked_backward_main_workload_sampled():
+def test_chunked_backward_main_workload():
     """The training shape the benchmark times (2 x 16 heads of 8192 tokens at
-    d = 128, bf16, scalar gate): the whole batch through gdn_backward, two
-    (batch, head) slices against the oracle over all 8192 tokens."""
+    d = 128, bf16, scalar gate): the whole batch through gdn_backward and
+    every (batch, head) slice against the oracle over all 8192 tokens (the
+    fp64 token loop takes about 15 s on 8 host threads)."""
     import torch
     from gated_delta_rule_12_amd.workloads import WORKLOADS, make_grads
     w = WORKLOADS[2]
@@ -136,12 +137,10 @@ def test_chunked_backward_main_workload_sampled():
     res = gdn.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state0"],
                        torch.from_numpy(gr["dout"]).cuda(), torch.from_numpy(gr["dstate"]).cuda())
     torch.cuda.synchronize()
-    for b, h in ((0, 3), (1, 15)):
-        sl = lambda x: x[b:b + 1, :, h:h + 1]
-        ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]), sl(inp["beta"]),
-                              inp["state0"][b:b + 1, h:h + 1], sl(gr["dout"]), gr["dstate"][b:b + 1, h:h + 1])
-        got = [sl(x).cpu().numpy() for x in res[:5]] + [res[5][b:b + 1, h:h + 1].cpu().numpy()]
-        check(got, ref)
+    got = [_np(x) for x in res]
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["state0"],
+                          gr["dout"], gr["dstate"])
+    check(got, ref)
 
 
 def test_chunked_backward_is_deterministic():
@@ -175,7 +174,7 @@ def test_backward_empty_sequence():
     assert np.array_equal(got[5], ref[5].astype(np.float32))
 
 
-def test_backward_long_sequence_sampled():
+def test_backward_long_sequence():
     """2048 tokens of d = 128 (32 checkpoint intervals), bf16, against the
     oracle on every head."""
     w = Workload("bwd-long", B=1, H=2, T=2048, dk=128, dv=128, chunk=64, state0_std=0.02,
