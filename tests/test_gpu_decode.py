@@ -138,9 +138,9 @@ def test_prefill_then_decode(gate):
     check(o, s2, o_ref, s_ref, tol=TOL["bf16"])
 
 
-def test_decode_workload_sampled():
-    """The benchmark's decode batch (every head one step, in place), checked
-    on sampled heads; the other heads' rows are checked for finiteness."""
+def test_decode_workload():
+    """The benchmark's decode batch (every head one step, in place), every
+    (batch, head) slice against the oracle."""
     import torch
     w = DECODE_WORKLOAD
     inp = make_inputs(w)
@@ -149,15 +149,10 @@ def test_decode_workload_sampled():
     args = [token(d, n, 0) for n in ("q", "k", "v", "alpha", "beta")]
     o, _ = gdn.decode_step(*args, st, inplace=True)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    bh = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H)))
-                                         for _ in range(10)]
-    o_ref, s_ref = oracle_on(inp, w.gate, PTD, bh)
+    o_ref, s_ref = oracle_on(inp, w.gate, PTD)
     on, sn = _np(o), _np(st)
-    assert np.isfinite(on).all() and np.isfinite(sn).all()
-    oo = np.stack([on[b, h][None, None] for b, h in bh])
-    ss = np.stack([sn[b, h] for b, h in bh])[:, None]
-    check(oo, ss, o_ref, s_ref)
+    # the step's output [B, H, dv] as a one-token sequence [B, 1, H, dv]
+    check(on[:, None], sn, o_ref, s_ref)
 
 
 @pytest.mark.parametrize("order", [PTD, DTP])

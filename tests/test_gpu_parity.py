@@ -299,12 +299,12 @@ def test_workspace_too_small_is_an_error():
 
 
 # --------------------------------------------------------------------------
-# full-size workloads (bench launch configuration), sampled slices
+# full-size workloads (bench launch configuration), every slice
 # --------------------------------------------------------------------------
 
 # --------------------------------------------------------------------------
 # whole-head chunk loop (scalar gate, at least 128 (head, segment) groups):
-# two passes and the start-state chain, sampled heads against the oracle
+# two passes and the start-state chain, every head against the oracle
 # --------------------------------------------------------------------------
 
 WHOLE = [
