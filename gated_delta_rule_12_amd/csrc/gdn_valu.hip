@@ -85,10 +85,13 @@ __global__ __launch_bounds__(kThreads) void k_prep_valu(Problem p, ValuWs w, flo
     }
     for (int t = tid; t < C; t += kThreads) bs[t] = t < nt ? p.beta[row(t)] : 0.f;
 
-    // chunk-local log prefixes; padded tokens neither decay nor write
+    // chunk-local log prefixes; padded tokens neither decay nor write (the
+    // loops over tokens and keys below read global memory every iteration and
+    // are unrolled so that several loads are in flight)
     if (!channel) {
         if (tid == 0) {
             float g = 0.f;
+#pragma unroll 8
             for (int t = 0; t < C; ++t) {
                 const float prev = g;
                 if (t < nt) g += logf(p.alpha[row(t)]);
@@ -98,6 +101,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_valu(Problem p, ValuWs w, flo
         }
     } else if (tid < dk) {
         float g = 0.f;
+#pragma unroll 8
         for (int t = 0; t < C; ++t) {
             if (t < nt) g += logf(p.alpha[row(t) * dk + tid]);
             Gl[t * dk + tid] = g;
@@ -133,6 +137,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_valu(Problem p, ValuWs w, flo
         const int t = e / C, j = e - (e / C) * C;
         float l = 0.f, s = 0.f;
         if (j <= t) {
+#pragma unroll 8
             for (int a = 0; a < dk; ++a) {
                 const float kj = Ks[j * (dk + 1) + a];
                 const float qt = t < nt ? gdn_ld<DT>(p.q, row(t) * dk + a) : 0.f;
@@ -215,6 +220,9 @@ __global__ __launch_bounds__(kThreads) void k_rec_valu(Problem p, ValuWs w, floa
     float* corr = reinterpret_cast<float*>(wsb + L.corr);
     const int i_begin = g * sp.per;
     const int i_end = min(p.NC, (g + 1) * sp.per);
+    // (the inner products read the chunk's operands from global memory, one
+    // load an iteration: unrolled so that eight loads are in flight at once
+    // instead of one round trip per term)
     for (int i = i_begin; i < i_end; ++i) {
         const int64_t ch = bh * p.NC + i;
         const int64_t t0 = (int64_t)i * C;
@@ -230,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void k_rec_valu(Problem p, ValuWs w, floa
         for (int e = tid; e < C * kRows; e += kThreads) {
             const int t = e >> 4, r = e & 15;
             float y = 0.f;
+#pragma unroll 8
             for (int a = 0; a < dk; ++a) y += Kp[t * dk + a] * Ss[r * (dk + 1) + a];
             float vv = 0.f;
             if (!scaling && t < nt) vv = gdn_ld<DT>(p.v, ((b * T + t0 + t) * H + h) * dv + r0 + r);
@@ -240,6 +249,7 @@ __global__ __launch_bounds__(kThreads) void k_rec_valu(Problem p, ValuWs w, floa
         for (int e = tid; e < C * kRows; e += kThreads) {
             const int t = e >> 4, r = e & 15;
             float d = 0.f;
+#pragma unroll 8
             for (int j = 0; j <= t; ++j) d += Tp[t * C + j] * Xs[j * (kRows + 1) + r];
             Ds[t * (kRows + 1) + r] = d;
         }
@@ -248,7 +258,9 @@ __global__ __launch_bounds__(kThreads) void k_rec_valu(Problem p, ValuWs w, floa
         for (int e = tid; e < C * kRows; e += kThreads) {
             const int t = e >> 4, r = e & 15;
             float o = 0.f;
+#pragma unroll 8
             for (int a = 0; a < dk; ++a) o += Qg[t * dk + a] * Ss[r * (dk + 1) + a];
+#pragma unroll 8
             for (int j = 0; j <= t; ++j) o += P[t * C + j] * Ds[j * (kRows + 1) + r];
             o *= p.scale;
             if (scaling) corr[ch * C * dk + (int64_t)t * dk + r0 + r] = o;
@@ -259,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_rec_valu(Problem p, ValuWs w, floa
         for (int e = tid; e < kRows * dk; e += kThreads) {
             const int r = e / dk, a = e - (e / dk) * dk;
             float s = Ss[r * (dk + 1) + a] * bC[a];
+#pragma unroll 8
             for (int t = 0; t < C; ++t) s += Ds[t * (kRows + 1) + r] * Kb[t * dk + a];
             Ss[r * (dk + 1) + a] = s;
         }
