@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kThreads, DT == GDN_BF16 ? 4 : 2) void k_bprep(BwdP
             if (tb >= w) acc = blk(pk[tb], db[tb], acc);
         st4f(ws.Ef + ci * Rec<D>::kRows + ((size_t)(vb * 4 + w) * 64 + l) * 4, p.scale * acc);
     }
-    ut_inverse_lds(AT);
+    ut_inverse_lds(AT, threadIdx.x);
 
     // T and T^T, row-major, zero above (below) the diagonal
     float* Tg = ws.T + ci * Rec<D>::kTile;

@@ -110,11 +110,11 @@ __host__ __device__ constexpr int tslot(int m, int s) { return m < 2 ? m : 2 + 2
 // strictly lower off-diagonal blocks transposed and its diagonal blocks in
 // place; T replaces the diagonal blocks and fills the lower triangle) and
 // T' = T diag(beta) written as A-operand fragments, for both stage-1 kernels.
-// Called by all threads of the workgroup (it contains barriers).
-__device__ __forceinline__ void ut_inverse_store(float* AT, const float* bsh, u16x8* dst) {
+// Called by all threads of a four-wave group (it contains barriers; tid is
+// the thread's index in the group); nothing is stored unless write is set.
+__device__ __forceinline__ void ut_inverse_store(float* AT, const float* bsh, u16x8* dst, int tid, bool write) {
     constexpr int LDA = C + 4;
-    const int tid = threadIdx.x;
-    ut_inverse_lds(AT);
+    ut_inverse_lds(AT, tid);
     // T' = T diag(beta): [slot(m, s)][hi/lo][lane] of 8 bf16; lane (row
     // 16m + lane % 16, group g), slot e -> column 32s + 4g + e (e < 4) or
     // 32s + 16 + 4g + e - 4; entries above the block diagonal are zero (the
@@ -137,8 +137,10 @@ __device__ __forceinline__ void ut_inverse_store(float* AT, const float* bsh, u1
         }
         // (non-temporal: written once here, read by the chunk loops later;
         // measured 5 % off stage 1 and nothing on the readers)
-        __builtin_nontemporal_store(__builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]}), &dst[(slot * 2 + 0) * 64 + lane]);
-        __builtin_nontemporal_store(__builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]}), &dst[(slot * 2 + 1) * 64 + lane]);
+        if (write) {
+            __builtin_nontemporal_store(__builtin_bit_cast(u16x8, uint4{hi[0], hi[1], hi[2], hi[3]}), &dst[(slot * 2 + 0) * 64 + lane]);
+            __builtin_nontemporal_store(__builtin_bit_cast(u16x8, uint4{lo[0], lo[1], lo[2], lo[3]}), &dst[(slot * 2 + 1) * 64 + lane]);
+        }
     }
 }
 
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* 
     }
     __syncthreads();
 
-    ut_inverse_store(AT, bsh, tfrag + ch * kTfragPerChunk);
+    ut_inverse_store(AT, bsh, tfrag + ch * kTfragPerChunk, threadIdx.x, true);
 }
 
 // Scalar gate, stage 1 with a small LDS footprint (18.3 KiB, so eight
@@ -437,15 +439,25 @@ __global__ __launch_bounds__(kThreads, 3) void k_prep_channel(Problem p, u16x8* 
 // (bf16) for the Gram product, then both the UT system A (strictly lower
 // blocks stored transposed in the upper triangle, diagonal blocks in place
 // until their inverse replaces them) and T = (I + A)^{-1} (lower triangle).
+struct PrepScalarShared {
+    float AT[C * (C + 4)];
+    float gsh[C], gpsh[C], bsh[C];
+    float rqsh[C], rksh[C];  // 1 / |q_t|, 1 / |k_t| (raw projections; else ones)
+};
+// Chunk i of head (b, h) by a four-wave group (tid: the thread's index in
+// the group; every barrier is a workgroup barrier, which a second group of
+// the workgroup passes with its own chunk); stores nothing unless write is set.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfrag, float* gates) {
+__device__ __forceinline__ void prep_scalar_chunk(const Problem& p, u16x8* tfrag, float* gates, int i, int h, int b,
+                                                  PrepScalarShared& ps, int tid, bool write) {
     constexpr int LDA = C + 4;
-    __shared__ __attribute__((aligned(16))) float AT[C * LDA];
-    __shared__ __attribute__((aligned(16))) float gsh[C], gpsh[C], bsh[C];
-    __shared__ __attribute__((aligned(16))) float rqsh[C], rksh[C];  // 1 / |q_t|, 1 / |k_t| (raw projections; else ones)
-
-    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    float* const AT = ps.AT;
+    float* const gsh = ps.gsh;
+    float* const gpsh = ps.gpsh;
+    float* const bsh = ps.bsh;
+    float* const rqsh = ps.rqsh;
+    float* const rksh = ps.rksh;
+    const int w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
     const int64_t H = p.H, T = p.T;
     const int64_t t0 = (int64_t)i * C;
     const int nt = (int)((T - t0) < C ? (T - t0) : C);
@@ -524,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
     __syncthreads();  // K rows, the gate prefix and the row factors visible
     // the gate block for the chunk loop (after the K rows, whose wait on the
     // vector-memory counter would otherwise include these stores)
-    if (w == 0) {
+    if (w == 0 && write) {
         const float gv = gsh[l], gpv = gpsh[l], gC = gsh[C - 1];
         const float rq = rqsh[l], rk = rksh[l];
         float* gb = gates + ch * kGateFloats;
@@ -580,7 +592,13 @@ __global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfra
     }
     __syncthreads();
 
-    ut_inverse_store(AT, bsh, tfrag + ch * kTfragPerChunk);
+    ut_inverse_store(AT, bsh, tfrag + ch * kTfragPerChunk, tid, write);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_prep_scalar(Problem p, u16x8* tfrag, float* gates) {
+    __shared__ __attribute__((aligned(16))) PrepScalarShared ps;
+    prep_scalar_chunk<D>(p, tfrag, gates, blockIdx.x, blockIdx.y, blockIdx.z, ps, threadIdx.x, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -2377,17 +2395,44 @@ constexpr int seg_threads() {
 }
 template <int D, int MODE>
 constexpr int seg_waves_per_eu() { return seg_threads<D, MODE>() / 256 < 1 ? 1 : seg_threads<D, MODE>() / 256; }
+// Stage 1 of the last segment's chunks of one head, inside the state pass
+// (which has no workgroup for that segment, and whose (head, segment)
+// workgroups leave compute units idle): the workgroup's two four-wave groups
+// take the chunks two at a time, each in its own part of the LDS; a group
+// with no chunk left in the last pair repeats the last chunk, storing nothing.
+template <int D>
+__device__ __forceinline__ void prep_last_segment(const Problem& p, const Split& sp, u16x8* tfrag, float* gates,
+                                                  int64_t head, SegShared<D, kSegState>& sh) {
+    static_assert(seg_threads<D, kSegState>() == 2 * kThreads, "two four-wave groups");
+    static_assert(2 * sizeof(PrepScalarShared) <= sizeof(SegShared<D, kSegState>), "two stage-1 tiles fit");
+    const int grp = threadIdx.x / kThreads, tid = threadIdx.x % kThreads;
+    PrepScalarShared& ps = reinterpret_cast<PrepScalarShared*>(&sh)[grp];
+    const int b = (int)(head / p.H), h = (int)(head % p.H);
+    const int i0 = (sp.G - 1) * sp.per;
+    for (int i = i0; i < p.NC; i += 2) {
+        if (i > i0) __syncthreads();  // the previous pair's LDS reads are done
+        const int ic = i + grp;
+        prep_scalar_chunk<D>(p, tfrag, gates, min(ic, p.NC - 1), h, b, ps, tid, ic < p.NC);
+    }
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__((seg_threads<D, MODE>()), (seg_waves_per_eu<D, MODE>())) void k_seg(
-    Problem p, Split sp, WsLayout L, char* wsb, const u16x8* tfrag, const float* gates) {
+    Problem p, Split sp, WsLayout L, char* wsb, u16x8* tfrag, float* gates) {
     constexpr int NV = kSegNV<D>;
     __shared__ __attribute__((aligned(16))) SegShared<D, MODE> sh;
     if constexpr (MODE == kSegOut) {
         const int id = blockIdx.x;
         seg_body<D, MODE, 0, NV>(p, sp, L, wsb, tfrag, gates, id / sp.G, id % sp.G, sh);
     } else {
-        // workgroup (head, segment g < G - 1)
+        // workgroup (head, segment g < G - 1), then one per head for stage 1
+        // of the last segment
         const int nseg = sp.G - 1;
+        const int64_t nstate = p.B * p.H * (int64_t)nseg;
+        if ((int64_t)blockIdx.x >= nstate) {
+            prep_last_segment<D>(p, sp, tfrag, gates, (int64_t)blockIdx.x - nstate, sh);
+            return;
+        }
         if constexpr (kSegPaired<D>)
             seg_body<D, MODE, 3, 2>(p, sp, L, wsb, tfrag, gates, blockIdx.x / nseg, blockIdx.x % nseg, sh);
         else
@@ -2568,8 +2613,12 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
     const int64_t nch = p.B * p.H * (int64_t)p.NC;
     const size_t fbytes = align256((size_t)nch * kTfragPerChunk * sizeof(u16x8));
     float* gates = reinterpret_cast<float*>(ws + L.prep + fbytes);
-    {
-        dim3 grid(p.NC, (unsigned)p.H, (unsigned)p.B);
+    // With segments, stage 1 of the last segment's chunks runs inside the
+    // state pass (which does not read them), on its extra workgroups.
+    const int64_t first_end = (int64_t)(sp.G - 1) * sp.per;
+    const int nc_first = sp.G > 1 && first_end < p.NC ? (int)first_end : p.NC;
+    if (nc_first > 0) {
+        dim3 grid(nc_first, (unsigned)p.H, (unsigned)p.B);
         prof_begin(p.timer, "k_prep_mfma", st);
         hipLaunchKernelGGL((k_prep_scalar<D>), grid, dim3(kThreads), 0, st, p, tfrag, gates);
         prof_end(p.timer, st);
@@ -2579,7 +2628,7 @@ hipError_t launch_seg(const Problem& p, const Split& sp, char* ws, const WsLayou
     const int64_t heads = p.B * p.H;
     if (sp.G > 1) {
         prof_begin(p.timer, "k_seg_state", st);
-        hipLaunchKernelGGL((k_seg<D, kSegState>), dim3((unsigned)(heads * (sp.G - 1))), dim3(seg_threads<D, kSegState>()), 0, st,
+        hipLaunchKernelGGL((k_seg<D, kSegState>), dim3((unsigned)(heads * sp.G)), dim3(seg_threads<D, kSegState>()), 0, st,
                            p, sp, L, ws, tfrag, gates);
         prof_end(p.timer, st);
         hipError_t e = hipGetLastError();

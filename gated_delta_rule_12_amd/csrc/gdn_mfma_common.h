@@ -59,7 +59,9 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
 // diagonal blocks and the lower triangle hold T (unit lower triangular, exact
 // zeros above the diagonal inside the diagonal blocks) and the upper
 // off-diagonal blocks still hold A transposed.  Called by all threads of a
-// four-wave workgroup (it contains barriers).  The strictly lower
+// four-wave group (it contains workgroup barriers; tid is the thread's index
+// in its group of 256, so two groups of one workgroup can each invert their
+// own tile, passing the same barriers).  The strictly lower
 // off-diagonal blocks are free until the off-diagonal phase fills them, so
 // the diagonal phase keeps each wave's power of N in one of them (row stride
 // C + 4 spreads a lane group's column writes over every bank).
@@ -68,9 +70,9 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
 //     accumulators (lane: column c16, rows 4 g4 + i) serve as B operands as
 //     they stand (instruction s contracts the indices 4G + s, G = lane / 16);
 //   off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
-__device__ __forceinline__ void ut_inverse_lds(float* AT) {
+__device__ __forceinline__ void ut_inverse_lds(float* AT, int tid) {
     constexpr int LDA = C + 4;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
+    const int w = tid >> 6, l = tid & 63, g4 = l >> 4, c16 = l & 15;
     {
         float* Xb = &AT[(16 * w) * LDA + 16 * w];
         // scratch block (1, 0), (2, 0), (3, 0) or (3, 1) for waves 0 .. 3
