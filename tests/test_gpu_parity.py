@@ -310,9 +310,11 @@ def test_workspace_too_small_is_an_error():
 WHOLE = [
     # B, H, T, d, G (None: gdn_chunk_fwd's schedule), order, state0_std, alpha_mean
     (1, 32, 1000, 128, 4, PTD, 0.5, 2.0),    # ragged tail, 4 chunks per segment
-    (1, 32, 1050, 128, 5, DTP, 0.5, 2.0),    # last segment a single ragged chunk
+    (1, 32, 1050, 128, 5, DTP, 0.5, 2.0),    # last segment a single ragged chunk (its stage 1
+                                             # in the state pass: one group of the pair idle)
     (1, 32, 700, 64, 4, DTP, 0.3, 2.0),
-    (1, 64, 640, 128, 2, PTD, 0.5, 2.0),     # two segments: no chain step
+    (1, 64, 640, 128, 2, PTD, 0.5, 2.0),     # two segments: no chain step; the last
+                                             # segment's five chunks end on an odd pair
     (2, 16, 2000, 128, None, PTD, 0.5, 2.0),  # library schedule (7 segments)
     (1, 32, 512, 128, 4, PTD, 0.0, 6.0),     # long memory, zero start state
     (1, 32, 512, 128, 4, DTP, 0.5, -6.0),    # fast forgetting
